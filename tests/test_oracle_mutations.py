@@ -1,0 +1,51 @@
+"""Each plausible mistake planted in a scratch copy of the oracle must make at
+least one oracle pin fail (CPU only; the repository's oracle is not touched)."""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MUTS = [
+ ("selection.py", "pos = n - w + np.arange(w)[:, None]", "pos = n - w + 1 + np.arange(w)[:, None]"),
+ ("selection.py", "k[h // g, :n]", "k[h % k.shape[0], :n]"),
+ ("selection.py", "order = np.lexsort((cand, -s))", "order = np.lexsort((-cand, -s))"),
+ ("selection.py", "* scale\n    pos", "* scale * 1.01\n    pos"),
+ ("attention.py", "kk = k[h // g, :n_rows]", "kk = k[h % k.shape[0], :n_rows]"),
+ ("attention.py", "z = kk @ q[h].astype(np.float64) * scale\n        m = z.max()", "z = kk @ q[h].astype(np.float64)\n        m = z.max()"),
+ ("attention.py", "den = (wgt * l).sum(axis=1)", "den = l.sum(axis=1)"),
+ ("cats.py", "return np.abs(act_f32) > t32", "return np.abs(act_f32) >= t32"),
+ ("cats.py", "return w_down_t.astype(np.float64).T @ hmid", "return w_up.astype(np.float64).T @ hmid"),
+ ("cats.py", "return g / (1.0 + np.exp(-g))", "return g / (1.0 + np.exp(g))"),
+ ("cats.py", "return float(v[k - 1])", "return float(v[k])"),
+ ("step.py", "lo * c - hi * s, hi * c + lo * s", "lo * c + hi * s, hi * c - lo * s"),
+ ("step.py", "np.sqrt(np.mean(x * x) + eps)", "np.sqrt(np.mean(x * x)) + eps"),
+ ("step.py", "out[nz] = np.round(x[nz] / ulp) * ulp", "out[nz] = np.floor(x[nz] / ulp + 0.5) * ulp"),
+ ("step.py", "h = h + layer.w_o @ o.reshape(-1)", "h = layer.w_o @ o.reshape(-1)"),
+ ("step.py", "inv_freq = theta ** (-(2.0 * np.arange(half)) / d_h)", "inv_freq = theta ** (-(np.arange(half)) / d_h)"),
+ ("byte_account.py", "return 2 * dm.d_model * dm.d_ff", "return 3 * dm.d_model * dm.d_ff"),
+ ("byte_account.py", "return dm.d_model * qkv_out + dm.n_q_heads * dm.head_dim * dm.d_model", "return dm.d_model * qkv_out"),
+ ("byte_account.py", "den = 2.0 * batch * dm.n_kv_heads", "den = 2.0 * dm.n_kv_heads"),
+]
+
+PIN_FILES = ["tests/test_oracle_byte_account.py", "tests/test_oracle_selection.py",
+             "tests/test_oracle_attention.py", "tests/test_oracle_cats.py",
+             "tests/test_oracle_step.py"]
+
+
+@pytest.mark.parametrize("fname,old,new", MUTS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTS)])
+def test_planted_mistake_is_caught(tmp_path, fname, old, new):
+    for sub in ("oracle", "tests", "synth"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
+                        ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
+    p = tmp_path / "oracle" / fname
+    s = p.read_text()
+    assert old in s, "mutation site vanished from the oracle"
+    p.write_text(s.replace(old, new, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider"]
+                       + PIN_FILES, cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, "planted mistake survived every pin:\n" + r.stdout[-2000:]
