@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X.
+
+Workload: 32 stacked 8B-class layers (d 4096, 32/8 heads, head_dim 128, FFN
+14336, bf16 weights and caches) with independent N(0, 0.02^2) weights and
+synthetic caches (K, V ~ N(0,1) times LogNormal(0, 0.5) channel scales), at
+context 2K/8K/32K/64K/128K, in four modes: dense, KV (10% keep, one-time
+attention-scored selection), CATS (thresholds for 50% gate sparsity from 256
+Gaussian calibration states per layer), and both.  The headline is the
+composed step ("both") at 128K.
+
+A step is one call of sd_decode_step through all 32 layers (each layer
+appends its key/value row, so the context grows by one per step).  Inputs are
+resident in HBM before timing; W warm-up steps, then K timed steps bracketed
+by a device synchronize and HIP events on the library's stream.
+
+value = algorithmic HBM bytes per step / time per step (GB/s, 1e9 bytes):
+weights read (QKV, O, gate, kept up rows, kept down rows), cached K/V rows
+read, and the appended rows written.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("decode-step µs and achieved HBM GB/s (% of peak) vs context length, "
+          "dense/KV/CATS/both")
+HBM_PEAK_GBS = 8000.0
+MODES = ("dense", "kv", "cats", "both")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--contexts", type=str, default="2048,8192,32768,65536,131072")
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--out", type=str, default="")
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+
+        import kv_cache_activation_amd as sd
+        import synth
+        from synth import device as sdev
+
+        self.torch, self.sd, self.synth = torch, sd, synth
+        self.args = args
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        wl = synth.STACK32_128K
+        self.wl = wl
+        self.L = args.layers
+        self.contexts = [int(c) for c in args.contexts.split(",")]
+        n_max = max(self.contexts)
+        grow = args.warmup + args.steps + 2
+        self.cap_full = n_max + grow + 64
+        self.cap_sel = int(math.floor(wl.keep_ratio * n_max)) + grow + 64
+        self.dims = sd.make_dims(wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff,
+                                 sd.SD_BF16, sd.SD_BF16)
+        self.ws = torch.empty(sd.sd_workspace_bytes(self.dims, n_max, wl.window),
+                              dtype=torch.uint8, device=self.dev)
+        self.W, self.K, self.V, self.KS, self.VS, self.QW, self.MASK = [], [], [], [], [], [], []
+        for li in range(self.L):
+            self.W.append(sdev.layer_weights(wl, li, self.dev))
+            k, v = sdev.kv_cache(wl, li, n_max, self.cap_full, self.dev)
+            self.K.append(k)
+            self.V.append(v)
+            self.KS.append(torch.zeros(wl.n_kv_heads, self.cap_sel, wl.head_dim,
+                                       dtype=torch.bfloat16, device=self.dev))
+            self.VS.append(torch.zeros_like(self.KS[-1]))
+            self.QW.append(sdev.window_queries(wl, li, self.dev))
+            self.MASK.append(torch.zeros(wl.d_ff, dtype=torch.uint8, device=self.dev))
+        self.scores = torch.empty(wl.n_kv_heads, n_max, device=self.dev)
+        self.idx = torch.empty(wl.n_kv_heads * n_max, dtype=torch.int32, device=self.dev)
+        self.h0 = sdev.hidden(wl, 0, self.dev)
+        self.hidden = self.h0.clone()
+        self.thresholds = self.calibrate()
+        layers = []
+        for li in range(self.L):
+            W = self.W[li]
+            layers.append(sd.sd_layer(
+                W["attn_norm"].data_ptr(), W["w_qkv"].data_ptr(), W["w_o"].data_ptr(),
+                W["mlp_norm"].data_ptr(), W["w_gate"].data_ptr(), W["w_up"].data_ptr(),
+                W["w_down_t"].data_ptr(), self.thresholds[li], 0, self.K[li].data_ptr(),
+                self.V[li].data_ptr(), self.cap_full, 0, self.KS[li].data_ptr(),
+                self.VS[li].data_ptr(), self.cap_sel, 0, self.MASK[li].data_ptr()))
+        self.layers = (sd.sd_layer * self.L)(*layers)
+        torch.cuda.synchronize()
+
+    def calibrate(self, n_states=256, sparsity=0.5):
+        torch, sd = self.torch, self.sd
+        from synth import device as sdev
+        ws = torch.empty(sd.sd_calibrate_workspace_bytes(self.dims, n_states), dtype=torch.uint8,
+                         device=self.dev)
+        thr = torch.empty(self.L, device=self.dev)
+        for li in range(self.L):
+            states = sdev.calibration_states(self.wl, li, n_states, self.dev)
+            sd.sd_cats_calibrate(self.dims, states, n_states, self.W[li]["mlp_norm"],
+                                 self.W[li]["w_gate"], sparsity, thr[li:li + 1], ws)
+        return thr.cpu().tolist()
+
+    def select(self, n):
+        """One-time selection at context n for every layer; returns seconds."""
+        torch, sd, wl = self.torch, self.sd, self.wl
+        k_keep = int(math.floor(wl.keep_ratio * n))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for li in range(self.L):
+            sd.sd_select_kv(self.dims, self.K[li], self.V[li], self.cap_full, n, self.QW[li],
+                            wl.window, wl.n_sink, k_keep, self.scores, self.idx, self.KS[li],
+                            self.VS[li], self.cap_sel, 0, self.ws)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, k_keep
+
+    def reset(self, n, k_keep):
+        for L in self.layers:
+            L.n_full = n
+            L.n_sel = k_keep
+        self.hidden.copy_(self.h0)
+
+    def run_steps(self, n, mode_flags, count):
+        for i in range(count):
+            self.sd.sd_decode_step(self.dims, self.layers, n + i, self.hidden, mode_flags, self.ws)
+
+    def step_bytes(self, n_read, n_kept_mean):
+        wl = self.wl
+        d, dh = wl.d_model, wl.head_dim
+        w = 2 * (d * wl.qkv_out + wl.n_q_heads * dh * d + d * wl.d_ff + 2 * d * n_kept_mean)
+        row = 2 * wl.n_kv_heads * dh * 2
+        return self.L * (w + row * n_read + 2 * row)
+
+    def mode_flags(self, mode):
+        sd = self.sd
+        return {"dense": 0, "kv": sd.SD_KV_SPARSE, "cats": sd.SD_MLP_SPARSE,
+                "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE}[mode]
+
+    def cell(self, n, k_keep, mode):
+        torch, args = self.torch, self.args
+        flags = self.mode_flags(mode)
+        self.reset(n, k_keep)
+        self.run_steps(n, flags, args.warmup)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        self.run_steps(n + args.warmup, flags, args.steps)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        kept = self.wl.d_ff
+        if flags & self.sd.SD_MLP_SPARSE:
+            kept = sum(int(m.sum()) for m in self.MASK) / self.L
+        base = k_keep if flags & self.sd.SD_KV_SPARSE else n
+        n_read = base + args.warmup + (args.steps - 1) / 2.0 + 1
+        b = self.step_bytes(n_read, kept)
+        return dict(context=n, mode=mode, ms_per_step=ms, us_per_step=ms * 1e3,
+                    bytes_per_step=b, gbs=b / ms / 1e6, hbm_frac=b / ms / 1e6 / HBM_PEAK_GBS,
+                    n_kept_mean=kept, kv_rows_read=n_read)
+
+    def profile_cell(self, n, k_keep, mode):
+        """Per-kernel event timing of the same steps (library profiler)."""
+        torch, sd, args = self.torch, self.sd, self.args
+        flags = self.mode_flags(mode)
+        self.reset(n, k_keep)
+        self.run_steps(n, flags, args.warmup)
+        torch.cuda.synchronize()
+        sd.sd_profile_start()
+        self.run_steps(n + args.warmup, flags, args.steps)
+        stats = sd.sd_profile_stop()
+        kept = sum(int(m.sum()) for m in self.MASK) / self.L if flags & sd.SD_MLP_SPARSE \
+            else self.wl.d_ff
+        wl = self.wl
+        d, dh = wl.d_model, wl.head_dim
+        base = k_keep if flags & sd.SD_KV_SPARSE else n
+        n_read = base + args.warmup + (args.steps - 1) / 2.0 + 1
+        alg = {  # algorithmic HBM bytes per launch of each kernel
+            "qkv_rope_append": 2 * d * wl.qkv_out,
+            "o_residual": 2 * d * wl.n_q_heads * dh,
+            "cats_gate_up": 2 * d * wl.d_ff + 2 * d * kept,
+            "cats_down": 2 * d * kept,
+            "attn_partial": n_read * 2 * wl.n_kv_heads * dh * 2,
+        }
+        out = {}
+        for name, (launches, tot) in stats.items():
+            avg_us = tot / launches * 1e3
+            e = dict(launches=launches, avg_us=avg_us, total_ms=tot)
+            if name in alg:
+                e["alg_bytes"] = alg[name]
+                e["gbs"] = alg[name] / (avg_us * 1e-6) / 1e9
+                e["frac"] = e["gbs"] / HBM_PEAK_GBS
+            out[name] = e
+        return out
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only
+    while the kernel's source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+        src = os.path.join(ROOT, "kv_cache_activation_amd", "csrc", rec["source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if digest != rec["sha256"]:
+            return None
+        return rec["bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(bench, n, seconds):
+    """The float64 oracle, timed as it stands on the host cores, on a bounded
+    sample of the headline workload: the first layer of the stack (its own
+    weights and 128K cache copied to the host), composed mode, repeated until
+    `seconds` have passed; per-step time scaled to all layers."""
+    import numpy as np
+    import torch
+
+    from oracle import cats as ocats, step as ostep
+
+    wl = bench.wl
+    W = {k: v.float().cpu().numpy() for k, v in bench.W[0].items()}
+    reps_cap = 512
+    shape = (wl.n_kv_heads, n + reps_cap, wl.head_dim)
+    k = np.zeros(shape, np.float32)
+    v = np.zeros(shape, np.float32)
+    k[:, :n] = bench.K[0][:, :n].float().cpu().numpy()
+    v[:, :n] = bench.V[0][:, :n].float().cpu().numpy()
+    k_keep = int(math.floor(wl.keep_ratio * n))
+    # the rows kept do not change the work; take the first k_keep rows
+    ks = np.zeros((wl.n_kv_heads, k_keep + reps_cap, wl.head_dim), np.float32)
+    vs = np.zeros_like(ks)
+    ks[:, :k_keep] = k[:, :k_keep]
+    vs[:, :k_keep] = v[:, :k_keep]
+    h = bench.h0.cpu().numpy().astype(np.float64)
+    x2 = ostep.rmsnorm(h, W["mlp_norm"], 1e-5)
+    t = float(np.median(np.abs(ocats.gate_act(x2, W["w_gate"]).astype(np.float32))))
+    layer = ostep.Layer(W["attn_norm"], W["w_qkv"], W["w_o"], W["mlp_norm"], W["w_gate"],
+                        W["w_up"], W["w_down_t"], t, k, v, n, ks, vs, k_keep)
+    dims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                kv_dtype="bf16", eps=1e-5, theta=500000.0)
+    reps = 0
+    t0 = time.perf_counter()
+    while reps < reps_cap - 2 and (reps == 0 or time.perf_counter() - t0 < seconds):
+        tr = []
+        h = ostep.decode_layer(layer, h, n + reps, kv_sparse=True, mlp_sparse=True, trace=tr,
+                               **dims)
+        reps += 1
+    per_layer = (time.perf_counter() - t0) / reps
+    kept = float(tr[0]["mask"].sum())
+    per_step = per_layer * bench.L
+    b = bench.step_bytes(k_keep + reps / 2.0 + 1, kept)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    return dict(value=b / per_step / 1e9, unit="GB/s", cores=int(cores), kind="oracle",
+                ms_per_step=per_step * 1e3,
+                sample=(f"float64 numpy oracle, layer 0 of the {bench.L}-layer stack at context "
+                        f"{n}, composed mode (first {k_keep} rows as the gathered buffer, "
+                        f"threshold at the median |a|), {reps} decode steps of that layer in "
+                        f"{per_layer * reps:.1f} s; per-step time scaled x{bench.L} layers"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the sharded multi-GPU path is a design note only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    bench = Bench(args)
+    sweep = []
+    sel_ms = {}
+    for n in sorted(bench.contexts):
+        secs, k_keep = bench.select(n)
+        sel_ms[n] = secs * 1e3
+        for mode in MODES:
+            c = bench.cell(n, k_keep, mode)
+            c["select_ms"] = sel_ms[n] if mode in ("kv", "both") else None
+            sweep.append(c)
+            print(f"# n={n:6d} {mode:5s} {c['us_per_step']:9.1f} us/step "
+                  f"{c['gbs']:7.1f} GB/s ({100 * c['hbm_frac']:.1f}% of peak)", flush=True)
+    n_head = max(bench.contexts)
+    head = next(c for c in sweep if c["context"] == n_head and c["mode"] == "both")
+    dense = next(c for c in sweep if c["context"] == n_head and c["mode"] == "dense")
+    kv = next(c for c in sweep if c["context"] == n_head and c["mode"] == "kv")
+    k_keep = int(math.floor(bench.wl.keep_ratio * n_head))
+    bench.select(n_head)
+    kern = bench.profile_cell(n_head, k_keep, "both")
+    dom = max((k for k in kern if "alg_bytes" in kern[k]), key=lambda k: kern[k]["total_ms"])
+    dk = kern[dom]
+    roof = dict(kernel=dom, bound="hbm", achieved=round(dk["gbs"], 1), peak=HBM_PEAK_GBS,
+                unit="GB/s", frac=round(dk["frac"], 4), avg_us=round(dk["avg_us"], 2),
+                alg_bytes_per_launch=dk["alg_bytes"], traffic=traffic_for(dom))
+    payback = None
+    if dense["ms_per_step"] > kv["ms_per_step"]:
+        payback = sel_ms[n_head] / (dense["ms_per_step"] - kv["ms_per_step"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bench, n_head, args.cpu_seconds)
+    line = dict(
+        metric=METRIC, value=round(head["gbs"], 1), unit="GB/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=round(head["ms_per_step"], 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload=bench.wl.name if n_head == 131072 else f"8b-{bench.L}layer-both-ctx{n_head}",
+                    layers=bench.L, context=n_head, mode="both", kv_keep=bench.wl.keep_ratio,
+                    cats_sparsity=0.5, storage="bf16", accumulate="f32",
+                    bytes_per_step=head["bytes_per_step"], hbm_frac=round(head["hbm_frac"], 4),
+                    us_per_step=round(head["us_per_step"], 1),
+                    select_ms_all_layers=round(sel_ms[n_head], 2),
+                    select_payback_steps=None if payback is None else round(payback, 1)),
+        roofline=roof, cpu_baseline=cpu,
+        kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
+                 for k, e in kern.items()},
+        sweep=[{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}
+               for c in sweep],
+    )
+    s = json.dumps(line)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+    print(s, flush=True)
+
+
+if __name__ == "__main__":
+    main()

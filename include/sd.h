@@ -1,0 +1,277 @@
+/*
+ * sd.h -- C ABI of the MI355X (gfx950) sparse decode-step library.
+ *
+ * One single-sequence LLM decode step with two sparsity branches, as
+ * described in "Where Activation Sparsity and KV-Cache Sparsity Cross in LLM
+ * Decoding" (below: [Cross]):
+ *
+ *   - KV branch ([Cross] §4.1): once after prefill, score the cache with the
+ *     attention of an observation window of queries, keep sinks, the window
+ *     and the best-scoring entries of each KV head, and gather them into one
+ *     contiguous buffer; every later step reads that buffer with the same
+ *     split-K attention kernel that dense mode uses and appends its own key
+ *     and value to it.
+ *   - Projection branch: CATS-style activation sparsity as kept by
+ *     "Sensitivity-Aware Thresholding and Token Routing for Activation
+ *     Sparsification in Large Language Models" (below: [SATS]): the SiLU gate
+ *     output is thresholded per layer and only the kept channels' up rows and
+ *     down columns are read.
+ *   - Byte account ([Cross] §3): bytes per step, savings, speedup bounds and
+ *     crossover lengths from model dimensions and keep ratios.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Pointers are device pointers unless marked [host].  The caller
+ *   owns every buffer; the library never allocates device memory and keeps no
+ *   pointer after the call returns.  Device buffers must stay valid until the
+ *   work enqueued on `stream` has finished.  Host structs are read (and, where
+ *   stated, updated) only during the call.
+ * Layouts.  Row-major, densely packed.  Caches are [n_kv_heads, cap, head_dim]
+ *   (row j of KV head h at element (h*cap + j)*head_dim).  Weights are
+ *   [out_features, in_features] (nn.Linear order) except the down projection,
+ *   stored transposed as w_down_t [d_ff, d_model] so that one kept channel's
+ *   down column is one contiguous row.  Activations are float32.
+ * Element types.  sd_dims.w_dtype applies to all projection weights and
+ *   sd_dims.kv_dtype to all cache buffers: SD_F32 or SD_BF16.  Norm vectors
+ *   are float32.  Arithmetic is float32 throughout (bf16 inputs are widened).
+ * Alignment.  Every device pointer must be 16-byte aligned.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
+ *   is asynchronous; there is no implicit synchronization.
+ * Workspace.  Entry points that take (ws, ws_bytes) use it for intermediate
+ *   state; size it with sd_workspace_bytes().  Its contents need no
+ *   initialisation and are undefined after a call.  Calls that share one
+ *   workspace must be ordered on one stream.
+ * Errors.  Every argument check runs on the host before anything is enqueued;
+ *   a failing call enqueues nothing and returns:
+ *     SD_EINVAL        null or misaligned pointer, inconsistent sizes;
+ *     SD_ENOSPC        workspace or buffer capacity too small;
+ *     SD_EUNSUPPORTED  head_dim not 64 or 128, d_model or input widths not a
+ *                      multiple of 8 or above 8192, unknown dtype;
+ *     SD_EHIP          a HIP launch or query failed (work may be partial).
+ *   sd_last_error() gives a message for the calling thread's last failure.
+ *   No exception crosses the ABI and the library never aborts.
+ * Threads.  The library is stateless and reentrant.
+ */
+#ifndef SD_H
+#define SD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SD_OK = 0,
+  SD_EINVAL = 1,
+  SD_ENOSPC = 2,
+  SD_EUNSUPPORTED = 3,
+  SD_EHIP = 4
+} sd_status;
+
+enum { SD_F32 = 0, SD_BF16 = 1 };
+
+/* flags */
+enum {
+  SD_SCORES_IN = 1u,  /* sd_select_kv: rank caller-given scores, skip scoring */
+  SD_GATE_IN = 2u,    /* sd_sparse_mlp: mask caller-given activations, skip gate */
+  SD_KV_SPARSE = 4u,  /* sd_decode_step: attend over the gathered buffer */
+  SD_MLP_SPARSE = 8u  /* sd_decode_step: CATS-threshold the MLP */
+};
+
+/* projection sets of the byte account */
+enum { SD_PROJ_ALL7 = 0, SD_PROJ_FFN = 1, SD_PROJ_CATS = 2 };
+
+typedef struct {
+  int32_t d_model;     /* hidden width d */
+  int32_t n_q_heads;   /* query heads h_q */
+  int32_t n_kv_heads;  /* KV heads h_kv; h_q % h_kv == 0, query head h reads KV head h / (h_q/h_kv) */
+  int32_t head_dim;    /* d_h: 64 or 128 */
+  int32_t d_ff;        /* feed-forward width */
+  int32_t w_dtype;     /* SD_F32 or SD_BF16 */
+  int32_t kv_dtype;    /* SD_F32 or SD_BF16 */
+  float rms_eps;       /* RMSNorm epsilon (Llama: 1e-5) */
+  float rope_theta;    /* RoPE base (Llama-3: 500000); <= 0 disables RoPE */
+} sd_dims;
+
+/* Bytes of workspace that every call below needs for these dims, for caches
+ * of up to max_rows rows and observation windows of up to max_window queries.
+ * [host]; returns 0 on invalid dims. */
+size_t sd_workspace_bytes(const sd_dims* dims, int32_t max_rows, int32_t max_window);
+
+/*
+ * sd_select_kv -- one-time attention-scored KV selection and gather
+ * ([Cross] §4.1, SnapKV-style).
+ *
+ * k_full, v_full  [h_kv, cap_full, d_h] kv_dtype: rows 0..n-1 valid.
+ * q_window        [h_q, w, d_h] float32: queries of the last w prompt tokens
+ *                 (already rotated); query i sits at position n - w + i and
+ *                 attends causally to rows 0..n-w+i.
+ * Score of row j for KV head kv: sum over the window queries and over the
+ * query heads of group kv of the softmax weight on row j (logits scaled by
+ * 1/sqrt(d_h)).  Rows [0, n_sink) and [n-w, n) are always kept; the other
+ * k_keep - n_sink - w kept rows are the highest scores of [n_sink, n-w), equal
+ * scores ordered by lower position.
+ * scores          [h_kv, n] float32: written, or read with SD_SCORES_IN (then
+ *                 q_window may be NULL; scores are compared as float32,
+ *                 NaN not allowed).
+ * idx             [h_kv, k_eff] int32 out, ascending, k_eff = min(k_keep, n);
+ *                 k_keep >= n keeps every row (keep ratio 1 disables the branch).
+ * k_sel, v_sel    [h_kv, cap_sel, d_h] kv_dtype out: rows 0..k_eff-1 = the kept
+ *                 rows in idx order; cap_sel >= k_eff, and later steps append
+ *                 at row k_eff onwards.
+ * Errors: EINVAL unless 1 <= w <= n, 0 <= n_sink, n_sink + w <= k_keep
+ *         (when k_keep < n), n <= cap_full; ENOSPC if cap_sel < k_eff.
+ */
+sd_status sd_select_kv(const sd_dims* dims, const void* k_full, const void* v_full,
+                       int32_t cap_full, int32_t n, const float* q_window, int32_t w,
+                       int32_t n_sink, int32_t k_keep, float* scores, int32_t* idx,
+                       void* k_sel, void* v_sel, int32_t cap_sel, uint32_t flags,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sd_decode_attn -- split-K (flash-decoding style) GQA decode attention over
+ * rows 0..n_ctx-1 of one cache, full or gathered ([Cross] §1, §4.1, §4.4:
+ * one kernel serves dense and sparse modes).
+ *
+ * q      [h_q, d_h] float32 (already rotated).
+ * k, v   [h_kv, cap, d_h] kv_dtype; n_ctx >= 1 rows read.
+ * out    [h_q, d_h] float32: softmax(scale * q.K^T) V per query head.
+ * lse    [h_q] float32 log-sum-exp of the scaled logits, or NULL.
+ * n_splits  chunks of the row range, 0 = chosen by the library; the result
+ *           depends on it only through float32 rounding.
+ * Errors: EINVAL unless 1 <= n_ctx <= cap; ENOSPC for a short workspace.
+ */
+sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, const void* v,
+                         int32_t cap, int32_t n_ctx, float scale, int32_t n_splits,
+                         float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sd_sparse_mlp -- CATS sparse SwiGLU MLP ([SATS], CATS runtime masking).
+ *
+ * x        [d] float32 input; if norm_w is not NULL it is first normalised,
+ *          x_hat = x / sqrt(mean(x^2) + rms_eps) * norm_w, else x_hat = x.
+ * w_gate, w_up [d_ff, d]; w_down_t [d_ff, d] (down projection transposed).
+ * act      [d_ff] float32: a = SiLU(w_gate x_hat), written; with SD_GATE_IN it is
+ *          read instead and the gate projection is skipped.
+ * Channel i is kept iff threshold < 0 or |a_i| > threshold (strict).
+ * y        [d] float32 out: sum over kept i of a_i (w_up[i] . x_hat) w_down_t[i].
+ * idx      [d_ff] int32 out: the kept channels ascending in idx[0..n_kept-1].
+ * n_kept   [1] int32 out (device).
+ * Errors: EINVAL for bad pointers; EUNSUPPORTED for widths (see above).
+ */
+sd_status sd_sparse_mlp(const sd_dims* dims, const float* x, const float* norm_w,
+                        const void* w_gate, const void* w_up, const void* w_down_t,
+                        float threshold, float* y, float* act, int32_t* idx,
+                        int32_t* n_kept, uint32_t flags, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* One decoder layer's state for sd_decode_step. */
+typedef struct {
+  const float* attn_norm;  /* [d] */
+  const void* w_qkv;       /* [(h_q + 2 h_kv) d_h, d]: q rows, then k rows, then v rows */
+  const void* w_o;         /* [d, h_q d_h] */
+  const float* mlp_norm;   /* [d] */
+  const void* w_gate;      /* [d_ff, d] */
+  const void* w_up;        /* [d_ff, d] */
+  const void* w_down_t;    /* [d_ff, d] */
+  float cats_threshold;    /* per-layer t; < 0 means dense even in sparse mode */
+  int32_t pad0;
+  void* k_full;            /* [h_kv, cap_full, d_h] */
+  void* v_full;
+  int32_t cap_full;
+  int32_t n_full;          /* valid rows before the step; advanced by one [host] */
+  void* k_sel;             /* gathered buffer [h_kv, cap_sel, d_h], or NULL */
+  void* v_sel;
+  int32_t cap_sel;
+  int32_t n_sel;           /* valid gathered rows; advanced by one when k_sel != NULL */
+  uint8_t* mask_out;       /* optional [d_ff]: receives 1 for kept channels, else 0 */
+} sd_layer;
+
+/*
+ * sd_decode_step -- one decode step through n_layers pre-norm Llama layers:
+ *   x = RMSNorm(h) attn_norm; [q;k;v] = w_qkv x; RoPE(q, k) at position pos
+ *   (rotate-half pairs (i, i + d_h/2)); k, v rounded to kv_dtype (nearest, ties
+ *   to even) are appended at row n_full of the full cache and, if the layer has
+ *   a gathered buffer, at row n_sel of it, in every mode ([Cross] §3.2: nothing
+ *   is discarded and modes may switch per step); attention over rows
+ *   0..n_full (dense) or 0..n_sel of the gathered buffer (SD_KV_SPARSE), scale
+ *   1/sqrt(d_h); h += w_o attn; x = RMSNorm(h) mlp_norm; h += CATS-MLP(x) with
+ *   the layer threshold under SD_MLP_SPARSE, dense otherwise.
+ * hidden  [d] float32, updated in place.
+ * layers  [host] array; n_full and n_sel are advanced on success.
+ * Errors: EINVAL for a missing gathered buffer under SD_KV_SPARSE or bad
+ *         pointers; ENOSPC when a cache is full (n_full == cap_full, or
+ *         n_sel == cap_sel) or the workspace is short.
+ */
+sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers, int32_t pos,
+                         float* hidden, uint32_t mode, void* ws, size_t ws_bytes, void* stream);
+
+/* Byte account record ([Cross] §3). Bytes as doubles (exact below 2^53). */
+typedef struct {
+  double b_attn;      /* bytes of W_q, W_k, W_v, W_o per layer */
+  double b_mlp;       /* bytes of W_gate, W_up, W_down per layer */
+  double b_kv;        /* bytes of the keys and values of n tokens per layer */
+  double b_total;     /* L (b_attn + b_mlp + b_kv) + fixed_bytes */
+  double delta_p;     /* bytes the projection branch skips per step */
+  double delta_kv;    /* bytes the KV branch skips per step */
+  double bound_p;     /* b_total / (b_total - delta_p) */
+  double bound_kv;
+  double bound_both;
+  double n_star;      /* crossover context in tokens (inf when r_kv == 1) */
+} sd_byte_record;
+
+/*
+ * sd_byte_account -- [Cross] §3.2-§3.3 from model dimensions: projection set
+ * SD_PROJ_ALL7 (all seven projections), SD_PROJ_FFN (gate, up, down) or
+ * SD_PROJ_CATS (up and down; the CATS gate is always read).  s_w, s_kv are
+ * bytes per weight and cache element; r_p, r_kv keep ratios in [0, 1].
+ * out [host].  Errors: EINVAL for out-of-range arguments.
+ */
+sd_status sd_byte_account(const sd_dims* dims, int32_t n_layers, double n, double r_p,
+                          double r_kv, double s_w, double s_kv, int32_t proj_set,
+                          double fixed_bytes, sd_byte_record* out);
+
+/*
+ * sd_cats_calibrate -- per-layer CATS threshold from calibration states, the
+ * percentile rule CATS uses ([SATS]): a = SiLU(w_gate RMSNorm(x) norm_w) for
+ * each of the n_states rows of `states` [n_states, d]; with v the float32 |a|
+ * values sorted ascending (N = n_states * d_ff of them) and
+ * k = round(sparsity N), threshold = v[k-1] (or -1 when k == 0).
+ * threshold [1] float32 out (device).  Errors: EINVAL for sparsity outside
+ * [0, 1] or n_states < 1; ENOSPC for a short workspace
+ * (needs sd_calibrate_workspace_bytes).
+ */
+size_t sd_calibrate_workspace_bytes(const sd_dims* dims, int32_t n_states);
+sd_status sd_cats_calibrate(const sd_dims* dims, const float* states, int32_t n_states,
+                            const float* norm_w, const void* w_gate, float sparsity,
+                            float* threshold, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Opt-in per-kernel timing.  Between sd_profile_start() and sd_profile_stop(),
+ * every kernel the library launches is bracketed by two HIP events on its
+ * stream.  sd_profile_stop() waits for the recorded work, writes up to
+ * max_stats entries (one per kernel kind that ran: launch count and summed
+ * event-to-event milliseconds) to out [host], and returns the number of kinds
+ * (-1 if an event query failed).  The state is process-wide; profiling adds
+ * two event records per launch, so time the step itself with it off.
+ */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  int32_t pad0;
+  double total_ms;
+} sd_kernel_stat;
+
+sd_status sd_profile_start(void);
+int32_t sd_profile_stop(sd_kernel_stat* out, int32_t max_stats);
+
+const char* sd_status_string(sd_status status);
+const char* sd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_H */

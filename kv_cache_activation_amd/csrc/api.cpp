@@ -1,0 +1,428 @@
+// C ABI of the sparse decode-step library: argument checks, workspace layout
+// and the order of kernel launches.  Every check runs before anything is
+// enqueued, so a failing call leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/sd.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sd_status fail(sd_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxSplitBlocks = 1024;  // split-K workgroups per call, upper bound
+constexpr int kMinChunk = 128;         // rows per split, lower bound (auto mode)
+constexpr int kSelChunk = 256;         // key rows per selection workgroup
+constexpr int kDownRange = 256;        // channels per down-projection range
+constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in VGPRs
+
+size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
+
+struct Layout {
+  size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, counters, lse_part, lse;
+  size_t kth_hist, kth_state, total;
+  int max_splits, n_tiles, tile_cols, n_ranges, range_len, sel_chunks;
+};
+
+Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t hq = dm.n_q_heads, dh = dm.head_dim, hkv = dm.n_kv_heads, d = dm.d_model,
+               ff = dm.d_ff;
+  const size_t G = hq / hkv;
+  L.max_splits = kMaxSplitBlocks / (int)hkv > 0 ? kMaxSplitBlocks / (int)hkv : 1;
+  L.q = take(hq * dh * 4);
+  L.attn = take(hq * dh * 4);
+  L.pm = take(hq * L.max_splits * 4);
+  L.pl = take(hq * L.max_splits * 4);
+  L.pacc = take(hq * L.max_splits * dh * 4);
+  L.act = take(ff * 4);
+  L.hmid = take(ff * 4);
+  L.keep = take(ff);
+  L.tile_cols = d >= 512 ? 512 : (d >= 256 ? 256 : 128);
+  L.n_tiles = (int)((d + L.tile_cols - 1) / L.tile_cols);
+  L.range_len = kDownRange;
+  L.n_ranges = (int)((ff + kDownRange - 1) / kDownRange);
+  L.down_part = take((size_t)L.n_ranges * d * 4);
+  L.counters = take((size_t)L.n_tiles * 4);
+  L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
+  L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
+  L.lse = take(hq * (size_t)max_window * 4);
+  L.kth_hist = take(256 * 4);
+  L.kth_state = take(16);
+  L.total = off;
+  return L;
+}
+
+sd_status check_dims(const sd_dims* dm) {
+  if (!dm) return fail(SD_EINVAL, "dims is NULL");
+  if (dm->d_model < 8 || dm->n_q_heads < 1 || dm->n_kv_heads < 1 || dm->d_ff < 1)
+    return fail(SD_EINVAL, "dims must be positive");
+  if (dm->n_q_heads % dm->n_kv_heads)
+    return fail(SD_EINVAL, "n_q_heads %d is not a multiple of n_kv_heads %d", dm->n_q_heads,
+                dm->n_kv_heads);
+  const int G = dm->n_q_heads / dm->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SD_EUNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+  if (dm->head_dim != 64 && dm->head_dim != 128)
+    return fail(SD_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", dm->head_dim);
+  if (dm->d_model % 8 || dm->d_model > kMaxWidth)
+    return fail(SD_EUNSUPPORTED, "d_model must be a multiple of 8 and at most %d", kMaxWidth);
+  if (dm->n_q_heads * dm->head_dim > kMaxWidth)
+    return fail(SD_EUNSUPPORTED, "n_q_heads * head_dim must be at most %d", kMaxWidth);
+  if ((dm->w_dtype != SD_F32 && dm->w_dtype != SD_BF16) ||
+      (dm->kv_dtype != SD_F32 && dm->kv_dtype != SD_BF16))
+    return fail(SD_EUNSUPPORTED, "dtype must be SD_F32 or SD_BF16");
+  if (!(dm->rms_eps >= 0.f)) return fail(SD_EINVAL, "rms_eps must be >= 0");
+  return SD_OK;
+}
+
+sd_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SD_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return SD_OK;
+}
+
+int cu_count() {
+  int dev = 0, cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+  return cu > 0 ? cu : 256;
+}
+
+int auto_splits(int n_ctx, int max_splits) {
+  int s = (n_ctx + kMinChunk - 1) / kMinChunk;
+  if (s > max_splits) s = max_splits;
+  return s < 1 ? 1 : s;
+}
+
+// Enqueue split-K attention; ws must hold the layout's attention buffers.
+void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, const void* k,
+                  const void* v, int cap, int n_ctx, float scale, int n_splits, float* out,
+                  float* lse, hipStream_t s) {
+  sd::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cap = cap;
+  a.n_ctx = n_ctx;
+  a.h_q = dm.n_q_heads;
+  a.h_kv = dm.n_kv_heads;
+  a.dh = dm.head_dim;
+  a.scale = scale;
+  a.chunk = (n_ctx + n_splits - 1) / n_splits;
+  a.n_splits = (n_ctx + a.chunk - 1) / a.chunk;
+  a.pm = reinterpret_cast<float*>(ws + L.pm);
+  a.pl = reinterpret_cast<float*>(ws + L.pl);
+  a.pacc = reinterpret_cast<float*>(ws + L.pacc);
+  a.out = out;
+  a.lse = lse;
+  sd::launch_attn(a, dm.kv_dtype, s);
+}
+
+void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, const float* norm,
+                 const void* wg, const void* wu, const void* wd, float t, int gate_in, float* act,
+                 uint8_t* keep, float* y, int accumulate, int32_t* idx, int32_t* n_kept,
+                 hipStream_t s) {
+  sd::GateUpArgs g{};
+  g.x = x;
+  g.norm = norm;
+  g.eps = dm.rms_eps;
+  g.w_gate = wg;
+  g.w_up = wu;
+  g.d = dm.d_model;
+  g.dff = dm.d_ff;
+  g.t = t;
+  g.gate_in = gate_in;
+  g.store_abs = 0;
+  g.act = act;
+  g.keep = keep;
+  g.hmid = reinterpret_cast<float*>(ws + L.hmid);
+  g.zero_buf = reinterpret_cast<unsigned*>(ws + L.counters);
+  g.zero_n = L.n_tiles;
+  const int pairs = (dm.d_ff + 1) / 2;
+  g.grid = (pairs + 7) / 8;
+  g.n_states = 1;
+  sd::launch_gate_up(g, dm.w_dtype, s);
+
+  sd::DownArgs dn{};
+  dn.w_down_t = wd;
+  dn.d = dm.d_model;
+  dn.dff = dm.d_ff;
+  dn.keep = keep;
+  dn.hmid = g.hmid;
+  dn.range_len = L.range_len;
+  dn.n_ranges = L.n_ranges;
+  dn.n_tiles = L.n_tiles;
+  dn.tile_cols = L.tile_cols;
+  dn.partials = reinterpret_cast<float*>(ws + L.down_part);
+  dn.counters = g.zero_buf;
+  dn.y = y;
+  dn.accumulate = accumulate;
+  dn.idx_out = idx;
+  dn.n_kept_out = n_kept;
+  sd::launch_down(dn, dm.w_dtype, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sd_status_string(sd_status st) {
+  switch (st) {
+    case SD_OK: return "ok";
+    case SD_EINVAL: return "invalid argument";
+    case SD_ENOSPC: return "insufficient workspace or capacity";
+    case SD_EUNSUPPORTED: return "unsupported shape or dtype";
+    case SD_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* sd_last_error(void) { return g_err; }
+
+size_t sd_workspace_bytes(const sd_dims* dims, int32_t max_rows, int32_t max_window) {
+  if (check_dims(dims) != SD_OK || max_rows < 0 || max_window < 0) return 0;
+  return make_layout(*dims, max_rows, max_window).total;
+}
+
+sd_status sd_select_kv(const sd_dims* dims, const void* k_full, const void* v_full,
+                       int32_t cap_full, int32_t n, const float* q_window, int32_t w,
+                       int32_t n_sink, int32_t k_keep, float* scores, int32_t* idx, void* k_sel,
+                       void* v_sel, int32_t cap_sel, uint32_t flags, void* ws, size_t ws_bytes,
+                       void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  const bool scores_in = flags & SD_SCORES_IN;
+  if (!aligned(k_full) || !aligned(v_full) || !aligned(scores) || !aligned(idx) ||
+      !aligned(k_sel) || !aligned(v_sel) || (!scores_in && !aligned(q_window)) || !aligned(ws))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (n < 1 || n > cap_full) return fail(SD_EINVAL, "need 1 <= n <= cap_full");
+  if (w < 1 || w > n) return fail(SD_EINVAL, "need 1 <= w <= n");
+  if (n_sink < 0) return fail(SD_EINVAL, "n_sink must be >= 0");
+  if (k_keep < n && k_keep < n_sink + w)
+    return fail(SD_EINVAL, "k_keep %d < n_sink + w = %d", k_keep, n_sink + w);
+  const int k_eff = k_keep < n ? k_keep : n;
+  if (cap_sel < k_eff) return fail(SD_ENOSPC, "cap_sel %d < kept rows %d", cap_sel, k_eff);
+  const Layout L = make_layout(*dims, n, w);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* wsb = static_cast<char*>(ws);
+  sd::SelectArgs a{};
+  a.k = k_full;
+  a.v = v_full;
+  a.cap_full = cap_full;
+  a.n = n;
+  a.q_win = q_window;
+  a.w = w;
+  a.n_sink = n_sink;
+  a.k_keep = k_keep;
+  a.h_q = dims->n_q_heads;
+  a.h_kv = dims->n_kv_heads;
+  a.dh = dims->head_dim;
+  a.scores = scores;
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.v_sel = v_sel;
+  a.cap_sel = cap_sel;
+  a.n_chunks = L.sel_chunks;
+  a.lse_part = reinterpret_cast<float*>(wsb + L.lse_part);
+  a.lse = reinterpret_cast<float*>(wsb + L.lse);
+  a.skip_scoring = scores_in;
+  sd::launch_select(a, dims->kv_dtype, static_cast<hipStream_t>(stream));
+  return check_launch("sd_select_kv");
+}
+
+sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, const void* v,
+                         int32_t cap, int32_t n_ctx, float scale, int32_t n_splits, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(out) || !aligned(ws) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (n_ctx < 1 || n_ctx > cap) return fail(SD_EINVAL, "need 1 <= n_ctx <= cap");
+  if (!std::isfinite(scale)) return fail(SD_EINVAL, "scale must be finite");
+  const Layout L = make_layout(*dims, 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (n_splits < 0) return fail(SD_EINVAL, "n_splits must be >= 0");
+  if (n_splits > L.max_splits)
+    return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
+  int s = n_splits ? (n_splits < n_ctx ? n_splits : n_ctx) : auto_splits(n_ctx, L.max_splits);
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, scale, s, out, lse,
+               static_cast<hipStream_t>(stream));
+  return check_launch("sd_decode_attn");
+}
+
+sd_status sd_sparse_mlp(const sd_dims* dims, const float* x, const float* norm_w,
+                        const void* w_gate, const void* w_up, const void* w_down_t,
+                        float threshold, float* y, float* act, int32_t* idx, int32_t* n_kept,
+                        uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  const bool gate_in = flags & SD_GATE_IN;
+  if (!aligned(x) || (norm_w && !aligned(norm_w)) || (!gate_in && !aligned(w_gate)) ||
+      !aligned(w_up) || !aligned(w_down_t) || !aligned(y) || !aligned(act) || !aligned(idx) ||
+      !n_kept || !aligned(ws))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (std::isnan(threshold)) return fail(SD_EINVAL, "threshold is NaN");
+  const Layout L = make_layout(*dims, 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* wsb = static_cast<char*>(ws);
+  enqueue_mlp(*dims, L, wsb, x, norm_w, w_gate, w_up, w_down_t, threshold, gate_in, act,
+              reinterpret_cast<uint8_t*>(wsb + L.keep), y, 0, idx, n_kept,
+              static_cast<hipStream_t>(stream));
+  return check_launch("sd_sparse_mlp");
+}
+
+sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers, int32_t pos,
+                         float* hidden, uint32_t mode, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (n_layers < 1 || !layers) return fail(SD_EINVAL, "need n_layers >= 1 and a layer array");
+  if (!aligned(hidden) || !aligned(ws)) return fail(SD_EINVAL, "null or misaligned pointer");
+  if (pos < 0) return fail(SD_EINVAL, "pos must be >= 0");
+  const bool kv_sparse = mode & SD_KV_SPARSE, mlp_sparse = mode & SD_MLP_SPARSE;
+  const Layout L = make_layout(*dims, 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  for (int i = 0; i < n_layers; ++i) {
+    const sd_layer& l = layers[i];
+    if (!aligned(l.attn_norm) || !aligned(l.w_qkv) || !aligned(l.w_o) || !aligned(l.mlp_norm) ||
+        !aligned(l.w_gate) || !aligned(l.w_up) || !aligned(l.w_down_t) || !aligned(l.k_full) ||
+        !aligned(l.v_full))
+      return fail(SD_EINVAL, "layer %d: null or misaligned pointer", i);
+    if (l.n_full < 0 || l.n_full >= l.cap_full)
+      return fail(SD_ENOSPC, "layer %d: full cache has no free row (n_full %d, cap %d)", i,
+                  l.n_full, l.cap_full);
+    if (l.k_sel || l.v_sel) {
+      if (!aligned(l.k_sel) || !aligned(l.v_sel))
+        return fail(SD_EINVAL, "layer %d: misaligned gathered buffer", i);
+      if (l.n_sel < 0 || l.n_sel >= l.cap_sel)
+        return fail(SD_ENOSPC, "layer %d: gathered buffer has no free row (n_sel %d, cap %d)",
+                    i, l.n_sel, l.cap_sel);
+    } else if (kv_sparse) {
+      return fail(SD_EINVAL, "layer %d: KV-sparse mode needs a gathered buffer", i);
+    }
+    if (std::isnan(l.cats_threshold)) return fail(SD_EINVAL, "layer %d: threshold is NaN", i);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  float* q = reinterpret_cast<float*>(wsb + L.q);
+  float* attn = reinterpret_cast<float*>(wsb + L.attn);
+  const int d = dims->d_model, hq = dims->n_q_heads, dh = dims->head_dim, hkv = dims->n_kv_heads;
+  const float scale = 1.0f / std::sqrt((float)dh);
+  for (int i = 0; i < n_layers; ++i) {
+    const sd_layer& l = layers[i];
+    const bool has_sel = l.k_sel != nullptr;
+    sd::QkvArgs qa{};
+    qa.h = hidden;
+    qa.norm = l.attn_norm;
+    qa.eps = dims->rms_eps;
+    qa.w = l.w_qkv;
+    qa.d = d;
+    qa.h_q = hq;
+    qa.h_kv = hkv;
+    qa.dh = dh;
+    qa.theta = dims->rope_theta;
+    qa.pos = pos;
+    qa.q_out = q;
+    qa.k_full = l.k_full;
+    qa.v_full = l.v_full;
+    qa.cap_full = l.cap_full;
+    qa.row_full = l.n_full;
+    qa.k_sel = has_sel ? l.k_sel : nullptr;
+    qa.v_sel = has_sel ? l.v_sel : nullptr;
+    qa.cap_sel = l.cap_sel;
+    qa.row_sel = l.n_sel;
+    qa.zero_buf = nullptr;
+    qa.zero_n = 0;
+    qa.grid = ((hq + 2 * hkv) * dh / 2 + 3) / 4;
+    sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
+
+    const void* kc = kv_sparse ? l.k_sel : l.k_full;
+    const void* vc = kv_sparse ? l.v_sel : l.v_full;
+    const int cap = kv_sparse ? l.cap_sel : l.cap_full;
+    const int n_ctx = (kv_sparse ? l.n_sel : l.n_full) + 1;
+    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, scale, auto_splits(n_ctx, L.max_splits),
+                 attn, nullptr, s);
+
+    sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, (d / 2 + 3) / 4, s);
+
+    uint8_t* keep = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + L.keep);
+    enqueue_mlp(*dims, L, wsb, hidden, l.mlp_norm, l.w_gate, l.w_up, l.w_down_t,
+                mlp_sparse ? l.cats_threshold : -1.0f, 0, reinterpret_cast<float*>(wsb + L.act),
+                keep, hidden, 1, nullptr, nullptr, s);
+  }
+  st = check_launch("sd_decode_step");
+  if (st) return st;
+  for (int i = 0; i < n_layers; ++i) {
+    layers[i].n_full += 1;
+    if (layers[i].k_sel) layers[i].n_sel += 1;
+  }
+  return SD_OK;
+}
+
+size_t sd_calibrate_workspace_bytes(const sd_dims* dims, int32_t n_states) {
+  if (check_dims(dims) != SD_OK || n_states < 1) return 0;
+  const Layout L = make_layout(*dims, 0, 0);
+  return L.total + (((size_t)n_states * dims->d_ff * 4 + 255) & ~size_t(255));
+}
+
+sd_status sd_cats_calibrate(const sd_dims* dims, const float* states, int32_t n_states,
+                            const float* norm_w, const void* w_gate, float sparsity,
+                            float* threshold, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (!aligned(states) || !aligned(w_gate) || !threshold || !aligned(ws) ||
+      (norm_w && !aligned(norm_w)))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (n_states < 1) return fail(SD_EINVAL, "n_states must be >= 1");
+  if (!(sparsity >= 0.f && sparsity <= 1.f)) return fail(SD_EINVAL, "sparsity outside [0, 1]");
+  const size_t need = sd_calibrate_workspace_bytes(dims, n_states);
+  if (ws_bytes < need) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, need);
+  const Layout L = make_layout(*dims, 0, 0);
+  char* wsb = static_cast<char*>(ws);
+  float* vals = reinterpret_cast<float*>(wsb + L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sd::GateUpArgs g{};
+  g.x = states;
+  g.norm = norm_w;
+  g.eps = dims->rms_eps;
+  g.w_gate = w_gate;
+  g.w_up = nullptr;
+  g.d = dims->d_model;
+  g.dff = dims->d_ff;
+  g.t = -1.f;
+  g.store_abs = 1;
+  g.act = vals;
+  const int pairs = (dims->d_ff + 1) / 2;
+  g.grid = (pairs + 7) / 8;
+  g.n_states = n_states;
+  sd::launch_gate_up(g, dims->w_dtype, s);
+  const size_t N = (size_t)n_states * dims->d_ff;
+  const size_t k = (size_t)std::floor((double)sparsity * (double)N + 0.5);
+  sd::launch_kth_smallest(vals, N, k, reinterpret_cast<unsigned*>(wsb + L.kth_hist),
+                          reinterpret_cast<unsigned*>(wsb + L.kth_state), threshold, s);
+  return check_launch("sd_cats_calibrate");
+}
+
+}  // extern "C"

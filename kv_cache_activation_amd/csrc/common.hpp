@@ -1,0 +1,135 @@
+// Device helpers shared by the gfx950 kernels of the sparse decode step.
+//
+// Everything here is wave64 CDNA code: lane groups of 16 (a DPP "row") are the
+// unit of the small dot-product reductions, 16-byte global loads are the unit
+// of HBM traffic, and bf16 is widened to float32 by a shift (its bits are the
+// upper half of a float32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- widening
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Eight consecutive elements of a row as float32, from one 16-byte load
+// (bf16) or two (float32).  p must be 16-byte aligned.
+template <typename T> struct Vec8;
+
+template <> struct Vec8<bf16_t> {
+  u32x4 raw;
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ void load_cached(const bf16_t* p) {
+    raw = *reinterpret_cast<const u32x4*>(p);
+  }
+  __device__ __forceinline__ void to_float(float (&f)[8]) const {
+    f[0] = bf16_lo(raw.x); f[1] = bf16_hi(raw.x);
+    f[2] = bf16_lo(raw.y); f[3] = bf16_hi(raw.y);
+    f[4] = bf16_lo(raw.z); f[5] = bf16_hi(raw.z);
+    f[6] = bf16_lo(raw.w); f[7] = bf16_hi(raw.w);
+  }
+};
+
+template <> struct Vec8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+  }
+  __device__ __forceinline__ void load_cached(const float* p) {
+    a = reinterpret_cast<const f32x4*>(p)[0];
+    b = reinterpret_cast<const f32x4*>(p)[1];
+  }
+  __device__ __forceinline__ void to_float(float (&f)[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ void store8(float* p, const float (&f)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+__device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Store one element of a cache row, rounded to the cache type.
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// ---------------------------------------------------------------- reductions
+// DPP controls (GCN/CDNA encoding).
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LANES lanes (4, 8 or 16); every lane gets the sum.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group of 4, 8 or 16 lanes");
+  x += dpp<kDppQuadSwap1>(x);
+  x += dpp<kDppQuadSwap2>(x);
+  if (LANES >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if (LANES >= 16) x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+template <int LANES>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group of 4, 8 or 16 lanes");
+  x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp<kDppQuadSwap2>(x));
+  if (LANES >= 8) x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  if (LANES >= 16) x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
+// Full-wave sum and max (every lane gets the result).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = group_max<16>(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace sd

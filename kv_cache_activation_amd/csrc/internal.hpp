@@ -1,0 +1,122 @@
+// Host-side launchers shared between the kernels and the C ABI layer.
+// All launchers enqueue on `s` and return without synchronizing; the caller
+// checks hipGetLastError() afterwards.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sd {
+
+// Kernel kinds for the opt-in profiler (order = names in profile.cpp).
+enum KernelKind {
+  K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_SEL_LSE, K_SEL_LSE_FINAL,
+  K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_COUNT
+};
+
+// Brackets one kernel launch with HIP events while profiling is on.
+struct ProfScope {
+  int kind;
+  hipStream_t s;
+  bool active;
+  ProfScope(int k, hipStream_t st);
+  ~ProfScope();
+};
+
+struct QkvArgs {
+  const float* h;
+  const float* norm;
+  float eps;
+  const void* w;
+  int d, h_q, h_kv, dh;
+  float theta;
+  int pos;
+  float* q_out;
+  void* k_full;
+  void* v_full;
+  int cap_full, row_full;
+  void* k_sel;
+  void* v_sel;
+  int cap_sel, row_sel;
+  unsigned* zero_buf;
+  int zero_n;
+  int grid;
+};
+
+struct GateUpArgs {
+  const float* x;
+  const float* norm;  // nullptr: x is used as is
+  float eps;
+  const void* w_gate;
+  const void* w_up;   // nullptr: gate only (calibration)
+  int d, dff;
+  float t;
+  int gate_in, store_abs;
+  float* act;
+  uint8_t* keep;
+  float* hmid;
+  unsigned* zero_buf;
+  int zero_n;
+  int grid;
+  int n_states;       // batched gate for calibration; 1 otherwise
+};
+
+struct DownArgs {
+  const void* w_down_t;
+  int d, dff;
+  const uint8_t* keep;
+  const float* hmid;
+  int range_len, n_ranges, n_tiles, tile_cols;
+  float* partials;     // [n_ranges, d]
+  unsigned* counters;  // [n_tiles], zero on entry
+  float* y;
+  int accumulate;      // y += result instead of y = result
+  int32_t* idx_out;    // optional ascending kept list
+  int32_t* n_kept_out; // optional
+};
+
+struct AttnArgs {
+  const float* q;
+  const void* k;
+  const void* v;
+  int cap, n_ctx, h_q, h_kv, dh;
+  float scale;
+  int n_splits, chunk;
+  float* pm;
+  float* pl;
+  float* pacc;
+  float* out;
+  float* lse;
+};
+
+struct SelectArgs {
+  const void* k;
+  const void* v;
+  int cap_full, n;
+  const float* q_win;
+  int w, n_sink, k_keep, h_q, h_kv, dh;
+  float* scores;
+  int32_t* idx;
+  void* k_sel;
+  void* v_sel;
+  int cap_sel;
+  int chunk, n_chunks;
+  float* lse_part;   // [h_kv, n_chunks, G*w, 2]
+  float* lse;        // [h_q, w] (log2 domain)
+  int skip_scoring;
+};
+
+void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s);
+void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,
+              int grid, hipStream_t s);
+void launch_gate_up(const GateUpArgs& a, int w_dtype, hipStream_t s);
+void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
+void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s);
+void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s);
+// k-th smallest (1-based k) of n non-negative float32 values; writes the value
+// to *out (or -1 when k == 0).  hist: 256 uint32 scratch words; state: 4 words.
+void launch_kth_smallest(const float* vals, size_t n, size_t k, unsigned* hist, unsigned* state,
+                         float* out, hipStream_t s);
+
+}  // namespace sd

@@ -1,0 +1,411 @@
+// One-time attention-scored KV selection (gfx950, wave64).
+//
+// "Where Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding"
+// §4.1: after prefill the cache is scored once with the attention of an
+// observation window of queries; sinks, the window and the best-scoring rows
+// of each KV head are kept and gathered into a contiguous buffer.
+//
+// Kernels, in launch order:
+//   lse_partial  grid (key chunks, KV heads); one key row per thread held in
+//                VGPRs, window queries staged in LDS in batches of 32.  For each
+//                query: the causal logits of the chunk's keys, a wave max/sum
+//                and a four-wave merge -> partial (max, sum) per (chunk, query).
+//   lse_final    one thread per window query: merge the chunk partials into
+//                the query's log-sum-exp (log2 domain).
+//   score        same layout as lse_partial; each thread sums, over the G*w
+//                queries of its KV head in a fixed order, the softmax weight
+//                that the query puts on its key -> scores[kv, j].
+//   topk         one 1024-thread workgroup per KV head: an 8-bit-digit radix
+//                select on order-preserving keys of the float32 scores finds
+//                the m-th largest candidate value T; a block-wide ballot scan
+//                then emits, in ascending position, the sinks, the window, all
+//                candidates above T and the lowest-position candidates equal to
+//                T up to m (ties to the lower position).
+//   gather       16-byte copies of the kept K and V rows into the buffer.
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sd {
+
+constexpr int kSelThreads = 256;  // == key chunk length
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kQBatch = 32;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+
+template <typename KT, int DH>
+__device__ __forceinline__ void load_row_f32(const KT* p, float (&r)[DH]) {
+#pragma unroll
+  for (int c = 0; c < DH; c += 8) {
+    Vec8<KT> v;
+    v.load_cached(p + c);
+    float f[8];
+    v.to_float(f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[c + e] = f[e];
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ float dot_lds(const float (&r)[DH], const float* qs) {
+  float a = 0.f;
+#pragma unroll
+  for (int c = 0; c < DH; c += 4) {
+    const float4 qq = *reinterpret_cast<const float4*>(qs + c);
+    a = fmaf(r[c], qq.x, a);
+    a = fmaf(r[c + 1], qq.y, a);
+    a = fmaf(r[c + 2], qq.z, a);
+    a = fmaf(r[c + 3], qq.w, a);
+  }
+  return a;
+}
+
+// Stage window queries qb..qb+kQBatch-1 of KV head kv into LDS.  Query index
+// qi = g * w + i is head kv*G + g at window slot i.
+template <int DH>
+__device__ void stage_queries(const float* __restrict__ q_win, int kv, int G, int w, int qb,
+                              int Q, float (*qs)[DH]) {
+  for (int t = threadIdx.x; t < kQBatch * DH; t += blockDim.x) {
+    const int qq = t / DH, c = t - qq * DH;
+    const int qi = qb + qq;
+    float v = 0.f;
+    if (qi < Q) {
+      const int g = qi / w, i = qi - g * w;
+      v = q_win[((size_t)(kv * G + g) * w + i) * DH + c];
+    }
+    qs[qq][c] = v;
+  }
+}
+
+template <typename KT, int DH>
+__global__ __launch_bounds__(kSelThreads) void sel_lse_partial_kernel(
+    const KT* __restrict__ K, int cap, int n, const float* __restrict__ q_win, int w, int G,
+    float scale_log2, int n_chunks, float* __restrict__ lse_part) {
+  __shared__ float qs[kQBatch][DH];
+  __shared__ float red_m[kSelWaves][kQBatch], red_l[kSelWaves][kQBatch];
+  const int chunk = blockIdx.x, kv = blockIdx.y;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int j = chunk * kSelThreads + threadIdx.x;
+  const bool have = j < n;
+  float kr[DH];
+  if (have) {
+    load_row_f32<KT, DH>(K + ((size_t)kv * cap + j) * DH, kr);
+  } else {
+#pragma unroll
+    for (int c = 0; c < DH; ++c) kr[c] = 0.f;
+  }
+  const int Q = G * w;
+  for (int qb = 0; qb < Q; qb += kQBatch) {
+    __syncthreads();
+    stage_queries<DH>(q_win, kv, G, w, qb, Q, qs);
+    __syncthreads();
+    for (int qq = 0; qq < kQBatch && qb + qq < Q; ++qq) {
+      const int i = (qb + qq) % w;
+      const bool vis = have && j <= n - w + i;
+      const float z = vis ? dot_lds<DH>(kr, qs[qq]) * scale_log2 : -INFINITY;
+      const float mw = wave_max(z);
+      const float e = vis ? exp2f(z - mw) : 0.f;
+      const float lw = wave_sum(e);
+      if (lane == 0) {
+        red_m[wave][qq] = mw;
+        red_l[wave][qq] = lw;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kQBatch && qb + threadIdx.x < Q) {
+      const int qq = threadIdx.x;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v) M = fmaxf(M, red_m[v][qq]);
+      float L = 0.f;
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v)
+        if (red_m[v][qq] != -INFINITY) L = fmaf(red_l[v][qq], exp2f(red_m[v][qq] - M), L);
+      float* o = lse_part + (((size_t)kv * n_chunks + chunk) * Q + qb + qq) * 2;
+      o[0] = M;
+      o[1] = L;
+    }
+  }
+}
+
+__global__ void sel_lse_final_kernel(const float* __restrict__ lse_part, int n_chunks, int G,
+                                     int w, int h_kv, float* __restrict__ lse) {
+  const int Q = G * w;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= h_kv * Q) return;
+  const int kv = t / Q, qi = t - kv * Q;
+  const float* p = lse_part + ((size_t)kv * n_chunks * Q + qi) * 2;
+  float M = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[(size_t)c * Q * 2]);
+  float L = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    const float m = p[(size_t)c * Q * 2];
+    if (m != -INFINITY) L = fmaf(p[(size_t)c * Q * 2 + 1], exp2f(m - M), L);
+  }
+  const int g = qi / w, i = qi - g * w;
+  lse[(kv * G + g) * w + i] = M + log2f(L);
+}
+
+template <typename KT, int DH>
+__global__ __launch_bounds__(kSelThreads) void sel_score_kernel(
+    const KT* __restrict__ K, int cap, int n, const float* __restrict__ q_win, int w, int G,
+    float scale_log2, const float* __restrict__ lse, float* __restrict__ scores) {
+  __shared__ float qs[kQBatch][DH];
+  __shared__ float ls[kQBatch];
+  const int chunk = blockIdx.x, kv = blockIdx.y;
+  const int j = chunk * kSelThreads + threadIdx.x;
+  const bool have = j < n;
+  float kr[DH];
+  if (have) {
+    load_row_f32<KT, DH>(K + ((size_t)kv * cap + j) * DH, kr);
+  } else {
+#pragma unroll
+    for (int c = 0; c < DH; ++c) kr[c] = 0.f;
+  }
+  const int Q = G * w;
+  float s = 0.f;
+  for (int qb = 0; qb < Q; qb += kQBatch) {
+    __syncthreads();
+    stage_queries<DH>(q_win, kv, G, w, qb, Q, qs);
+    if (threadIdx.x < kQBatch) {
+      const int qi = qb + threadIdx.x;
+      float v = 0.f;
+      if (qi < Q) {
+        const int g = qi / w, i = qi - g * w;
+        v = lse[(kv * G + g) * w + i];
+      }
+      ls[threadIdx.x] = v;
+    }
+    __syncthreads();
+    for (int qq = 0; qq < kQBatch && qb + qq < Q; ++qq) {
+      const int i = (qb + qq) % w;
+      if (have && j <= n - w + i) s += exp2f(dot_lds<DH>(kr, qs[qq]) * scale_log2 - ls[qq]);
+    }
+  }
+  if (have) scores[(size_t)kv * n + j] = s;
+}
+
+// Order-preserving map of float32 to uint32 (larger float -> larger key);
+// -0 and +0 map to one key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = f == 0.f ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive prefix count of `flag` (ascending thread order), plus
+// the block total; uses wave ballots and an LDS array of wave totals.
+__device__ __forceinline__ int block_prefix(bool flag, int* wave_tot, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const unsigned long long m = __ballot(flag);
+  if (lane == 0) wave_tot[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int v = 0; v < kTopkWaves; ++v) {
+    if (v < wave) before += wave_tot[v];
+    total += wave_tot[v];
+  }
+  __syncthreads();
+  return before + __popcll(m & ((1ull << lane) - 1ull));
+}
+
+__global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(const float* __restrict__ scores,
+                                                                 int n, int w, int n_sink,
+                                                                 int k_keep,
+                                                                 int32_t* __restrict__ idx) {
+  __shared__ unsigned hist[256];
+  __shared__ unsigned sh_prefix, sh_need;
+  __shared__ int wave_tot[kTopkWaves];
+  const int kv = blockIdx.x;
+  const float* S = scores + (size_t)kv * n;
+  if (k_keep >= n) {
+    int32_t* out = idx + (size_t)kv * n;
+    for (int j = threadIdx.x; j < n; j += kTopkThreads) out[j] = j;
+    return;
+  }
+  int32_t* out = idx + (size_t)kv * k_keep;
+  const int m = k_keep - n_sink - w;
+  const int c0 = n_sink, c1 = n - w;
+  unsigned T = 0, need = 0;
+  if (m > 0) {
+    unsigned prefix = 0;
+    need = (unsigned)m;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int b = threadIdx.x; b < 256; b += kTopkThreads) hist[b] = 0u;
+      __syncthreads();
+      for (int j = c0 + threadIdx.x; j < c1; j += kTopkThreads) {
+        const unsigned key = order_key(S[j]);
+        if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+          atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        unsigned above = 0;
+        int b = 255;
+        for (; b > 0; --b) {
+          if (above + hist[b] >= need) break;
+          above += hist[b];
+        }
+        sh_prefix = prefix | ((unsigned)b << shift);
+        sh_need = need - above;
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      need = sh_need;
+      __syncthreads();
+    }
+    T = prefix;
+  }
+  int base_take = 0, base_eq = 0;
+  for (int t0 = 0; t0 < n; t0 += kTopkThreads) {
+    const int j = t0 + threadIdx.x;
+    const bool valid = j < n;
+    const bool forced = valid && (j < c0 || j >= c1);
+    const bool cand = valid && !forced && m > 0;
+    const unsigned key = cand ? order_key(S[j]) : 0u;
+    const bool gt = cand && key > T;
+    const bool eq = cand && key == T;
+    int eq_total;
+    const int eq_rank = base_eq + block_prefix(eq, wave_tot, eq_total);
+    const bool take = forced || gt || (eq && eq_rank < (int)need);
+    int take_total;
+    const int pos = base_take + block_prefix(take, wave_tot, take_total);
+    if (take && pos < k_keep) out[pos] = j;  // pos < k_keep always; guard anyway
+    base_eq += eq_total;
+    base_take += take_total;
+  }
+}
+
+template <typename KT, int DH>
+__global__ void sel_gather_kernel(const KT* __restrict__ K, const KT* __restrict__ V,
+                                  int cap_full, const int32_t* __restrict__ idx, int k_eff,
+                                  KT* __restrict__ Ks, KT* __restrict__ Vs, int cap_sel) {
+  constexpr int P = DH * (int)sizeof(KT) / 16;  // 16-byte pieces per row
+  const int kv = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int r = t / P, piece = t - r * P;
+  if (r >= k_eff) return;
+  const int src = idx[(size_t)kv * k_eff + r];
+  if (src < 0 || src >= cap_full) return;  // indices come from data: never read outside
+  const uint4* ks = reinterpret_cast<const uint4*>(K + ((size_t)kv * cap_full + src) * DH) + piece;
+  const uint4* vs = reinterpret_cast<const uint4*>(V + ((size_t)kv * cap_full + src) * DH) + piece;
+  uint4* kd = reinterpret_cast<uint4*>(Ks + ((size_t)kv * cap_sel + r) * DH) + piece;
+  uint4* vd = reinterpret_cast<uint4*>(Vs + ((size_t)kv * cap_sel + r) * DH) + piece;
+  *kd = *ks;
+  *vd = *vs;
+}
+
+template <typename KT, int DH>
+static void select_typed(const SelectArgs& a, hipStream_t s) {
+  const int G = a.h_q / a.h_kv;
+  const float scale_log2 = (1.0f / sqrtf((float)DH)) * 1.44269504088896340736f;
+  const KT* k = (const KT*)a.k;
+  if (!a.skip_scoring) {
+    dim3 grid(a.n_chunks, a.h_kv);
+    {
+      ProfScope prof(K_SEL_LSE, s);
+      sel_lse_partial_kernel<KT, DH><<<grid, kSelThreads, 0, s>>>(
+          k, a.cap_full, a.n, a.q_win, a.w, G, scale_log2, a.n_chunks, a.lse_part);
+    }
+    const int nq = a.h_kv * G * a.w;
+    {
+      ProfScope prof(K_SEL_LSE_FINAL, s);
+      sel_lse_final_kernel<<<(nq + 255) / 256, 256, 0, s>>>(a.lse_part, a.n_chunks, G, a.w,
+                                                            a.h_kv, a.lse);
+    }
+    ProfScope prof(K_SEL_SCORE, s);
+    sel_score_kernel<KT, DH><<<grid, kSelThreads, 0, s>>>(k, a.cap_full, a.n, a.q_win, a.w, G,
+                                                           scale_log2, a.lse, a.scores);
+  }
+  {
+    ProfScope prof(K_SEL_TOPK, s);
+    sel_topk_kernel<<<a.h_kv, kTopkThreads, 0, s>>>(a.scores, a.n, a.w, a.n_sink, a.k_keep,
+                                                    a.idx);
+  }
+  const int k_eff = a.k_keep < a.n ? a.k_keep : a.n;
+  constexpr int P = DH * (int)sizeof(KT) / 16;
+  dim3 ggrid((k_eff * P + 255) / 256, a.h_kv);
+  ProfScope prof(K_SEL_GATHER, s);
+  sel_gather_kernel<KT, DH><<<ggrid, 256, 0, s>>>(k, (const KT*)a.v, a.cap_full, a.idx, k_eff,
+                                                   (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel);
+}
+
+void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s) {
+  if (a.dh == 64) {
+    if (kv_dtype == 1) select_typed<bf16_t, 64>(a, s);
+    else select_typed<float, 64>(a, s);
+  } else {
+    if (kv_dtype == 1) select_typed<bf16_t, 128>(a, s);
+    else select_typed<float, 128>(a, s);
+  }
+}
+
+// ------------------------------------------------------------------ k-th smallest
+// Order statistic of non-negative float32 values (their bit patterns order
+// like the values): four 8-bit digit passes, each a grid-wide histogram of the
+// values that match the digits found so far, then one thread picks the digit.
+// state[0] = prefix found so far, state[1] = rank still needed within it.
+__global__ void kth_init_kernel(unsigned* hist, unsigned* state, unsigned k) {
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) hist[b] = 0u;
+  if (threadIdx.x == 0) {
+    state[0] = 0u;
+    state[1] = k;
+  }
+}
+
+__global__ __launch_bounds__(256) void kth_hist_kernel(const float* __restrict__ vals, size_t n,
+                                                       int pass, const unsigned* __restrict__ state,
+                                                       unsigned* __restrict__ hist) {
+  __shared__ unsigned h[256];
+  h[threadIdx.x] = 0u;
+  __syncthreads();
+  const unsigned prefix = state[0];
+  const int shift = 24 - 8 * pass;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const float f = vals[i];
+    const unsigned key = f == 0.f ? 0u : __float_as_uint(f);
+    if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+      atomicAdd(&h[(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (h[threadIdx.x]) atomicAdd(&hist[threadIdx.x], h[threadIdx.x]);
+}
+
+__global__ void kth_pick_kernel(int pass, unsigned* hist, unsigned* state, float* out) {
+  if (threadIdx.x != 0) return;
+  const int shift = 24 - 8 * pass;
+  unsigned need = state[1], below = 0;
+  int b = 0;
+  for (; b < 255; ++b) {
+    if (below + hist[b] >= need) break;
+    below += hist[b];
+  }
+  state[0] |= (unsigned)b << shift;
+  state[1] = need - below;
+  for (int i = 0; i < 256; ++i) hist[i] = 0u;
+  if (pass == 3) *out = __uint_as_float(state[0]);
+}
+
+__global__ void fill_kernel(float* out, float v) { *out = v; }
+
+void launch_kth_smallest(const float* vals, size_t n, size_t k, unsigned* hist, unsigned* state,
+                         float* out, hipStream_t s) {
+  if (k == 0) {
+    fill_kernel<<<1, 1, 0, s>>>(out, -1.0f);
+    return;
+  }
+  ProfScope prof(K_KTH, s);
+  kth_init_kernel<<<1, 256, 0, s>>>(hist, state, (unsigned)k);
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  for (int pass = 0; pass < 4; ++pass) {
+    kth_hist_kernel<<<(unsigned)blocks, 256, 0, s>>>(vals, n, pass, state, hist);
+    kth_pick_kernel<<<1, 64, 0, s>>>(pass, hist, state, out);
+  }
+}
+
+}  // namespace sd

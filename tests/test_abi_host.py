@@ -1,0 +1,153 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol that
+include/sd.h declares, rejects bad arguments before touching the GPU, and its
+host-only byte account agrees with the oracle's independent one."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd.h")
+
+sd = pytest.importorskip("kv_cache_activation_amd", reason="libsd.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(sd.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(sd.EXPORTS)
+
+
+def test_struct_sizes_match_header_layout():
+    assert ctypes.sizeof(sd.sd_dims) == 36
+    assert ctypes.sizeof(sd.sd_layer) == 120
+    assert ctypes.sizeof(sd.sd_byte_record) == 80
+
+
+DIMS8B = dict(d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, d_ff=14336)
+
+
+def _dims(**over):
+    kw = dict(DIMS8B, w_dtype=sd.SD_BF16, kv_dtype=sd.SD_BF16)
+    kw.update(over)
+    return sd.make_dims(**kw)
+
+
+def test_status_strings():
+    assert sd.sd_status_string(sd.SD_OK) == "ok"
+    assert "workspace" in sd.sd_status_string(sd.SD_ENOSPC)
+
+
+def test_workspace_bytes_grows_with_rows_and_window():
+    a = sd.sd_workspace_bytes(_dims(), 0, 0)
+    b = sd.sd_workspace_bytes(_dims(), 131072, 32)
+    assert 0 < a < b
+    assert sd.sd_workspace_bytes(_dims(head_dim=96), 1024, 32) == 0  # unsupported dims
+
+
+FAKE = 1 << 20  # aligned address; never dereferenced because validation fails first
+
+
+class _FakeWs:
+    def __init__(self, nbytes):
+        self.n = nbytes
+
+    def data_ptr(self):
+        return FAKE
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(n_ctx=0), sd.SD_EINVAL),
+    (dict(n_ctx=10, cap=5), sd.SD_EINVAL),
+    (dict(q=FAKE + 4), sd.SD_EINVAL),
+    (dict(q=None), sd.SD_EINVAL),
+    (dict(ws_bytes=16), sd.SD_ENOSPC),
+    (dict(n_splits=100000), sd.SD_ENOSPC),
+    (dict(dims=dict(head_dim=96)), sd.SD_EUNSUPPORTED),
+    (dict(dims=dict(n_q_heads=24, n_kv_heads=8)), sd.SD_EUNSUPPORTED),
+    (dict(dims=dict(n_q_heads=30)), sd.SD_EINVAL),
+    (dict(dims=dict(d_model=4100)), sd.SD_EUNSUPPORTED),
+    (dict(dims=dict(w_dtype=7)), sd.SD_EUNSUPPORTED),
+])
+def test_decode_attn_rejects_before_launch(case, status):
+    dims = _dims(**case.get("dims", {}))
+    ws = _FakeWs(case.get("ws_bytes", 1 << 30))
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_attn(dims, case.get("q", FAKE), FAKE, FAKE, case.get("cap", 100),
+                          case.get("n_ctx", 50), 0.1, case.get("n_splits", 0), FAKE, None, ws, 0)
+    assert e.value.status == status
+    assert sd.sd_last_error()
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(w=0), sd.SD_EINVAL),
+    (dict(w=200), sd.SD_EINVAL),
+    (dict(k_keep=20, n_sink=4, w=32), sd.SD_EINVAL),
+    (dict(cap_sel=10), sd.SD_ENOSPC),
+    (dict(n=200), sd.SD_EINVAL),
+])
+def test_select_kv_rejects_before_launch(case, status):
+    a = dict(n=100, w=8, n_sink=4, k_keep=40, cap_sel=64)
+    a.update(case)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_select_kv(_dims(), FAKE, FAKE, 128, a["n"], FAKE, a["w"], a["n_sink"], a["k_keep"],
+                        FAKE, FAKE, FAKE, FAKE, a["cap_sel"], 0, _FakeWs(1 << 30), 0)
+    assert e.value.status == status
+
+
+def test_decode_step_rejects_full_cache_and_missing_buffer():
+    lay = sd.sd_layer(*([FAKE] * 7), 0.1, 0, FAKE, FAKE, 64, 64, None, None, 0, 0, None)
+    layers = (sd.sd_layer * 1)(lay)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step(_dims(), layers, 64, FAKE, 0, _FakeWs(1 << 30), 0)
+    assert e.value.status == sd.SD_ENOSPC
+    layers[0].n_full = 10
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step(_dims(), layers, 10, FAKE, sd.SD_KV_SPARSE, _FakeWs(1 << 30), 0)
+    assert e.value.status == sd.SD_EINVAL
+    assert layers[0].n_full == 10  # untouched on failure
+
+
+def test_sparse_mlp_rejects_nan_threshold():
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_sparse_mlp(_dims(), FAKE, None, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, FAKE,
+                         FAKE, 0, _FakeWs(1 << 30), 0)
+    assert e.value.status == sd.SD_EINVAL
+
+
+@pytest.mark.parametrize("proj,code", [("all7", sd.SD_PROJ_ALL7), ("ffn", sd.SD_PROJ_FFN),
+                                       ("cats", sd.SD_PROJ_CATS)])
+@pytest.mark.parametrize("n,r_p,r_kv,s_w,lm", [(2048, 0.5, 0.3, 2, 0), (131072, 0.5, 0.3, 2, 1.05e9),
+                                               (32768, 0.5, 0.1, 0.5, 0), (65536, 0.3, 1.0, 2, 0)])
+def test_byte_account_matches_oracle(proj, code, n, r_p, r_kv, s_w, lm):
+    from oracle import byte_account as ba
+    dm = ba.Dims(**DIMS8B)
+    want = ba.account(dm, 32, n, r_p, r_kv, s_w=s_w, s_kv=2, proj_set=proj, fixed_bytes=lm)
+    got = sd.sd_byte_account(_dims(), 32, n, r_p, r_kv, s_w, 2.0, code, lm)
+    for f in ("b_attn", "b_mlp", "b_kv", "b_total", "delta_p", "delta_kv", "bound_p", "bound_kv",
+              "bound_both", "n_star"):
+        a, b = getattr(got, f), getattr(want, f)
+        assert (math.isinf(a) and math.isinf(b)) or abs(a - b) <= 1e-12 * abs(b), (f, a, b)
+
+
+def test_byte_account_rejects_bad_ratio():
+    with pytest.raises(sd.SdError):
+        sd.sd_byte_account(_dims(), 32, 1024, 1.5, 0.3, 2, 2, sd.SD_PROJ_ALL7)

@@ -1,0 +1,94 @@
+"""GPU parity of sd_decode_attn (split-K decode attention) against the float64
+oracle's exact attention."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as oatt
+
+pytestmark = pytest.mark.gpu
+
+sd = pytest.importorskip("kv_cache_activation_amd")
+from gpu_helpers import DEV, TOL, dims_for, rel_l2, to_dev, to_host, workspace  # noqa: E402
+
+
+def _run(wl, k, v, cap, n_ctx, q, n_splits=0, scale=None):
+    dims = dims_for(wl)
+    scale = 1.0 / np.sqrt(wl.head_dim) if scale is None else scale
+    kd, vd, qd = to_dev(k, wl.dtype), to_dev(v, wl.dtype), to_dev(q)
+    out = torch.empty(wl.n_q_heads, wl.head_dim, device=DEV)
+    lse = torch.empty(wl.n_q_heads, device=DEV)
+    ws = workspace(dims)
+    sd.sd_decode_attn(dims, qd, kd, vd, cap, n_ctx, scale, n_splits, out, lse, ws)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(lse)
+
+
+@pytest.mark.parametrize("n_ctx,splits", [(1, 0), (2, 0), (127, 0), (129, 0), (2048, 0),
+                                          (2049, 0), (2049, 1), (2049, 3), (2049, 7), (300, 300),
+                                          (4099, 17)])
+def test_tiny_fp32_matches_oracle(n_ctx, splits):
+    wl = synth.TINY
+    cap = n_ctx + 5
+    k, v = synth.kv_cache(wl, 0, n_ctx, cap)
+    q = synth.decode_query(wl, 0)
+    out, lse = _run(wl, k, v, cap, n_ctx, q, splits)
+    want, want_lse = oatt.attend(q, k, v, n_ctx, 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(out, want) <= TOL["f32"]
+    assert rel_l2(lse, want_lse) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("n_ctx", [8193, 32769, 131073])
+def test_8b_bf16_matches_oracle(n_ctx):
+    # 8B-class shapes at the context lengths of the dense, KV and stacked
+    # workloads (rows read = context + the step's own row)
+    wl = synth.L8B_DENSE_8K
+    k, v = synth.kv_cache(wl, 0, n_ctx, n_ctx)
+    q = synth.decode_query(wl, 0)
+    out, lse = _run(wl, k, v, n_ctx, n_ctx, q)
+    want, want_lse = oatt.attend(q, k, v, n_ctx, 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(out, want) <= TOL["bf16"]
+    assert rel_l2(lse, want_lse) <= TOL["bf16"]
+    # float32 accumulation over exact bf16 inputs is far inside the bf16 bound
+    assert rel_l2(out, want) <= 1e-5
+
+
+def test_special_cases():
+    wl = synth.TINY
+    n = 777
+    k, v = synth.kv_cache(wl, 0, n, n)
+    q = synth.decode_query(wl, 0)
+    vc = np.full_like(v, 0.375)
+    out, _ = _run(wl, k, vc, n, n, q)
+    np.testing.assert_allclose(out, 0.375, rtol=1e-6)                    # constant V
+    out, lse = _run(wl, k, v, n, 1, q)                                   # one row
+    np.testing.assert_allclose(out, v[[0, 0, 1, 1], 0], rtol=1e-6, atol=1e-7)
+    out, lse = _run(wl, k, v, n, n, np.zeros_like(q))                    # q = 0
+    np.testing.assert_allclose(out, v[[0, 0, 1, 1], :n].mean(1), rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(lse, np.log(n), rtol=1e-6)
+
+
+def test_deterministic_and_split_invariant():
+    wl = synth.L8B_DENSE_8K
+    n = 20000
+    k, v = synth.kv_cache(wl, 3, n, n)
+    q = synth.decode_query(wl, 3)
+    a, _ = _run(wl, k, v, n, n, q)
+    b, _ = _run(wl, k, v, n, n, q)
+    assert np.array_equal(a, b)
+    c, _ = _run(wl, k, v, n, n, q, n_splits=5)
+    assert rel_l2(c, a) <= 1e-6
+
+
+def test_large_logits_stay_finite():
+    # logits near +-80 must not overflow: max subtraction per split and merge
+    wl = synth.TINY
+    n = 1000
+    k, v = synth.kv_cache(wl, 0, n, n)
+    q = synth.decode_query(wl, 0) * 40.0
+    out, lse = _run(wl, k, v, n, n, q)
+    want, want_lse = oatt.attend(q, k, v, n, 1 / np.sqrt(wl.head_dim))
+    assert np.all(np.isfinite(out))
+    assert rel_l2(out, want) <= 1e-5

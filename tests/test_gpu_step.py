@@ -1,0 +1,173 @@
+"""GPU parity of sd_decode_step (the composed decode step) against the float64
+oracle's decoder layer, in all four modes, across consecutive steps with mode
+switches, at tiny float32 and 8B-class bf16 sizes; plus properties at the
+full 32-layer, 128K-context size in the benchmark's launch configuration."""
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import selection as osel, step as ostep
+
+pytestmark = pytest.mark.gpu
+
+sd = pytest.importorskip("kv_cache_activation_amd")
+from gpu_helpers import (DEV, TOL, dims_for, midpoint_threshold, rel_l2, to_dev, to_host,  # noqa
+                         workspace)
+
+MODES = {"dense": 0, "kv": sd.SD_KV_SPARSE, "cats": sd.SD_MLP_SPARSE,
+         "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE}
+
+
+class Stack:
+    """Host (oracle) and device copies of a small layer stack with caches,
+    gathered buffers built from the oracle's own selection."""
+
+    def __init__(self, wl, n_layers, n, k_keep, extra=8, theta=500000.0):
+        self.wl, self.n, self.k_keep, self.theta = wl, n, k_keep, theta
+        self.dims = dims_for(wl, theta)
+        self.odims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                          kv_dtype=wl.dtype, eps=1e-5, theta=theta)
+        cap = n + extra
+        self.cap = cap
+        self.olayers, self.keep_alive, layers = [], [], []
+        for li in range(n_layers):
+            W = synth.layer_weights(wl, li)
+            k, v = synth.kv_cache(wl, li, n, cap)
+            qw = synth.window_queries(wl, li)
+            s32 = osel.window_scores(qw, k, n, 1 / np.sqrt(wl.head_dim)).astype(np.float32)
+            idx = osel.select_indices(s32, n, wl.window, wl.n_sink, k_keep)
+            ke = idx.shape[1]
+            ks = np.zeros((wl.n_kv_heads, ke + extra, wl.head_dim), np.float32)
+            vs = np.zeros_like(ks)
+            ks[:, :ke] = osel.gather(k, idx)
+            vs[:, :ke] = osel.gather(v, idx)
+            self.olayers.append(ostep.Layer(W["attn_norm"], W["w_qkv"], W["w_o"], W["mlp_norm"],
+                                            W["w_gate"], W["w_up"], W["w_down_t"], -1.0, k, v, n,
+                                            ks, vs, ke))
+            dW = {kk: to_dev(vv, "f32" if "norm" in kk else wl.dtype) for kk, vv in W.items()}
+            dk, dv, dks, dvs = (to_dev(a, wl.dtype) for a in (k, v, ks, vs))
+            mask = torch.zeros(wl.d_ff, dtype=torch.uint8, device=DEV)
+            self.keep_alive.append((dW, dk, dv, dks, dvs, mask))
+            layers.append(sd.sd_layer(dW["attn_norm"].data_ptr(), dW["w_qkv"].data_ptr(),
+                                      dW["w_o"].data_ptr(), dW["mlp_norm"].data_ptr(),
+                                      dW["w_gate"].data_ptr(), dW["w_up"].data_ptr(),
+                                      dW["w_down_t"].data_ptr(), -1.0, 0, dk.data_ptr(),
+                                      dv.data_ptr(), cap, n, dks.data_ptr(), dvs.data_ptr(),
+                                      ke + extra, ke, mask.data_ptr()))
+        self.layers = (sd.sd_layer * n_layers)(*layers)
+        self.ws = workspace(self.dims)
+
+    def step(self, h, pos, mode, sparsity=0.5):
+        kv_sparse = bool(MODES[mode] & sd.SD_KV_SPARSE)
+        mlp_sparse = bool(MODES[mode] & sd.SD_MLP_SPARSE)
+        if mlp_sparse:
+            from gpu_helpers import oracle_thresholds
+            ts = oracle_thresholds(self.olayers, h, pos, sparsity, kv_sparse, self.odims)
+            for li, t in enumerate(ts):
+                self.olayers[li].threshold = t
+                self.layers[li].cats_threshold = t
+        tr = []
+        want = ostep.decode_step(self.olayers, h, pos, kv_sparse=kv_sparse, mlp_sparse=mlp_sparse,
+                                 trace=tr, **self.odims)
+        hd = to_dev(h)
+        sd.sd_decode_step(self.dims, self.layers, pos, hd, MODES[mode], self.ws)
+        torch.cuda.synchronize()
+        return to_host(hd), want, tr
+
+
+def _check_caches(st, tol):
+    for li, ol in enumerate(st.olayers):
+        dW, dk, dv, dks, dvs, mask = st.keep_alive[li]
+        L = st.layers[li]
+        assert L.n_full == ol.n and L.n_sel == ol.n_sel
+        gk = to_host(dk)[:, :ol.n]
+        assert rel_l2(gk, ol.k_full[:, :ol.n]) <= tol
+        gks = to_host(dks)[:, :ol.n_sel]
+        assert rel_l2(gks, ol.k_sel[:, :ol.n_sel]) <= tol
+        # the appended rows match the oracle's rounded k, v
+        assert rel_l2(to_host(dv)[:, ol.n - 1], ol.v_full[:, ol.n - 1]) <= tol
+
+
+def test_tiny_fp32_mode_switching():
+    wl = synth.TINY
+    st = Stack(wl, 1, wl.n_ctx, wl.k_keep)
+    h = synth.hidden(wl, 0).astype(np.float64)
+    pos = wl.n_ctx
+    for mode in ("dense", "kv", "cats", "both", "both", "dense"):
+        got, want, tr = st.step(h, pos, mode)
+        assert rel_l2(got, want) <= TOL["f32"], mode
+        if MODES[mode] & sd.SD_MLP_SPARSE:
+            gmask = st.keep_alive[0][5].cpu().numpy().astype(bool)
+            assert np.array_equal(gmask, tr[0]["mask"]), mode
+        h = want  # the next step starts from the oracle's state
+        pos += 1
+    _check_caches(st, TOL["f32"])
+
+
+@pytest.mark.parametrize("theta", [500000.0, 0.0])
+def test_tiny_fp32_two_layers(theta):
+    wl = synth.TINY
+    st = Stack(wl, 2, 1000, 300, theta=theta)
+    h = synth.hidden(wl, 5)
+    got, want, _ = st.step(h, 1000, "both")
+    assert rel_l2(got, want) <= TOL["f32"]
+
+
+@pytest.fixture(scope="module")
+def stack8b():
+    # 8B-class layers (bf16) at the dense workload's 8K context, KV keep 16%
+    wl = synth.L8B_DENSE_8K
+    n = wl.n_ctx
+    return Stack(wl, 2, n, int(0.16 * n))
+
+
+@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both"])
+def test_8b_two_layers_each_mode(stack8b, mode):
+    st = stack8b
+    h = synth.hidden(st.wl, 7)
+    pos = st.olayers[0].n
+    got, want, tr = st.step(h, pos, mode)
+    assert rel_l2(got, want) <= TOL["bf16"], mode
+    if MODES[mode] & sd.SD_MLP_SPARSE:
+        for li in range(2):
+            gmask = st.keep_alive[li][5].cpu().numpy().astype(bool)
+            assert np.array_equal(gmask, tr[li]["mask"])
+    _check_caches(st, TOL["bf16"])
+
+
+def _identity_props(wl, n, n_layers=1):
+    """Dense vs KV with an identity gathered buffer, and CATS at t < 0 vs dense:
+    the same kernels on the same rows, so the results are bitwise equal."""
+    st = Stack(wl, n_layers, n, n)  # keep ratio 1: gathered buffer == full cache
+    h = synth.hidden(wl, 9)
+    outs = {}
+    for mode in ("dense", "kv", "cats"):
+        for li in range(n_layers):
+            st.layers[li].n_full = n
+            st.layers[li].n_sel = n
+            st.layers[li].cats_threshold = -1.0
+        hd = to_dev(h)
+        sd.sd_decode_step(st.dims, st.layers, n, hd, MODES[mode], st.ws)
+        torch.cuda.synchronize()
+        outs[mode] = to_host(hd)
+    assert np.array_equal(outs["dense"], outs["kv"])
+    assert np.array_equal(outs["dense"], outs["cats"])
+
+
+def test_identity_branches_equal_dense_tiny():
+    _identity_props(synth.TINY, 1500, 2)
+
+
+def test_errors_leave_state_untouched(stack8b):
+    st = stack8b
+    saved = [(L.n_full, L.n_sel) for L in st.layers]
+    st.layers[1].n_full = st.layers[1].cap_full  # full cache: no free row
+    hd = to_dev(synth.hidden(st.wl, 0))
+    with pytest.raises(sd.SdError):
+        sd.sd_decode_step(st.dims, st.layers, 5, hd, 0, st.ws)
+    st.layers[1].n_full = saved[1][0]
+    assert [(L.n_full, L.n_sel) for L in st.layers] == saved
