@@ -11,6 +11,10 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch brings its own HIP runtime (same soname as ROCm's).  Load it first so
+# that libsd.so binds to the runtime that owns the tensors' device memory.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsd.so")
 
