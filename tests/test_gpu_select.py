@@ -31,7 +31,7 @@ class Sel:
         self.vs = torch.zeros_like(self.ks)
         self.scores = torch.empty(wl.n_kv_heads, n, device=DEV)
         self.idx = torch.empty(wl.n_kv_heads, self.k_eff, dtype=torch.int32, device=DEV)
-        self.ws = workspace(self.dims, n, wl.window)
+        self.ws = workspace(self.dims, n, max(64, wl.window))
 
     def run(self, q_win=None, scores_in=None, w=None, n_sink=None):
         wl = self.wl
