@@ -25,10 +25,13 @@ sd_status fail(sd_status st, const char* fmt, ...) {
 
 bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxSplitBlocks = 1024;  // split-K workgroups per call, upper bound
-constexpr int kMinChunk = 128;         // rows per split, lower bound (auto mode)
+constexpr int kMaxSplits = 64;         // split-K chunks per KV head (merged in VGPRs)
+constexpr int kSplitBlocks = 512;      // auto mode: aim for this many split workgroups
+constexpr int kMinChunk = 256;         // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup
-constexpr int kDownRange = 256;        // channels per down-projection range
+constexpr int kDownTile = 128;         // columns per down-projection tile
+constexpr int kDownRanges = 16;        // channel ranges of the down projection
+constexpr int kMaxDownRange = 2048;    // channels per range the kernel compacts
 constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in VGPRs
 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
@@ -36,7 +39,8 @@ size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 struct Layout {
   size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, counters, lse_part, lse;
   size_t kth_hist, kth_state, total;
-  int max_splits, n_tiles, tile_cols, n_ranges, range_len, sel_chunks;
+  size_t attn_counters, down_counters;
+  int max_splits, n_tiles, n_ranges, range_len, sel_chunks;
 };
 
 Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
@@ -50,7 +54,7 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   const size_t hq = dm.n_q_heads, dh = dm.head_dim, hkv = dm.n_kv_heads, d = dm.d_model,
                ff = dm.d_ff;
   const size_t G = hq / hkv;
-  L.max_splits = kMaxSplitBlocks / (int)hkv > 0 ? kMaxSplitBlocks / (int)hkv : 1;
+  L.max_splits = kMaxSplits;
   L.q = take(hq * dh * 4);
   L.attn = take(hq * dh * 4);
   L.pm = take(hq * L.max_splits * 4);
@@ -59,12 +63,13 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.act = take(ff * 4);
   L.hmid = take(ff * 4);
   L.keep = take(ff);
-  L.tile_cols = d >= 512 ? 512 : (d >= 256 ? 256 : 128);
-  L.n_tiles = (int)((d + L.tile_cols - 1) / L.tile_cols);
-  L.range_len = kDownRange;
-  L.n_ranges = (int)((ff + kDownRange - 1) / kDownRange);
+  L.n_tiles = (int)((d + kDownTile - 1) / kDownTile);
+  L.range_len = (int)(((ff + kDownRanges - 1) / kDownRanges + 63) / 64 * 64);
+  L.n_ranges = (int)((ff + L.range_len - 1) / L.range_len);
   L.down_part = take((size_t)L.n_ranges * d * 4);
-  L.counters = take((size_t)L.n_tiles * 4);
+  L.counters = take(((size_t)hkv + L.n_tiles) * 4);
+  L.attn_counters = L.counters;
+  L.down_counters = L.counters + hkv * 4;
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
   L.lse = take(hq * (size_t)max_window * 4);
@@ -90,6 +95,8 @@ sd_status check_dims(const sd_dims* dm) {
     return fail(SD_EUNSUPPORTED, "d_model must be a multiple of 8 and at most %d", kMaxWidth);
   if (dm->n_q_heads * dm->head_dim > kMaxWidth)
     return fail(SD_EUNSUPPORTED, "n_q_heads * head_dim must be at most %d", kMaxWidth);
+  if (dm->d_ff > kDownRanges * kMaxDownRange)
+    return fail(SD_EUNSUPPORTED, "d_ff must be at most %d", kDownRanges * kMaxDownRange);
   if ((dm->w_dtype != SD_F32 && dm->w_dtype != SD_BF16) ||
       (dm->kv_dtype != SD_F32 && dm->kv_dtype != SD_BF16))
     return fail(SD_EUNSUPPORTED, "dtype must be SD_F32 or SD_BF16");
@@ -110,16 +117,20 @@ int cu_count() {
   return cu > 0 ? cu : 256;
 }
 
-int auto_splits(int n_ctx, int max_splits) {
-  int s = (n_ctx + kMinChunk - 1) / kMinChunk;
-  if (s > max_splits) s = max_splits;
+// Splits per KV head: about kSplitBlocks workgroups in all, at least kMinChunk
+// rows each, at most kMaxSplits.
+int auto_splits(int n_ctx, int h_kv) {
+  int s = (kSplitBlocks + h_kv - 1) / h_kv;
+  const int by_rows = (n_ctx + kMinChunk - 1) / kMinChunk;
+  if (s > by_rows) s = by_rows;
+  if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : s;
 }
 
 // Enqueue split-K attention; ws must hold the layout's attention buffers.
 void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, const void* k,
                   const void* v, int cap, int n_ctx, float scale, int n_splits, float* out,
-                  float* lse, hipStream_t s) {
+                  float* lse, bool zero_counters, hipStream_t s) {
   sd::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -135,6 +146,8 @@ void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, 
   a.pm = reinterpret_cast<float*>(ws + L.pm);
   a.pl = reinterpret_cast<float*>(ws + L.pl);
   a.pacc = reinterpret_cast<float*>(ws + L.pacc);
+  a.counters = reinterpret_cast<unsigned*>(ws + L.attn_counters);
+  a.zero_counters = zero_counters;
   a.out = out;
   a.lse = lse;
   sd::launch_attn(a, dm.kv_dtype, s);
@@ -158,10 +171,9 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   g.act = act;
   g.keep = keep;
   g.hmid = reinterpret_cast<float*>(ws + L.hmid);
-  g.zero_buf = reinterpret_cast<unsigned*>(ws + L.counters);
+  g.zero_buf = reinterpret_cast<unsigned*>(ws + L.down_counters);
   g.zero_n = L.n_tiles;
-  const int pairs = (dm.d_ff + 1) / 2;
-  g.grid = (pairs + 7) / 8;
+  g.grid = (dm.d_ff + 15) / 16;  // one block of 4 rows per wave
   g.n_states = 1;
   sd::launch_gate_up(g, dm.w_dtype, s);
 
@@ -174,7 +186,6 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   dn.range_len = L.range_len;
   dn.n_ranges = L.n_ranges;
   dn.n_tiles = L.n_tiles;
-  dn.tile_cols = L.tile_cols;
   dn.partials = reinterpret_cast<float*>(ws + L.down_part);
   dn.counters = g.zero_buf;
   dn.y = y;
@@ -267,8 +278,8 @@ sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, con
   if (n_splits < 0) return fail(SD_EINVAL, "n_splits must be >= 0");
   if (n_splits > L.max_splits)
     return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
-  int s = n_splits ? (n_splits < n_ctx ? n_splits : n_ctx) : auto_splits(n_ctx, L.max_splits);
-  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, scale, s, out, lse,
+  int s = n_splits ? (n_splits < n_ctx ? n_splits : n_ctx) : auto_splits(n_ctx, dims->n_kv_heads);
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, scale, s, out, lse, true,
                static_cast<hipStream_t>(stream));
   return check_launch("sd_decode_attn");
 }
@@ -353,8 +364,8 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     qa.v_sel = has_sel ? l.v_sel : nullptr;
     qa.cap_sel = l.cap_sel;
     qa.row_sel = l.n_sel;
-    qa.zero_buf = nullptr;
-    qa.zero_n = 0;
+    qa.zero_buf = reinterpret_cast<unsigned*>(wsb + L.attn_counters);  // tickets of this
+    qa.zero_n = hkv;                                                    // layer's attention
     qa.grid = ((hq + 2 * hkv) * dh / 2 + 3) / 4;
     sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
 
@@ -362,8 +373,8 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     const void* vc = kv_sparse ? l.v_sel : l.v_full;
     const int cap = kv_sparse ? l.cap_sel : l.cap_full;
     const int n_ctx = (kv_sparse ? l.n_sel : l.n_full) + 1;
-    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, scale, auto_splits(n_ctx, L.max_splits),
-                 attn, nullptr, s);
+    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, scale, auto_splits(n_ctx, hkv), attn,
+                 nullptr, false, s);
 
     sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, (d / 2 + 3) / 4, s);
 
@@ -414,8 +425,7 @@ sd_status sd_cats_calibrate(const sd_dims* dims, const float* states, int32_t n_
   g.t = -1.f;
   g.store_abs = 1;
   g.act = vals;
-  const int pairs = (dims->d_ff + 1) / 2;
-  g.grid = (pairs + 7) / 8;
+  g.grid = (dims->d_ff + 15) / 16;
   g.n_states = n_states;
   sd::launch_gate_up(g, dims->w_dtype, s);
   const size_t N = (size_t)n_states * dims->d_ff;

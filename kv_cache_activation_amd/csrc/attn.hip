@@ -14,9 +14,11 @@
 //   the lane groups and the four waves merge their states and write one
 //   (m, l, acc[d_h]) per query head and split.
 //
-//   combine kernel, grid (query heads): out = sum_s 2^(m_s - M) acc_s /
-//   sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2, splits in order, so the
-//   result does not depend on scheduling.
+//   The last workgroup to finish for a KV head (device-scope ticket counter,
+//   zeroed before the launch) merges that head's split partials:
+//   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2,
+//   splits in order, so the result does not depend on scheduling.  All split
+//   loads of that merge are issued together (at most kMaxSplits per head).
 #include <math.h>
 
 #include "common.hpp"
@@ -25,17 +27,19 @@
 namespace sd {
 
 constexpr int kAttnThreads = 256;
+constexpr int kMaxSplits = 64;  // splits per KV head (the merge holds them in VGPRs)
 constexpr int kAttnWaves = kAttnThreads / kWave;
 
 template <typename KT, int DH, int G>
 __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
     int n_ctx, float scale_log2, int chunk, int n_splits, float* __restrict__ pm,
-    float* __restrict__ pl, float* __restrict__ pacc) {
+    float* __restrict__ pl, float* __restrict__ pacc, unsigned* __restrict__ counters,
+    float* __restrict__ out, float* __restrict__ lse) {
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
-  constexpr int U = 2;                 // rows in flight per slot
+  constexpr int U = 4;                 // rows in flight per slot
   __shared__ float sm_m[kAttnWaves][G], sm_l[kAttnWaves][G];
   __shared__ float sm_acc[kAttnWaves][G][DH];
 
@@ -174,29 +178,75 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
       pl[hs] = L;
     }
   }
+
+  // ---- last workgroup of this KV head merges all splits
+  __shared__ int last_s;
+  __shared__ float w_s[G][kMaxSplits], l_s[G][kMaxSplits];
+  __shared__ float big_m[G], big_l[G];
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last_s = atomicAdd(&counters[kv], 1u) == (unsigned)(n_splits - 1);
+  __syncthreads();
+  if (!last_s) return;
+  __threadfence();
+  for (int t = threadIdx.x; t < G * n_splits; t += kAttnThreads) {
+    const int g = t / n_splits, sp = t - g * n_splits;
+    const size_t hs = (size_t)(kv * G + g) * n_splits + sp;
+    w_s[g][sp] = __builtin_nontemporal_load(pm + hs);
+    l_s[g][sp] = __builtin_nontemporal_load(pl + hs);
+  }
+  __syncthreads();
+  for (int g = wave; g < G; g += kAttnWaves) {
+    const float mi = lane < n_splits ? w_s[g][lane] : -INFINITY;
+    const float M = wave_max(mi);
+    const float wi = mi == -INFINITY ? 0.f : exp2f(mi - M);
+    const float L = wave_sum(lane < n_splits ? wi * l_s[g][lane] : 0.f);
+    if (lane < n_splits) w_s[g][lane] = wi;
+    if (lane == 0) {
+      big_m[g] = M;
+      big_l[g] = L;
+    }
+  }
+  __syncthreads();
+  // thread (split group sg, column quad cq) accumulates its splits' float4s of
+  // every head; then the split groups are summed through LDS in group order
+  constexpr int NQ = DH / 4;                 // float4 column quads per row
+  constexpr int GROUPS = kAttnThreads / NQ;  // split groups
+  constexpr int ITERS = kMaxSplits / GROUPS;
+  const int cq = threadIdx.x % NQ, sg = threadIdx.x / NQ;
+  __shared__ float red[GROUPS * G * DH];
+  for (int g = 0; g < G; ++g) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    f32x4 v[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int sp = sg + it * GROUPS;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      v[it] = sp < n_splits ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+                                  pacc + ((size_t)(kv * G + g) * n_splits + sp) * DH) + cq)
+                            : z;
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int sp = sg + it * GROUPS;
+      if (sp < n_splits) a += w_s[g][sp] * v[it];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[sg * G * DH + g * DH + 4 * cq + e] = a[e];
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < G * DH; o += kAttnThreads) {
+    const int g = o / DH, c = o - g * DH;
+    float A = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < GROUPS; ++grp) A += red[grp * G * DH + o];
+    out[(size_t)(kv * G + g) * DH + c] = A / big_l[g];
+    if (lse && c == 0) lse[kv * G + g] = (big_m[g] + log2f(big_l[g])) * 0.69314718055994530942f;
+  }
 }
 
-template <int DH>
-__global__ __launch_bounds__(DH) void attn_combine_kernel(const float* __restrict__ pm,
-                                                          const float* __restrict__ pl,
-                                                          const float* __restrict__ pacc,
-                                                          int n_splits, float* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  const int h = blockIdx.x, c = threadIdx.x;
-  const float* m = pm + (size_t)h * n_splits;
-  const float* l = pl + (size_t)h * n_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, m[s]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float ms = m[s];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - M);
-    L = fmaf(w, l[s], L);
-    A = fmaf(w, pacc[((size_t)h * n_splits + s) * DH + c], A);
-  }
-  out[(size_t)h * DH + c] = A / L;
-  if (lse && c == 0) lse[h] = (M + log2f(L)) * 0.69314718055994530942f;
+__global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
 template <typename KT, int DH>
@@ -206,22 +256,19 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_splits, a.h_kv);
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
+  if (a.zero_counters) zero_u32_kernel<<<1, 64, 0, s>>>(a.counters, a.h_kv);
 #define SD_ATTN_G(GG)                                                                      \
-  attn_partial_kernel<KT, DH, GG><<<grid, kAttnThreads, 0, s>>>(a.q, k, v, a.cap, a.n_ctx,   \
-                                                                scale_log2, a.chunk,        \
-                                                                a.n_splits, a.pm, a.pl, a.pacc)
-  {
-    ProfScope prof(K_ATTN_PARTIAL, s);
-    switch (G) {
-      case 1: SD_ATTN_G(1); break;
-      case 2: SD_ATTN_G(2); break;
-      case 4: SD_ATTN_G(4); break;
-      default: SD_ATTN_G(8); break;
-    }
+  attn_partial_kernel<KT, DH, GG><<<grid, kAttnThreads, 0, s>>>(                           \
+      a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc,      \
+      a.counters, a.out, a.lse)
+  ProfScope prof(K_ATTN_PARTIAL, s);
+  switch (G) {
+    case 1: SD_ATTN_G(1); break;
+    case 2: SD_ATTN_G(2); break;
+    case 4: SD_ATTN_G(4); break;
+    default: SD_ATTN_G(8); break;
   }
 #undef SD_ATTN_G
-  ProfScope prof(K_ATTN_COMBINE, s);
-  attn_combine_kernel<DH><<<a.h_q, DH, 0, s>>>(a.pm, a.pl, a.pacc, a.n_splits, a.out, a.lse);
 }
 
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s) {

@@ -7,15 +7,17 @@
 // stored transposed, w_down_t [d_ff, d], so one kept channel is one contiguous
 // row of d elements.
 //
-// Grid: (column tiles) x (channel ranges).  A workgroup
+// Grid: (128-column tiles) x (channel ranges, at most 32).  A workgroup
 //   1. compacts the kept channels of its range into an ascending LDS list with
-//      a wave ballot + popcount prefix (the keep bytes come from the gate
-//      kernel),
-//   2. streams its column tile of each kept row (one 16-byte load per lane,
-//      four rows in flight per lane) and accumulates hmid_i * w_down_t[i],
+//      wave ballots and popcount prefixes (the keep bytes come from the gate
+//      kernel; all of them are loaded in one round),
+//   2. streams its 256-byte segment of each kept row (one 16-byte load per
+//      lane, eight rows in flight per lane) and accumulates hmid_i * w_down_t[i],
 //   3. writes a partial sum for (range, tile); the last workgroup to finish a
 //      tile (device-scope counter) adds the partials of all ranges in range
 //      order, so the result is deterministic, and writes y (or y += result).
+// Few ranges keep that final sum to one round of loads; many tiles keep the
+// grid wide enough to fill the chip.
 // Column-tile workgroups of range r also emit that range's part of the global
 // ascending kept list at offset popcount(keep[0 .. range start)).
 #include "common.hpp"
@@ -25,42 +27,68 @@ namespace sd {
 
 constexpr int kDownThreads = 256;
 constexpr int kDownWaves = kDownThreads / kWave;
+constexpr int kMaxRanges = 32;   // channel ranges per call (the final sum holds them in VGPRs)
+constexpr int kDownTile = 128;   // columns per tile: 16 lanes x 8 columns
 
-template <typename WT, int LPR>
+// Block-wide exclusive prefix count of `flag` in thread order, and the total.
+__device__ __forceinline__ int down_prefix(bool flag, int* wave_tot, int& total) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const unsigned long long m = __ballot(flag);
+  if (lane == 0) wave_tot[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int v = 0; v < kDownWaves; ++v) {
+    before += v < wave ? wave_tot[v] : 0;
+    total += wave_tot[v];
+  }
+  __syncthreads();
+  return before + __popcll(m & ((1ull << lane) - 1ull));
+}
+
+template <typename WT>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(
     const WT* __restrict__ Wd, int d, int dff, const uint8_t* __restrict__ keep,
     const float* __restrict__ hmid, int range_len, int n_ranges, float* __restrict__ partials,
     unsigned* __restrict__ counters, float* __restrict__ y, int accumulate,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ n_kept_out) {
+  constexpr int LPR = kDownTile / 8;      // lanes per row segment
   constexpr int RPW = kWave / LPR;        // row slots per wave
   constexpr int SLOTS = kDownWaves * RPW; // row slots per workgroup
-  constexpr int TILE = 8 * LPR;           // columns per tile
-  constexpr int U = 4;                    // rows in flight per slot
+  constexpr int U = 8;                    // rows in flight per slot
   extern __shared__ int list[];           // [range_len]
-  __shared__ float red[kDownWaves][TILE];
-  __shared__ int cnt_s, last_s, prefix_s;
+  __shared__ float red[kDownWaves][kDownTile];
+  __shared__ int wave_tot[kDownWaves];
+  __shared__ int last_s, prefix_s;
 
   const int tile = blockIdx.x, range = blockIdx.y;
   const int i0 = range * range_len;
   const int i1 = min(dff, i0 + range_len);
   const int lane = lane_id(), wave = threadIdx.x / kWave;
 
-  if (wave == 0) {
-    int cnt = 0;
-    for (int base = i0; base < i1; base += kWave) {
-      const int i = base + lane;
-      const bool f = i < i1 && keep[i] != 0;
-      const unsigned long long m = __ballot(f);
-      if (f) list[cnt + __popcll(m & ((1ull << lane) - 1ull))] = i;
-      cnt += __popcll(m);
-    }
-    if (lane == 0) cnt_s = cnt;
+  // ascending list of the kept channels of [i0, i1): all flags loaded at once,
+  // then one ballot prefix per 256-channel round
+  constexpr int kRounds = 8;  // range_len <= 2048
+  bool f[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int i = i0 + r * kDownThreads + threadIdx.x;
+    f[r] = i < i1 && keep[i] != 0;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (i0 + r * kDownThreads >= i1) break;
+    int tot;
+    const int pos = cnt + down_prefix(f[r], wave_tot, tot);
+    if (f[r]) list[pos] = i0 + r * kDownThreads + threadIdx.x;
+    cnt += tot;
   }
   __syncthreads();
-  const int cnt = cnt_s;
 
   const int slot = wave * RPW + lane / LPR;
-  const int col = tile * TILE + 8 * (lane % LPR);
+  const int col = tile * kDownTile + 8 * (lane % LPR);
   const bool col_ok = col < d;
   float acc[8];
 #pragma unroll
@@ -81,14 +109,14 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j + u * SLOTS < cnt && col_ok) {
-        float f[8];
-        w[u].to_float(f);
+        float fw[8];
+        w[u].to_float(fw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv[u], f[e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv[u], fw[e], acc[e]);
       }
     }
   }
-  // row slots of a wave -> one sum per column chunk (lanes 0..LPR-1)
+  // row slots of a wave -> one sum per column (lanes 0..LPR-1)
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1)
 #pragma unroll
@@ -97,13 +125,13 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
   __syncthreads();
-  for (int c = threadIdx.x; c < TILE; c += kDownThreads) {
-    const int gc = tile * TILE + c;
+  for (int c = threadIdx.x; c < kDownTile; c += kDownThreads) {
+    const int gc = tile * kDownTile + c;
     if (gc < d) {
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDownWaves; ++w) s += red[w][c];
-      partials[(size_t)range * d + gc] = s;
+      for (int w = 0; w < kDownWaves; ++w) sum += red[w][c];
+      partials[(size_t)range * d + gc] = sum;
     }
   }
   __threadfence();
@@ -111,21 +139,29 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   if (threadIdx.x == 0) last_s = atomicAdd(&counters[tile], 1u) == (unsigned)(n_ranges - 1);
   __syncthreads();
   if (last_s) {
+    // last workgroup of this tile: sum the ranges in order, all loads at once
     __threadfence();
-    for (int c = threadIdx.x; c < TILE; c += kDownThreads) {
-      const int gc = tile * TILE + c;
+    for (int c = threadIdx.x; c < kDownTile; c += kDownThreads) {
+      const int gc = tile * kDownTile + c;
       if (gc < d) {
-        float s = 0.f;
-        for (int r = 0; r < n_ranges; ++r) s += __builtin_nontemporal_load(partials + (size_t)r * d + gc);
-        y[gc] = accumulate ? y[gc] + s : s;
+        float v[kMaxRanges];
+#pragma unroll
+        for (int r = 0; r < kMaxRanges; ++r)
+          v[r] = r < n_ranges ? __builtin_nontemporal_load(partials + (size_t)r * d + gc) : 0.f;
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < kMaxRanges; ++r) sum += v[r];
+        y[gc] = accumulate ? y[gc] + sum : sum;
       }
     }
   }
 
   if (idx_out && tile == 0) {
+    // offset of this range's list: kept channels before i0 (bytes are 0 or 1)
     int c = 0;
-    for (int i = threadIdx.x; i < i0; i += kDownThreads) c += keep[i] != 0;
-    c = (int)wave_sum((float)c);  // exact: counts stay far below 2^24
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(keep);
+    for (int q = threadIdx.x; q < i0 / 4; q += kDownThreads) c += (int)((kw[q] * 0x01010101u) >> 24);
+    for (int off = 1; off < kWave; off <<= 1) c += __shfl_xor(c, off);
     if (threadIdx.x == 0) prefix_s = 0;
     __syncthreads();
     if (lane == 0) atomicAdd(&prefix_s, c);
@@ -140,22 +176,11 @@ template <typename WT>
 static void down_typed(const DownArgs& a, hipStream_t s) {
   dim3 grid(a.n_tiles, a.n_ranges);
   size_t lds = (size_t)a.range_len * sizeof(int);
-  const WT* w = (const WT*)a.w_down_t;
   ProfScope prof(K_DOWN, s);
-  switch (a.tile_cols) {
-    case 128:
-      down_kernel<WT, 16><<<grid, kDownThreads, lds, s>>>(w, a.d, a.dff, a.keep, a.hmid,
-          a.range_len, a.n_ranges, a.partials, a.counters, a.y, a.accumulate, a.idx_out, a.n_kept_out);
-      break;
-    case 256:
-      down_kernel<WT, 32><<<grid, kDownThreads, lds, s>>>(w, a.d, a.dff, a.keep, a.hmid,
-          a.range_len, a.n_ranges, a.partials, a.counters, a.y, a.accumulate, a.idx_out, a.n_kept_out);
-      break;
-    default:
-      down_kernel<WT, 64><<<grid, kDownThreads, lds, s>>>(w, a.d, a.dff, a.keep, a.hmid,
-          a.range_len, a.n_ranges, a.partials, a.counters, a.y, a.accumulate, a.idx_out, a.n_kept_out);
-      break;
-  }
+  down_kernel<WT><<<grid, kDownThreads, lds, s>>>((const WT*)a.w_down_t, a.d, a.dff, a.keep,
+                                                  a.hmid, a.range_len, a.n_ranges, a.partials,
+                                                  a.counters, a.y, a.accumulate, a.idx_out,
+                                                  a.n_kept_out);
 }
 
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s) {

@@ -57,36 +57,46 @@ struct XSlice {
   }
 };
 
-// Full-wave dot products of R weight rows with the wave's input slice.
-// rows[r] < 0 marks an absent row (its result is 0).
+// R weight rows held by one wave: lane l holds the 16-byte chunks
+// 8(l + 64k) .. +8 of each row, k < NCH.  load() only issues the loads, so the
+// caller can overlap their latency with other work before dot().
+// rows[r] < 0 marks an absent row (its dot product is 0).
 template <typename WT, int NCH, int R>
-__device__ __forceinline__ void dot_rows(const WT* __restrict__ W, int ld, const int (&rows)[R],
-                                         const XSlice<NCH>& x, int d8, float (&out)[R]) {
-  const int lane = lane_id();
+struct RowBlock {
   Vec8<WT> w[R][NCH];
+
+  __device__ __forceinline__ void load(const WT* __restrict__ W, int ld, const int (&rows)[R],
+                                       int d8) {
+    const int lane = lane_id();
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      int c8 = lane + kWave * k;
-      if (rows[r] >= 0 && c8 < d8) w[r][k].load(W + (size_t)rows[r] * ld + 8 * c8);
-    }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      int c8 = lane + kWave * k;
-      if (rows[r] >= 0 && c8 < d8) {
-        float f[8];
-        w[r][k].to_float(f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(f[e], x.v[k][e], acc);
+      for (int k = 0; k < NCH; ++k) {
+        const int c8 = lane + kWave * k;
+        if (rows[r] >= 0 && c8 < d8) w[r][k].load(W + (size_t)rows[r] * ld + 8 * c8);
       }
-    }
-    out[r] = wave_sum(acc);
   }
-}
+
+  __device__ __forceinline__ void dot(const XSlice<NCH>& x, int d8, const int (&rows)[R],
+                                      float (&out)[R]) const {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c8 = lane + kWave * k;
+        if (rows[r] >= 0 && c8 < d8) {
+          float f[8];
+          w[r][k].to_float(f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf(f[e], x.v[k][e], acc);
+        }
+      }
+      out[r] = wave_sum(acc);
+    }
+  }
+};
 
 // ------------------------------------------------------------------ QKV
 // x = RMSNorm(h) * attn_norm; [q; k; v] = W_qkv x; RoPE on q and k at `pos`
@@ -104,9 +114,25 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
     unsigned* __restrict__ zero_buf, int zero_n) {
   extern __shared__ float xs[];
   __shared__ float rope_c[64], rope_s[64];
+  const int half = dh >> 1;
+  const int d8 = d >> 3;
+  const int n_pairs = (h_q + 2 * h_kv) * half;
+  const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int n_waves = gridDim.x * kWavesPerBlock;
+  // issue this wave's first weight rows before the prologue: their latency
+  // overlaps the norm reduction and the RoPE table
+  RowBlock<WT, NCH, 2> blk;
+  auto pair_rows = [&](int p, int (&rows)[2]) {
+    const int head = p / half, i = p - head * half;
+    rows[0] = p < n_pairs ? head * dh + i : -1;
+    rows[1] = p < n_pairs ? head * dh + i + half : -1;
+  };
+  int rows[2];
+  pair_rows(wave, rows);
+  blk.load(W, d, rows, d8);
+
   if (blockIdx.x == 0 && zero_buf)
     for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_buf[i] = 0u;
-  const int half = dh >> 1;
   // cos/sin of pos * theta^(-2i/d_h), in double precision: pos reaches 1e5+
   // and float angles would carry errors of order 1e-2 radians.
   if (threadIdx.x < half) {
@@ -123,18 +149,17 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
   }
   const float rs = stage_input(h, nw, d, eps, true, xs);
   __syncthreads();
-  const int d8 = d >> 3;
   XSlice<NCH> x;
   x.load(xs, d8);
 
-  const int n_pairs = (h_q + 2 * h_kv) * half;
-  const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const int n_waves = gridDim.x * kWavesPerBlock;
   for (int p = wave; p < n_pairs; p += n_waves) {
     const int head = p / half, i = p - head * half;
-    const int rows[2] = {head * dh + i, head * dh + i + half};
+    if (p != wave) {
+      pair_rows(p, rows);
+      blk.load(W, d, rows, d8);
+    }
     float s[2];
-    dot_rows<WT, NCH, 2>(W, d, rows, x, d8, s);
+    blk.dot(x, d8, rows, s);
     if (lane_id() == 0) {
       float a = s[0] * rs, b = s[1] * rs;
       if (head < h_q + h_kv) {  // rotate q and k, not v
@@ -172,17 +197,24 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
                                                               const WT* __restrict__ W, int din,
                                                               int dout, float* __restrict__ h) {
   extern __shared__ float xs[];
-  stage_input(attn, nullptr, din, 0.f, false, xs);
-  __syncthreads();
   const int d8 = din >> 3;
-  XSlice<NCH> x;
-  x.load(xs, d8);
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
+  RowBlock<WT, NCH, 2> blk;
+  int rows[2] = {2 * wave < dout ? 2 * wave : -1, 2 * wave + 1 < dout ? 2 * wave + 1 : -1};
+  blk.load(W, din, rows, d8);  // before the prologue
+  stage_input(attn, nullptr, din, 0.f, false, xs);
+  __syncthreads();
+  XSlice<NCH> x;
+  x.load(xs, d8);
   for (int r0 = 2 * wave; r0 < dout; r0 += 2 * n_waves) {
-    const int rows[2] = {r0, r0 + 1 < dout ? r0 + 1 : -1};
+    if (r0 != 2 * wave) {
+      rows[0] = r0;
+      rows[1] = r0 + 1 < dout ? r0 + 1 : -1;
+      blk.load(W, din, rows, d8);
+    }
     float s[2];
-    dot_rows<WT, NCH, 2>(W, din, rows, x, d8, s);
+    blk.dot(x, d8, rows, s);
     if (lane_id() == 0) {
       h[r0] += s[0];
       if (rows[1] >= 0) h[r0 + 1] += s[1];
@@ -203,50 +235,63 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     int store_abs, float* __restrict__ act, uint8_t* __restrict__ keep, float* __restrict__ hmid,
     unsigned* __restrict__ zero_buf, int zero_n) {
   extern __shared__ float xs[];
-  if (blockIdx.x == 0 && blockIdx.y == 0 && zero_buf)
-    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_buf[i] = 0u;
+  constexpr int R = 4;  // rows per wave iteration: their gate loads go out together
   xin += (size_t)blockIdx.y * d;
   act += (size_t)blockIdx.y * dff;
-  const float rs = stage_input(xin, nw, d, eps, norm != 0, xs);
-  __syncthreads();
   const int d8 = d >> 3;
-  XSlice<NCH> x;
-  x.load(xs, d8);
   const int lane = lane_id();
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  for (int r0 = 2 * wave; r0 < dff; r0 += 2 * n_waves) {
-    const int r1 = r0 + 1 < dff ? r0 + 1 : -1;
-    float a[2];
+  RowBlock<WT, NCH, R> blk;
+  int rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = R * wave + r < dff ? R * wave + r : -1;
+  if (!gate_in) blk.load(Wg, d, rows, d8);  // before the prologue
+
+  if (blockIdx.x == 0 && blockIdx.y == 0 && zero_buf)
+    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_buf[i] = 0u;
+  const float rs = stage_input(xin, nw, d, eps, norm != 0, xs);
+  __syncthreads();
+  XSlice<NCH> x;
+  x.load(xs, d8);
+  for (int r0 = R * wave; r0 < dff; r0 += R * n_waves) {
+    if (r0 != R * wave) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) rows[r] = r0 + r < dff ? r0 + r : -1;
+      if (!gate_in) blk.load(Wg, d, rows, d8);
+    }
+    float a[R];
     if (gate_in) {
-      a[0] = act[r0];
-      a[1] = r1 >= 0 ? act[r1] : 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[r] = rows[r] >= 0 ? act[rows[r]] : 0.f;
     } else {
-      const int rows[2] = {r0, r1};
-      float g[2];
-      dot_rows<WT, NCH, 2>(Wg, d, rows, x, d8, g);
-      a[0] = silu(g[0] * rs);
-      a[1] = silu(g[1] * rs);
-      if (lane == 0) {
-        act[r0] = store_abs ? fabsf(a[0]) : a[0];
-        if (r1 >= 0) act[r1] = store_abs ? fabsf(a[1]) : a[1];
-      }
+      float g[R];
+      blk.dot(x, d8, rows, g);
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[r] = silu(g[r] * rs);
+      if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (rows[r] >= 0) act[rows[r]] = store_abs ? fabsf(a[r]) : a[r];
     }
     if (!Wu) continue;
-    const bool k0 = t < 0.f || fabsf(a[0]) > t;
-    const bool k1 = r1 >= 0 && (t < 0.f || fabsf(a[1]) > t);
-    if (lane == 0) {
-      keep[r0] = k0;
-      if (r1 >= 0) keep[r1] = k1;
+    int urows[R];
+    bool any = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool k = rows[r] >= 0 && (t < 0.f || fabsf(a[r]) > t);
+      urows[r] = k ? rows[r] : -1;
+      any |= k;
+      if (lane == 0 && rows[r] >= 0) keep[rows[r]] = k;
     }
-    if (!k0 && !k1) continue;
-    const int rows[2] = {k0 ? r0 : -1, k1 ? r1 : -1};
-    float u[2];
-    dot_rows<WT, NCH, 2>(Wu, d, rows, x, d8, u);
-    if (lane == 0) {
-      if (k0) hmid[r0] = a[0] * (u[0] * rs);
-      if (k1) hmid[r1] = a[1] * (u[1] * rs);
-    }
+    if (!any) continue;
+    blk.load(Wu, d, urows, d8);  // only the kept channels' up rows
+    float u[R];
+    blk.dot(x, d8, urows, u);
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (urows[r] >= 0) hmid[urows[r]] = a[r] * (u[r] * rs);
   }
 }
 

@@ -67,7 +67,7 @@ struct DownArgs {
   int d, dff;
   const uint8_t* keep;
   const float* hmid;
-  int range_len, n_ranges, n_tiles, tile_cols;
+  int range_len, n_ranges, n_tiles;
   float* partials;     // [n_ranges, d]
   unsigned* counters;  // [n_tiles], zero on entry
   float* y;
@@ -86,6 +86,8 @@ struct AttnArgs {
   float* pm;
   float* pl;
   float* pacc;
+  unsigned* counters;  // [h_kv] tickets; zero before the launch
+  int zero_counters;   // clear them with a tiny kernel first (standalone calls)
   float* out;
   float* lse;
 };
