@@ -27,7 +27,7 @@ def _run(wl, k, v, cap, n_ctx, q, n_splits=0, scale=None):
 
 
 @pytest.mark.parametrize("n_ctx,splits", [(1, 0), (2, 0), (127, 0), (129, 0), (2048, 0),
-                                          (2049, 0), (2049, 1), (2049, 3), (2049, 7), (300, 300),
+                                          (2049, 0), (2049, 1), (2049, 3), (2049, 7), (64, 64), (300, 64),
                                           (4099, 17)])
 def test_tiny_fp32_matches_oracle(n_ctx, splits):
     wl = synth.TINY
