@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--contexts", type=str, default="2048,8192,32768,65536,131072")
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--modes", type=str, default=",".join(MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--out", type=str, default="")
@@ -293,26 +294,26 @@ def main():
     for n in sorted(bench.contexts):
         secs, k_keep = bench.select(n)
         sel_ms[n] = secs * 1e3
-        for mode in MODES:
+        for mode in [m for m in MODES if m in args.modes.split(",")]:
             c = bench.cell(n, k_keep, mode)
             c["select_ms"] = sel_ms[n] if mode in ("kv", "both") else None
             sweep.append(c)
             print(f"# n={n:6d} {mode:5s} {c['us_per_step']:9.1f} us/step "
                   f"{c['gbs']:7.1f} GB/s ({100 * c['hbm_frac']:.1f}% of peak)", flush=True)
     n_head = max(bench.contexts)
-    head = next(c for c in sweep if c["context"] == n_head and c["mode"] == "both")
-    dense = next(c for c in sweep if c["context"] == n_head and c["mode"] == "dense")
-    kv = next(c for c in sweep if c["context"] == n_head and c["mode"] == "kv")
+    at_head = {c["mode"]: c for c in sweep if c["context"] == n_head}
+    head = at_head.get("both") or next(iter(at_head.values()))
+    dense, kv = at_head.get("dense"), at_head.get("kv")
     k_keep = int(math.floor(bench.wl.keep_ratio * n_head))
     bench.select(n_head)
-    kern = bench.profile_cell(n_head, k_keep, "both")
+    kern = bench.profile_cell(n_head, k_keep, head["mode"])
     dom = max((k for k in kern if "alg_bytes" in kern[k]), key=lambda k: kern[k]["total_ms"])
     dk = kern[dom]
     roof = dict(kernel=dom, bound="hbm", achieved=round(dk["gbs"], 1), peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=round(dk["frac"], 4), avg_us=round(dk["avg_us"], 2),
                 alg_bytes_per_launch=dk["alg_bytes"], traffic=traffic_for(dom))
     payback = None
-    if dense["ms_per_step"] > kv["ms_per_step"]:
+    if dense and kv and dense["ms_per_step"] > kv["ms_per_step"]:
         payback = sel_ms[n_head] / (dense["ms_per_step"] - kv["ms_per_step"])
     cpu = None
     if not args.no_cpu_baseline:

@@ -29,9 +29,9 @@ constexpr int kMaxSplits = 64;         // split-K chunks per KV head (merged in 
 constexpr int kSplitBlocks = 512;      // auto mode: aim for this many split workgroups
 constexpr int kMinChunk = 256;         // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup
-constexpr int kDownTile = 128;         // columns per down-projection tile
-constexpr int kDownRanges = 16;        // channel ranges of the down projection
-constexpr int kMaxDownRange = 2048;    // channels per range the kernel compacts
+constexpr int kDownTile = 512;         // columns per down-projection tile
+constexpr int kDownRanges = 64;        // channel ranges of the down projection
+constexpr int kMaxDownRange = 512;     // channels per range the kernel compacts
 constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in VGPRs
 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
@@ -64,7 +64,7 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.hmid = take(ff * 4);
   L.keep = take(ff);
   L.n_tiles = (int)((d + kDownTile - 1) / kDownTile);
-  L.range_len = (int)(((ff + kDownRanges - 1) / kDownRanges + 63) / 64 * 64);
+  L.range_len = (int)(((ff + kDownRanges - 1) / kDownRanges + 31) / 32 * 32);
   L.n_ranges = (int)((ff + L.range_len - 1) / L.range_len);
   L.down_part = take((size_t)L.n_ranges * d * 4);
   L.counters = take(((size_t)hkv + L.n_tiles) * 4);
@@ -173,7 +173,6 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   g.hmid = reinterpret_cast<float*>(ws + L.hmid);
   g.zero_buf = reinterpret_cast<unsigned*>(ws + L.down_counters);
   g.zero_n = L.n_tiles;
-  g.grid = (dm.d_ff + 15) / 16;  // one block of 4 rows per wave
   g.n_states = 1;
   sd::launch_gate_up(g, dm.w_dtype, s);
 
@@ -341,6 +340,17 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
   float* attn = reinterpret_cast<float*>(wsb + L.attn);
   const int d = dims->d_model, hq = dims->n_q_heads, dh = dims->head_dim, hkv = dims->n_kv_heads;
   const float scale = 1.0f / std::sqrt((float)dh);
+  // RoPE angles pos * theta^(-2i/d_h) in double precision (theta <= 0: identity)
+  sd::RopeTable rope{};
+  for (int i = 0; i < dh / 2; ++i) {
+    rope.c[i] = 1.0f;
+    rope.s[i] = 0.0f;
+    if (dims->rope_theta > 0.f) {
+      const double ang = (double)pos * std::pow((double)dims->rope_theta, -2.0 * i / (double)dh);
+      rope.c[i] = (float)std::cos(ang);
+      rope.s[i] = (float)std::sin(ang);
+    }
+  }
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
     const bool has_sel = l.k_sel != nullptr;
@@ -353,8 +363,7 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     qa.h_q = hq;
     qa.h_kv = hkv;
     qa.dh = dh;
-    qa.theta = dims->rope_theta;
-    qa.pos = pos;
+    qa.rope = rope;
     qa.q_out = q;
     qa.k_full = l.k_full;
     qa.v_full = l.v_full;
@@ -366,7 +375,6 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     qa.row_sel = l.n_sel;
     qa.zero_buf = reinterpret_cast<unsigned*>(wsb + L.attn_counters);  // tickets of this
     qa.zero_n = hkv;                                                    // layer's attention
-    qa.grid = ((hq + 2 * hkv) * dh / 2 + 3) / 4;
     sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
 
     const void* kc = kv_sparse ? l.k_sel : l.k_full;
@@ -376,7 +384,7 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, scale, auto_splits(n_ctx, hkv), attn,
                  nullptr, false, s);
 
-    sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, (d / 2 + 3) / 4, s);
+    sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, s);
 
     uint8_t* keep = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + L.keep);
     enqueue_mlp(*dims, L, wsb, hidden, l.mlp_norm, l.w_gate, l.w_up, l.w_down_t,
@@ -425,7 +433,6 @@ sd_status sd_cats_calibrate(const sd_dims* dims, const float* states, int32_t n_
   g.t = -1.f;
   g.store_abs = 1;
   g.act = vals;
-  g.grid = (dims->d_ff + 15) / 16;
   g.n_states = n_states;
   sd::launch_gate_up(g, dims->w_dtype, s);
   const size_t N = (size_t)n_states * dims->d_ff;

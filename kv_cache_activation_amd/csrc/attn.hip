@@ -5,20 +5,22 @@
 // split-K decoding kernel (§1, §4.1), and §4.4 shows why the dense baseline
 // must be that efficient path.  This is this library's own design for CDNA:
 //
-//   partial kernel, grid (splits, KV heads): a workgroup owns a contiguous
-//   chunk of rows of one KV head and serves all G query heads of the group, so
-//   each K/V byte is read once.  A row of d_h elements is spread over d_h/8
-//   lanes (16-byte loads); the wave holds 64/(d_h/8) rows at once, each lane
-//   group keeping its own online-softmax state (max, sum, acc) in the log2
-//   domain.  Two rows per lane group are in flight per iteration.  At the end
-//   the lane groups and the four waves merge their states and write one
-//   (m, l, acc[d_h]) per query head and split.
+//   one launch, grid (splits, KV heads): a workgroup owns a contiguous chunk
+//   of rows of one KV head and serves all G query heads of the group, so each
+//   K/V byte is read once.  A row of d_h elements is spread over d_h/8 lanes
+//   (16-byte loads); the wave holds 64/(d_h/8) row slots, and each slot keeps
+//   U rows in flight per iteration, so a workgroup streams U*16 consecutive
+//   rows of K and of V per iteration (the chunk is read in address order).
+//   Every lane group keeps its own online-softmax state (max, sum, acc) in the
+//   log2 domain; at the end the groups and the four waves merge their states
+//   and write one (m, l, acc[d_h]) per query head and split.
 //
 //   The last workgroup to finish for a KV head (device-scope ticket counter,
-//   zeroed before the launch) merges that head's split partials:
+//   zeroed before the launch) merges that head's splits:
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2,
-//   splits in order, so the result does not depend on scheduling.  All split
-//   loads of that merge are issued together (at most kMaxSplits per head).
+//   splits in order, so the result does not depend on scheduling.  Partials
+//   travel between workgroups through device-scope coherent stores and loads,
+//   not through a cache-flushing fence.
 #include <math.h>
 
 #include "common.hpp"
@@ -27,11 +29,85 @@
 namespace sd {
 
 constexpr int kAttnThreads = 256;
-constexpr int kMaxSplits = 64;  // splits per KV head (the merge holds them in VGPRs)
+constexpr int kMaxSplits = 64;  // splits per KV head (the merge holds their weights in one wave)
 constexpr int kAttnWaves = kAttnThreads / kWave;
 
-template <typename KT, int DH, int G>
-__global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
+// Merge of the split partials of KV head kv by one workgroup: every load is
+// issued before the first one is consumed (one memory round trip), then
+// out = sum_s w_s acc_s / sum_s w_s l_s with w_s = 2^(m_s - M), in split order.
+template <int G, int DH>
+__device__ __forceinline__ void merge_splits(const float* __restrict__ pm,
+                                             const float* __restrict__ pl,
+                                             const float* __restrict__ pacc, int kv, int n_splits,
+                                             float* __restrict__ out, float* __restrict__ lse,
+                                             float (*w_s)[kMaxSplits], float* inv_l, float* big_m,
+                                             float* big_l) {
+  constexpr int OUTS = G * DH;        // (head, column) outputs of this KV head
+  constexpr int PER = 2;              // outputs per thread and pass
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  // split maxima and sums: wave w handles heads w, w + 4, ...
+  float mi[(G + kAttnWaves - 1) / kAttnWaves], li[(G + kAttnWaves - 1) / kAttnWaves];
+#pragma unroll
+  for (int k = 0; k < (G + kAttnWaves - 1) / kAttnWaves; ++k) {
+    const int g = wave + k * kAttnWaves;
+    const size_t h0 = (size_t)(kv * G + g) * n_splits;
+    const bool ok = g < G && lane < n_splits;
+    mi[k] = ok ? coherent_load(pm + h0 + lane) : -INFINITY;
+    li[k] = ok ? coherent_load(pl + h0 + lane) : 0.f;
+  }
+  float v[PER][kMaxSplits];
+  auto load_pass = [&](int o0) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int o = o0 + k * kAttnThreads;
+      const int g = o / DH, c = o - (o / DH) * DH;
+      const float* base = pacc + (size_t)(kv * G + g) * n_splits * DH + c;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        v[k][sp] = (o < OUTS && sp < n_splits) ? coherent_load(base + (size_t)sp * DH) : 0.f;
+    }
+  };
+  auto finish_pass = [&](int o0) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int o = o0 + k * kAttnThreads;
+      if (o < OUTS) {
+        const int g = o / DH, c = o - (o / DH) * DH;
+        float A = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+          if (sp < n_splits) A = fmaf(w_s[g][sp], v[k][sp], A);
+        out[(size_t)(kv * G + g) * DH + c] = A * inv_l[g];
+        if (lse && c == 0) lse[kv * G + g] = (big_m[g] + log2f(big_l[g])) * 0.69314718055994530942f;
+      }
+    }
+  };
+  load_pass(threadIdx.x);  // first pass in flight while the weights are formed
+#pragma unroll
+  for (int k = 0; k < (G + kAttnWaves - 1) / kAttnWaves; ++k) {
+    const int g = wave + k * kAttnWaves;
+    if (g < G) {  // wave-uniform
+      const float M = wave_max(mi[k]);
+      const float wi = mi[k] == -INFINITY ? 0.f : exp2f(mi[k] - M);
+      const float L = wave_sum(wi * li[k]);
+      if (lane < n_splits) w_s[g][lane] = wi;
+      if (lane == 0) {
+        big_m[g] = M;
+        big_l[g] = L;
+        inv_l[g] = 1.0f / L;
+      }
+    }
+  }
+  __syncthreads();  // every thread of the workgroup reaches this
+  finish_pass(threadIdx.x);
+  for (int o0 = threadIdx.x + PER * kAttnThreads; o0 < OUTS; o0 += PER * kAttnThreads) {
+    load_pass(o0);
+    finish_pass(o0);
+  }
+}
+
+template <typename KT, int DH, int G, int U>
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
     int n_ctx, float scale_log2, int chunk, int n_splits, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ pacc, unsigned* __restrict__ counters,
@@ -39,7 +115,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
-  constexpr int U = 4;                 // rows in flight per slot
   __shared__ float sm_m[kAttnWaves][G], sm_l[kAttnWaves][G];
   __shared__ float sm_acc[kAttnWaves][G][DH];
 
@@ -49,6 +124,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   const int slot = wave * RPW + lane / LPR;
   const int r0 = split * chunk;
   const int r1 = min(n_ctx, r0 + chunk);
+  const KT* Kb = K + (size_t)kv * cap * DH + 8 * sub;
+  const KT* Vb = V + (size_t)kv * cap * DH + 8 * sub;
+
+  // first rows in flight before the query is read
+  Vec8<KT> kr[U], vr[U];
+  int j = r0 + slot;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int jj = j + u * SLOTS;
+    if (jj < r1) {
+      kr[u].load(Kb + (size_t)jj * DH);
+      vr[u].load(Vb + (size_t)jj * DH);
+    }
+  }
 
   float qv[G][8];
 #pragma unroll
@@ -65,24 +154,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
-  const KT* Kb = K + (size_t)kv * cap * DH + 8 * sub;
-  const KT* Vb = V + (size_t)kv * cap * DH + 8 * sub;
 
-  for (int j = r0 + slot; j < r1; j += U * SLOTS) {
-    Vec8<KT> kr[U], vr[U];
-    bool ok[U];
+  for (; j < r1; j += U * SLOTS) {
+    float p[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int jj = j + u * SLOTS;
-      ok[u] = jj < r1;
-      if (ok[u]) {
-        kr[u].load(Kb + (size_t)jj * DH);
-        vr[u].load(Vb + (size_t)jj * DH);
-      }
-    }
-    float sc[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+      const bool ok = j + u * SLOTS < r1;
       float kf[8];
       kr[u].to_float(kf);
 #pragma unroll
@@ -91,40 +168,47 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) t = fmaf(kf[e], qv[g][e], t);
         t = group_sum<LPR>(t);
-        sc[u][g] = ok[u] ? t : -INFINITY;
+        p[u][g] = ok ? t : -INFINITY;
       }
-    }
-    float vf[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      vr[u].to_float(vf[u]);
-      if (!ok[u])
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[u][e] = 0.f;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mb = sc[0][g];
+      float mb = p[0][g];
 #pragma unroll
-      for (int u = 1; u < U; ++u) mb = fmaxf(mb, sc[u][g]);
+      for (int u = 1; u < U; ++u) mb = fmaxf(mb, p[u][g]);
       const float mn = fmaxf(m[g], mb);  // finite: row j itself is valid
       const float alpha = exp2f(m[g] - mn);
-      float p[U];
       float ps = 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        p[u] = exp2f(sc[u][g] - mn);
-        ps += p[u];
+        p[u][g] = exp2f(p[u][g] - mn);
+        ps += p[u][g];
       }
       l[g] = fmaf(l[g], alpha, ps);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = acc[g][e] * alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) a = fmaf(p[u], vf[u][e], a);
-        acc[g][e] = a;
-      }
+      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
       m[g] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      vr[u].to_float(vf);
+      if (!(j + u * SLOTS < r1))
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = 0.f;  // never loaded: keep NaN/Inf out
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
+    }
+    // next rows
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j + U * SLOTS + u * SLOTS;
+      if (jj < r1) {
+        kr[u].load(Kb + (size_t)jj * DH);
+        vr[u].load(Vb + (size_t)jj * DH);
+      }
     }
   }
 
@@ -172,77 +256,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
       A = fmaf(sm_acc[w][g][c], a, A);
     }
     const size_t hs = (size_t)(kv * G + g) * n_splits + split;
-    pacc[hs * DH + c] = A;
+    coherent_store(pacc + hs * DH + c, A);
     if (c == 0) {
-      pm[hs] = M;
-      pl[hs] = L;
+      coherent_store(pm + hs, M);
+      coherent_store(pl + hs, L);
     }
   }
 
   // ---- last workgroup of this KV head merges all splits
   __shared__ int last_s;
-  __shared__ float w_s[G][kMaxSplits], l_s[G][kMaxSplits];
-  __shared__ float big_m[G], big_l[G];
-  __threadfence();
+  __shared__ float w_s[G][kMaxSplits];
+  __shared__ float inv_l[G], big_m[G], big_l[G];
+  stores_done();
   __syncthreads();
-  if (threadIdx.x == 0) last_s = atomicAdd(&counters[kv], 1u) == (unsigned)(n_splits - 1);
+  if (threadIdx.x == 0) last_s = last_arrival(&counters[kv], (unsigned)n_splits);
   __syncthreads();
   if (!last_s) return;
-  __threadfence();
-  for (int t = threadIdx.x; t < G * n_splits; t += kAttnThreads) {
-    const int g = t / n_splits, sp = t - g * n_splits;
-    const size_t hs = (size_t)(kv * G + g) * n_splits + sp;
-    w_s[g][sp] = __builtin_nontemporal_load(pm + hs);
-    l_s[g][sp] = __builtin_nontemporal_load(pl + hs);
-  }
-  __syncthreads();
-  for (int g = wave; g < G; g += kAttnWaves) {
-    const float mi = lane < n_splits ? w_s[g][lane] : -INFINITY;
-    const float M = wave_max(mi);
-    const float wi = mi == -INFINITY ? 0.f : exp2f(mi - M);
-    const float L = wave_sum(lane < n_splits ? wi * l_s[g][lane] : 0.f);
-    if (lane < n_splits) w_s[g][lane] = wi;
-    if (lane == 0) {
-      big_m[g] = M;
-      big_l[g] = L;
-    }
-  }
-  __syncthreads();
-  // thread (split group sg, column quad cq) accumulates its splits' float4s of
-  // every head; then the split groups are summed through LDS in group order
-  constexpr int NQ = DH / 4;                 // float4 column quads per row
-  constexpr int GROUPS = kAttnThreads / NQ;  // split groups
-  constexpr int ITERS = kMaxSplits / GROUPS;
-  const int cq = threadIdx.x % NQ, sg = threadIdx.x / NQ;
-  __shared__ float red[GROUPS * G * DH];
-  for (int g = 0; g < G; ++g) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    f32x4 v[ITERS];
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int sp = sg + it * GROUPS;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      v[it] = sp < n_splits ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-                                  pacc + ((size_t)(kv * G + g) * n_splits + sp) * DH) + cq)
-                            : z;
-    }
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int sp = sg + it * GROUPS;
-      if (sp < n_splits) a += w_s[g][sp] * v[it];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[sg * G * DH + g * DH + 4 * cq + e] = a[e];
-  }
-  __syncthreads();
-  for (int o = threadIdx.x; o < G * DH; o += kAttnThreads) {
-    const int g = o / DH, c = o - g * DH;
-    float A = 0.f;
-#pragma unroll
-    for (int grp = 0; grp < GROUPS; ++grp) A += red[grp * G * DH + o];
-    out[(size_t)(kv * G + g) * DH + c] = A / big_l[g];
-    if (lse && c == 0) lse[kv * G + g] = (big_m[g] + log2f(big_l[g])) * 0.69314718055994530942f;
-  }
+  merge_splits<G, DH>(pm, pl, pacc, kv, n_splits, out, lse, w_s, inv_l, big_m, big_l);
 }
 
 __global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
@@ -257,16 +287,16 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
   if (a.zero_counters) zero_u32_kernel<<<1, 64, 0, s>>>(a.counters, a.h_kv);
-#define SD_ATTN_G(GG)                                                                      \
-  attn_partial_kernel<KT, DH, GG><<<grid, kAttnThreads, 0, s>>>(                           \
+#define SD_ATTN_G(GG, UU)                                                                   \
+  attn_kernel<KT, DH, GG, UU><<<grid, kAttnThreads, 0, s>>>(                               \
       a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc,      \
       a.counters, a.out, a.lse)
   ProfScope prof(K_ATTN_PARTIAL, s);
   switch (G) {
-    case 1: SD_ATTN_G(1); break;
-    case 2: SD_ATTN_G(2); break;
-    case 4: SD_ATTN_G(4); break;
-    default: SD_ATTN_G(8); break;
+    case 1: SD_ATTN_G(1, 8); break;
+    case 2: SD_ATTN_G(2, 8); break;
+    case 4: SD_ATTN_G(4, 8); break;
+    default: SD_ATTN_G(8, 4); break;
   }
 #undef SD_ATTN_G
 }

@@ -7,19 +7,19 @@
 // stored transposed, w_down_t [d_ff, d], so one kept channel is one contiguous
 // row of d elements.
 //
-// Grid: (128-column tiles) x (channel ranges, at most 32).  A workgroup
+// Grid: (512-column tiles) x (channel ranges).  A workgroup
 //   1. compacts the kept channels of its range into an ascending LDS list with
 //      wave ballots and popcount prefixes (the keep bytes come from the gate
-//      kernel; all of them are loaded in one round),
-//   2. streams its 256-byte segment of each kept row (one 16-byte load per
-//      lane, eight rows in flight per lane) and accumulates hmid_i * w_down_t[i],
-//   3. writes a partial sum for (range, tile); the last workgroup to finish a
-//      tile (device-scope counter) adds the partials of all ranges in range
-//      order, so the result is deterministic, and writes y (or y += result).
-// Few ranges keep that final sum to one round of loads; many tiles keep the
-// grid wide enough to fill the chip.
-// Column-tile workgroups of range r also emit that range's part of the global
-// ascending kept list at offset popcount(keep[0 .. range start)).
+//      kernel),
+//   2. streams the 1 KB segment (one 16-byte load per lane) of each kept row
+//      that falls in its tile, eight rows in flight per wave, accumulating
+//      hmid_i * w_down_t[i],
+//   3. hands a partial sum for (range, tile) to the last workgroup to finish
+//      the tile (device-scope ticket counter and coherent stores), which adds
+//      the partials of all ranges in range order -- deterministic -- and writes
+//      y (or y += result).
+// Column-tile-0 workgroups of range r also emit that range's part of the
+// global ascending kept list at offset popcount(keep[0 .. range start)).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -27,8 +27,9 @@ namespace sd {
 
 constexpr int kDownThreads = 256;
 constexpr int kDownWaves = kDownThreads / kWave;
-constexpr int kMaxRanges = 32;   // channel ranges per call (the final sum holds them in VGPRs)
-constexpr int kDownTile = 128;   // columns per tile: 16 lanes x 8 columns
+constexpr int kDownTile = 512;   // columns per tile: 64 lanes x 8 columns
+constexpr int kDownRounds = 2;   // range_len <= 512 = kDownRounds * kDownThreads
+constexpr int kDownMaxRanges = 64;  // channel ranges per call (the tail sum holds them in VGPRs)
 
 // Block-wide exclusive prefix count of `flag` in thread order, and the total.
 __device__ __forceinline__ int down_prefix(bool flag, int* wave_tot, int& total) {
@@ -53,11 +54,9 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
     const float* __restrict__ hmid, int range_len, int n_ranges, float* __restrict__ partials,
     unsigned* __restrict__ counters, float* __restrict__ y, int accumulate,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ n_kept_out) {
-  constexpr int LPR = kDownTile / 8;      // lanes per row segment
-  constexpr int RPW = kWave / LPR;        // row slots per wave
-  constexpr int SLOTS = kDownWaves * RPW; // row slots per workgroup
-  constexpr int U = 8;                    // rows in flight per slot
-  extern __shared__ int list[];           // [range_len]
+  constexpr int U = 8;  // rows in flight per wave
+  __shared__ int list[kDownRounds * kDownThreads];
+  __shared__ float hv_s[kDownRounds * kDownThreads];
   __shared__ float red[kDownWaves][kDownTile];
   __shared__ int wave_tot[kDownWaves];
   __shared__ int last_s, prefix_s;
@@ -67,63 +66,54 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   const int i1 = min(dff, i0 + range_len);
   const int lane = lane_id(), wave = threadIdx.x / kWave;
 
-  // ascending list of the kept channels of [i0, i1): all flags loaded at once,
-  // then one ballot prefix per 256-channel round
-  constexpr int kRounds = 8;  // range_len <= 2048
-  bool f[kRounds];
+  // ascending list of the kept channels of [i0, i1), with their hmid values
+  bool f[kDownRounds];
 #pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
+  for (int r = 0; r < kDownRounds; ++r) {
     const int i = i0 + r * kDownThreads + threadIdx.x;
     f[r] = i < i1 && keep[i] != 0;
   }
   int cnt = 0;
 #pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
+  for (int r = 0; r < kDownRounds; ++r) {
     if (i0 + r * kDownThreads >= i1) break;
     int tot;
     const int pos = cnt + down_prefix(f[r], wave_tot, tot);
-    if (f[r]) list[pos] = i0 + r * kDownThreads + threadIdx.x;
+    if (f[r]) {
+      const int i = i0 + r * kDownThreads + threadIdx.x;
+      list[pos] = i;
+      hv_s[pos] = hmid[i];
+    }
     cnt += tot;
   }
   __syncthreads();
 
-  const int slot = wave * RPW + lane / LPR;
-  const int col = tile * kDownTile + 8 * (lane % LPR);
+  const int col = tile * kDownTile + 8 * lane;
   const bool col_ok = col < d;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int j = slot; j < cnt; j += U * SLOTS) {
+  for (int j = wave; j < cnt; j += U * kDownWaves) {
     Vec8<WT> w[U];
-    float hv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int jj = j + u * SLOTS;
-      hv[u] = 0.f;
-      if (jj < cnt && col_ok) {
-        const int i = list[jj];
-        hv[u] = hmid[i];
-        w[u].load(Wd + (size_t)i * d + col);
-      }
+      const int jj = j + u * kDownWaves;
+      if (jj < cnt && col_ok) w[u].load(Wd + (size_t)list[jj] * d + col);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (j + u * SLOTS < cnt && col_ok) {
+      const int jj = j + u * kDownWaves;
+      if (jj < cnt && col_ok) {
+        const float hv = hv_s[jj];
         float fw[8];
         w[u].to_float(fw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv[u], fw[e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv, fw[e], acc[e]);
       }
     }
   }
-  // row slots of a wave -> one sum per column (lanes 0..LPR-1)
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
-  if (lane < LPR)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
+  for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
   __syncthreads();
   for (int c = threadIdx.x; c < kDownTile; c += kDownThreads) {
     const int gc = tile * kDownTile + c;
@@ -131,27 +121,35 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < kDownWaves; ++w) sum += red[w][c];
-      partials[(size_t)range * d + gc] = sum;
+      coherent_store(partials + (size_t)range * d + gc, sum);
     }
   }
-  __threadfence();
+  stores_done();
   __syncthreads();
-  if (threadIdx.x == 0) last_s = atomicAdd(&counters[tile], 1u) == (unsigned)(n_ranges - 1);
+  if (threadIdx.x == 0) last_s = last_arrival(&counters[tile], (unsigned)n_ranges);
   __syncthreads();
   if (last_s) {
-    // last workgroup of this tile: sum the ranges in order, all loads at once
-    __threadfence();
-    for (int c = threadIdx.x; c < kDownTile; c += kDownThreads) {
-      const int gc = tile * kDownTile + c;
-      if (gc < d) {
-        float v[kMaxRanges];
+    // last workgroup of this tile: each thread sums two columns over all ranges
+    // in range order, every load issued before the first one is consumed
+    for (int c0 = threadIdx.x; c0 < kDownTile; c0 += 2 * kDownThreads) {
+      float v[2][kDownMaxRanges];
 #pragma unroll
-        for (int r = 0; r < kMaxRanges; ++r)
-          v[r] = r < n_ranges ? __builtin_nontemporal_load(partials + (size_t)r * d + gc) : 0.f;
-        float sum = 0.f;
+      for (int k = 0; k < 2; ++k) {
+        const int gc = tile * kDownTile + c0 + k * kDownThreads;
 #pragma unroll
-        for (int r = 0; r < kMaxRanges; ++r) sum += v[r];
-        y[gc] = accumulate ? y[gc] + sum : sum;
+        for (int r = 0; r < kDownMaxRanges; ++r)
+          v[k][r] = (gc < d && r < n_ranges) ? coherent_load(partials + (size_t)r * d + gc) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int gc = tile * kDownTile + c0 + k * kDownThreads;
+        if (gc < d) {
+          float sum = 0.f;
+#pragma unroll
+          for (int r = 0; r < kDownMaxRanges; ++r)
+            if (r < n_ranges) sum += v[k][r];
+          y[gc] = accumulate ? y[gc] + sum : sum;
+        }
       }
     }
   }
@@ -161,7 +159,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
     int c = 0;
     const uint32_t* kw = reinterpret_cast<const uint32_t*>(keep);
     for (int q = threadIdx.x; q < i0 / 4; q += kDownThreads) c += (int)((kw[q] * 0x01010101u) >> 24);
-    for (int off = 1; off < kWave; off <<= 1) c += __shfl_xor(c, off);
+    c = wave_sum_int(c);
     if (threadIdx.x == 0) prefix_s = 0;
     __syncthreads();
     if (lane == 0) atomicAdd(&prefix_s, c);
@@ -175,12 +173,11 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
 template <typename WT>
 static void down_typed(const DownArgs& a, hipStream_t s) {
   dim3 grid(a.n_tiles, a.n_ranges);
-  size_t lds = (size_t)a.range_len * sizeof(int);
   ProfScope prof(K_DOWN, s);
-  down_kernel<WT><<<grid, kDownThreads, lds, s>>>((const WT*)a.w_down_t, a.d, a.dff, a.keep,
-                                                  a.hmid, a.range_len, a.n_ranges, a.partials,
-                                                  a.counters, a.y, a.accumulate, a.idx_out,
-                                                  a.n_kept_out);
+  down_kernel<WT><<<grid, kDownThreads, 0, s>>>((const WT*)a.w_down_t, a.d, a.dff, a.keep,
+                                                a.hmid, a.range_len, a.n_ranges, a.partials,
+                                                a.counters, a.y, a.accumulate, a.idx_out,
+                                                a.n_kept_out);
 }
 
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s) {

@@ -24,14 +24,19 @@ struct ProfScope {
   ~ProfScope();
 };
 
+// cos and sin of the rotation angle of each RoPE pair index (d_h / 2 <= 64)
+struct RopeTable {
+  float c[64];
+  float s[64];
+};
+
 struct QkvArgs {
   const float* h;
   const float* norm;
   float eps;
   const void* w;
   int d, h_q, h_kv, dh;
-  float theta;
-  int pos;
+  RopeTable rope;
   float* q_out;
   void* k_full;
   void* v_full;
@@ -41,7 +46,6 @@ struct QkvArgs {
   int cap_sel, row_sel;
   unsigned* zero_buf;
   int zero_n;
-  int grid;
 };
 
 struct GateUpArgs {
@@ -58,7 +62,6 @@ struct GateUpArgs {
   float* hmid;
   unsigned* zero_buf;
   int zero_n;
-  int grid;
   int n_states;       // batched gate for calibration; 1 otherwise
 };
 
@@ -111,7 +114,7 @@ struct SelectArgs {
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s);
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,
-              int grid, hipStream_t s);
+              hipStream_t s);
 void launch_gate_up(const GateUpArgs& a, int w_dtype, hipStream_t s);
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s);
