@@ -141,7 +141,7 @@ sd_status sd_select_kv(const sd_dims* dims, const void* k_full, const void* v_fu
  * lse    [h_q] float32 log-sum-exp of the scaled logits, or NULL.
  * n_splits  chunks of the row range per KV head (at most 64), 0 = chosen by
  *           the library; the result depends on it only through float32
- *           rounding.  The last workgroup of each KV head merges the chunks.
+ *           rounding.  A second launch merges the chunks in chunk order.
  * Errors: EINVAL unless 1 <= n_ctx <= cap; ENOSPC for a short workspace or
  *         n_splits above 64.
  */

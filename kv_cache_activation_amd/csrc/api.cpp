@@ -25,7 +25,7 @@ sd_status fail(sd_status st, const char* fmt, ...) {
 
 bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxSplits = 64;         // split-K chunks per KV head (merged in VGPRs)
+constexpr int kMaxSplits = 64;         // split-K chunks per KV head (the merge holds them in VGPRs)
 constexpr int kSplitBlocks = 512;      // auto mode: aim for this many split workgroups
 constexpr int kMinChunk = 256;         // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup
@@ -37,9 +37,8 @@ constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, counters, lse_part, lse;
+  size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, lse_part, lse;
   size_t kth_hist, kth_state, total;
-  size_t attn_counters, down_counters;
   int max_splits, n_tiles, n_ranges, range_len, sel_chunks;
 };
 
@@ -67,9 +66,6 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.range_len = (int)(((ff + kDownRanges - 1) / kDownRanges + 31) / 32 * 32);
   L.n_ranges = (int)((ff + L.range_len - 1) / L.range_len);
   L.down_part = take((size_t)L.n_ranges * d * 4);
-  L.counters = take(((size_t)hkv + L.n_tiles) * 4);
-  L.attn_counters = L.counters;
-  L.down_counters = L.counters + hkv * 4;
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
   L.lse = take(hq * (size_t)max_window * 4);
@@ -130,7 +126,7 @@ int auto_splits(int n_ctx, int h_kv) {
 // Enqueue split-K attention; ws must hold the layout's attention buffers.
 void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, const void* k,
                   const void* v, int cap, int n_ctx, float scale, int n_splits, float* out,
-                  float* lse, bool zero_counters, hipStream_t s) {
+                  float* lse, hipStream_t s) {
   sd::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -146,8 +142,6 @@ void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, 
   a.pm = reinterpret_cast<float*>(ws + L.pm);
   a.pl = reinterpret_cast<float*>(ws + L.pl);
   a.pacc = reinterpret_cast<float*>(ws + L.pacc);
-  a.counters = reinterpret_cast<unsigned*>(ws + L.attn_counters);
-  a.zero_counters = zero_counters;
   a.out = out;
   a.lse = lse;
   sd::launch_attn(a, dm.kv_dtype, s);
@@ -171,8 +165,6 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   g.act = act;
   g.keep = keep;
   g.hmid = reinterpret_cast<float*>(ws + L.hmid);
-  g.zero_buf = reinterpret_cast<unsigned*>(ws + L.down_counters);
-  g.zero_n = L.n_tiles;
   g.n_states = 1;
   sd::launch_gate_up(g, dm.w_dtype, s);
 
@@ -186,7 +178,6 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   dn.n_ranges = L.n_ranges;
   dn.n_tiles = L.n_tiles;
   dn.partials = reinterpret_cast<float*>(ws + L.down_part);
-  dn.counters = g.zero_buf;
   dn.y = y;
   dn.accumulate = accumulate;
   dn.idx_out = idx;
@@ -278,7 +269,7 @@ sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, con
   if (n_splits > L.max_splits)
     return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
   int s = n_splits ? (n_splits < n_ctx ? n_splits : n_ctx) : auto_splits(n_ctx, dims->n_kv_heads);
-  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, scale, s, out, lse, true,
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, scale, s, out, lse,
                static_cast<hipStream_t>(stream));
   return check_launch("sd_decode_attn");
 }
@@ -373,8 +364,6 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     qa.v_sel = has_sel ? l.v_sel : nullptr;
     qa.cap_sel = l.cap_sel;
     qa.row_sel = l.n_sel;
-    qa.zero_buf = reinterpret_cast<unsigned*>(wsb + L.attn_counters);  // tickets of this
-    qa.zero_n = hkv;                                                    // layer's attention
     sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
 
     const void* kc = kv_sparse ? l.k_sel : l.k_full;
@@ -382,7 +371,7 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     const int cap = kv_sparse ? l.cap_sel : l.cap_full;
     const int n_ctx = (kv_sparse ? l.n_sel : l.n_full) + 1;
     enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, scale, auto_splits(n_ctx, hkv), attn,
-                 nullptr, false, s);
+                 nullptr, s);
 
     sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, s);
 

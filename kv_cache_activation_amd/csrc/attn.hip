@@ -15,12 +15,13 @@
 //   log2 domain; at the end the groups and the four waves merge their states
 //   and write one (m, l, acc[d_h]) per query head and split.
 //
-//   The last workgroup to finish for a KV head (device-scope ticket counter,
-//   zeroed before the launch) merges that head's splits:
+//   A second, small launch merges the splits, one workgroup per query head:
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2,
-//   splits in order, so the result does not depend on scheduling.  Partials
-//   travel between workgroups through device-scope coherent stores and loads,
-//   not through a cache-flushing fence.
+//   splits in order, so the result does not depend on scheduling.  The launch
+//   boundary makes the partials visible to every XCD; measured on MI355X it is
+//   cheaper than a hand-off inside one launch (coherent stores, a wait for
+//   their acknowledgement, a ticket and coherent loads are three memory round
+//   trips).
 #include <math.h>
 
 #include "common.hpp"
@@ -32,86 +33,11 @@ constexpr int kAttnThreads = 256;
 constexpr int kMaxSplits = 64;  // splits per KV head (the merge holds their weights in one wave)
 constexpr int kAttnWaves = kAttnThreads / kWave;
 
-// Merge of the split partials of KV head kv by one workgroup: every load is
-// issued before the first one is consumed (one memory round trip), then
-// out = sum_s w_s acc_s / sum_s w_s l_s with w_s = 2^(m_s - M), in split order.
-template <int G, int DH>
-__device__ __forceinline__ void merge_splits(const float* __restrict__ pm,
-                                             const float* __restrict__ pl,
-                                             const float* __restrict__ pacc, int kv, int n_splits,
-                                             float* __restrict__ out, float* __restrict__ lse,
-                                             float (*w_s)[kMaxSplits], float* inv_l, float* big_m,
-                                             float* big_l) {
-  constexpr int OUTS = G * DH;        // (head, column) outputs of this KV head
-  constexpr int PER = 2;              // outputs per thread and pass
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  // split maxima and sums: wave w handles heads w, w + 4, ...
-  float mi[(G + kAttnWaves - 1) / kAttnWaves], li[(G + kAttnWaves - 1) / kAttnWaves];
-#pragma unroll
-  for (int k = 0; k < (G + kAttnWaves - 1) / kAttnWaves; ++k) {
-    const int g = wave + k * kAttnWaves;
-    const size_t h0 = (size_t)(kv * G + g) * n_splits;
-    const bool ok = g < G && lane < n_splits;
-    mi[k] = ok ? coherent_load(pm + h0 + lane) : -INFINITY;
-    li[k] = ok ? coherent_load(pl + h0 + lane) : 0.f;
-  }
-  float v[PER][kMaxSplits];
-  auto load_pass = [&](int o0) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int o = o0 + k * kAttnThreads;
-      const int g = o / DH, c = o - (o / DH) * DH;
-      const float* base = pacc + (size_t)(kv * G + g) * n_splits * DH + c;
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp)
-        v[k][sp] = (o < OUTS && sp < n_splits) ? coherent_load(base + (size_t)sp * DH) : 0.f;
-    }
-  };
-  auto finish_pass = [&](int o0) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int o = o0 + k * kAttnThreads;
-      if (o < OUTS) {
-        const int g = o / DH, c = o - (o / DH) * DH;
-        float A = 0.f;
-#pragma unroll
-        for (int sp = 0; sp < kMaxSplits; ++sp)
-          if (sp < n_splits) A = fmaf(w_s[g][sp], v[k][sp], A);
-        out[(size_t)(kv * G + g) * DH + c] = A * inv_l[g];
-        if (lse && c == 0) lse[kv * G + g] = (big_m[g] + log2f(big_l[g])) * 0.69314718055994530942f;
-      }
-    }
-  };
-  load_pass(threadIdx.x);  // first pass in flight while the weights are formed
-#pragma unroll
-  for (int k = 0; k < (G + kAttnWaves - 1) / kAttnWaves; ++k) {
-    const int g = wave + k * kAttnWaves;
-    if (g < G) {  // wave-uniform
-      const float M = wave_max(mi[k]);
-      const float wi = mi[k] == -INFINITY ? 0.f : exp2f(mi[k] - M);
-      const float L = wave_sum(wi * li[k]);
-      if (lane < n_splits) w_s[g][lane] = wi;
-      if (lane == 0) {
-        big_m[g] = M;
-        big_l[g] = L;
-        inv_l[g] = 1.0f / L;
-      }
-    }
-  }
-  __syncthreads();  // every thread of the workgroup reaches this
-  finish_pass(threadIdx.x);
-  for (int o0 = threadIdx.x + PER * kAttnThreads; o0 < OUTS; o0 += PER * kAttnThreads) {
-    load_pass(o0);
-    finish_pass(o0);
-  }
-}
-
 template <typename KT, int DH, int G, int U>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
     int n_ctx, float scale_log2, int chunk, int n_splits, float* __restrict__ pm,
-    float* __restrict__ pl, float* __restrict__ pacc, unsigned* __restrict__ counters,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ pl, float* __restrict__ pacc) {
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
@@ -256,27 +182,52 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       A = fmaf(sm_acc[w][g][c], a, A);
     }
     const size_t hs = (size_t)(kv * G + g) * n_splits + split;
-    coherent_store(pacc + hs * DH + c, A);
+    pacc[hs * DH + c] = A;
     if (c == 0) {
-      coherent_store(pm + hs, M);
-      coherent_store(pl + hs, L);
+      pm[hs] = M;
+      pl[hs] = L;
     }
   }
-
-  // ---- last workgroup of this KV head merges all splits
-  __shared__ int last_s;
-  __shared__ float w_s[G][kMaxSplits];
-  __shared__ float inv_l[G], big_m[G], big_l[G];
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) last_s = last_arrival(&counters[kv], (unsigned)n_splits);
-  __syncthreads();
-  if (!last_s) return;
-  merge_splits<G, DH>(pm, pl, pacc, kv, n_splits, out, lse, w_s, inv_l, big_m, big_l);
 }
 
-__global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+// One workgroup per query head, one thread per column: every split's value of
+// the thread's column is loaded before the first is used (one memory round
+// trip); wave 0 turns the split maxima into weights.
+template <int DH>
+__global__ __launch_bounds__(DH) void attn_merge_kernel(const float* __restrict__ pm,
+                                                        const float* __restrict__ pl,
+                                                        const float* __restrict__ pacc,
+                                                        int n_splits, float* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float inv_l, big_m, big_l;
+  const int h = blockIdx.x, c = threadIdx.x;
+  const float* base = pacc + (size_t)h * n_splits * DH + c;
+  float v[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    v[sp] = sp < n_splits ? base[(size_t)sp * DH] : 0.f;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const float mi = lane < n_splits ? pm[(size_t)h * n_splits + lane] : -INFINITY;
+    const float li = lane < n_splits ? pl[(size_t)h * n_splits + lane] : 0.f;
+    const float M = wave_max(mi);
+    const float wi = mi == -INFINITY ? 0.f : exp2f(mi - M);
+    const float L = wave_sum(wi * li);
+    w_s[lane] = wi;
+    if (lane == 0) {
+      big_m = M;
+      big_l = L;
+      inv_l = 1.0f / L;
+    }
+  }
+  __syncthreads();
+  float A = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < n_splits) A = fmaf(w_s[sp], v[sp], A);
+  out[(size_t)h * DH + c] = A * inv_l;
+  if (lse && c == 0) lse[h] = (big_m + log2f(big_l)) * 0.69314718055994530942f;
 }
 
 template <typename KT, int DH>
@@ -286,19 +237,21 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_splits, a.h_kv);
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
-  if (a.zero_counters) zero_u32_kernel<<<1, 64, 0, s>>>(a.counters, a.h_kv);
 #define SD_ATTN_G(GG, UU)                                                                   \
   attn_kernel<KT, DH, GG, UU><<<grid, kAttnThreads, 0, s>>>(                               \
-      a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc,      \
-      a.counters, a.out, a.lse)
-  ProfScope prof(K_ATTN_PARTIAL, s);
-  switch (G) {
-    case 1: SD_ATTN_G(1, 8); break;
-    case 2: SD_ATTN_G(2, 8); break;
-    case 4: SD_ATTN_G(4, 8); break;
-    default: SD_ATTN_G(8, 4); break;
+      a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
+  {
+    ProfScope prof(K_ATTN_PARTIAL, s);
+    switch (G) {
+      case 1: SD_ATTN_G(1, 8); break;
+      case 2: SD_ATTN_G(2, 8); break;
+      case 4: SD_ATTN_G(4, 8); break;
+      default: SD_ATTN_G(8, 4); break;
+    }
   }
 #undef SD_ATTN_G
+  ProfScope prof(K_ATTN_COMBINE, s);
+  attn_merge_kernel<DH><<<a.h_q, DH, 0, s>>>(a.pm, a.pl, a.pacc, a.n_splits, a.out, a.lse);
 }
 
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s) {

@@ -135,28 +135,6 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// ---------------------------------------------------------------- cross-block hand-off
-// Each XCD of the chip has its own L2, and plain stores may sit in one XCD's L2
-// where another XCD cannot see them.  Values that one workgroup hands to another
-// within a launch go through device-scope accesses instead: relaxed atomic
-// stores and loads at agent scope, which the hardware makes coherent across
-// XCDs per access, so no whole-cache writeback fence is needed.
-//   writer: coherent_store(...) ...; stores_done(); __syncthreads(); ticket;
-//   reader: (after seeing the last ticket) coherent_load(...)
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until every memory access this wave issued has completed (for stores:
-// acknowledged at the scope they were issued with).
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Take a ticket on a device-scope counter; true for the `n`-th (last) arrival.
-__device__ __forceinline__ bool last_arrival(unsigned* counter, unsigned n) {
-  return atomicAdd(counter, 1u) == n - 1u;
-}
-
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 }  // namespace sd

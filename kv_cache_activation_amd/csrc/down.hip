@@ -9,15 +9,18 @@
 //
 // Grid: (512-column tiles) x (channel ranges).  A workgroup
 //   1. compacts the kept channels of its range into an ascending LDS list with
-//      wave ballots and popcount prefixes (the keep bytes come from the gate
-//      kernel),
+//      wave ballots and popcount prefixes (the keep bytes and the hmid values
+//      of the range come from the gate kernel, loaded in one round),
 //   2. streams the 1 KB segment (one 16-byte load per lane) of each kept row
-//      that falls in its tile, eight rows in flight per wave, accumulating
-//      hmid_i * w_down_t[i],
-//   3. hands a partial sum for (range, tile) to the last workgroup to finish
-//      the tile (device-scope ticket counter and coherent stores), which adds
-//      the partials of all ranges in range order -- deterministic -- and writes
-//      y (or y += result).
+//      that falls in its tile, in groups of eight rows per wave with the next
+//      group's loads issued before the current group's arithmetic,
+//      accumulating hmid_i * w_down_t[i],
+//   3. writes a partial sum for (range, tile).
+// A second launch adds the partials of all ranges in range order --
+// deterministic -- and writes y (or y += result): one thread per column, every
+// range's value loaded before the first is used.  The launch boundary makes
+// the partials visible to every XCD, which on MI355X costs less than a
+// hand-off inside one launch.
 // Column-tile-0 workgroups of range r also emit that range's part of the
 // global ascending kept list at offset popcount(keep[0 .. range start)).
 #include "common.hpp"
@@ -52,14 +55,13 @@ template <typename WT>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(
     const WT* __restrict__ Wd, int d, int dff, const uint8_t* __restrict__ keep,
     const float* __restrict__ hmid, int range_len, int n_ranges, float* __restrict__ partials,
-    unsigned* __restrict__ counters, float* __restrict__ y, int accumulate,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ n_kept_out) {
   constexpr int U = 8;  // rows in flight per wave
   __shared__ int list[kDownRounds * kDownThreads];
   __shared__ float hv_s[kDownRounds * kDownThreads];
   __shared__ float red[kDownWaves][kDownTile];
   __shared__ int wave_tot[kDownWaves];
-  __shared__ int last_s, prefix_s;
+  __shared__ int prefix_s;
 
   const int tile = blockIdx.x, range = blockIdx.y;
   const int i0 = range * range_len;
@@ -67,11 +69,18 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   const int lane = lane_id(), wave = threadIdx.x / kWave;
 
   // ascending list of the kept channels of [i0, i1), with their hmid values
+  // (hmid of a dropped channel is stale and never used)
   bool f[kDownRounds];
+  float hv[kDownRounds];
 #pragma unroll
   for (int r = 0; r < kDownRounds; ++r) {
     const int i = i0 + r * kDownThreads + threadIdx.x;
-    f[r] = i < i1 && keep[i] != 0;
+    f[r] = false;
+    hv[r] = 0.f;
+    if (i < i1) {
+      f[r] = keep[i] != 0;
+      hv[r] = hmid[i];
+    }
   }
   int cnt = 0;
 #pragma unroll
@@ -80,9 +89,8 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
     int tot;
     const int pos = cnt + down_prefix(f[r], wave_tot, tot);
     if (f[r]) {
-      const int i = i0 + r * kDownThreads + threadIdx.x;
-      list[pos] = i;
-      hv_s[pos] = hmid[i];
+      list[pos] = i0 + r * kDownThreads + threadIdx.x;
+      hv_s[pos] = hv[r];
     }
     cnt += tot;
   }
@@ -93,24 +101,40 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int j = wave; j < cnt; j += U * kDownWaves) {
-    Vec8<WT> w[U];
+  // rows j0 + u*kDownWaves (u < U) form a group of this wave
+  auto load_group = [&](Vec8<WT> (&w)[U], int j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int jj = j + u * kDownWaves;
+      const int jj = j0 + u * kDownWaves;
       if (jj < cnt && col_ok) w[u].load(Wd + (size_t)list[jj] * d + col);
     }
+  };
+  auto use_group = [&](const Vec8<WT> (&w)[U], int j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int jj = j + u * kDownWaves;
+      const int jj = j0 + u * kDownWaves;
       if (jj < cnt && col_ok) {
-        const float hv = hv_s[jj];
+        const float h = hv_s[jj];
         float fw[8];
         w[u].to_float(fw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv, fw[e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(h, fw[e], acc[e]);
       }
     }
+  };
+  constexpr int STEP = U * kDownWaves;
+  Vec8<WT> wa[U], wb[U];
+  int j0 = wave;
+  if (j0 < cnt) load_group(wa, j0);
+  while (j0 < cnt) {
+    const int j1 = j0 + STEP;
+    if (j1 < cnt) load_group(wb, j1);
+    use_group(wa, j0);
+    if (j1 >= cnt) break;
+    const int j2 = j1 + STEP;
+    if (j2 < cnt) load_group(wa, j2);
+    use_group(wb, j1);
+    j0 = j2;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
@@ -121,36 +145,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < kDownWaves; ++w) sum += red[w][c];
-      coherent_store(partials + (size_t)range * d + gc, sum);
-    }
-  }
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) last_s = last_arrival(&counters[tile], (unsigned)n_ranges);
-  __syncthreads();
-  if (last_s) {
-    // last workgroup of this tile: each thread sums two columns over all ranges
-    // in range order, every load issued before the first one is consumed
-    for (int c0 = threadIdx.x; c0 < kDownTile; c0 += 2 * kDownThreads) {
-      float v[2][kDownMaxRanges];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int gc = tile * kDownTile + c0 + k * kDownThreads;
-#pragma unroll
-        for (int r = 0; r < kDownMaxRanges; ++r)
-          v[k][r] = (gc < d && r < n_ranges) ? coherent_load(partials + (size_t)r * d + gc) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int gc = tile * kDownTile + c0 + k * kDownThreads;
-        if (gc < d) {
-          float sum = 0.f;
-#pragma unroll
-          for (int r = 0; r < kDownMaxRanges; ++r)
-            if (r < n_ranges) sum += v[k][r];
-          y[gc] = accumulate ? y[gc] + sum : sum;
-        }
-      }
+      partials[(size_t)range * d + gc] = sum;
     }
   }
 
@@ -170,14 +165,35 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   }
 }
 
+// y[c] (+)= sum over ranges r, in order, of partials[r][c]
+__global__ __launch_bounds__(256) void down_reduce_kernel(const float* __restrict__ partials,
+                                                          int d, int n_ranges,
+                                                          float* __restrict__ y, int accumulate) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  float v[kDownMaxRanges];
+#pragma unroll
+  for (int r = 0; r < kDownMaxRanges; ++r)
+    v[r] = (c < d && r < n_ranges) ? partials[(size_t)r * d + c] : 0.f;
+  if (c >= d) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < kDownMaxRanges; ++r)
+    if (r < n_ranges) sum += v[r];
+  y[c] = accumulate ? y[c] + sum : sum;
+}
+
 template <typename WT>
 static void down_typed(const DownArgs& a, hipStream_t s) {
   dim3 grid(a.n_tiles, a.n_ranges);
-  ProfScope prof(K_DOWN, s);
-  down_kernel<WT><<<grid, kDownThreads, 0, s>>>((const WT*)a.w_down_t, a.d, a.dff, a.keep,
-                                                a.hmid, a.range_len, a.n_ranges, a.partials,
-                                                a.counters, a.y, a.accumulate, a.idx_out,
-                                                a.n_kept_out);
+  {
+    ProfScope prof(K_DOWN, s);
+    down_kernel<WT><<<grid, kDownThreads, 0, s>>>((const WT*)a.w_down_t, a.d, a.dff, a.keep,
+                                                  a.hmid, a.range_len, a.n_ranges, a.partials,
+                                                  a.idx_out, a.n_kept_out);
+  }
+  ProfScope prof(K_DOWN_REDUCE, s);
+  down_reduce_kernel<<<(a.d + 255) / 256, 256, 0, s>>>(a.partials, a.d, a.n_ranges, a.y,
+                                                       a.accumulate);
 }
 
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s) {

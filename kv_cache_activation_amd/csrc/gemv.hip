@@ -6,12 +6,11 @@
 // MI355X (one wave per weight row, rows dealt out across the whole grid so
 // that the waves in flight together read one contiguous window of the matrix,
 // which streams close to a plain sequential read):
-//   * every wave loads the whole input vector into VGPRs (lane l holds columns
-//     8(l + 64k) .. +8) straight from global memory (it stays in L2), times
-//     the norm weights when there is a norm, and reduces sum(x^2) itself for
-//     the RMSNorm scale rs, applied to each dot product at the end
-//     (RMSNorm(x) . w = rs * (x * norm) . w): no LDS, no workgroup barrier,
-//     and no extra pass over HBM for the norm;
+//   * a workgroup stages the input vector in LDS once (times the norm
+//     weights when there is a norm) and reduces sum(x^2) for the RMSNorm scale
+//     rs, applied to each dot product at the end (RMSNorm(x) . w =
+//     rs * (x * norm) . w), so the norm costs no extra pass over HBM; the
+//     first weight rows are already in flight while it does so;
 //   * a wave owns rows wave, wave + W, wave + 2W, ... (W = waves in the grid)
 //     and streams each with 16-byte loads, the next row's loads issued before
 //     the current row's arithmetic, reducing each dot product across the wave.
@@ -25,36 +24,30 @@ namespace sd {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-// Input vector slice of one lane: columns 8(l + 64k) .. +8, k < NCH.
-template <int NCH>
-struct XSlice {
-  float v[NCH][8];
-  // x (times nw when given) into v; returns this lane's part of sum(x^2).
-  __device__ __forceinline__ float load(const float* __restrict__ x, const float* __restrict__ nw,
-                                        int d8) {
-    const int lane = lane_id();
-    float ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int c8 = lane + kWave * k;
-      if (c8 < d8) {
-        load8f(x + 8 * c8, v[k]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(v[k][e], v[k][e], ss);
-        if (nw) {
-          float w[8];
-          load8f(nw + 8 * c8, w);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[k][e] *= w[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
-      }
+// Stage x (times nw when given) into LDS xs[0..d); returns the RMSNorm scale
+// 1/sqrt(mean(x^2) + eps) when `norm`, else 1.  Every thread of the workgroup
+// must call it (it holds a workgroup barrier).
+__device__ float stage_x(const float* __restrict__ x, const float* __restrict__ nw, int d,
+                         float eps, bool norm, float* xs) {
+  __shared__ float red[kWavesPerBlock];
+  float ss = 0.f;
+  for (int i = 4 * threadIdx.x; i < d; i += 4 * kThreads) {  // d % 8 == 0
+    float4 v = *reinterpret_cast<const float4*>(x + i);
+    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    if (nw) {
+      const float4 w = *reinterpret_cast<const float4*>(nw + i);
+      v.x *= w.x; v.y *= w.y; v.z *= w.z; v.w *= w.w;
     }
-    return ss;
+    *reinterpret_cast<float4*>(xs + i) = v;
   }
-};
+  ss = wave_sum(ss);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) tot += red[w];
+  return norm ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;
+}
 
 // One weight row held by a wave: lane l holds the 16-byte chunks 8(l + 64k) .. +8.
 template <typename WT, int NCH>
@@ -68,26 +61,24 @@ struct Row {
       if (c8 < d8) w[k].load(W + (size_t)row * ld + 8 * c8);
     }
   }
-  // Full dot product with x (every lane gets it).
-  __device__ __forceinline__ float dot(const XSlice<NCH>& x, int d8) const {
+  // Full dot product with the LDS vector xs (every lane gets it).
+  __device__ __forceinline__ float dot(const float* xs, int d8) const {
     const int lane = lane_id();
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      if (lane + kWave * k < d8) {
-        float f[8];
+      const int c8 = lane + kWave * k;
+      if (c8 < d8) {
+        float f[8], xv[8];
         w[k].to_float(f);
+        load8f(xs + 8 * c8, xv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(f[e], x.v[k][e], acc);
+        for (int e = 0; e < 8; ++e) acc = fmaf(f[e], xv[e], acc);
       }
     }
     return wave_sum(acc);
   }
 };
-
-__device__ __forceinline__ float rms_scale(float ss_lane, int d, float eps) {
-  return 1.0f / sqrtf(wave_sum(ss_lane) / (float)d + eps);
-}
 
 // ------------------------------------------------------------------ QKV
 // x = RMSNorm(h) * attn_norm; [q; k; v] = W_qkv x; RoPE on q and k with the
@@ -97,38 +88,33 @@ __device__ __forceinline__ float rms_scale(float ss_lane, int d, float eps) {
 // identity table turns RoPE off); q goes to q_out, k and v are
 // rounded to the cache type and written at row row_full of the full cache and,
 // when k_sel is given, at row row_sel of the gathered buffer.  A wave computes
-// both rows of one rotation pair.  Block 0 also clears `zero_n` words of
-// `zero_buf` (tickets of the attention launch that follows).
+// both rows of one rotation pair.
 template <typename WT, typename KT, int NCH>
 __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
     const float* __restrict__ h, const float* __restrict__ nw, float eps,
     const WT* __restrict__ W, int d, int h_q, int h_kv, int dh, RopeTable rope,
     float* __restrict__ q_out, KT* __restrict__ k_full, KT* __restrict__ v_full, int cap_full,
-    int row_full, KT* __restrict__ k_sel, KT* __restrict__ v_sel, int cap_sel, int row_sel,
-    unsigned* __restrict__ zero_buf, int zero_n) {
+    int row_full, KT* __restrict__ k_sel, KT* __restrict__ v_sel, int cap_sel, int row_sel) {
   const int half = dh >> 1;
   const int d8 = d >> 3;
   const int n_pairs = (h_q + 2 * h_kv) * half;
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  if (blockIdx.x == 0 && zero_buf)
-    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_buf[i] = 0u;
-  if (wave >= n_pairs) return;  // wave-uniform
-
+  extern __shared__ float xs[];
   Row<WT, NCH> ra, rb;
   int p = wave;
-  {
+  if (p < n_pairs) {  // first pair's rows in flight during the staging
     const int head = p / half, i = p - head * half;
     ra.load(W, d, head * dh + i, d8);
     rb.load(W, d, head * dh + i + half, d8);
   }
-  XSlice<NCH> x;
-  const float rs = rms_scale(x.load(h, nw, d8), d, eps);
+  const float rs = stage_x(h, nw, d, eps, true, xs);
+  if (p >= n_pairs) return;  // wave-uniform, after the workgroup barrier
 
   for (; p < n_pairs; p += n_waves) {
     const int head = p / half, i = p - head * half;
-    float a = ra.dot(x, d8) * rs;
-    float b = rb.dot(x, d8) * rs;
+    float a = ra.dot(xs, d8) * rs;
+    float b = rb.dot(xs, d8) * rs;
     const int pn = p + n_waves;
     if (pn < n_pairs) {  // next pair's rows in flight during the stores below
       const int hn = pn / half, in = pn - hn * half;
@@ -173,15 +159,18 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
   const int d8 = din >> 3;
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  if (wave >= dout) return;
+  extern __shared__ float xs[];
   // h[row] is loaded before the row's weights, so waiting for it never waits
   // for a prefetch issued later
   const int lane = lane_id();
   Row<WT, NCH> r0, r1;
-  float hc = lane == 0 ? h[wave] : 0.f;
-  r0.load(W, din, wave, d8);
-  XSlice<NCH> x;
-  x.load(attn, nullptr, d8);
+  float hc = 0.f;
+  if (wave < dout) {
+    if (lane == 0) hc = h[wave];
+    r0.load(W, din, wave, d8);
+  }
+  stage_x(attn, nullptr, din, 0.f, false, xs);
+  if (wave >= dout) return;  // wave-uniform, after the workgroup barrier
   int r = wave;
   for (;;) {
     const int rn = r + n_waves;
@@ -190,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
       if (lane == 0) hn = h[rn];
       r1.load(W, din, rn, d8);
     }
-    const float s0 = r0.dot(x, d8);
+    const float s0 = r0.dot(xs, d8);
     if (lane == 0) h[r] = hc + s0;
     if (rn >= dout) break;
     const int rnn = rn + n_waves;
@@ -198,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
       if (lane == 0) hc = h[rnn];
       r0.load(W, din, rnn, d8);
     }
-    const float s1 = r1.dot(x, d8);
+    const float s1 = r1.dot(xs, d8);
     if (lane == 0) h[rn] = hn + s1;
     if (rnn >= dout) break;
     r = rnn;
@@ -217,23 +206,19 @@ template <typename WT, int NCH>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const float* __restrict__ xin, const float* __restrict__ nw, float eps, int norm,
     const WT* __restrict__ Wg, const WT* __restrict__ Wu, int d, int dff, float t, int gate_in,
-    int store_abs, float* __restrict__ act, uint8_t* __restrict__ keep, float* __restrict__ hmid,
-    unsigned* __restrict__ zero_buf, int zero_n) {
+    int store_abs, float* __restrict__ act, uint8_t* __restrict__ keep,
+    float* __restrict__ hmid) {
   xin += (size_t)blockIdx.y * d;
   act += (size_t)blockIdx.y * dff;
   const int d8 = d >> 3;
   const int lane = lane_id();
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && zero_buf)
-    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_buf[i] = 0u;
-  if (wave >= dff) return;
-
+  extern __shared__ float xs[];
   Row<WT, NCH> ra, rb;
-  if (!gate_in) ra.load(Wg, d, wave, d8);
-  XSlice<NCH> x;
-  const float ss = x.load(xin, norm ? nw : nullptr, d8);
-  const float rs = norm ? rms_scale(ss, d, eps) : 1.0f;
+  if (wave < dff && !gate_in) ra.load(Wg, d, wave, d8);  // in flight during the staging
+  const float rs = stage_x(xin, norm ? nw : nullptr, d, eps, norm != 0, xs);
+  if (wave >= dff) return;  // wave-uniform, after the workgroup barrier
 
   // channel r with its gate row in `cur`; the next gate row goes into `nxt`
   auto channel = [&](Row<WT, NCH>& cur, Row<WT, NCH>& nxt, int r) {
@@ -243,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
       a = act[r];
     } else {
       if (rn < dff) nxt.load(Wg, d, rn, d8);
-      a = silu(cur.dot(x, d8) * rs);
+      a = silu(cur.dot(xs, d8) * rs);
       if (lane == 0) act[r] = store_abs ? fabsf(a) : a;
     }
     if (Wu) {
@@ -251,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
       if (lane == 0) keep[r] = k;
       if (k) {
         cur.load(Wu, d, r, d8);
-        const float u = cur.dot(x, d8) * rs;
+        const float u = cur.dot(xs, d8) * rs;
         if (lane == 0) hmid[r] = a * u;
       }
     }
@@ -281,25 +266,23 @@ static int nch_for(int d) {
     default: { constexpr int NCH = 16; __VA_ARGS__; } break; \
   }
 
-// Grid of a row-streaming kernel: at most kGemvBlocks workgroups, and no more
+// Grid of a row-streaming kernel: at most max_blocks workgroups, and no more
 // waves than rows.
-constexpr int kGemvBlocks = 512;
-static int gemv_grid(int rows) {
+static int gemv_grid(int rows, int max_blocks) {
   const int need = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-  return need < kGemvBlocks ? need : kGemvBlocks;
+  return need < max_blocks ? need : max_blocks;
 }
 
 template <typename WT, typename KT>
 static void qkv_typed(const QkvArgs& a, hipStream_t s) {
   ProfScope prof(K_QKV, s);
   // one rotation pair per wave (all of a wave's rows in flight at once)
-  const int pairs = (a.h_q + 2 * a.h_kv) * a.dh / 2;
-  int grid = (pairs + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (grid > 1024) grid = 1024;
-  SD_NCH_DISPATCH(a.d, qkv_rope_append_kernel<WT, KT, NCH><<<grid, kThreads, 0, s>>>(
+  const int grid = gemv_grid((a.h_q + 2 * a.h_kv) * a.dh / 2, 1024);
+  const size_t lds = (size_t)a.d * sizeof(float);
+  SD_NCH_DISPATCH(a.d, qkv_rope_append_kernel<WT, KT, NCH><<<grid, kThreads, lds, s>>>(
       a.h, a.norm, a.eps, (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
       (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full, (KT*)a.k_sel, (KT*)a.v_sel,
-      a.cap_sel, a.row_sel, a.zero_buf, a.zero_n));
+      a.cap_sel, a.row_sel));
 }
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {
@@ -312,27 +295,29 @@ void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,
               hipStream_t s) {
   ProfScope prof(K_O, s);
-  const int grid = gemv_grid(dout);
+  const int grid = gemv_grid(dout, 512);
+  const size_t lds = (size_t)din * sizeof(float);
   if (w_dtype == 1) {
-    SD_NCH_DISPATCH(din, o_residual_kernel<bf16_t, NCH><<<grid, kThreads, 0, s>>>(
+    SD_NCH_DISPATCH(din, o_residual_kernel<bf16_t, NCH><<<grid, kThreads, lds, s>>>(
         attn, (const bf16_t*)w, din, dout, h));
   } else {
-    SD_NCH_DISPATCH(din, o_residual_kernel<float, NCH><<<grid, kThreads, 0, s>>>(
+    SD_NCH_DISPATCH(din, o_residual_kernel<float, NCH><<<grid, kThreads, lds, s>>>(
         attn, (const float*)w, din, dout, h));
   }
 }
 
 void launch_gate_up(const GateUpArgs& a, int w_dtype, hipStream_t s) {
-  dim3 grid(gemv_grid(a.dff), a.n_states);
+  dim3 grid(gemv_grid(a.dff, 1024), a.n_states);
+  const size_t lds = (size_t)a.d * sizeof(float);
   ProfScope prof(K_GATE_UP, s);
   if (w_dtype == 1) {
-    SD_NCH_DISPATCH(a.d, gate_up_kernel<bf16_t, NCH><<<grid, kThreads, 0, s>>>(
+    SD_NCH_DISPATCH(a.d, gate_up_kernel<bf16_t, NCH><<<grid, kThreads, lds, s>>>(
         a.x, a.norm, a.eps, a.norm != nullptr, (const bf16_t*)a.w_gate, (const bf16_t*)a.w_up,
-        a.d, a.dff, a.t, a.gate_in, a.store_abs, a.act, a.keep, a.hmid, a.zero_buf, a.zero_n));
+        a.d, a.dff, a.t, a.gate_in, a.store_abs, a.act, a.keep, a.hmid));
   } else {
-    SD_NCH_DISPATCH(a.d, gate_up_kernel<float, NCH><<<grid, kThreads, 0, s>>>(
+    SD_NCH_DISPATCH(a.d, gate_up_kernel<float, NCH><<<grid, kThreads, lds, s>>>(
         a.x, a.norm, a.eps, a.norm != nullptr, (const float*)a.w_gate, (const float*)a.w_up,
-        a.d, a.dff, a.t, a.gate_in, a.store_abs, a.act, a.keep, a.hmid, a.zero_buf, a.zero_n));
+        a.d, a.dff, a.t, a.gate_in, a.store_abs, a.act, a.keep, a.hmid));
   }
 }
 

@@ -11,8 +11,8 @@ namespace sd {
 
 // Kernel kinds for the opt-in profiler (order = names in profile.cpp).
 enum KernelKind {
-  K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_SEL_LSE, K_SEL_LSE_FINAL,
-  K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_COUNT
+  K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_DOWN_REDUCE, K_SEL_LSE,
+  K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_COUNT
 };
 
 // Brackets one kernel launch with HIP events while profiling is on.
@@ -44,8 +44,6 @@ struct QkvArgs {
   void* k_sel;
   void* v_sel;
   int cap_sel, row_sel;
-  unsigned* zero_buf;
-  int zero_n;
 };
 
 struct GateUpArgs {
@@ -60,8 +58,6 @@ struct GateUpArgs {
   float* act;
   uint8_t* keep;
   float* hmid;
-  unsigned* zero_buf;
-  int zero_n;
   int n_states;       // batched gate for calibration; 1 otherwise
 };
 
@@ -72,7 +68,6 @@ struct DownArgs {
   const float* hmid;
   int range_len, n_ranges, n_tiles;
   float* partials;     // [n_ranges, d]
-  unsigned* counters;  // [n_tiles], zero on entry
   float* y;
   int accumulate;      // y += result instead of y = result
   int32_t* idx_out;    // optional ascending kept list
@@ -89,8 +84,6 @@ struct AttnArgs {
   float* pm;
   float* pl;
   float* pacc;
-  unsigned* counters;  // [h_kv] tickets; zero before the launch
-  int zero_counters;   // clear them with a tiny kernel first (standalone calls)
   float* out;
   float* lse;
 };
