@@ -49,6 +49,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--out", type=str, default="")
+    ap.add_argument("--pmc-copy-bytes", type=int, default=0,
+                    help="start with three plain device copies of this many bytes (counter "
+                         "calibration for rocprofv3 --pmc runs)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs of this script into "
+                         "per-kernel HBM bytes (needs --pmc-copy-bytes of those runs)")
+    ap.add_argument("--pmc-out", type=str, default=TRAFFIC_JSON)
     return ap.parse_args()
 
 
@@ -115,6 +122,24 @@ class Bench:
             sd.sd_cats_calibrate(self.dims, states, n_states, self.W[li]["mlp_norm"],
                                  self.W[li]["w_gate"], sparsity, thr[li:li + 1], ws)
         return thr.cpu().tolist()
+
+    def copy_ceiling(self, nbytes=1 << 30, reps=10):
+        """GB/s (read + write) of a plain device-to-device copy of nbytes: the
+        streaming rate this GPU reaches outside the decode step."""
+        torch = self.torch
+        src = torch.ones(nbytes, dtype=torch.uint8, device=self.dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del src, dst
+        return 2 * nbytes / ms / 1e6
 
     def select(self, n):
         """One-time selection at context n for every layer; returns seconds."""
@@ -209,21 +234,86 @@ class Bench:
         return out
 
 
+# library profiler kind -> (rocprofv3 kernel name, source file)
+KERNEL_SOURCES = {
+    "qkv_rope_append": ("qkv_rope_append_kernel", "gemv.hip"),
+    "attn_partial": ("attn_kernel", "attn.hip"),
+    "attn_combine": ("attn_merge_kernel", "attn.hip"),
+    "o_residual": ("o_residual_kernel", "gemv.hip"),
+    "cats_gate_up": ("gate_up_kernel", "gemv.hip"),
+    "cats_down": ("down_kernel", "down.hip"),
+    "cats_down_reduce": ("down_reduce_kernel", "down.hip"),
+}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(src: str) -> str:
+    """Hash of a kernel's source file and the headers every kernel includes."""
+    h = hashlib.sha256()
+    for f in (src, "common.hpp", "internal.hpp"):
+        h.update(open(os.path.join(ROOT, "kv_cache_activation_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, only
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only
     while the kernel's source is unchanged since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        rec = json.load(open(path)).get(kernel)
-        src = os.path.join(ROOT, "kv_cache_activation_amd", "csrc", rec["source"])
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if digest != rec["sha256"]:
+        rec = json.load(open(TRAFFIC_JSON))["kernels"][kernel]
+        if source_digest(KERNEL_SOURCES[kernel][1]) != rec["sha256"]:
             return None
         return rec["bytes_per_launch"]
     except Exception:
         return None
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out: str) -> None:
+    """Per-kernel HBM bytes per dispatch from two rocprofv3 --pmc runs of this
+    script (FETCH_SIZE, then WRITE_SIZE, in KiB), each scaled by what the same
+    counter reads for the plain device copy of `copy_bytes` bytes that the runs
+    start with (--pmc-copy-bytes).  The decode-step launches of a kernel are
+    its most frequent grid size (calibration launches differ)."""
+    import collections
+    import csv
+    import re
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Correlation_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copy" in r["Kernel_Name"] and float(r["Counter_Value"]) * 1024 > copy_bytes / 4]
+        if not copies:
+            raise SystemExit(f"{path}: no copy-kernel dispatch of about {copy_bytes} bytes found")
+        scale = copy_bytes / (sorted(copies)[len(copies) // 2] * 1024)
+        per = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in rows:
+            m = re.search(r"sd::(\w+)", r["Kernel_Name"])
+            if m:
+                per[m.group(1)][r["Grid_Size"]].append(float(r["Counter_Value"]) * 1024 * scale)
+        return scale, per
+
+    fs, fetch = load(fetch_csv, "FETCH_SIZE")
+    ws, write = load(write_csv, "WRITE_SIZE")
+    res = dict(about=("HBM bytes per dispatch of the decode-step kernels, from rocprofv3 --pmc "
+                      "FETCH_SIZE and WRITE_SIZE, each scaled by the counter's reading for a "
+                      f"plain {copy_bytes}-byte device copy"),
+               fetch_scale=fs, write_scale=ws, kernels={})
+    for kind, (rname, src) in KERNEL_SOURCES.items():
+        if rname not in fetch or rname not in write:
+            continue
+        grid = max(fetch[rname], key=lambda g: len(fetch[rname][g]))
+        f = fetch[rname][grid]
+        w = write[rname].get(grid, [0.0])
+        fb, wb = sum(f) / len(f), sum(w) / len(w)
+        res["kernels"][kind] = dict(rocprof_name=rname, grid_size=int(grid), dispatches=len(f),
+                                    fetch_bytes=round(fb), write_bytes=round(wb),
+                                    bytes_per_launch=round(fb + wb), source=src,
+                                    sha256=source_digest(src))
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
 
 
 def cpu_baseline(bench, n, seconds):
@@ -283,11 +373,21 @@ def cpu_baseline(bench, n, seconds):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_copy_bytes, args.pmc_out)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               "(the sharded multi-GPU path is a design note only)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.pmc_copy_bytes:
+        src = torch.ones(args.pmc_copy_bytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     bench = Bench(args)
     sweep = []
     sel_ms = {}
@@ -318,6 +418,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, n_head, args.cpu_seconds)
+    copy_gbs = bench.copy_ceiling()
     line = dict(
         metric=METRIC, value=round(head["gbs"], 1), unit="GB/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(head["ms_per_step"], 4), higher_is_better=True,
@@ -330,6 +431,7 @@ def main():
                     select_ms_all_layers=round(sel_ms[n_head], 2),
                     select_payback_steps=None if payback is None else round(payback, 1)),
         roofline=roof, cpu_baseline=cpu,
+        copy_ceiling_gbs=round(copy_gbs, 1),
         kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                  for k, e in kern.items()},
         sweep=[{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}

@@ -139,11 +139,11 @@ sd_status sd_select_kv(const sd_dims* dims, const void* k_full, const void* v_fu
  * k, v   [h_kv, cap, d_h] kv_dtype; n_ctx >= 1 rows read.
  * out    [h_q, d_h] float32: softmax(scale * q.K^T) V per query head.
  * lse    [h_q] float32 log-sum-exp of the scaled logits, or NULL.
- * n_splits  chunks of the row range per KV head (at most 64), 0 = chosen by
+ * n_splits  chunks of the row range per KV head (at most 128), 0 = chosen by
  *           the library; the result depends on it only through float32
  *           rounding.  A second launch merges the chunks in chunk order.
  * Errors: EINVAL unless 1 <= n_ctx <= cap; ENOSPC for a short workspace or
- *         n_splits above 64.
+ *         n_splits above 128.
  */
 sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, const void* v,
                          int32_t cap, int32_t n_ctx, float scale, int32_t n_splits,

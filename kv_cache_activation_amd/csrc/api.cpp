@@ -25,7 +25,7 @@ sd_status fail(sd_status st, const char* fmt, ...) {
 
 bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxSplits = 64;         // split-K chunks per KV head (the merge holds them in VGPRs)
+constexpr int kMaxSplits = 128;        // split-K chunks per KV head (the merge holds them in VGPRs)
 constexpr int kSplitBlocks = 512;      // auto mode: aim for this many split workgroups
 constexpr int kMinChunk = 256;         // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup

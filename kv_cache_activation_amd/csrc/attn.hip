@@ -9,8 +9,9 @@
 //   of rows of one KV head and serves all G query heads of the group, so each
 //   K/V byte is read once.  A row of d_h elements is spread over d_h/8 lanes
 //   (16-byte loads); the wave holds 64/(d_h/8) row slots, and each slot keeps
-//   U rows in flight per iteration, so a workgroup streams U*16 consecutive
-//   rows of K and of V per iteration (the chunk is read in address order).
+//   U rows in flight per iteration (U = 4 with four query heads per KV head:
+//   occupancy 3), so a workgroup streams U*16 consecutive rows of K and of V
+//   per iteration (the chunk is read in address order).
 //   Every lane group keeps its own online-softmax state (max, sum, acc) in the
 //   log2 domain; at the end the groups and the four waves merge their states
 //   and write one (m, l, acc[d_h]) per query head and split.
@@ -30,7 +31,7 @@
 namespace sd {
 
 constexpr int kAttnThreads = 256;
-constexpr int kMaxSplits = 64;  // splits per KV head (the merge holds their weights in one wave)
+constexpr int kMaxSplits = 128;  // splits per KV head (the merge holds one column of them in VGPRs)
 constexpr int kAttnWaves = kAttnThreads / kWave;
 
 template <typename KT, int DH, int G, int U>
@@ -207,14 +208,24 @@ __global__ __launch_bounds__(DH) void attn_merge_kernel(const float* __restrict_
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
     v[sp] = sp < n_splits ? base[(size_t)sp * DH] : 0.f;
-  if (threadIdx.x < kWave) {
+  if (threadIdx.x < kWave) {  // wave 0: split weights, two splits per lane
     const int lane = threadIdx.x;
-    const float mi = lane < n_splits ? pm[(size_t)h * n_splits + lane] : -INFINITY;
-    const float li = lane < n_splits ? pl[(size_t)h * n_splits + lane] : 0.f;
-    const float M = wave_max(mi);
-    const float wi = mi == -INFINITY ? 0.f : exp2f(mi - M);
-    const float L = wave_sum(wi * li);
-    w_s[lane] = wi;
+    float mi[2], li[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int sp = lane + k * kWave;
+      mi[k] = sp < n_splits ? pm[(size_t)h * n_splits + sp] : -INFINITY;
+      li[k] = sp < n_splits ? pl[(size_t)h * n_splits + sp] : 0.f;
+    }
+    const float M = wave_max(fmaxf(mi[0], mi[1]));
+    float wl = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float wi = mi[k] == -INFINITY ? 0.f : exp2f(mi[k] - M);
+      w_s[lane + k * kWave] = wi;
+      wl = fmaf(wi, li[k], wl);
+    }
+    const float L = wave_sum(wl);
     if (lane == 0) {
       big_m = M;
       big_l = L;
@@ -238,20 +249,17 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
 #define SD_ATTN_G(GG, UU)                                                                   \
-  attn_kernel<KT, DH, GG, UU><<<grid, kAttnThreads, 0, s>>>(                               \
-      a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
-  {
-    ProfScope prof(K_ATTN_PARTIAL, s);
-    switch (G) {
-      case 1: SD_ATTN_G(1, 8); break;
-      case 2: SD_ATTN_G(2, 8); break;
-      case 4: SD_ATTN_G(4, 8); break;
-      default: SD_ATTN_G(8, 4); break;
-    }
+  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU>, grid, dim3(kAttnThreads), 0, s, \
+                a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
+  switch (G) {
+    case 1: SD_ATTN_G(1, 8); break;
+    case 2: SD_ATTN_G(2, 8); break;
+    case 4: SD_ATTN_G(4, 4); break;
+    default: SD_ATTN_G(8, 4); break;
   }
 #undef SD_ATTN_G
-  ProfScope prof(K_ATTN_COMBINE, s);
-  attn_merge_kernel<DH><<<a.h_q, DH, 0, s>>>(a.pm, a.pl, a.pacc, a.n_splits, a.out, a.lse);
+  launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH>, dim3(a.h_q), dim3(DH), 0, s, a.pm, a.pl,
+                a.pacc, a.n_splits, a.out, a.lse);
 }
 
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s) {

@@ -185,15 +185,11 @@ __global__ __launch_bounds__(256) void down_reduce_kernel(const float* __restric
 template <typename WT>
 static void down_typed(const DownArgs& a, hipStream_t s) {
   dim3 grid(a.n_tiles, a.n_ranges);
-  {
-    ProfScope prof(K_DOWN, s);
-    down_kernel<WT><<<grid, kDownThreads, 0, s>>>((const WT*)a.w_down_t, a.d, a.dff, a.keep,
-                                                  a.hmid, a.range_len, a.n_ranges, a.partials,
-                                                  a.idx_out, a.n_kept_out);
-  }
-  ProfScope prof(K_DOWN_REDUCE, s);
-  down_reduce_kernel<<<(a.d + 255) / 256, 256, 0, s>>>(a.partials, a.d, a.n_ranges, a.y,
-                                                       a.accumulate);
+  launch_kernel(K_DOWN, down_kernel<WT>, grid, dim3(kDownThreads), 0, s, (const WT*)a.w_down_t,
+                a.d, a.dff, a.keep, a.hmid, a.range_len, a.n_ranges, a.partials, a.idx_out,
+                a.n_kept_out);
+  launch_kernel(K_DOWN_REDUCE, down_reduce_kernel, dim3((a.d + 255) / 256), dim3(256), 0, s,
+                (const float*)a.partials, a.d, a.n_ranges, a.y, a.accumulate);
 }
 
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s) {

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
 // is produced (|a| when store_abs; calibration over blockIdx.y states).
 // Two row buffers per wave: the next gate row streams in while the current
 // channel's up row (if kept) is read into the buffer the gate row just left.
-template <typename WT, int NCH>
+template <typename WT, int NCH, bool CALIB>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const float* __restrict__ xin, const float* __restrict__ nw, float eps, int norm,
     const WT* __restrict__ Wg, const WT* __restrict__ Wu, int d, int dff, float t, int gate_in,
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
       a = silu(cur.dot(xs, d8) * rs);
       if (lane == 0) act[r] = store_abs ? fabsf(a) : a;
     }
-    if (Wu) {
+    if (!CALIB) {
       const bool k = t < 0.f || fabsf(a) > t;  // wave-uniform
       if (lane == 0) keep[r] = k;
       if (k) {
@@ -275,14 +275,14 @@ static int gemv_grid(int rows, int max_blocks) {
 
 template <typename WT, typename KT>
 static void qkv_typed(const QkvArgs& a, hipStream_t s) {
-  ProfScope prof(K_QKV, s);
   // one rotation pair per wave (all of a wave's rows in flight at once)
   const int grid = gemv_grid((a.h_q + 2 * a.h_kv) * a.dh / 2, 1024);
   const size_t lds = (size_t)a.d * sizeof(float);
-  SD_NCH_DISPATCH(a.d, qkv_rope_append_kernel<WT, KT, NCH><<<grid, kThreads, lds, s>>>(
-      a.h, a.norm, a.eps, (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
-      (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full, (KT*)a.k_sel, (KT*)a.v_sel,
-      a.cap_sel, a.row_sel));
+  SD_NCH_DISPATCH(a.d, launch_kernel(K_QKV, qkv_rope_append_kernel<WT, KT, NCH>, dim3(grid),
+                                      dim3(kThreads), (uint32_t)lds, s, a.h, a.norm, a.eps,
+                                      (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
+                                      (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full,
+                                      (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel));
 }
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {
@@ -294,31 +294,44 @@ void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {
 
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,
               hipStream_t s) {
-  ProfScope prof(K_O, s);
   const int grid = gemv_grid(dout, 512);
   const size_t lds = (size_t)din * sizeof(float);
   if (w_dtype == 1) {
-    SD_NCH_DISPATCH(din, o_residual_kernel<bf16_t, NCH><<<grid, kThreads, lds, s>>>(
-        attn, (const bf16_t*)w, din, dout, h));
+    SD_NCH_DISPATCH(din, launch_kernel(K_O, o_residual_kernel<bf16_t, NCH>, dim3(grid),
+                                       dim3(kThreads), (uint32_t)lds, s, attn, (const bf16_t*)w,
+                                       din, dout, h));
   } else {
-    SD_NCH_DISPATCH(din, o_residual_kernel<float, NCH><<<grid, kThreads, lds, s>>>(
-        attn, (const float*)w, din, dout, h));
+    SD_NCH_DISPATCH(din, launch_kernel(K_O, o_residual_kernel<float, NCH>, dim3(grid),
+                                       dim3(kThreads), (uint32_t)lds, s, attn, (const float*)w,
+                                       din, dout, h));
   }
 }
 
 void launch_gate_up(const GateUpArgs& a, int w_dtype, hipStream_t s) {
   dim3 grid(gemv_grid(a.dff, 1024), a.n_states);
   const size_t lds = (size_t)a.d * sizeof(float);
-  ProfScope prof(K_GATE_UP, s);
+  // the calibration instance (no up projection) has a kernel name of its own
+#define SD_GATE_UP(T, CAL)                                                                    \
+  SD_NCH_DISPATCH(a.d, launch_kernel(K_GATE_UP, gate_up_kernel<T, NCH, CAL>, grid,            \
+                                     dim3(kThreads), (uint32_t)lds, s, a.x, a.norm, a.eps,    \
+                                     (int)(a.norm != nullptr), (const T*)a.w_gate,            \
+                                     (const T*)a.w_up, a.d, a.dff, a.t, a.gate_in,            \
+                                     a.store_abs, a.act, a.keep, a.hmid))
+  const bool calib = a.w_up == nullptr;
   if (w_dtype == 1) {
-    SD_NCH_DISPATCH(a.d, gate_up_kernel<bf16_t, NCH><<<grid, kThreads, lds, s>>>(
-        a.x, a.norm, a.eps, a.norm != nullptr, (const bf16_t*)a.w_gate, (const bf16_t*)a.w_up,
-        a.d, a.dff, a.t, a.gate_in, a.store_abs, a.act, a.keep, a.hmid));
+    if (calib) {
+      SD_GATE_UP(bf16_t, true);
+    } else {
+      SD_GATE_UP(bf16_t, false);
+    }
   } else {
-    SD_NCH_DISPATCH(a.d, gate_up_kernel<float, NCH><<<grid, kThreads, lds, s>>>(
-        a.x, a.norm, a.eps, a.norm != nullptr, (const float*)a.w_gate, (const float*)a.w_up,
-        a.d, a.dff, a.t, a.gate_in, a.store_abs, a.act, a.keep, a.hmid));
+    if (calib) {
+      SD_GATE_UP(float, true);
+    } else {
+      SD_GATE_UP(float, false);
+    }
   }
+#undef SD_GATE_UP
 }
 
 }  // namespace sd

@@ -3,6 +3,7 @@
 // checks hipGetLastError() afterwards.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -15,14 +16,21 @@ enum KernelKind {
   K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_COUNT
 };
 
-// Brackets one kernel launch with HIP events while profiling is on.
-struct ProfScope {
-  int kind;
-  hipStream_t s;
-  bool active;
-  ProfScope(int k, hipStream_t st);
-  ~ProfScope();
+// Start/stop events of one launch of kind `kind` while profiling is on (both
+// null otherwise, or for kind < 0).  The events are attached to the dispatch
+// itself, so they time the kernel's execution, not the queue around it.
+struct ProfEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
 };
+ProfEvents prof_events(int kind);
+
+// Every kernel of the library is launched through here.
+template <typename F, typename... Args>
+inline void launch_kernel(int kind, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                          Args... args) {
+  const ProfEvents e = prof_events(kind);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e.start, e.stop, 0u, args...);
+}
 
 // cos and sin of the rotation angle of each RoPE pair index (d_h / 2 <= 64)
 struct RopeTable {

@@ -1,7 +1,8 @@
-// Opt-in per-kernel timing: while on, every kernel launch of the library is
-// bracketed by a pair of HIP events on its stream; sd_profile_stop waits for
-// the last event and reports, per kernel kind, the launch count and the summed
-// event-to-event time.  Off by default; the state is process-wide.
+// Opt-in per-kernel timing: while on, every kernel launch of the library
+// carries a start and a stop event that the dispatch itself records (kernel
+// execution time); sd_profile_stop waits for them and reports, per kernel
+// kind, the launch count and the summed time.  Off by default; the state is
+// process-wide.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -42,25 +43,17 @@ const char* kKindNames[K_COUNT] = {
 
 }  // namespace
 
-ProfScope::ProfScope(int k, hipStream_t st) : kind(k), s(st), active(false) {
+ProfEvents prof_events(int kind) {
+  ProfEvents e;
+  if (kind < 0) return e;
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_on) return;
-  Rec r{k, take_event(), take_event()};
-  if (!r.a || !r.b) return;
-  if (hipEventRecord(r.a, s) != hipSuccess) return;
+  if (!g_on) return e;
+  Rec r{kind, take_event(), take_event()};
+  if (!r.a || !r.b) return e;
   g_recs.push_back(r);
-  active = true;
-}
-
-ProfScope::~ProfScope() {
-  if (!active) return;
-  std::lock_guard<std::mutex> lock(g_mu);
-  for (auto it = g_recs.rbegin(); it != g_recs.rend(); ++it) {
-    if (it->kind == kind) {
-      (void)hipEventRecord(it->b, s);
-      break;
-    }
-  }
+  e.start = r.a;
+  e.stop = r.b;
+  return e;
 }
 
 }  // namespace sd

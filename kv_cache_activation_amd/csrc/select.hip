@@ -305,32 +305,22 @@ static void select_typed(const SelectArgs& a, hipStream_t s) {
   const KT* k = (const KT*)a.k;
   if (!a.skip_scoring) {
     dim3 grid(a.n_chunks, a.h_kv);
-    {
-      ProfScope prof(K_SEL_LSE, s);
-      sel_lse_partial_kernel<KT, DH><<<grid, kSelThreads, 0, s>>>(
-          k, a.cap_full, a.n, a.q_win, a.w, G, scale_log2, a.n_chunks, a.lse_part);
-    }
+    launch_kernel(K_SEL_LSE, sel_lse_partial_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
+                  a.cap_full, a.n, a.q_win, a.w, G, scale_log2, a.n_chunks, a.lse_part);
     const int nq = a.h_kv * G * a.w;
-    {
-      ProfScope prof(K_SEL_LSE_FINAL, s);
-      sel_lse_final_kernel<<<(nq + 255) / 256, 256, 0, s>>>(a.lse_part, a.n_chunks, G, a.w,
-                                                            a.h_kv, a.lse);
-    }
-    ProfScope prof(K_SEL_SCORE, s);
-    sel_score_kernel<KT, DH><<<grid, kSelThreads, 0, s>>>(k, a.cap_full, a.n, a.q_win, a.w, G,
-                                                           scale_log2, a.lse, a.scores);
+    launch_kernel(K_SEL_LSE_FINAL, sel_lse_final_kernel, dim3((nq + 255) / 256), dim3(256), 0, s,
+                  (const float*)a.lse_part, a.n_chunks, G, a.w, a.h_kv, a.lse);
+    launch_kernel(K_SEL_SCORE, sel_score_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
+                  a.cap_full, a.n, a.q_win, a.w, G, scale_log2, (const float*)a.lse, a.scores);
   }
-  {
-    ProfScope prof(K_SEL_TOPK, s);
-    sel_topk_kernel<<<a.h_kv, kTopkThreads, 0, s>>>(a.scores, a.n, a.w, a.n_sink, a.k_keep,
-                                                    a.idx);
-  }
+  launch_kernel(K_SEL_TOPK, sel_topk_kernel, dim3(a.h_kv), dim3(kTopkThreads), 0, s,
+                (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.idx);
   const int k_eff = a.k_keep < a.n ? a.k_keep : a.n;
   constexpr int P = DH * (int)sizeof(KT) / 16;
   dim3 ggrid((k_eff * P + 255) / 256, a.h_kv);
-  ProfScope prof(K_SEL_GATHER, s);
-  sel_gather_kernel<KT, DH><<<ggrid, 256, 0, s>>>(k, (const KT*)a.v, a.cap_full, a.idx, k_eff,
-                                                   (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel);
+  launch_kernel(K_SEL_GATHER, sel_gather_kernel<KT, DH>, ggrid, dim3(256), 0, s, k,
+                (const KT*)a.v, a.cap_full, (const int32_t*)a.idx, k_eff, (KT*)a.k_sel,
+                (KT*)a.v_sel, a.cap_sel);
 }
 
 void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s) {
@@ -395,16 +385,16 @@ __global__ void fill_kernel(float* out, float v) { *out = v; }
 void launch_kth_smallest(const float* vals, size_t n, size_t k, unsigned* hist, unsigned* state,
                          float* out, hipStream_t s) {
   if (k == 0) {
-    fill_kernel<<<1, 1, 0, s>>>(out, -1.0f);
+    launch_kernel(-1, fill_kernel, dim3(1), dim3(1), 0, s, out, -1.0f);
     return;
   }
-  ProfScope prof(K_KTH, s);
-  kth_init_kernel<<<1, 256, 0, s>>>(hist, state, (unsigned)k);
+  launch_kernel(-1, kth_init_kernel, dim3(1), dim3(256), 0, s, hist, state, (unsigned)k);
   size_t blocks = (n + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   for (int pass = 0; pass < 4; ++pass) {
-    kth_hist_kernel<<<(unsigned)blocks, 256, 0, s>>>(vals, n, pass, state, hist);
-    kth_pick_kernel<<<1, 64, 0, s>>>(pass, hist, state, out);
+    launch_kernel(K_KTH, kth_hist_kernel, dim3((unsigned)blocks), dim3(256), 0, s, vals, n, pass,
+                  (const unsigned*)state, hist);
+    launch_kernel(-1, kth_pick_kernel, dim3(1), dim3(64), 0, s, pass, hist, state, out);
   }
 }
 
