@@ -194,33 +194,37 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 // One workgroup per query head, one thread per column: every split's value of
 // the thread's column is loaded before the first is used (one memory round
 // trip); wave 0 turns the split maxima into weights.
-template <int DH>
+template <int DH, int CAP>
 __global__ __launch_bounds__(DH) void attn_merge_kernel(const float* __restrict__ pm,
                                                         const float* __restrict__ pl,
                                                         const float* __restrict__ pacc,
                                                         int n_splits, float* __restrict__ out,
                                                         float* __restrict__ lse) {
-  __shared__ float w_s[kMaxSplits];
+  __shared__ float w_s[CAP];
   __shared__ float inv_l, big_m, big_l;
   const int h = blockIdx.x, c = threadIdx.x;
   const float* base = pacc + (size_t)h * n_splits * DH + c;
-  float v[kMaxSplits];
+  float v[CAP];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
+  for (int sp = 0; sp < CAP; ++sp)
     v[sp] = sp < n_splits ? base[(size_t)sp * DH] : 0.f;
-  if (threadIdx.x < kWave) {  // wave 0: split weights, two splits per lane
+  if (threadIdx.x < kWave) {  // wave 0: split weights, CAP / 64 splits per lane
+    constexpr int PL = CAP / kWave;
     const int lane = threadIdx.x;
-    float mi[2], li[2];
+    float mi[PL], li[PL];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PL; ++k) {
       const int sp = lane + k * kWave;
       mi[k] = sp < n_splits ? pm[(size_t)h * n_splits + sp] : -INFINITY;
       li[k] = sp < n_splits ? pl[(size_t)h * n_splits + sp] : 0.f;
     }
-    const float M = wave_max(fmaxf(mi[0], mi[1]));
+    float mm = mi[0];
+#pragma unroll
+    for (int k = 1; k < PL; ++k) mm = fmaxf(mm, mi[k]);
+    const float M = wave_max(mm);
     float wl = 0.f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PL; ++k) {
       const float wi = mi[k] == -INFINITY ? 0.f : exp2f(mi[k] - M);
       w_s[lane + k * kWave] = wi;
       wl = fmaf(wi, li[k], wl);
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(DH) void attn_merge_kernel(const float* __restrict_
   __syncthreads();
   float A = 0.f;
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
+  for (int sp = 0; sp < CAP; ++sp)
     if (sp < n_splits) A = fmaf(w_s[sp], v[sp], A);
   out[(size_t)h * DH + c] = A * inv_l;
   if (lse && c == 0) lse[h] = (big_m + log2f(big_l)) * 0.69314718055994530942f;
@@ -258,8 +262,12 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
     default: SD_ATTN_G(8, 4); break;
   }
 #undef SD_ATTN_G
-  launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH>, dim3(a.h_q), dim3(DH), 0, s, a.pm, a.pl,
-                a.pacc, a.n_splits, a.out, a.lse);
+  if (a.n_splits <= 64)
+    launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, 64>, dim3(a.h_q), dim3(DH), 0, s, a.pm,
+                  a.pl, a.pacc, a.n_splits, a.out, a.lse);
+  else
+    launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, kMaxSplits>, dim3(a.h_q), dim3(DH), 0, s,
+                  a.pm, a.pl, a.pacc, a.n_splits, a.out, a.lse);
 }
 
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s) {
