@@ -12,8 +12,8 @@
 //      wave ballots and popcount prefixes (the keep bytes and the hmid values
 //      of the range come from the gate kernel, loaded in one round),
 //   2. streams the 1 KB segment (one 16-byte load per lane) of each kept row
-//      that falls in its tile, in groups of eight rows per wave with the next
-//      group's loads issued before the current group's arithmetic,
+//      that falls in its tile, in groups of sixteen rows per wave with the
+//      next group's loads issued before the current group's arithmetic,
 //      accumulating hmid_i * w_down_t[i],
 //   3. writes a partial sum for (range, tile).
 // A second launch adds the partials of all ranges in range order --
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
     const WT* __restrict__ Wd, int d, int dff, const uint8_t* __restrict__ keep,
     const float* __restrict__ hmid, int range_len, int n_ranges, float* __restrict__ partials,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ n_kept_out) {
-  constexpr int U = 8;  // rows in flight per wave
+  constexpr int U = 16;  // rows per group; two groups in flight per wave
   __shared__ int list[kDownRounds * kDownThreads];
   __shared__ float hv_s[kDownRounds * kDownThreads];
   __shared__ float red[kDownWaves][kDownTile];
