@@ -77,7 +77,10 @@ enum {
   SD_SCORES_IN = 1u,  /* sd_select_kv: rank caller-given scores, skip scoring */
   SD_GATE_IN = 2u,    /* sd_sparse_mlp: mask caller-given activations, skip gate */
   SD_KV_SPARSE = 4u,  /* sd_decode_step: attend over the gathered buffer */
-  SD_MLP_SPARSE = 8u  /* sd_decode_step: CATS-threshold the MLP */
+  SD_MLP_SPARSE = 8u, /* sd_decode_step: CATS-threshold the MLP */
+  SD_KV_WINDOW = 16u, /* sd_decode_step: attend over sinks + recent rows of the full cache */
+  SD_ATTN_MASKED = 32u, /* sd_decode_step: dense attention by the masked comparison path */
+  SD_ATTN_FUSED = 64u   /* sd_decode_step: dense attention by the fused (no split-K) path */
 };
 
 /* projection sets of the byte account */
@@ -96,7 +99,8 @@ typedef struct {
 } sd_dims;
 
 /* Bytes of workspace that every call below needs for these dims, for caches
- * of up to max_rows rows and observation windows of up to max_window queries.
+ * of up to max_rows rows and observation windows of up to max_window queries
+ * (max_rows also sizes the score rows of the masked comparison path).
  * [host]; returns 0 on invalid dims. */
 size_t sd_workspace_bytes(const sd_dims* dims, int32_t max_rows, int32_t max_window);
 
@@ -150,6 +154,36 @@ sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, con
                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sd_decode_attn_window -- attention over a sink-plus-recent window read in
+ * place from one cache ([Cross] §4.1: the StreamingLLM-style policy that reads
+ * as many entries as the selection keeps; §4.4 times it): of the n_rows valid
+ * rows, rows [0, n_sink) and the most recent n_keep - n_sink rows, for every
+ * KV head; all rows when n_keep >= n_rows.  Same kernel, outputs and n_splits
+ * rule as sd_decode_attn over those rows.
+ * Errors: EINVAL unless 1 <= n_rows <= cap and 0 <= n_sink <= n_keep, n_keep >= 1.
+ */
+sd_status sd_decode_attn_window(const sd_dims* dims, const float* q, const void* k, const void* v,
+                                int32_t cap, int32_t n_rows, int32_t n_sink, int32_t n_keep,
+                                float scale, int32_t n_splits, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * sd_decode_attn_baseline -- dense decode attention by one of the two
+ * comparison paths of [Cross] §4.4, with the outputs of sd_decode_attn:
+ *   SD_ATTN_MASKED  scores of every query head over every allocated row
+ *                   (rows >= n_ctx masked to -inf), a row softmax, then P.V --
+ *                   each query head reads its KV head's rows itself; needs the
+ *                   workspace of sd_workspace_bytes(dims, cap, 0);
+ *   SD_ATTN_FUSED   one pass per query head in one workgroup (online softmax,
+ *                   no split-K).
+ * Errors: EINVAL unless 1 <= n_ctx <= cap and path is one of the two.
+ */
+sd_status sd_decode_attn_baseline(const sd_dims* dims, const float* q, const void* k,
+                                  const void* v, int32_t cap, int32_t n_ctx, float scale,
+                                  int32_t path, float* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
  * sd_sparse_mlp -- CATS sparse SwiGLU MLP ([SATS], CATS runtime masking).
  *
  * x        [d] float32 input; if norm_w is not NULL it is first normalised,
@@ -189,6 +223,8 @@ typedef struct {
   int32_t cap_sel;
   int32_t n_sel;           /* valid gathered rows; advanced by one when k_sel != NULL */
   uint8_t* mask_out;       /* optional [d_ff]: receives 1 for kept channels, else 0 */
+  int32_t window_keep;     /* SD_KV_WINDOW: entries read (sinks included) */
+  int32_t window_sink;     /* SD_KV_WINDOW: sink entries among them */
 } sd_layer;
 
 /*
@@ -201,6 +237,12 @@ typedef struct {
  *   0..n_full (dense) or 0..n_sel of the gathered buffer (SD_KV_SPARSE), scale
  *   1/sqrt(d_h); h += w_o attn; x = RMSNorm(h) mlp_norm; h += CATS-MLP(x) with
  *   the layer threshold under SD_MLP_SPARSE, dense otherwise.
+ *   SD_KV_WINDOW attends instead over rows [0, window_sink) and the most recent
+ *   window_keep - window_sink rows of the full cache (after the append), read
+ *   in place ([Cross] §4.1, §4.4).  SD_ATTN_MASKED / SD_ATTN_FUSED run dense
+ *   attention by the comparison paths of sd_decode_attn_baseline (the masked
+ *   path needs the workspace of sd_workspace_bytes(dims, largest cap_full, 0)).
+ *   At most one of SD_KV_SPARSE, SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED.
  * hidden  [d] float32, updated in place.
  * layers  [host] array; n_full and n_sel are advanced on success.
  * Errors: EINVAL for a missing gathered buffer under SD_KV_SPARSE or bad

@@ -26,9 +26,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 SD_OK, SD_EINVAL, SD_ENOSPC, SD_EUNSUPPORTED, SD_EHIP = range(5)
 SD_F32, SD_BF16 = 0, 1
 SD_SCORES_IN, SD_GATE_IN, SD_KV_SPARSE, SD_MLP_SPARSE = 1, 2, 4, 8
+SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED = 16, 32, 64
 SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 
-EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_decode_attn", "sd_sparse_mlp",
+EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_decode_attn", "sd_decode_attn_window",
+           "sd_decode_attn_baseline", "sd_sparse_mlp",
            "sd_decode_step", "sd_byte_account", "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
@@ -52,7 +54,8 @@ class sd_layer(ctypes.Structure):
                 ("cap_full", ctypes.c_int32), ("n_full", ctypes.c_int32),
                 ("k_sel", ctypes.c_void_p), ("v_sel", ctypes.c_void_p),
                 ("cap_sel", ctypes.c_int32), ("n_sel", ctypes.c_int32),
-                ("mask_out", ctypes.c_void_p)]
+                ("mask_out", ctypes.c_void_p), ("window_keep", ctypes.c_int32),
+                ("window_sink", ctypes.c_int32)]
 
 
 class sd_byte_record(ctypes.Structure):
@@ -81,6 +84,12 @@ _lib.sd_select_kv.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _I, _I, _P, _I, _
 _lib.sd_decode_attn.restype = _I
 _lib.sd_decode_attn.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I, _I, _F, _I, _P, _P,
                                 _P, _S, _P]
+_lib.sd_decode_attn_window.restype = _I
+_lib.sd_decode_attn_window.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I, _I, _I, _I, _F,
+                                       _I, _P, _P, _P, _S, _P]
+_lib.sd_decode_attn_baseline.restype = _I
+_lib.sd_decode_attn_baseline.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I, _I, _F, _I, _P,
+                                         _P, _P, _S, _P]
 _lib.sd_sparse_mlp.restype = _I
 _lib.sd_sparse_mlp.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _P, _P, _F, _P, _P, _P, _P,
                                _U, _P, _S, _P]
@@ -160,6 +169,22 @@ def sd_decode_attn(dims, q, k, v, cap, n_ctx, scale, n_splits, out, lse, ws, str
     p, nb = _ws(ws)
     _check(_lib.sd_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), cap, n_ctx, scale,
                                n_splits, _ptr(out), _ptr(lse), p, nb, _stream(stream)))
+
+
+def sd_decode_attn_window(dims, q, k, v, cap, n_rows, n_sink, n_keep, scale, n_splits, out, lse,
+                          ws, stream=None) -> None:
+    p, nb = _ws(ws)
+    _check(_lib.sd_decode_attn_window(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), cap, n_rows,
+                                      n_sink, n_keep, scale, n_splits, _ptr(out), _ptr(lse), p,
+                                      nb, _stream(stream)))
+
+
+def sd_decode_attn_baseline(dims, q, k, v, cap, n_ctx, scale, path, out, lse, ws,
+                            stream=None) -> None:
+    p, nb = _ws(ws)
+    _check(_lib.sd_decode_attn_baseline(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), cap, n_ctx,
+                                        scale, path, _ptr(out), _ptr(lse), p, nb,
+                                        _stream(stream)))
 
 
 def sd_sparse_mlp(dims, x, norm_w, w_gate, w_up, w_down_t, threshold, y, act, idx, n_kept,

@@ -37,7 +37,7 @@ constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, lse_part, lse;
+  size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, lse_part, lse, scores;
   size_t kth_hist, kth_state, total;
   int max_splits, n_tiles, n_ranges, range_len, sel_chunks;
 };
@@ -69,6 +69,7 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
   L.lse = take(hq * (size_t)max_window * 4);
+  L.scores = take(hq * (size_t)max_rows * 4);  // masked comparison path: [h_q, rows]
   L.kth_hist = take(256 * 4);
   L.kth_state = take(16);
   L.total = off;
@@ -123,10 +124,15 @@ int auto_splits(int n_ctx, int h_kv) {
   return s < 1 ? 1 : s;
 }
 
-// Enqueue split-K attention; ws must hold the layout's attention buffers.
+// Attention paths (the step's mode bits select them).
+enum Path { P_SPLITK = 0, P_MASKED = 1, P_FUSED = 2 };
+
+// Enqueue attention over logical rows 0..n_ctx-1 (row j read from physical
+// row j + (j >= sink ? shift : 0)); ws must hold the layout's attention
+// buffers (and, for the masked path, its score rows for `cap` rows).
 void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, const void* k,
-                  const void* v, int cap, int n_ctx, float scale, int n_splits, float* out,
-                  float* lse, hipStream_t s) {
+                  const void* v, int cap, int n_ctx, int sink, int shift, float scale,
+                  int n_splits, Path path, float* out, float* lse, hipStream_t s) {
   sd::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -136,14 +142,22 @@ void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, 
   a.h_q = dm.n_q_heads;
   a.h_kv = dm.n_kv_heads;
   a.dh = dm.head_dim;
+  a.sink = sink;
+  a.shift = shift;
   a.scale = scale;
-  a.chunk = (n_ctx + n_splits - 1) / n_splits;
-  a.n_splits = (n_ctx + a.chunk - 1) / a.chunk;
   a.pm = reinterpret_cast<float*>(ws + L.pm);
   a.pl = reinterpret_cast<float*>(ws + L.pl);
   a.pacc = reinterpret_cast<float*>(ws + L.pacc);
   a.out = out;
   a.lse = lse;
+  if (path == P_MASKED) {
+    sd::launch_attn_masked(a, reinterpret_cast<float*>(ws + L.scores), dm.kv_dtype, s);
+    return;
+  }
+  a.per_query_head = path == P_FUSED;
+  if (path == P_FUSED) n_splits = 1;  // one pass per query head, no split-K
+  a.chunk = (n_ctx + n_splits - 1) / n_splits;
+  a.n_splits = (n_ctx + a.chunk - 1) / a.chunk;
   sd::launch_attn(a, dm.kv_dtype, s);
 }
 
@@ -269,9 +283,57 @@ sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, con
   if (n_splits > L.max_splits)
     return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
   int s = n_splits ? (n_splits < n_ctx ? n_splits : n_ctx) : auto_splits(n_ctx, dims->n_kv_heads);
-  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, scale, s, out, lse,
-               static_cast<hipStream_t>(stream));
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, n_ctx, 0, scale, s,
+               P_SPLITK, out, lse, static_cast<hipStream_t>(stream));
   return check_launch("sd_decode_attn");
+}
+
+sd_status sd_decode_attn_window(const sd_dims* dims, const float* q, const void* k, const void* v,
+                                int32_t cap, int32_t n_rows, int32_t n_sink, int32_t n_keep,
+                                float scale, int32_t n_splits, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(out) || !aligned(ws) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (n_rows < 1 || n_rows > cap) return fail(SD_EINVAL, "need 1 <= n_rows <= cap");
+  if (n_keep < 1 || n_sink < 0 || n_sink > n_keep)
+    return fail(SD_EINVAL, "need 0 <= n_sink <= n_keep and n_keep >= 1");
+  if (!std::isfinite(scale)) return fail(SD_EINVAL, "scale must be finite");
+  const Layout L = make_layout(*dims, 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (n_splits < 0) return fail(SD_EINVAL, "n_splits must be >= 0");
+  if (n_splits > L.max_splits)
+    return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
+  const int n_ctx = n_keep < n_rows ? n_keep : n_rows;
+  const int sink = n_keep < n_rows ? n_sink : n_ctx;
+  const int shift = n_keep < n_rows ? n_rows - n_keep : 0;
+  int s = n_splits ? (n_splits < n_ctx ? n_splits : n_ctx) : auto_splits(n_ctx, dims->n_kv_heads);
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, sink, shift, scale, s,
+               P_SPLITK, out, lse, static_cast<hipStream_t>(stream));
+  return check_launch("sd_decode_attn_window");
+}
+
+sd_status sd_decode_attn_baseline(const sd_dims* dims, const float* q, const void* k,
+                                  const void* v, int32_t cap, int32_t n_ctx, float scale,
+                                  int32_t path, float* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(out) || !aligned(ws) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (n_ctx < 1 || n_ctx > cap) return fail(SD_EINVAL, "need 1 <= n_ctx <= cap");
+  if (!std::isfinite(scale)) return fail(SD_EINVAL, "scale must be finite");
+  if (path != SD_ATTN_MASKED && path != SD_ATTN_FUSED)
+    return fail(SD_EINVAL, "path must be SD_ATTN_MASKED or SD_ATTN_FUSED");
+  const Layout L = make_layout(*dims, path == SD_ATTN_MASKED ? cap : 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_ctx, n_ctx, 0, scale, 1,
+               path == SD_ATTN_MASKED ? P_MASKED : P_FUSED, out, lse,
+               static_cast<hipStream_t>(stream));
+  return check_launch("sd_decode_attn_baseline");
 }
 
 sd_status sd_sparse_mlp(const sd_dims* dims, const float* x, const float* norm_w,
@@ -303,7 +365,16 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
   if (!aligned(hidden) || !aligned(ws)) return fail(SD_EINVAL, "null or misaligned pointer");
   if (pos < 0) return fail(SD_EINVAL, "pos must be >= 0");
   const bool kv_sparse = mode & SD_KV_SPARSE, mlp_sparse = mode & SD_MLP_SPARSE;
-  const Layout L = make_layout(*dims, 0, 0);
+  const bool kv_window = mode & SD_KV_WINDOW;
+  const bool masked = mode & SD_ATTN_MASKED, fused = mode & SD_ATTN_FUSED;
+  if (mode & ~(uint32_t)(SD_KV_SPARSE | SD_MLP_SPARSE | SD_KV_WINDOW | SD_ATTN_MASKED | SD_ATTN_FUSED))
+    return fail(SD_EINVAL, "unknown mode bits 0x%x", mode);
+  if ((int)kv_sparse + (int)kv_window + (int)masked + (int)fused > 1)
+    return fail(SD_EINVAL, "at most one of SD_KV_SPARSE, SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED");
+  int max_cap = 0;
+  for (int i = 0; i < n_layers; ++i)
+    if (layers[i].cap_full > max_cap) max_cap = layers[i].cap_full;
+  const Layout L = make_layout(*dims, masked ? max_cap : 0, 0);
   if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
@@ -324,6 +395,8 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
       return fail(SD_EINVAL, "layer %d: KV-sparse mode needs a gathered buffer", i);
     }
     if (std::isnan(l.cats_threshold)) return fail(SD_EINVAL, "layer %d: threshold is NaN", i);
+    if (kv_window && (l.window_keep < 1 || l.window_sink < 0 || l.window_sink > l.window_keep))
+      return fail(SD_EINVAL, "layer %d: need 0 <= window_sink <= window_keep, window_keep >= 1", i);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
@@ -369,9 +442,16 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     const void* kc = kv_sparse ? l.k_sel : l.k_full;
     const void* vc = kv_sparse ? l.v_sel : l.v_full;
     const int cap = kv_sparse ? l.cap_sel : l.cap_full;
-    const int n_ctx = (kv_sparse ? l.n_sel : l.n_full) + 1;
-    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, scale, auto_splits(n_ctx, hkv), attn,
-                 nullptr, s);
+    int n_ctx = (kv_sparse ? l.n_sel : l.n_full) + 1;
+    int sink = n_ctx, shift = 0;
+    if (kv_window && l.window_keep < n_ctx) {  // sinks + most recent rows, in place
+      shift = n_ctx - l.window_keep;
+      sink = l.window_sink;
+      n_ctx = l.window_keep;
+    }
+    const Path path = masked ? P_MASKED : fused ? P_FUSED : P_SPLITK;
+    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, sink, shift, scale,
+                 auto_splits(n_ctx, hkv), path, attn, nullptr, s);
 
     sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, s);
 

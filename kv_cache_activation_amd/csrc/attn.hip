@@ -37,8 +37,8 @@ constexpr int kAttnWaves = kAttnThreads / kWave;
 template <typename KT, int DH, int G, int U>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
-    int n_ctx, float scale_log2, int chunk, int n_splits, float* __restrict__ pm,
-    float* __restrict__ pl, float* __restrict__ pacc) {
+    int n_ctx, int sink, int shift, int kv_div, float scale_log2, int chunk, int n_splits,
+    float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ pacc) {
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
@@ -51,8 +51,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   const int slot = wave * RPW + lane / LPR;
   const int r0 = split * chunk;
   const int r1 = min(n_ctx, r0 + chunk);
-  const KT* Kb = K + (size_t)kv * cap * DH + 8 * sub;
-  const KT* Vb = V + (size_t)kv * cap * DH + 8 * sub;
+  // logical row j is physical row j, or j + shift from `sink` on (a window of
+  // sinks plus recent rows read in place); query-head group kv reads KV head
+  // kv / kv_div (kv_div > 1: one workgroup per query head)
+  const KT* Kb = K + (size_t)(kv / kv_div) * cap * DH + 8 * sub;
+  const KT* Vb = V + (size_t)(kv / kv_div) * cap * DH + 8 * sub;
+  auto phys = [&](int jj) { return (size_t)(jj + (jj >= sink ? shift : 0)); };
 
   // first rows in flight before the query is read
   Vec8<KT> kr[U], vr[U];
@@ -61,8 +65,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   for (int u = 0; u < U; ++u) {
     const int jj = j + u * SLOTS;
     if (jj < r1) {
-      kr[u].load(Kb + (size_t)jj * DH);
-      vr[u].load(Vb + (size_t)jj * DH);
+      kr[u].load(Kb + phys(jj) * DH);
+      vr[u].load(Vb + phys(jj) * DH);
     }
   }
 
@@ -133,8 +137,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     for (int u = 0; u < U; ++u) {
       const int jj = j + U * SLOTS + u * SLOTS;
       if (jj < r1) {
-        kr[u].load(Kb + (size_t)jj * DH);
-        vr[u].load(Vb + (size_t)jj * DH);
+        kr[u].load(Kb + phys(jj) * DH);
+        vr[u].load(Vb + phys(jj) * DH);
       }
     }
   }
@@ -247,14 +251,18 @@ __global__ __launch_bounds__(DH) void attn_merge_kernel(const float* __restrict_
 
 template <typename KT, int DH>
 static void attn_dh(const AttnArgs& a, hipStream_t s) {
-  const int G = a.h_q / a.h_kv;
+  // per_query_head: one workgroup (group of one) per query head, reading KV head h / G
+  const int G = a.per_query_head ? 1 : a.h_q / a.h_kv;
+  const int kv_div = a.per_query_head ? a.h_q / a.h_kv : 1;
+  const int groups = a.per_query_head ? a.h_q : a.h_kv;
   const float scale_log2 = a.scale * 1.44269504088896340736f;
-  dim3 grid(a.n_splits, a.h_kv);
+  dim3 grid(a.n_splits, groups);
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
 #define SD_ATTN_G(GG, UU)                                                                   \
   launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU>, grid, dim3(kAttnThreads), 0, s, \
-                a.q, k, v, a.cap, a.n_ctx, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
+                a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, scale_log2, a.chunk, a.n_splits, a.pm, \
+      a.pl, a.pacc)
   switch (G) {
     case 1: SD_ATTN_G(1, 8); break;
     case 2: SD_ATTN_G(2, 8); break;

@@ -13,7 +13,8 @@ namespace sd {
 // Kernel kinds for the opt-in profiler (order = names in profile.cpp).
 enum KernelKind {
   K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_DOWN_REDUCE, K_SEL_LSE,
-  K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_COUNT
+  K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_MASKED_SCORES,
+  K_MASKED_SOFTMAX, K_MASKED_PV, K_COUNT
 };
 
 // Start/stop events of one launch of kind `kind` while profiling is on (both
@@ -87,6 +88,8 @@ struct AttnArgs {
   const void* k;
   const void* v;
   int cap, n_ctx, h_q, h_kv, dh;
+  int sink, shift;      // logical row j reads physical row j + (j >= sink ? shift : 0)
+  int per_query_head;   // one workgroup per query head (no K/V sharing across a group)
   float scale;
   int n_splits, chunk;
   float* pm;
@@ -119,6 +122,10 @@ void launch_o(const float* attn, const void* w, int din, int dout, float* h, int
 void launch_gate_up(const GateUpArgs& a, int w_dtype, hipStream_t s);
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s);
+// Masked dense attention over every allocated row (rows >= n_ctx masked): scores
+// of each query head into `scores` [h_q, cap], a row softmax, then P.V in
+// n_splits chunks summed in order.  A deliberately plain comparison path.
+void launch_attn_masked(const AttnArgs& a, float* scores, int kv_dtype, hipStream_t s);
 void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s);
 // k-th smallest (1-based k) of n non-negative float32 values; writes the value
 // to *out (or -1 when k == 0).  hist: 256 uint32 scratch words; state: 4 words.

@@ -20,6 +20,8 @@ Readings where the page is silent or garbled (each also listed in the design doc):
   [n_sink, n - w), ties to the lower position; the kept list is ascending.
 * k_keep >= n keeps everything (a keep ratio of 1 disables the branch,
   [Cross] §5.3).
+* The sink-plus-recent window ([Cross] §4.1, §4.4) keeps the first n_sink
+  rows and the most recent rows up to the same count, read in place.
 
 The top-k decision is taken on float32 scores (the precision of the HIP
 kernels; the page fixes none), so that both sides decide identically when
@@ -103,6 +105,19 @@ def select_indices(scores_f32: np.ndarray, n: int, w: int, n_sink: int,
         keep = np.concatenate([np.arange(n_sink), chosen, np.arange(n - w, n)])
         out[kv] = np.sort(keep)
     return out
+
+
+def window_indices(n: int, n_sink: int, n_keep: int) -> np.ndarray:
+    """Rows a sink-plus-recent window reads from a cache of n rows ([Cross] §4.1:
+    the StreamingLLM-style comparison policy, which reads as many entries as the
+    selection keeps, in place): the first n_sink rows and the most recent
+    n_keep - n_sink rows, ascending; every row when n_keep >= n.  The same
+    positions for every KV head."""
+    if n_keep >= n:
+        return np.arange(n, dtype=np.int64)
+    if not 0 <= n_sink <= n_keep:
+        raise ValueError("need 0 <= n_sink <= n_keep")
+    return np.concatenate([np.arange(n_sink), np.arange(n - (n_keep - n_sink), n)]).astype(np.int64)
 
 
 def gather(cache: np.ndarray, idx: np.ndarray) -> np.ndarray:

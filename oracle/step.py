@@ -11,6 +11,8 @@ Llama layer without biases:
         has a gathered buffer, at its row n_sel too   ([Cross] §3.2, §4.1)
     o  = attention over rows 0..n of the full cache   (dense mode)
          or rows 0..n_sel of the gathered buffer      (KV mode)
+         or the sinks plus the most recent rows of the full cache, read in
+         place (window mode, [Cross] §4.1, §4.4)
     h += W_o o
     x  = RMSNorm(h) * mlp_norm
     h += CATS-MLP(x, t)  (dense when the MLP branch is off or t < 0)
@@ -108,8 +110,10 @@ class Layer:
 def decode_layer(layer: Layer, h: np.ndarray, pos: int, *, n_q_heads: int,
                  n_kv_heads: int, head_dim: int, kv_dtype: str, kv_sparse: bool,
                  mlp_sparse: bool, eps: float = 1e-5, theta: float = 500000.0,
-                 mask_override=None, trace=None) -> np.ndarray:
-    """One layer; appends to layer's caches in place and returns the new h."""
+                 mask_override=None, trace=None, kv_window=None) -> np.ndarray:
+    """One layer; appends to layer's caches in place and returns the new h.
+    kv_window = (n_sink, n_keep) attends over selection.window_indices of the
+    full cache instead (after the append)."""
     h = np.asarray(h, dtype=np.float64).copy()
     qd = n_q_heads * head_dim
     kd = n_kv_heads * head_dim
@@ -128,7 +132,11 @@ def decode_layer(layer: Layer, h: np.ndarray, pos: int, *, n_q_heads: int,
         layer.v_sel[:, layer.n_sel] = v_r
         layer.n_sel += 1
     scale = 1.0 / np.sqrt(head_dim)
-    if kv_sparse:
+    if kv_window is not None:
+        from . import selection
+        idx = selection.window_indices(layer.n, kv_window[0], kv_window[1])
+        o, _ = attention.attend(q, layer.k_full[:, idx], layer.v_full[:, idx], len(idx), scale)
+    elif kv_sparse:
         if layer.k_sel is None:
             raise ValueError("KV-sparse mode needs a gathered buffer")
         o, _ = attention.attend(q, layer.k_sel, layer.v_sel, layer.n_sel, scale)
@@ -149,10 +157,10 @@ def decode_layer(layer: Layer, h: np.ndarray, pos: int, *, n_q_heads: int,
 
 
 def decode_step(layers, h, pos, *, kv_sparse, mlp_sparse, masks=None, trace=None,
-                **dims):
+                kv_window=None, **dims):
     """All layers in order; returns the new hidden state."""
     for li, layer in enumerate(layers):
         m = None if masks is None else masks[li]
         h = decode_layer(layer, h, pos, kv_sparse=kv_sparse, mlp_sparse=mlp_sparse,
-                         mask_override=m, trace=trace, **dims)
+                         mask_override=m, trace=trace, kv_window=kv_window, **dims)
     return h

@@ -61,7 +61,7 @@ def midpoint_threshold(act: np.ndarray, sparsity: float) -> float:
     return float((np.float64(v[k - 1]) + np.float64(v[k])) / 2)
 
 
-def oracle_thresholds(layers, h, pos, sparsity, kv_sparse, odims):
+def oracle_thresholds(layers, h, pos, sparsity, kv_sparse, odims, kv_window=None):
     """Per-layer midpoint thresholds from the oracle's own activations, layer by
     layer (a layer's gate input does not depend on its own threshold).  The
     oracle layers are left untouched; returns the list of thresholds."""
@@ -71,9 +71,11 @@ def oracle_thresholds(layers, h, pos, sparsity, kv_sparse, odims):
     for layer in work:
         tr = []
         probe = copy.deepcopy(layer)
-        ostep.decode_layer(probe, hh, pos, kv_sparse=kv_sparse, mlp_sparse=False, trace=tr, **odims)
+        ostep.decode_layer(probe, hh, pos, kv_sparse=kv_sparse, mlp_sparse=False, trace=tr,
+                           kv_window=kv_window, **odims)
         t = midpoint_threshold(tr[0]["act"], sparsity)
         layer.threshold = t
-        hh = ostep.decode_layer(layer, hh, pos, kv_sparse=kv_sparse, mlp_sparse=True, **odims)
+        hh = ostep.decode_layer(layer, hh, pos, kv_sparse=kv_sparse, mlp_sparse=True,
+                                kv_window=kv_window, **odims)
         ts.append(t)
     return ts

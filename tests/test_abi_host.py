@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
-    assert ctypes.sizeof(sd.sd_layer) == 120
+    assert ctypes.sizeof(sd.sd_layer) == 128
     assert ctypes.sizeof(sd.sd_byte_record) == 80
 
 
@@ -151,3 +151,33 @@ def test_byte_account_matches_oracle(proj, code, n, r_p, r_kv, s_w, lm):
 def test_byte_account_rejects_bad_ratio():
     with pytest.raises(sd.SdError):
         sd.sd_byte_account(_dims(), 32, 1024, 1.5, 0.3, 2, 2, sd.SD_PROJ_ALL7)
+
+
+def test_window_and_baseline_reject_before_launch():
+    ws = _FakeWs(1 << 30)
+    with pytest.raises(sd.SdError) as e:   # sinks beyond the window
+        sd.sd_decode_attn_window(_dims(), FAKE, FAKE, FAKE, 100, 50, 10, 5, 0.1, 0, FAKE, None, ws, 0)
+    assert e.value.status == sd.SD_EINVAL
+    with pytest.raises(sd.SdError) as e:   # more rows than the cache holds
+        sd.sd_decode_attn_window(_dims(), FAKE, FAKE, FAKE, 100, 101, 4, 20, 0.1, 0, FAKE, None, ws, 0)
+    assert e.value.status == sd.SD_EINVAL
+    with pytest.raises(sd.SdError) as e:   # not a comparison path
+        sd.sd_decode_attn_baseline(_dims(), FAKE, FAKE, FAKE, 100, 50, 0.1, 0, FAKE, None, ws, 0)
+    assert e.value.status == sd.SD_EINVAL
+    small = _FakeWs(sd.sd_workspace_bytes(_dims(), 0, 0))  # no room for the score rows
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_attn_baseline(_dims(), FAKE, FAKE, FAKE, 100000, 50, 0.1, sd.SD_ATTN_MASKED,
+                                   FAKE, None, small, 0)
+    assert e.value.status == sd.SD_ENOSPC
+
+
+@pytest.mark.parametrize("mode", [sd.SD_KV_SPARSE | sd.SD_KV_WINDOW,
+                                  sd.SD_ATTN_MASKED | sd.SD_ATTN_FUSED,
+                                  sd.SD_KV_SPARSE | sd.SD_ATTN_FUSED, 1 << 9])
+def test_decode_step_rejects_conflicting_modes(mode):
+    lay = sd.sd_layer(*([FAKE] * 7), 0.1, 0, FAKE, FAKE, 64, 10, FAKE, FAKE, 64, 10, None, 8, 4)
+    layers = (sd.sd_layer * 1)(lay)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step(_dims(), layers, 10, FAKE, mode, _FakeWs(1 << 30), 0)
+    assert e.value.status == sd.SD_EINVAL
+    assert layers[0].n_full == 10

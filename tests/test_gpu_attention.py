@@ -93,3 +93,84 @@ def test_large_logits_stay_finite():
     want, want_lse = oatt.attend(q, k, v, n, 1 / np.sqrt(wl.head_dim))
     assert np.all(np.isfinite(out))
     assert rel_l2(out, want) <= 1e-5
+
+
+# ---- sink-plus-recent window read in place ([Cross] §4.1, §4.4)
+from oracle import selection as osel  # noqa: E402
+
+
+def _run_window(wl, k, v, cap, n_rows, n_sink, n_keep, q, n_splits=0):
+    dims = dims_for(wl)
+    kd, vd, qd = to_dev(k, wl.dtype), to_dev(v, wl.dtype), to_dev(q)
+    out = torch.empty(wl.n_q_heads, wl.head_dim, device=DEV)
+    lse = torch.empty(wl.n_q_heads, device=DEV)
+    sd.sd_decode_attn_window(dims, qd, kd, vd, cap, n_rows, n_sink, n_keep,
+                             1 / np.sqrt(wl.head_dim), n_splits, out, lse, workspace(dims))
+    torch.cuda.synchronize()
+    return to_host(out), to_host(lse)
+
+
+@pytest.mark.parametrize("n_rows,n_sink,n_keep,splits", [(2049, 4, 614, 0), (2049, 0, 614, 0),
+                                                         (2049, 614, 614, 0), (500, 4, 600, 0),
+                                                         (4099, 4, 1229, 7), (300, 4, 5, 0)])
+def test_window_tiny_fp32_matches_oracle(n_rows, n_sink, n_keep, splits):
+    wl = synth.TINY
+    cap = n_rows + 3
+    k, v = synth.kv_cache(wl, 1, n_rows, cap)
+    q = synth.decode_query(wl, 1)
+    out, lse = _run_window(wl, k, v, cap, n_rows, n_sink, n_keep, q, splits)
+    idx = osel.window_indices(n_rows, n_sink, n_keep)
+    want, want_lse = oatt.attend(q, k[:, idx], v[:, idx], len(idx), 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(out, want) <= TOL["f32"]
+    assert rel_l2(lse, want_lse) <= TOL["f32"]
+
+
+def test_window_8b_bf16_30pct_at_32k():
+    wl = synth.L8B_KV_32K
+    n = 32769
+    k, v = synth.kv_cache(wl, 0, n, n)
+    q = synth.decode_query(wl, 0)
+    keep = int(0.3 * n)
+    out, lse = _run_window(wl, k, v, n, n, 4, keep, q)
+    idx = osel.window_indices(n, 4, keep)
+    want, want_lse = oatt.attend(q, k[:, idx], v[:, idx], len(idx), 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(out, want) <= 1e-5 and rel_l2(lse, want_lse) <= 1e-5
+
+
+# ---- deliberately plain dense comparison paths ([Cross] §4.4)
+@pytest.mark.parametrize("path", ["masked", "fused"])
+@pytest.mark.parametrize("n_ctx,extra", [(1, 0), (777, 5), (2049, 300), (4100, 0)])
+def test_baselines_tiny_fp32_match_oracle(path, n_ctx, extra):
+    wl = synth.TINY
+    cap = n_ctx + extra
+    k, v = synth.kv_cache(wl, 2, n_ctx, cap)
+    k[:, n_ctx:] = np.nan  # rows past n_ctx are allocated but hold anything
+    v[:, n_ctx:] = np.nan
+    q = synth.decode_query(wl, 2)
+    dims = dims_for(wl)
+    code = {"masked": sd.SD_ATTN_MASKED, "fused": sd.SD_ATTN_FUSED}[path]
+    out = torch.empty(wl.n_q_heads, wl.head_dim, device=DEV)
+    lse = torch.empty(wl.n_q_heads, device=DEV)
+    ws = workspace(dims, cap)
+    sd.sd_decode_attn_baseline(dims, to_dev(q), to_dev(k), to_dev(v), cap, n_ctx,
+                               1 / np.sqrt(wl.head_dim), code, out, lse, ws)
+    torch.cuda.synchronize()
+    want, want_lse = oatt.attend(q, k, v, n_ctx, 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(to_host(out), want) <= TOL["f32"]
+    assert rel_l2(to_host(lse), want_lse) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("path", ["masked", "fused"])
+def test_baselines_8b_bf16_match_oracle(path):
+    wl = synth.L8B_DENSE_8K
+    n, cap = 8193, 8300
+    k, v = synth.kv_cache(wl, 1, n, cap)
+    q = synth.decode_query(wl, 1)
+    dims = dims_for(wl)
+    code = {"masked": sd.SD_ATTN_MASKED, "fused": sd.SD_ATTN_FUSED}[path]
+    out = torch.empty(wl.n_q_heads, wl.head_dim, device=DEV)
+    sd.sd_decode_attn_baseline(dims, to_dev(q), to_dev(k, "bf16"), to_dev(v, "bf16"), cap, n,
+                               1 / np.sqrt(wl.head_dim), code, out, None, workspace(dims, cap))
+    torch.cuda.synchronize()
+    want, _ = oatt.attend(q, k, v, n, 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(to_host(out), want) <= 1e-5

@@ -19,7 +19,9 @@ from gpu_helpers import (DEV, TOL, dims_for, midpoint_threshold, rel_l2, to_dev,
                          workspace)
 
 MODES = {"dense": 0, "kv": sd.SD_KV_SPARSE, "cats": sd.SD_MLP_SPARSE,
-         "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE}
+         "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE, "window": sd.SD_KV_WINDOW,
+         "window+cats": sd.SD_KV_WINDOW | sd.SD_MLP_SPARSE, "masked": sd.SD_ATTN_MASKED,
+         "fused": sd.SD_ATTN_FUSED}
 
 
 class Stack:
@@ -28,6 +30,7 @@ class Stack:
 
     def __init__(self, wl, n_layers, n, k_keep, extra=8, theta=500000.0):
         self.wl, self.n, self.k_keep, self.theta = wl, n, k_keep, theta
+        self.window_keep = k_keep  # the window reads as many entries as the selection keeps
         self.dims = dims_for(wl, theta)
         self.odims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
                           kv_dtype=wl.dtype, eps=1e-5, theta=theta)
@@ -57,22 +60,24 @@ class Stack:
                                       dW["w_gate"].data_ptr(), dW["w_up"].data_ptr(),
                                       dW["w_down_t"].data_ptr(), -1.0, 0, dk.data_ptr(),
                                       dv.data_ptr(), cap, n, dks.data_ptr(), dvs.data_ptr(),
-                                      ke + extra, ke, mask.data_ptr()))
+                                      ke + extra, ke, mask.data_ptr(), self.window_keep, 4))
         self.layers = (sd.sd_layer * n_layers)(*layers)
-        self.ws = workspace(self.dims)
+        self.ws = workspace(self.dims, cap)
 
     def step(self, h, pos, mode, sparsity=0.5):
         kv_sparse = bool(MODES[mode] & sd.SD_KV_SPARSE)
         mlp_sparse = bool(MODES[mode] & sd.SD_MLP_SPARSE)
+        window = (4, self.window_keep) if MODES[mode] & sd.SD_KV_WINDOW else None
         if mlp_sparse:
             from gpu_helpers import oracle_thresholds
-            ts = oracle_thresholds(self.olayers, h, pos, sparsity, kv_sparse, self.odims)
+            ts = oracle_thresholds(self.olayers, h, pos, sparsity, kv_sparse, self.odims,
+                                   kv_window=window)
             for li, t in enumerate(ts):
                 self.olayers[li].threshold = t
                 self.layers[li].cats_threshold = t
         tr = []
         want = ostep.decode_step(self.olayers, h, pos, kv_sparse=kv_sparse, mlp_sparse=mlp_sparse,
-                                 trace=tr, **self.odims)
+                                 trace=tr, kv_window=window, **self.odims)
         hd = to_dev(h)
         sd.sd_decode_step(self.dims, self.layers, pos, hd, MODES[mode], self.ws)
         torch.cuda.synchronize()
@@ -94,10 +99,11 @@ def _check_caches(st, tol):
 
 def test_tiny_fp32_mode_switching():
     wl = synth.TINY
-    st = Stack(wl, 1, wl.n_ctx, wl.k_keep)
+    st = Stack(wl, 1, wl.n_ctx, wl.k_keep, extra=16)
     h = synth.hidden(wl, 0).astype(np.float64)
     pos = wl.n_ctx
-    for mode in ("dense", "kv", "cats", "both", "both", "dense"):
+    for mode in ("dense", "kv", "cats", "both", "window", "masked", "fused", "window+cats",
+                 "both", "dense"):
         got, want, tr = st.step(h, pos, mode)
         assert rel_l2(got, want) <= TOL["f32"], mode
         if MODES[mode] & sd.SD_MLP_SPARSE:
@@ -125,7 +131,7 @@ def stack8b():
     return Stack(wl, 2, n, int(0.16 * n))
 
 
-@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both"])
+@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both", "window", "masked", "fused"])
 def test_8b_two_layers_each_mode(stack8b, mode):
     st = stack8b
     h = synth.hidden(st.wl, 7)

@@ -141,3 +141,32 @@ def test_planted_keys_recovered():
     s, idx, _, _ = sel.select_kv(qw, k, v, n, small.n_sink, small.k_keep)
     for kv in range(small.n_kv_heads):
         assert set(pos.tolist()) <= set(idx[kv].tolist())
+
+
+def test_window_indices_definition():
+    # brute force: the first n_sink rows and the last n_keep - n_sink rows
+    for n, s_, k in [(100, 4, 30), (100, 0, 30), (10, 4, 4), (7, 4, 10), (50, 4, 50)]:
+        got = sel.window_indices(n, s_, k).tolist()
+        if k >= n:
+            want = list(range(n))
+        else:
+            want = sorted(set(range(s_)) | set(range(n - (k - s_), n)))
+        assert got == want
+        assert len(got) == min(k, n)
+
+
+def test_window_attention_equals_attention_over_its_rows():
+    # the window reads its rows in place; attending over them equals attending
+    # over a gathered copy of them
+    from oracle import attention
+    r = np.random.default_rng(9)
+    q = r.standard_normal((4, 8))
+    k = r.standard_normal((2, 60, 8))
+    v = r.standard_normal((2, 60, 8))
+    idx = sel.window_indices(60, 4, 20)
+    o1, l1 = attention.attend(q, k[:, idx], v[:, idx], len(idx), 0.3)
+    z = np.einsum("hd,hjd->hj", q, np.repeat(k[:, idx], 2, axis=0)) * 0.3
+    w = np.exp(z - z.max(1, keepdims=True))
+    w /= w.sum(1, keepdims=True)
+    np.testing.assert_allclose(o1, np.einsum("hj,hjd->hd", w, np.repeat(v[:, idx], 2, axis=0)),
+                               rtol=1e-12)
