@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--modes", type=str, default=",".join(MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attn-baselines", action="store_true",
+                    help="skip the window-vs-dense-attention-path comparison at the largest context")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--out", type=str, default="")
     ap.add_argument("--pmc-copy-bytes", type=int, default=0,
@@ -81,7 +83,7 @@ class Bench:
         self.cap_sel = int(math.floor(wl.keep_ratio * n_max)) + grow + 64
         self.dims = sd.make_dims(wl.d_model, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff,
                                  sd.SD_BF16, sd.SD_BF16)
-        self.ws = torch.empty(sd.sd_workspace_bytes(self.dims, n_max, wl.window),
+        self.ws = torch.empty(sd.sd_workspace_bytes(self.dims, self.cap_full, wl.window),
                               dtype=torch.uint8, device=self.dev)
         self.W, self.K, self.V, self.KS, self.VS, self.QW, self.MASK = [], [], [], [], [], [], []
         for li in range(self.L):
@@ -198,6 +200,55 @@ class Bench:
         return dict(context=n, mode=mode, ms_per_step=ms, us_per_step=ms * 1e3,
                     bytes_per_step=b, gbs=b / ms / 1e6, hbm_frac=b / ms / 1e6 / HBM_PEAK_GBS,
                     n_kept_mean=kept, kv_rows_read=n_read)
+
+    def attention_baselines(self, n, window_ratio=0.3, steps=4, warmup=1):
+        """[Cross] §4.4 on this GPU: the same sink-plus-recent window (30% of
+        the context, 4 sinks, read in place) against dense decoding whose
+        attention runs split-K, fused (one workgroup per query head, no
+        split-K) or masked (scores over every allocated row, softmax, P.V;
+        K and V read once per query head).  Returns per path the step time,
+        the attention kernels' time per layer and the bandwidth they reach on
+        the K/V bytes attention must read, plus the window's speedups and its
+        byte bound from the library's byte account."""
+        torch, sd, wl = self.torch, self.sd, self.wl
+        win = int(math.floor(window_ratio * n))
+        for L in self.layers:
+            L.window_keep = win
+            L.window_sink = wl.n_sink
+        paths = {"split-K": 0, "fused": sd.SD_ATTN_FUSED, "masked": sd.SD_ATTN_MASKED,
+                 "window (split-K)": sd.SD_KV_WINDOW}
+        attn_kinds = ("attn_partial", "attn_combine", "masked_scores", "masked_softmax",
+                      "masked_pv")
+        out = {}
+        for name, flags in paths.items():
+            self.reset(n, 0)
+            self.run_steps(n, flags, warmup)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            self.run_steps(n + warmup, flags, steps)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            self.reset(n, 0)
+            sd.sd_profile_start()
+            self.run_steps(n, flags, 2)
+            stats = sd.sd_profile_stop()
+            attn_ms = sum(v[1] for k, v in stats.items() if k in attn_kinds) / (2 * self.L)
+            rows = (win if flags & sd.SD_KV_WINDOW else n) + 1
+            kv_bytes = rows * 2 * wl.n_kv_heads * wl.head_dim * 2  # K and V rows attention reads
+            out[name] = dict(us_per_step=round(ms * 1e3, 1), attn_us_per_layer=round(attn_ms * 1e3, 2),
+                             attn_kv_bytes=kv_bytes,
+                             attn_gbs=round(kv_bytes / attn_ms / 1e6, 1),
+                             attn_frac_of_peak=round(kv_bytes / attn_ms / 1e6 / HBM_PEAK_GBS, 4))
+        rec = sd.sd_byte_account(self.dims, self.L, float(n), 1.0, win / n, 2.0, 2.0,
+                                 sd.SD_PROJ_ALL7, 0.0)
+        w = out["window (split-K)"]["us_per_step"]
+        speedup = {f"vs dense {k}": round(out[k]["us_per_step"] / w, 3)
+                   for k in ("split-K", "fused", "masked")}
+        return dict(context=n, window_entries=win, sinks=wl.n_sink, paths=out,
+                    window_speedup=speedup, window_byte_bound=round(rec.bound_kv, 3))
 
     def profile_cell(self, n, k_keep, mode):
         """Per-kernel event timing of the same steps (library profiler)."""
@@ -419,6 +470,15 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, n_head, args.cpu_seconds)
     copy_gbs = bench.copy_ceiling()
+    base = None
+    if not args.no_attn_baselines:
+        base = bench.attention_baselines(n_head)
+        for k, v in base["paths"].items():
+            print(f"# n={n_head:6d} {k:16s} {v['us_per_step']:9.1f} us/step, attention "
+                  f"{v['attn_us_per_layer']:8.2f} us/layer = {100 * v['attn_frac_of_peak']:.1f}% of peak",
+                  flush=True)
+        print(f"# window speedups {base['window_speedup']} (byte bound {base['window_byte_bound']})",
+              flush=True)
     line = dict(
         metric=METRIC, value=round(head["gbs"], 1), unit="GB/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(head["ms_per_step"], 4), higher_is_better=True,
@@ -432,6 +492,7 @@ def main():
                     select_payback_steps=None if payback is None else round(payback, 1)),
         roofline=roof, cpu_baseline=cpu,
         copy_ceiling_gbs=round(copy_gbs, 1),
+        attention_baselines=base,
         kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                  for k, e in kern.items()},
         sweep=[{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}
