@@ -29,17 +29,14 @@ constexpr int kMaxSplits = 128;        // split-K chunks per KV head (the merge 
 constexpr int kSplitBlocks = 512;      // auto mode: aim for this many split workgroups
 constexpr int kMinChunk = 256;         // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup
-constexpr int kDownTile = 512;         // columns per down-projection tile
-constexpr int kDownRanges = 64;        // channel ranges of the down projection
-constexpr int kMaxDownRange = 512;     // channels per range the kernel compacts
 constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in VGPRs
 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t q, attn, pm, pl, pacc, act, hmid, keep, down_part, lse_part, lse, scores;
+  size_t q, attn, pm, pl, pacc, act, keep, mlp_part, lse_part, lse, scores;
   size_t kth_hist, kth_state, total;
-  int max_splits, n_tiles, n_ranges, range_len, sel_chunks;
+  int max_splits, sel_chunks;
 };
 
 Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
@@ -60,12 +57,8 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.pl = take(hq * L.max_splits * 4);
   L.pacc = take(hq * L.max_splits * dh * 4);
   L.act = take(ff * 4);
-  L.hmid = take(ff * 4);
   L.keep = take(ff);
-  L.n_tiles = (int)((d + kDownTile - 1) / kDownTile);
-  L.range_len = (int)(((ff + kDownRanges - 1) / kDownRanges + 31) / 32 * 32);
-  L.n_ranges = (int)((ff + L.range_len - 1) / L.range_len);
-  L.down_part = take((size_t)L.n_ranges * d * 4);
+  L.mlp_part = take((size_t)sd::up_down_parts((int)ff) * d * 4);
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
   L.lse = take(hq * (size_t)max_window * 4);
@@ -92,8 +85,8 @@ sd_status check_dims(const sd_dims* dm) {
     return fail(SD_EUNSUPPORTED, "d_model must be a multiple of 8 and at most %d", kMaxWidth);
   if (dm->n_q_heads * dm->head_dim > kMaxWidth)
     return fail(SD_EUNSUPPORTED, "n_q_heads * head_dim must be at most %d", kMaxWidth);
-  if (dm->d_ff > kDownRanges * kMaxDownRange)
-    return fail(SD_EUNSUPPORTED, "d_ff must be at most %d", kDownRanges * kMaxDownRange);
+  if (dm->d_ff > sd::kUdList * sd::kUdMaxParts)
+    return fail(SD_EUNSUPPORTED, "d_ff must be at most %d", sd::kUdList * sd::kUdMaxParts);
   if ((dm->w_dtype != SD_F32 && dm->w_dtype != SD_BF16) ||
       (dm->kv_dtype != SD_F32 && dm->kv_dtype != SD_BF16))
     return fail(SD_EUNSUPPORTED, "dtype must be SD_F32 or SD_BF16");
@@ -165,38 +158,36 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
                  const void* wg, const void* wu, const void* wd, float t, int gate_in, float* act,
                  uint8_t* keep, float* y, int accumulate, int32_t* idx, int32_t* n_kept,
                  hipStream_t s) {
-  sd::GateUpArgs g{};
+  sd::GateArgs g{};
   g.x = x;
   g.norm = norm;
   g.eps = dm.rms_eps;
   g.w_gate = wg;
-  g.w_up = wu;
   g.d = dm.d_model;
   g.dff = dm.d_ff;
   g.t = t;
   g.gate_in = gate_in;
-  g.store_abs = 0;
   g.act = act;
   g.keep = keep;
-  g.hmid = reinterpret_cast<float*>(ws + L.hmid);
   g.n_states = 1;
-  sd::launch_gate_up(g, dm.w_dtype, s);
+  sd::launch_gate(g, dm.w_dtype, s);
 
-  sd::DownArgs dn{};
-  dn.w_down_t = wd;
-  dn.d = dm.d_model;
-  dn.dff = dm.d_ff;
-  dn.keep = keep;
-  dn.hmid = g.hmid;
-  dn.range_len = L.range_len;
-  dn.n_ranges = L.n_ranges;
-  dn.n_tiles = L.n_tiles;
-  dn.partials = reinterpret_cast<float*>(ws + L.down_part);
-  dn.y = y;
-  dn.accumulate = accumulate;
-  dn.idx_out = idx;
-  dn.n_kept_out = n_kept;
-  sd::launch_down(dn, dm.w_dtype, s);
+  sd::UpDownArgs u{};
+  u.x = x;
+  u.norm = norm;
+  u.eps = dm.rms_eps;
+  u.w_up = wu;
+  u.w_down_t = wd;
+  u.d = dm.d_model;
+  u.dff = dm.d_ff;
+  u.keep = keep;
+  u.act = act;
+  u.partials = reinterpret_cast<float*>(ws + L.mlp_part);
+  u.y = y;
+  u.accumulate = accumulate;
+  u.idx_out = idx;
+  u.n_kept_out = n_kept;
+  sd::launch_up_down(u, dm.w_dtype, s);
 }
 
 }  // namespace
@@ -395,6 +386,8 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
       return fail(SD_EINVAL, "layer %d: KV-sparse mode needs a gathered buffer", i);
     }
     if (std::isnan(l.cats_threshold)) return fail(SD_EINVAL, "layer %d: threshold is NaN", i);
+    if (l.mask_out && !aligned(l.mask_out))
+      return fail(SD_EINVAL, "layer %d: misaligned mask_out", i);
     if (kv_window && (l.window_keep < 1 || l.window_sink < 0 || l.window_sink > l.window_keep))
       return fail(SD_EINVAL, "layer %d: need 0 <= window_sink <= window_keep, window_keep >= 1", i);
   }
@@ -491,19 +484,19 @@ sd_status sd_cats_calibrate(const sd_dims* dims, const float* states, int32_t n_
   char* wsb = static_cast<char*>(ws);
   float* vals = reinterpret_cast<float*>(wsb + L.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  sd::GateUpArgs g{};
+  sd::GateArgs g{};
   g.x = states;
   g.norm = norm_w;
   g.eps = dims->rms_eps;
   g.w_gate = w_gate;
-  g.w_up = nullptr;
+  g.calib = 1;
   g.d = dims->d_model;
   g.dff = dims->d_ff;
   g.t = -1.f;
   g.store_abs = 1;
   g.act = vals;
   g.n_states = n_states;
-  sd::launch_gate_up(g, dims->w_dtype, s);
+  sd::launch_gate(g, dims->w_dtype, s);
   const size_t N = (size_t)n_states * dims->d_ff;
   const size_t k = (size_t)std::floor((double)sparsity * (double)N + 0.5);
   sd::launch_kth_smallest(vals, N, k, reinterpret_cast<unsigned*>(wsb + L.kth_hist),

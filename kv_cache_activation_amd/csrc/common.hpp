@@ -137,4 +137,148 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Stage x (times nw when given) into LDS xs[0..d) with a workgroup of THREADS
+// threads; returns the RMSNorm scale 1/sqrt(mean(x^2) + eps) when `norm`, else
+// 1.  Every thread of the workgroup must call it (it holds a workgroup
+// barrier).  d % 4 == 0 and x, nw 16-byte aligned.
+template <int THREADS>
+__device__ float stage_x(const float* __restrict__ x, const float* __restrict__ nw, int d,
+                         float eps, bool norm, float* xs) {
+  constexpr int kWaves = THREADS / kWave;
+  __shared__ float red[kWaves];
+  float ss = 0.f;
+  for (int i = 4 * threadIdx.x; i < d; i += 4 * THREADS) {
+    float4 v = *reinterpret_cast<const float4*>(x + i);
+    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    if (nw) {
+      const float4 w = *reinterpret_cast<const float4*>(nw + i);
+      v.x *= w.x; v.y *= w.y; v.z *= w.z; v.w *= w.w;
+    }
+    *reinterpret_cast<float4*>(xs + i) = v;
+  }
+  ss = wave_sum(ss);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += red[w];
+  return norm ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;
+}
+
+// stage_x in two halves, so the input's loads can be issued before the first
+// weight rows and the workgroup's staging waits only for them: load() reads
+// this thread's float4 chunks 4(t + THREADS k) of x (and nw) into registers,
+// finish() reduces sum(x^2), writes x * nw to LDS and holds the barrier.
+// d <= 4 NV THREADS; FULL: d == 4 NV THREADS (no bounds tests); NW: nw is
+// given (the loads then have no branch around them either).
+template <int THREADS, int NV, bool FULL, bool NW>
+struct XStage {
+  float4 x[NV], w[NV];
+  __device__ __forceinline__ void load(const float* __restrict__ xin,
+                                       const float* __restrict__ nw, int d) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = 4 * (threadIdx.x + THREADS * k);
+      x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      w[k] = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (FULL || i < d) {
+        x[k] = *reinterpret_cast<const float4*>(xin + i);
+        if (NW) w[k] = *reinterpret_cast<const float4*>(nw + i);
+      }
+    }
+  }
+  __device__ __forceinline__ float finish(int d, float eps, bool norm, float* xs) {
+    constexpr int kWaves = THREADS / kWave;
+    __shared__ float red[kWaves];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = 4 * (threadIdx.x + THREADS * k);
+      const float4 v = x[k];
+      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+      if (FULL || i < d)
+        *reinterpret_cast<float4*>(xs + i) =
+            make_float4(v.x * w[k].x, v.y * w[k].y, v.z * w[k].z, v.w * w[k].w);
+    }
+    ss = wave_sum(ss);
+    if (lane_id() == 0) red[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) tot += red[v];
+    return norm ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;
+  }
+};
+
+// One weight row held by a wave: lane l holds the 16-byte chunks 8(l + 64k) .. +8.
+template <typename WT, int NCH>
+struct Row {
+  Vec8<WT> w[NCH];
+  __device__ __forceinline__ void load(const WT* __restrict__ W, int ld, int row, int d8) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c8 = lane + kWave * k;
+      if (c8 < d8) w[k].load(W + (size_t)row * ld + 8 * c8);
+    }
+  }
+  // All NCH chunks, no bounds test (d == 512 NCH): with no branch around the
+  // loads the compiler can wait for exactly this row's loads later instead of
+  // for every load in flight.
+  __device__ __forceinline__ void load_full(const WT* __restrict__ W, int ld, int row) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) w[k].load(W + (size_t)row * ld + 8 * (lane + kWave * k));
+  }
+  // Full dot product with the LDS vector xs (every lane gets it).
+  __device__ __forceinline__ float dot(const float* xs, int d8) const {
+    const int lane = lane_id();
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c8 = lane + kWave * k;
+      if (c8 < d8) {
+        float f[8], xv[8];
+        w[k].to_float(f);
+        load8f(xs + 8 * c8, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(f[e], xv[e], acc);
+      }
+    }
+    return wave_sum(acc);
+  }
+  // dot() for d == 512 NCH (no bounds tests)
+  __device__ __forceinline__ float dot_full(const float* xs) const {
+    const int lane = lane_id();
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      float f[8], xv[8];
+      w[k].to_float(f);
+      load8f(xs + 8 * (lane + kWave * k), xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(f[e], xv[e], acc);
+    }
+    return wave_sum(acc);
+  }
+};
+
+// Chunks of 8 columns a row of d (d % 8 == 0) elements needs per lane, as a
+// power of two (the template argument NCH of Row).
+inline int nch_for(int d) {
+  int need = (d / 8 + kWave - 1) / kWave;
+  int n = 1;
+  while (n < need) n <<= 1;
+  return n;
+}
+
+#define SD_NCH_DISPATCH(D, ...)                                  \
+  switch (::sd::nch_for(D)) {                                    \
+    case 1: { constexpr int NCH = 1; __VA_ARGS__; } break;   \
+    case 2: { constexpr int NCH = 2; __VA_ARGS__; } break;   \
+    case 4: { constexpr int NCH = 4; __VA_ARGS__; } break;   \
+    case 8: { constexpr int NCH = 8; __VA_ARGS__; } break;   \
+    default: { constexpr int NCH = 16; __VA_ARGS__; } break; \
+  }
+
 }  // namespace sd

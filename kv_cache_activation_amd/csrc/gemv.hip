@@ -16,6 +16,10 @@
 //     the current row's arithmetic, reducing each dot product across the wave.
 #include <math.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -24,61 +28,62 @@ namespace sd {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-// Stage x (times nw when given) into LDS xs[0..d); returns the RMSNorm scale
-// 1/sqrt(mean(x^2) + eps) when `norm`, else 1.  Every thread of the workgroup
-// must call it (it holds a workgroup barrier).
-__device__ float stage_x(const float* __restrict__ x, const float* __restrict__ nw, int d,
-                         float eps, bool norm, float* xs) {
-  __shared__ float red[kWavesPerBlock];
-  float ss = 0.f;
-  for (int i = 4 * threadIdx.x; i < d; i += 4 * kThreads) {  // d % 8 == 0
-    float4 v = *reinterpret_cast<const float4*>(x + i);
-    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-    if (nw) {
-      const float4 w = *reinterpret_cast<const float4*>(nw + i);
-      v.x *= w.x; v.y *= w.y; v.z *= w.z; v.w *= w.w;
-    }
-    *reinterpret_cast<float4*>(xs + i) = v;
-  }
-  ss = wave_sum(ss);
-  if (lane_id() == 0) red[threadIdx.x / kWave] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) tot += red[w];
-  return norm ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;
+// Full dot product of a row with the LDS copy of x (every lane gets it).
+// FULL: d == 512 NCH.
+template <bool FULL, typename WT, int NCH>
+__device__ __forceinline__ float row_dot(const Row<WT, NCH>& r, const float* xs, int d8) {
+  return FULL ? r.dot_full(xs) : r.dot(xs, d8);
 }
 
-// One weight row held by a wave: lane l holds the 16-byte chunks 8(l + 64k) .. +8.
-template <typename WT, int NCH>
-struct Row {
-  Vec8<WT> w[NCH];
-  __device__ __forceinline__ void load(const WT* __restrict__ W, int ld, int row, int d8) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int c8 = lane + kWave * k;
-      if (c8 < d8) w[k].load(W + (size_t)row * ld + 8 * c8);
-    }
+template <bool FULL, typename WT, int NCH>
+__device__ __forceinline__ void load_row(Row<WT, NCH>& r, const WT* __restrict__ W, int ld,
+                                         int row, int d8) {
+  if constexpr (FULL) r.load_full(W, ld, row);
+  else r.load(W, ld, row, d8);
+}
+
+// Streams the n rows row_of(0), row_of(1), ... of W (1 <= n <= 64) through
+// the calling wave with two rows in flight and returns in lane k the dot
+// product of row k with x (LDS copy xs); `ra` already holds row 0.  What
+// keeps the loads flowing, measured on MI355X (117 MB gate matrix: 25.6 ->
+// 20.9 us):
+//  * the loop body issues the next row's loads with no branch around them
+//    (the last row is peeled off, and full-width rows have no bounds tests),
+//    so the compiler waits for exactly the older row's loads instead of for
+//    every load in flight;
+//  * x is read from LDS for every row: an empty asm with a memory clobber
+//    stops the compiler from hoisting those reads into 64 more VGPRs, which
+//    would cost a wave per SIMD of occupancy;
+//  * results stay in registers until the caller stores them after the loop
+//    (a store in the loop shares the loads' completion counter).
+template <bool FULL, typename WT, int NCH, typename RowOf>
+__device__ __forceinline__ float stream_rows(const WT* __restrict__ W, int ld, int d8, int n,
+                                             const float* xs, Row<WT, NCH>& ra,
+                                             Row<WT, NCH>& rb, RowOf row_of) {
+  const int lane = lane_id();
+  float mine = 0.f;
+  auto take = [&](const Row<WT, NCH>& r, int k) {
+    asm volatile("" ::: "memory");
+    const float s = row_dot<FULL>(r, xs, d8);
+    if (lane == k) mine = s;
+  };
+  int k = 0;
+#pragma unroll 1
+  for (; k + 2 < n; k += 2) {
+    load_row<FULL>(rb, W, ld, row_of(k + 1), d8);
+    take(ra, k);
+    load_row<FULL>(ra, W, ld, row_of(k + 2), d8);
+    take(rb, k + 1);
   }
-  // Full dot product with the LDS vector xs (every lane gets it).
-  __device__ __forceinline__ float dot(const float* xs, int d8) const {
-    const int lane = lane_id();
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int c8 = lane + kWave * k;
-      if (c8 < d8) {
-        float f[8], xv[8];
-        w[k].to_float(f);
-        load8f(xs + 8 * c8, xv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(f[e], xv[e], acc);
-      }
-    }
-    return wave_sum(acc);
+  if (k + 1 < n) {
+    load_row<FULL>(rb, W, ld, row_of(k + 1), d8);
+    take(ra, k);
+    take(rb, k + 1);
+  } else {
+    take(ra, k);
   }
-};
+  return mine;
+}
 
 // ------------------------------------------------------------------ QKV
 // x = RMSNorm(h) * attn_norm; [q; k; v] = W_qkv x; RoPE on q and k with the
@@ -88,8 +93,9 @@ struct Row {
 // identity table turns RoPE off); q goes to q_out, k and v are
 // rounded to the cache type and written at row row_full of the full cache and,
 // when k_sel is given, at row row_sel of the gathered buffer.  A wave computes
-// both rows of one rotation pair.
-template <typename WT, typename KT, int NCH>
+// both rows of the rotation pairs wave, wave + W, ... (W waves in the grid,
+// at most 32 pairs per wave); lane j then rotates and stores its j-th pair.
+template <typename WT, typename KT, int NCH, bool FULL>
 __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
     const float* __restrict__ h, const float* __restrict__ nw, float eps,
     const WT* __restrict__ W, int d, int h_q, int h_kv, int dh, RopeTable rope,
@@ -100,186 +106,201 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
   const int n_pairs = (h_q + 2 * h_kv) * half;
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
+  const int lane = lane_id();
+  const int my_pairs = wave < n_pairs ? (n_pairs - wave + n_waves - 1) / n_waves : 0;
+  // row k of this wave: pair wave + (k / 2) W, first (k even) or second row
+  auto row_of = [&](int k) {
+    const int p = wave + (k >> 1) * n_waves;
+    const int head = p / half, i = p - head * half;
+    return head * dh + i + (k & 1) * half;
+  };
   extern __shared__ float xs[];
+  XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), true> st;
+  st.load(h, nw, d);  // x first: the staging then waits for it alone
+  // the first pair's rows are in flight during the staging (a wave without
+  // pairs, only when waves outnumber pairs, reads pair 0 and drops it: no
+  // branch around the loads)
   Row<WT, NCH> ra, rb;
-  int p = wave;
-  if (p < n_pairs) {  // first pair's rows in flight during the staging
-    const int head = p / half, i = p - head * half;
-    ra.load(W, d, head * dh + i, d8);
-    rb.load(W, d, head * dh + i + half, d8);
+  {
+    const int p0 = my_pairs > 0 ? wave : 0;
+    const int head = p0 / half, i = p0 - head * half;
+    load_row<FULL>(ra, W, d, head * dh + i, d8);
+    load_row<FULL>(rb, W, d, head * dh + i + half, d8);
   }
-  const float rs = stage_x(h, nw, d, eps, true, xs);
-  if (p >= n_pairs) return;  // wave-uniform, after the workgroup barrier
-
-  for (; p < n_pairs; p += n_waves) {
-    const int head = p / half, i = p - head * half;
-    float a = ra.dot(xs, d8) * rs;
-    float b = rb.dot(xs, d8) * rs;
-    const int pn = p + n_waves;
-    if (pn < n_pairs) {  // next pair's rows in flight during the stores below
-      const int hn = pn / half, in = pn - hn * half;
-      ra.load(W, d, hn * dh + in, d8);
-      rb.load(W, d, hn * dh + in + half, d8);
-    }
-    if (lane_id() == 0) {
-      if (head < h_q + h_kv) {  // rotate q and k, not v
-        const float c = rope.c[i], sn = rope.s[i];
-        const float ra_ = a * c - b * sn;
-        const float rb_ = b * c + a * sn;
-        a = ra_;
-        b = rb_;
-      }
-      if (head < h_q) {
-        q_out[head * dh + i] = a;
-        q_out[head * dh + i + half] = b;
-      } else {
-        const bool is_k = head < h_q + h_kv;
-        const int kv = is_k ? head - h_q : head - h_q - h_kv;
-        KT* full = is_k ? k_full : v_full;
-        const size_t off = ((size_t)kv * cap_full + row_full) * dh + i;
-        store_elem(full + off, a);
-        store_elem(full + off + half, b);
-        if (k_sel) {
-          KT* sel = is_k ? k_sel : v_sel;
-          const size_t offs = ((size_t)kv * cap_sel + row_sel) * dh + i;
-          store_elem(sel + offs, a);
-          store_elem(sel + offs + half, b);
-        }
-      }
+  const float rs = st.finish(d, eps, true, xs);
+  if (my_pairs == 0) return;  // wave-uniform, after the workgroup barrier
+  // rows 0 and 1 are both in flight: take them first, then stream the rest
+  const float s0 = row_dot<FULL>(ra, xs, d8), s1 = row_dot<FULL>(rb, xs, d8);
+  float mine = lane == 0 ? s0 : lane == 1 ? s1 : 0.f;
+  const int n_rows = 2 * my_pairs;
+  if (n_rows > 2) {
+    load_row<FULL>(ra, W, d, row_of(2), d8);
+    const float rest = stream_rows<FULL>(W, d, d8, n_rows - 2, xs, ra, rb,
+                                         [&](int k) { return row_of(k + 2); });
+    const float up = __shfl_up(rest, 2);
+    if (lane >= 2) mine = up;
+  }
+  // lane j: rows 2j and 2j+1 of the wave
+  const float a0 = __shfl(mine, 2 * lane) * rs;
+  const float b0 = __shfl(mine, 2 * lane + 1) * rs;
+  if (lane >= my_pairs) return;
+  const int p = wave + lane * n_waves;
+  const int head = p / half, i = p - head * half;
+  float a = a0, b = b0;
+  if (head < h_q + h_kv) {  // rotate q and k, not v
+    const float c = rope.c[i], sn = rope.s[i];
+    a = a0 * c - b0 * sn;
+    b = b0 * c + a0 * sn;
+  }
+  if (head < h_q) {
+    q_out[head * dh + i] = a;
+    q_out[head * dh + i + half] = b;
+  } else {
+    const bool is_k = head < h_q + h_kv;
+    const int kv = is_k ? head - h_q : head - h_q - h_kv;
+    KT* full = is_k ? k_full : v_full;
+    const size_t off = ((size_t)kv * cap_full + row_full) * dh + i;
+    store_elem(full + off, a);
+    store_elem(full + off + half, b);
+    if (k_sel) {
+      KT* sel = is_k ? k_sel : v_sel;
+      const size_t offs = ((size_t)kv * cap_sel + row_sel) * dh + i;
+      store_elem(sel + offs, a);
+      store_elem(sel + offs + half, b);
     }
   }
 }
 
 // ------------------------------------------------------------------ O
-// h[r] += W_o[r] . attn  (residual add; attn is the attention output).
-template <typename WT, int NCH>
+// h[r] += W_o[r] . attn  (residual add; attn is the attention output).  ONE:
+// the grid has a wave per row (no second row buffer: more waves fit).
+template <typename WT, int NCH, bool FULL, bool ONE>
 __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __restrict__ attn,
                                                               const WT* __restrict__ W, int din,
                                                               int dout, float* __restrict__ h) {
   const int d8 = din >> 3;
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  extern __shared__ float xs[];
-  // h[row] is loaded before the row's weights, so waiting for it never waits
-  // for a prefetch issued later
   const int lane = lane_id();
-  Row<WT, NCH> r0, r1;
-  float hc = 0.f;
-  if (wave < dout) {
-    if (lane == 0) hc = h[wave];
-    r0.load(W, din, wave, d8);
+  const int n = wave < dout ? (dout - wave + n_waves - 1) / n_waves : 0;  // <= 64
+  extern __shared__ float xs[];
+  XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), false> st;
+  st.load(attn, nullptr, din);  // x first: the staging then waits for it alone
+  Row<WT, NCH> ra, rb;  // rb unused (no registers) when ONE
+  load_row<FULL>(ra, W, din, n > 0 ? wave : 0, d8);  // no branch around the loads
+  st.finish(din, 0.f, false, xs);
+  if (n == 0) return;  // wave-uniform, after the workgroup barrier
+  float s;
+  if constexpr (ONE) {
+    s = row_dot<FULL>(ra, xs, d8);
+  } else {
+    s = stream_rows<FULL>(W, din, d8, n, xs, ra, rb, [&](int k) { return wave + k * n_waves; });
   }
-  stage_x(attn, nullptr, din, 0.f, false, xs);
-  if (wave >= dout) return;  // wave-uniform, after the workgroup barrier
-  int r = wave;
-  for (;;) {
-    const int rn = r + n_waves;
-    float hn = 0.f;
-    if (rn < dout) {
-      if (lane == 0) hn = h[rn];
-      r1.load(W, din, rn, d8);
-    }
-    const float s0 = r0.dot(xs, d8);
-    if (lane == 0) h[r] = hc + s0;
-    if (rn >= dout) break;
-    const int rnn = rn + n_waves;
-    if (rnn < dout) {
-      if (lane == 0) hc = h[rnn];
-      r0.load(W, din, rnn, d8);
-    }
-    const float s1 = r1.dot(xs, d8);
-    if (lane == 0) h[rn] = hn + s1;
-    if (rnn >= dout) break;
-    r = rnn;
+  if (lane < n) {
+    const int r = wave + lane * n_waves;
+    h[r] += s;
   }
 }
 
-// ------------------------------------------------------------------ CATS gate + up
-// x = RMSNorm(h) * mlp_norm (or x itself without norm); a_i = SiLU(W_gate[i] . x)
-// (or a_i read from `act` when gate_in); channel i is kept iff t < 0 or
-// |a_i| > t; for kept channels hmid_i = a_i (W_up[i] . x): the up row is read
-// only for kept channels.  keep[i] is 1 or 0.  With W_up == nullptr only `act`
-// is produced (|a| when store_abs; calibration over blockIdx.y states).
-// Two row buffers per wave: the next gate row streams in while the current
-// channel's up row (if kept) is read into the buffer the gate row just left.
-template <typename WT, int NCH, bool CALIB>
-__global__ __launch_bounds__(kThreads) void gate_up_kernel(
-    const float* __restrict__ xin, const float* __restrict__ nw, float eps, int norm,
-    const WT* __restrict__ Wg, const WT* __restrict__ Wu, int d, int dff, float t, int gate_in,
-    int store_abs, float* __restrict__ act, uint8_t* __restrict__ keep,
-    float* __restrict__ hmid) {
+// ------------------------------------------------------------------ CATS gate
+// x = RMSNorm(h) * mlp_norm (NORM; x itself otherwise); a_i = SiLU(W_gate[i] . x)
+// (or a_i read from `act` when gate_in); act[i] = a_i (|a_i| when store_abs);
+// keep[i] = 1 iff t < 0 or |a_i| > t, else 0 (keep may be null).  The gate is
+// dense in CATS: every row is read, so this is a plain row-streaming GEMV.
+// blockIdx.y selects one of several input states (calibration); the
+// calibration instance (CALIB) only has a kernel name of its own.
+template <typename WT, int NCH, bool FULL, bool NORM, bool CALIB>
+__global__ __launch_bounds__(kThreads) void gate_kernel(
+    const float* __restrict__ xin, const float* __restrict__ nw, float eps,
+    const WT* __restrict__ Wg, int d, int dff, float t, int gate_in, int store_abs,
+    float* __restrict__ act, uint8_t* __restrict__ keep) {
   xin += (size_t)blockIdx.y * d;
   act += (size_t)blockIdx.y * dff;
   const int d8 = d >> 3;
   const int lane = lane_id();
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
+  if (gate_in) {  // mask from the caller's activations; no GEMV
+    for (int r = wave * kWave + lane; r < dff; r += n_waves * kWave)
+      keep[r] = t < 0.f || fabsf(act[r]) > t;
+    return;
+  }
+  const int n = wave < dff ? (dff - wave + n_waves - 1) / n_waves : 0;  // <= 64
   extern __shared__ float xs[];
+  XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), NORM> st;
+  st.load(xin, nw, d);  // x first: the staging then waits for it alone
   Row<WT, NCH> ra, rb;
-  if (wave < dff && !gate_in) ra.load(Wg, d, wave, d8);  // in flight during the staging
-  const float rs = stage_x(xin, norm ? nw : nullptr, d, eps, norm != 0, xs);
-  if (wave >= dff) return;  // wave-uniform, after the workgroup barrier
-
-  // channel r with its gate row in `cur`; the next gate row goes into `nxt`
-  auto channel = [&](Row<WT, NCH>& cur, Row<WT, NCH>& nxt, int r) {
-    const int rn = r + n_waves;
-    float a;
-    if (gate_in) {
-      a = act[r];
-    } else {
-      if (rn < dff) nxt.load(Wg, d, rn, d8);
-      a = silu(cur.dot(xs, d8) * rs);
-      if (lane == 0) act[r] = store_abs ? fabsf(a) : a;
-    }
-    if (!CALIB) {
-      const bool k = t < 0.f || fabsf(a) > t;  // wave-uniform
-      if (lane == 0) keep[r] = k;
-      if (k) {
-        cur.load(Wu, d, r, d8);
-        const float u = cur.dot(xs, d8) * rs;
-        if (lane == 0) hmid[r] = a * u;
-      }
-    }
-  };
-#pragma unroll 1
-  for (int r = wave; r < dff; r += 2 * n_waves) {
-    channel(ra, rb, r);
-    if (r + n_waves >= dff) break;
-    channel(rb, ra, r + n_waves);
+  load_row<FULL>(ra, Wg, d, n > 0 ? wave : 0, d8);  // in flight during the staging
+  const float rs = st.finish(d, eps, NORM, xs);
+  if (n == 0) return;  // wave-uniform, after the workgroup barrier
+  const float s = stream_rows<FULL>(Wg, d, d8, n, xs, ra, rb,
+                                    [&](int k) { return wave + k * n_waves; });
+  if (lane < n) {
+    const int r = wave + lane * n_waves;
+    const float a = silu(s * rs);
+    act[r] = store_abs ? fabsf(a) : a;
+    if (!CALIB && keep) keep[r] = t < 0.f || fabsf(a) > t;
   }
 }
 
 // ------------------------------------------------------------------ launchers
-static int nch_for(int d) {
-  int need = (d / 8 + kWave - 1) / kWave;
-  int n = 1;
-  while (n < need) n <<= 1;
-  return n;
+// Grid of a row-streaming kernel: as many workgroups as the chip holds at
+// once (compute units x resident workgroups per unit, which the kernel's
+// register use decides), no more waves than work items, and at most
+// per_wave items per wave (a wave keeps one result per lane).
+template <typename K>
+static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
+  // resident workgroups per compute unit, per kernel and LDS size (queried once)
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    const auto key = std::make_pair(reinterpret_cast<const void*>(kernel), lds);
+    auto it = cache.find(key);
+    if (it == cache.end()) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, lds) != hipSuccess ||
+          nb < 1)
+        nb = 1;
+      it = cache.emplace(key, nb).first;
+    }
+    per_cu = it->second;
+  }
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int grid = cus * per_cu;
+  const int need = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int least = (rows + kWavesPerBlock * per_wave - 1) / (kWavesPerBlock * per_wave);
+  if (grid > need) grid = need;
+  if (grid < least) grid = least;
+  return grid < 1 ? 1 : grid;
 }
 
-#define SD_NCH_DISPATCH(D, ...)                 \
-  switch (nch_for(D)) {                         \
-    case 1: { constexpr int NCH = 1; __VA_ARGS__; } break;   \
-    case 2: { constexpr int NCH = 2; __VA_ARGS__; } break;   \
-    case 4: { constexpr int NCH = 4; __VA_ARGS__; } break;   \
-    case 8: { constexpr int NCH = 8; __VA_ARGS__; } break;   \
-    default: { constexpr int NCH = 16; __VA_ARGS__; } break; \
-  }
+// SD_NCH_DISPATCH plus FULL = (the row width is exactly 512 NCH elements)
+#define SD_ROW_DISPATCH(D, ...)                                                   \
+  SD_NCH_DISPATCH(D, if ((D) == 512 * NCH) {                                     \
+    constexpr bool FULL = true;                                                   \
+    __VA_ARGS__;                                                                  \
+  } else {                                                                        \
+    constexpr bool FULL = false;                                                  \
+    __VA_ARGS__;                                                                  \
+  })
 
-// Grid of a row-streaming kernel: at most max_blocks workgroups, and no more
-// waves than rows.
-static int gemv_grid(int rows, int max_blocks) {
-  const int need = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-  return need < max_blocks ? need : max_blocks;
+template <typename K, typename... Args>
+static void launch_rows(int kind, K kernel, int items, int per_wave, int grid_y, size_t lds,
+                        hipStream_t s, Args... args) {
+  const int grid = gemv_grid(kernel, items, per_wave, lds);
+  launch_kernel(kind, kernel, dim3(grid, grid_y), dim3(kThreads), (uint32_t)lds, s, args...);
 }
 
 template <typename WT, typename KT>
 static void qkv_typed(const QkvArgs& a, hipStream_t s) {
-  // one rotation pair per wave (all of a wave's rows in flight at once)
-  const int grid = gemv_grid((a.h_q + 2 * a.h_kv) * a.dh / 2, 1024);
+  const int pairs = (a.h_q + 2 * a.h_kv) * a.dh / 2;
   const size_t lds = (size_t)a.d * sizeof(float);
-  SD_NCH_DISPATCH(a.d, launch_kernel(K_QKV, qkv_rope_append_kernel<WT, KT, NCH>, dim3(grid),
-                                      dim3(kThreads), (uint32_t)lds, s, a.h, a.norm, a.eps,
+  SD_ROW_DISPATCH(a.d, launch_rows(K_QKV, qkv_rope_append_kernel<WT, KT, NCH, FULL>, pairs, kWave / 2,
+                                   1, lds, s, a.h, a.norm, a.eps,
                                       (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
                                       (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full,
                                       (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel));
@@ -294,44 +315,57 @@ void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {
 
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,
               hipStream_t s) {
-  const int grid = gemv_grid(dout, 1024);  // one row per wave for 4096 rows (measured best)
   const size_t lds = (size_t)din * sizeof(float);
+  // a wave per row while that fits the grid limit, else streamed rows
+  const bool one = dout <= 4096 * kWavesPerBlock;
+#define SD_O(T, ONE_)                                                                          \
+  SD_ROW_DISPATCH(din, launch_rows(K_O, o_residual_kernel<T, NCH, FULL, ONE_>, dout,          \
+                                   ONE_ ? 1 : kWave, 1, lds, s, attn, (const T*)w, din, dout, h))
   if (w_dtype == 1) {
-    SD_NCH_DISPATCH(din, launch_kernel(K_O, o_residual_kernel<bf16_t, NCH>, dim3(grid),
-                                       dim3(kThreads), (uint32_t)lds, s, attn, (const bf16_t*)w,
-                                       din, dout, h));
+    if (one) {
+      SD_O(bf16_t, true);
+    } else {
+      SD_O(bf16_t, false);
+    }
   } else {
-    SD_NCH_DISPATCH(din, launch_kernel(K_O, o_residual_kernel<float, NCH>, dim3(grid),
-                                       dim3(kThreads), (uint32_t)lds, s, attn, (const float*)w,
-                                       din, dout, h));
+    if (one) {
+      SD_O(float, true);
+    } else {
+      SD_O(float, false);
+    }
   }
+#undef SD_O
 }
 
-void launch_gate_up(const GateUpArgs& a, int w_dtype, hipStream_t s) {
-  dim3 grid(gemv_grid(a.dff, 1024), a.n_states);
+void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s) {
   const size_t lds = (size_t)a.d * sizeof(float);
-  // the calibration instance (no up projection) has a kernel name of its own
-#define SD_GATE_UP(T, CAL)                                                                    \
-  SD_NCH_DISPATCH(a.d, launch_kernel(K_GATE_UP, gate_up_kernel<T, NCH, CAL>, grid,            \
-                                     dim3(kThreads), (uint32_t)lds, s, a.x, a.norm, a.eps,    \
-                                     (int)(a.norm != nullptr), (const T*)a.w_gate,            \
-                                     (const T*)a.w_up, a.d, a.dff, a.t, a.gate_in,            \
-                                     a.store_abs, a.act, a.keep, a.hmid))
-  const bool calib = a.w_up == nullptr;
+  // the calibration instance has a kernel name of its own
+#define SD_GATE_N(T, NRM, CAL)                                                               \
+  SD_ROW_DISPATCH(a.d, launch_rows(K_GATE, gate_kernel<T, NCH, FULL, NRM, CAL>, a.dff, kWave,  \
+                                   a.n_states, lds, s, a.x, a.norm, a.eps,                    \
+                                   (const T*)a.w_gate, a.d, a.dff, a.t, a.gate_in,            \
+                                   a.store_abs, a.act, a.keep))
+#define SD_GATE(T, CAL)          \
+  if (a.norm) {                  \
+    SD_GATE_N(T, true, CAL);     \
+  } else {                       \
+    SD_GATE_N(T, false, CAL);    \
+  }
   if (w_dtype == 1) {
-    if (calib) {
-      SD_GATE_UP(bf16_t, true);
+    if (a.calib) {
+      SD_GATE(bf16_t, true);
     } else {
-      SD_GATE_UP(bf16_t, false);
+      SD_GATE(bf16_t, false);
     }
   } else {
-    if (calib) {
-      SD_GATE_UP(float, true);
+    if (a.calib) {
+      SD_GATE(float, true);
     } else {
-      SD_GATE_UP(float, false);
+      SD_GATE(float, false);
     }
   }
-#undef SD_GATE_UP
+#undef SD_GATE
+#undef SD_GATE_N
 }
 
 }  // namespace sd
