@@ -269,8 +269,8 @@ class Bench:
         alg = {  # algorithmic HBM bytes per launch of each kernel
             "qkv_rope_append": 2 * d * wl.qkv_out,
             "o_residual": 2 * d * wl.n_q_heads * dh,
-            "cats_gate": 2 * d * wl.d_ff,
-            "cats_up_down": 2 * 2 * d * kept,
+            "cats_gate_up": 2 * d * wl.d_ff + 2 * d * kept,
+            "cats_down": 2 * d * kept,
             "attn_partial": n_read * 2 * wl.n_kv_heads * dh * 2,
         }
         out = {}
@@ -291,9 +291,9 @@ KERNEL_SOURCES = {
     "attn_partial": ("attn_kernel", "attn.hip"),
     "attn_combine": ("attn_merge_kernel", "attn.hip"),
     "o_residual": ("o_residual_kernel", "gemv.hip"),
-    "cats_gate": ("gate_kernel", "gemv.hip"),
-    "cats_up_down": ("up_down_kernel", "updown.hip"),
-    "cats_reduce": ("mlp_reduce_kernel", "updown.hip"),
+    "cats_gate_up": ("gate_kernel", "gemv.hip"),
+    "cats_down": ("down_kernel", "down.hip"),
+    "cats_reduce": ("mlp_reduce_kernel", "down.hip"),
 }
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 

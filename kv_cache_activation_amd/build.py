@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsd.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "byte_account.cpp", "profile.cpp", "gemv.hip", "updown.hip", "attn.hip",
+SOURCES = ["api.cpp", "byte_account.cpp", "profile.cpp", "gemv.hip", "down.hip", "attn.hip",
            "attn_naive.hip", "select.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

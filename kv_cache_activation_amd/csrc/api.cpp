@@ -34,7 +34,7 @@ constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t q, attn, pm, pl, pacc, act, keep, mlp_part, lse_part, lse, scores;
+  size_t q, attn, pm, pl, pacc, act, hmid, keep, mlp_part, lse_part, lse, scores;
   size_t kth_hist, kth_state, total;
   int max_splits, sel_chunks;
 };
@@ -57,8 +57,9 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.pl = take(hq * L.max_splits * 4);
   L.pacc = take(hq * L.max_splits * dh * 4);
   L.act = take(ff * 4);
+  L.hmid = take(ff * 4);
   L.keep = take(ff);
-  L.mlp_part = take((size_t)sd::up_down_parts((int)ff) * d * 4);
+  L.mlp_part = take((size_t)sd::down_parts((int)ff) * d * 4);
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
   L.lse = take(hq * (size_t)max_window * 4);
@@ -85,8 +86,8 @@ sd_status check_dims(const sd_dims* dm) {
     return fail(SD_EUNSUPPORTED, "d_model must be a multiple of 8 and at most %d", kMaxWidth);
   if (dm->n_q_heads * dm->head_dim > kMaxWidth)
     return fail(SD_EUNSUPPORTED, "n_q_heads * head_dim must be at most %d", kMaxWidth);
-  if (dm->d_ff > sd::kUdList * sd::kUdMaxParts)
-    return fail(SD_EUNSUPPORTED, "d_ff must be at most %d", sd::kUdList * sd::kUdMaxParts);
+  if (dm->d_ff > sd::kDownList * sd::kDownMaxParts)
+    return fail(SD_EUNSUPPORTED, "d_ff must be at most %d", sd::kDownList * sd::kDownMaxParts);
   if ((dm->w_dtype != SD_F32 && dm->w_dtype != SD_BF16) ||
       (dm->kv_dtype != SD_F32 && dm->kv_dtype != SD_BF16))
     return fail(SD_EUNSUPPORTED, "dtype must be SD_F32 or SD_BF16");
@@ -163,31 +164,29 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   g.norm = norm;
   g.eps = dm.rms_eps;
   g.w_gate = wg;
+  g.w_up = wu;
   g.d = dm.d_model;
   g.dff = dm.d_ff;
   g.t = t;
   g.gate_in = gate_in;
   g.act = act;
   g.keep = keep;
+  g.hmid = reinterpret_cast<float*>(ws + L.hmid);
   g.n_states = 1;
   sd::launch_gate(g, dm.w_dtype, s);
 
-  sd::UpDownArgs u{};
-  u.x = x;
-  u.norm = norm;
-  u.eps = dm.rms_eps;
-  u.w_up = wu;
-  u.w_down_t = wd;
-  u.d = dm.d_model;
-  u.dff = dm.d_ff;
-  u.keep = keep;
-  u.act = act;
-  u.partials = reinterpret_cast<float*>(ws + L.mlp_part);
-  u.y = y;
-  u.accumulate = accumulate;
-  u.idx_out = idx;
-  u.n_kept_out = n_kept;
-  sd::launch_up_down(u, dm.w_dtype, s);
+  sd::DownArgs dn{};
+  dn.w_down_t = wd;
+  dn.d = dm.d_model;
+  dn.dff = dm.d_ff;
+  dn.keep = keep;
+  dn.hmid = g.hmid;
+  dn.partials = reinterpret_cast<float*>(ws + L.mlp_part);
+  dn.y = y;
+  dn.accumulate = accumulate;
+  dn.idx_out = idx;
+  dn.n_kept_out = n_kept;
+  sd::launch_down(dn, dm.w_dtype, s);
 }
 
 }  // namespace

@@ -113,11 +113,34 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// x of lane l ^ OFF (OFF = 8, 16 or 32), with VALU lane exchanges only: a
+// DPP row rotation by 8 (within a row of 16 lanes it is the xor by 8), and
+// gfx950's permlane swaps for rows and half-waves (each swap exchanges the
+// odd rows / upper half of one operand with the even rows / lower half of
+// the other, so swapping x with itself gives each lane its partner in one of
+// the two results).  An LDS permute per exchange costs a round trip through
+// the LDS unit instead; this is on the path of every dot-product reduction.
+template <int OFF>
+__device__ __forceinline__ float xor_lanes(float x) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "xor by 8, 16 or 32");
+  if constexpr (OFF == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane_id() & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane_id() & 32) ? r[0] : r[1]);
+  }
+}
+
 // Full-wave sum and max (every lane gets the result).
 __device__ __forceinline__ float wave_sum(float x) {
   x = group_sum<16>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+  x += xor_lanes<16>(x);
+  x += xor_lanes<32>(x);
   return x;
 }
 
@@ -126,14 +149,25 @@ __device__ __forceinline__ int wave_sum_int(int x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  x = group_max<16>(x);
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+// Inclusive prefix sum over the wave's lanes (DPP row shifts, then row
+// broadcasts of lanes 15 and 31 into the following rows).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ float wave_max(float x) {
+  x = group_max<16>(x);
+  x = fmaxf(x, xor_lanes<16>(x));
+  x = fmaxf(x, xor_lanes<32>(x));
+  return x;
+}
+
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 

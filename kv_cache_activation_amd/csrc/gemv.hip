@@ -202,44 +202,73 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
   }
 }
 
-// ------------------------------------------------------------------ CATS gate
+// ------------------------------------------------------------------ CATS gate (+ up)
 // x = RMSNorm(h) * mlp_norm (NORM; x itself otherwise); a_i = SiLU(W_gate[i] . x)
 // (or a_i read from `act` when gate_in); act[i] = a_i (|a_i| when store_abs);
 // keep[i] = 1 iff t < 0 or |a_i| > t, else 0 (keep may be null).  The gate is
-// dense in CATS: every row is read, so this is a plain row-streaming GEMV.
-// blockIdx.y selects one of several input states (calibration); the
-// calibration instance (CALIB) only has a kernel name of its own.
+// dense in CATS: every row is read, so the first phase is a plain
+// row-streaming GEMV over the wave's rows.  With W_up given, each wave then
+// reads the up rows of its kept channels only, two at a time with both
+// loads issued together, and writes hmid_i = a_i (W_up[i] . x) (hmid of a
+// dropped channel is left as it was and never read).  blockIdx.y selects one
+// of several input states (calibration); the calibration instance (CALIB)
+// only has a kernel name of its own.
 template <typename WT, int NCH, bool FULL, bool NORM, bool CALIB>
 __global__ __launch_bounds__(kThreads) void gate_kernel(
     const float* __restrict__ xin, const float* __restrict__ nw, float eps,
-    const WT* __restrict__ Wg, int d, int dff, float t, int gate_in, int store_abs,
-    float* __restrict__ act, uint8_t* __restrict__ keep) {
+    const WT* __restrict__ Wg, const WT* __restrict__ Wu, int d, int dff, float t, int gate_in,
+    int store_abs, float* __restrict__ act, uint8_t* __restrict__ keep,
+    float* __restrict__ hmid) {
   xin += (size_t)blockIdx.y * d;
   act += (size_t)blockIdx.y * dff;
   const int d8 = d >> 3;
   const int lane = lane_id();
   const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int n_waves = gridDim.x * kWavesPerBlock;
-  if (gate_in) {  // mask from the caller's activations; no GEMV
-    for (int r = wave * kWave + lane; r < dff; r += n_waves * kWave)
-      keep[r] = t < 0.f || fabsf(act[r]) > t;
-    return;
-  }
   const int n = wave < dff ? (dff - wave + n_waves - 1) / n_waves : 0;  // <= 64
   extern __shared__ float xs[];
   XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), NORM> st;
   st.load(xin, nw, d);  // x first: the staging then waits for it alone
   Row<WT, NCH> ra, rb;
-  load_row<FULL>(ra, Wg, d, n > 0 ? wave : 0, d8);  // in flight during the staging
+  if (!gate_in) load_row<FULL>(ra, Wg, d, n > 0 ? wave : 0, d8);  // in flight during the staging
   const float rs = st.finish(d, eps, NORM, xs);
   if (n == 0) return;  // wave-uniform, after the workgroup barrier
-  const float s = stream_rows<FULL>(Wg, d, d8, n, xs, ra, rb,
-                                    [&](int k) { return wave + k * n_waves; });
+  // lane k: channel wave + k W (k < n)
+  const int r = wave + lane * n_waves;
+  float a = 0.f;
+  if (gate_in) {
+    if (lane < n) a = act[r];
+  } else {
+    const float s = stream_rows<FULL>(Wg, d, d8, n, xs, ra, rb,
+                                      [&](int k) { return wave + k * n_waves; });
+    a = silu(s * rs);
+  }
+  const bool kept = lane < n && (t < 0.f || fabsf(a) > t);
+  float hm = 0.f;
+  if (!CALIB && Wu) {
+    uint64_t km = __ballot(kept);  // wave-uniform
+#pragma unroll 1
+    while (km) {
+      const int k0 = __ffsll((unsigned long long)km) - 1;
+      km &= km - 1;
+      const int k1 = km ? __ffsll((unsigned long long)km) - 1 : -1;
+      if (k1 >= 0) km &= km - 1;
+      load_row<FULL>(ra, Wu, d, wave + k0 * n_waves, d8);
+      if (k1 >= 0) load_row<FULL>(rb, Wu, d, wave + k1 * n_waves, d8);
+      asm volatile("" ::: "memory");  // x from LDS per row, as in stream_rows
+      const float u0 = row_dot<FULL>(ra, xs, d8) * rs;
+      if (lane == k0) hm = a * u0;
+      if (k1 >= 0) {
+        asm volatile("" ::: "memory");
+        const float u1 = row_dot<FULL>(rb, xs, d8) * rs;
+        if (lane == k1) hm = a * u1;
+      }
+    }
+  }
   if (lane < n) {
-    const int r = wave + lane * n_waves;
-    const float a = silu(s * rs);
-    act[r] = store_abs ? fabsf(a) : a;
-    if (!CALIB && keep) keep[r] = t < 0.f || fabsf(a) > t;
+    if (!gate_in) act[r] = store_abs ? fabsf(a) : a;
+    if (!CALIB && keep) keep[r] = kept;
+    if (!CALIB && Wu && kept) hmid[r] = hm;
   }
 }
 
@@ -341,10 +370,10 @@ void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s) {
   const size_t lds = (size_t)a.d * sizeof(float);
   // the calibration instance has a kernel name of its own
 #define SD_GATE_N(T, NRM, CAL)                                                               \
-  SD_ROW_DISPATCH(a.d, launch_rows(K_GATE, gate_kernel<T, NCH, FULL, NRM, CAL>, a.dff, kWave,  \
+  SD_ROW_DISPATCH(a.d, launch_rows(K_GATE_UP, gate_kernel<T, NCH, FULL, NRM, CAL>, a.dff, kWave,  \
                                    a.n_states, lds, s, a.x, a.norm, a.eps,                    \
-                                   (const T*)a.w_gate, a.d, a.dff, a.t, a.gate_in,            \
-                                   a.store_abs, a.act, a.keep))
+                                   (const T*)a.w_gate, (const T*)a.w_up, a.d, a.dff, a.t,     \
+                                   a.gate_in, a.store_abs, a.act, a.keep, a.hmid))
 #define SD_GATE(T, CAL)          \
   if (a.norm) {                  \
     SD_GATE_N(T, true, CAL);     \

@@ -12,7 +12,7 @@ namespace sd {
 
 // Kernel kinds for the opt-in profiler (order = names in profile.cpp).
 enum KernelKind {
-  K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE, K_UP_DOWN, K_MLP_REDUCE, K_SEL_LSE,
+  K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_MLP_REDUCE, K_SEL_LSE,
   K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_MASKED_SCORES,
   K_MASKED_SOFTMAX, K_MASKED_PV, K_COUNT
 };
@@ -60,31 +60,30 @@ struct GateArgs {
   const float* norm;  // nullptr: x is used as is
   float eps;
   const void* w_gate;
+  const void* w_up;   // nullptr: no up projection
   int d, dff;
   float t;
   int gate_in, store_abs, calib;
   float* act;
   uint8_t* keep;      // nullptr: activations only (calibration)
+  float* hmid;        // a_i (W_up[i] . x) for kept channels
   int n_states;       // batched gate for calibration; 1 otherwise
 };
 
-// Up/down over the kept channels: the kept list is split into P equal slices
-// (P = up_down_parts(d_ff) workgroups, each at most kUdList channels).
-constexpr int kUdList = 64;
-constexpr int kUdMinParts = 256;
-constexpr int kUdMaxParts = 512;  // d_ff <= kUdList * kUdMaxParts
-int up_down_parts(int dff);
+// Down projection over the kept channels: the kept list is split into P
+// equal slices (P = down_parts(d_ff) workgroups, each at most kDownList
+// channels).
+constexpr int kDownList = 64;
+constexpr int kDownMinParts = 256;
+constexpr int kDownMaxParts = 512;  // d_ff <= kDownList * kDownMaxParts
+int down_parts(int dff);
 
-struct UpDownArgs {
-  const float* x;
-  const float* norm;
-  float eps;
-  const void* w_up;
+struct DownArgs {
   const void* w_down_t;
   int d, dff;
   const uint8_t* keep;
-  const float* act;
-  float* partials;     // [up_down_parts(dff), d]
+  const float* hmid;
+  float* partials;     // [down_parts(dff), d]
   float* y;
   int accumulate;      // y += result instead of y = result
   int32_t* idx_out;    // optional ascending kept list
@@ -128,7 +127,7 @@ void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s);
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,
               hipStream_t s);
 void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s);
-void launch_up_down(const UpDownArgs& a, int w_dtype, hipStream_t s);
+void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s);
 // Masked dense attention over every allocated row (rows >= n_ctx masked): scores
 // of each query head into `scores` [h_q, cap], a row softmax, then P.V in

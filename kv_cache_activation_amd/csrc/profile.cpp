@@ -37,8 +37,8 @@ hipEvent_t take_event() {
 }
 
 const char* kKindNames[K_COUNT] = {
-    "qkv_rope_append", "attn_partial",  "attn_combine",    "o_residual",    "cats_gate",
-    "cats_up_down",    "cats_reduce", "sel_lse_partial", "sel_lse_final", "sel_score",
+    "qkv_rope_append", "attn_partial",  "attn_combine",    "o_residual",    "cats_gate_up",
+    "cats_down",       "cats_reduce", "sel_lse_partial", "sel_lse_final", "sel_score",
     "sel_topk",        "sel_gather",    "kth_select",      "masked_scores", "masked_softmax",
     "masked_pv"};
 
