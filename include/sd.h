@@ -222,7 +222,7 @@ typedef struct {
   void* v_sel;
   int32_t cap_sel;
   int32_t n_sel;           /* valid gathered rows; advanced by one when k_sel != NULL */
-  uint8_t* mask_out;       /* optional [d_ff]: receives 1 for kept channels, else 0 */
+  uint8_t* mask_out;       /* optional [d_ff], 16-byte aligned: receives 1 for kept channels, else 0 */
   int32_t window_keep;     /* SD_KV_WINDOW: entries read (sinks included) */
   int32_t window_sink;     /* SD_KV_WINDOW: sink entries among them */
 } sd_layer;
