@@ -15,7 +15,7 @@ channels zeroed, so the oracle computes it masked-dense
 
 and gathering only the kept channels is the kernel's way of reaching it.
 
-Readings (also in DESIGN.md):
+Readings:
 * keep channel i iff |a_i| > t (strict); t < 0 means dense.  The [SATS] text
   drops values "below" t, which would keep |a| == t; the strict form is the
   one the hot path states, and |a| == t is then dropped.

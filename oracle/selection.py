@@ -6,7 +6,7 @@ queries (the observation window), a few sink tokens plus the best-scoring
 entries of each KV head are kept up to a keep ratio, and the kept entries are
 gathered into one contiguous buffer that later steps read and extend.
 
-Readings where the page is silent or garbled (each also listed in the design doc):
+Readings where the page is silent or garbled:
 
 * Window size w is a parameter (the page's text says 64; [CateKV] B.1 gives 32
   for SnapKV; the workloads here use 32).

@@ -29,11 +29,16 @@ MUTS = [
  ("byte_account.py", "return 2 * dm.d_model * dm.d_ff", "return 3 * dm.d_model * dm.d_ff"),
  ("byte_account.py", "return dm.d_model * qkv_out + dm.n_q_heads * dm.head_dim * dm.d_model", "return dm.d_model * qkv_out"),
  ("byte_account.py", "den = 2.0 * batch * dm.n_kv_heads", "den = 2.0 * dm.n_kv_heads"),
+ ("teal.py", "return np.abs(x_f32) > t32", "return np.abs(x_f32) >= t32"),
+ ("teal.py", "g = linear_masked(layer.w_gate, x2, m_m)", "g = linear_masked(layer.w_gate, x, m_m)"),
+ ("teal.py", "m_d = mask_of(DOWN_IN, hmid)", "m_d = mask_of(DOWN_IN, u)"),
+ ("teal.py", "h = h + linear_masked(layer.w_o, o, m_o)", "h = h + linear_masked(layer.w_o, o, m_a)"),
+ ("teal.py", "hmid = cats.silu(g) * u", "hmid = g * u"),
 ]
 
 PIN_FILES = ["tests/test_oracle_byte_account.py", "tests/test_oracle_selection.py",
              "tests/test_oracle_attention.py", "tests/test_oracle_cats.py",
-             "tests/test_oracle_step.py"]
+             "tests/test_oracle_step.py", "tests/test_oracle_teal.py"]
 
 
 @pytest.mark.parametrize("fname,old,new", MUTS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTS)])
