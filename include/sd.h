@@ -80,7 +80,9 @@ enum {
   SD_MLP_SPARSE = 8u, /* sd_decode_step: CATS-threshold the MLP */
   SD_KV_WINDOW = 16u, /* sd_decode_step: attend over sinks + recent rows of the full cache */
   SD_ATTN_MASKED = 32u, /* sd_decode_step: dense attention by the masked comparison path */
-  SD_ATTN_FUSED = 64u   /* sd_decode_step: dense attention by the fused (no split-K) path */
+  SD_ATTN_FUSED = 64u,  /* sd_decode_step: dense attention by the fused (no split-K) path */
+  SD_PROJ_TEAL = 128u,  /* sd_decode_step: TEAL-threshold the inputs of all seven projections */
+  SD_ACCUMULATE = 256u  /* sd_teal_gemv: y += result instead of y = result */
 };
 
 /* projection sets of the byte account */
@@ -203,6 +205,34 @@ sd_status sd_sparse_mlp(const sd_dims* dims, const float* x, const float* norm_w
                         int32_t* n_kept, uint32_t flags, void* ws, size_t ws_bytes,
                         void* stream);
 
+/*
+ * sd_teal_gemv -- one TEAL-sparse projection ([Cross] §3.2 "Sparse Branches",
+ * §4.1 "Setup": the projection keeps only the input activation channels whose
+ * magnitude clears a calibrated threshold and loads only their weights).
+ *
+ * x        [d_in] float32 input; if norm_w is not NULL it is first normalised,
+ *          x_hat = x / sqrt(mean(x^2) + rms_eps) * norm_w, else x_hat = x.
+ * Input channel j is kept iff threshold < 0 or |x_hat_j| > threshold (strict,
+ * decided in float32).
+ * w_t      [d_in, d_out] in dims->w_dtype: the projection's weight transposed,
+ *          so a kept channel is one contiguous row; only kept rows are read.
+ * w2_t     optional second matrix [d_in, d_out] with the same input (gate and
+ *          up), its result in y2; NULL for one projection.
+ * y        [d_out] float32 out: sum over kept j of x_hat_j w_t[j]; with
+ *          SD_ACCUMULATE it is added to y.  Fixed summation order.
+ * idx      [d_in] int32 out or NULL: the kept channels ascending in
+ *          idx[0..n_kept-1].  n_kept [1] int32 out (device) or NULL.
+ * Sizes:   d_in, d_out multiples of 8; d_in <= 32768; the workspace of
+ *          sd_workspace_bytes(dims, ...) covers any d_in, d_out up to the
+ *          widths of dims (d_model, d_ff, n_q_heads d_h, (n_q + 2 n_kv) d_h),
+ *          else ENOSPC.
+ * Errors: EINVAL for bad pointers or sizes.
+ */
+sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const float* norm_w,
+                       float threshold, const void* w_t, const void* w2_t, int32_t d_out,
+                       float* y, float* y2, uint32_t flags, int32_t* idx, int32_t* n_kept,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* One decoder layer's state for sd_decode_step. */
 typedef struct {
   const float* attn_norm;  /* [d] */
@@ -225,6 +255,16 @@ typedef struct {
   uint8_t* mask_out;       /* optional [d_ff], 16-byte aligned: receives 1 for kept channels, else 0 */
   int32_t window_keep;     /* SD_KV_WINDOW: entries read (sinks included) */
   int32_t window_sink;     /* SD_KV_WINDOW: sink entries among them */
+  /* SD_PROJ_TEAL: the projections transposed (input-major) and the four
+   * input thresholds, attention input, O input, MLP input, down input
+   * (w_down_t above serves both modes) */
+  const void* w_qkv_t;     /* [d, (h_q + 2 h_kv) d_h] */
+  const void* w_o_t;       /* [h_q d_h, d] */
+  const void* w_gate_t;    /* [d, d_ff] */
+  const void* w_up_t;      /* [d, d_ff] */
+  float teal_t[4];
+  uint8_t* teal_masks_out; /* optional, 16-byte aligned: the four keep masks (1 kept, 0 dropped),
+                              [d | h_q d_h | d | d_ff] bytes in that order */
 } sd_layer;
 
 /*
@@ -237,6 +277,11 @@ typedef struct {
  *   0..n_full (dense) or 0..n_sel of the gathered buffer (SD_KV_SPARSE), scale
  *   1/sqrt(d_h); h += w_o attn; x = RMSNorm(h) mlp_norm; h += CATS-MLP(x) with
  *   the layer threshold under SD_MLP_SPARSE, dense otherwise.
+ *   SD_PROJ_TEAL makes all seven projections TEAL-sparse instead (sd_teal_gemv
+ *   semantics, w_*_t weights, thresholds teal_t): the attention input feeds
+ *   W_q, W_k, W_v under one mask, the attention output W_o, the MLP input
+ *   W_gate and W_up under one mask, and SiLU(gate) * up the down projection;
+ *   it excludes SD_MLP_SPARSE.
  *   SD_KV_WINDOW attends instead over rows [0, window_sink) and the most recent
  *   window_keep - window_sink rows of the full cache (after the append), read
  *   in place ([Cross] §4.1, §4.4).  SD_ATTN_MASKED / SD_ATTN_FUSED run dense

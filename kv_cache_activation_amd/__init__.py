@@ -27,10 +27,11 @@ SD_OK, SD_EINVAL, SD_ENOSPC, SD_EUNSUPPORTED, SD_EHIP = range(5)
 SD_F32, SD_BF16 = 0, 1
 SD_SCORES_IN, SD_GATE_IN, SD_KV_SPARSE, SD_MLP_SPARSE = 1, 2, 4, 8
 SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED = 16, 32, 64
+SD_PROJ_TEAL, SD_ACCUMULATE = 128, 256
 SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 
 EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_decode_attn", "sd_decode_attn_window",
-           "sd_decode_attn_baseline", "sd_sparse_mlp",
+           "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
            "sd_decode_step", "sd_byte_account", "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
@@ -55,7 +56,10 @@ class sd_layer(ctypes.Structure):
                 ("k_sel", ctypes.c_void_p), ("v_sel", ctypes.c_void_p),
                 ("cap_sel", ctypes.c_int32), ("n_sel", ctypes.c_int32),
                 ("mask_out", ctypes.c_void_p), ("window_keep", ctypes.c_int32),
-                ("window_sink", ctypes.c_int32)]
+                ("window_sink", ctypes.c_int32),
+                ("w_qkv_t", ctypes.c_void_p), ("w_o_t", ctypes.c_void_p),
+                ("w_gate_t", ctypes.c_void_p), ("w_up_t", ctypes.c_void_p),
+                ("teal_t", ctypes.c_float * 4), ("teal_masks_out", ctypes.c_void_p)]
 
 
 class sd_byte_record(ctypes.Structure):
@@ -93,6 +97,9 @@ _lib.sd_decode_attn_baseline.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I
 _lib.sd_sparse_mlp.restype = _I
 _lib.sd_sparse_mlp.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _P, _P, _F, _P, _P, _P, _P,
                                _U, _P, _S, _P]
+_lib.sd_teal_gemv.restype = _I
+_lib.sd_teal_gemv.argtypes = [ctypes.POINTER(sd_dims), _P, _I, _P, _F, _P, _P, _I, _P, _P, _U,
+                              _P, _P, _P, _S, _P]
 _lib.sd_decode_step.restype = _I
 _lib.sd_decode_step.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_layer), _I, _P,
                                 _U, _P, _S, _P]
@@ -193,6 +200,14 @@ def sd_sparse_mlp(dims, x, norm_w, w_gate, w_up, w_down_t, threshold, y, act, id
     _check(_lib.sd_sparse_mlp(ctypes.byref(dims), _ptr(x), _ptr(norm_w), _ptr(w_gate), _ptr(w_up),
                               _ptr(w_down_t), threshold, _ptr(y), _ptr(act), _ptr(idx),
                               _ptr(n_kept), flags, p, nb, _stream(stream)))
+
+
+def sd_teal_gemv(dims, x, d_in, norm_w, threshold, w_t, w2_t, d_out, y, y2, flags, idx, n_kept,
+                 ws, stream=None) -> None:
+    p, nb = _ws(ws)
+    _check(_lib.sd_teal_gemv(ctypes.byref(dims), _ptr(x), d_in, _ptr(norm_w), threshold, _ptr(w_t),
+                             _ptr(w2_t), d_out, _ptr(y), _ptr(y2), flags, _ptr(idx), _ptr(n_kept),
+                             p, nb, _stream(stream)))
 
 
 def sd_decode_step(dims, layers, pos, hidden, mode, ws, stream=None) -> None:

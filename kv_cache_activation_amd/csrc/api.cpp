@@ -3,6 +3,7 @@
 // enqueued, so a failing call leaves the stream untouched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -34,7 +35,8 @@ constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t q, attn, pm, pl, pacc, act, hmid, keep, mlp_part, lse_part, lse, scores;
+  size_t q, attn, pm, pl, pacc, act, hmid, keep, mlp_part, teal_part, lse_part, lse, scores;
+  size_t teal_part_floats;
   size_t kth_hist, kth_state, total;
   int max_splits, sel_chunks;
 };
@@ -60,6 +62,18 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.hmid = take(ff * 4);
   L.keep = take(ff);
   L.mlp_part = take((size_t)sd::down_parts((int)ff) * d * 4);
+  {  // TEAL partials: the largest of the layer's four sparse projections
+    const int qkv_out = (int)((hq + 2 * hkv) * dh);
+    auto need = [](int din, int dout, int mats) {
+      return (size_t)sd::teal_grid(din, dout).parts * dout * mats;
+    };
+    size_t f = need((int)d, qkv_out, 1);
+    f = std::max(f, need((int)(hq * dh), (int)d, 1));
+    f = std::max(f, need((int)d, (int)ff, 2));
+    f = std::max(f, need((int)ff, (int)d, 1));
+    L.teal_part_floats = f;
+    L.teal_part = take(f * 4);
+  }
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
   L.lse = take(hq * (size_t)max_window * 4);
@@ -187,6 +201,31 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   dn.idx_out = idx;
   dn.n_kept_out = n_kept;
   sd::launch_down(dn, dm.w_dtype, s);
+}
+
+// One TEAL projection's gathered GEMV into the layout's partials (part0, and
+// part1 right after it when w1 is given); the caller launches the reduce.
+void enqueue_teal(int kind, const sd_dims& dm, const Layout& L, char* ws, const float* x,
+                  int d_in, const float* norm, float t, const void* w0, const void* w1, int d_out,
+                  uint8_t* keep_out, hipStream_t s, int32_t* idx = nullptr,
+                  int32_t* n_kept = nullptr) {
+  const sd::TealGrid g = sd::teal_grid(d_in, d_out);
+  sd::TealArgs a{};
+  a.kind = kind;
+  a.x = x;
+  a.d_in = d_in;
+  a.norm = norm;
+  a.eps = dm.rms_eps;
+  a.t = t;
+  a.w0 = w0;
+  a.w1 = w1;
+  a.d_out = d_out;
+  a.part0 = reinterpret_cast<float*>(ws + L.teal_part);
+  a.part1 = w1 ? a.part0 + (size_t)g.parts * d_out : nullptr;
+  a.idx_out = idx;
+  a.n_kept_out = n_kept;
+  a.keep_out = keep_out;
+  sd::launch_teal(a, dm.w_dtype, s);
 }
 
 }  // namespace
@@ -347,6 +386,41 @@ sd_status sd_sparse_mlp(const sd_dims* dims, const float* x, const float* norm_w
   return check_launch("sd_sparse_mlp");
 }
 
+sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const float* norm_w,
+                       float threshold, const void* w_t, const void* w2_t, int32_t d_out,
+                       float* y, float* y2, uint32_t flags, int32_t* idx, int32_t* n_kept,
+                       void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (!aligned(x) || (norm_w && !aligned(norm_w)) || !aligned(w_t) || !aligned(y) ||
+      !aligned(ws) || (idx && !aligned(idx)) || (w2_t && (!aligned(w2_t) || !aligned(y2))))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (flags & ~(uint32_t)SD_ACCUMULATE) return fail(SD_EINVAL, "unknown flags 0x%x", flags);
+  if (d_in < 8 || d_out < 8 || d_in % 8 || d_out % 8)
+    return fail(SD_EINVAL, "d_in and d_out must be positive multiples of 8");
+  if (d_in > sd::kTealList * sd::kTealMaxParts)
+    return fail(SD_EUNSUPPORTED, "d_in must be at most %d", sd::kTealList * sd::kTealMaxParts);
+  if (std::isnan(threshold)) return fail(SD_EINVAL, "threshold is NaN");
+  const Layout L = make_layout(*dims, 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  const sd::TealGrid g = sd::teal_grid(d_in, d_out);
+  const size_t need = (size_t)g.parts * d_out * (w2_t ? 2 : 1);
+  if (need > L.teal_part_floats)
+    return fail(SD_ENOSPC, "d_in %d x d_out %d needs %zu partial floats, the workspace holds %zu",
+                d_in, d_out, need, L.teal_part_floats);
+  char* wsb = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  enqueue_teal(sd::K_TEAL_O, *dims, L, wsb, x, d_in, norm_w, threshold, w_t, w2_t, d_out,
+               nullptr, s, idx, n_kept);
+  float* part = reinterpret_cast<float*>(wsb + L.teal_part);
+  const int acc = (flags & SD_ACCUMULATE) ? 1 : 0;
+  sd::launch_teal_reduce(part, nullptr, g.parts, d_out, y, acc, 0, sd::K_TEAL_REDUCE, s);
+  if (w2_t)
+    sd::launch_teal_reduce(part + (size_t)g.parts * d_out, nullptr, g.parts, d_out, y2, acc, 0,
+                           sd::K_TEAL_REDUCE, s);
+  return check_launch("sd_teal_gemv");
+}
+
 sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers, int32_t pos,
                          float* hidden, uint32_t mode, void* ws, size_t ws_bytes, void* stream) {
   sd_status st = check_dims(dims);
@@ -357,8 +431,11 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
   const bool kv_sparse = mode & SD_KV_SPARSE, mlp_sparse = mode & SD_MLP_SPARSE;
   const bool kv_window = mode & SD_KV_WINDOW;
   const bool masked = mode & SD_ATTN_MASKED, fused = mode & SD_ATTN_FUSED;
-  if (mode & ~(uint32_t)(SD_KV_SPARSE | SD_MLP_SPARSE | SD_KV_WINDOW | SD_ATTN_MASKED | SD_ATTN_FUSED))
+  const bool teal = mode & SD_PROJ_TEAL;
+  if (mode & ~(uint32_t)(SD_KV_SPARSE | SD_MLP_SPARSE | SD_KV_WINDOW | SD_ATTN_MASKED |
+                         SD_ATTN_FUSED | SD_PROJ_TEAL))
     return fail(SD_EINVAL, "unknown mode bits 0x%x", mode);
+  if (teal && mlp_sparse) return fail(SD_EINVAL, "SD_PROJ_TEAL excludes SD_MLP_SPARSE");
   if ((int)kv_sparse + (int)kv_window + (int)masked + (int)fused > 1)
     return fail(SD_EINVAL, "at most one of SD_KV_SPARSE, SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED");
   int max_cap = 0;
@@ -368,10 +445,19 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
   if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
-    if (!aligned(l.attn_norm) || !aligned(l.w_qkv) || !aligned(l.w_o) || !aligned(l.mlp_norm) ||
-        !aligned(l.w_gate) || !aligned(l.w_up) || !aligned(l.w_down_t) || !aligned(l.k_full) ||
-        !aligned(l.v_full))
+    if (!aligned(l.attn_norm) || !aligned(l.mlp_norm) || !aligned(l.w_down_t) ||
+        !aligned(l.k_full) || !aligned(l.v_full))
       return fail(SD_EINVAL, "layer %d: null or misaligned pointer", i);
+    if (teal) {
+      if (!aligned(l.w_qkv_t) || !aligned(l.w_o_t) || !aligned(l.w_gate_t) || !aligned(l.w_up_t))
+        return fail(SD_EINVAL, "layer %d: SD_PROJ_TEAL needs the transposed weights", i);
+      for (int k = 0; k < 4; ++k)
+        if (std::isnan(l.teal_t[k])) return fail(SD_EINVAL, "layer %d: TEAL threshold is NaN", i);
+      if (l.teal_masks_out && !aligned(l.teal_masks_out))
+        return fail(SD_EINVAL, "layer %d: misaligned teal_masks_out", i);
+    } else if (!aligned(l.w_qkv) || !aligned(l.w_o) || !aligned(l.w_gate) || !aligned(l.w_up)) {
+      return fail(SD_EINVAL, "layer %d: null or misaligned pointer", i);
+    }
     if (l.n_full < 0 || l.n_full >= l.cap_full)
       return fail(SD_ENOSPC, "layer %d: full cache has no free row (n_full %d, cap %d)", i,
                   l.n_full, l.cap_full);
@@ -429,7 +515,17 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     qa.v_sel = has_sel ? l.v_sel : nullptr;
     qa.cap_sel = l.cap_sel;
     qa.row_sel = l.n_sel;
-    sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
+    const int qkv_out = (hq + 2 * hkv) * dh;
+    uint8_t* tm = teal ? l.teal_masks_out : nullptr;  // [d | h_q d_h | d | d_ff]
+    if (teal) {
+      const sd::TealGrid g = sd::teal_grid(d, qkv_out);
+      enqueue_teal(sd::K_TEAL_QKV, *dims, L, wsb, hidden, d, l.attn_norm, l.teal_t[0], l.w_qkv_t,
+                   nullptr, qkv_out, tm, s);
+      sd::launch_teal_qkv_reduce(reinterpret_cast<float*>(wsb + L.teal_part), g.parts, qa,
+                                 dims->kv_dtype, s);
+    } else {
+      sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
+    }
 
     const void* kc = kv_sparse ? l.k_sel : l.k_full;
     const void* vc = kv_sparse ? l.v_sel : l.v_full;
@@ -445,6 +541,28 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, sink, shift, scale,
                  auto_splits(n_ctx, hkv), path, attn, nullptr, s);
 
+    if (teal) {
+      float* part = reinterpret_cast<float*>(wsb + L.teal_part);
+      float* hmid = reinterpret_cast<float*>(wsb + L.hmid);
+      const int ff = dims->d_ff;
+      // O: attention output -> h += W_o (mask * attn)
+      enqueue_teal(sd::K_TEAL_O, *dims, L, wsb, attn, hq * dh, nullptr, l.teal_t[1], l.w_o_t,
+                   nullptr, d, tm ? tm + d : nullptr, s);
+      sd::launch_teal_reduce(part, nullptr, sd::teal_grid(hq * dh, d).parts, d, hidden, 1, 0,
+                             sd::K_TEAL_REDUCE, s);
+      // gate and up share the MLP input; hmid = SiLU(gate) * up
+      enqueue_teal(sd::K_TEAL_GATE_UP, *dims, L, wsb, hidden, d, l.mlp_norm, l.teal_t[2],
+                   l.w_gate_t, l.w_up_t, ff, tm ? tm + d + hq * dh : nullptr, s);
+      const int pg = sd::teal_grid(d, ff).parts;
+      sd::launch_teal_reduce(part, part + (size_t)pg * ff, pg, ff, hmid, 0, 1, sd::K_TEAL_REDUCE,
+                             s);
+      // down: h += W_down (mask * hmid)
+      enqueue_teal(sd::K_TEAL_DOWN, *dims, L, wsb, hmid, ff, nullptr, l.teal_t[3], l.w_down_t,
+                   nullptr, d, tm ? tm + 2 * d + hq * dh : nullptr, s);
+      sd::launch_teal_reduce(part, nullptr, sd::teal_grid(ff, d).parts, d, hidden, 1, 0,
+                             sd::K_TEAL_REDUCE, s);
+      continue;
+    }
     sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, s);
 
     uint8_t* keep = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + L.keep);

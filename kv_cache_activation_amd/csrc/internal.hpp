@@ -14,7 +14,8 @@ namespace sd {
 enum KernelKind {
   K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_MLP_REDUCE, K_SEL_LSE,
   K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_MASKED_SCORES,
-  K_MASKED_SOFTMAX, K_MASKED_PV, K_COUNT
+  K_MASKED_SOFTMAX, K_MASKED_PV, K_TEAL_QKV, K_TEAL_QKV_REDUCE, K_TEAL_O, K_TEAL_GATE_UP,
+  K_TEAL_DOWN, K_TEAL_REDUCE, K_COUNT
 };
 
 // Start/stop events of one launch of kind `kind` while profiling is on (both
@@ -90,6 +91,33 @@ struct DownArgs {
   int32_t* n_kept_out; // optional
 };
 
+// TEAL projection: y = sum over kept inputs j (|x_j| > t, after the optional
+// RMSNorm) of x_j w_t[j], w_t [d_in, d_out]; P slices of the kept list (each
+// at most kTealList channels) x column tiles of 4096 outputs.
+constexpr int kTealList = 64;
+constexpr int kTealMinBlocks = 256;  // slices x tiles, at least
+constexpr int kTealMaxParts = 512;   // d_in <= kTealList * kTealMaxParts
+struct TealGrid {
+  int parts, tiles;
+};
+TealGrid teal_grid(int d_in, int d_out);
+
+struct TealArgs {
+  int kind;            // profiler kind of this projection
+  const float* x;
+  int d_in;
+  const float* norm;   // nullptr: no RMSNorm
+  float eps, t;        // t < 0: keep every channel
+  const void* w0;      // [d_in, d_out]
+  const void* w1;      // optional second matrix with the same input (gate and up)
+  int d_out;
+  float* part0;        // [parts, d_out]
+  float* part1;
+  int32_t* idx_out;    // optional ascending kept list
+  int32_t* n_kept_out; // optional
+  uint8_t* keep_out;   // optional keep bytes [d_in]
+};
+
 struct AttnArgs {
   const float* q;
   const void* k;
@@ -128,6 +156,13 @@ void launch_o(const float* attn, const void* w, int din, int dout, float* h, int
               hipStream_t s);
 void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s);
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
+void launch_teal(const TealArgs& a, int w_dtype, hipStream_t s);
+// y (+)= column sums of the partials, or y = SiLU(sums of part0) * sums of part1
+void launch_teal_reduce(const float* part0, const float* part1, int parts, int d_out, float* y,
+                        int accumulate, int swiglu, int kind, hipStream_t s);
+// QKV epilogue over the column sums: RoPE, q out, k and v appended (a.h is unused)
+void launch_teal_qkv_reduce(const float* part, int parts, const QkvArgs& a, int kv_dtype,
+                            hipStream_t s);
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s);
 // Masked dense attention over every allocated row (rows >= n_ctx masked): scores
 // of each query head into `scores` [h_q, cap], a row softmax, then P.V in

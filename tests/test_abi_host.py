@@ -32,8 +32,34 @@ def test_every_declared_symbol_is_exported():
 
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
-    assert ctypes.sizeof(sd.sd_layer) == 128
+    assert ctypes.sizeof(sd.sd_layer) == 184
     assert ctypes.sizeof(sd.sd_byte_record) == 80
+
+
+def test_struct_layout_matches_the_c_compiler(tmp_path):
+    # every field offset of the ctypes mirrors equals the C compiler's offsetof
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("no C compiler")
+    structs = {"sd_dims": sd.sd_dims, "sd_layer": sd.sd_layer, "sd_byte_record": sd.sd_byte_record}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "sd.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(tmp_path / "layout")], check=True)
+    out = subprocess.run([str(tmp_path / "layout")], capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    got = dict(l.split() for l in out if l)
+    for name, cls in structs.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, (name, f)
 
 
 DIMS8B = dict(d_model=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, d_ff=14336)
@@ -169,6 +195,52 @@ def test_window_and_baseline_reject_before_launch():
         sd.sd_decode_attn_baseline(_dims(), FAKE, FAKE, FAKE, 100000, 50, 0.1, sd.SD_ATTN_MASKED,
                                    FAKE, None, small, 0)
     assert e.value.status == sd.SD_ENOSPC
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(d_in=12), sd.SD_EINVAL),
+    (dict(d_out=0), sd.SD_EINVAL),
+    (dict(d_in=40000), sd.SD_EUNSUPPORTED),
+    (dict(x=FAKE + 4), sd.SD_EINVAL),
+    (dict(t=float("nan")), sd.SD_EINVAL),
+    (dict(flags=1), sd.SD_EINVAL),
+    (dict(w2=FAKE, y2=None), sd.SD_EINVAL),
+    (dict(d_in=14336, d_out=14336, w2=FAKE, y2=FAKE), sd.SD_ENOSPC),
+    (dict(ws_bytes=64), sd.SD_ENOSPC),
+])
+def test_teal_gemv_rejects_before_launch(case, status):
+    a = dict(x=FAKE, d_in=4096, d_out=4096, t=0.5, w2=None, y2=None, flags=0, ws_bytes=1 << 30)
+    a.update(case)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_teal_gemv(_dims(), a["x"], a["d_in"], None, a["t"], FAKE, a["w2"], a["d_out"], FAKE,
+                        a["y2"], a["flags"], None, None, _FakeWs(a["ws_bytes"]), 0)
+    assert e.value.status == status
+
+
+def test_decode_step_teal_needs_transposed_weights_and_no_cats():
+    L = (sd.sd_layer * 1)()
+    l = L[0]
+    for f in ("attn_norm", "mlp_norm", "w_down_t", "k_full", "v_full"):
+        setattr(l, f, FAKE)
+    l.cap_full, l.n_full = 100, 10
+    ws = _FakeWs(1 << 30)
+    with pytest.raises(sd.SdError) as e:  # no transposed weights
+        sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_PROJ_TEAL, ws, 0)
+    assert e.value.status == sd.SD_EINVAL and "transposed" in sd.sd_last_error()
+    for f in ("w_qkv_t", "w_o_t", "w_gate_t", "w_up_t"):
+        setattr(l, f, FAKE)
+    with pytest.raises(sd.SdError) as e:  # excludes CATS
+        sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_PROJ_TEAL | sd.SD_MLP_SPARSE, ws, 0)
+    assert e.value.status == sd.SD_EINVAL
+    l.teal_t[2] = float("nan")
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_PROJ_TEAL, ws, 0)
+    assert e.value.status == sd.SD_EINVAL and "NaN" in sd.sd_last_error()
+    l.teal_t[2] = 0.1
+    l.teal_masks_out = FAKE + 8
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_PROJ_TEAL, ws, 0)
+    assert e.value.status == sd.SD_EINVAL
 
 
 @pytest.mark.parametrize("mode", [sd.SD_KV_SPARSE | sd.SD_KV_WINDOW,
