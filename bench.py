@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("decode-step µs and achieved HBM GB/s (% of peak) vs context length, "
           "dense/KV/CATS/both")
 HBM_PEAK_GBS = 8000.0
-MODES = ("dense", "kv", "cats", "both")
+MODES = ("dense", "kv", "cats", "both", "teal", "teal+kv")
 
 
 def parse():
@@ -111,7 +111,60 @@ class Bench:
                 self.V[li].data_ptr(), self.cap_full, 0, self.KS[li].data_ptr(),
                 self.VS[li].data_ptr(), self.cap_sel, 0, self.MASK[li].data_ptr()))
         self.layers = (sd.sd_layer * self.L)(*layers)
+        self.teal = any(m.startswith("teal") for m in getattr(args, "modes", "").split(","))
+        if self.teal:  # TEAL mode reads the projections transposed (input-major)
+            self.WT, self.TMASK = [], []
+            d, qd, ff = wl.d_model, wl.n_q_heads * wl.head_dim, wl.d_ff
+            self.teal_sizes = (d, qd, d, ff)
+            for li in range(self.L):
+                W = self.W[li]
+                wt = {k: W[k].t().contiguous() for k in ("w_qkv", "w_o", "w_gate", "w_up")}
+                self.WT.append(wt)
+                self.TMASK.append(torch.zeros(sum(self.teal_sizes), dtype=torch.uint8,
+                                              device=self.dev))
+                L = self.layers[li]
+                L.w_qkv_t, L.w_o_t = wt["w_qkv"].data_ptr(), wt["w_o"].data_ptr()
+                L.w_gate_t, L.w_up_t = wt["w_gate"].data_ptr(), wt["w_up"].data_ptr()
+                L.teal_masks_out = self.TMASK[li].data_ptr()
         torch.cuda.synchronize()
+
+    def teal_keep_fractions(self):
+        """Per layer, the kept fraction of each of the four TEAL inputs in the
+        last step (from the step's own mask output)."""
+        cut = [0]
+        for n in self.teal_sizes:
+            cut.append(cut[-1] + n)
+        out = []
+        for m in self.TMASK:
+            v = m.float()
+            out.append([float(v[cut[k]:cut[k + 1]].mean()) for k in range(4)])
+        return out
+
+    def teal_calibrate(self, n, k_keep, flags, target=0.5, iters=18):
+        """TEAL thresholds (harness): per layer and input, a bisection in log
+        space on the threshold until the step keeps the target fraction of that
+        input (one decode step per round, from the same state each time).  The
+        page calibrates TEAL's magnitude thresholds offline to 50% keep; here
+        the synthetic inputs' own magnitudes stand in for calibration data."""
+        lo = [[math.log(1e-6)] * 4 for _ in range(self.L)]
+        hi = [[math.log(1e3)] * 4 for _ in range(self.L)]
+        for _ in range(iters):
+            for li, L in enumerate(self.layers):
+                for k in range(4):
+                    L.teal_t[k] = math.exp(0.5 * (lo[li][k] + hi[li][k]))
+            self.reset(n, k_keep)
+            self.run_steps(n, flags, 1)
+            fr = self.teal_keep_fractions()
+            for li in range(self.L):
+                for k in range(4):
+                    mid = 0.5 * (lo[li][k] + hi[li][k])
+                    if fr[li][k] > target:
+                        lo[li][k] = mid
+                    else:
+                        hi[li][k] = mid
+        for li, L in enumerate(self.layers):
+            for k in range(4):
+                L.teal_t[k] = math.exp(0.5 * (lo[li][k] + hi[li][k]))
 
     def calibrate(self, n_states=256, sparsity=0.5):
         torch, sd = self.torch, self.sd
@@ -176,11 +229,24 @@ class Bench:
     def mode_flags(self, mode):
         sd = self.sd
         return {"dense": 0, "kv": sd.SD_KV_SPARSE, "cats": sd.SD_MLP_SPARSE,
-                "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE}[mode]
+                "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE, "teal": sd.SD_PROJ_TEAL,
+                "teal+kv": sd.SD_PROJ_TEAL | sd.SD_KV_SPARSE}[mode]
+
+    def teal_step_bytes(self, n_read, fr):
+        """Algorithmic bytes of a TEAL step: each projection's kept rows (mean
+        kept fraction of its input over the layers) plus the cache rows."""
+        wl = self.wl
+        d, qd, ff = wl.d_model, wl.n_q_heads * wl.head_dim, wl.d_ff
+        f = [sum(x[k] for x in fr) / len(fr) for k in range(4)]
+        w = 2 * (d * wl.qkv_out * f[0] + qd * d * f[1] + 2 * d * ff * f[2] + ff * d * f[3])
+        row = 2 * wl.n_kv_heads * wl.head_dim * 2
+        return self.L * (w + row * n_read + 2 * row), f
 
     def cell(self, n, k_keep, mode):
         torch, args = self.torch, self.args
         flags = self.mode_flags(mode)
+        if flags & self.sd.SD_PROJ_TEAL:
+            self.teal_calibrate(n, k_keep, flags)
         self.reset(n, k_keep)
         self.run_steps(n, flags, args.warmup)
         torch.cuda.synchronize()
@@ -196,10 +262,16 @@ class Bench:
             kept = sum(int(m.sum()) for m in self.MASK) / self.L
         base = k_keep if flags & self.sd.SD_KV_SPARSE else n
         n_read = base + args.warmup + (args.steps - 1) / 2.0 + 1
-        b = self.step_bytes(n_read, kept)
+        extra = {}
+        if flags & self.sd.SD_PROJ_TEAL:
+            b, f = self.teal_step_bytes(n_read, self.teal_keep_fractions())
+            extra = dict(teal_keep=[round(x, 4) for x in f])
+        else:
+            b = self.step_bytes(n_read, kept)
+            extra = dict(n_kept_mean=kept)
         return dict(context=n, mode=mode, ms_per_step=ms, us_per_step=ms * 1e3,
                     bytes_per_step=b, gbs=b / ms / 1e6, hbm_frac=b / ms / 1e6 / HBM_PEAK_GBS,
-                    n_kept_mean=kept, kv_rows_read=n_read)
+                    kv_rows_read=n_read, **extra)
 
     def attention_baselines(self, n, window_ratio=0.3, steps=4, warmup=1):
         """[Cross] §4.4 on this GPU: the same sink-plus-recent window (30% of
