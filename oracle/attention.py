@@ -15,10 +15,14 @@ log-sum-exp only reaches the same numbers faster; `combine` is the merge rule
 written out on its own so that the GPU's merge can be checked in isolation.
 An empty chunk is (m = -inf, l = 0, acc = 0) and contributes nothing.
 
+Ragged lengths (one row count per KV head, for per-head budgets) are the
+same definition applied head by head.
+
 Pins (tests/test_oracle_attention.py): brute-force loops on tiny inputs,
 weights sum to one, constant V gives that constant, a single row gives that
-row, q = 0 gives the mean of V, and combining any partition of the rows
-reproduces the unsplit result.
+row, q = 0 gives the mean of V, combining any partition of the rows
+reproduces the unsplit result, and ragged lengths equal the per-head
+brute-force loops.
 """
 
 from __future__ import annotations
@@ -45,6 +49,22 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_rows: int,
         l = e.sum()
         out[h] = (e @ vv) / l
         lse[h] = m + np.log(l)
+    return out, lse
+
+
+def attend_ragged(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads,
+                  scale: float) -> tuple[np.ndarray, np.ndarray]:
+    """Ragged per-head lengths: the query heads of KV head kv attend over its
+    rows 0..n_heads[kv]-1 (a gathered buffer with one budget per head)."""
+    h_q, d_h = q.shape
+    h_kv = k.shape[0]
+    g = h_q // h_kv
+    out = np.empty((h_q, d_h), dtype=np.float64)
+    lse = np.empty(h_q, dtype=np.float64)
+    for kv in range(h_kv):
+        o, l = attend(q[kv * g:(kv + 1) * g], k[kv:kv + 1], v[kv:kv + 1], int(n_heads[kv]), scale)
+        out[kv * g:(kv + 1) * g] = o
+        lse[kv * g:(kv + 1) * g] = l
     return out, lse
 
 

@@ -27,10 +27,15 @@ The top-k decision is taken on float32 scores (the precision of the HIP
 kernels; the page fixes none), so that both sides decide identically when
 they are handed the same float32 array.
 
+* Ragged budgets (CateKV-style hybrid retention): each KV head has its own
+  k_keep and follows the same rule; which heads are adaptive is an input (the
+  page classifies heads offline from reference data).
+
 Pins (tests/test_oracle_selection.py): softmax rows sum to one so the scores of
 a KV head sum to G*w; brute-force Python loops on tiny inputs; identity at
 k_keep >= n; all-equal scores pick the lowest positions; planted high-logit
-keys are recovered.  Output parity on random data beyond these invariants is
+keys are recovered; ragged budgets equal to one k reproduce the uniform
+selection head by head; the CateKV budgets' kept fraction in closed form.  Output parity on random data beyond these invariants is
 unpinned: the selection is a heuristic defined by the steps above.
 """
 
@@ -105,6 +110,31 @@ def select_indices(scores_f32: np.ndarray, n: int, w: int, n_sink: int,
         keep = np.concatenate([np.arange(n_sink), chosen, np.arange(n - w, n)])
         out[kv] = np.sort(keep)
     return out
+
+
+def select_indices_ragged(scores_f32: np.ndarray, n: int, w: int, n_sink: int,
+                          k_heads) -> list:
+    """Per-KV-head budgets: KV head kv keeps k_heads[kv] entries by the rule of
+    select_indices (CateKV's hybrid retention, "CateKV: On Sequential
+    Consistency for Long-Context LLM Inference Acceleration", §3 "CateKV Cache
+    Policy": a few critical entries for consistent heads, most for adaptive
+    heads).  Returns one ascending int32 array per head, min(k, n) long."""
+    scores_f32 = np.asarray(scores_f32)
+    return [select_indices(scores_f32[kv:kv + 1], n, w, n_sink, int(k))[0]
+            for kv, k in enumerate(k_heads)]
+
+
+def catekv_budgets(n: int, adaptive, budget: int, eta: float) -> list:
+    """CateKV's two budgets per KV head (same page, "CateKV Cache Policy" and
+    its benchmark setting): a consistent head keeps its top `budget` entries,
+    an adaptive head floor(eta n) of them (eta = 1 keeps them all); never more
+    than n."""
+    return [min(n, int(np.floor(eta * n))) if a else min(n, int(budget)) for a in adaptive]
+
+
+def gather_ragged(cache: np.ndarray, idx_list) -> list:
+    """Per head, the contiguous copy of its kept rows: [k_h, d_h] each."""
+    return [cache[kv, idx] for kv, idx in enumerate(idx_list)]
 
 
 def window_indices(n: int, n_sink: int, n_keep: int) -> np.ndarray:

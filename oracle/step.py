@@ -90,7 +90,8 @@ class Layer:
     of the bf16 / fp32 tensors the HIP path holds)."""
 
     def __init__(self, attn_norm, w_qkv, w_o, mlp_norm, w_gate, w_up, w_down_t,
-                 threshold, k_full, v_full, n, k_sel=None, v_sel=None, n_sel=0):
+                 threshold, k_full, v_full, n, k_sel=None, v_sel=None, n_sel=0,
+                 n_sel_heads=None):
         self.attn_norm = np.asarray(attn_norm, dtype=np.float64)
         self.w_qkv = np.asarray(w_qkv, dtype=np.float64)
         self.w_o = np.asarray(w_o, dtype=np.float64)
@@ -105,6 +106,8 @@ class Layer:
         self.k_sel = None if k_sel is None else np.array(k_sel, dtype=np.float64)
         self.v_sel = None if v_sel is None else np.array(v_sel, dtype=np.float64)
         self.n_sel = int(n_sel)
+        # ragged budgets: valid gathered rows per KV head (n_sel is then unused)
+        self.n_sel_heads = None if n_sel_heads is None else [int(x) for x in n_sel_heads]
 
 
 def decode_layer(layer: Layer, h: np.ndarray, pos: int, *, n_q_heads: int,
@@ -128,11 +131,21 @@ def decode_layer(layer: Layer, h: np.ndarray, pos: int, *, n_q_heads: int,
     layer.v_full[:, layer.n] = v_r
     layer.n += 1
     if layer.k_sel is not None:
-        layer.k_sel[:, layer.n_sel] = k_r
-        layer.v_sel[:, layer.n_sel] = v_r
-        layer.n_sel += 1
+        if layer.n_sel_heads is not None:  # ragged: each KV head appends at its own row
+            for kv in range(n_kv_heads):
+                layer.k_sel[kv, layer.n_sel_heads[kv]] = k_r[kv]
+                layer.v_sel[kv, layer.n_sel_heads[kv]] = v_r[kv]
+                layer.n_sel_heads[kv] += 1
+        else:
+            layer.k_sel[:, layer.n_sel] = k_r
+            layer.v_sel[:, layer.n_sel] = v_r
+            layer.n_sel += 1
     scale = 1.0 / np.sqrt(head_dim)
-    if kv_window is not None:
+    if kv_sparse and layer.n_sel_heads is not None:
+        if kv_window is not None:
+            raise ValueError("ragged budgets and the window are separate policies")
+        o, _ = attention.attend_ragged(q, layer.k_sel, layer.v_sel, layer.n_sel_heads, scale)
+    elif kv_window is not None:
         from . import selection
         idx = selection.window_indices(layer.n, kv_window[0], kv_window[1])
         o, _ = attention.attend(q, layer.k_full[:, idx], layer.v_full[:, idx], len(idx), scale)

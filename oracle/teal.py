@@ -106,12 +106,21 @@ def teal_layer(layer, h, pos, thresholds, *, n_q_heads, n_kv_heads, head_dim, kv
     layer.k_full[:, layer.n] = k_r
     layer.v_full[:, layer.n] = v_r
     layer.n += 1
+    ragged = getattr(layer, "n_sel_heads", None) is not None
     if layer.k_sel is not None:
-        layer.k_sel[:, layer.n_sel] = k_r
-        layer.v_sel[:, layer.n_sel] = v_r
-        layer.n_sel += 1
+        if ragged:
+            for kv in range(n_kv_heads):
+                layer.k_sel[kv, layer.n_sel_heads[kv]] = k_r[kv]
+                layer.v_sel[kv, layer.n_sel_heads[kv]] = v_r[kv]
+                layer.n_sel_heads[kv] += 1
+        else:
+            layer.k_sel[:, layer.n_sel] = k_r
+            layer.v_sel[:, layer.n_sel] = v_r
+            layer.n_sel += 1
     scale = 1.0 / np.sqrt(head_dim)
-    if kv_sparse:
+    if kv_sparse and ragged:
+        o, _ = attention.attend_ragged(q, layer.k_sel, layer.v_sel, layer.n_sel_heads, scale)
+    elif kv_sparse:
         o, _ = attention.attend(q, layer.k_sel, layer.v_sel, layer.n_sel, scale)
     else:
         o, _ = attention.attend(q, layer.k_full, layer.v_full, layer.n, scale)

@@ -75,3 +75,20 @@ def test_combine_two_chunks_by_hand():
     o, lse = att.combine(m, l, acc)
     np.testing.assert_allclose(o, [[(1 + 6) / 3]])
     np.testing.assert_allclose(lse, [np.log(3.0)])
+
+
+def test_ragged_lengths_match_per_head_loops():
+    r = np.random.default_rng(31)
+    q = r.standard_normal((6, 16))
+    k = r.standard_normal((3, 40, 16))
+    v = r.standard_normal((3, 40, 16))
+    lens = [7, 40, 1]
+    out, lse = att.attend_ragged(q, k, v, lens, 0.25)
+    for kv, n in enumerate(lens):
+        o, l = att.attend_loops(q[2 * kv:2 * kv + 2], k[kv:kv + 1], v[kv:kv + 1], n, 0.25)
+        np.testing.assert_allclose(out[2 * kv:2 * kv + 2], o, rtol=1e-12, atol=1e-12)
+    # one row: the output is that row of V
+    np.testing.assert_allclose(out[4:6], np.tile(v[2, 0], (2, 1)), rtol=1e-12)
+    # equal lengths: the uniform attention, bit for bit
+    o2, _ = att.attend_ragged(q, k, v, [40, 40, 40], 0.25)
+    assert np.array_equal(o2, att.attend(q, k, v, 40, 0.25)[0])

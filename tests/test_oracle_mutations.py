@@ -34,6 +34,10 @@ MUTS = [
  ("teal.py", "m_d = mask_of(DOWN_IN, hmid)", "m_d = mask_of(DOWN_IN, u)"),
  ("teal.py", "h = h + linear_masked(layer.w_o, o, m_o)", "h = h + linear_masked(layer.w_o, o, m_a)"),
  ("teal.py", "hmid = cats.silu(g) * u", "hmid = g * u"),
+ ("attention.py", "int(n_heads[kv])", "int(n_heads[0])"),
+ ("step.py", "layer.k_sel[kv, layer.n_sel_heads[kv]] = k_r[kv]", "layer.k_sel[kv, layer.n_sel_heads[0]] = k_r[kv]"),
+ ("selection.py", "return [min(n, int(np.floor(eta * n))) if a else min(n, int(budget)) for a in adaptive]",
+  "return [min(n, int(np.floor(eta * n))) if not a else min(n, int(budget)) for a in adaptive]"),
 ]
 
 PIN_FILES = ["tests/test_oracle_byte_account.py", "tests/test_oracle_selection.py",

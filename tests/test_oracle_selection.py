@@ -170,3 +170,34 @@ def test_window_attention_equals_attention_over_its_rows():
     w /= w.sum(1, keepdims=True)
     np.testing.assert_allclose(o1, np.einsum("hj,hjd->hd", w, np.repeat(v[:, idx], 2, axis=0)),
                                rtol=1e-12)
+
+
+def test_ragged_budgets_equal_to_one_k_are_the_uniform_selection():
+    r = np.random.default_rng(21)
+    s = r.random((4, 300)).astype(np.float32)
+    want = sel.select_indices(s, 300, 16, 4, 90)
+    got = sel.select_indices_ragged(s, 300, 16, 4, [90] * 4)
+    assert all(np.array_equal(g, w) for g, w in zip(got, want))
+
+
+def test_ragged_budgets_per_head():
+    r = np.random.default_rng(22)
+    s = r.random((3, 200)).astype(np.float32)
+    got = sel.select_indices_ragged(s, 200, 8, 2, [10, 500, 64])
+    assert [len(g) for g in got] == [10, 200, 64]
+    assert np.array_equal(got[1], np.arange(200))  # k >= n keeps every row
+    for kv, k in ((0, 10), (2, 64)):
+        assert np.array_equal(got[kv], sel.select_indices(s[kv:kv + 1], 200, 8, 2, k)[0])
+        # sinks and window are forced, the rest are the top scores of the candidates
+        assert set(range(2)) <= set(got[kv]) and set(range(192, 200)) <= set(got[kv])
+
+
+def test_catekv_budgets_closed_form():
+    # the page's benchmark setting: adaptive heads keep everything (eta = 1),
+    # consistent heads a 2048-entry budget; with 3 of 8 KV heads adaptive at
+    # 128K the kept fraction is (3 n + 5 * 2048) / (8 n)
+    n = 131072
+    ks = sel.catekv_budgets(n, [1, 0, 0, 1, 0, 0, 1, 0], 2048, 1.0)
+    assert ks == [n, 2048, 2048, n, 2048, 2048, n, 2048]
+    assert abs(sum(ks) / (8 * n) - (3 * n + 5 * 2048) / (8 * n)) < 1e-15
+    assert sel.catekv_budgets(1000, [1, 0], 2048, 0.5) == [500, 1000]

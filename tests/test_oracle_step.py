@@ -2,6 +2,8 @@
 composed step (Llama-style pre-norm layer; modes of "Where Activation Sparsity
 and KV-Cache Sparsity Cross in LLM Decoding", §3.2 and §5.3)."""
 
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -138,3 +140,27 @@ def test_sparse_kv_reads_only_gathered_rows():
     # and differs from attending over the full cache
     o_full, _ = attention.attend(q, la.k_full, la.v_full, 31, 1 / np.sqrt(8))
     assert np.abs(o_full - o).max() > 1e-3
+
+
+def test_ragged_layer_appends_per_head_and_equals_uniform_when_equal():
+    r = np.random.default_rng(8)
+    la = _layer(r)
+    lb = step.Layer(**{k: copy.deepcopy(getattr(la, k)) for k in
+                       ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down_t",
+                        "threshold", "k_full", "v_full", "n", "k_sel", "v_sel", "n_sel")},
+                    n_sel_heads=[la.n_sel, la.n_sel])
+    h = r.standard_normal(32)
+    ha = step.decode_step([la], h, 30, kv_sparse=True, mlp_sparse=False, **DIMS)
+    hb = step.decode_step([lb], h, 30, kv_sparse=True, mlp_sparse=False, **DIMS)
+    assert np.array_equal(ha, hb) and lb.n_sel_heads == [31, 31]
+    # unequal lengths: head 0 keeps 10 rows, head 1 all 30; each appends at its own row
+    lc = _layer(np.random.default_rng(8))
+    lc.n_sel_heads = [10, 30]
+    tr = []
+    step.decode_step([lc], h, 30, kv_sparse=True, mlp_sparse=False, trace=tr, **DIMS)
+    assert lc.n_sel_heads == [11, 31]
+    assert np.array_equal(lc.k_sel[0, 10], lc.k_full[0, 30])
+    assert np.array_equal(lc.k_sel[1, 30], lc.k_full[1, 30])
+    from oracle import attention
+    o, _ = attention.attend_ragged(tr[0]["q"], lc.k_sel, lc.v_sel, [11, 31], 1 / np.sqrt(8))
+    assert np.array_equal(tr[0]["attn"], o)
