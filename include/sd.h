@@ -156,6 +156,47 @@ sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, con
                          float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sd_select_kv_ragged -- sd_select_kv with a budget per KV head
+ * ("CateKV: On Sequential Consistency for Long-Context LLM Inference
+ * Acceleration", §3 "CateKV Cache Policy": consistent heads keep a small
+ * fixed number of critical entries, adaptive heads a large share of theirs).
+ *
+ * k_keep_heads    [h_kv] int32 [host]: KV head kv keeps k_eff[kv] =
+ *                 min(k_keep_heads[kv], n) rows by the rule of sd_select_kv.
+ * idx             [h_kv, idx_stride] int32 out: head kv's kept rows ascending
+ *                 in idx[kv*idx_stride .. kv*idx_stride + k_eff[kv] - 1]; the
+ *                 rest of each row is left untouched.
+ * k_sel, v_sel    [h_kv, cap_sel, d_h] out: rows 0..k_eff[kv]-1 of head kv
+ *                 are its kept rows; later steps append at row k_eff[kv].
+ * Everything else as sd_select_kv (same kernels, same scores, same ranking).
+ * Errors: EINVAL unless each k_keep_heads[kv] >= n_sink + w (or >= n) and
+ *         idx_stride >= max k_eff; ENOSPC if cap_sel < max k_eff;
+ *         EUNSUPPORTED for more than 32 KV heads.
+ */
+sd_status sd_select_kv_ragged(const sd_dims* dims, const void* k_full, const void* v_full,
+                              int32_t cap_full, int32_t n, const float* q_window, int32_t w,
+                              int32_t n_sink, const int32_t* k_keep_heads, float* scores,
+                              int32_t* idx, int32_t idx_stride, void* k_sel, void* v_sel,
+                              int32_t cap_sel, uint32_t flags, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * sd_decode_attn_ragged -- sd_decode_attn where KV head kv reads its own
+ * n_ctx_heads[kv] rows (the gathered buffers of sd_select_kv_ragged; same
+ * CateKV passage).  Query heads of group kv attend over rows
+ * 0..n_ctx_heads[kv]-1 of KV head kv.
+ * n_ctx_heads  [h_kv] int32 [host].
+ * n_splits     as sd_decode_attn, counted on the longest head; a head shorter
+ *              than the others leaves its surplus chunks empty.
+ * Errors: EINVAL unless 1 <= n_ctx_heads[kv] <= cap for every head; ENOSPC as
+ *         sd_decode_attn; EUNSUPPORTED for more than 32 KV heads.
+ */
+sd_status sd_decode_attn_ragged(const sd_dims* dims, const float* q, const void* k, const void* v,
+                                int32_t cap, const int32_t* n_ctx_heads, float scale,
+                                int32_t n_splits, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
  * sd_decode_attn_window -- attention over a sink-plus-recent window read in
  * place from one cache ([Cross] §4.1: the StreamingLLM-style policy that reads
  * as many entries as the selection keeps; §4.4 times it): of the n_rows valid
@@ -265,6 +306,9 @@ typedef struct {
   float teal_t[4];
   uint8_t* teal_masks_out; /* optional, 16-byte aligned: the four keep masks (1 kept, 0 dropped),
                               [d | h_q d_h | d | d_ff] bytes in that order */
+  int32_t* n_sel_heads;    /* optional [h_kv] [host]: per-KV-head valid gathered rows (ragged
+                              budgets of sd_select_kv_ragged); replaces n_sel when not NULL,
+                              each entry advanced by one; excludes SD_KV_WINDOW */
 } sd_layer;
 
 /*

@@ -30,7 +30,8 @@ SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED = 16, 32, 64
 SD_PROJ_TEAL, SD_ACCUMULATE = 128, 256
 SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 
-EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_decode_attn", "sd_decode_attn_window",
+EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_decode_attn",
+           "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
            "sd_decode_step", "sd_byte_account", "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
@@ -59,7 +60,8 @@ class sd_layer(ctypes.Structure):
                 ("window_sink", ctypes.c_int32),
                 ("w_qkv_t", ctypes.c_void_p), ("w_o_t", ctypes.c_void_p),
                 ("w_gate_t", ctypes.c_void_p), ("w_up_t", ctypes.c_void_p),
-                ("teal_t", ctypes.c_float * 4), ("teal_masks_out", ctypes.c_void_p)]
+                ("teal_t", ctypes.c_float * 4), ("teal_masks_out", ctypes.c_void_p),
+                ("n_sel_heads", ctypes.POINTER(ctypes.c_int32))]
 
 
 class sd_byte_record(ctypes.Structure):
@@ -85,6 +87,12 @@ _lib.sd_workspace_bytes.argtypes = [ctypes.POINTER(sd_dims), _I, _I]
 _lib.sd_select_kv.restype = _I
 _lib.sd_select_kv.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _I, _I, _P, _I, _I, _I, _P, _P,
                               _P, _P, _I, _U, _P, _S, _P]
+_lib.sd_select_kv_ragged.restype = _I
+_lib.sd_select_kv_ragged.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _I, _I, _P, _I, _I,
+                                     ctypes.POINTER(_I), _P, _P, _I, _P, _P, _I, _U, _P, _S, _P]
+_lib.sd_decode_attn_ragged.restype = _I
+_lib.sd_decode_attn_ragged.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I,
+                                       ctypes.POINTER(_I), _F, _I, _P, _P, _P, _S, _P]
 _lib.sd_decode_attn.restype = _I
 _lib.sd_decode_attn.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I, _I, _F, _I, _P, _P,
                                 _P, _S, _P]
@@ -170,6 +178,29 @@ def sd_select_kv(dims, k_full, v_full, cap_full, n, q_window, w, n_sink, k_keep,
     _check(_lib.sd_select_kv(ctypes.byref(dims), _ptr(k_full), _ptr(v_full), cap_full, n,
                              _ptr(q_window), w, n_sink, k_keep, _ptr(scores), _ptr(idx),
                              _ptr(k_sel), _ptr(v_sel), cap_sel, flags, p, nb, _stream(stream)))
+
+
+def _host_ints(vals):
+    vals = [int(x) for x in vals]
+    return (_I * max(1, len(vals)))(*vals)
+
+
+def sd_select_kv_ragged(dims, k_full, v_full, cap_full, n, q_window, w, n_sink, k_keep_heads,
+                        scores, idx, idx_stride, k_sel, v_sel, cap_sel, flags, ws,
+                        stream=None) -> None:
+    p, nb = _ws(ws)
+    _check(_lib.sd_select_kv_ragged(ctypes.byref(dims), _ptr(k_full), _ptr(v_full), cap_full, n,
+                                    _ptr(q_window), w, n_sink, _host_ints(k_keep_heads),
+                                    _ptr(scores), _ptr(idx), idx_stride, _ptr(k_sel), _ptr(v_sel),
+                                    cap_sel, flags, p, nb, _stream(stream)))
+
+
+def sd_decode_attn_ragged(dims, q, k, v, cap, n_ctx_heads, scale, n_splits, out, lse, ws,
+                          stream=None) -> None:
+    p, nb = _ws(ws)
+    _check(_lib.sd_decode_attn_ragged(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), cap,
+                                      _host_ints(n_ctx_heads), scale, n_splits, _ptr(out),
+                                      _ptr(lse), p, nb, _stream(stream)))
 
 
 def sd_decode_attn(dims, q, k, v, cap, n_ctx, scale, n_splits, out, lse, ws, stream=None) -> None:

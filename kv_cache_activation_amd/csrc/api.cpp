@@ -140,7 +140,8 @@ enum Path { P_SPLITK = 0, P_MASKED = 1, P_FUSED = 2 };
 // buffers (and, for the masked path, its score rows for `cap` rows).
 void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, const void* k,
                   const void* v, int cap, int n_ctx, int sink, int shift, float scale,
-                  int n_splits, Path path, float* out, float* lse, hipStream_t s) {
+                  int n_splits, Path path, float* out, float* lse, hipStream_t s,
+                  const sd::HeadInts* lens = nullptr) {
   sd::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -158,6 +159,10 @@ void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, 
   a.pacc = reinterpret_cast<float*>(ws + L.pacc);
   a.out = out;
   a.lse = lse;
+  if (lens) {  // ragged per-head lengths (split-K path); n_ctx is their maximum
+    a.ragged = 1;
+    a.lens = *lens;
+  }
   if (path == P_MASKED) {
     sd::launch_attn_masked(a, reinterpret_cast<float*>(ws + L.scores), dm.kv_dtype, s);
     return;
@@ -317,6 +322,98 @@ sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, con
   return check_launch("sd_decode_attn");
 }
 
+sd_status sd_select_kv_ragged(const sd_dims* dims, const void* k_full, const void* v_full,
+                              int32_t cap_full, int32_t n, const float* q_window, int32_t w,
+                              int32_t n_sink, const int32_t* k_keep_heads, float* scores,
+                              int32_t* idx, int32_t idx_stride, void* k_sel, void* v_sel,
+                              int32_t cap_sel, uint32_t flags, void* ws, size_t ws_bytes,
+                              void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  const bool scores_in = flags & SD_SCORES_IN;
+  if (!aligned(k_full) || !aligned(v_full) || !aligned(scores) || !aligned(idx) ||
+      !aligned(k_sel) || !aligned(v_sel) || (!scores_in && !aligned(q_window)) || !aligned(ws) ||
+      !k_keep_heads)
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (dims->n_kv_heads > sd::kMaxKvHeads)
+    return fail(SD_EUNSUPPORTED, "ragged budgets need n_kv_heads <= %d", sd::kMaxKvHeads);
+  if (n < 1 || n > cap_full) return fail(SD_EINVAL, "need 1 <= n <= cap_full");
+  if (w < 1 || w > n) return fail(SD_EINVAL, "need 1 <= w <= n");
+  if (n_sink < 0) return fail(SD_EINVAL, "n_sink must be >= 0");
+  sd::HeadInts kh{};
+  int k_max = 0;
+  for (int h = 0; h < dims->n_kv_heads; ++h) {
+    const int k = k_keep_heads[h];
+    if (k < n && k < n_sink + w)
+      return fail(SD_EINVAL, "head %d: k_keep %d < n_sink + w = %d", h, k, n_sink + w);
+    kh.v[h] = k;
+    const int ke = k < n ? k : n;
+    if (ke > k_max) k_max = ke;
+  }
+  if (idx_stride < k_max) return fail(SD_EINVAL, "idx_stride %d < largest kept count %d", idx_stride, k_max);
+  if (cap_sel < k_max) return fail(SD_ENOSPC, "cap_sel %d < kept rows %d", cap_sel, k_max);
+  const Layout L = make_layout(*dims, n, w);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* wsb = static_cast<char*>(ws);
+  sd::SelectArgs a{};
+  a.k = k_full;
+  a.v = v_full;
+  a.cap_full = cap_full;
+  a.n = n;
+  a.q_win = q_window;
+  a.w = w;
+  a.n_sink = n_sink;
+  a.k_keep = k_max;
+  a.h_q = dims->n_q_heads;
+  a.h_kv = dims->n_kv_heads;
+  a.dh = dims->head_dim;
+  a.scores = scores;
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.v_sel = v_sel;
+  a.cap_sel = cap_sel;
+  a.n_chunks = L.sel_chunks;
+  a.lse_part = reinterpret_cast<float*>(wsb + L.lse_part);
+  a.lse = reinterpret_cast<float*>(wsb + L.lse);
+  a.skip_scoring = scores_in;
+  a.ragged = 1;
+  a.k_heads = kh;
+  a.idx_stride = idx_stride;
+  sd::launch_select(a, dims->kv_dtype, static_cast<hipStream_t>(stream));
+  return check_launch("sd_select_kv_ragged");
+}
+
+sd_status sd_decode_attn_ragged(const sd_dims* dims, const float* q, const void* k, const void* v,
+                                int32_t cap, const int32_t* n_ctx_heads, float scale,
+                                int32_t n_splits, float* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(out) || !aligned(ws) ||
+      !n_ctx_heads || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(SD_EINVAL, "null or misaligned pointer");
+  if (dims->n_kv_heads > sd::kMaxKvHeads)
+    return fail(SD_EUNSUPPORTED, "ragged lengths need n_kv_heads <= %d", sd::kMaxKvHeads);
+  sd::HeadInts lens{};
+  int n_max = 0;
+  for (int h = 0; h < dims->n_kv_heads; ++h) {
+    if (n_ctx_heads[h] < 1 || n_ctx_heads[h] > cap)
+      return fail(SD_EINVAL, "head %d: need 1 <= n_ctx <= cap", h);
+    lens.v[h] = n_ctx_heads[h];
+    if (lens.v[h] > n_max) n_max = lens.v[h];
+  }
+  if (!std::isfinite(scale)) return fail(SD_EINVAL, "scale must be finite");
+  const Layout L = make_layout(*dims, 0, 0);
+  if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (n_splits < 0) return fail(SD_EINVAL, "n_splits must be >= 0");
+  if (n_splits > L.max_splits)
+    return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
+  int sp = n_splits ? (n_splits < n_max ? n_splits : n_max) : auto_splits(n_max, dims->n_kv_heads);
+  enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_max, n_max, 0, scale, sp,
+               P_SPLITK, out, lse, static_cast<hipStream_t>(stream), &lens);
+  return check_launch("sd_decode_attn_ragged");
+}
+
 sd_status sd_decode_attn_window(const sd_dims* dims, const float* q, const void* k, const void* v,
                                 int32_t cap, int32_t n_rows, int32_t n_sink, int32_t n_keep,
                                 float scale, int32_t n_splits, float* out, float* lse, void* ws,
@@ -464,9 +561,17 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     if (l.k_sel || l.v_sel) {
       if (!aligned(l.k_sel) || !aligned(l.v_sel))
         return fail(SD_EINVAL, "layer %d: misaligned gathered buffer", i);
-      if (l.n_sel < 0 || l.n_sel >= l.cap_sel)
+      if (l.n_sel_heads) {
+        if (dims->n_kv_heads > sd::kMaxKvHeads)
+          return fail(SD_EUNSUPPORTED, "ragged budgets need n_kv_heads <= %d", sd::kMaxKvHeads);
+        if (kv_window) return fail(SD_EINVAL, "layer %d: ragged budgets exclude the window", i);
+        for (int h = 0; h < dims->n_kv_heads; ++h)
+          if (l.n_sel_heads[h] < 0 || l.n_sel_heads[h] >= l.cap_sel)
+            return fail(SD_ENOSPC, "layer %d head %d: gathered buffer has no free row", i, h);
+      } else if (l.n_sel < 0 || l.n_sel >= l.cap_sel) {
         return fail(SD_ENOSPC, "layer %d: gathered buffer has no free row (n_sel %d, cap %d)",
                     i, l.n_sel, l.cap_sel);
+      }
     } else if (kv_sparse) {
       return fail(SD_EINVAL, "layer %d: KV-sparse mode needs a gathered buffer", i);
     }
@@ -515,6 +620,16 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     qa.v_sel = has_sel ? l.v_sel : nullptr;
     qa.cap_sel = l.cap_sel;
     qa.row_sel = l.n_sel;
+    sd::HeadInts lens{};  // ragged budgets: per-head append rows, then per-head lengths
+    int n_ragged = 0;
+    if (has_sel && l.n_sel_heads) {
+      qa.ragged = 1;
+      for (int h = 0; h < hkv; ++h) {
+        qa.sel_rows.v[h] = l.n_sel_heads[h];
+        lens.v[h] = l.n_sel_heads[h] + 1;
+        if (lens.v[h] > n_ragged) n_ragged = lens.v[h];
+      }
+    }
     const int qkv_out = (hq + 2 * hkv) * dh;
     uint8_t* tm = teal ? l.teal_masks_out : nullptr;  // [d | h_q d_h | d | d_ff]
     if (teal) {
@@ -538,8 +653,10 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
       n_ctx = l.window_keep;
     }
     const Path path = masked ? P_MASKED : fused ? P_FUSED : P_SPLITK;
+    const bool ragged = kv_sparse && qa.ragged;
+    if (ragged) n_ctx = sink = n_ragged;
     enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, sink, shift, scale,
-                 auto_splits(n_ctx, hkv), path, attn, nullptr, s);
+                 auto_splits(n_ctx, hkv), path, attn, nullptr, s, ragged ? &lens : nullptr);
 
     if (teal) {
       float* part = reinterpret_cast<float*>(wsb + L.teal_part);
@@ -574,7 +691,13 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
   if (st) return st;
   for (int i = 0; i < n_layers; ++i) {
     layers[i].n_full += 1;
-    if (layers[i].k_sel) layers[i].n_sel += 1;
+    if (layers[i].k_sel) {
+      if (layers[i].n_sel_heads) {
+        for (int h = 0; h < dims->n_kv_heads; ++h) layers[i].n_sel_heads[h] += 1;
+      } else {
+        layers[i].n_sel += 1;
+      }
+    }
   }
   return SD_OK;
 }

@@ -37,8 +37,9 @@ constexpr int kAttnWaves = kAttnThreads / kWave;
 template <typename KT, int DH, int G, int U>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
-    int n_ctx, int sink, int shift, int kv_div, float scale_log2, int chunk, int n_splits,
-    float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ pacc) {
+    int n_ctx, int sink, int shift, int kv_div, int ragged, HeadInts lens, float scale_log2,
+    int chunk, int n_splits, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ pacc) {
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
@@ -49,8 +50,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int sub = lane % LPR;
   const int slot = wave * RPW + lane / LPR;
+  // rows of this KV head: n_ctx, or its own count under ragged budgets (a
+  // split past the end has no rows and writes the empty partial)
+  const int rows = ragged ? lens.v[(kv / kv_div) & (kMaxKvHeads - 1)] : n_ctx;
   const int r0 = split * chunk;
-  const int r1 = min(n_ctx, r0 + chunk);
+  const int r1 = min(rows, r0 + chunk);
   // logical row j is physical row j, or j + shift from `sink` on (a window of
   // sinks plus recent rows read in place); query-head group kv reads KV head
   // kv / kv_div (kv_div > 1: one workgroup per query head)
@@ -261,8 +265,8 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   const KT* v = (const KT*)a.v;
 #define SD_ATTN_G(GG, UU)                                                                   \
   launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU>, grid, dim3(kAttnThreads), 0, s, \
-                a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, scale_log2, a.chunk, a.n_splits, a.pm, \
-      a.pl, a.pacc)
+                a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, scale_log2,      \
+                a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
   switch (G) {
     case 1: SD_ATTN_G(1, 8); break;
     case 2: SD_ATTN_G(2, 8); break;

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
     const float* __restrict__ h, const float* __restrict__ nw, float eps,
     const WT* __restrict__ W, int d, int h_q, int h_kv, int dh, RopeTable rope,
     float* __restrict__ q_out, KT* __restrict__ k_full, KT* __restrict__ v_full, int cap_full,
-    int row_full, KT* __restrict__ k_sel, KT* __restrict__ v_sel, int cap_sel, int row_sel) {
+    int row_full, KT* __restrict__ k_sel, KT* __restrict__ v_sel, int cap_sel, int row_sel,
+    int ragged, HeadInts sel_rows) {
   const int half = dh >> 1;
   const int d8 = d >> 3;
   const int n_pairs = (h_q + 2 * h_kv) * half;
@@ -164,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
     store_elem(full + off + half, b);
     if (k_sel) {
       KT* sel = is_k ? k_sel : v_sel;
-      const size_t offs = ((size_t)kv * cap_sel + row_sel) * dh + i;
+      // ragged budgets: each KV head appends at its own row
+      const int rsel = ragged ? sel_rows.v[kv & (kMaxKvHeads - 1)] : row_sel;
+      const size_t offs = ((size_t)kv * cap_sel + rsel) * dh + i;
       store_elem(sel + offs, a);
       store_elem(sel + offs + half, b);
     }
@@ -332,7 +335,8 @@ static void qkv_typed(const QkvArgs& a, hipStream_t s) {
                                    1, lds, s, a.h, a.norm, a.eps,
                                       (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
                                       (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full,
-                                      (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel));
+                                      (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel, a.ragged,
+                                   a.sel_rows));
 }
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {

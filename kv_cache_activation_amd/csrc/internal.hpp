@@ -34,6 +34,12 @@ inline void launch_kernel(int kind, F kernel, dim3 grid, dim3 block, uint32_t ld
   hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e.start, e.stop, 0u, args...);
 }
 
+// One int per KV head (ragged per-head budgets), passed by value.
+constexpr int kMaxKvHeads = 32;
+struct HeadInts {
+  int v[kMaxKvHeads];
+};
+
 // cos and sin of the rotation angle of each RoPE pair index (d_h / 2 <= 64)
 struct RopeTable {
   float c[64];
@@ -54,6 +60,8 @@ struct QkvArgs {
   void* k_sel;
   void* v_sel;
   int cap_sel, row_sel;
+  int ragged;          // the gathered buffer's row per KV head is sel_rows.v[kv]
+  HeadInts sel_rows;
 };
 
 struct GateArgs {
@@ -125,6 +133,8 @@ struct AttnArgs {
   int cap, n_ctx, h_q, h_kv, dh;
   int sink, shift;      // logical row j reads physical row j + (j >= sink ? shift : 0)
   int per_query_head;   // one workgroup per query head (no K/V sharing across a group)
+  int ragged;           // KV head kv has lens.v[kv] rows (n_ctx is their maximum)
+  HeadInts lens;
   float scale;
   int n_splits, chunk;
   float* pm;
@@ -149,6 +159,9 @@ struct SelectArgs {
   float* lse_part;   // [h_kv, n_chunks, G*w, 2]
   float* lse;        // [h_q, w] (log2 domain)
   int skip_scoring;
+  int ragged;        // per-head budgets k_heads (k_keep unused), idx rows of idx_stride
+  HeadInts k_heads;
+  int idx_stride;
 };
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s);

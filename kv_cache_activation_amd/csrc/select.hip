@@ -213,19 +213,21 @@ __device__ __forceinline__ int block_prefix(bool flag, int* wave_tot, int& total
 
 __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(const float* __restrict__ scores,
                                                                  int n, int w, int n_sink,
-                                                                 int k_keep,
+                                                                 int k_keep_all, int ragged,
+                                                                 HeadInts k_heads, int stride,
                                                                  int32_t* __restrict__ idx) {
   __shared__ unsigned hist[256];
   __shared__ unsigned sh_prefix, sh_need;
   __shared__ int wave_tot[kTopkWaves];
   const int kv = blockIdx.x;
   const float* S = scores + (size_t)kv * n;
+  // this head's budget (one budget for all heads unless ragged)
+  const int k_keep = ragged ? k_heads.v[kv & (kMaxKvHeads - 1)] : k_keep_all;
+  int32_t* out = idx + (size_t)kv * stride;
   if (k_keep >= n) {
-    int32_t* out = idx + (size_t)kv * n;
     for (int j = threadIdx.x; j < n; j += kTopkThreads) out[j] = j;
     return;
   }
-  int32_t* out = idx + (size_t)kv * k_keep;
   const int m = k_keep - n_sink - w;
   const int c0 = n_sink, c1 = n - w;
   unsigned T = 0, need = 0;
@@ -281,14 +283,16 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(const float* __r
 
 template <typename KT, int DH>
 __global__ void sel_gather_kernel(const KT* __restrict__ K, const KT* __restrict__ V,
-                                  int cap_full, const int32_t* __restrict__ idx, int k_eff,
+                                  int cap_full, const int32_t* __restrict__ idx, int k_eff_all,
+                                  int ragged, HeadInts k_eff_heads, int stride,
                                   KT* __restrict__ Ks, KT* __restrict__ Vs, int cap_sel) {
   constexpr int P = DH * (int)sizeof(KT) / 16;  // 16-byte pieces per row
   const int kv = blockIdx.y;
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int r = t / P, piece = t - r * P;
+  const int k_eff = ragged ? k_eff_heads.v[kv & (kMaxKvHeads - 1)] : k_eff_all;
   if (r >= k_eff) return;
-  const int src = idx[(size_t)kv * k_eff + r];
+  const int src = idx[(size_t)kv * stride + r];
   if (src < 0 || src >= cap_full) return;  // indices come from data: never read outside
   const uint4* ks = reinterpret_cast<const uint4*>(K + ((size_t)kv * cap_full + src) * DH) + piece;
   const uint4* vs = reinterpret_cast<const uint4*>(V + ((size_t)kv * cap_full + src) * DH) + piece;
@@ -313,14 +317,25 @@ static void select_typed(const SelectArgs& a, hipStream_t s) {
     launch_kernel(K_SEL_SCORE, sel_score_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
                   a.cap_full, a.n, a.q_win, a.w, G, scale_log2, (const float*)a.lse, a.scores);
   }
+  // per-head kept counts (one count for all heads unless the budgets are ragged)
+  HeadInts k_eff_heads{};
+  int k_eff = a.k_keep < a.n ? a.k_keep : a.n, k_max = k_eff;
+  if (a.ragged) {
+    k_max = 0;
+    for (int h = 0; h < a.h_kv; ++h) {
+      k_eff_heads.v[h] = a.k_heads.v[h] < a.n ? a.k_heads.v[h] : a.n;
+      if (k_eff_heads.v[h] > k_max) k_max = k_eff_heads.v[h];
+    }
+  }
+  const int stride = a.ragged ? a.idx_stride : k_eff;
   launch_kernel(K_SEL_TOPK, sel_topk_kernel, dim3(a.h_kv), dim3(kTopkThreads), 0, s,
-                (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.idx);
-  const int k_eff = a.k_keep < a.n ? a.k_keep : a.n;
+                (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.ragged, a.k_heads, stride,
+                a.idx);
   constexpr int P = DH * (int)sizeof(KT) / 16;
-  dim3 ggrid((k_eff * P + 255) / 256, a.h_kv);
+  dim3 ggrid((k_max * P + 255) / 256, a.h_kv);
   launch_kernel(K_SEL_GATHER, sel_gather_kernel<KT, DH>, ggrid, dim3(256), 0, s, k,
-                (const KT*)a.v, a.cap_full, (const int32_t*)a.idx, k_eff, (KT*)a.k_sel,
-                (KT*)a.v_sel, a.cap_sel);
+                (const KT*)a.v, a.cap_full, (const int32_t*)a.idx, k_eff, a.ragged, k_eff_heads,
+                stride, (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel);
 }
 
 void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s) {

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kRCols * kRSlices) void teal_qkv_reduce_kernel(
     const float* __restrict__ part, int P, int d_out, int h_q, int h_kv, int dh,
     RopeTable rope, float* __restrict__ q_out, KT* __restrict__ k_full, KT* __restrict__ v_full,
     int cap_full, int row_full, KT* __restrict__ k_sel, KT* __restrict__ v_sel, int cap_sel,
-    int row_sel) {
+    int row_sel, int ragged, HeadInts sel_rows) {
   __shared__ float red[kRSlices][kRCols];
   __shared__ float tot[kRCols];
   const int half = dh >> 1;
@@ -249,7 +249,9 @@ __global__ __launch_bounds__(kRCols * kRSlices) void teal_qkv_reduce_kernel(
     store_elem(full + off + half, b);
     if (k_sel) {
       KT* sel = is_k ? k_sel : v_sel;
-      const size_t offs = ((size_t)kv * cap_sel + row_sel) * dh + i;
+      // ragged budgets: each KV head appends at its own row
+      const int rsel = ragged ? sel_rows.v[kv & (kMaxKvHeads - 1)] : row_sel;
+      const size_t offs = ((size_t)kv * cap_sel + rsel) * dh + i;
       store_elem(sel + offs, a);
       store_elem(sel + offs + half, b);
     }
@@ -311,7 +313,8 @@ void launch_teal_qkv_reduce(const float* part, int parts, const QkvArgs& a, int 
 #define SD_QKV_R(KT)                                                                          \
   launch_kernel(K_TEAL_QKV_REDUCE, teal_qkv_reduce_kernel<KT>, grid, block, 0, s, part, parts, \
                 d_out, a.h_q, a.h_kv, a.dh, a.rope, a.q_out, (KT*)a.k_full, (KT*)a.v_full,     \
-                a.cap_full, a.row_full, (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel)
+                a.cap_full, a.row_full, (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel,       \
+                a.ragged, a.sel_rows)
   if (kv_dtype == 1) SD_QKV_R(bf16_t);
   else SD_QKV_R(float);
 #undef SD_QKV_R

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
-    assert ctypes.sizeof(sd.sd_layer) == 184
+    assert ctypes.sizeof(sd.sd_layer) == 192
     assert ctypes.sizeof(sd.sd_byte_record) == 80
 
 
@@ -253,3 +253,59 @@ def test_decode_step_rejects_conflicting_modes(mode):
         sd.sd_decode_step(_dims(), layers, 10, FAKE, mode, _FakeWs(1 << 30), 0)
     assert e.value.status == sd.SD_EINVAL
     assert layers[0].n_full == 10
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(k=[40, 40, 40, 10, 40, 40, 40, 40]), sd.SD_EINVAL),   # one head below n_sink + w
+    (dict(stride=30), sd.SD_EINVAL),                            # stride below the largest count
+    (dict(cap_sel=39), sd.SD_ENOSPC),
+    (dict(w=0), sd.SD_EINVAL),
+    (dict(dims=dict(n_q_heads=64, n_kv_heads=64, d_model=8192)), sd.SD_EUNSUPPORTED),
+])
+def test_select_kv_ragged_rejects_before_launch(case, status):
+    a = dict(n=100, w=8, n_sink=4, k=[12, 40, 100, 150, 12, 12, 40, 20], stride=100, cap_sel=100)
+    a.update(case)
+    dims = _dims(**case.get("dims", {}))
+    k = a["k"] if dims.n_kv_heads == 8 else [40] * dims.n_kv_heads
+    if case.get("cap_sel"):
+        k = [40] * 8
+        a["stride"] = 40
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_select_kv_ragged(dims, FAKE, FAKE, 128, a["n"], FAKE, a["w"], a["n_sink"], k,
+                               FAKE, FAKE, a["stride"], FAKE, FAKE, a["cap_sel"], 0,
+                               _FakeWs(1 << 30), 0)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(lens=[10, 0, 10, 10, 10, 10, 10, 10]), sd.SD_EINVAL),
+    (dict(lens=[10, 10, 10, 10, 10, 10, 10, 101]), sd.SD_EINVAL),
+    (dict(n_splits=100000), sd.SD_ENOSPC),
+    (dict(q=None), sd.SD_EINVAL),
+])
+def test_decode_attn_ragged_rejects_before_launch(case, status):
+    lens = case.get("lens", [10, 20, 30, 40, 50, 60, 70, 80])
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_attn_ragged(_dims(), case.get("q", FAKE), FAKE, FAKE, 100, lens, 0.1,
+                                 case.get("n_splits", 0), FAKE, None, _FakeWs(1 << 30), 0)
+    assert e.value.status == status
+
+
+def test_decode_step_ragged_checks_every_head_and_advances_each():
+    L = (sd.sd_layer * 1)()
+    l = L[0]
+    for f in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down_t", "k_full",
+              "v_full", "k_sel", "v_sel"):
+        setattr(l, f, FAKE)
+    l.cap_full, l.n_full, l.cap_sel = 100, 10, 50
+    heads = (ctypes.c_int32 * 8)(5, 6, 7, 8, 9, 50, 11, 12)   # head 5 has no free row
+    l.n_sel_heads = heads
+    ws = _FakeWs(1 << 30)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_KV_SPARSE, ws, 0)
+    assert e.value.status == sd.SD_ENOSPC and "head 5" in sd.sd_last_error()
+    heads[5] = 10
+    with pytest.raises(sd.SdError) as e:   # ragged budgets exclude the window
+        sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_KV_WINDOW, ws, 0)
+    assert e.value.status == sd.SD_EINVAL
+    assert list(heads) == [5, 6, 7, 8, 9, 10, 11, 12] and l.n_full == 10

@@ -130,6 +130,9 @@ class TealStack(Stack):
 
     def __init__(self, wl, n_layers, n, k_keep, **kw):
         super().__init__(wl, n_layers, n, k_keep, **kw)
+        self.add_teal(wl, n_layers)
+
+    def add_teal(self, wl, n_layers):
         self.teal_keep = []
         d, qd, ff = wl.d_model, wl.n_q_heads * wl.head_dim, wl.d_ff
         self.mask_sizes = (d, qd, d, ff)
