@@ -35,7 +35,12 @@ sys.path.insert(0, ROOT)
 METRIC = ("decode-step µs and achieved HBM GB/s (% of peak) vs context length, "
           "dense/KV/CATS/both")
 HBM_PEAK_GBS = 8000.0
-MODES = ("dense", "kv", "cats", "both", "teal", "teal+kv")
+MODES = ("dense", "kv", "cats", "both", "teal", "teal+kv", "catekv", "catekv+cats")
+# CateKV's benchmark setting: 40% of the KV heads adaptive (eta = 1 keeps all
+# their entries), the others keep a budget of 2048
+CATEKV_RATIO, CATEKV_ETA, CATEKV_BUDGET = 0.4, 1.0, 2048
+# decode lengths over which the latency gate charges one-time selection
+GATE_HORIZONS = (256, 1024, 4096, 16384)
 
 
 def parse():
@@ -111,6 +116,18 @@ class Bench:
                 self.V[li].data_ptr(), self.cap_full, 0, self.KS[li].data_ptr(),
                 self.VS[li].data_ptr(), self.cap_sel, 0, self.MASK[li].data_ptr()))
         self.layers = (sd.sd_layer * self.L)(*layers)
+        self.ragged = any(m.startswith("catekv") for m in getattr(args, "modes", "").split(","))
+        if self.ragged:  # CateKV: one gathered buffer per layer with a budget per KV head
+            import ctypes
+            self.adaptive = synth.catekv_adaptive(wl, self.L, CATEKV_RATIO)
+            self.cap_r = n_max + grow + 64
+            self.KR, self.VR, self.RH = [], [], []
+            for li in range(self.L):
+                self.KR.append(torch.zeros(wl.n_kv_heads, self.cap_r, wl.head_dim,
+                                           dtype=torch.bfloat16, device=self.dev))
+                self.VR.append(torch.zeros_like(self.KR[-1]))
+                self.RH.append((ctypes.c_int32 * wl.n_kv_heads)())
+            self.ragged_keep = None
         self.teal = any(m.startswith("teal") for m in getattr(args, "modes", "").split(","))
         if self.teal:  # TEAL mode reads the projections transposed (input-major)
             self.WT, self.TMASK = [], []
@@ -209,10 +226,46 @@ class Bench:
         torch.cuda.synchronize()
         return time.perf_counter() - t0, k_keep
 
-    def reset(self, n, k_keep):
-        for L in self.layers:
+    def catekv_budgets(self, n, li):
+        return [min(n, int(math.floor(CATEKV_ETA * n))) if a else min(n, CATEKV_BUDGET)
+                for a in self.adaptive[li]]
+
+    def select_ragged(self, n):
+        """One-time CateKV selection at context n for every layer (same scores
+        and ranking as select(), one budget per KV head); returns seconds."""
+        torch, sd, wl = self.torch, self.sd, self.wl
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        keep = []
+        for li in range(self.L):
+            kh = self.catekv_budgets(n, li)
+            sd.sd_select_kv_ragged(self.dims, self.K[li], self.V[li], self.cap_full, n,
+                                   self.QW[li], wl.window, wl.n_sink, kh, self.scores, self.idx,
+                                   n, self.KR[li], self.VR[li], self.cap_r, 0, self.ws)
+            keep.append(kh)
+        torch.cuda.synchronize()
+        self.ragged_keep = keep
+        return time.perf_counter() - t0
+
+    def use_ragged(self, on):
+        """Point every layer at the CateKV buffers (on) or the uniform ones."""
+        for li, L in enumerate(self.layers):
+            if on:
+                L.k_sel, L.v_sel = self.KR[li].data_ptr(), self.VR[li].data_ptr()
+                L.cap_sel, L.n_sel_heads = self.cap_r, self.RH[li]
+            else:
+                L.k_sel, L.v_sel = self.KS[li].data_ptr(), self.VS[li].data_ptr()
+                L.cap_sel, L.n_sel_heads = self.cap_sel, None
+
+    def reset(self, n, k_keep, ragged=False):
+        if self.ragged:
+            self.use_ragged(ragged)
+        for li, L in enumerate(self.layers):
             L.n_full = n
             L.n_sel = k_keep
+            if ragged:
+                for h, k in enumerate(self.ragged_keep[li]):
+                    self.RH[li][h] = k
         self.hidden.copy_(self.h0)
 
     def run_steps(self, n, mode_flags, count):
@@ -230,7 +283,8 @@ class Bench:
         sd = self.sd
         return {"dense": 0, "kv": sd.SD_KV_SPARSE, "cats": sd.SD_MLP_SPARSE,
                 "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE, "teal": sd.SD_PROJ_TEAL,
-                "teal+kv": sd.SD_PROJ_TEAL | sd.SD_KV_SPARSE}[mode]
+                "teal+kv": sd.SD_PROJ_TEAL | sd.SD_KV_SPARSE, "catekv": sd.SD_KV_SPARSE,
+                "catekv+cats": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE}[mode]
 
     def teal_step_bytes(self, n_read, fr):
         """Algorithmic bytes of a TEAL step: each projection's kept rows (mean
@@ -245,9 +299,10 @@ class Bench:
     def cell(self, n, k_keep, mode):
         torch, args = self.torch, self.args
         flags = self.mode_flags(mode)
+        ragged = mode.startswith("catekv")
         if flags & self.sd.SD_PROJ_TEAL:
             self.teal_calibrate(n, k_keep, flags)
-        self.reset(n, k_keep)
+        self.reset(n, k_keep, ragged)
         self.run_steps(n, flags, args.warmup)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -261,14 +316,18 @@ class Bench:
         if flags & self.sd.SD_MLP_SPARSE:
             kept = sum(int(m.sum()) for m in self.MASK) / self.L
         base = k_keep if flags & self.sd.SD_KV_SPARSE else n
+        if ragged:  # mean over layers and KV heads of the per-head kept rows
+            base = sum(sum(k) for k in self.ragged_keep) / (self.L * self.wl.n_kv_heads)
         n_read = base + args.warmup + (args.steps - 1) / 2.0 + 1
         extra = {}
+        if ragged:
+            extra["kv_keep_fraction"] = round(base / n, 4)
         if flags & self.sd.SD_PROJ_TEAL:
             b, f = self.teal_step_bytes(n_read, self.teal_keep_fractions())
             extra = dict(teal_keep=[round(x, 4) for x in f])
         else:
             b = self.step_bytes(n_read, kept)
-            extra = dict(n_kept_mean=kept)
+            extra["n_kept_mean"] = kept
         return dict(context=n, mode=mode, ms_per_step=ms, us_per_step=ms * 1e3,
                     bytes_per_step=b, gbs=b / ms / 1e6, hbm_frac=b / ms / 1e6 / HBM_PEAK_GBS,
                     kv_rows_read=n_read, **extra)
@@ -494,6 +553,23 @@ def cpu_baseline(bench, n, seconds):
                         f"{per_layer * reps:.1f} s; per-step time scaled x{bench.L} layers"))
 
 
+def latency_gate(sweep):
+    """The lookup table of a latency gate ([Cross] §3, "Dispatch and
+    batching"): for each timed context and each decode length T, the mode
+    with the least total time, T steps plus its one-time selection (KV
+    modes).  Every timed mode is treated as admissible here: admissibility
+    is a quality test that needs trained weights and real text."""
+    out = []
+    for n in sorted({c["context"] for c in sweep}):
+        cells = [c for c in sweep if c["context"] == n]
+        for T in GATE_HORIZONS:
+            cost = {c["mode"]: T * c["ms_per_step"] + (c.get("select_ms") or 0.0) for c in cells}
+            best = min(cost, key=cost.get)
+            out.append(dict(context=n, horizon=T, best=best,
+                            total_ms={k: round(v, 2) for k, v in cost.items()}))
+    return out
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -517,9 +593,13 @@ def main():
     for n in sorted(bench.contexts):
         secs, k_keep = bench.select(n)
         sel_ms[n] = secs * 1e3
-        for mode in [m for m in MODES if m in args.modes.split(",")]:
+        modes = [m for m in MODES if m in args.modes.split(",")]
+        sel_r = bench.select_ragged(n) * 1e3 if bench.ragged else None
+        for mode in modes:
             c = bench.cell(n, k_keep, mode)
-            c["select_ms"] = sel_ms[n] if mode in ("kv", "both") else None
+            flags = bench.mode_flags(mode)
+            c["select_ms"] = (sel_r if mode.startswith("catekv") else sel_ms[n]) \
+                if flags & bench.sd.SD_KV_SPARSE else None
             sweep.append(c)
             print(f"# n={n:6d} {mode:5s} {c['us_per_step']:9.1f} us/step "
                   f"{c['gbs']:7.1f} GB/s ({100 * c['hbm_frac']:.1f}% of peak)", flush=True)
@@ -551,6 +631,9 @@ def main():
                   flush=True)
         print(f"# window speedups {base['window_speedup']} (byte bound {base['window_byte_bound']})",
               flush=True)
+    gate = latency_gate(sweep)
+    for g in gate:
+        print(f"# gate n={g['context']:6d} horizon {g['horizon']:5d}: {g['best']}", flush=True)
     line = dict(
         metric=METRIC, value=round(head["gbs"], 1), unit="GB/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=round(head["ms_per_step"], 4), higher_is_better=True,
@@ -565,6 +648,7 @@ def main():
         roofline=roof, cpu_baseline=cpu,
         copy_ceiling_gbs=round(copy_gbs, 1),
         attention_baselines=base,
+        latency_gate=gate,
         kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                  for k, e in kern.items()},
         sweep=[{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}

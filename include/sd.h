@@ -145,11 +145,11 @@ sd_status sd_select_kv(const sd_dims* dims, const void* k_full, const void* v_fu
  * k, v   [h_kv, cap, d_h] kv_dtype; n_ctx >= 1 rows read.
  * out    [h_q, d_h] float32: softmax(scale * q.K^T) V per query head.
  * lse    [h_q] float32 log-sum-exp of the scaled logits, or NULL.
- * n_splits  chunks of the row range per KV head (at most 128), 0 = chosen by
+ * n_splits  chunks of the row range per KV head (at most 256), 0 = chosen by
  *           the library; the result depends on it only through float32
  *           rounding.  A second launch merges the chunks in chunk order.
  * Errors: EINVAL unless 1 <= n_ctx <= cap; ENOSPC for a short workspace or
- *         n_splits above 128.
+ *         n_splits above 256.
  */
 sd_status sd_decode_attn(const sd_dims* dims, const float* q, const void* k, const void* v,
                          int32_t cap, int32_t n_ctx, float scale, int32_t n_splits,
@@ -186,8 +186,9 @@ sd_status sd_select_kv_ragged(const sd_dims* dims, const void* k_full, const voi
  * CateKV passage).  Query heads of group kv attend over rows
  * 0..n_ctx_heads[kv]-1 of KV head kv.
  * n_ctx_heads  [h_kv] int32 [host].
- * n_splits     as sd_decode_attn, counted on the longest head; a head shorter
- *              than the others leaves its surplus chunks empty.
+ * n_splits     chunks of the longest head (at most 256); a shorter head leaves
+ *              its trailing chunks empty.  0 = chosen by the library so that the
+ *              rows of all heads together spread over the whole GPU.
  * Errors: EINVAL unless 1 <= n_ctx_heads[kv] <= cap for every head; ENOSPC as
  *         sd_decode_attn; EUNSUPPORTED for more than 32 KV heads.
  */

@@ -26,9 +26,9 @@ sd_status fail(sd_status st, const char* fmt, ...) {
 
 bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kMaxSplits = 128;        // split-K chunks per KV head (the merge holds them in VGPRs)
-constexpr int kSplitBlocks = 512;      // auto mode: aim for this many split workgroups
-constexpr int kMinChunk = 256;         // auto mode: rows per split, lower bound
+constexpr int kMaxSplits = 256;        // split-K chunks per KV head (the merge's capacity)
+constexpr int kSplitBlocks = 512;      // auto mode: at most this many split workgroups
+constexpr int kMinChunk = 64;          // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup
 constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in VGPRs
 
@@ -122,14 +122,41 @@ int cu_count() {
   return cu > 0 ? cu : 256;
 }
 
-// Splits per KV head: about kSplitBlocks workgroups in all, at least kMinChunk
-// rows each, at most kMaxSplits.
-int auto_splits(int n_ctx, int h_kv) {
-  int s = (kSplitBlocks + h_kv - 1) / h_kv;
-  const int by_rows = (n_ctx + kMinChunk - 1) / kMinChunk;
-  if (s > by_rows) s = by_rows;
+// Split count of the split-K attention.  Measured on MI355X, two resident
+// workgroups per CU stream best, and a launch with more than kSplitBlocks
+// (= 2 per CU) workgroups with work runs its surplus as a second, slow round
+// (25% longer just above the line).  So: chunks of at least kMinChunk rows,
+// about kSplitBlocks of them over all heads, then the largest split count
+// whose chunks (ceil(n_max / s) rows, the size the launch uses) number at most
+// kSplitBlocks, at most kMaxSplits.  Ragged lengths count each head's own
+// chunks; a long head among short ones then gets many splits.
+int plan_splits(const sd::HeadInts& lens, int h_kv, int n_max) {
+  long long total = 0;
+  for (int h = 0; h < h_kv; ++h) total += lens.v[h];
+  long long chunk = (total + kSplitBlocks - 1) / kSplitBlocks;
+  if (chunk < kMinChunk) chunk = kMinChunk;
+  int s = (int)((n_max + chunk - 1) / chunk);
   if (s > kMaxSplits) s = kMaxSplits;
+  for (; s > 1; --s) {
+    const int c = (n_max + s - 1) / s;
+    long long blocks = 0;
+    for (int h = 0; h < h_kv; ++h) blocks += (lens.v[h] + c - 1) / c;
+    if (blocks <= kSplitBlocks) break;
+  }
   return s < 1 ? 1 : s;
+}
+
+int auto_splits(int n_ctx, int h_kv) {
+  sd::HeadInts lens{};
+  for (int h = 0; h < h_kv && h < sd::kMaxKvHeads; ++h) lens.v[h] = n_ctx;
+  // more KV heads than the table holds: equal lengths, so scale the count
+  if (h_kv > sd::kMaxKvHeads) {
+    int s = kSplitBlocks / h_kv;
+    const int by_rows = (n_ctx + kMinChunk - 1) / kMinChunk;
+    if (s > by_rows) s = by_rows;
+    return s < 1 ? 1 : s;
+  }
+  return plan_splits(lens, h_kv, n_ctx);
 }
 
 // Attention paths (the step's mode bits select them).
@@ -408,7 +435,8 @@ sd_status sd_decode_attn_ragged(const sd_dims* dims, const float* q, const void*
   if (n_splits < 0) return fail(SD_EINVAL, "n_splits must be >= 0");
   if (n_splits > L.max_splits)
     return fail(SD_ENOSPC, "n_splits %d above the workspace's %d", n_splits, L.max_splits);
-  int sp = n_splits ? (n_splits < n_max ? n_splits : n_max) : auto_splits(n_max, dims->n_kv_heads);
+  int sp = n_splits ? (n_splits < n_max ? n_splits : n_max)
+                    : plan_splits(lens, dims->n_kv_heads, n_max);
   enqueue_attn(*dims, L, static_cast<char*>(ws), q, k, v, cap, n_max, n_max, 0, scale, sp,
                P_SPLITK, out, lse, static_cast<hipStream_t>(stream), &lens);
   return check_launch("sd_decode_attn_ragged");
@@ -655,8 +683,9 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     const Path path = masked ? P_MASKED : fused ? P_FUSED : P_SPLITK;
     const bool ragged = kv_sparse && qa.ragged;
     if (ragged) n_ctx = sink = n_ragged;
-    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, sink, shift, scale,
-                 auto_splits(n_ctx, hkv), path, attn, nullptr, s, ragged ? &lens : nullptr);
+    const int splits = ragged ? plan_splits(lens, hkv, n_ctx) : auto_splits(n_ctx, hkv);
+    enqueue_attn(*dims, L, wsb, q, kc, vc, cap, n_ctx, sink, shift, scale, splits, path, attn,
+                 nullptr, s, ragged ? &lens : nullptr);
 
     if (teal) {
       float* part = reinterpret_cast<float*>(wsb + L.teal_part);

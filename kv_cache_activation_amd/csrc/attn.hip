@@ -16,13 +16,23 @@
 //   log2 domain; at the end the groups and the four waves merge their states
 //   and write one (m, l, acc[d_h]) per query head and split.
 //
-//   A second, small launch merges the splits, one workgroup per query head:
+//   Ragged per-head lengths launch only the chunks that hold rows: a flat
+//   grid whose block index is mapped to (KV head, chunk) by per-head prefix
+//   counts, so a few long heads next to many short ones leave no idle
+//   workgroups behind.
+//
+//   A second, small launch merges the splits: workgroup (query head, 32
+//   columns), eight split groups of 32 threads; every thread loads its share
+//   of split values at once (one memory round trip), the workgroup turns the
+//   split maxima into weights meanwhile,
 //   out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2,
-//   splits in order, so the result does not depend on scheduling.  The launch
+//   and the groups are added in a fixed order, so the result does not depend
+//   on scheduling.  The launch
 //   boundary makes the partials visible to every XCD; measured on MI355X it is
 //   cheaper than a hand-off inside one launch (coherent stores, a wait for
 //   their acknowledgement, a ticket and coherent loads are three memory round
 //   trips).
+#include <limits.h>
 #include <math.h>
 
 #include "common.hpp"
@@ -31,14 +41,14 @@
 namespace sd {
 
 constexpr int kAttnThreads = 256;
-constexpr int kMaxSplits = 128;  // splits per KV head (the merge holds one column of them in VGPRs)
+constexpr int kMaxSplits = 256;  // splits per KV head (the merge holds a column's share in VGPRs)
 constexpr int kAttnWaves = kAttnThreads / kWave;
 
 template <typename KT, int DH, int G, int U>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
-    int n_ctx, int sink, int shift, int kv_div, int ragged, HeadInts lens, float scale_log2,
-    int chunk, int n_splits, float* __restrict__ pm, float* __restrict__ pl,
+    int n_ctx, int sink, int shift, int kv_div, int ragged, HeadInts lens, HeadInts starts,
+    float scale_log2, int chunk, int n_splits, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ pacc) {
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
@@ -46,12 +56,20 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   __shared__ float sm_m[kAttnWaves][G], sm_l[kAttnWaves][G];
   __shared__ float sm_acc[kAttnWaves][G][DH];
 
-  const int split = blockIdx.x, kv = blockIdx.y;
+  // grid (splits, groups); ragged: a flat grid, block b belongs to the last
+  // head whose first chunk starts at or before b (starts ascending, unused
+  // entries past the last head hold INT_MAX)
+  int split = blockIdx.x, kv = blockIdx.y;
+  if (ragged) {
+    kv = 0;
+#pragma unroll
+    for (int h = 1; h < kMaxKvHeads; ++h) kv += (int)(split >= starts.v[h]);
+    split -= starts.v[kv];
+  }
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int sub = lane % LPR;
   const int slot = wave * RPW + lane / LPR;
-  // rows of this KV head: n_ctx, or its own count under ragged budgets (a
-  // split past the end has no rows and writes the empty partial)
+  // rows of this KV head: n_ctx, or its own count under ragged budgets
   const int rows = ragged ? lens.v[(kv / kv_div) & (kMaxKvHeads - 1)] : n_ctx;
   const int r0 = split * chunk;
   const int r1 = min(rows, r0 + chunk);
@@ -199,58 +217,68 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
 }
 
-// One workgroup per query head, one thread per column: every split's value of
-// the thread's column is loaded before the first is used (one memory round
-// trip); wave 0 turns the split maxima into weights.
+// Merge of the splits: workgroup (query head, kMergeCols columns); thread t
+// serves column t % kMergeCols for splits g, g + kMergeGroups, ... (g = t /
+// kMergeCols), at most CAP splits.  Loads come from clamped indices, so none
+// depends on a branch and all are in flight together; splits past the count
+// get weight zero.  Ragged lengths: query head h reads counts.v[h / G] splits.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeCols = 32;
+constexpr int kMergeGroups = kMergeThreads / kMergeCols;
+
 template <int DH, int CAP>
-__global__ __launch_bounds__(DH) void attn_merge_kernel(const float* __restrict__ pm,
-                                                        const float* __restrict__ pl,
-                                                        const float* __restrict__ pacc,
-                                                        int n_splits, float* __restrict__ out,
-                                                        float* __restrict__ lse) {
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
+    const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ pacc,
+    int stride, int ragged, HeadInts counts, int G, float* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int PER = CAP / kMergeGroups;  // splits per thread
+  constexpr int NW = kMergeThreads / kWave;
   __shared__ float w_s[CAP];
-  __shared__ float inv_l, big_m, big_l;
-  const int h = blockIdx.x, c = threadIdx.x;
-  const float* base = pacc + (size_t)h * n_splits * DH + c;
-  float v[CAP];
+  __shared__ float red_m[NW], red_l[NW];
+  __shared__ float share[kMergeGroups][kMergeCols];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int col = blockIdx.y * kMergeCols + t % kMergeCols, grp = t / kMergeCols;
+  const int ns = ragged ? counts.v[(h / G) & (kMaxKvHeads - 1)] : stride;
+  const float* base = pacc + (size_t)h * stride * DH + col;
+  float v[PER];
 #pragma unroll
-  for (int sp = 0; sp < CAP; ++sp)
-    v[sp] = sp < n_splits ? base[(size_t)sp * DH] : 0.f;
-  if (threadIdx.x < kWave) {  // wave 0: split weights, CAP / 64 splits per lane
-    constexpr int PL = CAP / kWave;
-    const int lane = threadIdx.x;
-    float mi[PL], li[PL];
-#pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      const int sp = lane + k * kWave;
-      mi[k] = sp < n_splits ? pm[(size_t)h * n_splits + sp] : -INFINITY;
-      li[k] = sp < n_splits ? pl[(size_t)h * n_splits + sp] : 0.f;
-    }
-    float mm = mi[0];
-#pragma unroll
-    for (int k = 1; k < PL; ++k) mm = fmaxf(mm, mi[k]);
-    const float M = wave_max(mm);
-    float wl = 0.f;
-#pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      const float wi = mi[k] == -INFINITY ? 0.f : exp2f(mi[k] - M);
-      w_s[lane + k * kWave] = wi;
-      wl = fmaf(wi, li[k], wl);
-    }
-    const float L = wave_sum(wl);
-    if (lane == 0) {
-      big_m = M;
-      big_l = L;
-      inv_l = 1.0f / L;
-    }
+  for (int i = 0; i < PER; ++i) {
+    const int sp = min(grp + i * kMergeGroups, ns - 1);
+    v[i] = base[(size_t)sp * DH];
   }
+  // split weights: thread t owns split t (CAP <= kMergeThreads)
+  const int ts = min(t, ns - 1);
+  const float mt = t < ns ? pm[(size_t)h * stride + ts] : -INFINITY;
+  const float lt = pl[(size_t)h * stride + ts];
+  const int lane = lane_id(), wave = t / kWave;
+  float M = wave_max(mt);
+  if (lane == 0) red_m[wave] = M;
   __syncthreads();
+  M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w]);
+  const float wt = mt == -INFINITY ? 0.f : exp2f(mt - M);
+  if (t < CAP) w_s[t] = wt;
+  const float lsum = wave_sum(wt * (t < ns ? lt : 0.f));
+  if (lane == 0) red_l[wave] = lsum;
+  __syncthreads();
+  float L = red_l[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) L += red_l[w];
   float A = 0.f;
 #pragma unroll
-  for (int sp = 0; sp < CAP; ++sp)
-    if (sp < n_splits) A = fmaf(w_s[sp], v[sp], A);
-  out[(size_t)h * DH + c] = A * inv_l;
-  if (lse && c == 0) lse[h] = (big_m + log2f(big_l)) * 0.69314718055994530942f;
+  for (int i = 0; i < PER; ++i) {
+    const int sp = grp + i * kMergeGroups;
+    if (sp < ns) A = fmaf(w_s[sp], v[i], A);
+  }
+  share[grp][t % kMergeCols] = A;
+  __syncthreads();
+  if (grp) return;
+  float S = share[0][t];
+#pragma unroll
+  for (int g = 1; g < kMergeGroups; ++g) S += share[g][t];
+  out[(size_t)h * DH + col] = S / L;
+  if (lse && col == 0) lse[h] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
 template <typename KT, int DH>
@@ -261,12 +289,23 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   const int groups = a.per_query_head ? a.h_q : a.h_kv;
   const float scale_log2 = a.scale * 1.44269504088896340736f;
   dim3 grid(a.n_splits, groups);
+  // ragged: chunks per KV head and the flat grid's per-head first block
+  HeadInts counts{}, starts{};
+  if (a.ragged) {
+    int total = 0;
+    for (int h = 0; h < kMaxKvHeads; ++h) {
+      counts.v[h] = h < a.h_kv ? (a.lens.v[h] + a.chunk - 1) / a.chunk : 0;
+      starts.v[h] = h < a.h_kv ? total : INT_MAX;
+      total += counts.v[h];
+    }
+    grid = dim3(total, 1);
+  }
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
 #define SD_ATTN_G(GG, UU)                                                                   \
   launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU>, grid, dim3(kAttnThreads), 0, s, \
-                a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, scale_log2,      \
-                a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
+                a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, starts,        \
+                scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
   switch (G) {
     case 1: SD_ATTN_G(1, 8); break;
     case 2: SD_ATTN_G(2, 8); break;
@@ -274,12 +313,15 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
     default: SD_ATTN_G(8, 4); break;
   }
 #undef SD_ATTN_G
-  if (a.n_splits <= 64)
-    launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, 64>, dim3(a.h_q), dim3(DH), 0, s, a.pm,
-                  a.pl, a.pacc, a.n_splits, a.out, a.lse);
-  else
-    launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, kMaxSplits>, dim3(a.h_q), dim3(DH), 0, s,
-                  a.pm, a.pl, a.pacc, a.n_splits, a.out, a.lse);
+  const dim3 mgrid(a.h_q, DH / kMergeCols);
+  const int G_all = a.h_q / a.h_kv;
+#define SD_MERGE(CAPV)                                                                        \
+  launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, CAPV>, mgrid, dim3(kMergeThreads), 0, s, \
+                a.pm, a.pl, a.pacc, a.n_splits, a.ragged, counts, G_all, a.out, a.lse)
+  if (a.n_splits <= 64) SD_MERGE(64);
+  else if (a.n_splits <= 128) SD_MERGE(128);
+  else SD_MERGE(kMaxSplits);
+#undef SD_MERGE
 }
 
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s) {

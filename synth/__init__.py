@@ -11,6 +11,10 @@ Recipes (the pages use real text and trained weights, which are not here):
 * cached K, V ~ N(0, 1), multiplied per (KV head, channel) by scales drawn
   from LogNormal(0, 0.5) for the 8B-class workloads (outlier channels);
 * window queries and decode queries ~ N(0, 1); hidden state ~ N(0, 1);
+* adaptive heads (CateKV's head classes, which the pages obtain offline from
+  reference data): round(ratio * n_kv_heads * n_layers) adaptive KV heads in
+  all, each layer holding the floor or the ceiling of the per-layer mean,
+  layers and heads picked by seeded permutations;
 * planted keys (retrieval stand-in): 64 positions drawn without replacement
   from the non-forced range, shared by all KV heads; the key at each is
   4 sqrt(d_h) times the unit vector along the sum of that KV head's window
@@ -27,7 +31,7 @@ import numpy as np
 
 # tensor ids for the seed sequence
 T_QKV, T_O, T_GATE, T_UP, T_DOWN, T_K, T_V, T_KSCALE, T_VSCALE = range(9)
-T_QWIN, T_Q, T_H, T_PLANT, T_CAL, T_PARTIALS, T_GATE_IN = range(9, 16)
+T_QWIN, T_Q, T_H, T_PLANT, T_CAL, T_PARTIALS, T_GATE_IN, T_ADAPT = range(9, 17)
 
 
 @dataclass(frozen=True)
@@ -174,3 +178,18 @@ def hidden(wl: Workload, draw: int = 0) -> np.ndarray:
 def calibration_states(wl: Workload, layer: int, n_states: int = 256) -> np.ndarray:
     return rng(wl.wid, layer, T_CAL).standard_normal((n_states, wl.d_model),
                                                      dtype=np.float32)
+
+
+def catekv_adaptive(wl: Workload, n_layers: int, ratio: float = 0.4) -> list:
+    """Per layer, which KV heads are adaptive (True) or consistent (False)."""
+    h = wl.n_kv_heads
+    total = int(np.floor(ratio * h * n_layers + 0.5))
+    base, extra = divmod(total, n_layers)
+    r = rng(wl.wid, 0, T_ADAPT)
+    more = set(r.permutation(n_layers)[:extra].tolist())
+    out = []
+    for li in range(n_layers):
+        k = base + (1 if li in more else 0)
+        heads = set(rng(wl.wid, li, T_ADAPT).permutation(h)[:k].tolist())
+        out.append([j in heads for j in range(h)])
+    return out

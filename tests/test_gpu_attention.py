@@ -29,7 +29,8 @@ def _run(wl, k, v, cap, n_ctx, q, n_splits=0, scale=None):
 @pytest.mark.parametrize("n_ctx,splits", [(1, 0), (2, 0), (127, 0), (129, 0), (2048, 0),
                                           (2049, 0), (2049, 1), (2049, 3), (2049, 7), (64, 64), (300, 64),
                                           (4099, 17), (300, 128), (4099, 128), (16385, 0),
-                                          (16385, 97)])
+                                          (16385, 97), (16385, 129), (16385, 200), (4099, 256),
+                                          (70001, 0)])
 def test_tiny_fp32_matches_oracle(n_ctx, splits):
     wl = synth.TINY
     cap = n_ctx + 5

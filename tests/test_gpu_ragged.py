@@ -133,7 +133,9 @@ def _attn(wl, k, v, cap, lens, q, n_splits=0):
 
 
 @pytest.mark.parametrize("lens,splits", [([1, 2048], 0), ([2049, 1], 0), ([300, 4099], 17),
-                                         ([4099, 129], 128), ([64, 64], 64), ([5, 3000], 7)])
+                                         ([4099, 129], 128), ([64, 64], 64), ([5, 3000], 7),
+                                         ([4099, 129], 256), ([70000, 3000], 0),
+                                         ([2000, 40000], 200)])
 def test_tiny_fp32_ragged_attention_matches_oracle(lens, splits):
     wl = synth.TINY
     cap = max(lens) + 8
