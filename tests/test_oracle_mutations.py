@@ -38,11 +38,16 @@ MUTS = [
  ("step.py", "layer.k_sel[kv, layer.n_sel_heads[kv]] = k_r[kv]", "layer.k_sel[kv, layer.n_sel_heads[0]] = k_r[kv]"),
  ("selection.py", "return [min(n, int(np.floor(eta * n))) if a else min(n, int(budget)) for a in adaptive]",
   "return [min(n, int(np.floor(eta * n))) if not a else min(n, int(budget)) for a in adaptive]"),
+ ("batch.py", "return np.any(m, axis=0)", "return np.all(m, axis=0)"),
+ ("batch.py", "return 1.0 - (1.0 - keep) ** batch", "return 1.0 - keep ** batch"),
+ ("batch.py", "for b, (layers, h, pos) in enumerate(zip(seq_layers, hs, positions)):",
+  "for b, (layers, h, pos) in enumerate(zip(seq_layers, hs, positions[::-1])):"),
 ]
 
 PIN_FILES = ["tests/test_oracle_byte_account.py", "tests/test_oracle_selection.py",
              "tests/test_oracle_attention.py", "tests/test_oracle_cats.py",
-             "tests/test_oracle_step.py", "tests/test_oracle_teal.py"]
+             "tests/test_oracle_step.py", "tests/test_oracle_teal.py",
+             "tests/test_oracle_batch.py"]
 
 
 @pytest.mark.parametrize("fname,old,new", MUTS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTS)])
