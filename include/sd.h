@@ -342,6 +342,50 @@ typedef struct {
 sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers, int32_t pos,
                          float* hidden, uint32_t mode, void* ws, size_t ws_bytes, void* stream);
 
+/* One sequence's caches in one layer, for sd_decode_step_batch (the fields of
+ * sd_layer with the same names, same meaning). */
+typedef struct {
+  void* k_full;            /* [h_kv, cap_full, d_h] */
+  void* v_full;
+  int32_t cap_full;
+  int32_t n_full;          /* valid rows before the step; advanced by one [host] */
+  void* k_sel;             /* gathered buffer [h_kv, cap_sel, d_h], or NULL */
+  void* v_sel;
+  int32_t cap_sel;
+  int32_t n_sel;           /* advanced by one when k_sel != NULL */
+} sd_seq_kv;
+
+/*
+ * sd_batch_workspace_bytes -- workspace of sd_decode_step_batch for `batch`
+ * sequences [host]; 0 on invalid dims or batch.
+ */
+size_t sd_batch_workspace_bytes(const sd_dims* dims, int32_t batch);
+
+/*
+ * sd_decode_step_batch -- one decode step of `batch` sequences (2..8) that
+ * share every weight read ([Cross] §3.2 "Dispatch and batching", §4.4
+ * "Batching"): each sequence computes exactly its own sd_decode_step (its own
+ * hidden state, position, caches and CATS mask, the layer threshold shared),
+ * but each weight row is read once for the whole batch.  Under SD_MLP_SPARSE
+ * the up rows and down columns read are those of the union of the batch's
+ * masks (a channel kept by at least one sequence); a sequence that dropped a
+ * channel gets no contribution from it.
+ * layers  [host] [n_layers]: weights, norms and cats_threshold as in
+ *         sd_decode_step (its cache fields are not used); mask_out, when not
+ *         NULL, receives the union mask [d_ff] (1 kept by some sequence).
+ * kv      [host] [batch * n_layers], sequence-major (kv[b * n_layers + l]):
+ *         each sequence's caches; n_full and n_sel advanced on success.
+ * pos     [host] [batch] positions; hidden [batch, d] float32, in place.
+ * mode    0, SD_KV_SPARSE, SD_MLP_SPARSE or both.
+ * Sizes:  d_model and n_q_heads * d_h at most 4096.
+ * Errors: EINVAL for batch outside 2..8, other mode bits, bad pointers or a
+ *         missing gathered buffer under SD_KV_SPARSE; ENOSPC for a full cache or
+ *         a short workspace (sd_batch_workspace_bytes); EUNSUPPORTED for widths.
+ */
+sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_layer* layers,
+                               int32_t batch, sd_seq_kv* kv, const int32_t* pos, float* hidden,
+                               uint32_t mode, void* ws, size_t ws_bytes, void* stream);
+
 /* Byte account record ([Cross] §3). Bytes as doubles (exact below 2^53). */
 typedef struct {
   double b_attn;      /* bytes of W_q, W_k, W_v, W_o per layer */

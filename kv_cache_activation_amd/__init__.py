@@ -33,7 +33,7 @@ SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_decode_attn",
            "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
-           "sd_decode_step", "sd_byte_account", "sd_calibrate_workspace_bytes",
+           "sd_decode_step", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account", "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
 
@@ -62,6 +62,13 @@ class sd_layer(ctypes.Structure):
                 ("w_gate_t", ctypes.c_void_p), ("w_up_t", ctypes.c_void_p),
                 ("teal_t", ctypes.c_float * 4), ("teal_masks_out", ctypes.c_void_p),
                 ("n_sel_heads", ctypes.POINTER(ctypes.c_int32))]
+
+
+class sd_seq_kv(ctypes.Structure):
+    _fields_ = [("k_full", ctypes.c_void_p), ("v_full", ctypes.c_void_p),
+                ("cap_full", ctypes.c_int32), ("n_full", ctypes.c_int32),
+                ("k_sel", ctypes.c_void_p), ("v_sel", ctypes.c_void_p),
+                ("cap_sel", ctypes.c_int32), ("n_sel", ctypes.c_int32)]
 
 
 class sd_byte_record(ctypes.Structure):
@@ -93,6 +100,12 @@ _lib.sd_select_kv_ragged.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _I, _I, _P
 _lib.sd_decode_attn_ragged.restype = _I
 _lib.sd_decode_attn_ragged.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I,
                                        ctypes.POINTER(_I), _F, _I, _P, _P, _P, _S, _P]
+_lib.sd_batch_workspace_bytes.restype = _S
+_lib.sd_batch_workspace_bytes.argtypes = [ctypes.POINTER(sd_dims), _I]
+_lib.sd_decode_step_batch.restype = _I
+_lib.sd_decode_step_batch.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_layer), _I,
+                                      ctypes.POINTER(sd_seq_kv), ctypes.POINTER(_I), _P, _U, _P,
+                                      _S, _P]
 _lib.sd_decode_attn.restype = _I
 _lib.sd_decode_attn.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I, _I, _F, _I, _P, _P,
                                 _P, _S, _P]
@@ -239,6 +252,22 @@ def sd_teal_gemv(dims, x, d_in, norm_w, threshold, w_t, w2_t, d_out, y, y2, flag
     _check(_lib.sd_teal_gemv(ctypes.byref(dims), _ptr(x), d_in, _ptr(norm_w), threshold, _ptr(w_t),
                              _ptr(w2_t), d_out, _ptr(y), _ptr(y2), flags, _ptr(idx), _ptr(n_kept),
                              p, nb, _stream(stream)))
+
+
+def sd_batch_workspace_bytes(dims: sd_dims, batch: int) -> int:
+    return int(_lib.sd_batch_workspace_bytes(ctypes.byref(dims), batch))
+
+
+def sd_decode_step_batch(dims, layers, kv, pos, hidden, mode, ws, stream=None) -> None:
+    """`layers`: ctypes array of sd_layer [n_layers] (weights); `kv`: ctypes
+    array of sd_seq_kv [batch * n_layers], sequence-major (advanced in place);
+    `pos`: the batch's positions."""
+    p, nb = _ws(ws)
+    n_layers = len(layers)
+    batch = len(kv) // n_layers if n_layers else 0
+    _check(_lib.sd_decode_step_batch(ctypes.byref(dims), n_layers, layers, batch, kv,
+                                     _host_ints(pos), _ptr(hidden), mode, p, nb,
+                                     _stream(stream)))
 
 
 def sd_decode_step(dims, layers, pos, hidden, mode, ws, stream=None) -> None:

@@ -731,6 +731,192 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
   return SD_OK;
 }
 
+// Batched decode: the single-sequence layout (attention partials, reused by
+// every sequence in stream order) plus the batch's own buffers.
+struct BatchLayout {
+  Layout base;
+  size_t qkv, q, attn, act, hmid, keep, uni, part, total;
+};
+
+BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
+  BatchLayout B{};
+  B.base = make_layout(dm, 0, 0);
+  size_t off = B.base.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  const size_t hq = dm.n_q_heads, dh = dm.head_dim, hkv = dm.n_kv_heads, d = dm.d_model,
+               ff = dm.d_ff, n = nb;
+  B.qkv = take(n * (hq + 2 * hkv) * dh * 4);
+  B.q = take(n * hq * dh * 4);
+  B.attn = take(n * hq * dh * 4);
+  B.act = take(n * ff * 4);
+  B.hmid = take(n * ff * 4);
+  B.keep = take(n * ff);
+  B.uni = take(ff);
+  B.part = take((size_t)sd::down_parts((int)ff) * n * d * 4);
+  B.total = off;
+  return B;
+}
+
+sd_status check_batch_dims(const sd_dims* dims, int32_t batch) {
+  sd_status st = check_dims(dims);
+  if (st) return st;
+  if (batch < 2 || batch > sd::kMaxBatch)
+    return fail(SD_EINVAL, "batch must be 2..%d (one sequence: sd_decode_step)", sd::kMaxBatch);
+  if (dims->d_model > 4096 || dims->n_q_heads * dims->head_dim > 4096)
+    return fail(SD_EUNSUPPORTED, "batched step: d_model and n_q_heads * head_dim at most 4096");
+  return SD_OK;
+}
+
+size_t sd_batch_workspace_bytes(const sd_dims* dims, int32_t batch) {
+  if (check_batch_dims(dims, batch) != SD_OK) return 0;
+  return make_batch_layout(*dims, batch).total;
+}
+
+sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_layer* layers,
+                               int32_t batch, sd_seq_kv* kv, const int32_t* pos, float* hidden,
+                               uint32_t mode, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_batch_dims(dims, batch);
+  if (st) return st;
+  if (n_layers < 1 || !layers || !kv || !pos || !aligned(hidden) || !aligned(ws))
+    return fail(SD_EINVAL, "null or misaligned argument");
+  if (mode & ~(uint32_t)(SD_KV_SPARSE | SD_MLP_SPARSE))
+    return fail(SD_EINVAL, "batched step modes: SD_KV_SPARSE and/or SD_MLP_SPARSE");
+  const bool kv_sparse = mode & SD_KV_SPARSE, mlp_sparse = mode & SD_MLP_SPARSE;
+  const BatchLayout B = make_batch_layout(*dims, batch);
+  if (ws_bytes < B.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, B.total);
+  for (int i = 0; i < n_layers; ++i) {
+    const sd_layer& l = layers[i];
+    if (!aligned(l.attn_norm) || !aligned(l.mlp_norm) || !aligned(l.w_qkv) || !aligned(l.w_o) ||
+        !aligned(l.w_gate) || !aligned(l.w_up) || !aligned(l.w_down_t))
+      return fail(SD_EINVAL, "layer %d: null or misaligned weight", i);
+    if (std::isnan(l.cats_threshold)) return fail(SD_EINVAL, "layer %d: threshold is NaN", i);
+    if (l.mask_out && !aligned(l.mask_out))
+      return fail(SD_EINVAL, "layer %d: misaligned mask_out", i);
+    for (int b = 0; b < batch; ++b) {
+      const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
+      if (!aligned(c.k_full) || !aligned(c.v_full))
+        return fail(SD_EINVAL, "sequence %d layer %d: null or misaligned cache", b, i);
+      if (c.n_full < 0 || c.n_full >= c.cap_full)
+        return fail(SD_ENOSPC, "sequence %d layer %d: full cache has no free row", b, i);
+      if (c.k_sel || c.v_sel) {
+        if (!aligned(c.k_sel) || !aligned(c.v_sel))
+          return fail(SD_EINVAL, "sequence %d layer %d: misaligned gathered buffer", b, i);
+        if (c.n_sel < 0 || c.n_sel >= c.cap_sel)
+          return fail(SD_ENOSPC, "sequence %d layer %d: gathered buffer has no free row", b, i);
+      } else if (kv_sparse) {
+        return fail(SD_EINVAL, "sequence %d layer %d: KV-sparse mode needs a gathered buffer",
+                    b, i);
+      }
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  const int d = dims->d_model, hq = dims->n_q_heads, dh = dims->head_dim, hkv = dims->n_kv_heads;
+  const int ff = dims->d_ff, qkv_out = (hq + 2 * hkv) * dh;
+  const float scale = 1.0f / std::sqrt((float)dh);
+  float* qkv = reinterpret_cast<float*>(wsb + B.qkv);
+  float* q = reinterpret_cast<float*>(wsb + B.q);
+  float* attn = reinterpret_cast<float*>(wsb + B.attn);
+  for (int i = 0; i < n_layers; ++i) {
+    const sd_layer& l = layers[i];
+    // QKV for every sequence from one read of W_qkv, then RoPE and the appends
+    sd::BgemvArgs g{};
+    g.kind = sd::K_BATCH_QKV;
+    g.x = hidden;
+    g.nb = batch;
+    g.d_in = d;
+    g.norm = l.attn_norm;
+    g.eps = dims->rms_eps;
+    g.w = l.w_qkv;
+    g.rows = qkv_out;
+    g.mode = 0;
+    g.out = qkv;
+    sd::launch_bgemv(g, dims->w_dtype, s);
+    sd::BatchKv kvs{};
+    for (int b = 0; b < batch; ++b) {
+      const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
+      kvs.pos[b] = pos[b];
+      kvs.k_full[b] = c.k_full;
+      kvs.v_full[b] = c.v_full;
+      kvs.k_sel[b] = c.k_sel;
+      kvs.v_sel[b] = c.k_sel ? c.v_sel : nullptr;
+      kvs.cap_full[b] = c.cap_full;
+      kvs.row_full[b] = c.n_full;
+      kvs.cap_sel[b] = c.cap_sel;
+      kvs.row_sel[b] = c.n_sel;
+    }
+    sd::launch_brope_append(qkv, batch, qkv_out, hq, hkv, dh, dims->rope_theta, kvs, q,
+                            dims->kv_dtype, s);
+    // attention: each sequence over its own cache (full or gathered)
+    for (int b = 0; b < batch; ++b) {
+      const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
+      const void* kc = kv_sparse ? c.k_sel : c.k_full;
+      const void* vc = kv_sparse ? c.v_sel : c.v_full;
+      const int cap = kv_sparse ? c.cap_sel : c.cap_full;
+      const int n_ctx = (kv_sparse ? c.n_sel : c.n_full) + 1;
+      enqueue_attn(*dims, B.base, wsb, q + (size_t)b * hq * dh, kc, vc, cap, n_ctx, n_ctx, 0,
+                   scale, auto_splits(n_ctx, hkv), P_SPLITK, attn + (size_t)b * hq * dh, nullptr,
+                   s);
+    }
+    // O with the residual, for every sequence from one read of W_o
+    g = sd::BgemvArgs{};
+    g.kind = sd::K_BATCH_O;
+    g.x = attn;
+    g.nb = batch;
+    g.d_in = hq * dh;
+    g.w = l.w_o;
+    g.rows = d;
+    g.mode = 1;
+    g.out = hidden;
+    sd::launch_bgemv(g, dims->w_dtype, s);
+    // CATS gate per sequence, the union, the union's up rows
+    uint8_t* uni = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + B.uni);
+    float* hmid = reinterpret_cast<float*>(wsb + B.hmid);
+    g = sd::BgemvArgs{};
+    g.kind = sd::K_BATCH_GATE_UP;
+    g.x = hidden;
+    g.nb = batch;
+    g.d_in = d;
+    g.norm = l.mlp_norm;
+    g.eps = dims->rms_eps;
+    g.w = l.w_gate;
+    g.rows = ff;
+    g.mode = 2;
+    g.w_up = l.w_up;
+    g.t = mlp_sparse ? l.cats_threshold : -1.0f;
+    g.act = reinterpret_cast<float*>(wsb + B.act);
+    g.keep = reinterpret_cast<uint8_t*>(wsb + B.keep);
+    g.uni = uni;
+    g.hmid = hmid;
+    sd::launch_bgemv(g, dims->w_dtype, s);
+    // down over the union for every sequence, then h_b += y_b
+    sd::DownArgs da{};
+    da.w_down_t = l.w_down_t;
+    da.d = d;
+    da.dff = ff;
+    da.keep = uni;
+    da.hmid = hmid;
+    da.partials = reinterpret_cast<float*>(wsb + B.part);
+    da.y = hidden;
+    da.accumulate = 1;
+    da.nb = batch;
+    sd::launch_down(da, dims->w_dtype, s);
+  }
+  st = check_launch("sd_decode_step_batch");
+  if (st) return st;
+  for (int b = 0; b < batch; ++b)
+    for (int i = 0; i < n_layers; ++i) {
+      sd_seq_kv& c = kv[(size_t)b * n_layers + i];
+      c.n_full += 1;
+      if (c.k_sel) c.n_sel += 1;
+    }
+  return SD_OK;
+}
+
 size_t sd_calibrate_workspace_bytes(const sd_dims* dims, int32_t n_states) {
   if (check_dims(dims) != SD_OK || n_states < 1) return 0;
   const Layout L = make_layout(*dims, 0, 0);

@@ -26,6 +26,12 @@
 // writes y (or y += result): deterministic, and the launch boundary makes the
 // partials visible to every XCD, which on MI355X costs less than a hand-off
 // inside one launch.
+//
+// Batches: with nb sequences sharing the weight reads ("Where Activation
+// Sparsity and KV-Cache Sparsity Cross in LLM Decoding", §3.2 "Dispatch and
+// batching") the keep bytes are the union of the batch's masks, hmid is
+// [nb, d_ff] (zero where a sequence dropped a channel the union keeps), each
+// row read once serves all nb sequences, and the partials are [P, nb, d].
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -44,12 +50,13 @@ __device__ __forceinline__ uint32_t nz_bits(uint32_t w) {
   return ((hi >> 7) & 1u) | ((hi >> 14) & 2u) | ((hi >> 21) & 4u) | ((hi >> 28) & 8u);
 }
 
-template <typename WT>
+template <typename WT, int NB>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(
     const WT* __restrict__ Wd, int d, int dff, int chunk, const uint8_t* __restrict__ keep,
-    const float* __restrict__ hmid, float* __restrict__ partials, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ n_kept_out) {
-  constexpr int U = 64 / (int)sizeof(WT);  // rows per batch (32 for bf16, 16 for fp32)
+    const float* __restrict__ hmid, int nb, float* __restrict__ partials,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ n_kept_out) {
+  // rows per batch: 32 for bf16, 16 for fp32, halved for four or more sequences
+  constexpr int U = 64 / (int)sizeof(WT) / (NB >= 4 ? 2 : 1);
   __shared__ int list[kDownList];
   __shared__ int wave_tot[kDownWaves];
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -115,15 +122,20 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   if (m == 0) {  // wave-uniform: an empty slice still writes its zero partial
     for (int c8 = wave * kWave + lane; c8 < d8; c8 += kDownWaves * kWave) {
       const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      store8(partials + (size_t)blockIdx.x * d + 8 * c8, z);
+      for (int b = 0; b < nb; ++b) store8(partials + ((size_t)blockIdx.x * nb + b) * d + 8 * c8, z);
     }
     return;
   }
-  const float hv = lane < m ? hmid[list[lane]] : 0.f;
-  for (int c8 = wave * kWave + lane; c8 < d8; c8 += kDownWaves * kWave) {
-    float acc[8];
+  float hv[NB];  // hmid of list entry `lane`, per sequence
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int b = 0; b < NB; ++b)
+    hv[b] = lane < m && b < nb ? hmid[(size_t)b * dff + list[lane]] : 0.f;
+  for (int c8 = wave * kWave + lane; c8 < d8; c8 += kDownWaves * kWave) {
+    float acc[NB][8];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
 #pragma unroll 1
     for (int j0 = 0; j0 < m; j0 += U) {
       Vec8<WT> g[U];
@@ -134,16 +146,22 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), j0 + u));
-        const float h = j0 + u < m ? hj : 0.f;
         float f[8];
         g[u].to_float(f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(h, f[e], acc[e]);
+        for (int b = 0; b < NB; ++b) {
+          const float hj =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv[b]), j0 + u));
+          const float h = j0 + u < m ? hj : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(h, f[e], acc[b][e]);
+        }
       }
     }
-    // 3. this workgroup's partial sum
-    store8(partials + (size_t)blockIdx.x * d + 8 * c8, acc);
+    // 3. this workgroup's partial sums
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < nb) store8(partials + ((size_t)blockIdx.x * nb + b) * d + 8 * c8, acc[b]);
   }
 }
 
@@ -184,10 +202,20 @@ static void down_typed(const DownArgs& a, hipStream_t s) {
   const int P = down_parts(a.dff);
   int chunk = (a.dff + kDownThreads - 1) / kDownThreads;
   chunk = (chunk + 15) / 16 * 16;
-  launch_kernel(K_DOWN, down_kernel<WT>, dim3(P), dim3(kDownThreads), 0, s, (const WT*)a.w_down_t,
-                a.d, a.dff, chunk, a.keep, a.hmid, a.partials, a.idx_out, a.n_kept_out);
-  launch_kernel(K_MLP_REDUCE, mlp_reduce_kernel, dim3((a.d + kRedCols - 1) / kRedCols),
-                dim3(kRedCols * kRedSlices), 0, s, (const float*)a.partials, a.d, P, a.y,
+  const int nb = a.nb > 1 ? a.nb : 1;
+#define SD_DOWN(NBV)                                                                        \
+  launch_kernel(K_DOWN, down_kernel<WT, NBV>, dim3(P), dim3(kDownThreads), 0, s,            \
+                (const WT*)a.w_down_t, a.d, a.dff, chunk, a.keep, a.hmid, nb, a.partials,   \
+                a.idx_out, a.n_kept_out)
+  if (nb == 1) SD_DOWN(1);
+  else if (nb == 2) SD_DOWN(2);
+  else if (nb <= 4) SD_DOWN(4);
+  else SD_DOWN(8);
+#undef SD_DOWN
+  // the partials [P, nb, d] are [P, nb d]: one reduce over nb d columns
+  const int cols = nb * a.d;
+  launch_kernel(K_MLP_REDUCE, mlp_reduce_kernel, dim3((cols + kRedCols - 1) / kRedCols),
+                dim3(kRedCols * kRedSlices), 0, s, (const float*)a.partials, cols, P, a.y,
                 a.accumulate);
 }
 

@@ -15,7 +15,7 @@ enum KernelKind {
   K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_MLP_REDUCE, K_SEL_LSE,
   K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_MASKED_SCORES,
   K_MASKED_SOFTMAX, K_MASKED_PV, K_TEAL_QKV, K_TEAL_QKV_REDUCE, K_TEAL_O, K_TEAL_GATE_UP,
-  K_TEAL_DOWN, K_TEAL_REDUCE, K_COUNT
+  K_TEAL_DOWN, K_TEAL_REDUCE, K_BATCH_QKV, K_BATCH_ROPE, K_BATCH_O, K_BATCH_GATE_UP, K_COUNT
 };
 
 // Start/stop events of one launch of kind `kind` while profiling is on (both
@@ -97,6 +97,7 @@ struct DownArgs {
   int accumulate;      // y += result instead of y = result
   int32_t* idx_out;    // optional ascending kept list
   int32_t* n_kept_out; // optional
+  int nb;              // sequences sharing the rows (0 or 1: one); hmid [nb, dff], y [nb, d]
 };
 
 // TEAL projection: y = sum over kept inputs j (|x_j| > t, after the optional
@@ -163,6 +164,43 @@ struct SelectArgs {
   HeadInts k_heads;
   int idx_stride;
 };
+
+// Batched decode (nb sequences sharing the weight reads): the sequences'
+// positions and caches, passed by value.
+constexpr int kMaxBatch = 8;
+struct BatchKv {
+  int pos[kMaxBatch];
+  void* k_full[kMaxBatch];
+  void* v_full[kMaxBatch];
+  void* k_sel[kMaxBatch];   // nullptr: no gathered buffer
+  void* v_sel[kMaxBatch];
+  int cap_full[kMaxBatch], row_full[kMaxBatch], cap_sel[kMaxBatch], row_sel[kMaxBatch];
+};
+
+// Batched GEMV y[b] = W x_b, W [rows, d_in] row-major, x [nb, d_in]
+// (d_in <= 4096, a multiple of 8); mode 0 store out [nb, rows], 1 out +=,
+// 2 the CATS gate with the up rows of the union (act, keep, hmid [nb, rows],
+// uni [rows]).
+struct BgemvArgs {
+  int kind;
+  const float* x;
+  int nb, d_in;
+  const float* norm;  // nullptr: x as is
+  float eps;
+  const void* w;
+  int rows, mode;
+  float* out;
+  const void* w_up;
+  float t;
+  float* act;
+  uint8_t* keep;
+  uint8_t* uni;
+  float* hmid;
+};
+void launch_bgemv(const BgemvArgs& a, int w_dtype, hipStream_t s);
+void launch_brope_append(const float* qkv, int nb, int qkv_out, int h_q, int h_kv, int dh,
+                         float theta, const BatchKv& kvs, float* q, int kv_dtype, hipStream_t s);
+int cu_count_dev();
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s);
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,

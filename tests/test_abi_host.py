@@ -34,6 +34,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
     assert ctypes.sizeof(sd.sd_layer) == 192
     assert ctypes.sizeof(sd.sd_byte_record) == 80
+    assert ctypes.sizeof(sd.sd_seq_kv) == 48
 
 
 def test_struct_layout_matches_the_c_compiler(tmp_path):
@@ -42,7 +43,8 @@ def test_struct_layout_matches_the_c_compiler(tmp_path):
     import subprocess
     if not shutil.which("gcc"):
         pytest.skip("no C compiler")
-    structs = {"sd_dims": sd.sd_dims, "sd_layer": sd.sd_layer, "sd_byte_record": sd.sd_byte_record}
+    structs = {"sd_dims": sd.sd_dims, "sd_layer": sd.sd_layer, "sd_byte_record": sd.sd_byte_record,
+               "sd_seq_kv": sd.sd_seq_kv}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "sd.h"', "int main(void) {"]
     for name, cls in structs.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
@@ -309,3 +311,35 @@ def test_decode_step_ragged_checks_every_head_and_advances_each():
         sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_KV_WINDOW, ws, 0)
     assert e.value.status == sd.SD_EINVAL
     assert list(heads) == [5, 6, 7, 8, 9, 10, 11, 12] and l.n_full == 10
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(batch=1), sd.SD_EINVAL),
+    (dict(batch=9), sd.SD_EINVAL),
+    (dict(mode=sd.SD_KV_WINDOW), sd.SD_EINVAL),
+    (dict(mode=sd.SD_PROJ_TEAL), sd.SD_EINVAL),
+    (dict(ws_bytes=64), sd.SD_ENOSPC),
+    (dict(full=True), sd.SD_ENOSPC),
+    (dict(no_sel=True, mode=sd.SD_KV_SPARSE), sd.SD_EINVAL),
+    (dict(dims=dict(d_model=8192)), sd.SD_EUNSUPPORTED),
+])
+def test_decode_step_batch_rejects_before_launch(case, status):
+    batch = case.get("batch", 4)
+    layers = (sd.sd_layer * 1)(sd.sd_layer(*([FAKE] * 7), 0.1, 0))
+    kv = (sd.sd_seq_kv * batch)(*[sd.sd_seq_kv(FAKE, FAKE, 64, 10, None if case.get("no_sel") else FAKE,
+                                              None if case.get("no_sel") else FAKE, 32, 5)
+                                  for _ in range(batch)])
+    if case.get("full"):
+        kv[2].n_full = 64
+    dims = _dims(**case.get("dims", {}))
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step_batch(dims, layers, kv, [10] * batch, FAKE, case.get("mode", 0),
+                                _FakeWs(case.get("ws_bytes", 1 << 32)), 0)
+    assert e.value.status == status
+    assert all(k.n_full in (10, 64) and k.n_sel == 5 for k in kv)
+
+
+def test_batch_workspace_grows_with_batch():
+    a = sd.sd_batch_workspace_bytes(_dims(), 2)
+    b = sd.sd_batch_workspace_bytes(_dims(), 8)
+    assert 0 < a < b and sd.sd_batch_workspace_bytes(_dims(), 1) == 0

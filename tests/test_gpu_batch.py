@@ -1,0 +1,191 @@
+"""GPU parity of sd_decode_step_batch (B sequences sharing every weight read,
+union channel masks; "Where Activation Sparsity and KV-Cache Sparsity Cross
+in LLM Decoding", §3.2 "Dispatch and batching", §4.4 "Batching") against the
+float64 batch oracle: every sequence's new hidden state, the union mask bit
+for bit, and the appended cache rows."""
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import batch as obatch, selection as osel, step as ostep
+
+pytestmark = pytest.mark.gpu
+
+sd = pytest.importorskip("kv_cache_activation_amd")
+from gpu_helpers import (DEV, TOL, dims_for, midpoint_threshold, rel_l2, to_dev,  # noqa: E402
+                         to_host)
+
+MODES = {"dense": 0, "kv": sd.SD_KV_SPARSE, "cats": sd.SD_MLP_SPARSE,
+         "both": sd.SD_KV_SPARSE | sd.SD_MLP_SPARSE}
+
+
+class BatchStack:
+    """B sequences over shared layer weights: each sequence has its own caches
+    (its own context length) and its own gathered buffer from the oracle's
+    selection."""
+
+    def __init__(self, wl, n_layers, batch, n, keep_ratio, extra=8):
+        self.wl, self.B, self.L = wl, batch, n_layers
+        self.dims = dims_for(wl)
+        self.odims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                          head_dim=wl.head_dim, kv_dtype=wl.dtype, eps=1e-5, theta=500000.0)
+        self.keep_alive = []
+        W = [synth.layer_weights(wl, li) for li in range(n_layers)]
+        layers = []
+        for li in range(n_layers):
+            dW = {k: to_dev(v, "f32" if "norm" in k else wl.dtype) for k, v in W[li].items()}
+            mask = torch.zeros(wl.d_ff, dtype=torch.uint8, device=DEV)
+            self.keep_alive.append((dW, mask))
+            layers.append(sd.sd_layer(dW["attn_norm"].data_ptr(), dW["w_qkv"].data_ptr(),
+                                      dW["w_o"].data_ptr(), dW["mlp_norm"].data_ptr(),
+                                      dW["w_gate"].data_ptr(), dW["w_up"].data_ptr(),
+                                      dW["w_down_t"].data_ptr(), -1.0, 0, None, None, 0, 0,
+                                      None, None, 0, 0, mask.data_ptr()))
+        self.layers = (sd.sd_layer * n_layers)(*layers)
+        self.n = [n - 3 * b for b in range(batch)]       # a different length per sequence
+        self.seq, kvs, self.dev_kv = [], [], []
+        for b in range(batch):
+            nb = self.n[b]
+            cap = nb + extra
+            k_keep = max(wl.n_sink + wl.window, int(keep_ratio * nb))
+            seq = []
+            for li in range(n_layers):
+                seed = li + 100 * (b + 1)
+                k, v = synth.kv_cache(wl, seed, nb, cap)
+                qw = synth.window_queries(wl, seed)
+                s32 = osel.window_scores(qw, k, nb, 1 / np.sqrt(wl.head_dim)).astype(np.float32)
+                idx = osel.select_indices(s32, nb, wl.window, wl.n_sink, k_keep)
+                ke = idx.shape[1]
+                ks = np.zeros((wl.n_kv_heads, ke + extra, wl.head_dim), np.float32)
+                vs = np.zeros_like(ks)
+                ks[:, :ke] = osel.gather(k, idx)
+                vs[:, :ke] = osel.gather(v, idx)
+                w = W[li]
+                seq.append(ostep.Layer(w["attn_norm"], w["w_qkv"], w["w_o"], w["mlp_norm"],
+                                       w["w_gate"], w["w_up"], w["w_down_t"], -1.0, k, v, nb,
+                                       ks, vs, ke))
+                dk, dv, dks, dvs = (to_dev(a, wl.dtype) for a in (k, v, ks, vs))
+                self.dev_kv.append((dk, dv, dks, dvs))
+                kvs.append(sd.sd_seq_kv(dk.data_ptr(), dv.data_ptr(), cap, nb, dks.data_ptr(),
+                                        dvs.data_ptr(), ke + extra, ke))
+            self.seq.append(seq)
+        self.kv = (sd.sd_seq_kv * (batch * n_layers))(*kvs)
+        self.ws = torch.empty(sd.sd_batch_workspace_bytes(self.dims, batch), dtype=torch.uint8,
+                              device=DEV)
+
+    def thresholds(self, hs, pos, sparsity, kv_sparse):
+        """Per layer one midpoint threshold over all sequences' gate
+        activations (each layer's inputs follow the earlier layers' masks)."""
+        work = copy.deepcopy(self.seq)
+        hh = [np.asarray(h, np.float64) for h in hs]
+        ts = []
+        for li in range(self.L):
+            acts = []
+            for b in range(self.B):
+                tr = []
+                ostep.decode_layer(copy.deepcopy(work[b][li]), hh[b], pos[b], kv_sparse=kv_sparse,
+                                   mlp_sparse=False, trace=tr, **self.odims)
+                acts.append(tr[0]["act"])
+            t = midpoint_threshold(np.concatenate(acts), sparsity)
+            for b in range(self.B):
+                work[b][li].threshold = t
+                hh[b] = ostep.decode_layer(work[b][li], hh[b], pos[b], kv_sparse=kv_sparse,
+                                           mlp_sparse=True, **self.odims)
+            ts.append(t)
+        return ts
+
+    def step(self, hs, pos, mode, sparsity=0.5):
+        kv_sparse = bool(MODES[mode] & sd.SD_KV_SPARSE)
+        mlp_sparse = bool(MODES[mode] & sd.SD_MLP_SPARSE)
+        if mlp_sparse:
+            for li, t in enumerate(self.thresholds(hs, pos, sparsity, kv_sparse)):
+                self.layers[li].cats_threshold = t
+                for b in range(self.B):
+                    self.seq[b][li].threshold = t
+        tr = []
+        want, unions = obatch.decode_step_batch(self.seq, hs, pos, kv_sparse=kv_sparse,
+                                                mlp_sparse=mlp_sparse, trace=tr, **self.odims)
+        hd = to_dev(np.stack(hs))
+        sd.sd_decode_step_batch(self.dims, self.layers, self.kv, pos, hd, MODES[mode], self.ws)
+        torch.cuda.synchronize()
+        got_unions = [m.cpu().numpy().astype(bool) for _, m in self.keep_alive]
+        return to_host(hd), want, unions, got_unions
+
+
+def _check_appends(st, tol):
+    for b in range(st.B):
+        for li in range(st.L):
+            ol = st.seq[b][li]
+            kv = st.kv[b * st.L + li]
+            assert kv.n_full == ol.n and kv.n_sel == ol.n_sel
+            dk, dv, dks, dvs = st.dev_kv[b * st.L + li]
+            assert rel_l2(to_host(dk)[:, ol.n - 1], ol.k_full[:, ol.n - 1]) <= tol
+            assert rel_l2(to_host(dvs)[:, ol.n_sel - 1], ol.v_sel[:, ol.n_sel - 1]) <= tol
+
+
+@pytest.mark.parametrize("batch", [2, 3, 4, 8])
+def test_tiny_fp32_batch_modes_over_steps(batch):
+    wl = synth.TINY
+    st = BatchStack(wl, 2, batch, 600, 0.25, extra=8)
+    hs = [synth.hidden(wl, 10 + b).astype(np.float64) for b in range(batch)]
+    pos = list(st.n)
+    for mode in ("dense", "both", "kv", "cats"):
+        got, want, unions, gu = st.step(hs, pos, mode)
+        for b in range(batch):
+            assert rel_l2(got[b], want[b]) <= TOL["f32"], (mode, b)
+        if MODES[mode] & sd.SD_MLP_SPARSE:
+            for li in range(st.L):
+                assert np.array_equal(gu[li], unions[li]), (mode, li)
+        else:
+            assert all(u.all() for u in gu)
+        hs = [w for w in want]
+        pos = [p + 1 for p in pos]
+    _check_appends(st, TOL["f32"])
+
+
+def test_8b_bf16_batch_of_four_both():
+    wl = synth.L8B_DENSE_8K
+    st = BatchStack(wl, 1, 4, 2048, 0.16)
+    hs = [synth.hidden(wl, 20 + b) for b in range(4)]
+    got, want, unions, gu = st.step(hs, list(st.n), "both")
+    for b in range(4):
+        assert rel_l2(got[b], want[b]) <= TOL["bf16"], b
+    assert np.array_equal(gu[0], unions[0])
+    # four independent-looking masks at 50% sparsity: the union is near 1 - 0.5^4
+    u = gu[0].mean()
+    assert 0.85 < u < 0.99, u
+    _check_appends(st, TOL["bf16"])
+
+
+def test_batch_matches_single_sequence_steps():
+    # the batched kernels against the single-sequence path on the same inputs
+    wl = synth.TINY
+    st = BatchStack(wl, 1, 3, 500, 0.3)
+    hs = [synth.hidden(wl, 30 + b) for b in range(3)]
+    single = []
+    for b in range(3):
+        one = copy.deepcopy(st.seq[b])
+        single.append(ostep.decode_step(one, hs[b], st.n[b], kv_sparse=True, mlp_sparse=False,
+                                        **st.odims))
+    got, want, _, _ = st.step(hs, list(st.n), "kv")
+    for b in range(3):
+        assert rel_l2(got[b], single[b]) <= TOL["f32"]
+        assert np.array_equal(want[b], single[b])
+
+
+def test_batch_rejections_leave_state_untouched():
+    wl = synth.TINY
+    st = BatchStack(wl, 1, 2, 300, 0.3)
+    hd = to_dev(np.stack([synth.hidden(wl, 0), synth.hidden(wl, 1)]))
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step_batch(st.dims, st.layers, st.kv, st.n, hd, sd.SD_KV_WINDOW, st.ws)
+    assert e.value.status == sd.SD_EINVAL
+    small = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step_batch(st.dims, st.layers, st.kv, st.n, hd, 0, small)
+    assert e.value.status == sd.SD_ENOSPC
+    assert st.kv[0].n_full == st.n[0] and st.kv[1].n_full == st.n[1]
