@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-baselines", action="store_true",
                     help="skip the window-vs-dense-attention-path comparison at the largest context")
+    ap.add_argument("--batches", type=str, default="4,8",
+                    help="batch sizes of the batched-decode leg (empty: skip it)")
+    ap.add_argument("--batch-contexts", type=str, default="8192,32768")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--out", type=str, default="")
     ap.add_argument("--pmc-copy-bytes", type=int, default=0,
@@ -381,6 +384,83 @@ class Bench:
         return dict(context=n, window_entries=win, sinks=wl.n_sink, paths=out,
                     window_speedup=speedup, window_byte_bound=round(rec.bound_kv, 3))
 
+    def batch_cells(self, n, B, modes):
+        """Batched decode ([Cross] §3.2 "Dispatch and batching", §4.4
+        "Batching"): B sequences of context n, each with its own synthetic
+        caches, selection and hidden state, stepped together so that every
+        weight row is read once per step.  Per mode: µs per step, tokens/s
+        (B per step), algorithmic GB/s (weights once, the union's up and down
+        rows under CATS, every sequence's cache rows), and the measured union
+        fraction u_B of the CATS masks."""
+        torch, sd, wl, args = self.torch, self.sd, self.wl, self.args
+        from synth import device as sdev
+        grow = args.warmup + args.steps + 2
+        cap, k_keep = n + grow + 64, int(math.floor(wl.keep_ratio * n))
+        cap_sel = k_keep + grow + 64
+        keep, kvs = [], []
+        # selection buffers sized for this context
+        scores = torch.empty(wl.n_kv_heads, n, device=self.dev)
+        idx = torch.empty(wl.n_kv_heads * n, dtype=torch.int32, device=self.dev)
+        sws = torch.empty(sd.sd_workspace_bytes(self.dims, cap, wl.window), dtype=torch.uint8,
+                          device=self.dev)
+        for b in range(B):
+            for li in range(self.L):
+                seed = li + 1000 * (b + 1)
+                k, v = sdev.kv_cache(wl, seed, n, cap, self.dev)
+                ks = torch.zeros(wl.n_kv_heads, cap_sel, wl.head_dim, dtype=torch.bfloat16,
+                                 device=self.dev)
+                vs = torch.zeros_like(ks)
+                sd.sd_select_kv(self.dims, k, v, cap, n, sdev.window_queries(wl, seed, self.dev),
+                                wl.window, wl.n_sink, k_keep, scores, idx, ks, vs, cap_sel, 0,
+                                sws)
+                keep.append((k, v, ks, vs))
+                kvs.append(sd.sd_seq_kv(k.data_ptr(), v.data_ptr(), cap, n, ks.data_ptr(),
+                                        vs.data_ptr(), cap_sel, k_keep))
+        kv = (sd.sd_seq_kv * (B * self.L))(*kvs)
+        h0 = torch.stack([sdev.hidden(wl, b, self.dev) for b in range(B)])
+        hid = h0.clone()
+        ws = torch.empty(sd.sd_batch_workspace_bytes(self.dims, B), dtype=torch.uint8,
+                         device=self.dev)
+        d, dh = wl.d_model, wl.head_dim
+        w_attn = 2 * (d * wl.qkv_out + wl.n_q_heads * dh * d)
+        row = 2 * wl.n_kv_heads * dh * 2
+        out = []
+        for mode in modes:
+            flags = self.mode_flags(mode)
+            for i, c in enumerate(kv):
+                c.n_full, c.n_sel = n, k_keep
+            hid.copy_(h0)
+            pos = [n] * B
+
+            def steps(count):
+                for _ in range(count):
+                    sd.sd_decode_step_batch(self.dims, self.layers, kv, pos, hid, flags, ws)
+                    for b in range(B):
+                        pos[b] += 1
+
+            steps(args.warmup)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            steps(args.steps)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            u = 1.0
+            if flags & sd.SD_MLP_SPARSE:
+                u = sum(float(m.float().mean()) for m in self.MASK) / self.L
+            base = k_keep if flags & sd.SD_KV_SPARSE else n
+            n_read = base + args.warmup + (args.steps - 1) / 2.0 + 1
+            b_step = self.L * (w_attn + 2 * d * wl.d_ff * (1 + 2 * u) + B * row * n_read)
+            out.append(dict(context=n, batch=B, mode=mode, us_per_step=ms * 1e3,
+                            tokens_per_s=B / (ms * 1e-3), bytes_per_step=b_step,
+                            gbs=b_step / ms / 1e6, hbm_frac=b_step / ms / 1e6 / HBM_PEAK_GBS,
+                            union_fraction=u if flags & sd.SD_MLP_SPARSE else None))
+        del keep, kv, ws, scores, idx, sws
+        torch.cuda.empty_cache()
+        return out
+
     def profile_cell(self, n, k_keep, mode):
         """Per-kernel event timing of the same steps (library profiler)."""
         torch, sd, args = self.torch, self.sd, self.args
@@ -631,6 +711,27 @@ def main():
                   flush=True)
         print(f"# window speedups {base['window_speedup']} (byte bound {base['window_byte_bound']})",
               flush=True)
+    batch = None
+    if args.batches:
+        cells = []
+        for n in [int(c) for c in args.batch_contexts.split(",") if c]:
+            for B in [int(b) for b in args.batches.split(",") if b]:
+                for c in bench.batch_cells(n, B, ("dense", "kv", "cats", "both")):
+                    cells.append(c)
+                    print(f"# batch {B} n={n:6d} {c['mode']:5s} {c['us_per_step']:9.1f} us/step "
+                          f"{c['tokens_per_s']:8.1f} tok/s {c['gbs']:7.1f} GB/s"
+                          + (f" u_B {c['union_fraction']:.4f}" if c["union_fraction"] else ""),
+                          flush=True)
+        union = {}
+        for B in sorted({c["batch"] for c in cells}):
+            us = [c["union_fraction"] for c in cells if c["batch"] == B and c["union_fraction"]]
+            u = sum(us) / len(us)
+            n_star = bench.sd.sd_byte_crossover_batch(bench.dims, B, u, bench.wl.keep_ratio, 2.0,
+                                                      2.0, bench.sd.SD_PROJ_CATS)
+            union[str(B)] = dict(measured=round(u, 4), independent=round(1 - 0.5 ** B, 4),
+                                 n_star_tokens=round(n_star, 1))
+        batch = dict(cells=[{k: (round(v, 4) if isinstance(v, float) else v)
+                             for k, v in c.items()} for c in cells], union=union)
     gate = latency_gate(sweep)
     for g in gate:
         print(f"# gate n={g['context']:6d} horizon {g['horizon']:5d}: {g['best']}", flush=True)
@@ -649,6 +750,7 @@ def main():
         copy_ceiling_gbs=round(copy_gbs, 1),
         attention_baselines=base,
         latency_gate=gate,
+        batch=batch,
         kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                  for k, e in kern.items()},
         sweep=[{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}

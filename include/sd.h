@@ -412,6 +412,17 @@ sd_status sd_byte_account(const sd_dims* dims, int32_t n_layers, double n, doubl
                           double fixed_bytes, sd_byte_record* out);
 
 /*
+ * sd_byte_crossover_batch -- the per-sequence crossover of a batch ([Cross]
+ * §3.2 "Dispatch and batching"): B sequences share each weight read and the
+ * union of their kept channels covers a fraction u_b of the projection set,
+ * so n_B* = P s_w (1 - u_b) / (2 B h_kv d_h s_kv (1 - r_kv)) tokens (infinite
+ * at r_kv = 1).  n_star [host] out.  Errors: EINVAL for out-of-range
+ * arguments.
+ */
+sd_status sd_byte_crossover_batch(const sd_dims* dims, int32_t batch, double u_b, double r_kv,
+                                  double s_w, double s_kv, int32_t proj_set, double* n_star);
+
+/*
  * sd_cats_calibrate -- per-layer CATS threshold from calibration states, the
  * percentile rule CATS uses ([SATS]): a = SiLU(w_gate RMSNorm(x) norm_w) for
  * each of the n_states rows of `states` [n_states, d]; with v the float32 |a|

@@ -33,7 +33,8 @@ SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_decode_attn",
            "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
-           "sd_decode_step", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account", "sd_calibrate_workspace_bytes",
+           "sd_decode_step", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account",
+           "sd_byte_crossover_batch", "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
 
@@ -282,6 +283,18 @@ def sd_byte_account(dims, n_layers, n, r_p, r_kv, s_w, s_kv, proj_set, fixed_byt
     _check(_lib.sd_byte_account(ctypes.byref(dims), n_layers, n, r_p, r_kv, s_w, s_kv, proj_set,
                                 fixed_bytes, ctypes.byref(rec)))
     return rec
+
+
+_lib.sd_byte_crossover_batch.restype = _I
+_lib.sd_byte_crossover_batch.argtypes = [ctypes.POINTER(sd_dims), _I, _D, _D, _D, _D, _I,
+                                         ctypes.POINTER(_D)]
+
+
+def sd_byte_crossover_batch(dims, batch, u_b, r_kv, s_w, s_kv, proj_set) -> float:
+    out = _D()
+    _check(_lib.sd_byte_crossover_batch(ctypes.byref(dims), batch, u_b, r_kv, s_w, s_kv, proj_set,
+                                        ctypes.byref(out)))
+    return out.value
 
 
 def sd_calibrate_workspace_bytes(dims, n_states) -> int:

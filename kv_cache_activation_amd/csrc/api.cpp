@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -735,7 +736,7 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
 // every sequence in stream order) plus the batch's own buffers.
 struct BatchLayout {
   Layout base;
-  size_t qkv, q, attn, act, hmid, keep, uni, part, total;
+  size_t qkv, q, attn, pm, pl, pacc, act, hmid, keep, uni, part, total;
 };
 
 BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
@@ -752,6 +753,9 @@ BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
   B.qkv = take(n * (hq + 2 * hkv) * dh * 4);
   B.q = take(n * hq * dh * 4);
   B.attn = take(n * hq * dh * 4);
+  B.pm = take(n * hq * kMaxSplits * 4);
+  B.pl = take(n * hq * kMaxSplits * 4);
+  B.pacc = take(n * hq * kMaxSplits * dh * 4);
   B.act = take(n * ff * 4);
   B.hmid = take(n * ff * 4);
   B.keep = take(n * ff);
@@ -759,6 +763,40 @@ BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
   B.part = take((size_t)sd::down_parts((int)ff) * n * d * 4);
   B.total = off;
   return B;
+}
+
+// Chunks of the batched attention: one chunk size c for every sequence, about
+// kSplitBlocks chunk workgroups over all (sequence, KV head) pairs and never
+// more (the measured cliff of the split-K kernel), at least kMinChunk rows,
+// at most kMaxSplits chunks per head; then each sequence's chunk is evened
+// out over its split count.
+void plan_batch_splits(const int* rows, int nb, int hkv, long long total, sd::AttnBatch& bt) {
+  long long c = (total + kSplitBlocks - 1) / kSplitBlocks;
+  if (c < kMinChunk) c = kMinChunk;
+  for (;;) {
+    long long blocks = 0;
+    for (int b = 0; b < nb; ++b) {
+      long long sp = (rows[b] + c - 1) / c;
+      if (sp > kMaxSplits) sp = kMaxSplits;
+      blocks += hkv * sp;
+    }
+    if (blocks <= kSplitBlocks) break;
+    c += c / 16 + 1;
+  }
+  int start = 0;
+  for (int b = 0; b < 8; ++b) {
+    if (b >= nb) {
+      bt.starts[b] = INT_MAX;
+      continue;
+    }
+    int sp = (int)((rows[b] + c - 1) / c);
+    if (sp > kMaxSplits) sp = kMaxSplits;
+    if (sp < 1) sp = 1;
+    bt.chunk[b] = (rows[b] + sp - 1) / sp;
+    bt.splits[b] = (rows[b] + bt.chunk[b] - 1) / bt.chunk[b];
+    bt.starts[b] = start;
+    start += hkv * bt.splits[b];
+  }
 }
 
 sd_status check_batch_dims(const sd_dims* dims, int32_t batch) {
@@ -851,16 +889,41 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
     }
     sd::launch_brope_append(qkv, batch, qkv_out, hq, hkv, dh, dims->rope_theta, kvs, q,
                             dims->kv_dtype, s);
-    // attention: each sequence over its own cache (full or gathered)
-    for (int b = 0; b < batch; ++b) {
-      const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
-      const void* kc = kv_sparse ? c.k_sel : c.k_full;
-      const void* vc = kv_sparse ? c.v_sel : c.v_full;
-      const int cap = kv_sparse ? c.cap_sel : c.cap_full;
-      const int n_ctx = (kv_sparse ? c.n_sel : c.n_full) + 1;
-      enqueue_attn(*dims, B.base, wsb, q + (size_t)b * hq * dh, kc, vc, cap, n_ctx, n_ctx, 0,
-                   scale, auto_splits(n_ctx, hkv), P_SPLITK, attn + (size_t)b * hq * dh, nullptr,
-                   s);
+    // attention: one launch over every sequence's own cache (full or
+    // gathered), chunks planned over all sequences' rows, then one merge
+    {
+      sd::AttnArgs a{};
+      a.q = q;
+      a.h_q = hq;
+      a.h_kv = hkv;
+      a.dh = dh;
+      a.scale = scale;
+      a.out = attn;
+      a.pm = reinterpret_cast<float*>(wsb + B.pm);
+      a.pl = reinterpret_cast<float*>(wsb + B.pl);
+      a.pacc = reinterpret_cast<float*>(wsb + B.pacc);
+      a.batched = batch;
+      long long total = 0;
+      int rows[sd::kMaxBatch];
+      for (int b = 0; b < batch; ++b) {
+        const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
+        a.bt.k[b] = kv_sparse ? c.k_sel : c.k_full;
+        a.bt.v[b] = kv_sparse ? c.v_sel : c.v_full;
+        a.bt.cap[b] = kv_sparse ? c.cap_sel : c.cap_full;
+        rows[b] = (kv_sparse ? c.n_sel : c.n_full) + 1;
+        a.bt.rows[b] = rows[b];
+        total += (long long)hkv * rows[b];
+      }
+      plan_batch_splits(rows, batch, hkv, total, a.bt);
+      a.n_splits = 0;
+      for (int b = 0; b < batch; ++b) a.n_splits = std::max(a.n_splits, a.bt.splits[b]);
+      a.n_ctx = rows[0];
+      a.chunk = a.bt.chunk[0];
+      a.cap = a.bt.cap[0];
+      a.k = a.bt.k[0];
+      a.v = a.bt.v[0];
+      a.sink = a.n_ctx;
+      sd::launch_attn(a, dims->kv_dtype, s);
     }
     // O with the residual, for every sequence from one read of W_o
     g = sd::BgemvArgs{};

@@ -48,8 +48,8 @@ template <typename KT, int DH, int G, int U>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
     int n_ctx, int sink, int shift, int kv_div, int ragged, HeadInts lens, HeadInts starts,
-    float scale_log2, int chunk, int n_splits, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ pacc) {
+    int batched, AttnBatch bt, int h_q, float scale_log2, int chunk, int n_splits,
+    float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ pacc) {
   constexpr int LPR = DH / 8;          // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
@@ -66,11 +66,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     for (int h = 1; h < kMaxKvHeads; ++h) kv += (int)(split >= starts.v[h]);
     split -= starts.v[kv];
   }
+  // batched: a flat grid over (sequence, KV head, chunk); each sequence reads
+  // its own cache with its own query rows and partial slots
+  int seq = 0, rows = ragged ? lens.v[(kv / kv_div) & (kMaxKvHeads - 1)] : n_ctx;
+  if (batched) {
+#pragma unroll
+    for (int b = 1; b < 8; ++b) seq += (int)(split >= bt.starts[b]);
+    const int local = split - bt.starts[seq];
+    kv = local / bt.splits[seq];
+    split = local - kv * bt.splits[seq];
+    K = (const KT*)bt.k[seq];
+    V = (const KT*)bt.v[seq];
+    cap = bt.cap[seq];
+    chunk = bt.chunk[seq];
+    rows = bt.rows[seq];
+    q += (size_t)seq * h_q * DH;
+  }
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int sub = lane % LPR;
   const int slot = wave * RPW + lane / LPR;
-  // rows of this KV head: n_ctx, or its own count under ragged budgets
-  const int rows = ragged ? lens.v[(kv / kv_div) & (kMaxKvHeads - 1)] : n_ctx;
   const int r0 = split * chunk;
   const int r1 = min(rows, r0 + chunk);
   // logical row j is physical row j, or j + shift from `sink` on (a window of
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       L = fmaf(sm_l[w][g], a, L);
       A = fmaf(sm_acc[w][g][c], a, A);
     }
-    const size_t hs = (size_t)(kv * G + g) * n_splits + split;
+    const size_t hs = ((size_t)seq * h_q + kv * G + g) * n_splits + split;
     pacc[hs * DH + c] = A;
     if (c == 0) {
       pm[hs] = M;
@@ -221,7 +235,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 // serves column t % kMergeCols for splits g, g + kMergeGroups, ... (g = t /
 // kMergeCols), at most CAP splits.  Loads come from clamped indices, so none
 // depends on a branch and all are in flight together; splits past the count
-// get weight zero.  Ragged lengths: query head h reads counts.v[h / G] splits.
+// get weight zero.  Ragged lengths: query head h reads counts.v[h / G] splits;
+// a batch: query head h of the flat [nb, h_q] list reads its sequence's count.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeCols = 32;
 constexpr int kMergeGroups = kMergeThreads / kMergeCols;
@@ -229,8 +244,8 @@ constexpr int kMergeGroups = kMergeThreads / kMergeCols;
 template <int DH, int CAP>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ pacc,
-    int stride, int ragged, HeadInts counts, int G, float* __restrict__ out,
-    float* __restrict__ lse) {
+    int stride, int ragged, HeadInts counts, int G, int batched, AttnBatch bt, int h_q,
+    float* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = CAP / kMergeGroups;  // splits per thread
   constexpr int NW = kMergeThreads / kWave;
   __shared__ float w_s[CAP];
@@ -238,7 +253,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
   __shared__ float share[kMergeGroups][kMergeCols];
   const int h = blockIdx.x, t = threadIdx.x;
   const int col = blockIdx.y * kMergeCols + t % kMergeCols, grp = t / kMergeCols;
-  const int ns = ragged ? counts.v[(h / G) & (kMaxKvHeads - 1)] : stride;
+  const int ns = batched  ? bt.splits[(h / h_q) & 7]
+                 : ragged ? counts.v[(h / G) & (kMaxKvHeads - 1)]
+                          : stride;
   const float* base = pacc + (size_t)h * stride * DH + col;
   float v[PER];
 #pragma unroll
@@ -300,12 +317,19 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
     }
     grid = dim3(total, 1);
   }
+  int nq = a.h_q;  // query heads the merge covers
+  if (a.batched) {
+    int total = 0;
+    for (int b = 0; b < a.batched; ++b) total += a.h_kv * a.bt.splits[b];
+    grid = dim3(total, 1);
+    nq = a.batched * a.h_q;
+  }
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
 #define SD_ATTN_G(GG, UU)                                                                   \
   launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU>, grid, dim3(kAttnThreads), 0, s, \
                 a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, starts,        \
-                scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
+                a.batched, a.bt, a.h_q, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
   switch (G) {
     case 1: SD_ATTN_G(1, 8); break;
     case 2: SD_ATTN_G(2, 8); break;
@@ -313,11 +337,12 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
     default: SD_ATTN_G(8, 4); break;
   }
 #undef SD_ATTN_G
-  const dim3 mgrid(a.h_q, DH / kMergeCols);
+  const dim3 mgrid(nq, DH / kMergeCols);
   const int G_all = a.h_q / a.h_kv;
 #define SD_MERGE(CAPV)                                                                        \
   launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, CAPV>, mgrid, dim3(kMergeThreads), 0, s, \
-                a.pm, a.pl, a.pacc, a.n_splits, a.ragged, counts, G_all, a.out, a.lse)
+                a.pm, a.pl, a.pacc, a.n_splits, a.ragged, counts, G_all, a.batched, a.bt, a.h_q, \
+                a.out, a.lse)
   if (a.n_splits <= 64) SD_MERGE(64);
   else if (a.n_splits <= 128) SD_MERGE(128);
   else SD_MERGE(kMaxSplits);

@@ -47,3 +47,25 @@ extern "C" sd_status sd_byte_account(const sd_dims* dims, int32_t n_layers, doub
                            : std::numeric_limits<double>::infinity();
   return SD_OK;
 }
+
+// Batched crossover ([Cross] §3.2, "Dispatch and batching"): B sequences share
+// each weight read, so the projection branch skips only the channels no
+// sequence keeps, a fraction 1 - u_b of its projection set, once per step,
+// while the KV branch still skips (1 - r_kv) of every sequence's cache.  Per
+// sequence the savings meet at n_B* = P s_w (1 - u_b) / (B 2 h_kv d_h s_kv (1 - r_kv)).
+extern "C" sd_status sd_byte_crossover_batch(const sd_dims* dims, int32_t batch, double u_b,
+                                             double r_kv, double s_w, double s_kv,
+                                             int32_t proj_set, double* n_star) {
+  if (!dims || !n_star || batch < 1 || !(u_b >= 0 && u_b <= 1) || !(r_kv >= 0 && r_kv <= 1) ||
+      !(s_w > 0) || !(s_kv > 0))
+    return SD_EINVAL;
+  sd_byte_record rec;
+  // the projection set's parameter count: the one-sequence skipped bytes at r_p = 0
+  const sd_status st = sd_byte_account(dims, 1, 0.0, 0.0, r_kv, s_w, s_kv, proj_set, 0.0, &rec);
+  if (st != SD_OK) return st;
+  const double sparse_bytes = rec.delta_p;  // P s_w
+  const double per_token_kv = 2.0 * dims->n_kv_heads * dims->head_dim * s_kv;
+  *n_star = r_kv < 1.0 ? sparse_bytes * (1.0 - u_b) / (batch * per_token_kv * (1.0 - r_kv))
+                       : std::numeric_limits<double>::infinity();
+  return SD_OK;
+}

@@ -127,6 +127,16 @@ struct TealArgs {
   uint8_t* keep_out;   // optional keep bytes [d_in]
 };
 
+// Batched attention: sequence s has its own cache (k[s], v[s], cap[s]) of
+// rows[s] valid rows per KV head, split into splits[s] chunks of chunk[s]
+// rows; a flat grid where sequence s owns blocks [starts[s], starts[s+1])
+// (entries past the last sequence hold INT_MAX).
+struct AttnBatch {
+  const void* k[8];
+  const void* v[8];
+  int cap[8], rows[8], chunk[8], splits[8], starts[8];
+};
+
 struct AttnArgs {
   const float* q;
   const void* k;
@@ -136,6 +146,8 @@ struct AttnArgs {
   int per_query_head;   // one workgroup per query head (no K/V sharing across a group)
   int ragged;           // KV head kv has lens.v[kv] rows (n_ctx is their maximum)
   HeadInts lens;
+  int batched;          // > 0: that many sequences, described by bt (q, out: [nb, h_q, d_h])
+  AttnBatch bt;
   float scale;
   int n_splits, chunk;
   float* pm;

@@ -176,6 +176,17 @@ def test_byte_account_matches_oracle(proj, code, n, r_p, r_kv, s_w, lm):
         assert (math.isinf(a) and math.isinf(b)) or abs(a - b) <= 1e-12 * abs(b), (f, a, b)
 
 
+@pytest.mark.parametrize("proj,code", [("all7", sd.SD_PROJ_ALL7), ("cats", sd.SD_PROJ_CATS)])
+@pytest.mark.parametrize("batch,u_b,r_kv,s_w", [(4, 0.92, 0.3, 2), (8, 0.985, 0.1, 2),
+                                               (4, 0.9375, 0.2, 0.5), (1, 0.5, 0.3, 2)])
+def test_batched_crossover_matches_oracle(proj, code, batch, u_b, r_kv, s_w):
+    from oracle import byte_account as ba
+    want = ba.crossover_batched(ba.Dims(**DIMS8B), batch, u_b, r_kv, s_w, 2.0, proj)
+    got = sd.sd_byte_crossover_batch(_dims(), batch, u_b, r_kv, s_w, 2.0, code)
+    assert abs(got - want) <= 1e-12 * want
+    assert math.isinf(sd.sd_byte_crossover_batch(_dims(), batch, u_b, 1.0, s_w, 2.0, code))
+
+
 def test_byte_account_rejects_bad_ratio():
     with pytest.raises(sd.SdError):
         sd.sd_byte_account(_dims(), 32, 1024, 1.5, 0.3, 2, 2, sd.SD_PROJ_ALL7)
