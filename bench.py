@@ -465,7 +465,7 @@ class Bench:
         """Per-kernel event timing of the same steps (library profiler)."""
         torch, sd, args = self.torch, self.sd, self.args
         flags = self.mode_flags(mode)
-        self.reset(n, k_keep)
+        self.reset(n, k_keep, mode.startswith("catekv"))
         self.run_steps(n, flags, args.warmup)
         torch.cuda.synchronize()
         sd.sd_profile_start()

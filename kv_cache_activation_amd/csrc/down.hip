@@ -40,7 +40,7 @@ namespace sd {
 constexpr int kDownThreads = 512;
 constexpr int kDownWaves = kDownThreads / kWave;
 constexpr int kDownScanBytes = 64;  // keep bytes per thread: d_ff <= 64 * 512
-constexpr int kRedCols = 16;      // reduce: columns per workgroup
+constexpr int kRedCols = 32;      // reduce: columns per workgroup (128-byte pieces of a partial)
 constexpr int kRedSlices = 16;    // reduce: partition slices per column
 constexpr int kRedPer = kDownMaxParts / kRedSlices;  // partitions per slice, at most
 
@@ -167,6 +167,8 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
 
 // y[c] (+)= sum over partitions w of partials[w][c]: slice s of a column sums
 // partitions [s*per, s*per + per) in order, then the slices are added in order.
+// A workgroup's 32 columns make each partial read one 128-byte piece (16
+// columns read half lines, which HBM counters show as twice the bytes).
 __global__ __launch_bounds__(kRedCols * kRedSlices) void mlp_reduce_kernel(
     const float* __restrict__ partials, int d, int P, float* __restrict__ y, int accumulate) {
   __shared__ float red[kRedSlices][kRedCols];
