@@ -147,18 +147,33 @@ def test_tiny_fp32_batch_modes_over_steps(batch):
     _check_appends(st, TOL["f32"])
 
 
-def test_8b_bf16_batch_of_four_both():
+@pytest.mark.parametrize("batch", [2, 4, 8])
+def test_8b_bf16_batch_both(batch):
     wl = synth.L8B_DENSE_8K
-    st = BatchStack(wl, 1, 4, 2048, 0.16)
-    hs = [synth.hidden(wl, 20 + b) for b in range(4)]
+    st = BatchStack(wl, 1, batch, 2048, 0.16)
+    hs = [synth.hidden(wl, 20 + b) for b in range(batch)]
     got, want, unions, gu = st.step(hs, list(st.n), "both")
-    for b in range(4):
+    for b in range(batch):
         assert rel_l2(got[b], want[b]) <= TOL["bf16"], b
     assert np.array_equal(gu[0], unions[0])
-    # four independent-looking masks at 50% sparsity: the union is near 1 - 0.5^4
+    # independent-looking masks at 50% sparsity: the union is near 1 - 0.5^B
     u = gu[0].mean()
-    assert 0.85 < u < 0.99, u
+    assert abs(u - (1 - 0.5 ** batch)) < 0.03, u
     _check_appends(st, TOL["bf16"])
+
+
+def test_8b_bf16_batch_dense_two_layers_over_steps():
+    wl = synth.L8B_DENSE_8K
+    st = BatchStack(wl, 2, 3, 1024, 0.2)
+    hs = [synth.hidden(wl, 40 + b) for b in range(3)]
+    pos = list(st.n)
+    for mode in ("dense", "kv"):
+        got, want, _, gu = st.step(hs, pos, mode)
+        for b in range(3):
+            assert rel_l2(got[b], want[b]) <= TOL["bf16"], (mode, b)
+        assert all(u.all() for u in gu)
+        hs = [w for w in want]
+        pos = [p + 1 for p in pos]
 
 
 def test_batch_matches_single_sequence_steps():
