@@ -130,22 +130,45 @@ __global__ __launch_bounds__(kSelThreads) void sel_lse_partial_kernel(
   }
 }
 
-__global__ void sel_lse_final_kernel(const float* __restrict__ lse_part, int n_chunks, int G,
-                                     int w, int h_kv, float* __restrict__ lse) {
+// One wave per window query: lane l merges chunks l, l + 64, ... (all of its
+// loads issued together), then a wave max and a wave sum in a fixed order.
+constexpr int kLsePer = 32;  // chunks per lane in one pass (n_chunks <= 64 * 32 per pass)
+__global__ __launch_bounds__(256) void sel_lse_final_kernel(const float* __restrict__ lse_part,
+                                                            int n_chunks, int G, int w, int h_kv,
+                                                            float* __restrict__ lse) {
   const int Q = G * w;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= h_kv * Q) return;
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;  // query of the wave
+  if (t >= h_kv * Q) return;  // wave-uniform
+  const int lane = lane_id();
   const int kv = t / Q, qi = t - kv * Q;
-  const float* p = lse_part + ((size_t)kv * n_chunks * Q + qi) * 2;
-  float M = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[(size_t)c * Q * 2]);
-  float L = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const float m = p[(size_t)c * Q * 2];
-    if (m != -INFINITY) L = fmaf(p[(size_t)c * Q * 2 + 1], exp2f(m - M), L);
+  const float2* p = reinterpret_cast<const float2*>(lse_part) + (size_t)kv * n_chunks * Q + qi;
+  float M = -INFINITY, L = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += kWave * kLsePer) {
+    float2 v[kLsePer];
+#pragma unroll
+    for (int u = 0; u < kLsePer; ++u) {
+      const int c = min(c0 + lane + kWave * u, n_chunks - 1);
+      v[u] = p[(size_t)c * Q];
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kLsePer; ++u)
+      if (c0 + lane + kWave * u < n_chunks) m = fmaxf(m, v[u].x);
+    const float mn = fmaxf(M, m);
+    float l = 0.f;
+#pragma unroll
+    for (int u = 0; u < kLsePer; ++u)
+      if (c0 + lane + kWave * u < n_chunks && v[u].x != -INFINITY)
+        l = fmaf(v[u].y, exp2f(v[u].x - mn), l);
+    L = (M == -INFINITY ? 0.f : L * exp2f(M - mn)) + l;
+    M = mn;
   }
-  const int g = qi / w, i = qi - g * w;
-  lse[(kv * G + g) * w + i] = M + log2f(L);
+  const float MW = wave_max(M);
+  const float LW = wave_sum(M == -INFINITY ? 0.f : L * exp2f(M - MW));
+  if (lane == 0) {
+    const int g = qi / w, i = qi - g * w;
+    lse[(kv * G + g) * w + i] = MW + log2f(LW);
+  }
 }
 
 template <typename KT, int DH>
@@ -185,6 +208,237 @@ __global__ __launch_bounds__(kSelThreads) void sel_score_kernel(
     }
   }
   if (have) scores[(size_t)kv * n + j] = s;
+}
+
+// ------------------------------------------------------------------ matrix cores
+// Scoring with bf16 caches on the matrix cores.  Per KV head the logits are a
+// product Z [G w, n] = Q_win [G w, d_h] K^T [d_h, n] with d_h-long dot
+// products: about 2 G w flops per cache byte, a dense contraction, so
+// v_mfma_f32_16x16x32_bf16 computes them.  The window queries are float32:
+// each is split into three bf16 parts (hi + mid + lo carries its 24-bit
+// significand), the bf16 keys are exact, every product is exact in float32 and
+// the sums accumulate in float32, so the logits have float32 accuracy, as on
+// the vector ALUs.  Operand layout (lane l): A = queries, row l % 16, dims
+// 8 (l / 16) + e of each 32-dim step; B = keys, column l % 16 (one key row,
+// 16 contiguous bytes per lane and step); result rows 4 (l / 16) + r, column
+// l % 16.
+//   A workgroup (four waves) takes a chunk of 256 keys of one KV head, each
+//   wave 64 of them (four 16-key tiles) held in registers; the queries go
+//   through LDS in batches of 64 (four 16-query tiles).  lse pass: each query's (max, sum of 2^z) over the wave's visible
+//   keys (DPP over the 16 lanes of a result row), then over the four waves in
+//   LDS -> the chunk partial, as the vector-ALU kernel writes it.  score pass:
+//   each key's sum over the queries of 2^(z - lse), lanes of one column added
+//   with lane swaps, accumulated over the query tiles in a fixed order.
+typedef __attribute__((ext_vector_type(8))) __bf16 sel_bf16x8;
+constexpr int kSelQB = 64;  // queries staged per batch (four 16-row tiles)
+constexpr int kSelSub = 1;  // key chunks per workgroup (measured: staging once for 2 or 4
+                            // chunks, or batches of 128 queries, were no faster)
+
+__device__ __forceinline__ sel_bf16x8 sel_as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(sel_bf16x8, v);
+}
+
+// Eight float32 values as three bf16 parts (hi + mid + lo == x to 24 bits).
+__device__ __forceinline__ void sel_split3(const float (&x)[8], u32x4& hi, u32x4& mid,
+                                           u32x4& lo) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t hh[2], mm[2], ll[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v = x[2 * p + e];
+      const bf16_t bh = f32_to_bf16(v);
+      const float r1 = v - bf16_lo((uint32_t)bh);
+      const bf16_t bm = f32_to_bf16(r1);
+      hh[e] = bh;
+      mm[e] = bm;
+      ll[e] = f32_to_bf16(r1 - bf16_lo((uint32_t)bm));
+    }
+    h[p] = hh[0] | (hh[1] << 16);
+    m[p] = mm[0] | (mm[1] << 16);
+    l[p] = ll[0] | (ll[1] << 16);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  mid = u32x4{m[0], m[1], m[2], m[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
+// Logits of one 16-query tile (rows of qs starting at qrow) against the
+// wave's four 16-key tiles: z[c][r] for query 4 (l / 16) + r of the tile and
+// key column l % 16 of key tile c.
+template <int DH>
+__device__ __forceinline__ void sel_tile_logits(const float* qs, int qrow,
+                                                const u32x4 (&kf)[4][DH / 32], f32x4 (&z)[4]) {
+  constexpr int NS = DH / 32;
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    float xv[8];
+    load8f(qs + (qrow + lane % 16) * (DH + 4) + 32 * st + 8 * (lane / 16), xv);
+    u32x4 ah, am, al;
+    sel_split3(xv, ah, am, al);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(ah), sel_as_bf16x8(kf[c][st]),
+                                                     z[c], 0, 0, 0);
+      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(am), sel_as_bf16x8(kf[c][st]),
+                                                     z[c], 0, 0, 0);
+      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(al), sel_as_bf16x8(kf[c][st]),
+                                                     z[c], 0, 0, 0);
+    }
+  }
+}
+
+// Keys of the wave: four tiles of 16 from key j0, 16 bytes per lane and step
+// (rows past n read row n - 1 and are masked by the callers).
+template <int DH>
+__device__ __forceinline__ void sel_load_keys(const bf16_t* __restrict__ Kh, int n, int j0,
+                                              u32x4 (&kf)[4][DH / 32]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j = min(j0 + 16 * c + lane % 16, n - 1);
+#pragma unroll
+    for (int st = 0; st < DH / 32; ++st)
+      kf[c][st] = *reinterpret_cast<const u32x4*>(Kh + (size_t)j * DH + 32 * st + 8 * (lane / 16));
+  }
+}
+
+// Stage queries [qb, qb + kSelQB) of KV head kv (rows padded by 4 floats).
+template <int DH>
+__device__ void sel_stage_q(const float* __restrict__ q_win, int kv, int Q, int qb, float* qs) {
+  const float* src = q_win + (size_t)kv * Q * DH;
+  for (int t = threadIdx.x; t < kSelQB * DH / 4; t += kSelThreads) {
+    const int qq = t / (DH / 4), c4 = t - qq * (DH / 4);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qb + qq < Q) v = reinterpret_cast<const float4*>(src + (size_t)(qb + qq) * DH)[c4];
+    *reinterpret_cast<float4*>(qs + qq * (DH + 4) + 4 * c4) = v;
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(kSelThreads) void sel_lse_partial_mfma_kernel(
+    const bf16_t* __restrict__ K, int cap, int n, const float* __restrict__ q_win, int w, int G,
+    float scale_log2, int n_chunks, float* __restrict__ lse_part) {
+  __shared__ __align__(16) float qs[kSelQB * (DH + 4)];
+  __shared__ float red_m[kSelWaves][kSelQB], red_l[kSelWaves][kSelQB];
+  const int kv = blockIdx.y;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int Q = G * w;
+  for (int qb = 0; qb < Q; qb += kSelQB) {
+    __syncthreads();
+    sel_stage_q<DH>(q_win, kv, Q, qb, qs);
+    __syncthreads();
+#pragma unroll 1
+  for (int sub = 0; sub < kSelSub; ++sub) {
+    const int chunk = blockIdx.x * kSelSub + sub;
+    if (chunk >= n_chunks) break;  // workgroup-uniform
+    const int j0 = chunk * kSelThreads + wave * 64;
+    u32x4 kf[4][DH / 32];
+    sel_load_keys<DH>(K + (size_t)kv * cap * DH, n, j0, kf);
+#pragma unroll 1
+    for (int rt = 0; rt < kSelQB / 16; ++rt) {
+      f32x4 z[4];
+      sel_tile_logits<DH>(qs, 16 * rt, kf, z);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ql = 16 * rt + 4 * (lane / 16) + r, q = qb + ql;
+        const int i = q % w;
+        float zz[4], mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = j0 + 16 * c + lane % 16;
+          const bool vis = q < Q && j < n && j <= n - w + i;
+          zz[c] = vis ? z[c][r] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, zz[c]);
+        }
+        mx = group_max<16>(mx);
+        float e = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) e += zz[c] == -INFINITY ? 0.f : exp2f(zz[c] - mx);
+        e = group_sum<16>(e);
+        if (lane % 16 == 0) {
+          red_m[wave][ql] = mx;
+          red_l[wave][ql] = e;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kSelQB && qb + threadIdx.x < Q) {
+      const int ql = threadIdx.x;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v) M = fmaxf(M, red_m[v][ql]);
+      float L = 0.f;
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v)
+        if (red_m[v][ql] != -INFINITY) L = fmaf(red_l[v][ql], exp2f(red_m[v][ql] - M), L);
+      float* o = lse_part + (((size_t)kv * n_chunks + chunk) * Q + qb + ql) * 2;
+      o[0] = M;
+      o[1] = L;
+    }
+    __syncthreads();  // red_m / red_l are reused by the next chunk
+  }
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(kSelThreads) void sel_score_mfma_kernel(
+    const bf16_t* __restrict__ K, int cap, int n, const float* __restrict__ q_win, int w, int G,
+    float scale_log2, const float* __restrict__ lse, float* __restrict__ scores) {
+  __shared__ __align__(16) float qs[kSelQB * (DH + 4)];
+  __shared__ float ls[kSelQB];
+  const int kv = blockIdx.y;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int Q = G * w;
+#pragma unroll 1
+  for (int sub = 0; sub < kSelSub; ++sub) {
+  const int chunk = blockIdx.x * kSelSub + sub;
+  if (chunk * kSelThreads >= n) break;  // workgroup-uniform
+  const int j0 = chunk * kSelThreads + wave * 64;
+  u32x4 kf[4][DH / 32];
+  sel_load_keys<DH>(K + (size_t)kv * cap * DH, n, j0, kf);
+  float sc[4] = {0.f, 0.f, 0.f, 0.f};  // per key tile, this lane's column
+  for (int qb = 0; qb < Q; qb += kSelQB) {
+    if (sub == 0 || Q > kSelQB) {  // one batch: staged once for all chunks
+      __syncthreads();
+      sel_stage_q<DH>(q_win, kv, Q, qb, qs);
+      if (threadIdx.x < kSelQB)  // lse of query q = g w + i is lse[(kv G + g) w + i]
+        ls[threadIdx.x] = qb + threadIdx.x < Q ? lse[(size_t)kv * Q + qb + threadIdx.x] : 0.f;
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int rt = 0; rt < kSelQB / 16; ++rt) {
+      f32x4 z[4];
+      sel_tile_logits<DH>(qs, 16 * rt, kf, z);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = j0 + 16 * c + lane % 16;
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ql = 16 * rt + 4 * (lane / 16) + r, q = qb + ql;
+          const bool vis = q < Q && j < n && j <= n - w + q % w;
+          part += vis ? exp2f(z[c][r] * scale_log2 - ls[ql]) : 0.f;
+        }
+        // add the four row groups of the column (lanes l, l ^ 16, l ^ 32, l ^ 48)
+        part += xor_lanes<16>(part);
+        part += xor_lanes<32>(part);
+        sc[c] += part;
+      }
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + 16 * c + lane;
+      if (j < n) scores[(size_t)kv * n + j] = sc[c];
+    }
+  }
+  }
 }
 
 // Order-preserving map of float32 to uint32 (larger float -> larger key);
@@ -309,13 +563,25 @@ static void select_typed(const SelectArgs& a, hipStream_t s) {
   const KT* k = (const KT*)a.k;
   if (!a.skip_scoring) {
     dim3 grid(a.n_chunks, a.h_kv);
-    launch_kernel(K_SEL_LSE, sel_lse_partial_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
-                  a.cap_full, a.n, a.q_win, a.w, G, scale_log2, a.n_chunks, a.lse_part);
-    const int nq = a.h_kv * G * a.w;
-    launch_kernel(K_SEL_LSE_FINAL, sel_lse_final_kernel, dim3((nq + 255) / 256), dim3(256), 0, s,
+    constexpr bool kMfma = sizeof(KT) == 2;  // bf16 caches: matrix cores
+    const dim3 mgrid((a.n_chunks + kSelSub - 1) / kSelSub, a.h_kv);
+    if constexpr (kMfma)
+      launch_kernel(K_SEL_LSE, sel_lse_partial_mfma_kernel<DH>, mgrid, dim3(kSelThreads), 0, s,
+                    (const bf16_t*)k, a.cap_full, a.n, a.q_win, a.w, G, scale_log2, a.n_chunks,
+                    a.lse_part);
+    else
+      launch_kernel(K_SEL_LSE, sel_lse_partial_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
+                    a.cap_full, a.n, a.q_win, a.w, G, scale_log2, a.n_chunks, a.lse_part);
+    const int nq = a.h_kv * G * a.w;  // one wave each, four per workgroup
+    launch_kernel(K_SEL_LSE_FINAL, sel_lse_final_kernel, dim3((nq + 3) / 4), dim3(256), 0, s,
                   (const float*)a.lse_part, a.n_chunks, G, a.w, a.h_kv, a.lse);
-    launch_kernel(K_SEL_SCORE, sel_score_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
-                  a.cap_full, a.n, a.q_win, a.w, G, scale_log2, (const float*)a.lse, a.scores);
+    if constexpr (kMfma)
+      launch_kernel(K_SEL_SCORE, sel_score_mfma_kernel<DH>, mgrid, dim3(kSelThreads), 0, s,
+                    (const bf16_t*)k, a.cap_full, a.n, a.q_win, a.w, G, scale_log2,
+                    (const float*)a.lse, a.scores);
+    else
+      launch_kernel(K_SEL_SCORE, sel_score_kernel<KT, DH>, grid, dim3(kSelThreads), 0, s, k,
+                    a.cap_full, a.n, a.q_win, a.w, G, scale_log2, (const float*)a.lse, a.scores);
   }
   // per-head kept counts (one count for all heads unless the budgets are ragged)
   HeadInts k_eff_heads{};

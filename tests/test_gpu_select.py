@@ -154,3 +154,20 @@ def test_select_is_deterministic():
     a_s, a_i = s.run(qw)
     b_s, b_i = s.run(qw)
     assert np.array_equal(a_s, b_s) and np.array_equal(a_i, b_i)
+
+
+@pytest.mark.parametrize("n,w", [(3001, 5), (2048, 32), (777, 64), (300, 1)])
+def test_8b_bf16_scores_match_oracle(n, w):
+    # bf16 caches score on the matrix cores (queries split into three bf16
+    # parts): float32-accurate logits, ragged chunk and query-batch tails
+    wl = dataclasses.replace(synth.L8B_KV_32K, n_ctx=n, window=w)
+    k, v = synth.kv_cache(wl, 5, n, n + 8)
+    qw = synth.window_queries(wl, 5)
+    s = Sel(wl, k, v, n, n + 8, min(n, max(wl.n_sink + w, n // 4)))
+    got, idx = s.run(qw)
+    want = osel.window_scores(qw, k, n, 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(got, want) <= 1e-5
+    # each window query's softmax sums to one: G * w per KV head
+    np.testing.assert_allclose(got.sum(1), 4 * w, rtol=1e-5)
+    want_idx = osel.select_indices(got, n, w, wl.n_sink, s.k_keep)
+    assert np.array_equal(idx, want_idx)   # the GPU ranks its own scores exactly
