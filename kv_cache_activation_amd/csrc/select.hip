@@ -17,10 +17,12 @@
 //                that the query puts on its key -> scores[kv, j].
 //   topk         one 1024-thread workgroup per KV head: an 8-bit-digit radix
 //                select on order-preserving keys of the float32 scores finds
-//                the m-th largest candidate value T; a block-wide ballot scan
-//                then emits, in ascending position, the sinks, the window, all
-//                candidates above T and the lowest-position candidates equal to
-//                T up to m (ties to the lower position).
+//                the m-th largest candidate value T; each wave then counts its
+//                contiguous range with ballots, two block scans place the
+//                ranges, and each wave emits, in ascending position, the
+//                sinks, the window, all candidates above T and the
+//                lowest-position candidates equal to T up to m (ties to the
+//                lower position).
 //   gather       16-byte copies of the kept K and V rows into the buffer.
 #include <math.h>
 
@@ -448,12 +450,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide exclusive prefix count of `flag` (ascending thread order), plus
-// the block total; uses wave ballots and an LDS array of wave totals.
-__device__ __forceinline__ int block_prefix(bool flag, int* wave_tot, int& total) {
+// Block-wide exclusive prefix sum of per-thread counts (thread order), plus
+// the block total: a DPP wave scan, then the wave totals through LDS.
+__device__ __forceinline__ int block_excl_sum(int x, int* wave_tot, int& total) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const unsigned long long m = __ballot(flag);
-  if (lane == 0) wave_tot[wave] = __popcll(m);
+  const int incl = wave_incl_scan(x);
+  if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
   int before = 0;
   total = 0;
@@ -462,7 +464,7 @@ __device__ __forceinline__ int block_prefix(bool flag, int* wave_tot, int& total
     total += wave_tot[v];
   }
   __syncthreads();
-  return before + __popcll(m & ((1ull << lane) - 1ull));
+  return before + incl - x;
 }
 
 __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(const float* __restrict__ scores,
@@ -486,26 +488,39 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(const float* __r
   const int c0 = n_sink, c1 = n - w;
   unsigned T = 0, need = 0;
   if (m > 0) {
+    // the m-th largest candidate key T: four 8-bit digit passes, each a
+    // histogram of the candidates whose higher digits match those found
     unsigned prefix = 0;
     need = (unsigned)m;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int b = threadIdx.x; b < 256; b += kTopkThreads) hist[b] = 0u;
+      for (int bb = threadIdx.x; bb < 256; bb += kTopkThreads) hist[bb] = 0u;
       __syncthreads();
-      for (int j = c0 + threadIdx.x; j < c1; j += kTopkThreads) {
-        const unsigned key = order_key(S[j]);
-        if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
-          atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      // eight scores per thread in flight (from clamped, always valid
+      // positions) before their histogram adds
+      constexpr int HU = 8;
+      for (int j0 = c0; j0 < c1; j0 += kTopkThreads * HU) {  // uniform trip count
+        unsigned key[HU];
+#pragma unroll
+        for (int u = 0; u < HU; ++u)
+          key[u] = order_key(S[min(j0 + (int)threadIdx.x + kTopkThreads * u, c1 - 1)]);
+#pragma unroll
+        for (int u = 0; u < HU; ++u) {
+          const int j = j0 + (int)threadIdx.x + kTopkThreads * u;
+          const bool match =
+              j < c1 && (pass == 0 || (key[u] >> (shift + 8)) == (prefix >> (shift + 8)));
+          if (match) atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
+        }
       }
       __syncthreads();
       if (threadIdx.x == 0) {
         unsigned above = 0;
-        int b = 255;
-        for (; b > 0; --b) {
-          if (above + hist[b] >= need) break;
-          above += hist[b];
+        int bb = 255;
+        for (; bb > 0; --bb) {
+          if (above + hist[bb] >= need) break;
+          above += hist[bb];
         }
-        sh_prefix = prefix | ((unsigned)b << shift);
+        sh_prefix = prefix | ((unsigned)bb << shift);
         sh_need = need - above;
       }
       __syncthreads();
@@ -515,23 +530,62 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(const float* __r
     }
     T = prefix;
   }
-  int base_take = 0, base_eq = 0;
-  for (int t0 = 0; t0 < n; t0 += kTopkThreads) {
-    const int j = t0 + threadIdx.x;
-    const bool valid = j < n;
-    const bool forced = valid && (j < c0 || j >= c1);
-    const bool cand = valid && !forced && m > 0;
-    const unsigned key = cand ? order_key(S[j]) : 0u;
-    const bool gt = cand && key > T;
-    const bool eq = cand && key == T;
-    int eq_total;
-    const int eq_rank = base_eq + block_prefix(eq, wave_tot, eq_total);
-    const bool take = forced || gt || (eq && eq_rank < (int)need);
-    int take_total;
-    const int pos = base_take + block_prefix(take, wave_tot, take_total);
-    if (take && pos < k_keep) out[pos] = j;  // pos < k_keep always; guard anyway
-    base_eq += eq_total;
-    base_take += take_total;
+  // emission in ascending position: wave v owns positions [v R, v R + R),
+  // read 64 at a time (coalesced); kept are the forced rows, candidates above
+  // T, and the first `need` candidates equal to T in position order.  A
+  // first sweep counts, two block scans place the waves, a second sweep
+  // writes with ballot ranks.
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int R = (n + kTopkWaves - 1) / kTopkWaves;
+  const int p0 = min(n, wave * R), p1 = min(n, p0 + R);
+  // eight 64-position blocks per step, their loads in flight together
+  constexpr int EU = 8;
+  auto key_at = [&](int j) { return order_key(S[min(j, n - 1)]); };
+  int n_take = 0, n_eq = 0;  // wave totals (uniform)
+  for (int jb = p0; jb < p1; jb += kWave * EU) {
+    unsigned kk[EU];
+#pragma unroll
+    for (int u = 0; u < EU; ++u) kk[u] = key_at(jb + kWave * u + lane);
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int j = jb + kWave * u + lane;
+      const bool valid = j < p1;
+      const bool forced = valid && (j < c0 || j >= c1);
+      const bool cand = valid && !forced && m > 0;
+      n_take += __popcll(__ballot(forced || (cand && kk[u] > T)));
+      n_eq += __popcll(__ballot(cand && kk[u] == T));
+    }
+  }
+  int eq_total;
+  const int eq_before = block_excl_sum(lane == 0 ? n_eq : 0, wave_tot, eq_total);
+  const int eq_wave = __shfl(eq_before, 0);
+  const int ties = max(0, min(n_eq, (int)need - eq_wave));  // ties this wave keeps
+  int take_total;
+  const int pos_before = block_excl_sum(lane == 0 ? n_take + ties : 0, wave_tot, take_total);
+  int pos = __shfl(pos_before, 0), eq_seen = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int jb = p0; jb < p1; jb += kWave * EU) {
+    unsigned kk[EU];
+#pragma unroll
+    for (int u = 0; u < EU; ++u) kk[u] = key_at(jb + kWave * u + lane);
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int j = jb + kWave * u + lane;
+      const bool valid = j < p1;
+      const bool forced = valid && (j < c0 || j >= c1);
+      const bool cand = valid && !forced && m > 0;
+      const bool eq = cand && kk[u] == T;
+      const unsigned long long eqm = __ballot(eq);
+      const bool take = forced || (cand && kk[u] > T) ||
+                        (eq && eq_seen + __popcll(eqm & below) < ties);
+      const unsigned long long tm = __ballot(take);
+      if (take) {
+        const int p = pos + __popcll(tm & below);
+        if (p < k_keep) out[p] = j;  // p < k_keep always; guard anyway
+      }
+      pos += __popcll(tm);
+      eq_seen += __popcll(eqm);
+    }
   }
 }
 
