@@ -37,7 +37,8 @@ namespace sd {
 constexpr int kTealThreads = 512;
 constexpr int kTealWaves = kTealThreads / kWave;
 constexpr int kTealTile = kTealWaves * kWave * 8;  // 4096 output columns per workgroup
-constexpr int kRCols = 16, kRSlices = 16;          // reduce: 16 columns x 16 slices
+constexpr int kRCols = 16, kRSlices = 16;          // QKV reduce: 16 columns x 16 slices
+constexpr int kRCols2 = 32;  // plain reduce: 32 columns, so a partial is read in 128-byte pieces
 constexpr int kRPer = kTealMaxParts / kRSlices;    // partitions per slice, at most
 
 // NQ float4 chunks of the input per thread (d_in <= 4 NQ 512).
@@ -173,8 +174,9 @@ __global__ __launch_bounds__(kTealThreads) void teal_kernel(
 
 // Sum of the P partials of column c: slice sl of the column sums partitions
 // [sl per, sl per + per) in order, then the slices are added in order.
+template <int COLS>
 __device__ __forceinline__ float column_sum(const float* __restrict__ part, int P, int d_out,
-                                            int c, int sl, int cl, float (*red)[kRCols]) {
+                                            int c, int sl, int cl, float (*red)[COLS]) {
   const int per = (P + kRSlices - 1) / kRSlices;
   const int w0 = sl * per;
   float v[kRPer];
@@ -195,15 +197,15 @@ __device__ __forceinline__ float column_sum(const float* __restrict__ part, int 
 
 // y[c] (+)= sum of partials (EPI 0), or y[c] = SiLU(sum part0) * (sum part1) (EPI 1).
 template <int EPI>
-__global__ __launch_bounds__(kRCols * kRSlices) void teal_reduce_kernel(
+__global__ __launch_bounds__(kRCols2 * kRSlices) void teal_reduce_kernel(
     const float* __restrict__ part0, const float* __restrict__ part1, int P, int d_out,
     float* __restrict__ y, int accumulate) {
-  __shared__ float red0[kRSlices][kRCols], red1[kRSlices][kRCols];
-  const int cl = threadIdx.x % kRCols, sl = threadIdx.x / kRCols;
-  const int c = blockIdx.x * kRCols + cl;
-  const float a = column_sum(part0, P, d_out, c, sl, cl, red0);
+  __shared__ float red0[kRSlices][kRCols2], red1[kRSlices][kRCols2];
+  const int cl = threadIdx.x % kRCols2, sl = threadIdx.x / kRCols2;
+  const int c = blockIdx.x * kRCols2 + cl;
+  const float a = column_sum<kRCols2>(part0, P, d_out, c, sl, cl, red0);
   float b = 0.f;
-  if (EPI == 1) b = column_sum(part1, P, d_out, c, sl, cl, red1);
+  if (EPI == 1) b = column_sum<kRCols2>(part1, P, d_out, c, sl, cl, red1);
   if (sl == 0 && c < d_out) {
     if (EPI == 1) y[c] = silu(a) * b;
     else y[c] = accumulate ? y[c] + a : a;
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(kRCols * kRSlices) void teal_qkv_reduce_kernel(
   const int head = blockIdx.x / per_head, i0 = (blockIdx.x % per_head) * 8;
   const int cl = threadIdx.x % kRCols, sl = threadIdx.x / kRCols;
   const int c = head * dh + (cl < 8 ? i0 + cl : half + i0 + cl - 8);
-  const float v = column_sum(part, P, d_out, c, sl, cl, red);
+  const float v = column_sum<kRCols>(part, P, d_out, c, sl, cl, red);
   if (sl == 0) tot[cl] = v;
   __syncthreads();
   if (threadIdx.x >= 8) return;
@@ -297,7 +299,7 @@ void launch_teal(const TealArgs& a, int w_dtype, hipStream_t s) {
 
 void launch_teal_reduce(const float* part0, const float* part1, int parts, int d_out, float* y,
                         int accumulate, int swiglu, int kind, hipStream_t s) {
-  const dim3 grid((d_out + kRCols - 1) / kRCols), block(kRCols * kRSlices);
+  const dim3 grid((d_out + kRCols2 - 1) / kRCols2), block(kRCols2 * kRSlices);
   if (swiglu)
     launch_kernel(kind, teal_reduce_kernel<1>, grid, block, 0, s, part0, part1, parts, d_out, y,
                   accumulate);
