@@ -7,14 +7,18 @@
 //
 //   one launch, grid (splits, KV heads): a workgroup owns a contiguous chunk
 //   of rows of one KV head and serves all G query heads of the group, so each
-//   K/V byte is read once.  A row of d_h elements is spread over d_h/8 lanes
-//   (16-byte loads); the wave holds 64/(d_h/8) row slots, and each slot keeps
-//   U rows in flight per iteration (U = 4 with four query heads per KV head:
-//   occupancy 3), so a workgroup streams U*16 consecutive rows of K and of V
-//   per iteration (the chunk is read in address order).
+//   K/V byte is read once.  A row of d_h elements is spread over d_h/16 lanes
+//   (two 16-byte loads per lane, each load instruction covering whole 128-byte
+//   lines); the wave holds 64/(d_h/16) row slots, and two register buffers of
+//   U rows per slot alternate, so the next rows are in flight while the
+//   current ones are computed (the chunk is read in address order).  The
+//   kernel spends its vector-ALU time on the dot products and the P V update:
+//   wide rows per lane keep the lane exchanges and the softmax bookkeeping
+//   per element small, and the running maximum is only raised (with a
+//   rescale) when a logit passes it by 2^8.
 //   Every lane group keeps its own online-softmax state (max, sum, acc) in the
-//   log2 domain; at the end the groups and the four waves merge their states
-//   and write one (m, l, acc[d_h]) per query head and split.
+//   log2 domain; at the end the groups write their states to LDS and the
+//   workgroup merges them into one (m, l, acc[d_h]) per query head and split.
 //
 //   Ragged per-head lengths launch only the chunks that hold rows: a flat
 //   grid whose block index is mapped to (KV head, chunk) by per-head prefix
@@ -43,24 +47,54 @@ namespace sd {
 constexpr int kAttnThreads = 256;
 constexpr int kMaxSplits = 256;  // splits per KV head (the merge holds a column's share in VGPRs)
 constexpr int kAttnWaves = kAttnThreads / kWave;
+// Lazy rescaling: the running maximum of a lane group only moves when a new
+// logit exceeds it by more than this (log2 domain), so the exponentials stay
+// below 2^8 and the accumulator is rescaled a few times per chunk, not per row.
+constexpr float kLazyMax = 8.f;
+// Maximum of a lane group that has seen no row yet: finite, so 2^(z - m) of a
+// masked logit (z = -inf) is 0 and never NaN.
+constexpr float kNoRow = -1e30f;
 
-template <typename KT, int DH, int G, int U>
+// Raw v_exp_f32: 2^x with -inf -> 0.  The arguments here are at most kLazyMax,
+// and results that would be denormal only lose weights below 2^-126.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Split-K partial attention.  EPL = elements of a row per lane (16, or 8 when
+// G = 8 so that the query and accumulator registers fit): a row of d_h
+// elements is spread over LPR = d_h / EPL lanes, lane `sub` holding the
+// 8-element pieces at 8 sub + h d_h / H for h < H = EPL / 8, so each 16-byte
+// load instruction of the wave covers whole 128-byte lines of its rows.  A
+// dot product then needs log2(LPR) lane exchanges per query head (3 for
+// d_h = 128), and the softmax bookkeeping is shared by EPL elements.
+// Two register buffers of U rows per slot alternate: the loads of the next
+// U * SLOTS rows are in flight while the current ones are computed.  Rows
+// past the chunk's end load the chunk's last row (a repeat the cache serves)
+// and get weight 0.
+// MODE: 0 = one cache and one length (grid (splits, groups)); 1 = ragged
+// per-head lengths; 2 = a batch of sequences.  A compile-time mode leaves the
+// plain path without the branches that would make it fetch its arguments in
+// several dependent rounds.
+template <typename KT, int DH, int G, int U, int EPL, int MODE>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
     int n_ctx, int sink, int shift, int kv_div, int ragged, HeadInts lens, HeadInts starts,
     int batched, AttnBatch bt, int h_q, float scale_log2, int chunk, int n_splits,
     float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ pacc) {
-  constexpr int LPR = DH / 8;          // lanes per row
+  constexpr int H = EPL / 8;           // 8-element pieces per lane and row
+  constexpr int LPR = DH / EPL;        // lanes per row
   constexpr int RPW = kWave / LPR;     // row slots per wave
   constexpr int SLOTS = kAttnWaves * RPW;
-  __shared__ float sm_m[kAttnWaves][G], sm_l[kAttnWaves][G];
-  __shared__ float sm_acc[kAttnWaves][G][DH];
+  constexpr int STEP = U * SLOTS;      // rows of one register buffer
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "lanes per row");
+  // per row slot: its softmax state; 64 KB of LDS at most (SLOTS G DH floats)
+  __shared__ float sm_m[SLOTS][G], sm_l[SLOTS][G], sm_w[SLOTS][G], sm_M[G];
+  __shared__ __align__(16) float sm_acc[SLOTS][G][DH];
 
   // grid (splits, groups); ragged: a flat grid, block b belongs to the last
   // head whose first chunk starts at or before b (starts ascending, unused
   // entries past the last head hold INT_MAX)
   int split = blockIdx.x, kv = blockIdx.y;
-  if (ragged) {
+  if constexpr (MODE == 1) {
     kv = 0;
 #pragma unroll
     for (int h = 1; h < kMaxKvHeads; ++h) kv += (int)(split >= starts.v[h]);
@@ -68,8 +102,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
   // batched: a flat grid over (sequence, KV head, chunk); each sequence reads
   // its own cache with its own query rows and partial slots
-  int seq = 0, rows = ragged ? lens.v[(kv / kv_div) & (kMaxKvHeads - 1)] : n_ctx;
-  if (batched) {
+  int seq = 0, rows = n_ctx;
+  if constexpr (MODE == 1) rows = lens.v[(kv / kv_div) & (kMaxKvHeads - 1)];
+  if constexpr (MODE == 2) {
 #pragma unroll
     for (int b = 1; b < 8; ++b) seq += (int)(split >= bt.starts[b]);
     const int local = split - bt.starts[seq];
@@ -82,6 +117,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     rows = bt.rows[seq];
     q += (size_t)seq * h_q * DH;
   }
+  // pointers in registers now: one round of argument loads, not one per branch
+  asm volatile("" ::"s"(q), "s"(K), "s"(V), "s"(pm), "s"(pl), "s"(pacc));
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int sub = lane % LPR;
   const int slot = wave * RPW + lane / LPR;
@@ -94,138 +131,173 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   const KT* Vb = V + (size_t)(kv / kv_div) * cap * DH + 8 * sub;
   auto phys = [&](int jj) { return (size_t)(jj + (jj >= sink ? shift : 0)); };
 
-  // first rows in flight before the query is read
-  Vec8<KT> kr[U], vr[U];
-  int j = r0 + slot;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int jj = j + u * SLOTS;
-    if (jj < r1) {
-      kr[u].load(Kb + phys(jj) * DH);
-      vr[u].load(Vb + phys(jj) * DH);
-    }
-  }
-
-  float qv[G][8];
+  float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    load8f(q + (size_t)(kv * G + g) * DH + 8 * sub, qv[g]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[g][e] *= scale_log2;
-  }
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
+    m[g] = kNoRow;
     l[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
-  for (; j < r1; j += U * SLOTS) {
-    float p[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = j + u * SLOTS < r1;
-      float kf[8];
-      kr[u].to_float(kf);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t = fmaf(kf[e], qv[g][e], t);
-        t = group_sum<LPR>(t);
-        p[u][g] = ok ? t : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mb = p[0][g];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mb = fmaxf(mb, p[u][g]);
-      const float mn = fmaxf(m[g], mb);  // finite: row j itself is valid
-      const float alpha = exp2f(m[g] - mn);
-      float ps = 0.f;
+  if (r0 < r1) {  // workgroup-uniform; every chunk of a launch holds rows
+    Vec8<KT> ka[U][H], va[U][H], kb[U][H], vb[U][H];
+    // rows jb + slot + u SLOTS of this lane, clamped into the chunk
+    auto issue = [&](Vec8<KT>(&kr)[U][H], Vec8<KT>(&vr)[U][H], int jb) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        p[u][g] = exp2f(p[u][g] - mn);
-        ps += p[u][g];
+        const size_t o = phys(min(jb + slot + u * SLOTS, r1 - 1)) * DH;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          kr[u][h].load(Kb + o + h * (DH / H));
+          vr[u][h].load(Vb + o + h * (DH / H));
+        }
       }
-      l[g] = fmaf(l[g], alpha, ps);
+    };
+    issue(ka, va, r0);  // first rows in flight before the query is read
+
+    float qv[G][EPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
-      m[g] = mn;
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        float t[8];
+        load8f(q + (size_t)(kv * G + g) * DH + 8 * sub + h * (DH / H), t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[g][8 * h + e] = t[e] * scale_log2;
+      }
     }
+
+    auto compute = [&](const Vec8<KT>(&kr)[U][H], const Vec8<KT>(&vr)[U][H], int jb) {
+      float p[U][G];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[8];
-      vr[u].to_float(vf);
-      if (!(j + u * SLOTS < r1))
+      for (int u = 0; u < U; ++u) {
+        float kf[EPL];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = 0.f;  // never loaded: keep NaN/Inf out
+        for (int h = 0; h < H; ++h) {
+          float t[8];
+          kr[u][h].to_float(t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kf[8 * h + e] = t[e];
+        }
+        const bool ok = jb + slot + u * SLOTS < r1;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) t = fmaf(kf[e], qv[g][e], t);
+          t = group_sum<LPR>(t);
+          p[u][g] = ok ? t : -INFINITY;
+        }
+      }
+      float mb[G];
+      bool up = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        mb[g] = p[0][g];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mb[g] = fmaxf(mb[g], p[u][g]);
+        up |= mb[g] > m[g] + kLazyMax;
+      }
+      if (up) {  // per lane; after the first rows of a chunk this is rare
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float mn = fmaxf(m[g], mb[g]);
+          const float alpha = exp2_raw(m[g] - mn);
+          l[g] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+          m[g] = mn;
+        }
+      }
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
-    }
-    // next rows
+        for (int u = 0; u < U; ++u) {
+          p[u][g] = exp2_raw(p[u][g] - m[g]);
+          l[g] += p[u][g];
+        }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int jj = j + U * SLOTS + u * SLOTS;
-      if (jj < r1) {
-        kr[u].load(Kb + phys(jj) * DH);
-        vr[u].load(Vb + phys(jj) * DH);
+      for (int u = 0; u < U; ++u) {
+        float vf[EPL];
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          float t[8];
+          vr[u][h].to_float(t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[8 * h + e] = t[e];
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[u][g], vf[e], acc[g][e]);
       }
+    };
+
+    // two buffers: issue the next STEP rows, then compute the current ones.
+    // The issues are unconditional (past the end they repeat row r1 - 1, one
+    // line per lane group that the cache serves), so every wait for a buffer
+    // counts exactly the other buffer's loads as still in flight.
+    const int n_it = (r1 - r0 + STEP - 1) / STEP;  // >= 1, uniform
+    // The scheduling barriers keep each buffer's loads together ahead of the
+    // other buffer's arithmetic (left alone, the compiler moves half of them
+    // behind the first wait).
+    for (int it = 0; it < n_it; it += 2) {
+      const int jb = r0 + it * STEP;
+      issue(kb, vb, jb + STEP);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ka, va, jb);
+      issue(ka, va, jb + 2 * STEP);
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + 1 < n_it) compute(kb, vb, jb + STEP);
     }
   }
 
-  // merge the row slots of the wave (lane groups that differ in lane / LPR)
-#pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
+  // Merge of the workgroup's row slots through LDS: each lane group writes its
+  // state once, then every thread sums its outputs over the slots with the
+  // weights 2^(m_slot - M).  (A tree of lane exchanges costs about a thousand
+  // vector instructions per lane for 4 heads x 16 elements, more than a short
+  // chunk's whole stream.)
+  if (sub == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], mo);
-      const float a1 = m[g] == -INFINITY ? 0.f : exp2f(m[g] - mn);
-      const float a2 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
-      l[g] = l[g] * a1 + lo * a2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(acc[g][e], off);
-        acc[g][e] = acc[g][e] * a1 + ao * a2;
-      }
-      m[g] = mn;
+      sm_m[slot][g] = m[g];
+      sm_l[slot][g] = l[g];
     }
   }
-  if (lane < LPR) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (lane == 0) {
-        sm_m[wave][g] = m[g];
-        sm_l[wave][g] = l[g];
-      }
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][g][8 * lane + e] = acc[g][e];
+    for (int h = 0; h < H; ++h) {
+      float* dst = &sm_acc[slot][g][8 * sub + h * (DH / H)];
+      reinterpret_cast<float4*>(dst)[0] =
+          make_float4(acc[g][8 * h], acc[g][8 * h + 1], acc[g][8 * h + 2], acc[g][8 * h + 3]);
+      reinterpret_cast<float4*>(dst)[1] =
+          make_float4(acc[g][8 * h + 4], acc[g][8 * h + 5], acc[g][8 * h + 6], acc[g][8 * h + 7]);
     }
+  __syncthreads();
+  // slot weights: thread (s, g) -> sm_w[s][g] = 2^(m_s - M_g), sm_M[g] = M_g
+  for (int t = threadIdx.x; t < SLOTS * G; t += kAttnThreads) {
+    const int s2 = t / G, g = t - s2 * G;
+    float M = kNoRow;
+#pragma unroll 8
+    for (int s3 = 0; s3 < SLOTS; ++s3) M = fmaxf(M, sm_m[s3][g]);
+    sm_w[s2][g] = exp2_raw(sm_m[s2][g] - M);
+    if (s2 == 0) sm_M[g] = M;
   }
   __syncthreads();
   for (int t = threadIdx.x; t < G * DH; t += kAttnThreads) {
     const int g = t / DH, c = t - g * DH;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w][g]);
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      const float a = sm_m[w][g] == -INFINITY ? 0.f : exp2f(sm_m[w][g] - M);
-      L = fmaf(sm_l[w][g], a, L);
-      A = fmaf(sm_acc[w][g][c], a, A);
-    }
+    float A = 0.f;
+#pragma unroll 8
+    for (int s2 = 0; s2 < SLOTS; ++s2) A = fmaf(sm_acc[s2][g][c], sm_w[s2][g], A);
     const size_t hs = ((size_t)seq * h_q + kv * G + g) * n_splits + split;
     pacc[hs * DH + c] = A;
     if (c == 0) {
-      pm[hs] = M;
+      float L = 0.f;
+#pragma unroll 8
+      for (int s2 = 0; s2 < SLOTS; ++s2) L = fmaf(sm_l[s2][g], sm_w[s2][g], L);
+      pm[hs] = L > 0.f ? sm_M[g] : -INFINITY;  // a split without rows: (-inf, 0, 0)
       pl[hs] = L;
     }
   }
@@ -241,7 +313,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeCols = 32;
 constexpr int kMergeGroups = kMergeThreads / kMergeCols;
 
-template <int DH, int CAP>
+template <int DH, int CAP, int MODE>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
     const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ pacc,
     int stride, int ragged, HeadInts counts, int G, int batched, AttnBatch bt, int h_q,
@@ -253,9 +325,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(
   __shared__ float share[kMergeGroups][kMergeCols];
   const int h = blockIdx.x, t = threadIdx.x;
   const int col = blockIdx.y * kMergeCols + t % kMergeCols, grp = t / kMergeCols;
-  const int ns = batched  ? bt.splits[(h / h_q) & 7]
-                 : ragged ? counts.v[(h / G) & (kMaxKvHeads - 1)]
-                          : stride;
+  asm volatile("" ::"s"(pm), "s"(pl), "s"(pacc), "s"(out), "s"(lse));  // one round of argument loads
+  int ns = stride;  // MODE as in attn_kernel
+  if constexpr (MODE == 1) ns = counts.v[(h / G) & (kMaxKvHeads - 1)];
+  if constexpr (MODE == 2) ns = bt.splits[(h / h_q) & 7];
   const float* base = pacc + (size_t)h * stride * DH + col;
   float v[PER];
 #pragma unroll
@@ -326,27 +399,41 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   }
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
-#define SD_ATTN_G(GG, UU)                                                                   \
-  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU>, grid, dim3(kAttnThreads), 0, s, \
-                a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, starts,        \
+#define SD_ATTN_M(GG, UU, EE, MM)                                                           \
+  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU, EE, MM>, grid, dim3(kAttnThreads), 0, \
+                s, a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, starts,   \
                 a.batched, a.bt, a.h_q, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
+#define SD_ATTN_G(GG, UU, EE)                  \
+  do {                                         \
+    if (a.batched) SD_ATTN_M(GG, UU, EE, 2);   \
+    else if (a.ragged) SD_ATTN_M(GG, UU, EE, 1); \
+    else SD_ATTN_M(GG, UU, EE, 0);             \
+  } while (0)
   switch (G) {
-    case 1: SD_ATTN_G(1, 8); break;
-    case 2: SD_ATTN_G(2, 8); break;
-    case 4: SD_ATTN_G(4, 4); break;
-    default: SD_ATTN_G(8, 4); break;
+    case 1: SD_ATTN_G(1, 4, 16); break;
+    case 2: SD_ATTN_G(2, 4, 16); break;
+    case 4: SD_ATTN_G(4, 2, 16); break;
+    default: SD_ATTN_G(8, 2, 8); break;
   }
 #undef SD_ATTN_G
+#undef SD_ATTN_M
   const dim3 mgrid(nq, DH / kMergeCols);
   const int G_all = a.h_q / a.h_kv;
-#define SD_MERGE(CAPV)                                                                        \
-  launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, CAPV>, mgrid, dim3(kMergeThreads), 0, s, \
-                a.pm, a.pl, a.pacc, a.n_splits, a.ragged, counts, G_all, a.batched, a.bt, a.h_q, \
+#define SD_MERGE_M(CAPV, MM)                                                                   \
+  launch_kernel(K_ATTN_COMBINE, attn_merge_kernel<DH, CAPV, MM>, mgrid, dim3(kMergeThreads), 0, s, \
+                a.pm, a.pl, a.pacc, a.n_splits, a.ragged, counts, G_all, a.batched, a.bt, a.h_q,   \
                 a.out, a.lse)
+#define SD_MERGE(CAPV)                        \
+  do {                                        \
+    if (a.batched) SD_MERGE_M(CAPV, 2);       \
+    else if (a.ragged) SD_MERGE_M(CAPV, 1);   \
+    else SD_MERGE_M(CAPV, 0);                 \
+  } while (0)
   if (a.n_splits <= 64) SD_MERGE(64);
   else if (a.n_splits <= 128) SD_MERGE(128);
   else SD_MERGE(kMaxSplits);
 #undef SD_MERGE
+#undef SD_MERGE_M
 }
 
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s) {
