@@ -28,7 +28,7 @@ sd_status fail(sd_status st, const char* fmt, ...) {
 bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kMaxSplits = 256;        // split-K chunks per KV head (the merge's capacity)
-constexpr int kSplitBlocks = 512;      // auto mode: at most this many split workgroups
+constexpr int kSplitBlocks = 256;      // auto mode: at most this many split workgroups
 constexpr int kMinChunk = 64;          // auto mode: rows per split, lower bound
 constexpr int kSelChunk = 256;         // key rows per selection workgroup
 constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in VGPRs
@@ -123,12 +123,14 @@ int cu_count() {
   return cu > 0 ? cu : 256;
 }
 
-// Split count of the split-K attention.  Measured on MI355X, two resident
-// workgroups per CU stream best, and a launch with more than kSplitBlocks
-// (= 2 per CU) workgroups with work runs its surplus as a second, slow round
-// (25% longer just above the line).  So: chunks of at least kMinChunk rows,
-// about kSplitBlocks of them over all heads, then the largest split count
-// whose chunks (ceil(n_max / s) rows, the size the launch uses) number at most
+// Split count of the split-K attention.  Measured on MI355X (partial +
+// combine, bf16, 8 KV heads, caches rotated past the Infinity Cache): the
+// launch costs about 9.5 us plus its bytes at 7.3 TB/s, and one workgroup per
+// CU (kSplitBlocks = 256 chunks over all heads) is the fastest grid at every
+// length from 3K to 128K rows per head (13114 rows: 16.8 us at 256 chunks,
+// 17.9 at 512, 23.7 at 1024).  So: chunks of at least kMinChunk rows, about
+// kSplitBlocks of them over all heads, then the largest split count whose
+// chunks (ceil(n_max / s) rows, the size the launch uses) number at most
 // kSplitBlocks, at most kMaxSplits.  Ragged lengths count each head's own
 // chunks; a long head among short ones then gets many splits.
 int plan_splits(const sd::HeadInts& lens, int h_kv, int n_max) {
