@@ -54,6 +54,26 @@ constexpr float kLazyMax = 8.f;
 // Maximum of a lane group that has seen no row yet: finite, so 2^(z - m) of a
 // masked logit (z = -inf) is 0 and never NaN.
 constexpr float kNoRow = -1e30f;
+// Register buffers of rows in rotation (NBUF - 1 in flight during a compute).
+constexpr int kAttnBufs = 2;
+
+// Max and sum over aligned groups of N lanes (16, 32 or 64), VALU exchanges.
+template <int N>
+__device__ __forceinline__ float slot_max(float x) {
+  static_assert(N == 16 || N == 32 || N == 64, "slot groups of 16, 32 or 64 lanes");
+  x = group_max<16>(x);
+  if (N >= 32) x = fmaxf(x, xor_lanes<16>(x));
+  if (N >= 64) x = fmaxf(x, xor_lanes<32>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float slot_sum(float x) {
+  static_assert(N == 16 || N == 32 || N == 64, "slot groups of 16, 32 or 64 lanes");
+  x = group_sum<16>(x);
+  if (N >= 32) x += xor_lanes<16>(x);
+  if (N >= 64) x += xor_lanes<32>(x);
+  return x;
+}
 
 // Raw v_exp_f32: 2^x with -inf -> 0.  The arguments here are at most kLazyMax,
 // and results that would be denormal only lose weights below 2^-126.
@@ -74,7 +94,7 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 // per-head lengths; 2 = a batch of sequences.  A compile-time mode leaves the
 // plain path without the branches that would make it fetch its arguments in
 // several dependent rounds.
-template <typename KT, int DH, int G, int U, int EPL, int MODE>
+template <typename KT, int DH, int G, int U, int EPL, int MODE, int NBUF>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const float* __restrict__ q, const KT* __restrict__ K, const KT* __restrict__ V, int cap,
     int n_ctx, int sink, int shift, int kv_div, int ragged, HeadInts lens, HeadInts starts,
@@ -87,7 +107,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   constexpr int STEP = U * SLOTS;      // rows of one register buffer
   static_assert(LPR == 4 || LPR == 8 || LPR == 16, "lanes per row");
   // per row slot: its softmax state; 64 KB of LDS at most (SLOTS G DH floats)
-  __shared__ float sm_m[SLOTS][G], sm_l[SLOTS][G], sm_w[SLOTS][G], sm_M[G];
+  __shared__ float sm_m[SLOTS][G], sm_l[SLOTS][G], sm_M[G], sm_L[G];
+  __shared__ __align__(16) float sm_w[G][SLOTS];
   __shared__ __align__(16) float sm_acc[SLOTS][G][DH];
 
   // grid (splits, groups); ragged: a flat grid, block b belongs to the last
@@ -141,7 +162,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
 
   if (r0 < r1) {  // workgroup-uniform; every chunk of a launch holds rows
-    Vec8<KT> ka[U][H], va[U][H], kb[U][H], vb[U][H];
+    Vec8<KT> kbuf[NBUF][U][H], vbuf[NBUF][U][H];
     // rows jb + slot + u SLOTS of this lane, clamped into the chunk
     auto issue = [&](Vec8<KT>(&kr)[U][H], Vec8<KT>(&vr)[U][H], int jb) {
 #pragma unroll
@@ -154,7 +175,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
         }
       }
     };
-    issue(ka, va, r0);  // first rows in flight before the query is read
+    // the first NBUF - 1 buffers in flight before the query is read
+#pragma unroll
+    for (int i = 0; i + 1 < NBUF; ++i) issue(kbuf[i], vbuf[i], r0 + i * STEP);
 
     float qv[G][EPL];
 #pragma unroll
@@ -234,28 +257,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
       }
     };
 
-    // two buffers: issue the next STEP rows, then compute the current ones.
+    // NBUF buffers in rotation: step k of a round issues iteration it + k +
+    // NBUF - 1 into the buffer freed by step k - 1, then computes iteration
+    // it + k, so NBUF - 1 buffers of rows are in flight during every compute.
     // The issues are unconditional (past the end they repeat row r1 - 1, one
     // line per lane group that the cache serves), so every wait for a buffer
-    // counts exactly the other buffer's loads as still in flight.
+    // counts exactly the newer buffers' loads as still in flight; the
+    // scheduling barriers keep each buffer's loads together ahead of the
+    // arithmetic.
     const int n_it = (r1 - r0 + STEP - 1) / STEP;  // >= 1, uniform
-    // The scheduling barriers keep each buffer's loads together ahead of the
-    // other buffer's arithmetic (left alone, the compiler moves half of them
-    // behind the first wait).
-    for (int it = 0; it < n_it; it += 2) {
-      const int jb = r0 + it * STEP;
-      issue(kb, vb, jb + STEP);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(ka, va, jb);
-      issue(ka, va, jb + 2 * STEP);
-      __builtin_amdgcn_sched_barrier(0);
-      if (it + 1 < n_it) compute(kb, vb, jb + STEP);
+    for (int it = 0; it < n_it; it += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        issue(kbuf[(k + NBUF - 1) % NBUF], vbuf[(k + NBUF - 1) % NBUF],
+              r0 + (it + k + NBUF - 1) * STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k == 0 || it + k < n_it) compute(kbuf[k], vbuf[k], r0 + (it + k) * STEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
   // Merge of the workgroup's row slots through LDS: each lane group writes its
-  // state once, then every thread sums its outputs over the slots with the
-  // weights 2^(m_slot - M).  (A tree of lane exchanges costs about a thousand
+  // state once, lane reductions turn the slot maxima into weights 2^(m_slot -
+  // M), then every thread sums two columns over the slots.  (A tree of lane exchanges costs about a thousand
   // vector instructions per lane for 4 heads x 16 elements, more than a short
   // chunk's whole stream.)
   if (sub == 0) {
@@ -276,27 +301,44 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
           make_float4(acc[g][8 * h + 4], acc[g][8 * h + 5], acc[g][8 * h + 6], acc[g][8 * h + 7]);
     }
   __syncthreads();
-  // slot weights: thread (s, g) -> sm_w[s][g] = 2^(m_s - M_g), sm_M[g] = M_g
-  for (int t = threadIdx.x; t < SLOTS * G; t += kAttnThreads) {
-    const int s2 = t / G, g = t - s2 * G;
-    float M = kNoRow;
-#pragma unroll 8
-    for (int s3 = 0; s3 < SLOTS; ++s3) M = fmaxf(M, sm_m[s3][g]);
-    sm_w[s2][g] = exp2_raw(sm_m[s2][g] - M);
-    if (s2 == 0) sm_M[g] = M;
+  // slot weights: lane group g of SLOTS threads holds slot s = t % SLOTS of
+  // head g; lane reductions give M_g = max_s m_s and L_g = sum_s l_s 2^(m_s - M_g)
+  {
+    const int t = threadIdx.x;
+    if (t < G * SLOTS) {  // whole lane groups
+      const int g = t / SLOTS, s2 = t - g * SLOTS;
+      const float ms = sm_m[s2][g];
+      const float M = slot_max<SLOTS>(ms);
+      const float w = exp2_raw(ms - M);
+      const float L = slot_sum<SLOTS>(sm_l[s2][g] * w);
+      sm_w[g][s2] = w;
+      if (s2 == 0) {
+        sm_M[g] = M;
+        sm_L[g] = L;
+      }
+    }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < G * DH; t += kAttnThreads) {
-    const int g = t / DH, c = t - g * DH;
-    float A = 0.f;
-#pragma unroll 8
-    for (int s2 = 0; s2 < SLOTS; ++s2) A = fmaf(sm_acc[s2][g][c], sm_w[s2][g], A);
+  // outputs: two adjacent columns of one head per thread, four slot weights
+  // per LDS read
+  for (int o = threadIdx.x; o < G * DH / 2; o += kAttnThreads) {
+    const int g = o / (DH / 2), c = 2 * (o - g * (DH / 2));
+    float A0 = 0.f, A1 = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < SLOTS; s4 += 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&sm_w[g][s4]);
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float2 a = *reinterpret_cast<const float2*>(&sm_acc[s4 + k][g][c]);
+        A0 = fmaf(a.x, wv[k], A0);
+        A1 = fmaf(a.y, wv[k], A1);
+      }
+    }
     const size_t hs = ((size_t)seq * h_q + kv * G + g) * n_splits + split;
-    pacc[hs * DH + c] = A;
+    *reinterpret_cast<float2*>(pacc + hs * DH + c) = make_float2(A0, A1);
     if (c == 0) {
-      float L = 0.f;
-#pragma unroll 8
-      for (int s2 = 0; s2 < SLOTS; ++s2) L = fmaf(sm_l[s2][g], sm_w[s2][g], L);
+      const float L = sm_L[g];
       pm[hs] = L > 0.f ? sm_M[g] : -INFINITY;  // a split without rows: (-inf, 0, 0)
       pl[hs] = L;
     }
@@ -400,7 +442,8 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
 #define SD_ATTN_M(GG, UU, EE, MM)                                                           \
-  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU, EE, MM>, grid, dim3(kAttnThreads), 0, \
+  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU, EE, MM, kAttnBufs>, grid,            \
+                dim3(kAttnThreads), 0,                                                        \
                 s, a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, starts,   \
                 a.batched, a.bt, a.h_q, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
 #define SD_ATTN_G(GG, UU, EE)                  \
