@@ -38,7 +38,7 @@ size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 struct Layout {
   size_t q, attn, pm, pl, pacc, act, hmid, keep, mlp_part, teal_part, lse_part, lse, scores;
   size_t teal_part_floats;
-  size_t kth_hist, kth_state, total;
+  size_t kth_hist, kth_state, topk, total;
   int max_splits, sel_chunks;
 };
 
@@ -81,6 +81,7 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.scores = take(hq * (size_t)max_rows * 4);  // masked comparison path: [h_q, rows]
   L.kth_hist = take(256 * 4);
   L.kth_state = take(16);
+  L.topk = take(sd::topk_ws_words((int)hkv) * 4);
   L.total = off;
   return L;
 }
@@ -326,6 +327,7 @@ sd_status sd_select_kv(const sd_dims* dims, const void* k_full, const void* v_fu
   a.n_chunks = L.sel_chunks;
   a.lse_part = reinterpret_cast<float*>(wsb + L.lse_part);
   a.lse = reinterpret_cast<float*>(wsb + L.lse);
+  a.topk_ws = reinterpret_cast<unsigned*>(wsb + L.topk);
   a.skip_scoring = scores_in;
   sd::launch_select(a, dims->kv_dtype, static_cast<hipStream_t>(stream));
   return check_launch("sd_select_kv");
@@ -405,6 +407,7 @@ sd_status sd_select_kv_ragged(const sd_dims* dims, const void* k_full, const voi
   a.n_chunks = L.sel_chunks;
   a.lse_part = reinterpret_cast<float*>(wsb + L.lse_part);
   a.lse = reinterpret_cast<float*>(wsb + L.lse);
+  a.topk_ws = reinterpret_cast<unsigned*>(wsb + L.topk);
   a.skip_scoring = scores_in;
   a.ragged = 1;
   a.k_heads = kh;

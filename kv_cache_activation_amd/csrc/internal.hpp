@@ -175,7 +175,12 @@ struct SelectArgs {
   int ragged;        // per-head budgets k_heads (k_keep unused), idx rows of idx_stride
   HeadInts k_heads;
   int idx_stride;
+  unsigned* topk_ws; // chunked top-k: topk_ws_words(h_kv) words, or null for one workgroup per head
 };
+
+// Chunked top-k over long contexts: at most kTopkMaxChunks chunks per KV head.
+constexpr int kTopkMaxChunks = 64;
+inline size_t topk_ws_words(int h_kv) { return (size_t)h_kv * (kTopkMaxChunks * (256 + 2) + 2); }
 
 // Batched decode (nb sequences sharing the weight reads): the sequences'
 // positions and caches, passed by value.

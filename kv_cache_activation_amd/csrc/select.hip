@@ -610,6 +610,177 @@ __global__ void sel_gather_kernel(const KT* __restrict__ K, const KT* __restrict
   *vd = *vs;
 }
 
+// ------------------------------------------------------------------ chunked top-k
+// The same selection (m largest candidate keys, ties to the lower position,
+// ascending list with the forced rows) spread over C chunks of kTopkChunk
+// positions per KV head, for long contexts where one workgroup per head
+// leaves the chip nearly idle.  Four digit passes, each a chunk histogram
+// launch and a per-head pick launch (state[kv] = (prefix, need)); then each
+// chunk counts what it keeps, and each chunk emits its part of the list at
+// the offset that the counts of the chunks before it give (ties go to the
+// first `need` equal candidates in position order, chunk by chunk).
+constexpr int kTopkChunk = 4096;
+
+__device__ __forceinline__ int topk_budget(int ragged, const HeadInts& k_heads, int k_keep_all,
+                                           int kv) {
+  return ragged ? k_heads.v[kv & (kMaxKvHeads - 1)] : k_keep_all;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void sel_topk_hist_kernel(
+    const float* __restrict__ scores, int n, int w, int n_sink, int k_keep_all, int ragged,
+    HeadInts k_heads, int pass, const unsigned* __restrict__ state, unsigned* __restrict__ hist) {
+  __shared__ unsigned h[256];
+  const int ch = blockIdx.x, kv = blockIdx.y, C = gridDim.x;
+  const float* S = scores + (size_t)kv * n;
+  const int k_keep = topk_budget(ragged, k_heads, k_keep_all, kv);
+  const int m = k_keep - n_sink - w;
+  for (int b = threadIdx.x; b < 256; b += kTopkThreads) h[b] = 0u;
+  __syncthreads();
+  if (k_keep < n && m > 0) {  // workgroup-uniform
+    const int shift = 24 - 8 * pass;
+    const unsigned prefix = pass ? state[2 * kv] : 0u;
+    const int c0 = max(n_sink, ch * kTopkChunk), c1 = min(n - w, (ch + 1) * kTopkChunk);
+    constexpr int HU = kTopkChunk / kTopkThreads;  // keys per thread, all in flight
+    if (c0 < c1) {
+      unsigned key[HU];
+#pragma unroll
+      for (int u = 0; u < HU; ++u)
+        key[u] = order_key(S[min(c0 + (int)threadIdx.x + kTopkThreads * u, c1 - 1)]);
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+        const int j = c0 + (int)threadIdx.x + kTopkThreads * u;
+        const bool match =
+            j < c1 && (pass == 0 || (key[u] >> (shift + 8)) == (prefix >> (shift + 8)));
+        if (match) atomicAdd(&h[(key[u] >> shift) & 255u], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  unsigned* out = hist + ((size_t)kv * C + ch) * 256;
+  for (int b = threadIdx.x; b < 256; b += kTopkThreads) out[b] = h[b];
+}
+
+__global__ __launch_bounds__(256) void sel_topk_pick_kernel(int n, int w, int n_sink,
+                                                            int k_keep_all, int ragged,
+                                                            HeadInts k_heads, int pass, int C,
+                                                            unsigned* __restrict__ state,
+                                                            const unsigned* __restrict__ hist) {
+  __shared__ unsigned tot[256];
+  const int kv = blockIdx.x, b = threadIdx.x;
+  const int k_keep = topk_budget(ragged, k_heads, k_keep_all, kv);
+  const int m = k_keep - n_sink - w;
+  if (k_keep >= n || m <= 0) return;  // workgroup-uniform; the count kernel does not read state
+  unsigned sum = 0u;
+  for (int c = 0; c < C; ++c) sum += hist[((size_t)kv * C + c) * 256 + b];
+  tot[b] = sum;
+  __syncthreads();
+  if (b == 0) {
+    const int shift = 24 - 8 * pass;
+    const unsigned prefix = pass ? state[2 * kv] : 0u;
+    const unsigned need = pass ? state[2 * kv + 1] : (unsigned)m;
+    unsigned above = 0;
+    int bb = 255;
+    for (; bb > 0; --bb) {
+      if (above + tot[bb] >= need) break;
+      above += tot[bb];
+    }
+    state[2 * kv] = prefix | ((unsigned)bb << shift);
+    state[2 * kv + 1] = need - above;
+  }
+}
+
+// COUNT: write (kept-above-T plus forced, equal-to-T candidates) of the chunk.
+// !COUNT: emit the chunk's part of the ascending list.
+template <bool COUNT>
+__global__ __launch_bounds__(kTopkThreads) void sel_topk_chunk_kernel(
+    const float* __restrict__ scores, int n, int w, int n_sink, int k_keep_all, int ragged,
+    HeadInts k_heads, int stride, const unsigned* __restrict__ state, int* __restrict__ counts,
+    int32_t* __restrict__ idx) {
+  __shared__ int wave_tot[kTopkWaves];
+  __shared__ int sh_pos, sh_ties;
+  const int ch = blockIdx.x, kv = blockIdx.y, C = gridDim.x;
+  const float* S = scores + (size_t)kv * n;
+  const int k_keep = topk_budget(ragged, k_heads, k_keep_all, kv);
+  int32_t* out = idx + (size_t)kv * stride;
+  const int q0 = ch * kTopkChunk, q1 = min(n, q0 + kTopkChunk);
+  if (k_keep >= n) {  // identity selection
+    if (!COUNT)
+      for (int j = q0 + threadIdx.x; j < q1; j += kTopkThreads) out[j] = j;
+    return;
+  }
+  const int m = k_keep - n_sink - w;
+  const int c0 = n_sink, c1 = n - w;
+  const unsigned T = m > 0 ? state[2 * kv] : 0u;
+  const int need = m > 0 ? (int)state[2 * kv + 1] : 0;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  // one 64-position block per wave and step (the chunk is 4096 positions: 4 blocks per wave)
+  constexpr int EU = kTopkChunk / kTopkThreads;
+  const int p0 = q0 + wave * kWave * EU;
+  auto key_at = [&](int j) { return order_key(S[min(j, n - 1)]); };
+  unsigned kk[EU];
+#pragma unroll
+  for (int u = 0; u < EU; ++u) kk[u] = key_at(p0 + kWave * u + lane);
+  int n_take = 0, n_eq = 0;  // wave totals (uniform)
+#pragma unroll
+  for (int u = 0; u < EU; ++u) {
+    const int j = p0 + kWave * u + lane;
+    const bool valid = j < q1;
+    const bool forced = valid && (j < c0 || j >= c1);
+    const bool cand = valid && !forced && m > 0;
+    n_take += __popcll(__ballot(forced || (cand && kk[u] > T)));
+    n_eq += __popcll(__ballot(cand && kk[u] == T));
+  }
+  if (COUNT) {
+    int take_total, eq_total;
+    (void)block_excl_sum(lane == 0 ? n_take : 0, wave_tot, take_total);
+    (void)block_excl_sum(lane == 0 ? n_eq : 0, wave_tot, eq_total);
+    if (threadIdx.x == 0) {
+      counts[2 * ((size_t)kv * C + ch)] = take_total;
+      counts[2 * ((size_t)kv * C + ch) + 1] = eq_total;
+    }
+    return;
+  }
+  // this chunk's list offset and ties from the chunks before it
+  if (threadIdx.x == 0) {
+    int pos = 0, eq_before = 0;
+    for (int c = 0; c < ch; ++c) {
+      const int take_c = counts[2 * ((size_t)kv * C + c)], eq_c = counts[2 * ((size_t)kv * C + c) + 1];
+      pos += take_c + max(0, min(eq_c, need - eq_before));
+      eq_before += eq_c;
+    }
+    sh_pos = pos;
+    sh_ties = max(0, need - eq_before);  // ties still to keep, this chunk first
+  }
+  __syncthreads();
+  const int chunk_ties = sh_ties;
+  int eq_total;
+  const int eq_before = block_excl_sum(lane == 0 ? n_eq : 0, wave_tot, eq_total);
+  const int eq_wave = __shfl(eq_before, 0);
+  const int ties = max(0, min(n_eq, chunk_ties - eq_wave));  // ties this wave keeps
+  int take_total;
+  const int pos_before = block_excl_sum(lane == 0 ? n_take + ties : 0, wave_tot, take_total);
+  int pos = sh_pos + __shfl(pos_before, 0), eq_seen = 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < EU; ++u) {
+    const int j = p0 + kWave * u + lane;
+    const bool valid = j < q1;
+    const bool forced = valid && (j < c0 || j >= c1);
+    const bool cand = valid && !forced && m > 0;
+    const bool eq = cand && kk[u] == T;
+    const unsigned long long eqm = __ballot(eq);
+    const bool take = forced || (cand && kk[u] > T) ||
+                      (eq && eq_seen + __popcll(eqm & below) < ties);
+    const unsigned long long tm = __ballot(take);
+    if (take) {
+      const int p = pos + __popcll(tm & below);
+      if (p < k_keep) out[p] = j;  // p < k_keep always; guard anyway
+    }
+    pos += __popcll(tm);
+    eq_seen += __popcll(eqm);
+  }
+}
+
 template <typename KT, int DH>
 static void select_typed(const SelectArgs& a, hipStream_t s) {
   const int G = a.h_q / a.h_kv;
@@ -648,9 +819,31 @@ static void select_typed(const SelectArgs& a, hipStream_t s) {
     }
   }
   const int stride = a.ragged ? a.idx_stride : k_eff;
-  launch_kernel(K_SEL_TOPK, sel_topk_kernel, dim3(a.h_kv), dim3(kTopkThreads), 0, s,
-                (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.ragged, a.k_heads, stride,
-                a.idx);
+  const int C = (a.n + kTopkChunk - 1) / kTopkChunk;
+  if (C <= 2 || C > kTopkMaxChunks || !a.topk_ws) {
+    launch_kernel(K_SEL_TOPK, sel_topk_kernel, dim3(a.h_kv), dim3(kTopkThreads), 0, s,
+                  (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.ragged, a.k_heads,
+                  stride, a.idx);
+  } else {
+    // workspace: hist [h_kv, C, 256], counts [h_kv, C, 2], state [h_kv, 2]
+    unsigned* hist = a.topk_ws;
+    int* counts = reinterpret_cast<int*>(hist + (size_t)a.h_kv * kTopkMaxChunks * 256);
+    unsigned* state = reinterpret_cast<unsigned*>(counts + (size_t)a.h_kv * kTopkMaxChunks * 2);
+    for (int pass = 0; pass < 4; ++pass) {
+      launch_kernel(K_SEL_TOPK, sel_topk_hist_kernel, dim3(C, a.h_kv), dim3(kTopkThreads), 0, s,
+                    (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.ragged, a.k_heads,
+                    pass, (const unsigned*)state, hist);
+      launch_kernel(K_SEL_TOPK, sel_topk_pick_kernel, dim3(a.h_kv), dim3(256), 0, s, a.n, a.w,
+                    a.n_sink, a.k_keep, a.ragged, a.k_heads, pass, C, state,
+                    (const unsigned*)hist);
+    }
+    launch_kernel(K_SEL_TOPK, sel_topk_chunk_kernel<true>, dim3(C, a.h_kv), dim3(kTopkThreads), 0,
+                  s, (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.ragged, a.k_heads,
+                  stride, (const unsigned*)state, counts, a.idx);
+    launch_kernel(K_SEL_TOPK, sel_topk_chunk_kernel<false>, dim3(C, a.h_kv), dim3(kTopkThreads),
+                  0, s, (const float*)a.scores, a.n, a.w, a.n_sink, a.k_keep, a.ragged, a.k_heads,
+                  stride, (const unsigned*)state, counts, a.idx);
+  }
   constexpr int P = DH * (int)sizeof(KT) / 16;
   dim3 ggrid((k_max * P + 255) / 256, a.h_kv);
   launch_kernel(K_SEL_GATHER, sel_gather_kernel<KT, DH>, ggrid, dim3(256), 0, s, k,

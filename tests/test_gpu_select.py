@@ -91,6 +91,47 @@ def test_topk_ties_go_to_lower_position(levels):
     assert np.array_equal(idx, osel.select_indices(scores, 3000, wl.window, wl.n_sink, 700))
 
 
+# Long contexts use the chunked top-k (chunks of 4096 positions, several
+# workgroups per KV head); these cases span chunk boundaries, a ragged last
+# chunk, ties across chunks, and the degenerate budgets.
+@pytest.mark.parametrize("n,w,n_sink,k_keep", [(9000, 32, 4, 1000), (20000, 32, 4, 3000),
+                                               (40961, 64, 0, 4097), (16384, 32, 4, 36),
+                                               (12289, 1, 1, 12000), (131072, 32, 4, 13107)])
+def test_chunked_topk_bit_exact_on_oracle_scores(n, w, n_sink, k_keep):
+    wl, k, v, _, cap = _tiny(n)
+    r = np.random.default_rng(n + k_keep)
+    scores = r.random((wl.n_kv_heads, n)).astype(np.float32)
+    s = Sel(wl, k, v, n, cap, k_keep)
+    _, idx = s.run(scores_in=scores, w=w, n_sink=n_sink)
+    assert np.array_equal(idx, osel.select_indices(scores, n, w, n_sink, k_keep))
+
+
+@pytest.mark.parametrize("levels", [1, 2, 7, 1000])
+def test_chunked_topk_ties_go_to_lower_position(levels):
+    n, k_keep = 20000, 5000
+    wl, k, v, _, cap = _tiny(n)
+    r = np.random.default_rng(100 + levels)
+    scores = (r.integers(0, levels, (wl.n_kv_heads, n)) * 0.25).astype(np.float32)
+    scores[0, 4000:4200] = -0.0    # signed zeros across a chunk boundary
+    s = Sel(wl, k, v, n, cap, k_keep)
+    _, idx = s.run(scores_in=scores)
+    assert np.array_equal(idx, osel.select_indices(scores, n, wl.window, wl.n_sink, k_keep))
+
+
+def test_chunked_topk_identity_and_all_equal():
+    n = 9000
+    wl, k, v, _, cap = _tiny(n)
+    s = Sel(wl, k, v, n, cap, n)
+    _, idx = s.run(scores_in=np.zeros((wl.n_kv_heads, n), np.float32))
+    assert np.array_equal(idx, np.tile(np.arange(n, dtype=np.int32), (wl.n_kv_heads, 1)))
+    s2 = Sel(wl, k, v, n, cap, 1000)
+    _, idx2 = s2.run(scores_in=np.full((wl.n_kv_heads, n), 0.5, np.float32))
+    m = 1000 - wl.n_sink - wl.window
+    want = list(range(wl.n_sink)) + list(range(wl.n_sink, wl.n_sink + m)) + \
+        list(range(n - wl.window, n))
+    assert idx2.tolist() == [want] * wl.n_kv_heads
+
+
 def test_gather_copies_selected_rows_exactly():
     wl, k, v, qw, cap = _tiny()
     s = Sel(wl, k, v, 2048, cap, wl.k_keep)
