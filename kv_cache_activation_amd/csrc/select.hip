@@ -266,22 +266,29 @@ __device__ __forceinline__ void sel_split3(const float (&x)[8], u32x4& hi, u32x4
   lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
-// Logits of one 16-query tile (rows of qs starting at qrow) against the
-// wave's four 16-key tiles: z[c][r] for query 4 (l / 16) + r of the tile and
-// key column l % 16 of key tile c.
+// Staged queries on the matrix-core path: the three bf16 parts (hi, mid, lo)
+// of kSelQB query rows, part p of row r at qp[(p kSelQB + r) QS + dim], rows
+// padded to QS = DH + 8 elements (16-byte aligned rows, reads spread over the
+// LDS banks).
 template <int DH>
-__device__ __forceinline__ void sel_tile_logits(const float* qs, int qrow,
+constexpr int sel_qs() { return DH + 8; }
+
+// Logits of one 16-query tile (staged rows from qrow) against the wave's four
+// 16-key tiles: z[c][r] for query 4 (l / 16) + r of the tile and key column
+// l % 16 of key tile c.  The A operands are the staged parts, read as is.
+template <int DH>
+__device__ __forceinline__ void sel_tile_logits(const bf16_t* qp, int qrow,
                                                 const u32x4 (&kf)[4][DH / 32], f32x4 (&z)[4]) {
-  constexpr int NS = DH / 32;
+  constexpr int NS = DH / 32, QS = sel_qs<DH>();
   const int lane = lane_id();
 #pragma unroll
   for (int c = 0; c < 4; ++c) z[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    float xv[8];
-    load8f(qs + (qrow + lane % 16) * (DH + 4) + 32 * st + 8 * (lane / 16), xv);
-    u32x4 ah, am, al;
-    sel_split3(xv, ah, am, al);
+    const bf16_t* base = qp + (qrow + lane % 16) * QS + 32 * st + 8 * (lane / 16);
+    const u32x4 ah = *reinterpret_cast<const u32x4*>(base);
+    const u32x4 am = *reinterpret_cast<const u32x4*>(base + kSelQB * QS);
+    const u32x4 al = *reinterpret_cast<const u32x4*>(base + 2 * kSelQB * QS);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(ah), sel_as_bf16x8(kf[c][st]),
@@ -309,23 +316,33 @@ __device__ __forceinline__ void sel_load_keys(const bf16_t* __restrict__ Kh, int
   }
 }
 
-// Stage queries [qb, qb + kSelQB) of KV head kv (rows padded by 4 floats).
+// Stage queries [qb, qb + kSelQB) of KV head kv as their three bf16 parts
+// (split once per staging, not once per key chunk and wave).
 template <int DH>
-__device__ void sel_stage_q(const float* __restrict__ q_win, int kv, int Q, int qb, float* qs) {
+__device__ void sel_stage_q(const float* __restrict__ q_win, int kv, int Q, int qb, bf16_t* qp) {
+  constexpr int QS = sel_qs<DH>();
   const float* src = q_win + (size_t)kv * Q * DH;
-  for (int t = threadIdx.x; t < kSelQB * DH / 4; t += kSelThreads) {
-    const int qq = t / (DH / 4), c4 = t - qq * (DH / 4);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (qb + qq < Q) v = reinterpret_cast<const float4*>(src + (size_t)(qb + qq) * DH)[c4];
-    *reinterpret_cast<float4*>(qs + qq * (DH + 4) + 4 * c4) = v;
+  for (int t = threadIdx.x; t < kSelQB * DH / 8; t += kSelThreads) {
+    const int qq = t / (DH / 8), c8 = t - qq * (DH / 8);
+    float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (qb + qq < Q) load8f(src + (size_t)(qb + qq) * DH + 8 * c8, xv);
+    u32x4 hi, mid, lo;
+    sel_split3(xv, hi, mid, lo);
+    bf16_t* dst = qp + qq * QS + 8 * c8;
+    *reinterpret_cast<u32x4*>(dst) = hi;
+    *reinterpret_cast<u32x4*>(dst + kSelQB * QS) = mid;
+    *reinterpret_cast<u32x4*>(dst + 2 * kSelQB * QS) = lo;
   }
 }
+
+// Raw v_exp_f32 (2^x, -inf -> 0); its arguments here are at most 0.
+__device__ __forceinline__ float sel_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int DH>
 __global__ __launch_bounds__(kSelThreads) void sel_lse_partial_mfma_kernel(
     const bf16_t* __restrict__ K, int cap, int n, const float* __restrict__ q_win, int w, int G,
     float scale_log2, int n_chunks, float* __restrict__ lse_part) {
-  __shared__ __align__(16) float qs[kSelQB * (DH + 4)];
+  __shared__ __align__(16) bf16_t qs[3 * kSelQB * sel_qs<DH>()];
   __shared__ float red_m[kSelWaves][kSelQB], red_l[kSelWaves][kSelQB];
   const int kv = blockIdx.y;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -360,7 +377,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_lse_partial_mfma_kernel(
         mx = group_max<16>(mx);
         float e = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) e += zz[c] == -INFINITY ? 0.f : exp2f(zz[c] - mx);
+        for (int c = 0; c < 4; ++c) e += zz[c] == -INFINITY ? 0.f : sel_exp2(zz[c] - mx);
         e = group_sum<16>(e);
         if (lane % 16 == 0) {
           red_m[wave][ql] = mx;
@@ -377,7 +394,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_lse_partial_mfma_kernel(
       float L = 0.f;
 #pragma unroll
       for (int v = 0; v < kSelWaves; ++v)
-        if (red_m[v][ql] != -INFINITY) L = fmaf(red_l[v][ql], exp2f(red_m[v][ql] - M), L);
+        if (red_m[v][ql] != -INFINITY) L = fmaf(red_l[v][ql], sel_exp2(red_m[v][ql] - M), L);
       float* o = lse_part + (((size_t)kv * n_chunks + chunk) * Q + qb + ql) * 2;
       o[0] = M;
       o[1] = L;
@@ -391,7 +408,7 @@ template <int DH>
 __global__ __launch_bounds__(kSelThreads) void sel_score_mfma_kernel(
     const bf16_t* __restrict__ K, int cap, int n, const float* __restrict__ q_win, int w, int G,
     float scale_log2, const float* __restrict__ lse, float* __restrict__ scores) {
-  __shared__ __align__(16) float qs[kSelQB * (DH + 4)];
+  __shared__ __align__(16) bf16_t qs[3 * kSelQB * sel_qs<DH>()];
   __shared__ float ls[kSelQB];
   const int kv = blockIdx.y;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -424,7 +441,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_score_mfma_kernel(
         for (int r = 0; r < 4; ++r) {
           const int ql = 16 * rt + 4 * (lane / 16) + r, q = qb + ql;
           const bool vis = q < Q && j < n && j <= n - w + q % w;
-          part += vis ? exp2f(z[c][r] * scale_log2 - ls[ql]) : 0.f;
+          part += vis ? sel_exp2(z[c][r] * scale_log2 - ls[ql]) : 0.f;
         }
         // add the four row groups of the column (lanes l, l ^ 16, l ^ 32, l ^ 48)
         part += xor_lanes<16>(part);
