@@ -347,17 +347,18 @@ __global__ __launch_bounds__(kSelThreads) void sel_lse_partial_mfma_kernel(
   const int kv = blockIdx.y;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int Q = G * w;
-  for (int qb = 0; qb < Q; qb += kSelQB) {
-    __syncthreads();
-    sel_stage_q<DH>(q_win, kv, Q, qb, qs);
-    __syncthreads();
 #pragma unroll 1
   for (int sub = 0; sub < kSelSub; ++sub) {
     const int chunk = blockIdx.x * kSelSub + sub;
     if (chunk >= n_chunks) break;  // workgroup-uniform
     const int j0 = chunk * kSelThreads + wave * 64;
+    // the chunk's keys once, for every query batch
     u32x4 kf[4][DH / 32];
     sel_load_keys<DH>(K + (size_t)kv * cap * DH, n, j0, kf);
+  for (int qb = 0; qb < Q; qb += kSelQB) {
+    __syncthreads();
+    sel_stage_q<DH>(q_win, kv, Q, qb, qs);
+    __syncthreads();
 #pragma unroll 1
     for (int rt = 0; rt < kSelQB / 16; ++rt) {
       f32x4 z[4];
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_lse_partial_mfma_kernel(
       o[0] = M;
       o[1] = L;
     }
-    __syncthreads();  // red_m / red_l are reused by the next chunk
+    __syncthreads();  // red_m / red_l are reused by the next query batch
   }
   }
 }
@@ -682,27 +683,43 @@ __global__ __launch_bounds__(256) void sel_topk_pick_kernel(int n, int w, int n_
                                                             HeadInts k_heads, int pass, int C,
                                                             unsigned* __restrict__ state,
                                                             const unsigned* __restrict__ hist) {
-  __shared__ unsigned tot[256];
-  const int kv = blockIdx.x, b = threadIdx.x;
+  __shared__ unsigned binv[256], sfx[257], wave_sum_s[4];
+  const int kv = blockIdx.x, t = threadIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
   const int k_keep = topk_budget(ragged, k_heads, k_keep_all, kv);
   const int m = k_keep - n_sink - w;
   if (k_keep >= n || m <= 0) return;  // workgroup-uniform; the count kernel does not read state
-  unsigned sum = 0u;
-  for (int c = 0; c < C; ++c) sum += hist[((size_t)kv * C + c) * 256 + b];
-  tot[b] = sum;
+  // bin t's total over the chunks, eight loads in flight at a time
+  const unsigned* hb = hist + (size_t)kv * C * 256 + t;
+  unsigned part[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  for (int c0 = 0; c0 < C; c0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < C) part[u] += hb[(size_t)(c0 + u) * 256];
+  }
+  unsigned tot = 0u;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) tot += part[u];
+  binv[t] = tot;
   __syncthreads();
-  if (b == 0) {
-    const int shift = 24 - 8 * pass;
-    const unsigned prefix = pass ? state[2 * kv] : 0u;
-    const unsigned need = pass ? state[2 * kv + 1] : (unsigned)m;
-    unsigned above = 0;
-    int bb = 255;
-    for (; bb > 0; --bb) {
-      if (above + tot[bb] >= need) break;
-      above += tot[bb];
-    }
-    state[2 * kv] = prefix | ((unsigned)bb << shift);
-    state[2 * kv + 1] = need - above;
+  // suffix sums: thread t scans bin 255 - t, so its inclusive prefix is
+  // S(255 - t) = candidates in bins >= 255 - t
+  const int incl = wave_incl_scan((int)binv[255 - t]);
+  if (lane == kWave - 1) wave_sum_s[wave] = (unsigned)incl;
+  __syncthreads();
+  unsigned before = 0u;
+  for (int v = 0; v < wave; ++v) before += wave_sum_s[v];
+  sfx[255 - t] = before + (unsigned)incl;
+  if (t == 0) sfx[256] = 0u;
+  __syncthreads();
+  // the digit is the highest bin bb (bb >= 1) with S(bb) >= need, else 0;
+  // above = S(bb + 1).  S is non-increasing, so exactly one thread matches.
+  const unsigned prefix = pass ? state[2 * kv] : 0u;
+  const unsigned need = pass ? state[2 * kv + 1] : (unsigned)m;
+  const int bb = t;
+  const bool here = bb >= 1 ? (sfx[bb] >= need && sfx[bb + 1] < need) : (sfx[1] < need);
+  if (here) {
+    state[2 * kv] = prefix | ((unsigned)bb << (24 - 8 * pass));
+    state[2 * kv + 1] = need - sfx[bb + 1];
   }
 }
 
