@@ -104,7 +104,7 @@ struct DownArgs {
 // RMSNorm) of x_j w_t[j], w_t [d_in, d_out]; P slices of the kept list (each
 // at most kTealList channels) x column tiles of 4096 outputs.
 constexpr int kTealList = 64;
-constexpr int kTealMinBlocks = 256;  // slices x tiles, at least
+constexpr int kTealMinBlocks = 64;   // slices x tiles, at least (measured: 64 beats 128 and 256)
 constexpr int kTealMaxParts = 512;   // d_in <= kTealList * kTealMaxParts
 struct TealGrid {
   int parts, tiles;
