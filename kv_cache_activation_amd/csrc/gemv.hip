@@ -27,6 +27,19 @@ namespace sd {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+// Workgroup size of the d = 4096 instances with bf16 weights.  Measured on
+// MI355X (32-layer composed step at 131072 context): 1024 threads for O, one
+// row per wave, stage its 16 KB input once per 16 rows instead of per 4
+// (7.0 vs 8.2 us per launch); QKV and gate + up were no faster that way.
+constexpr int kQkvWide = kThreads, kOWide = 1024, kGateWide = kThreads;
+
+// float4 chunks per thread when T threads stage a row of 512 NCH elements
+// (EXACT: no bounds tests)
+template <int T, int NCH>
+struct StageNV {
+  static constexpr int NV = (NCH * 128 + T - 1) / T;
+  static constexpr bool EXACT = (NCH * 128) % T == 0;
+};
 
 // Full dot product of a row with the LDS copy of x (every lane gets it).
 // FULL: d == 512 NCH.
@@ -95,8 +108,8 @@ __device__ __forceinline__ float stream_rows(const WT* __restrict__ W, int ld, i
 // when k_sel is given, at row row_sel of the gathered buffer.  A wave computes
 // both rows of the rotation pairs wave, wave + W, ... (W waves in the grid,
 // at most 32 pairs per wave); lane j then rotates and stores its j-th pair.
-template <typename WT, typename KT, int NCH, bool FULL>
-__global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
+template <typename WT, typename KT, int NCH, bool FULL, int T>
+__global__ __launch_bounds__(T) void qkv_rope_append_kernel(
     const float* __restrict__ h, const float* __restrict__ nw, float eps,
     const WT* __restrict__ W, int d, int h_q, int h_kv, int dh, RopeTable rope,
     float* __restrict__ q_out, KT* __restrict__ k_full, KT* __restrict__ v_full, int cap_full,
@@ -105,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
   const int half = dh >> 1;
   const int d8 = d >> 3;
   const int n_pairs = (h_q + 2 * h_kv) * half;
-  const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const int n_waves = gridDim.x * kWavesPerBlock;
+  const int wave = blockIdx.x * (T / kWave) + threadIdx.x / kWave;
+  const int n_waves = gridDim.x * (T / kWave);
   const int lane = lane_id();
   const int my_pairs = wave < n_pairs ? (n_pairs - wave + n_waves - 1) / n_waves : 0;
   // row k of this wave: pair wave + (k / 2) W, first (k even) or second row
@@ -116,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
     return head * dh + i + (k & 1) * half;
   };
   extern __shared__ float xs[];
-  XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), true> st;
+  XStage<T, StageNV<T, NCH>::NV, FULL && StageNV<T, NCH>::EXACT, true> st;
   st.load(h, nw, d);  // x first: the staging then waits for it alone
   // the first pair's rows are in flight during the staging (a wave without
   // pairs, only when waves outnumber pairs, reads pair 0 and drops it: no
@@ -177,17 +190,17 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_append_kernel(
 // ------------------------------------------------------------------ O
 // h[r] += W_o[r] . attn  (residual add; attn is the attention output).  ONE:
 // the grid has a wave per row (no second row buffer: more waves fit).
-template <typename WT, int NCH, bool FULL, bool ONE>
-__global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __restrict__ attn,
+template <typename WT, int NCH, bool FULL, bool ONE, int T>
+__global__ __launch_bounds__(T) void o_residual_kernel(const float* __restrict__ attn,
                                                               const WT* __restrict__ W, int din,
                                                               int dout, float* __restrict__ h) {
   const int d8 = din >> 3;
-  const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const int n_waves = gridDim.x * kWavesPerBlock;
+  const int wave = blockIdx.x * (T / kWave) + threadIdx.x / kWave;
+  const int n_waves = gridDim.x * (T / kWave);
   const int lane = lane_id();
   const int n = wave < dout ? (dout - wave + n_waves - 1) / n_waves : 0;  // <= 64
   extern __shared__ float xs[];
-  XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), false> st;
+  XStage<T, StageNV<T, NCH>::NV, FULL && StageNV<T, NCH>::EXACT, false> st;
   st.load(attn, nullptr, din);  // x first: the staging then waits for it alone
   Row<WT, NCH> ra, rb;  // rb unused (no registers) when ONE
   load_row<FULL>(ra, W, din, n > 0 ? wave : 0, d8);  // no branch around the loads
@@ -216,8 +229,8 @@ __global__ __launch_bounds__(kThreads) void o_residual_kernel(const float* __res
 // dropped channel is left as it was and never read).  blockIdx.y selects one
 // of several input states (calibration); the calibration instance (CALIB)
 // only has a kernel name of its own.
-template <typename WT, int NCH, bool FULL, bool NORM, bool CALIB>
-__global__ __launch_bounds__(kThreads) void gate_kernel(
+template <typename WT, int NCH, bool FULL, bool NORM, bool CALIB, int T>
+__global__ __launch_bounds__(T) void gate_kernel(
     const float* __restrict__ xin, const float* __restrict__ nw, float eps,
     const WT* __restrict__ Wg, const WT* __restrict__ Wu, int d, int dff, float t, int gate_in,
     int store_abs, float* __restrict__ act, uint8_t* __restrict__ keep,
@@ -226,11 +239,11 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
   act += (size_t)blockIdx.y * dff;
   const int d8 = d >> 3;
   const int lane = lane_id();
-  const int wave = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const int n_waves = gridDim.x * kWavesPerBlock;
+  const int wave = blockIdx.x * (T / kWave) + threadIdx.x / kWave;
+  const int n_waves = gridDim.x * (T / kWave);
   const int n = wave < dff ? (dff - wave + n_waves - 1) / n_waves : 0;  // <= 64
   extern __shared__ float xs[];
-  XStage<kThreads, (NCH + 1) / 2, FULL && (NCH >= 2), NORM> st;
+  XStage<T, StageNV<T, NCH>::NV, FULL && StageNV<T, NCH>::EXACT, NORM> st;
   st.load(xin, nw, d);  // x first: the staging then waits for it alone
   Row<WT, NCH> ra, rb;
   if (!gate_in) load_row<FULL>(ra, Wg, d, n > 0 ? wave : 0, d8);  // in flight during the staging
@@ -280,8 +293,9 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
 // once (compute units x resident workgroups per unit, which the kernel's
 // register use decides), no more waves than work items, and at most
 // per_wave items per wave (a wave keeps one result per lane).
-template <typename K>
+template <int T, typename K>
 static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
+  constexpr int kWavesPerBlock = T / kWave;
   // resident workgroups per compute unit, per kernel and LDS size (queried once)
   static std::mutex mu;
   static std::map<std::pair<const void*, size_t>, int> cache;
@@ -292,7 +306,7 @@ static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
     auto it = cache.find(key);
     if (it == cache.end()) {
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, lds) != hipSuccess ||
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, T, lds) != hipSuccess ||
           nb < 1)
         nb = 1;
       it = cache.emplace(key, nb).first;
@@ -320,18 +334,19 @@ static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
     __VA_ARGS__;                                                                  \
   })
 
-template <typename K, typename... Args>
+template <int T, typename K, typename... Args>
 static void launch_rows(int kind, K kernel, int items, int per_wave, int grid_y, size_t lds,
                         hipStream_t s, Args... args) {
-  const int grid = gemv_grid(kernel, items, per_wave, lds);
-  launch_kernel(kind, kernel, dim3(grid, grid_y), dim3(kThreads), (uint32_t)lds, s, args...);
+  const int grid = gemv_grid<T>(kernel, items, per_wave, lds);
+  launch_kernel(kind, kernel, dim3(grid, grid_y), dim3(T), (uint32_t)lds, s, args...);
 }
 
 template <typename WT, typename KT>
 static void qkv_typed(const QkvArgs& a, hipStream_t s) {
   const int pairs = (a.h_q + 2 * a.h_kv) * a.dh / 2;
   const size_t lds = (size_t)a.d * sizeof(float);
-  SD_ROW_DISPATCH(a.d, launch_rows(K_QKV, qkv_rope_append_kernel<WT, KT, NCH, FULL>, pairs, kWave / 2,
+  SD_ROW_DISPATCH(a.d, constexpr int TH = (NCH == 8 && FULL && sizeof(WT) == 2) ? kQkvWide : kThreads;
+                  launch_rows<TH>(K_QKV, qkv_rope_append_kernel<WT, KT, NCH, FULL, TH>, pairs, kWave / 2,
                                    1, lds, s, a.h, a.norm, a.eps,
                                       (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
                                       (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full,
@@ -352,7 +367,8 @@ void launch_o(const float* attn, const void* w, int din, int dout, float* h, int
   // a wave per row while that fits the grid limit, else streamed rows
   const bool one = dout <= 4096 * kWavesPerBlock;
 #define SD_O(T, ONE_)                                                                          \
-  SD_ROW_DISPATCH(din, launch_rows(K_O, o_residual_kernel<T, NCH, FULL, ONE_>, dout,          \
+  SD_ROW_DISPATCH(din, constexpr int TH = (NCH == 8 && FULL && sizeof(T) == 2) ? kOWide : kThreads; \
+                  launch_rows<TH>(K_O, o_residual_kernel<T, NCH, FULL, ONE_, TH>, dout,       \
                                    ONE_ ? 1 : kWave, 1, lds, s, attn, (const T*)w, din, dout, h))
   if (w_dtype == 1) {
     if (one) {
@@ -374,7 +390,8 @@ void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s) {
   const size_t lds = (size_t)a.d * sizeof(float);
   // the calibration instance has a kernel name of its own
 #define SD_GATE_N(T, NRM, CAL)                                                               \
-  SD_ROW_DISPATCH(a.d, launch_rows(K_GATE_UP, gate_kernel<T, NCH, FULL, NRM, CAL>, a.dff, kWave,  \
+  SD_ROW_DISPATCH(a.d, constexpr int TH = (NCH == 8 && FULL && sizeof(T) == 2) ? kGateWide : kThreads; \
+                  launch_rows<TH>(K_GATE_UP, gate_kernel<T, NCH, FULL, NRM, CAL, TH>, a.dff, kWave, \
                                    a.n_states, lds, s, a.x, a.norm, a.eps,                    \
                                    (const T*)a.w_gate, (const T*)a.w_up, a.d, a.dff, a.t,     \
                                    a.gate_in, a.store_abs, a.act, a.keep, a.hmid))
