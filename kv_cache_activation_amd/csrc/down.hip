@@ -98,13 +98,21 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(
   const int P = gridDim.x;
   const int lo = (int)((int64_t)blockIdx.x * n_k / P);
   const int hi = (int)((int64_t)(blockIdx.x + 1) * n_k / P);
-  if (before < hi && before + cnt > lo) {
-    uint64_t bits = mask;
-    for (int r = before; bits; ++r) {
-      const int bit = __ffsll((unsigned long long)bits) - 1;
-      bits &= bits - 1;
+  // the slice's channels: each thread that holds part of it hands its mask to
+  // its whole wave (lane b takes bit b, ranked by a popcount), so a list entry
+  // costs one step instead of one iteration of a serial walk over the bits
+  uint64_t holders = __ballot(before < hi && before + cnt > lo);  // wave-uniform
+  while (holders) {
+    const int src = __ffsll((unsigned long long)holders) - 1;
+    holders &= holders - 1;
+    const uint32_t mlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mask, src);
+    const uint32_t mhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mask >> 32), src);
+    const uint64_t mk = ((uint64_t)mhi << 32) | mlo;
+    const int bf = __builtin_amdgcn_readlane(before, src);
+    if ((mk >> lane) & 1ull) {
+      const int r = bf + __popcll(mk & ((1ull << lane) - 1ull));
       if (r >= lo && r < hi) {
-        const int c = c0 + bit;
+        const int c = (wave * kWave + src) * chunk + lane;
         list[r - lo] = c;
         if (idx_out) idx_out[r] = c;
       }
