@@ -182,6 +182,8 @@ __global__ __launch_bounds__(kRedCols * kRedSlices) void mlp_reduce_kernel(
   __shared__ float red[kRedSlices][kRedCols];
   const int cl = threadIdx.x % kRedCols, sl = threadIdx.x / kRedCols;
   const int c = blockIdx.x * kRedCols + cl;
+  // the value accumulated into, read with the partials rather than after them
+  const float y_old = accumulate && sl == 0 && c < d ? y[c] : 0.f;
   const int per = (P + kRedSlices - 1) / kRedSlices;
   const int w0 = sl * per;
   float v[kRedPer];
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(kRedCols * kRedSlices) void mlp_reduce_kernel(
     float t = 0.f;
 #pragma unroll
     for (int s = 0; s < kRedSlices; ++s) t += red[s][cl];
-    y[c] = accumulate ? y[c] + t : t;
+    y[c] = y_old + t;
   }
 }
 

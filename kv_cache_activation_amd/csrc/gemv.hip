@@ -122,6 +122,14 @@ __global__ __launch_bounds__(T) void qkv_rope_append_kernel(
   const int n_waves = gridDim.x * (T / kWave);
   const int lane = lane_id();
   const int my_pairs = wave < n_pairs ? (n_pairs - wave + n_waves - 1) / n_waves : 0;
+  // the epilogue's inputs now, not after the dot products: the output
+  // pointers, and lane j's rotation angle (pair wave + j W) and gathered row
+  asm volatile("" ::"s"(q_out), "s"(k_full), "s"(v_full), "s"(k_sel), "s"(v_sel));
+  const int ep = wave + (lane < my_pairs ? lane : 0) * n_waves;
+  const int ep_head = ep / half, ep_i = ep - ep_head * half;
+  const float ep_c = rope.c[ep_i], ep_s = rope.s[ep_i];
+  const int ep_kv = ep_head < h_q + h_kv ? ep_head - h_q : ep_head - h_q - h_kv;
+  const int ep_rsel = ragged ? sel_rows.v[ep_kv & (kMaxKvHeads - 1)] : row_sel;
   // row k of this wave: pair wave + (k / 2) W, first (k even) or second row
   auto row_of = [&](int k) {
     const int p = wave + (k >> 1) * n_waves;
@@ -158,29 +166,25 @@ __global__ __launch_bounds__(T) void qkv_rope_append_kernel(
   const float a0 = __shfl(mine, 2 * lane) * rs;
   const float b0 = __shfl(mine, 2 * lane + 1) * rs;
   if (lane >= my_pairs) return;
-  const int p = wave + lane * n_waves;
-  const int head = p / half, i = p - head * half;
+  const int head = ep_head, i = ep_i;
   float a = a0, b = b0;
   if (head < h_q + h_kv) {  // rotate q and k, not v
-    const float c = rope.c[i], sn = rope.s[i];
-    a = a0 * c - b0 * sn;
-    b = b0 * c + a0 * sn;
+    a = a0 * ep_c - b0 * ep_s;
+    b = b0 * ep_c + a0 * ep_s;
   }
   if (head < h_q) {
     q_out[head * dh + i] = a;
     q_out[head * dh + i + half] = b;
   } else {
     const bool is_k = head < h_q + h_kv;
-    const int kv = is_k ? head - h_q : head - h_q - h_kv;
+    const int kv = ep_kv;
     KT* full = is_k ? k_full : v_full;
     const size_t off = ((size_t)kv * cap_full + row_full) * dh + i;
     store_elem(full + off, a);
     store_elem(full + off + half, b);
     if (k_sel) {
-      KT* sel = is_k ? k_sel : v_sel;
-      // ragged budgets: each KV head appends at its own row
-      const int rsel = ragged ? sel_rows.v[kv & (kMaxKvHeads - 1)] : row_sel;
-      const size_t offs = ((size_t)kv * cap_sel + rsel) * dh + i;
+      KT* sel = is_k ? k_sel : v_sel;  // ragged budgets: each KV head at its own row (ep_rsel)
+      const size_t offs = ((size_t)kv * cap_sel + ep_rsel) * dh + i;
       store_elem(sel + offs, a);
       store_elem(sel + offs + half, b);
     }
@@ -202,6 +206,8 @@ __global__ __launch_bounds__(T) void o_residual_kernel(const float* __restrict__
   extern __shared__ float xs[];
   XStage<T, StageNV<T, NCH>::NV, FULL && StageNV<T, NCH>::EXACT, false> st;
   st.load(attn, nullptr, din);  // x first: the staging then waits for it alone
+  // lane k's residual h[wave + k W] now, not after the dot products
+  const float h_old = lane < n ? h[wave + lane * n_waves] : 0.f;
   Row<WT, NCH> ra, rb;  // rb unused (no registers) when ONE
   load_row<FULL>(ra, W, din, n > 0 ? wave : 0, d8);  // no branch around the loads
   st.finish(din, 0.f, false, xs);
@@ -212,10 +218,7 @@ __global__ __launch_bounds__(T) void o_residual_kernel(const float* __restrict__
   } else {
     s = stream_rows<FULL>(W, din, d8, n, xs, ra, rb, [&](int k) { return wave + k * n_waves; });
   }
-  if (lane < n) {
-    const int r = wave + lane * n_waves;
-    h[r] += s;
-  }
+  if (lane < n) h[wave + lane * n_waves] = h_old + s;
 }
 
 // ------------------------------------------------------------------ CATS gate (+ up)
