@@ -475,7 +475,8 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
     else if (a.ragged) SD_MERGE_M(CAPV, 1);   \
     else SD_MERGE_M(CAPV, 0);                 \
   } while (0)
-  if (a.n_splits <= 64) SD_MERGE(64);
+  if (a.n_splits <= 32) SD_MERGE(32);
+  else if (a.n_splits <= 64) SD_MERGE(64);
   else if (a.n_splits <= 128) SD_MERGE(128);
   else SD_MERGE(kMaxSplits);
 #undef SD_MERGE
