@@ -42,13 +42,20 @@ constexpr int kRCols2 = 32;  // plain reduce: 32 columns, so a partial is read i
 constexpr int kRPer = kTealMaxParts / kRSlices;    // partitions per slice, at most
 
 // NQ float4 chunks of the input per thread (d_in <= 4 NQ 512).
-template <typename WT, int NQ, bool DUAL>
+// RG row groups: the workgroup's column tile is kTealTile / RG columns and
+// its eight waves form RG groups that take interleaved rows of the slice;
+// the groups' sums are added in LDS in a fixed order.  RG > 1 gives narrow
+// projections (O, QKV) more workgroups at the same slice count, so the
+// partial sums do not grow.
+template <typename WT, int NQ, bool DUAL, int RG>
 __global__ __launch_bounds__(kTealThreads) void teal_kernel(
     const float* __restrict__ x, int d_in, const float* __restrict__ nw, float eps, float t,
     const WT* __restrict__ W0, const WT* __restrict__ W1, int d_out,
     float* __restrict__ part0, float* __restrict__ part1, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ n_kept_out, uint8_t* __restrict__ keep_out) {
-  constexpr int U = (DUAL ? 32 : 64) / (int)sizeof(WT);  // rows per batch and matrix
+  constexpr int U = (DUAL ? 32 : 64) / (int)sizeof(WT) / RG;  // rows per batch, matrix and group
+  constexpr int CW = kTealWaves / RG;                          // waves per row group
+  constexpr int TILE = kTealTile / RG;                         // output columns per workgroup
   __shared__ int list[kTealList];
   __shared__ float xl[kTealList];
   __shared__ int wave_tot[kTealWaves];
@@ -131,9 +138,11 @@ __global__ __launch_bounds__(kTealThreads) void teal_kernel(
   __syncthreads();
   const int m = hi - lo;  // <= kTealList (the host sizes P so)
 
-  // 2. rows of the slice over this workgroup's column tile
+  // 2. rows of the slice over this workgroup's column tile; row group rg
+  //    takes list entries rg, rg + RG, ...
+  const int rg = __builtin_amdgcn_readfirstlane(wave / CW), cw = wave - rg * CW;
   const int d8 = d_out >> 3;
-  const int c8 = blockIdx.y * (kTealTile / 8) + wave * kWave + lane;
+  const int c8 = blockIdx.y * (TILE / 8) + cw * kWave + lane;
   const bool col_ok = c8 < d8;
   const float hv = lane < m ? xl[lane] : 0.f;
   float acc0[8], acc1[8];
@@ -141,18 +150,19 @@ __global__ __launch_bounds__(kTealThreads) void teal_kernel(
   for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
   if (m > 0 && col_ok) {
 #pragma unroll 1
-    for (int j0 = 0; j0 < m; j0 += U) {
+    for (int j0 = rg; j0 < m; j0 += U * RG) {
       Vec8<WT> g0[U], g1[DUAL ? U : 1];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const size_t row = (size_t)list[min(j0 + u, m - 1)] * d_out + 8 * c8;
+        const size_t row = (size_t)list[min(j0 + RG * u, m - 1)] * d_out + 8 * c8;
         g0[u].load(W0 + row);
         if constexpr (DUAL) g1[u].load(W1 + row);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), j0 + u));
-        const float h = j0 + u < m ? hj : 0.f;
+        const int j = j0 + RG * u;  // wave-uniform
+        const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), min(j, 63)));
+        const float h = j < m ? hj : 0.f;
         float f[8];
         g0[u].to_float(f);
 #pragma unroll
@@ -165,8 +175,23 @@ __global__ __launch_bounds__(kTealThreads) void teal_kernel(
       }
     }
   }
+  if constexpr (RG > 1) {  // row groups 1.. add into group 0, in order
+    __shared__ float grp[kTealWaves * kWave * 8];  // 16 KB
+    static_assert(!DUAL, "row groups are for single-matrix projections");
+    if (rg > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) grp[((wave - CW) * kWave + lane) * 8 + e] = acc0[e];
+    }
+    __syncthreads();
+    if (rg == 0) {
+#pragma unroll
+      for (int r = 1; r < RG; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc0[e] += grp[(((r - 1) * CW + cw) * kWave + lane) * 8 + e];
+    }
+  }
   // 3. partial sums of this slice
-  if (col_ok) {
+  if (rg == 0 && col_ok) {
     store8(part0 + (size_t)s * d_out + 8 * c8, acc0);
     if constexpr (DUAL) store8(part1 + (size_t)s * d_out + 8 * c8, acc1);
   }
@@ -271,18 +296,38 @@ TealGrid teal_grid(int d_in, int d_out) {
   return g;
 }
 
+// Row groups for a projection: four for single matrices up to 8192 outputs
+// (O and QKV of the 8B-class layer: 256 and 384 workgroups at 64 slices
+// instead of 64 and 128), one otherwise.
+template <bool DUAL>
+static int teal_row_groups(int d_out) { return !DUAL && d_out <= 8192 ? 4 : 1; }
+
 template <typename WT, bool DUAL>
 static void teal_typed(const TealArgs& a, hipStream_t s) {
-  const TealGrid g = teal_grid(a.d_in, a.d_out);
+  const TealGrid g = teal_grid(a.d_in, a.d_out);  // slices as the workspace is sized
+  const int rgs = teal_row_groups<DUAL>(a.d_out);
+  const int tiles = (a.d_out + kTealTile / rgs - 1) / (kTealTile / rgs);
   const int nq4 = (a.d_in + 4 * kTealThreads - 1) / (4 * kTealThreads);  // float4 per thread
-#define SD_TEAL(NQ)                                                                         \
-  launch_kernel(a.kind, teal_kernel<WT, NQ, DUAL>, dim3(g.parts, g.tiles), dim3(kTealThreads), \
-                0, s, a.x, a.d_in, a.norm, a.eps, a.t, (const WT*)a.w0, (const WT*)a.w1,       \
-                a.d_out, a.part0, a.part1, a.idx_out, a.n_kept_out, a.keep_out)
-  if (nq4 <= 2) SD_TEAL(2);
-  else if (nq4 <= 4) SD_TEAL(4);
-  else if (nq4 <= 8) SD_TEAL(8);
-  else SD_TEAL(16);
+#define SD_TEAL(NQ, RGV)                                                                    \
+  launch_kernel(a.kind, teal_kernel<WT, NQ, DUAL, RGV>, dim3(g.parts, tiles),                \
+                dim3(kTealThreads), 0, s, a.x, a.d_in, a.norm, a.eps, a.t, (const WT*)a.w0,   \
+                (const WT*)a.w1, a.d_out, a.part0, a.part1, a.idx_out, a.n_kept_out,          \
+                a.keep_out)
+#define SD_TEAL_RG(NQ)           \
+  do {                           \
+    if constexpr (!DUAL) {       \
+      if (rgs == 4) {            \
+        SD_TEAL(NQ, 4);          \
+        break;                   \
+      }                          \
+    }                            \
+    SD_TEAL(NQ, 1);              \
+  } while (0)
+  if (nq4 <= 2) SD_TEAL_RG(2);
+  else if (nq4 <= 4) SD_TEAL_RG(4);
+  else if (nq4 <= 8) SD_TEAL_RG(8);
+  else SD_TEAL_RG(16);
+#undef SD_TEAL_RG
 #undef SD_TEAL
 }
 
