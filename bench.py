@@ -160,31 +160,67 @@ class Bench:
             out.append([float(v[cut[k]:cut[k + 1]].mean()) for k in range(4)])
         return out
 
-    def teal_calibrate(self, n, k_keep, flags, target=0.5, iters=18):
-        """TEAL thresholds (harness): per layer and input, a bisection in log
-        space on the threshold until the step keeps the target fraction of that
-        input (one decode step per round, from the same state each time).  The
-        page calibrates TEAL's magnitude thresholds offline to 50% keep; here
-        the synthetic inputs' own magnitudes stand in for calibration data."""
+    def teal_calibrate(self, n, k_keep, flags, target=0.5, iters=18, tol=0.01, refine=40):
+        """TEAL thresholds (harness): per layer and input, the threshold at which
+        the step keeps the target fraction of that input (one decode step per
+        round, from the same state each time).  The page calibrates TEAL's
+        magnitude thresholds offline to 50% keep; here the synthetic inputs'
+        own magnitudes stand in for calibration data.  A bisection in log space
+        moves every threshold at once; since an input's magnitudes depend on
+        the thresholds before it (earlier layers, earlier inputs of its layer),
+        a bracket can close on a target that later moves, so damped Newton
+        steps in log t follow (slope of a half-normal's kept fraction at its
+        median, about -0.43 per unit of log t; a threshold's step is halved
+        whenever its error changes sign and grows back while it keeps its
+        sign) until every input keeps within `tol` of the target."""
         lo = [[math.log(1e-6)] * 4 for _ in range(self.L)]
         hi = [[math.log(1e3)] * 4 for _ in range(self.L)]
-        for _ in range(iters):
+        logt = [[0.0] * 4 for _ in range(self.L)]
+
+        def fractions():
             for li, L in enumerate(self.layers):
                 for k in range(4):
-                    L.teal_t[k] = math.exp(0.5 * (lo[li][k] + hi[li][k]))
+                    L.teal_t[k] = math.exp(logt[li][k])
             self.reset(n, k_keep)
             self.run_steps(n, flags, 1)
-            fr = self.teal_keep_fractions()
+            return self.teal_keep_fractions()
+
+        for _ in range(iters):
             for li in range(self.L):
                 for k in range(4):
-                    mid = 0.5 * (lo[li][k] + hi[li][k])
+                    logt[li][k] = 0.5 * (lo[li][k] + hi[li][k])
+            fr = fractions()
+            for li in range(self.L):
+                for k in range(4):
                     if fr[li][k] > target:
-                        lo[li][k] = mid
+                        lo[li][k] = logt[li][k]
                     else:
-                        hi[li][k] = mid
-        for li, L in enumerate(self.layers):
+                        hi[li][k] = logt[li][k]
+        for li in range(self.L):
             for k in range(4):
-                L.teal_t[k] = math.exp(0.5 * (lo[li][k] + hi[li][k]))
+                logt[li][k] = 0.5 * (lo[li][k] + hi[li][k])
+        self.teal_calib_rounds = 0
+        gain = [[2.0] * 4 for _ in range(self.L)]
+        err = [[0.0] * 4 for _ in range(self.L)]
+        for r in range(refine + 1):  # the thresholds kept are the ones last measured
+            fr = fractions()
+            self.teal_calib_worst = max(abs(f - target) for row in fr for f in row)
+            if self.teal_calib_worst <= tol or r == refine:
+                li, k = max(((i, j) for i in range(self.L) for j in range(4)),
+                            key=lambda ij: abs(fr[ij[0]][ij[1]] - target))
+                print(f"# teal calibration n={n}: {r} Newton rounds, worst layer {li} input {k} "
+                      f"keeps {fr[li][k]:.4f} at t={math.exp(logt[li][k]):.4g}", flush=True)
+                break
+            self.teal_calib_rounds += 1
+            for li in range(self.L):
+                for k in range(4):
+                    e = fr[li][k] - target
+                    if e * err[li][k] < 0:  # overshot: halve this threshold's step
+                        gain[li][k] *= 0.5
+                    elif e * err[li][k] > 0:  # still short: let it grow back
+                        gain[li][k] = min(2.0, 1.5 * gain[li][k])
+                    err[li][k] = e
+                    logt[li][k] += max(-1.0, min(1.0, gain[li][k] * e))
 
     def calibrate(self, n_states=256, sparsity=0.5):
         torch, sd = self.torch, self.sd
@@ -327,7 +363,9 @@ class Bench:
             extra["kv_keep_fraction"] = round(base / n, 4)
         if flags & self.sd.SD_PROJ_TEAL:
             b, f = self.teal_step_bytes(n_read, self.teal_keep_fractions())
-            extra = dict(teal_keep=[round(x, 4) for x in f])
+            extra = dict(teal_keep=[round(x, 4) for x in f],
+                         teal_calib_worst=round(self.teal_calib_worst, 4),
+                         teal_calib_rounds=self.teal_calib_rounds)
         else:
             b = self.step_bytes(n_read, kept)
             extra["n_kept_mean"] = kept
@@ -682,7 +720,10 @@ def main():
                 if flags & bench.sd.SD_KV_SPARSE else None
             sweep.append(c)
             print(f"# n={n:6d} {mode:5s} {c['us_per_step']:9.1f} us/step "
-                  f"{c['gbs']:7.1f} GB/s ({100 * c['hbm_frac']:.1f}% of peak)", flush=True)
+                  f"{c['gbs']:7.1f} GB/s ({100 * c['hbm_frac']:.1f}% of peak)"
+                  + (f" keep {c['teal_keep']} (calibration off by <= {c['teal_calib_worst']}"
+                     f" after {c['teal_calib_rounds']} Newton rounds)"
+                     if "teal_keep" in c else ""), flush=True)
     n_head = max(bench.contexts)
     at_head = {c["mode"]: c for c in sweep if c["context"] == n_head}
     head = at_head.get("both") or next(iter(at_head.values()))

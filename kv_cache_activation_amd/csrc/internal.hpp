@@ -225,9 +225,11 @@ void launch_o(const float* attn, const void* w, int din, int dout, float* h, int
 void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s);
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
 void launch_teal(const TealArgs& a, int w_dtype, hipStream_t s);
-// y (+)= column sums of the partials, or y = SiLU(sums of part0) * sums of part1
+// y (+)= column sums of the partials, or y = SiLU(sums of part0) * sums of part1;
+// keep (optional): keep[c] = |y[c]| > t (t < 0: every column)
 void launch_teal_reduce(const float* part0, const float* part1, int parts, int d_out, float* y,
-                        int accumulate, int swiglu, int kind, hipStream_t s);
+                        int accumulate, int swiglu, int kind, hipStream_t s, float t = -1.f,
+                        uint8_t* keep = nullptr);
 // QKV epilogue over the column sums: RoPE, q out, k and v appended (a.h is unused)
 void launch_teal_qkv_reduce(const float* part, int parts, const QkvArgs& a, int kv_dtype,
                             hipStream_t s);
