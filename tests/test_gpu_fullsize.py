@@ -7,7 +7,9 @@ The oracle cannot run the whole stack, so the step runs through the C ABI one
 layer per call (every layer's kernels are launched exactly as in a 32-layer
 call), and sampled layers are checked one by one against the float64 oracle
 from the GPU's own input to that layer.  The selection of a sampled layer is
-checked at 131072 context, and the whole stack for run-to-run determinism."""
+checked at 131072 context, and the whole stack for run-to-run determinism.
+The TEAL + KV step (all seven projections sparse, thresholds calibrated by
+the benchmark's own harness) is checked the same way."""
 
 import ctypes
 import math
@@ -17,7 +19,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import selection as osel, step as ostep
+from oracle import selection as osel, step as ostep, teal as oteal
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +33,8 @@ SAMPLED = (0, 31)
 @pytest.fixture(scope="module")
 def stack():
     import bench
-    args = types.SimpleNamespace(contexts=str(N), layers=32, warmup=0, steps=2)
+    args = types.SimpleNamespace(contexts=str(N), layers=32, warmup=0, steps=2,
+                                 modes="both,teal+kv")
     b = bench.Bench(args)
     secs, k_keep = b.select(N)
     return b, k_keep
@@ -121,3 +124,38 @@ def test_whole_stack_is_deterministic(stack):
         outs.append(b.hidden.cpu().numpy().copy())
     assert np.array_equal(outs[0], outs[1])
     assert np.all(np.isfinite(outs[0]))
+
+
+def test_teal_kv_step_sampled_layers_match_oracle(stack):
+    b, k_keep = stack
+    wl = b.wl
+    odims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                 kv_dtype="bf16", eps=1e-5, theta=500000.0)
+    mode = sd.SD_KV_SPARSE | sd.SD_PROJ_TEAL
+    b.teal_calibrate(N, k_keep, mode)
+    cut = np.cumsum((0,) + tuple(b.teal_sizes))
+    b.reset(N, k_keep)
+    for li in range(b.L):
+        if li in SAMPLED:
+            h_in = to_host(b.hidden).astype(np.float64)
+            ol = _oracle_layer(b, li, k_keep)
+        sd.sd_decode_step(b.dims, _one_layer(b, li), N, b.hidden, mode, b.ws)
+        if li not in SAMPLED:
+            continue
+        torch.cuda.synchronize()
+        got = to_host(b.hidden)
+        tm = b.TMASK[li].cpu().numpy().astype(bool)
+        gm = [tm[cut[k]:cut[k + 1]] for k in range(4)]
+        t = [float(b.layers[li].teal_t[k]) for k in range(4)]
+        tr = []
+        # the oracle with the GPU's four masks injected
+        want = oteal.teal_layer(ol, h_in, N, t, kv_sparse=True, masks=gm, trace=tr, **odims)
+        err = rel_l2(got, want)
+        assert err <= TOL["bf16"], (li, err)
+        # the GPU's masks against the oracle's own decisions on the oracle's
+        # inputs: they differ only next to the threshold (informational bound)
+        own = (tr[0]["x"], tr[0]["attn"], tr[0]["x2"], tr[0]["hmid"])
+        for k in range(4):
+            flips = int(np.sum(oteal.teal_mask(own[k].astype(np.float32), t[k]) != gm[k]))
+            assert flips <= 0.005 * gm[k].size + 4, (li, k, flips)
+            assert abs(gm[k].mean() - 0.5) < 0.1, (li, k, gm[k].mean())
