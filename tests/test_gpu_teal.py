@@ -234,3 +234,30 @@ def test_8b_teal_layer_matches_oracle_with_its_masks(kv_sparse):
     assert rel_l2(got, want) <= TOL["bf16"]
     for k, n in enumerate(st.mask_sizes):
         assert abs(gm[0][k].mean() - 0.5) < 0.01, k
+
+
+@pytest.mark.parametrize("t_down", [1e30, -1.0])
+def test_tiny_fp32_teal_step_down_input_all_dropped_or_all_kept(t_down):
+    # the step decides the down projection's mask in the SwiGLU reduce and
+    # streams the kept rows with the kept-row kernel: with every down input
+    # dropped the MLP adds nothing, with t < 0 it reads every row
+    wl = synth.TINY
+    st = TealStack(wl, 1, 1000, 300)
+    h = synth.hidden(wl, 7).astype(np.float64)
+    ts = st.thresholds(h, 1000, False, 0.5)
+    ts = [(t[0], t[1], t[2], t_down) for t in ts]
+    for k in range(4):
+        st.layers[0].teal_t[k] = ts[0][k]
+    hd = to_dev(h)
+    sd.sd_decode_step(st.dims, st.layers, 1000, hd, sd.SD_PROJ_TEAL, st.ws)
+    torch.cuda.synchronize()
+    tr = []
+    want = oteal.teal_step(st.olayers, h, 1000, ts, kv_sparse=False, trace=tr, **st.odims)
+    assert rel_l2(to_host(hd), want) <= TOL["f32"]
+    raw = st.teal_keep[0][1].cpu().numpy().astype(bool)
+    down = raw[sum(st.mask_sizes[:3]):]
+    assert down.size == wl.d_ff
+    assert (not down.any()) if t_down > 0 else down.all()
+    for k in range(4):
+        cut = np.cumsum((0,) + st.mask_sizes)
+        assert np.array_equal(raw[cut[k]:cut[k + 1]], tr[0]["masks"][k]), k
