@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -344,13 +345,19 @@ class Bench:
         self.reset(n, k_keep, ragged)
         self.run_steps(n, flags, args.warmup)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
-        self.run_steps(n + args.warmup, flags, args.steps)
-        e1.record(self.stream)
+        # the timed steps in up to 4 blocks, an event at each block boundary
+        # (on the library's stream, inside the one timed region)
+        nblk = max(1, min(4, args.steps))
+        cuts = [round(i * args.steps / nblk) for i in range(nblk + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in cuts]
+        ev[0].record(self.stream)
+        for i in range(nblk):
+            self.run_steps(n + args.warmup + cuts[i], flags, cuts[i + 1] - cuts[i])
+            ev[i + 1].record(self.stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        ms = ev[0].elapsed_time(ev[-1]) / args.steps
+        blk = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / (cuts[i + 1] - cuts[i])
+                     for i in range(nblk))
         kept = self.wl.d_ff
         if flags & self.sd.SD_MLP_SPARSE:
             kept = sum(int(m.sum()) for m in self.MASK) / self.L
@@ -369,6 +376,9 @@ class Bench:
         else:
             b = self.step_bytes(n_read, kept)
             extra["n_kept_mean"] = kept
+        extra["us_per_step_blocks"] = dict(blocks=nblk, min=round(blk[0], 1),
+                                           median=round(statistics.median(blk), 1),
+                                           max=round(blk[-1], 1))
         return dict(context=n, mode=mode, ms_per_step=ms, us_per_step=ms * 1e3,
                     bytes_per_step=b, gbs=b / ms / 1e6, hbm_frac=b / ms / 1e6 / HBM_PEAK_GBS,
                     kv_rows_read=n_read, **extra)
@@ -785,6 +795,7 @@ def main():
                     cats_sparsity=0.5, storage="bf16", accumulate="f32",
                     bytes_per_step=head["bytes_per_step"], hbm_frac=round(head["hbm_frac"], 4),
                     us_per_step=round(head["us_per_step"], 1),
+                    us_per_step_blocks=head["us_per_step_blocks"],
                     select_ms_all_layers=round(sel_ms[n_head], 2),
                     select_payback_steps=None if payback is None else round(payback, 1)),
         roofline=roof, cpu_baseline=cpu,
