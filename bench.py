@@ -668,13 +668,27 @@ def cpu_baseline(bench, n, seconds):
     kept = float(tr[0]["mask"].sum())
     per_step = per_layer * bench.L
     b = bench.step_bytes(k_keep + reps / 2.0 + 1, kept)
+    cores, blas, single = 1, None, None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        cores = 1
+        from threadpoolctl import threadpool_info, threadpool_limits
+        info = threadpool_info()
+        cores = max((p.get("num_threads", 1) for p in info), default=1)
+        blas = ",".join(sorted({str(p.get("internal_api")) for p in info})) or None
+        # the same oracle on one thread, a few more steps of the same layer
+        r1, t1 = 0, time.perf_counter()
+        with threadpool_limits(limits=1):
+            while reps + r1 < reps_cap - 2 and (r1 == 0 or time.perf_counter() - t1 < seconds / 2):
+                h = ostep.decode_layer(layer, h, n + reps + r1, kv_sparse=True, mlp_sparse=True,
+                                       **dims)
+                r1 += 1
+        single = dict(value=b / ((time.perf_counter() - t1) / r1 * bench.L) / 1e9, steps=r1)
+    except ImportError:
+        pass
     return dict(value=b / per_step / 1e9, unit="GB/s", cores=int(cores), kind="oracle",
-                ms_per_step=per_step * 1e3,
+                ms_per_step=per_step * 1e3, blas=blas,
+                affinity_cores=len(os.sched_getaffinity(0)),
+                single_thread_gbs=None if single is None else round(single["value"], 4),
+                single_thread_steps=None if single is None else single["steps"],
                 sample=(f"float64 numpy oracle, layer 0 of the {bench.L}-layer stack at context "
                         f"{n}, composed mode (first {k_keep} rows as the gathered buffer, "
                         f"threshold at the median |a|), {reps} decode steps of that layer in "
