@@ -151,3 +151,34 @@ def test_calibration_matches_oracle(sparsity):
         assert got == -1.0
     else:
         assert abs(got - want) <= 1e-5 * abs(want)
+
+
+def _mlp_weights(wl):
+    """The three MLP matrices of `wl` (seeded as synth.layer_weights draws them)."""
+    f, d = wl.d_ff, wl.d_model
+
+    def w(tid):
+        return synth._cast(synth.rng(wl.wid, 0, tid).standard_normal((f, d), dtype=np.float32)
+                           * 0.02, wl.dtype)
+
+    return dict(mlp_norm=np.ones(d, np.float32), w_gate=w(synth.T_GATE), w_up=w(synth.T_UP),
+                w_down_t=w(synth.T_DOWN))
+
+
+@pytest.mark.parametrize("sparsity", [0.0, 0.5])
+def test_max_size_cats_matches_oracle(sparsity):
+    # the largest sizes the library accepts: d_model 8192 (the widest GEMV
+    # input) and d_ff 32768 (512 down slices of at most 64 kept channels;
+    # keeping every channel fills every slice exactly)
+    wl = dataclasses.replace(synth.L8B_CATS_4K, name="max-width-cats", wid=5, d_model=8192,
+                             n_q_heads=64, d_ff=32768)
+    m = Mlp(wl, weights=_mlp_weights(wl))
+    x = synth.hidden(wl, 2)
+    _, a, _, _ = m.oracle(x, -1.0)
+    t = midpoint_threshold(a, sparsity) if sparsity > 0 else -1.0
+    y, act, idx = m.run(x, t)
+    wy, wa, wmask, widx = m.oracle(x, t)
+    assert rel_l2(act, wa) <= TOL["bf16"]
+    assert np.array_equal(idx, widx)
+    assert idx.size == (wl.d_ff if sparsity == 0 else wl.d_ff // 2)
+    assert rel_l2(y, wy) <= TOL["bf16"]
