@@ -1,6 +1,8 @@
 """GPU parity of sd_decode_attn (split-K decode attention) against the float64
 oracle's exact attention."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -175,3 +177,20 @@ def test_baselines_8b_bf16_match_oracle(path):
     torch.cuda.synchronize()
     want, _ = oatt.attend(q, k, v, n, 1 / np.sqrt(wl.head_dim))
     assert rel_l2(to_host(out), want) <= 1e-5
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(8, 8), (64, 8)])
+@pytest.mark.parametrize("dtype,dh", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("n_ctx,splits", [(4099, 0), (20001, 256), (20001, 129)])
+def test_query_group_sizes_match_oracle(h_q, h_kv, dtype, dh, n_ctx, splits):
+    # one and eight query heads per KV head (the kernel's other group
+    # instances), up to the largest split count and the widest merge
+    wl = dataclasses.replace(synth.L8B_DENSE_8K, name=f"attn-g{h_q // h_kv}-{dtype}", wid=6,
+                             n_q_heads=h_q, n_kv_heads=h_kv, head_dim=dh, dtype=dtype)
+    k, v = synth.kv_cache(wl, 0, n_ctx, n_ctx + 3)
+    q = synth.decode_query(wl, 0)
+    out, lse = _run(wl, k, v, n_ctx + 3, n_ctx, q, splits)
+    want, want_lse = oatt.attend(q, k, v, n_ctx, 1 / np.sqrt(dh))
+    tol = TOL["bf16"] if dtype == "bf16" else TOL["f32"]
+    assert rel_l2(out, want) <= tol
+    assert rel_l2(lse, want_lse) <= tol

@@ -212,3 +212,22 @@ def test_8b_bf16_scores_match_oracle(n, w):
     np.testing.assert_allclose(got.sum(1), 4 * w, rtol=1e-5)
     want_idx = osel.select_indices(got, n, w, wl.n_sink, s.k_keep)
     assert np.array_equal(idx, want_idx)   # the GPU ranks its own scores exactly
+
+
+@pytest.mark.parametrize("h_q,h_kv,dtype,dh", [(8, 8, "bf16", 128), (64, 8, "bf16", 128),
+                                               (16, 2, "f32", 64), (2, 2, "f32", 64)])
+def test_query_group_sizes_scores_and_ranking(h_q, h_kv, dtype, dh):
+    # one and eight query heads per KV head: the summed window scores against
+    # the oracle, and the GPU's ranking of its own scores exact
+    n, w = 5000, 32
+    wl = dataclasses.replace(synth.L8B_KV_32K, name=f"sel-g{h_q // h_kv}-{dtype}", wid=6,
+                             n_q_heads=h_q, n_kv_heads=h_kv, head_dim=dh, dtype=dtype, n_ctx=n,
+                             window=w)
+    k, v = synth.kv_cache(wl, 3, n, n + 8)
+    qw = synth.window_queries(wl, 3)
+    s = Sel(wl, k, v, n, n + 8, 1200)
+    got, idx = s.run(qw)
+    want = osel.window_scores(qw, k, n, 1 / np.sqrt(dh))
+    assert rel_l2(got, want) <= 1e-5
+    np.testing.assert_allclose(got.sum(1), (h_q // h_kv) * w, rtol=1e-5)
+    assert np.array_equal(idx, osel.select_indices(got, n, w, wl.n_sink, 1200))
