@@ -4,6 +4,7 @@ switches, at tiny float32 and 8B-class bf16 sizes; plus properties at the
 full 32-layer, 128K-context size in the benchmark's launch configuration."""
 
 import copy
+import dataclasses
 
 import numpy as np
 import pytest
@@ -177,3 +178,25 @@ def test_errors_leave_state_untouched(stack8b):
         sd.sd_decode_step(st.dims, st.layers, 5, hd, 0, st.ws)
     st.layers[1].n_full = saved[1][0]
     assert [(L.n_full, L.n_sel) for L in st.layers] == saved
+
+
+@pytest.fixture(scope="module")
+def stack_wide():
+    # a wide layer (d_model 8192, 64 query heads over 8 KV heads, FFN 28672,
+    # bf16): the widest GEMV inputs and eight query heads per KV head in the step
+    wl = dataclasses.replace(synth.L8B_DENSE_8K, name="wide-layer-bf16", wid=7, d_model=8192,
+                             n_q_heads=64, n_kv_heads=8, head_dim=128, d_ff=28672, n_ctx=3000)
+    return Stack(wl, 1, wl.n_ctx, 600)
+
+
+@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both"])
+def test_wide_layer_each_mode(stack_wide, mode):
+    st = stack_wide
+    h = synth.hidden(st.wl, 8)
+    pos = st.olayers[0].n
+    got, want, tr = st.step(h, pos, mode)
+    assert rel_l2(got, want) <= TOL["bf16"], mode
+    if MODES[mode] & sd.SD_MLP_SPARSE:
+        gmask = st.keep_alive[0][5].cpu().numpy().astype(bool)
+        assert np.array_equal(gmask, tr[0]["mask"])
+    _check_caches(st, TOL["bf16"])
