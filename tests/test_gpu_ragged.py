@@ -7,6 +7,8 @@ projections) against the oracle's decoder layer."""
 
 import ctypes
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -262,3 +264,20 @@ def test_tiny_fp32_ragged_teal_step():
     assert rel_l2(got, want) <= TOL["f32"]
     assert st.olayers[0].n_sel_heads == [wl.n_ctx + 1, 201]
     _check_ragged_caches(st, TOL["f32"])
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(8, 8), (64, 8)])
+@pytest.mark.parametrize("splits", [0, 256])
+def test_ragged_attention_group_sizes_match_oracle(h_q, h_kv, splits):
+    # one and eight query heads per KV head over per-head lengths from one
+    # row to 20001 (bf16, d_h 128)
+    wl = dataclasses.replace(synth.L8B_DENSE_8K, name=f"ragged-g{h_q // h_kv}", wid=6,
+                             n_q_heads=h_q, n_kv_heads=h_kv)
+    lens = [1, 20001, 300, 4099, 64, 12000, 2, 777]
+    cap = max(lens) + 8
+    k, v = synth.kv_cache(wl, 1, cap, cap)
+    q = synth.decode_query(wl, 1)
+    out, lse = _attn(wl, k, v, cap, lens, q, splits)
+    want, wlse = oatt.attend_ragged(q, k, v, lens, 1 / np.sqrt(wl.head_dim))
+    assert rel_l2(out, want) <= TOL["bf16"]
+    assert rel_l2(lse, wlse) <= TOL["bf16"]
