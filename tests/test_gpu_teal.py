@@ -3,6 +3,7 @@ only the kept input channels' weight rows read) and of the SD_PROJ_TEAL decode
 step (all seven projections) against the float64 TEAL oracle."""
 
 import copy
+import dataclasses
 
 import numpy as np
 import pytest
@@ -261,3 +262,23 @@ def test_tiny_fp32_teal_step_down_input_all_dropped_or_all_kept(t_down):
     for k in range(4):
         cut = np.cumsum((0,) + st.mask_sizes)
         assert np.array_equal(raw[cut[k]:cut[k + 1]], tr[0]["masks"][k]), k
+
+
+@pytest.mark.parametrize("d_in,d_out", [(32768, 4096), (32768, 8192), (4096, 8192), (4096, 8000),
+                                        (6144, 1000)])
+@pytest.mark.parametrize("norm", [False, True])
+def test_teal_gemv_widest_inputs_and_row_group_tails(d_in, d_out, norm):
+    # the widest input the library accepts (64 channels x 512 slices), and
+    # single-matrix outputs on the four-row-group form (1024-column tiles)
+    # with a ragged last tile
+    # dims whose widths cover these sizes (the workspace is sized from them)
+    wl = dataclasses.replace(synth.L8B_DENSE_8K, name="teal-widest", wid=7, d_model=8192,
+                             n_q_heads=64, d_ff=32768)
+    g = Gemv(wl, d_in, d_out, seed=d_in + d_out + 1)
+    x = np.random.default_rng(d_out).standard_normal(d_in).astype(np.float32)
+    xh = g.xhat(x, norm)
+    t = midpoint_threshold(xh, 0.5)
+    y, _, idx = g.run(x, t, norm)
+    want, mask, widx = oteal.teal_linear(g.wt.T, xh, t)
+    assert np.array_equal(idx, widx)
+    assert rel_l2(y, want) <= TOL["bf16"]
