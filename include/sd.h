@@ -50,7 +50,10 @@
  *     SD_EHIP          a HIP launch or query failed (work may be partial).
  *   sd_last_error() gives a message for the calling thread's last failure.
  *   No exception crosses the ABI and the library never aborts.
- * Threads.  The library is stateless and reentrant.
+ * Threads.  Every compute entry point is reentrant and keeps no state between
+ *   calls.  The opt-in kernel profiler (sd_profile_start / sd_profile_stop)
+ *   is the exception: it keeps one process-wide recording that is not safe to
+ *   drive from several threads at once.
  */
 #ifndef SD_H
 #define SD_H
@@ -363,7 +366,7 @@ size_t sd_batch_workspace_bytes(const sd_dims* dims, int32_t batch);
 
 /*
  * sd_decode_step_batch -- one decode step of `batch` sequences (2..8) that
- * share every weight read ([Cross] §3.2 "Dispatch and batching", §4.4
+ * share every weight read ([Cross] §3.3 "Dispatch and batching", §4.4
  * "Batching"): each sequence computes exactly its own sd_decode_step (its own
  * hidden state, position, caches and CATS mask, the layer threshold shared),
  * but each weight row is read once for the whole batch.  Under SD_MLP_SPARSE
@@ -388,32 +391,88 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
 
 /* Byte account record ([Cross] §3). Bytes as doubles (exact below 2^53). */
 typedef struct {
-  double b_attn;      /* bytes of W_q, W_k, W_v, W_o per layer */
-  double b_mlp;       /* bytes of W_gate, W_up, W_down per layer */
-  double b_kv;        /* bytes of the keys and values of n tokens per layer */
-  double b_total;     /* L (b_attn + b_mlp + b_kv) + fixed_bytes */
-  double delta_p;     /* bytes the projection branch skips per step */
-  double delta_kv;    /* bytes the KV branch skips per step */
-  double bound_p;     /* b_total / (b_total - delta_p) */
+  double b_attn;        /* bytes of W_q, W_k, W_v, W_o per layer */
+  double b_mlp;         /* bytes of W_gate, W_up, W_down per layer */
+  double b_kv;          /* bytes of the keys and values of n tokens per layer */
+  double b_total;       /* L (b_attn + b_mlp + b_kv) + fixed_bytes */
+  double delta_p;       /* bytes the projection branch skips per step */
+  double delta_kv;      /* bytes the KV branch skips per step */
+  double bound_p;       /* b_total / (b_total - delta_p) */
   double bound_kv;
   double bound_both;
-  double n_star;      /* crossover context in tokens (inf when r_kv == 1) */
+  double n_star;        /* crossover context in tokens (inf when r_kv == 1) */
+  double n_star_budget; /* crossover of a KV method that keeps a fixed budget b = r_kv n
+                           tokens whatever the context: b + P s_w (1 - r_p) / (2 h_kv d_h s_kv)
+                           ([Cross] §3.3) */
+  double gap_per_k;     /* s: seconds by which the byte-time gap between the branches grows
+                           per 1K more tokens, the KV bytes the KV branch skips in 1024
+                           tokens over bw_eff ([Cross] §4.3); NaN without a latency model */
+  double n_lat;         /* latency crossing n* - (c_p - c_kv) / s * 1024 tokens ([Cross] §4.3);
+                           inf when r_kv == 1; NaN without a latency model */
 } sd_byte_record;
+
+/* Kernel costs beyond byte time, for the latency crossing ([Cross] §4.3). */
+typedef struct {
+  double bw_eff;  /* effective bandwidth in bytes/s (> 0) */
+  double c_p;     /* projection branch: seconds per step beyond its byte time */
+  double c_kv;    /* KV branch: seconds per step beyond its byte time */
+} sd_latency_model;
 
 /*
  * sd_byte_account -- [Cross] §3.2-§3.3 from model dimensions: projection set
  * SD_PROJ_ALL7 (all seven projections), SD_PROJ_FFN (gate, up, down) or
  * SD_PROJ_CATS (up and down; the CATS gate is always read).  s_w, s_kv are
  * bytes per weight and cache element; r_p, r_kv keep ratios in [0, 1].
- * out [host].  Errors: EINVAL for out-of-range arguments.
+ * lat [host] or NULL: kernel costs for gap_per_k and n_lat (NaN when NULL).
+ * out [host].  Errors: EINVAL for out-of-range arguments (bw_eff <= 0 among them).
  */
 sd_status sd_byte_account(const sd_dims* dims, int32_t n_layers, double n, double r_p,
                           double r_kv, double s_w, double s_kv, int32_t proj_set,
-                          double fixed_bytes, sd_byte_record* out);
+                          double fixed_bytes, const sd_latency_model* lat, sd_byte_record* out);
+
+/*
+ * sd_latency_fit -- the latency model of a measured context sweep ([Cross]
+ * §4.3, the kernel costs its predictions use): a bandwidth-bound step takes
+ * its bytes / bw_eff plus a fixed kernel cost.
+ *   bw_eff    = inverse slope of the least-squares line of the dense step's time
+ *               t_dense[i] (seconds) against its bytes bytes_dense[i];
+ *   c_modes[m] = mean over i of t_modes[m][i] - bytes_modes[m][i] / bw_eff.
+ * bytes_modes, t_modes [host] [n_modes, n_points] row-major; bw_eff [host] out,
+ * c_modes [host] [n_modes] out.
+ * Errors: EINVAL for n_points < 2, non-finite values, or a dense time that
+ *         does not grow with its bytes.
+ */
+sd_status sd_latency_fit(int32_t n_points, const double* bytes_dense, const double* t_dense,
+                         int32_t n_modes, const double* bytes_modes, const double* t_modes,
+                         double* bw_eff, double* c_modes);
+
+/*
+ * sd_latency_crossing -- measured crossing of two latency curves sampled at
+ * the same ascending contexts ([Cross] §4.3 "Locating the Crossing"): linear
+ * interpolation of t_a - t_b between the first neighbouring contexts whose
+ * differences change sign; a zero difference is itself the crossing.
+ * n_cross [host] out: the context in tokens, NaN when the curves do not cross
+ * inside the sweep.  Errors: EINVAL for n_points < 1 or contexts that do not
+ * ascend.
+ */
+sd_status sd_latency_crossing(int32_t n_points, const double* ctx, const double* t_a,
+                              const double* t_b, double* n_cross);
+
+/*
+ * sd_latency_gate -- the latency gate of [Cross] §3.3 "Dispatch and batching":
+ * among the admissible configurations, the one with the least total time over
+ * a decode of `horizon` steps, horizon * t_step[i] + t_once[i] (t_once: the
+ * one-time KV selection, 0 for configurations without one); equal totals go to
+ * the lower index.  admissible [host] [n_configs] bytes (0 = excluded by a
+ * quality test) or NULL for all.  best [host] out: the index, -1 when none is
+ * admissible.  Errors: EINVAL for n_configs < 1, negative or non-finite times.
+ */
+sd_status sd_latency_gate(int32_t n_configs, const double* t_step, const double* t_once,
+                          const uint8_t* admissible, double horizon, int32_t* best);
 
 /*
  * sd_byte_crossover_batch -- the per-sequence crossover of a batch ([Cross]
- * §3.2 "Dispatch and batching"): B sequences share each weight read and the
+ * §3.3 "Dispatch and batching"): B sequences share each weight read and the
  * union of their kept channels covers a fraction u_b of the projection set,
  * so n_B* = P s_w (1 - u_b) / (2 B h_kv d_h s_kv (1 - r_kv)) tokens (infinite
  * at r_kv = 1).  n_star [host] out.  Errors: EINVAL for out-of-range

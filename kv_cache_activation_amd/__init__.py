@@ -34,7 +34,8 @@ EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_deco
            "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
            "sd_decode_step", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account",
-           "sd_byte_crossover_batch", "sd_calibrate_workspace_bytes",
+           "sd_byte_crossover_batch", "sd_latency_fit", "sd_latency_crossing", "sd_latency_gate",
+           "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
 
@@ -75,7 +76,11 @@ class sd_seq_kv(ctypes.Structure):
 class sd_byte_record(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in
                 ("b_attn", "b_mlp", "b_kv", "b_total", "delta_p", "delta_kv", "bound_p",
-                 "bound_kv", "bound_both", "n_star")]
+                 "bound_kv", "bound_both", "n_star", "n_star_budget", "gap_per_k", "n_lat")]
+
+
+class sd_latency_model(ctypes.Structure):
+    _fields_ = [("bw_eff", ctypes.c_double), ("c_p", ctypes.c_double), ("c_kv", ctypes.c_double)]
 
 
 class sd_kernel_stat(ctypes.Structure):
@@ -127,7 +132,15 @@ _lib.sd_decode_step.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_l
                                 _U, _P, _S, _P]
 _lib.sd_byte_account.restype = _I
 _lib.sd_byte_account.argtypes = [ctypes.POINTER(sd_dims), _I, _D, _D, _D, _D, _D, _I, _D,
-                                 ctypes.POINTER(sd_byte_record)]
+                                 ctypes.POINTER(sd_latency_model), ctypes.POINTER(sd_byte_record)]
+_DP = ctypes.POINTER(_D)
+_lib.sd_latency_fit.restype = _I
+_lib.sd_latency_fit.argtypes = [_I, _DP, _DP, _I, _DP, _DP, _DP, _DP]
+_lib.sd_latency_crossing.restype = _I
+_lib.sd_latency_crossing.argtypes = [_I, _DP, _DP, _DP, _DP]
+_lib.sd_latency_gate.restype = _I
+_lib.sd_latency_gate.argtypes = [_I, _DP, _DP, ctypes.POINTER(ctypes.c_uint8), _D,
+                                 ctypes.POINTER(_I)]
 _lib.sd_calibrate_workspace_bytes.restype = _S
 _lib.sd_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(sd_dims), _I]
 _lib.sd_cats_calibrate.restype = _I
@@ -278,11 +291,49 @@ def sd_decode_step(dims, layers, pos, hidden, mode, ws, stream=None) -> None:
                                p, nb, _stream(stream)))
 
 
-def sd_byte_account(dims, n_layers, n, r_p, r_kv, s_w, s_kv, proj_set, fixed_bytes=0.0):
+def sd_byte_account(dims, n_layers, n, r_p, r_kv, s_w, s_kv, proj_set, fixed_bytes=0.0,
+                    latency=None):
+    """`latency`: None or (bw_eff bytes/s, c_p s, c_kv s) for gap_per_k and n_lat."""
     rec = sd_byte_record()
+    lat = None if latency is None else ctypes.byref(sd_latency_model(*latency))
     _check(_lib.sd_byte_account(ctypes.byref(dims), n_layers, n, r_p, r_kv, s_w, s_kv, proj_set,
-                                fixed_bytes, ctypes.byref(rec)))
+                                fixed_bytes, lat, ctypes.byref(rec)))
     return rec
+
+
+def _host_doubles(vals):
+    vals = [float(x) for x in vals]
+    return (_D * max(1, len(vals)))(*vals)
+
+
+def sd_latency_fit(bytes_dense, t_dense, bytes_modes, t_modes):
+    """(bw_eff, [c per mode]) from a sweep: `bytes_modes`/`t_modes` are one
+    list per mode, each as long as `bytes_dense`."""
+    npts, nm = len(bytes_dense), len(bytes_modes)
+    bw = _D()
+    c = (_D * max(1, nm))()
+    _check(_lib.sd_latency_fit(npts, _host_doubles(bytes_dense), _host_doubles(t_dense), nm,
+                               _host_doubles([x for row in bytes_modes for x in row]),
+                               _host_doubles([x for row in t_modes for x in row]),
+                               ctypes.byref(bw), c))
+    return bw.value, [c[i] for i in range(nm)]
+
+
+def sd_latency_crossing(ctx, t_a, t_b) -> float:
+    out = _D()
+    _check(_lib.sd_latency_crossing(len(ctx), _host_doubles(ctx), _host_doubles(t_a),
+                                    _host_doubles(t_b), ctypes.byref(out)))
+    return out.value
+
+
+def sd_latency_gate(t_step, t_once, horizon, admissible=None) -> int:
+    best = _I()
+    adm = None
+    if admissible is not None:
+        adm = (ctypes.c_uint8 * max(1, len(admissible)))(*[1 if a else 0 for a in admissible])
+    _check(_lib.sd_latency_gate(len(t_step), _host_doubles(t_step), _host_doubles(t_once), adm,
+                                horizon, ctypes.byref(best)))
+    return best.value
 
 
 _lib.sd_byte_crossover_batch.restype = _I

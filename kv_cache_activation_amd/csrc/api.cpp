@@ -792,13 +792,17 @@ void plan_batch_splits(const int* rows, int nb, int hkv, long long total, sd::At
   long long c = (total + kSplitBlocks - 1) / kSplitBlocks;
   if (c < kMinChunk) c = kMinChunk;
   for (;;) {
-    long long blocks = 0;
+    long long blocks = 0, most = 1;
     for (int b = 0; b < nb; ++b) {
       long long sp = (rows[b] + c - 1) / c;
       if (sp > kMaxSplits) sp = kMaxSplits;
+      if (sp > most) most = sp;
       blocks += hkv * sp;
     }
-    if (blocks <= kSplitBlocks) break;
+    // stop at the cap, or once every sequence is down to one chunk per head
+    // (more (sequence, KV head) pairs than the cap: one chunk each, as many
+    // workgroups as pairs)
+    if (blocks <= kSplitBlocks || most == 1) break;
     c += c / 16 + 1;
   }
   int start = 0;

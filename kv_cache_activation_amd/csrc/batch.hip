@@ -1,7 +1,7 @@
 // Batched decode: nb sequences (2..8) share every weight read (gfx950, wave64).
 //
 // "Where Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding",
-// §3.2 "Dispatch and batching" and §4.4 "Batching": a batch of B sequences
+// §3.3 "Dispatch and batching" and §4.4 "Batching": a batch of B sequences
 // reads each weight once for all of them, while every sequence reads its own
 // cache; a sparse projection must then read every channel that at least one
 // sequence keeps (the union of the masks).

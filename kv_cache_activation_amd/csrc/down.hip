@@ -28,7 +28,7 @@
 // inside one launch.
 //
 // Batches: with nb sequences sharing the weight reads ("Where Activation
-// Sparsity and KV-Cache Sparsity Cross in LLM Decoding", §3.2 "Dispatch and
+// Sparsity and KV-Cache Sparsity Cross in LLM Decoding", §3.3 "Dispatch and
 // batching") the keep bytes are the union of the batch's masks, hmid is
 // [nb, d_ff] (zero where a sequence dropped a channel the union keeps), each
 // row read once serves all nb sequences, and the partials are [P, nb, d].

@@ -1,6 +1,6 @@
 """Oracle: batch-B decode with union channel masks (test infrastructure only).
 
-"Where Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding", §3.2
+"Where Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding", §3.3
 "Dispatch and batching" and §4.4 "Batching": a batch of B sequences shares
 every weight read, while each sequence reads its own cache.  A sparse
 projection then has to read every channel that at least one sequence of the

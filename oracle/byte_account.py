@@ -110,8 +110,10 @@ def delta_kv(dm: Dims, n_layers: int, n: float, r_kv: float, s_kv: float) -> flo
 
 
 def speedup_bound(total: float, removed: float) -> float:
-    """Ideal speedup of a bandwidth-bound step that skips `removed` bytes."""
-    return total / (total - removed)
+    """Ideal speedup of a bandwidth-bound step that skips `removed` bytes
+    (unbounded when nothing is left to read)."""
+    left = total - removed
+    return total / left if left > 0 else float("inf")
 
 
 def crossover(dm: Dims, r_p: float, r_kv: float, s_w: float, s_kv: float,
@@ -150,6 +152,69 @@ def latency_crossing(n_star_tokens: float, c_p: float, c_kv: float,
     return n_star_tokens - (c_p - c_kv) / s_per_k * K_TOKENS
 
 
+# ------------------------------------------------- from a measured sweep (§4.3)
+# The page locates its crossings from kernel costs measured on a context sweep
+# (its Appendix D, which the extracted text does not hold).  The plainest
+# reading: a bandwidth-bound step takes its bytes / BW_eff plus a fixed kernel
+# cost, BW_eff comes from how the dense step's time grows with its bytes, and
+# each branch's cost c_X is what its measured time holds beyond its byte time.
+
+def effective_bandwidth(bytes_dense, t_dense) -> float:
+    """BW_eff (bytes/s): inverse slope of the least-squares line of the dense
+    step's time against its bytes over the sweep's contexts."""
+    b = [float(x) for x in bytes_dense]
+    t = [float(x) for x in t_dense]
+    if len(b) < 2 or len(b) != len(t):
+        raise ValueError("need two or more (bytes, time) points")
+    bm = sum(b) / len(b)
+    tm = sum(t) / len(t)
+    sbb = sum((x - bm) ** 2 for x in b)
+    sbt = sum((x - bm) * (y - tm) for x, y in zip(b, t))
+    if sbb <= 0 or sbt <= 0:
+        raise ValueError("time must grow with bytes")
+    return sbb / sbt
+
+
+def kernel_cost(bytes_x, t_x, bw_eff: float) -> float:
+    """c_X (s): mean over the sweep of the branch's time beyond its byte time."""
+    pts = list(zip(bytes_x, t_x))
+    if not pts:
+        raise ValueError("empty sweep")
+    return sum(float(t) - float(b) / bw_eff for b, t in pts) / len(pts)
+
+
+def measured_crossing(ctx, t_a, t_b) -> float:
+    """Context (tokens) where the latency curves t_a and t_b cross, by linear
+    interpolation of t_a - t_b between the first two neighbouring contexts
+    whose differences change sign (a zero difference is itself the crossing);
+    NaN when the curves do not cross inside the sweep.  `ctx` ascending."""
+    n = [float(x) for x in ctx]
+    dlt = [float(a) - float(b) for a, b in zip(t_a, t_b)]
+    if len(n) != len(dlt) or any(x >= y for x, y in zip(n, n[1:])):
+        raise ValueError("contexts must ascend, one time per context and curve")
+    for i in range(len(n)):
+        if dlt[i] == 0.0:
+            return n[i]
+        if i + 1 < len(n) and (dlt[i] < 0.0) != (dlt[i + 1] < 0.0) and dlt[i + 1] != 0.0:
+            return n[i] + (n[i + 1] - n[i]) * dlt[i] / (dlt[i] - dlt[i + 1])
+    return float("nan")
+
+
+def latency_gate(t_step, t_once, horizon: float, admissible=None) -> int:
+    """The latency gate of [Cross] §3.3 "Dispatch and batching": among the
+    admissible configurations, the one with the least time for `horizon`
+    decode steps, horizon * t_step plus its one-time cost (the KV selection);
+    equal times go to the lower index.  -1 when none is admissible."""
+    best, best_t = -1, 0.0
+    for i, (ts, to) in enumerate(zip(t_step, t_once)):
+        if admissible is not None and not admissible[i]:
+            continue
+        tot = horizon * float(ts) + float(to)
+        if best < 0 or tot < best_t:
+            best, best_t = i, tot
+    return best
+
+
 @dataclass(frozen=True)
 class Record:
     """Everything the account says about one (dims, n, keep ratios) point."""
@@ -163,20 +228,34 @@ class Record:
     bound_kv: float
     bound_both: float
     n_star: float
+    n_star_budget: float  # crossover of a KV method keeping a fixed r_kv * n tokens
+    gap_per_k: float      # s (seconds per 1K tokens) at bw_eff; NaN without one
+    n_lat: float          # latency crossing n* - (c_P - c_KV)/s (tokens); NaN without bw_eff
 
 
 def account(dm: Dims, n_layers: int, n: float, r_p: float, r_kv: float,
             s_w: float = 2.0, s_kv: float = 2.0, proj_set: str = "all7",
-            fixed_bytes: float = 0.0) -> Record:
+            fixed_bytes: float = 0.0, bw_eff: float = 0.0, c_p: float = 0.0,
+            c_kv: float = 0.0) -> Record:
     tot = b_total(dm, n_layers, n, s_w, s_kv, fixed_bytes)
     dp = delta_p(dm, n_layers, r_p, s_w, proj_set)
     dk = delta_kv(dm, n_layers, n, r_kv, s_kv)
     n_star = crossover(dm, r_p, r_kv, s_w, s_kv, proj_set) if r_kv < 1.0 else float("inf")
+    nan = float("nan")
+    s = gap_growth_per_k(dm, n_layers, r_kv, s_kv, bw_eff) if bw_eff > 0 else nan
+    if bw_eff > 0 and r_kv < 1.0:
+        n_lat = latency_crossing(n_star, c_p, c_kv, s)
+    elif bw_eff > 0:
+        n_lat = float("inf")
+    else:
+        n_lat = nan
     return Record(
         b_attn=b_attn(dm, s_w), b_mlp=b_mlp(dm, s_w), b_kv=b_kv(dm, n, s_kv),
         b_total=tot, delta_p=dp, delta_kv=dk,
         bound_p=speedup_bound(tot, dp), bound_kv=speedup_bound(tot, dk),
         bound_both=speedup_bound(tot, dp + dk), n_star=n_star,
+        n_star_budget=crossover_fixed_budget(dm, r_kv * n, r_p, s_w, s_kv, proj_set),
+        gap_per_k=s, n_lat=n_lat,
     )
 
 

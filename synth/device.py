@@ -8,6 +8,7 @@ from __future__ import annotations
 import torch
 
 from . import (T_DOWN, T_GATE, T_K, T_KSCALE, T_O, T_QKV, T_QWIN, T_UP, T_V, T_VSCALE, T_CAL,
+               T_PLANT,
                T_H, Workload)
 
 
@@ -68,3 +69,19 @@ def calibration_states(wl: Workload, layer: int, n_states: int, device):
 
 def hidden(wl: Workload, draw: int, device):
     return normal((wl.d_model,), 1.0, wl, 1000 + draw, T_H, device, torch.float32)
+
+
+def plant_keys(wl: Workload, layer: int, k, n: int, q_win, n_planted: int):
+    """Device version of synth.plant_keys: n_planted positions drawn without
+    replacement from [n_sink, n - window), shared by the KV heads; at each,
+    head kv's key is 4 sqrt(d_h) times the unit vector of the sum of its query
+    group's window queries.  Writes k in place; returns the sorted positions."""
+    lo, hi = wl.n_sink, n - wl.window
+    g = torch.Generator(device="cpu")
+    g.manual_seed(((wl.wid * 1000 + layer) * 100 + T_PLANT) * 7919 + 17)
+    pos = (torch.randperm(hi - lo, generator=g)[:n_planted] + lo).sort().values
+    grp = wl.n_q_heads // wl.n_kv_heads
+    s = q_win.double().reshape(wl.n_kv_heads, grp * wl.window, wl.head_dim).sum(dim=1)
+    key = (4.0 * wl.head_dim ** 0.5) * s / s.norm(dim=1, keepdim=True)
+    k[:, pos.to(k.device)] = key.to(k.dtype)[:, None, :]
+    return pos

@@ -14,6 +14,8 @@ HEADER = os.path.join(ROOT, "include", "sd.h")
 
 sd = pytest.importorskip("kv_cache_activation_amd", reason="libsd.so not built")
 
+import account_cases  # noqa: E402
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -33,7 +35,8 @@ def test_every_declared_symbol_is_exported():
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
     assert ctypes.sizeof(sd.sd_layer) == 192
-    assert ctypes.sizeof(sd.sd_byte_record) == 80
+    assert ctypes.sizeof(sd.sd_byte_record) == 104
+    assert ctypes.sizeof(sd.sd_latency_model) == 24
     assert ctypes.sizeof(sd.sd_seq_kv) == 48
 
 
@@ -44,7 +47,7 @@ def test_struct_layout_matches_the_c_compiler(tmp_path):
     if not shutil.which("gcc"):
         pytest.skip("no C compiler")
     structs = {"sd_dims": sd.sd_dims, "sd_layer": sd.sd_layer, "sd_byte_record": sd.sd_byte_record,
-               "sd_seq_kv": sd.sd_seq_kv}
+               "sd_seq_kv": sd.sd_seq_kv, "sd_latency_model": sd.sd_latency_model}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "sd.h"', "int main(void) {"]
     for name, cls in structs.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
@@ -161,30 +164,41 @@ def test_sparse_mlp_rejects_nan_threshold():
     assert e.value.status == sd.SD_EINVAL
 
 
-@pytest.mark.parametrize("proj,code", [("all7", sd.SD_PROJ_ALL7), ("ffn", sd.SD_PROJ_FFN),
-                                       ("cats", sd.SD_PROJ_CATS)])
-@pytest.mark.parametrize("n,r_p,r_kv,s_w,lm", [(2048, 0.5, 0.3, 2, 0), (131072, 0.5, 0.3, 2, 1.05e9),
-                                               (32768, 0.5, 0.1, 0.5, 0), (65536, 0.3, 1.0, 2, 0)])
-def test_byte_account_matches_oracle(proj, code, n, r_p, r_kv, s_w, lm):
-    from oracle import byte_account as ba
-    dm = ba.Dims(**DIMS8B)
-    want = ba.account(dm, 32, n, r_p, r_kv, s_w=s_w, s_kv=2, proj_set=proj, fixed_bytes=lm)
-    got = sd.sd_byte_account(_dims(), 32, n, r_p, r_kv, s_w, 2.0, code, lm)
-    for f in ("b_attn", "b_mlp", "b_kv", "b_total", "delta_p", "delta_kv", "bound_p", "bound_kv",
-              "bound_both", "n_star"):
-        a, b = getattr(got, f), getattr(want, f)
-        assert (math.isinf(a) and math.isinf(b)) or abs(a - b) <= 1e-12 * abs(b), (f, a, b)
+@pytest.mark.parametrize("proj,code", account_cases.PROJ)
+@pytest.mark.parametrize("point", account_cases.POINTS)
+@pytest.mark.parametrize("latency", account_cases.LATENCY)
+def test_byte_account_matches_oracle(proj, code, point, latency):
+    account_cases.check_account(sd, _dims(), proj, code, point, latency)
 
 
-@pytest.mark.parametrize("proj,code", [("all7", sd.SD_PROJ_ALL7), ("cats", sd.SD_PROJ_CATS)])
-@pytest.mark.parametrize("batch,u_b,r_kv,s_w", [(4, 0.92, 0.3, 2), (8, 0.985, 0.1, 2),
-                                               (4, 0.9375, 0.2, 0.5), (1, 0.5, 0.3, 2)])
-def test_batched_crossover_matches_oracle(proj, code, batch, u_b, r_kv, s_w):
-    from oracle import byte_account as ba
-    want = ba.crossover_batched(ba.Dims(**DIMS8B), batch, u_b, r_kv, s_w, 2.0, proj)
-    got = sd.sd_byte_crossover_batch(_dims(), batch, u_b, r_kv, s_w, 2.0, code)
-    assert abs(got - want) <= 1e-12 * want
-    assert math.isinf(sd.sd_byte_crossover_batch(_dims(), batch, u_b, 1.0, s_w, 2.0, code))
+@pytest.mark.parametrize("proj,code", account_cases.PROJ)
+@pytest.mark.parametrize("case", account_cases.BATCH)
+def test_batched_crossover_matches_oracle(proj, code, case):
+    account_cases.check_batched(sd, _dims(), proj, code, case)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_latency_fit_and_crossing_match_oracle(seed):
+    account_cases.check_sweep(sd, seed)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_latency_gate_matches_oracle(seed):
+    account_cases.check_gate(sd, seed)
+
+
+def test_latency_helpers_reject_bad_input():
+    with pytest.raises(sd.SdError):  # one point gives no slope
+        sd.sd_latency_fit([1.0], [1.0], [], [])
+    with pytest.raises(sd.SdError):  # time falling with bytes
+        sd.sd_latency_fit([1.0, 2.0], [2.0, 1.0], [], [])
+    with pytest.raises(sd.SdError):  # contexts must ascend
+        sd.sd_latency_crossing([2.0, 1.0], [0.0, 1.0], [1.0, 0.0])
+    with pytest.raises(sd.SdError):
+        sd.sd_latency_gate([1.0, -1.0], [0.0, 0.0], 10)
+    with pytest.raises(sd.SdError):  # a latency model needs a positive bandwidth
+        sd.sd_byte_account(_dims(), 32, 1024, 0.5, 0.3, 2, 2, sd.SD_PROJ_ALL7,
+                           latency=(0.0, 1e-3, 0.0))
 
 
 def test_byte_account_rejects_bad_ratio():

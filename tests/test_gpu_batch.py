@@ -1,6 +1,6 @@
 """GPU parity of sd_decode_step_batch (B sequences sharing every weight read,
 union channel masks; "Where Activation Sparsity and KV-Cache Sparsity Cross
-in LLM Decoding", §3.2 "Dispatch and batching", §4.4 "Batching") against the
+in LLM Decoding", §3.3 "Dispatch and batching", §4.4 "Batching") against the
 float64 batch oracle: every sequence's new hidden state, the union mask bit
 for bit, and the appended cache rows."""
 
@@ -204,3 +204,23 @@ def test_batch_rejections_leave_state_untouched():
         sd.sd_decode_step_batch(st.dims, st.layers, st.kv, st.n, hd, 0, small)
     assert e.value.status == sd.SD_ENOSPC
     assert st.kv[0].n_full == st.n[0] and st.kv[1].n_full == st.n[1]
+
+
+def test_more_sequence_heads_than_split_workgroups():
+    # 5 sequences x 64 KV heads (one query head each) = 320 (sequence, head)
+    # pairs, more than the 256 chunk workgroups the planner aims for: every
+    # pair gets one chunk and the grid has one workgroup per pair
+    from dataclasses import replace
+    wl = replace(synth.TINY, name="g1-64kv-heads", d_model=4096, n_q_heads=64, n_kv_heads=64,
+                 head_dim=64, d_ff=1024)
+    batch = 5
+    st = BatchStack(wl, 1, batch, 200, 0.5)
+    hs = [synth.hidden(wl, 50 + b) for b in range(batch)]
+    pos = list(st.n)
+    for mode in ("dense", "kv"):
+        got, want, _, _ = st.step(hs, pos, mode)
+        for b in range(batch):
+            assert rel_l2(got[b], want[b]) <= TOL["f32"], (mode, b)
+        hs = [w for w in want]
+        pos = [p + 1 for p in pos]
+    _check_appends(st, TOL["f32"])

@@ -1,7 +1,7 @@
 """GPU parity at the full size of the composed workload that bench.py times:
 32 stacked 8B-class bf16 layers at context 131072, KV keep 10% (one-time
 selection), CATS thresholds calibrated for sparsity 0.5 -- built by bench.py's
-own Bench class, so the launch configuration is the timed one.
+own Stack class, so the launch configuration is the timed one.
 
 The oracle cannot run the whole stack, so the step runs through the C ABI one
 layer per call (every layer's kernels are launched exactly as in a 32-layer
@@ -33,11 +33,14 @@ SAMPLED = (0, 31)
 @pytest.fixture(scope="module")
 def stack():
     import bench
-    args = types.SimpleNamespace(contexts=str(N), layers=32, warmup=0, steps=2,
-                                 modes="both,teal+kv")
-    b = bench.Bench(args)
+    args = types.SimpleNamespace(contexts=str(N), layers=32, warmup=0, steps=2, blocks=1,
+                                 block_steps=1)
+    b = bench.Stack(args)
+    b.enable_teal()
     secs, k_keep = b.select(N)
-    return b, k_keep
+    yield b, k_keep
+    del b
+    torch.cuda.empty_cache()
 
 
 def _one_layer(b, li):

@@ -1,6 +1,6 @@
 """Pins of the batch oracle: B sequences sharing weights, union channel masks
 ("Where Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding",
-§3.2 "Dispatch and batching", §4.4 "Batching")."""
+§3.3 "Dispatch and batching", §4.4 "Batching")."""
 
 import copy
 

@@ -42,6 +42,16 @@ MUTS = [
  ("batch.py", "return 1.0 - (1.0 - keep) ** batch", "return 1.0 - keep ** batch"),
  ("batch.py", "for b, (layers, h, pos) in enumerate(zip(seq_layers, hs, positions)):",
   "for b, (layers, h, pos) in enumerate(zip(seq_layers, hs, positions[::-1])):"),
+ ("byte_account.py", "b_kv(dm, K_TOKENS, s_kv) * (1.0 - r_kv) / bw_bytes_per_s",
+  "b_kv(dm, K_TOKENS, s_kv) / bw_bytes_per_s"),
+ ("selection.py", "return [cache[kv, idx] for kv, idx in enumerate(idx_list)]",
+  "return [cache[0, idx] for kv, idx in enumerate(idx_list)]"),
+ ("byte_account.py", "    return sbb / sbt\n", "    return sbb / sbt * len(b) / (len(b) - 1)\n"),
+ ("byte_account.py", "float(t) - float(b) / bw_eff", "float(t) + float(b) / bw_eff"),
+ ("byte_account.py", "* dlt[i] / (dlt[i] - dlt[i + 1])", "* dlt[i + 1] / (dlt[i] - dlt[i + 1])"),
+ ("byte_account.py", "tot = horizon * float(ts) + float(to)", "tot = horizon * float(ts)"),
+ ("byte_account.py", "n_star_budget=crossover_fixed_budget(dm, r_kv * n,",
+  "n_star_budget=crossover_fixed_budget(dm, n,"),
 ]
 
 PIN_FILES = ["tests/test_oracle_byte_account.py", "tests/test_oracle_selection.py",

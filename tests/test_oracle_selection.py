@@ -201,3 +201,45 @@ def test_catekv_budgets_closed_form():
     assert ks == [n, 2048, 2048, n, 2048, 2048, n, 2048]
     assert abs(sum(ks) / (8 * n) - (3 * n + 5 * 2048) / (8 * n)) < 1e-15
     assert sel.catekv_budgets(1000, [1, 0], 2048, 0.5) == [500, 1000]
+
+
+def test_gather_ragged_hand_built_rows():
+    # row j of head kv holds the value 1000 kv + j in every channel, so each
+    # gathered row names the head and position it came from
+    h_kv, cap, d_h = 3, 9, 4
+    cache = (1000.0 * np.arange(h_kv)[:, None, None] + np.arange(cap)[None, :, None]
+             + np.zeros((1, 1, d_h)))
+    idx = [np.array([0, 3]), np.array([1]), np.array([0, 2, 4, 8])]
+    got = sel.gather_ragged(cache, idx)
+    want = [[0, 3], [1001], [2000, 2002, 2004, 2008]]
+    assert [g.shape for g in got] == [(2, d_h), (1, d_h), (4, d_h)]
+    for g, w in zip(got, want):
+        assert np.array_equal(g, np.repeat(np.array(w, float)[:, None], d_h, axis=1))
+
+
+def test_gather_ragged_equal_budgets_is_the_uniform_gather():
+    r = np.random.default_rng(23)
+    n, h_kv, d_h = 200, 4, 8
+    s = r.random((h_kv, n)).astype(np.float32)
+    cache = r.standard_normal((h_kv, n + 5, d_h))
+    idx_u = sel.select_indices(s, n, 8, 2, 50)
+    idx_r = sel.select_indices_ragged(s, n, 8, 2, [50] * h_kv)
+    want = sel.gather(cache, idx_u)
+    got = sel.gather_ragged(cache, idx_r)
+    for kv in range(h_kv):
+        assert np.array_equal(got[kv], want[kv])
+
+
+def test_gather_ragged_matches_a_per_head_loop():
+    r = np.random.default_rng(24)
+    n, h_kv, d_h = 120, 5, 4
+    s = r.random((h_kv, n)).astype(np.float32)
+    cache = r.standard_normal((h_kv, n, d_h))
+    budgets = [12, 120, 40, 13, 77]
+    idx = sel.select_indices_ragged(s, n, 6, 3, budgets)
+    got = sel.gather_ragged(cache, idx)
+    for kv in range(h_kv):
+        assert len(got[kv]) == min(budgets[kv], n)
+        for r_, j in enumerate(idx[kv]):
+            for c in range(d_h):
+                assert got[kv][r_, c] == cache[kv, j, c]
