@@ -69,6 +69,8 @@ def parse():
                     default="2048,8192,16384,24576,32768,49152,65536,131072")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--legs", type=str, default=",".join(LEGS))
+    ap.add_argument("--modes", type=str, default=",".join(HEAD_MODES),
+                    help="modes of the sweep (the crossing needs all four)")
     ap.add_argument("--teal-contexts", type=str, default="32768,131072")
     ap.add_argument("--catekv-contexts", type=str, default="32768,131072")
     ap.add_argument("--batches", type=str, default="4,8")
@@ -1008,7 +1010,8 @@ def main():
             continue
         secs, k_keep = stack.select(n)
         sel_ms[n] = secs * 1e3
-        for mode in (HEAD_MODES if "sweep" in legs else ("both",)):
+        modes = [m for m in HEAD_MODES if m in args.modes.split(",")]
+        for mode in (modes if "sweep" in legs else ("both",)):
             c = stack.cell(n, k_keep, mode)
             c["select_ms"] = sel_ms[n] if stack.mode_flags(mode) & stack.sd.SD_KV_SPARSE else None
             sweep.append(c)
@@ -1033,7 +1036,8 @@ def main():
     if cross:
         full["crossing"] = rnd(cross)
         note("crossing", rnd({k: v for k, v in cross.items() if k != "method"}, 1))
-    if "sweep" in legs:
+    if "sweep" in legs and all((n_head, m) in {(c["context"], c["mode"]) for c in sweep}
+                               for m in ("dense", "kv")):
         gate = latency_gate(stack, sweep)
         full["latency_gate"] = gate
         note("latency_gate", {f"{g['context']}/{g['horizon']}": g["best"] for g in gate})
