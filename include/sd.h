@@ -345,6 +345,26 @@ typedef struct {
 sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers, int32_t pos,
                          float* hidden, uint32_t mode, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * sd_decode_step_noalloc -- sd_decode_step without a caller workspace, for
+ * callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, semantics and kernels as sd_decode_step; the intermediate
+ * state lives in a buffer of SD_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (set up on the first call on a
+ * device).  It runs on the current device; `stream` must belong to it.  Every
+ * call on one GPU shares that buffer: calls that overlap on one GPU (other
+ * streams, other threads) race, so order them on one stream.  The buffer keeps
+ * the last call's contents; the step needs none of them.
+ * Errors: as sd_decode_step; ENOSPC when the step's workspace
+ *         (sd_workspace_bytes(dims, 0, 0), or with SD_ATTN_MASKED
+ *         sd_workspace_bytes(dims, largest cap_full, 0)) exceeds the buffer;
+ *         EHIP if the buffer's device address cannot be obtained.
+ */
+#define SD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sd_status sd_decode_step_noalloc(const sd_dims* dims, int32_t n_layers, sd_layer* layers,
+                                 int32_t pos, float* hidden, uint32_t mode, void* stream);
+
 /* One sequence's caches in one layer, for sd_decode_step_batch (the fields of
  * sd_layer with the same names, same meaning). */
 typedef struct {

@@ -33,7 +33,7 @@ SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_decode_attn",
            "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
-           "sd_decode_step", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account",
+           "sd_decode_step", "sd_decode_step_noalloc", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account",
            "sd_byte_crossover_batch", "sd_latency_fit", "sd_latency_crossing", "sd_latency_gate",
            "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
@@ -130,6 +130,10 @@ _lib.sd_teal_gemv.argtypes = [ctypes.POINTER(sd_dims), _P, _I, _P, _F, _P, _P, _
 _lib.sd_decode_step.restype = _I
 _lib.sd_decode_step.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_layer), _I, _P,
                                 _U, _P, _S, _P]
+_lib.sd_decode_step_noalloc.restype = _I
+_lib.sd_decode_step_noalloc.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_layer), _I,
+                                        _P, _U, _P]
+SD_NOALLOC_SCRATCH_BYTES = 64 << 20
 _lib.sd_byte_account.restype = _I
 _lib.sd_byte_account.argtypes = [ctypes.POINTER(sd_dims), _I, _D, _D, _D, _D, _D, _I, _D,
                                  ctypes.POINTER(sd_latency_model), ctypes.POINTER(sd_byte_record)]
@@ -289,6 +293,12 @@ def sd_decode_step(dims, layers, pos, hidden, mode, ws, stream=None) -> None:
     p, nb = _ws(ws)
     _check(_lib.sd_decode_step(ctypes.byref(dims), len(layers), layers, pos, _ptr(hidden), mode,
                                p, nb, _stream(stream)))
+
+
+def sd_decode_step_noalloc(dims, layers, pos, hidden, mode, stream=None) -> None:
+    """sd_decode_step on the library's own per-GPU scratch buffer (no workspace)."""
+    _check(_lib.sd_decode_step_noalloc(ctypes.byref(dims), len(layers), layers, pos,
+                                       _ptr(hidden), mode, _stream(stream)))
 
 
 def sd_byte_account(dims, n_layers, n, r_p, r_kv, s_w, s_kv, proj_set, fixed_bytes=0.0,

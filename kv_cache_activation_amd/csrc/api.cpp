@@ -266,6 +266,10 @@ void enqueue_teal(int kind, const sd_dims& dm, const Layout& L, char* ws, const 
 
 }  // namespace
 
+namespace sd {
+sd_status set_error(sd_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace sd
+
 extern "C" {
 
 const char* sd_status_string(sd_status st) {

@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/sd.h"
+
 namespace sd {
 
 // Kernel kinds for the opt-in profiler (order = names in profile.cpp).
@@ -243,5 +245,8 @@ void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s);
 // to *out (or -1 when k == 0).  hist: 256 uint32 scratch words; state: 4 words.
 void launch_kth_smallest(const float* vals, size_t n, size_t k, unsigned* hist, unsigned* state,
                          float* out, hipStream_t s);
+
+// Records a message for sd_last_error() on the calling thread; returns st.
+sd_status set_error(sd_status st, const char* msg);
 
 }  // namespace sd

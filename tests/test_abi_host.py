@@ -368,3 +368,16 @@ def test_batch_workspace_grows_with_batch():
     a = sd.sd_batch_workspace_bytes(_dims(), 2)
     b = sd.sd_batch_workspace_bytes(_dims(), 8)
     assert 0 < a < b and sd.sd_batch_workspace_bytes(_dims(), 1) == 0
+
+
+def test_noalloc_step_rejects_beyond_its_buffer_before_launch():
+    # masked attention over 2^20 allocated rows needs 128 MiB of score rows,
+    # more than the library's 64 MiB per-GPU buffer: refused on the host
+    L = sd.sd_layer()
+    L.cap_full = 1 << 20
+    layers = (sd.sd_layer * 1)(L)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step_noalloc(_dims(), layers, 0, FAKE, sd.SD_ATTN_MASKED, 0)
+    assert e.value.status == sd.SD_ENOSPC
+    assert sd.SD_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert sd.sd_workspace_bytes(_dims(), 0, 0) <= sd.SD_NOALLOC_SCRATCH_BYTES
