@@ -199,14 +199,16 @@ class Stack:
         self.torch.cuda.empty_cache()
 
     def enable_teal(self):
-        """TEAL reads the projections transposed (input-major)."""
+        """TEAL reads the projections in column blocks of 128 outputs,
+        [ceil(d_out / 128)][d_in][128]."""
+        from synth import device as sdev
         torch, wl = self.torch, self.wl
         self.WT, self.TMASK = [], []
         d, qd, ff = wl.d_model, wl.n_q_heads * wl.head_dim, wl.d_ff
         self.teal_sizes = (d, qd, d, ff)
         for li in range(self.L):
             W = self.W[li]
-            wt = {k: W[k].t().contiguous() for k in ("w_qkv", "w_o", "w_gate", "w_up")}
+            wt = {k: sdev.teal_blocked(W[k]) for k in ("w_qkv", "w_o", "w_gate", "w_up")}
             self.WT.append(wt)
             self.TMASK.append(torch.zeros(sum(self.teal_sizes), dtype=torch.uint8,
                                           device=self.dev))
@@ -474,6 +476,12 @@ class Stack:
             "cats_down": 2 * d * kept,
             "attn_partial": n_read * 2 * wl.n_kv_heads * dh * 2,
         }
+        if flags & sd.SD_PROJ_TEAL:  # kept rows of each projection (mean keep per input)
+            fr = self.teal_keep_fractions()
+            f = [sum(x[k] for x in fr) / len(fr) for k in range(4)]
+            qd = wl.n_q_heads * dh
+            alg.update(teal_qkv=2 * d * wl.qkv_out * f[0], teal_o=2 * qd * d * f[1],
+                       teal_gate_up=4 * d * wl.d_ff * f[2], cats_down=2 * wl.d_ff * d * f[3])
         out = {}
         for name, (launches, tot) in stats.items():
             avg_us = tot / launches * 1e3
@@ -1059,6 +1067,12 @@ def main():
                 c = stack.cell(n, k_keep, mode)
                 extra.append(c)
                 note("teal", rnd(c))
+            if n == max(int(c) for c in args.teal_contexts.split(",") if c):
+                kt = stack.profile_cell(n, k_keep, "teal+kv")
+                full["teal_kernels"] = rnd(kt)
+                note("teal_kernels", {k: rnd({kk: e[kk] for kk in ("launches", "avg_us", "gbs",
+                                                                   "frac") if kk in e}, 3)
+                                      for k, e in kt.items()})
         stack.disable_teal()
     if "catekv" in legs:
         stack.enable_ragged()

@@ -88,6 +88,9 @@ enum {
   SD_ACCUMULATE = 256u  /* sd_teal_gemv: y += result instead of y = result */
 };
 
+/* output columns per block of the TEAL weight layout (sd_teal_gemv) */
+#define SD_TEAL_BLOCK 128
+
 /* projection sets of the byte account */
 enum { SD_PROJ_ALL7 = 0, SD_PROJ_FFN = 1, SD_PROJ_CATS = 2 };
 
@@ -259,12 +262,17 @@ sd_status sd_sparse_mlp(const sd_dims* dims, const float* x, const float* norm_w
  *          x_hat = x / sqrt(mean(x^2) + rms_eps) * norm_w, else x_hat = x.
  * Input channel j is kept iff threshold < 0 or |x_hat_j| > threshold (strict,
  * decided in float32).
- * w_t      [d_in, d_out] in dims->w_dtype: the projection's weight transposed,
- *          so a kept channel is one contiguous row; only kept rows are read.
- * w2_t     optional second matrix [d_in, d_out] with the same input (gate and
- *          up), its result in y2; NULL for one projection.
- * y        [d_out] float32 out: sum over kept j of x_hat_j w_t[j]; with
- *          SD_ACCUMULATE it is added to y.  Fixed summation order.
+ * w_t      the projection's weight W [d_out, d_in] in dims->w_dtype, stored in
+ *          column blocks of SD_TEAL_BLOCK (128) outputs: element (c, j) of W at
+ *          ((c / 128) d_in + j) 128 + c % 128, [ceil(d_out / 128)][d_in][128]
+ *          elements (columns past d_out are padding, never written out).  A
+ *          kept channel's piece of a block is one contiguous 128-element row;
+ *          only kept channels' pieces are read.
+ * w2_t     optional second matrix in the same layout with the same input
+ *          (gate and up), its result in y2; NULL for one projection.
+ * y        [d_out] float32 out: sum over kept j of x_hat_j W[:, j]; with
+ *          SD_ACCUMULATE it is added to y.  Fixed summation order.  y, y2 must
+ *          not overlap x.
  * idx      [d_in] int32 out or NULL: the kept channels ascending in
  *          idx[0..n_kept-1].  n_kept [1] int32 out (device) or NULL.
  * Sizes:   d_in, d_out multiples of 8; d_in <= 32768; the workspace of
@@ -300,13 +308,13 @@ typedef struct {
   uint8_t* mask_out;       /* optional [d_ff], 16-byte aligned: receives 1 for kept channels, else 0 */
   int32_t window_keep;     /* SD_KV_WINDOW: entries read (sinks included) */
   int32_t window_sink;     /* SD_KV_WINDOW: sink entries among them */
-  /* SD_PROJ_TEAL: the projections transposed (input-major) and the four
-   * input thresholds, attention input, O input, MLP input, down input
-   * (w_down_t above serves both modes) */
-  const void* w_qkv_t;     /* [d, (h_q + 2 h_kv) d_h] */
-  const void* w_o_t;       /* [h_q d_h, d] */
-  const void* w_gate_t;    /* [d, d_ff] */
-  const void* w_up_t;      /* [d, d_ff] */
+  /* SD_PROJ_TEAL: the projections in the column-block layout of sd_teal_gemv
+   * ([ceil(d_out / 128)][d_in][128]) and the four input thresholds, attention
+   * input, O input, MLP input, down input (w_down_t above serves both modes) */
+  const void* w_qkv_t;     /* W_qkv in column blocks: d_in = d, d_out = (h_q + 2 h_kv) d_h */
+  const void* w_o_t;       /* W_o: d_in = h_q d_h, d_out = d */
+  const void* w_gate_t;    /* W_gate: d_in = d, d_out = d_ff */
+  const void* w_up_t;      /* W_up: d_in = d, d_out = d_ff */
   float teal_t[4];
   uint8_t* teal_masks_out; /* optional, 16-byte aligned: the four keep masks (1 kept, 0 dropped),
                               [d | h_q d_h | d | d_ff] bytes in that order */

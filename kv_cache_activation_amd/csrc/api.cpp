@@ -36,7 +36,8 @@ constexpr int kMaxWidth = 8192;        // widest GEMV input the kernels hold in 
 size_t elem_size(int dtype) { return dtype == SD_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t q, attn, pm, pl, pacc, act, hmid, keep, mlp_part, teal_part, lse_part, lse, scores;
+  size_t q, attn, pm, pl, pacc, act, hmid, keep, mlp_part, teal_part, teal_tickets, lse_part,
+      lse, scores;
   size_t teal_part_floats;
   size_t kth_hist, kth_state, topk, total;
   int max_splits, sel_chunks;
@@ -63,10 +64,12 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
   L.hmid = take(ff * 4);
   L.keep = take(ff);
   L.mlp_part = take((size_t)sd::down_parts((int)ff) * d * 4);
-  {  // TEAL partials: the largest of the layer's four sparse projections
+  {  // TEAL partials: the largest of the layer's four sparse projections, at
+     // the most slices any launch takes
     const int qkv_out = (int)((hq + 2 * hkv) * dh);
-    auto need = [](int din, int dout, int mats) {
-      return (size_t)sd::teal_grid(din, dout).parts * dout * mats;
+    auto need = [](int, int dout, int mats) {
+      const size_t nblk = (dout + sd::kTealBlock - 1) / sd::kTealBlock;
+      return (size_t)sd::kTealMaxSlices * nblk * sd::kTealBlock * mats;
     };
     size_t f = need((int)d, qkv_out, 1);
     f = std::max(f, need((int)(hq * dh), (int)d, 1));
@@ -74,6 +77,7 @@ Layout make_layout(const sd_dims& dm, int max_rows, int max_window) {
     f = std::max(f, need((int)ff, (int)d, 1));
     L.teal_part_floats = f;
     L.teal_part = take(f * 4);
+    L.teal_tickets = take(sd::kTealMaxBlocks * 4);
   }
   L.sel_chunks = max_rows > 0 ? (max_rows + kSelChunk - 1) / kSelChunk : 0;
   L.lse_part = take(hkv * (size_t)L.sel_chunks * G * (size_t)max_window * 2 * 4);
@@ -239,13 +243,12 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   sd::launch_down(dn, dm.w_dtype, s);
 }
 
-// One TEAL projection's gathered GEMV into the layout's partials (part0, and
-// part1 right after it when w1 is given); the caller launches the reduce.
-void enqueue_teal(int kind, const sd_dims& dm, const Layout& L, char* ws, const float* x,
-                  int d_in, const float* norm, float t, const void* w0, const void* w1, int d_out,
-                  uint8_t* keep_out, hipStream_t s, int32_t* idx = nullptr,
-                  int32_t* n_kept = nullptr) {
-  const sd::TealGrid g = sd::teal_grid(d_in, d_out);
+// One TEAL projection over column blocks, epilogue included (the layout's
+// partials and tickets; the tickets must be zero, and the launch leaves them
+// zero).
+sd::TealArgs teal_args(int kind, const sd_dims& dm, const Layout& L, char* ws, const float* x,
+                       int d_in, const float* norm, float t, const void* w0, const void* w1,
+                       int d_out, int epi) {
   sd::TealArgs a{};
   a.kind = kind;
   a.x = x;
@@ -256,12 +259,11 @@ void enqueue_teal(int kind, const sd_dims& dm, const Layout& L, char* ws, const 
   a.w0 = w0;
   a.w1 = w1;
   a.d_out = d_out;
-  a.part0 = reinterpret_cast<float*>(ws + L.teal_part);
-  a.part1 = w1 ? a.part0 + (size_t)g.parts * d_out : nullptr;
-  a.idx_out = idx;
-  a.n_kept_out = n_kept;
-  a.keep_out = keep_out;
-  sd::launch_teal(a, dm.w_dtype, s);
+  a.part = reinterpret_cast<float*>(ws + L.teal_part);
+  a.tickets = reinterpret_cast<unsigned*>(ws + L.teal_tickets);
+  a.epi = epi;
+  a.t_next = -1.f;
+  return a;
 }
 
 }  // namespace
@@ -533,26 +535,25 @@ sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const 
   if (flags & ~(uint32_t)SD_ACCUMULATE) return fail(SD_EINVAL, "unknown flags 0x%x", flags);
   if (d_in < 8 || d_out < 8 || d_in % 8 || d_out % 8)
     return fail(SD_EINVAL, "d_in and d_out must be positive multiples of 8");
-  if (d_in > sd::kTealList * sd::kTealMaxParts)
-    return fail(SD_EUNSUPPORTED, "d_in must be at most %d", sd::kTealList * sd::kTealMaxParts);
+  if (d_in > 32768) return fail(SD_EUNSUPPORTED, "d_in must be at most 32768");
   if (std::isnan(threshold)) return fail(SD_EINVAL, "threshold is NaN");
   const Layout L = make_layout(*dims, 0, 0);
   if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
-  const sd::TealGrid g = sd::teal_grid(d_in, d_out);
-  const size_t need = (size_t)g.parts * d_out * (w2_t ? 2 : 1);
-  if (need > L.teal_part_floats)
+  const int nblk = (d_out + sd::kTealBlock - 1) / sd::kTealBlock;
+  const size_t need = (size_t)sd::teal_slices(d_in, d_out) * nblk * sd::kTealBlock * (w2_t ? 2 : 1);
+  if (need > L.teal_part_floats || nblk > sd::kTealMaxBlocks)
     return fail(SD_ENOSPC, "d_in %d x d_out %d needs %zu partial floats, the workspace holds %zu",
                 d_in, d_out, need, L.teal_part_floats);
   char* wsb = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  enqueue_teal(sd::K_TEAL_O, *dims, L, wsb, x, d_in, norm_w, threshold, w_t, w2_t, d_out,
-               nullptr, s, idx, n_kept);
-  float* part = reinterpret_cast<float*>(wsb + L.teal_part);
-  const int acc = (flags & SD_ACCUMULATE) ? 1 : 0;
-  sd::launch_teal_reduce(part, nullptr, g.parts, d_out, y, acc, 0, sd::K_TEAL_REDUCE, s);
-  if (w2_t)
-    sd::launch_teal_reduce(part + (size_t)g.parts * d_out, nullptr, g.parts, d_out, y2, acc, 0,
-                           sd::K_TEAL_REDUCE, s);
+  sd::TealArgs a = teal_args(sd::K_TEAL_O, *dims, L, wsb, x, d_in, norm_w, threshold, w_t, w2_t,
+                             d_out, (flags & SD_ACCUMULATE) ? sd::TEAL_ACC : sd::TEAL_STORE);
+  a.y = y;
+  a.y2 = y2;
+  a.idx_out = idx;
+  a.n_kept_out = n_kept;
+  sd::launch_teal_zero(a.tickets, nblk, s);
+  sd::launch_teal(a, dims->w_dtype, dims->kv_dtype, s);
   return check_launch("sd_teal_gemv");
 }
 
@@ -585,7 +586,7 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
       return fail(SD_EINVAL, "layer %d: null or misaligned pointer", i);
     if (teal) {
       if (!aligned(l.w_qkv_t) || !aligned(l.w_o_t) || !aligned(l.w_gate_t) || !aligned(l.w_up_t))
-        return fail(SD_EINVAL, "layer %d: SD_PROJ_TEAL needs the transposed weights", i);
+        return fail(SD_EINVAL, "layer %d: SD_PROJ_TEAL needs the column-block weights", i);
       for (int k = 0; k < 4; ++k)
         if (std::isnan(l.teal_t[k])) return fail(SD_EINVAL, "layer %d: TEAL threshold is NaN", i);
       if (l.teal_masks_out && !aligned(l.teal_masks_out))
@@ -671,11 +672,14 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     const int qkv_out = (hq + 2 * hkv) * dh;
     uint8_t* tm = teal ? l.teal_masks_out : nullptr;  // [d | h_q d_h | d | d_ff]
     if (teal) {
-      const sd::TealGrid g = sd::teal_grid(d, qkv_out);
-      enqueue_teal(sd::K_TEAL_QKV, *dims, L, wsb, hidden, d, l.attn_norm, l.teal_t[0], l.w_qkv_t,
-                   nullptr, qkv_out, tm, s);
-      sd::launch_teal_qkv_reduce(reinterpret_cast<float*>(wsb + L.teal_part), g.parts, qa,
-                                 dims->kv_dtype, s);
+      if (i == 0)  // every TEAL launch leaves its tickets zero for the next
+        sd::launch_teal_zero(reinterpret_cast<unsigned*>(wsb + L.teal_tickets), sd::kTealMaxBlocks,
+                             s);
+      sd::TealArgs a = teal_args(sd::K_TEAL_QKV, *dims, L, wsb, hidden, d, l.attn_norm,
+                                 l.teal_t[0], l.w_qkv_t, nullptr, qkv_out, sd::TEAL_QKV);
+      a.qkv = qa;
+      a.keep_out = tm;
+      sd::launch_teal(a, dims->w_dtype, dims->kv_dtype, s);
     } else {
       sd::launch_qkv(qa, dims->w_dtype, dims->kv_dtype, s);
     }
@@ -698,27 +702,27 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
                  nullptr, s, ragged ? &lens : nullptr);
 
     if (teal) {
-      float* part = reinterpret_cast<float*>(wsb + L.teal_part);
       float* hmid = reinterpret_cast<float*>(wsb + L.hmid);
       const int ff = dims->d_ff;
       // O: attention output -> h += W_o (mask * attn)
-      enqueue_teal(sd::K_TEAL_O, *dims, L, wsb, attn, hq * dh, nullptr, l.teal_t[1], l.w_o_t,
-                   nullptr, d, tm ? tm + d : nullptr, s);
-      sd::launch_teal_reduce(part, nullptr, sd::teal_grid(hq * dh, d).parts, d, hidden, 1, 0,
-                             sd::K_TEAL_REDUCE, s);
-      // gate and up share the MLP input; hmid = SiLU(gate) * up
-      enqueue_teal(sd::K_TEAL_GATE_UP, *dims, L, wsb, hidden, d, l.mlp_norm, l.teal_t[2],
-                   l.w_gate_t, l.w_up_t, ff, tm ? tm + d + hq * dh : nullptr, s);
-      // the reduce also decides the down projection's input mask, so the
-      // down projection is the kept-row kernel of the CATS branch (w_down_t
-      // is the same [d_ff, d] layout): it ranks keep bytes instead of
-      // re-reading and re-testing the float input in every workgroup
-      // (measured on MI355X, 8B-class layer at 50% keep: 14.5 + 5 us
-      // against 20.6 + 5.1 us for the TEAL kernel and its reduce)
+      sd::TealArgs ao = teal_args(sd::K_TEAL_O, *dims, L, wsb, attn, hq * dh, nullptr,
+                                  l.teal_t[1], l.w_o_t, nullptr, d, sd::TEAL_ACC);
+      ao.y = hidden;
+      ao.keep_out = tm ? tm + d : nullptr;
+      sd::launch_teal(ao, dims->w_dtype, dims->kv_dtype, s);
+      // gate and up share the MLP input; hmid = SiLU(gate) * up.  The epilogue
+      // also decides the down projection's input mask, so the down projection
+      // is the kept-row kernel of the CATS branch (w_down_t is the same
+      // [d_ff, d] layout): it ranks keep bytes instead of re-reading and
+      // re-testing the float input in every workgroup
       uint8_t* dkeep = tm ? tm + 2 * d + hq * dh : reinterpret_cast<uint8_t*>(wsb + L.keep);
-      const int pg = sd::teal_grid(d, ff).parts;
-      sd::launch_teal_reduce(part, part + (size_t)pg * ff, pg, ff, hmid, 0, 1, sd::K_TEAL_REDUCE,
-                             s, l.teal_t[3], dkeep);
+      sd::TealArgs ag = teal_args(sd::K_TEAL_GATE_UP, *dims, L, wsb, hidden, d, l.mlp_norm,
+                                  l.teal_t[2], l.w_gate_t, l.w_up_t, ff, sd::TEAL_SWIGLU);
+      ag.y = hmid;
+      ag.t_next = l.teal_t[3];
+      ag.keep_next = dkeep;
+      ag.keep_out = tm ? tm + d + hq * dh : nullptr;
+      sd::launch_teal(ag, dims->w_dtype, dims->kv_dtype, s);
       // down: h += W_down (mask * hmid)
       sd::DownArgs dn{};
       dn.w_down_t = l.w_down_t;

@@ -16,8 +16,8 @@ namespace sd {
 enum KernelKind {
   K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_MLP_REDUCE, K_SEL_LSE,
   K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_MASKED_SCORES,
-  K_MASKED_SOFTMAX, K_MASKED_PV, K_TEAL_QKV, K_TEAL_QKV_REDUCE, K_TEAL_O, K_TEAL_GATE_UP,
-  K_TEAL_DOWN, K_TEAL_REDUCE, K_BATCH_QKV, K_BATCH_ROPE, K_BATCH_O, K_BATCH_GATE_UP, K_COUNT
+  K_MASKED_SOFTMAX, K_MASKED_PV, K_TEAL_QKV, K_TEAL_ZERO, K_TEAL_O, K_TEAL_GATE_UP,
+  K_TEAL_DOWN, K_BATCH_QKV, K_BATCH_ROPE, K_BATCH_O, K_BATCH_GATE_UP, K_COUNT
 };
 
 // Start/stop events of one launch of kind `kind` while profiling is on (both
@@ -102,16 +102,20 @@ struct DownArgs {
   int nb;              // sequences sharing the rows (0 or 1: one); hmid [nb, dff], y [nb, d]
 };
 
-// TEAL projection: y = sum over kept inputs j (|x_j| > t, after the optional
-// RMSNorm) of x_j w_t[j], w_t [d_in, d_out]; P slices of the kept list (each
-// at most kTealList channels) x column tiles of 4096 outputs.
-constexpr int kTealList = 64;
-constexpr int kTealMinBlocks = 64;   // slices x tiles, at least (measured: 64 beats 128 and 256)
-constexpr int kTealMaxParts = 512;   // d_in <= kTealList * kTealMaxParts
-struct TealGrid {
-  int parts, tiles;
-};
-TealGrid teal_grid(int d_in, int d_out);
+// TEAL projection over column blocks: y = sum over kept inputs j (|x_j| > t,
+// after the optional RMSNorm) of x_j w[j, :], the weight stored in blocks of
+// kTealBlock output columns, w_blk [nblk][d_in][kTealBlock] (nblk =
+// ceil(d_out / kTealBlock), padding columns past d_out never written out).
+// Grid (slices, blocks): slice s takes the input channels [s R, (s + 1) R)
+// of the input, block b the columns [b kTealBlock, (b + 1) kTealBlock); the
+// last slice of a block to finish adds the slices' partial sums and applies
+// the epilogue.
+constexpr int kTealBlock = 128;
+constexpr int kTealMaxRange = 2048;  // input channels per slice, at most
+constexpr int kTealMaxSlices = 32;
+constexpr int kTealMaxBlocks = 1024; // blocks' tickets in the workspace
+enum TealEpi { TEAL_STORE = 0, TEAL_ACC = 1, TEAL_SWIGLU = 2, TEAL_QKV = 3 };
+int teal_slices(int d_in, int d_out);
 
 struct TealArgs {
   int kind;            // profiler kind of this projection
@@ -119,11 +123,17 @@ struct TealArgs {
   int d_in;
   const float* norm;   // nullptr: no RMSNorm
   float eps, t;        // t < 0: keep every channel
-  const void* w0;      // [d_in, d_out]
+  const void* w0;      // column blocks [nblk][d_in][kTealBlock]
   const void* w1;      // optional second matrix with the same input (gate and up)
   int d_out;
-  float* part0;        // [parts, d_out]
-  float* part1;
+  float* part;         // [slices, nblk kTealBlock] per matrix (w1's after w0's)
+  unsigned* tickets;   // [nblk]: zero before the launch, zero again after it
+  int epi;             // TealEpi
+  float* y;            // STORE / ACC: the outputs of w0; SWIGLU: SiLU(y0) * y1
+  float* y2;           // STORE / ACC with w1: its outputs
+  float t_next;        // SWIGLU: the next projection's threshold, for
+  uint8_t* keep_next;  //   keep_next[c] = |SiLU(y0) y1| > t_next (t_next < 0: all)
+  QkvArgs qkv;         // QKV: RoPE table, q out, cache appends (qkv.h unused)
   int32_t* idx_out;    // optional ascending kept list
   int32_t* n_kept_out; // optional
   uint8_t* keep_out;   // optional keep bytes [d_in]
@@ -226,15 +236,9 @@ void launch_o(const float* attn, const void* w, int din, int dout, float* h, int
               hipStream_t s);
 void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s);
 void launch_down(const DownArgs& a, int w_dtype, hipStream_t s);
-void launch_teal(const TealArgs& a, int w_dtype, hipStream_t s);
-// y (+)= column sums of the partials, or y = SiLU(sums of part0) * sums of part1;
-// keep (optional): keep[c] = |y[c]| > t (t < 0: every column)
-void launch_teal_reduce(const float* part0, const float* part1, int parts, int d_out, float* y,
-                        int accumulate, int swiglu, int kind, hipStream_t s, float t = -1.f,
-                        uint8_t* keep = nullptr);
-// QKV epilogue over the column sums: RoPE, q out, k and v appended (a.h is unused)
-void launch_teal_qkv_reduce(const float* part, int parts, const QkvArgs& a, int kv_dtype,
-                            hipStream_t s);
+void launch_teal(const TealArgs& a, int w_dtype, int kv_dtype, hipStream_t s);
+// zero n ticket words (before the first TEAL projection of a call)
+void launch_teal_zero(unsigned* tickets, int n, hipStream_t s);
 void launch_attn(const AttnArgs& a, int kv_dtype, hipStream_t s);
 // Masked dense attention over every allocated row (rows >= n_ctx masked): scores
 // of each query head into `scores` [h_q, cap], a row softmax, then P.V in

@@ -40,9 +40,8 @@ const char* kKindNames[K_COUNT] = {
     "qkv_rope_append", "attn_partial",  "attn_combine",    "o_residual",    "cats_gate_up",
     "cats_down",       "cats_reduce", "sel_lse_partial", "sel_lse_final", "sel_score",
     "sel_topk",        "sel_gather",    "kth_select",      "masked_scores", "masked_softmax",
-    "masked_pv",       "teal_qkv",      "teal_qkv_reduce", "teal_o",        "teal_gate_up",
-    "teal_down",       "teal_reduce",   "batch_qkv",       "batch_rope",    "batch_o",
-    "batch_gate_up"};
+    "masked_pv",       "teal_qkv",      "teal_zero",       "teal_o",        "teal_gate_up",
+    "teal_down",       "batch_qkv",     "batch_rope",      "batch_o",       "batch_gate_up"};
 
 }  // namespace
 

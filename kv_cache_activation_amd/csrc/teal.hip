@@ -1,34 +1,40 @@
-// TEAL-style sparse projections: column-gathered GEMV over the kept input
-// channels (gfx950, wave64).
+// TEAL-style sparse projections over column blocks of the weight (gfx950,
+// wave64).
 //
 // "Where Activation Sparsity and KV-Cache Sparsity Cross in LLM Decoding"
 // takes its projection branch from TEAL (§3.2 "Sparse Branches", §4.1
 // "Setup"): each of a layer's seven projections keeps only the input
 // channels whose magnitude clears a calibrated threshold and loads only those
-// channels' weights.  With the weight stored transposed, w_t [d_in, d_out],
-// a kept input channel j is one contiguous row, and
-//     y = sum over kept j of x_j w_t[j]
-// reads exactly the kept rows.
+// channels' weights, y = sum over kept j of x_j w[j, :].
 //
-// One launch, grid (P slices, column tiles of 4096 outputs, or 1024 with
-// four row groups for a narrow single matrix whose slices leave compute
-// units idle).  A workgroup
-//   1. reads the whole input vector (one chunk per thread), applies the
-//      RMSNorm when given (x * rs * norm_w, rs reduced over the workgroup),
-//      decides keep_j = |x_j| > t (t < 0: all) in float32, and takes an
-//      exclusive block scan of the per-thread counts, which ranks every kept
-//      channel; the ranks [s n_k / P, (s + 1) n_k / P) form its slice, so
-//      every workgroup reads the same number of rows whatever the mask;
-//   2. streams its slice's rows over its column tile: wave v owns the
-//      8-column chunks of 512 columns, lane j holds x of list entry j, and a
-//      batch of rows is loaded with no branch between the loads (entries
-//      past the slice repeat its last row with weight 0);
-//   3. writes a partial sum [d_out] per slice.  With two weight matrices
-//      (gate and up share their input) it does both.
-// A second launch adds the P partials of each column in a fixed order and
-// applies the projection's epilogue: plain (y = or +=), SwiGLU
-// (hmid = SiLU(gate) * up), or the QKV epilogue (RoPE on q and k, q out,
-// k and v rounded and appended to the caches).  Deterministic.
+// Layout.  The weight is stored in blocks of 128 output columns,
+// w_blk [nblk][d_in][128]: within a block, input channel j is one contiguous
+// 256-byte piece (bf16), and a block's rows are contiguous.  A workgroup that
+// owns one block reads, for each kept channel, exactly that channel's piece:
+// two whole 128-byte lines, with no other workgroup sharing them.
+//
+// Grid (S slices, nblk blocks), 256 threads.  Workgroup (s, b):
+//   1. with an RMSNorm, adds up x^2 over the whole input (every workgroup
+//      needs the scale); then decides keep_j = |x_j * rs * norm_j| > t (t < 0:
+//      all) in float32 for the channels of its slice [s R, (s + 1) R) and
+//      ranks the kept ones in channel order (block scan of per-thread counts);
+//   2. streams the kept channels' pieces of block b: lane l loads 16 bytes of
+//      row (l / 16) of a group of four, so a wave instruction brings four
+//      rows and the four waves sixteen; U instructions per wave are issued
+//      before any arithmetic, entries past the list's end repeat its last
+//      row with weight 0;
+//   3. adds its sixteen row groups in LDS in a fixed order and stores the
+//      slice's partial sums of the block with agent-scope stores (written
+//      through to memory, where every XCD's loads see them), then takes a
+//      ticket for the block;
+//   4. the slice that draws the last ticket of the block adds the S partials
+//      in slice order (agent-scope loads), clears the ticket for the next
+//      launch, and applies the projection's epilogue to the block's columns:
+//      y = or y +=; SwiGLU with the next projection's keep bytes; or RoPE on q
+//      and k with q written out and k, v rounded and appended to the caches.
+// No workgroup waits for another: the ones that do not finish last exit, and
+// the last one finds every partial stored.  One launch per projection, and
+// the summation order is fixed, so results do not depend on scheduling.
 #include <math.h>
 
 #include "common.hpp"
@@ -36,346 +42,322 @@
 
 namespace sd {
 
-constexpr int kTealThreads = 512;
-constexpr int kTealWaves = kTealThreads / kWave;
-constexpr int kTealTile = kTealWaves * kWave * 8;  // 4096 output columns per workgroup
-constexpr int kRCols = 16, kRSlices = 16;          // QKV reduce: 16 columns x 16 slices
-constexpr int kRCols2 = 32;  // plain reduce: 32 columns, so a partial is read in 128-byte pieces
-constexpr int kRPer = kTealMaxParts / kRSlices;    // partitions per slice, at most
+constexpr int kTbThreads = 256;
+constexpr int kTbWaves = kTbThreads / kWave;   // 4
+constexpr int kTbSub = kWave / 16;             // rows per wave load instruction (4)
+constexpr int kTbGroups = kTbWaves * kTbSub;   // row groups of a workgroup (16)
+constexpr int kTbCh = kTealMaxRange / kTbThreads;  // slice channels per thread, at most (8)
+static_assert(kTealBlock == 16 * 8, "a block row is 16 lanes x 8 columns");
 
-// NQ float4 chunks of the input per thread (d_in <= 4 NQ 512).
-// RG row groups: the workgroup's column tile is kTealTile / RG columns and
-// its eight waves form RG groups that take interleaved rows of the slice;
-// the groups' sums are added in LDS in a fixed order.  RG > 1 gives narrow
-// projections (O, QKV) more workgroups at the same slice count, so the
-// partial sums do not grow.
-template <typename WT, int NQ, bool DUAL, int RG>
-__global__ __launch_bounds__(kTealThreads) void teal_kernel(
-    const float* __restrict__ x, int d_in, const float* __restrict__ nw, float eps, float t,
-    const WT* __restrict__ W0, const WT* __restrict__ W1, int d_out,
-    float* __restrict__ part0, float* __restrict__ part1, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ n_kept_out, uint8_t* __restrict__ keep_out) {
-  constexpr int U = (DUAL ? 32 : 64) / (int)sizeof(WT) / RG;  // rows per batch, matrix and group
-  constexpr int CW = kTealWaves / RG;                          // waves per row group
-  constexpr int TILE = kTealTile / RG;                         // output columns per workgroup
-  __shared__ int list[kTealList];
-  __shared__ float xl[kTealList];
-  __shared__ int wave_tot[kTealWaves];
-  __shared__ float red[kTealWaves];
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <typename WT, bool DUAL, int EPI, typename KT>
+__global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
+  // rows per wave instruction group in flight: 8 instructions (32 rows) per
+  // matrix and wave for bf16, half for float32
+  constexpr int U = (DUAL ? 8 : 16) * 2 / (int)sizeof(WT);
+  __shared__ int list[kTealMaxRange];
+  __shared__ float xl[kTealMaxRange];
+  __shared__ int wave_tot[kTbWaves];
+  __shared__ float wred[kTbWaves];
+  __shared__ float red[kTbGroups][(DUAL ? 2 : 1) * kTealBlock];
+  __shared__ float col[(DUAL ? 2 : 1) * kTealBlock];
+  __shared__ unsigned tk_s;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int S = gridDim.x, s = blockIdx.x, b = blockIdx.y;
+  const int d_in = a.d_in, d_out = a.d_out;
+  const int nblk = gridDim.y;
+  const float* __restrict__ x = a.x;
+  const float* __restrict__ nw = a.norm;
 
-  // 1. this thread's inputs [c0, c0 + 4 NQ)
-  const int c0 = threadIdx.x * 4 * NQ;
-  float4 xv[NQ];
-  float ss = 0.f;
+  // 1. this slice's inputs (and norm weights) are loaded with the pass that
+  //    adds up x^2 for the RMSNorm scale, so both take one memory round trip
+  const int R = (d_in + S - 1) / S;
+  const int r0 = s * R, r1 = min(d_in, r0 + R);
+  const int ch = (R + kTbThreads - 1) / kTbThreads;  // <= kTbCh
+  const int c0 = r0 + threadIdx.x * ch;              // this thread's channels [c0, c0 + ch)
+  float xv[kTbCh], wv[kTbCh];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int i = c0 + 4 * q;
-    xv[q] = i < d_in ? *reinterpret_cast<const float4*>(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-    ss = fmaf(xv[q].x, xv[q].x, fmaf(xv[q].y, xv[q].y, fmaf(xv[q].z, xv[q].z, fmaf(xv[q].w, xv[q].w, ss))));
+  for (int k = 0; k < kTbCh; ++k) {
+    const int c = min(c0 + k, d_in - 1);  // unconditional loads, discarded past the slice
+    xv[k] = k < ch ? x[c] : 0.f;
+    wv[k] = nw && k < ch ? nw[c] : 1.f;
   }
-  if (nw) {  // RMSNorm: x * rs * nw
+  float rs = 1.f;
+  if (nw) {
+    float ss = 0.f;
+    for (int i = 4 * threadIdx.x; i < d_in; i += 4 * kTbThreads) {
+      const float4 v = *reinterpret_cast<const float4*>(x + i);
+      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    }
     ss = wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
+    if (lane == 0) wred[wave] = ss;
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int v = 0; v < kTealWaves; ++v) tot += red[v];
-    const float rs = 1.0f / sqrtf(tot / (float)d_in + eps);
+    for (int v = 0; v < kTbWaves; ++v) tot += wred[v];
+    rs = 1.0f / sqrtf(tot / (float)d_in + a.eps);
+  }
+  uint32_t mask = 0;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int i = c0 + 4 * q;
-      if (i < d_in) {
-        const float4 w = *reinterpret_cast<const float4*>(nw + i);
-        xv[q] = make_float4(xv[q].x * rs * w.x, xv[q].y * rs * w.y, xv[q].z * rs * w.z,
-                            xv[q].w * rs * w.w);
-      }
+  for (int k = 0; k < kTbCh; ++k) {
+    float v = 0.f;
+    if (k < ch && c0 + k < r1) {
+      v = xv[k];
+      if (nw) v = v * rs * wv[k];
+      if (a.t < 0.f || fabsf(v) > a.t) mask |= 1u << k;
     }
+    xv[k] = v;
   }
-  uint64_t mask = 0;
+  if (a.keep_out && b == 0) {
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const float e[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (c0 + 4 * q + k < d_in && (t < 0.f || fabsf(e[k]) > t)) mask |= 1ull << (4 * q + k);
+    for (int k = 0; k < kTbCh; ++k)
+      if (k < ch && c0 + k < r1) a.keep_out[c0 + k] = (uint8_t)((mask >> k) & 1u);
   }
-  if (keep_out && blockIdx.x == 0 && blockIdx.y == 0) {
-#pragma unroll
-    for (int b = 0; b < 4 * NQ; ++b)
-      if (c0 + b < d_in) keep_out[c0 + b] = (uint8_t)((mask >> b) & 1ull);
-  }
-  const int cnt = __popcll(mask);
+  const int cnt = __popc(mask);
   const int incl = wave_incl_scan(cnt);
   if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
-  int before = incl - cnt, n_k = 0;
+  int before = incl - cnt, m = 0;
 #pragma unroll
-  for (int v = 0; v < kTealWaves; ++v) {
+  for (int v = 0; v < kTbWaves; ++v) {
     before += v < wave ? wave_tot[v] : 0;
-    n_k += wave_tot[v];
+    m += wave_tot[v];
   }
-  const int P = gridDim.x, s = blockIdx.x;
-  const int lo = (int)((int64_t)s * n_k / P);
-  const int hi = (int)((int64_t)(s + 1) * n_k / P);
-  if (before < hi && before + cnt > lo) {  // this thread holds part of the slice
+  {
     int r = before;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const float e[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if ((mask >> (4 * q + k)) & 1ull) {
-          if (r >= lo && r < hi) {
-            list[r - lo] = c0 + 4 * q + k;
-            xl[r - lo] = e[k];
-            if (idx_out && blockIdx.y == 0) idx_out[r] = c0 + 4 * q + k;
-          }
-          ++r;
-        }
+    for (int k = 0; k < kTbCh; ++k)
+      if ((mask >> k) & 1u) {
+        list[r] = c0 + k;
+        xl[r] = xv[k];
+        ++r;
       }
-    }
   }
-  if (n_kept_out && s == 0 && blockIdx.y == 0 && threadIdx.x == 0) *n_kept_out = n_k;
+  if ((a.idx_out || a.n_kept_out) && b == 0) {
+    // ranks before this slice: the kept channels of [0, r0), same rule
+    int prior = 0;
+    for (int c = threadIdx.x; c < r0; c += kTbThreads) {
+      float v = x[c];
+      if (nw) v = v * rs * nw[c];
+      prior += (a.t < 0.f || fabsf(v) > a.t) ? 1 : 0;
+    }
+    prior = (int)wave_sum((float)prior);  // exact below 2^24
+    __syncthreads();
+    if (lane == 0) wave_tot[wave] = prior;
+    __syncthreads();
+    int off = 0;
+#pragma unroll
+    for (int v = 0; v < kTbWaves; ++v) off += wave_tot[v];
+    if (a.idx_out) {
+      int r = before;
+#pragma unroll
+      for (int k = 0; k < kTbCh; ++k)
+        if ((mask >> k) & 1u) a.idx_out[off + r++] = c0 + k;
+    }
+    if (a.n_kept_out && s == S - 1 && threadIdx.x == 0) *a.n_kept_out = off + m;
+  }
   __syncthreads();
-  const int m = hi - lo;  // <= kTealList (the host sizes P so)
 
-  // 2. rows of the slice over this workgroup's column tile; row group rg
-  //    takes list entries rg, rg + RG, ...
-  const int rg = __builtin_amdgcn_readfirstlane(wave / CW), cw = wave - rg * CW;
-  const int d8 = d_out >> 3;
-  const int c8 = blockIdx.y * (TILE / 8) + cw * kWave + lane;
-  const bool col_ok = c8 < d8;
-  const float hv = lane < m ? xl[lane] : 0.f;
+  // 2. the kept channels' pieces of block b; lane (sub, q): row sub of each
+  //    group of four, columns 8q .. 8q + 7 of the block
+  const int sub = lane >> 4, q = lane & 15;
+  const WT* __restrict__ W0 = static_cast<const WT*>(a.w0) + (size_t)b * d_in * kTealBlock + 8 * q;
+  const WT* __restrict__ W1 =
+      DUAL ? static_cast<const WT*>(a.w1) + (size_t)b * d_in * kTealBlock + 8 * q : nullptr;
   float acc0[8], acc1[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
-  if (m > 0 && col_ok) {
+  const int g = wave * kTbSub + sub;  // this lane's row group
 #pragma unroll 1
-    for (int j0 = rg; j0 < m; j0 += U * RG) {
-      Vec8<WT> g0[U], g1[DUAL ? U : 1];
+  for (int j0 = 0; j0 < m; j0 += U * kTbGroups) {
+    Vec8<WT> w0[U], w1[DUAL ? U : 1];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const size_t row = (size_t)list[min(j0 + RG * u, m - 1)] * d_out + 8 * c8;
-        g0[u].load(W0 + row);
-        if constexpr (DUAL) g1[u].load(W1 + row);
+    for (int u = 0; u < U; ++u) {
+      const int j = min(j0 + u * kTbGroups + g, m - 1);
+      const uint32_t off = (uint32_t)list[j] * kTealBlock;  // d_in * 128 < 2^32
+      w0[u].load(W0 + off);
+      if constexpr (DUAL) w1[u].load(W1 + off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kTbGroups + g;
+      const float h = j < m ? xl[min(j, m - 1)] : 0.f;
+      float f[8];
+      w0[u].to_float(f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc0[e] = fmaf(h, f[e], acc0[e]);
+      if constexpr (DUAL) {
+        w1[DUAL ? u : 0].to_float(f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc1[e] = fmaf(h, f[e], acc1[e]);
       }
+    }
+  }
+
+  // 3. the row groups in a fixed order, then this slice's partial sums
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + RG * u;  // wave-uniform
-        const float hj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), min(j, 63)));
-        const float h = j < m ? hj : 0.f;
-        float f[8];
-        g0[u].to_float(f);
+  for (int e = 0; e < 8; ++e) {
+    red[g][8 * q + e] = acc0[e];
+    if constexpr (DUAL) red[g][kTealBlock + 8 * q + e] = acc1[e];
+  }
+  __syncthreads();
+  constexpr int NCOL = (DUAL ? 2 : 1) * kTealBlock;  // <= kTbThreads
+  const int bw = nblk * kTealBlock;                  // a slice's partial width per matrix
+  float* part = a.part + (size_t)s * bw;
+  if (threadIdx.x < NCOL) {
+    float v = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc0[e] = fmaf(h, f[e], acc0[e]);
-        if constexpr (DUAL) {
-          g1[DUAL ? u : 0].to_float(f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc1[e] = fmaf(h, f[e], acc1[e]);
+    for (int k = 0; k < kTbGroups; ++k) v += red[k][threadIdx.x];
+    const int mat = threadIdx.x / kTealBlock, cc = threadIdx.x % kTealBlock;
+    store_agent(part + (size_t)mat * S * bw + b * kTealBlock + cc, v);
+    __builtin_amdgcn_s_waitcnt(0);  // stored before the ticket
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    tk_s = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tk_s != (unsigned)(S - 1)) return;  // workgroup-uniform: not the block's last slice
+
+  // 4. the block's column sums over the slices, in slice order
+  if (threadIdx.x < NCOL) {
+    const int mat = threadIdx.x / kTealBlock, cc = threadIdx.x % kTealBlock;
+    const float* p = a.part + (size_t)mat * S * bw + b * kTealBlock + cc;
+    float v = 0.f;
+    for (int k = 0; k < S; ++k) v += load_agent(p + (size_t)k * bw);
+    col[threadIdx.x] = v;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int cb = b * kTealBlock;
+  if constexpr (EPI == TEAL_STORE || EPI == TEAL_ACC) {
+    if (threadIdx.x < NCOL) {
+      const int mat = threadIdx.x / kTealBlock, c = cb + threadIdx.x % kTealBlock;
+      float* y = mat ? a.y2 : a.y;
+      if (c < d_out) y[c] = (EPI == TEAL_ACC ? y[c] : 0.f) + col[threadIdx.x];
+    }
+  } else if constexpr (EPI == TEAL_SWIGLU) {
+    if (threadIdx.x < kTealBlock) {
+      const int c = cb + threadIdx.x;
+      if (c < d_out) {
+        const float h = silu(col[threadIdx.x]) * col[kTealBlock + threadIdx.x];
+        a.y[c] = h;
+        if (a.keep_next) a.keep_next[c] = a.t_next < 0.f || fabsf(h) > a.t_next;
+      }
+    }
+  } else {  // TEAL_QKV: rotation pairs (i, i + d_h/2) of the heads within the block
+    const QkvArgs& qa = a.qkv;
+    const int dh = qa.dh, half = dh >> 1;
+    if (threadIdx.x < kTealBlock / 2) {
+      const int hb = threadIdx.x / half;            // head within the block
+      const int i = threadIdx.x - hb * half;
+      const int head = (cb / dh) + hb;
+      const int ca = hb * dh + i;                   // block-local columns of the pair
+      if (cb + ca < d_out) {
+        float va = col[ca], vb = col[ca + half];
+        if (head < qa.h_q + qa.h_kv) {  // rotate q and k, not v
+          const float cs = qa.rope.c[i], sn = qa.rope.s[i];
+          const float ra = va * cs - vb * sn, rb = vb * cs + va * sn;
+          va = ra;
+          vb = rb;
+        }
+        if (head < qa.h_q) {
+          qa.q_out[head * dh + i] = va;
+          qa.q_out[head * dh + i + half] = vb;
+        } else {
+          const bool is_k = head < qa.h_q + qa.h_kv;
+          const int kv = is_k ? head - qa.h_q : head - qa.h_q - qa.h_kv;
+          KT* full = static_cast<KT*>(is_k ? qa.k_full : qa.v_full);
+          const size_t off = ((size_t)kv * qa.cap_full + qa.row_full) * dh + i;
+          store_elem(full + off, va);
+          store_elem(full + off + half, vb);
+          if (qa.k_sel) {
+            KT* sel = static_cast<KT*>(is_k ? qa.k_sel : qa.v_sel);
+            // ragged budgets: each KV head appends at its own row
+            const int rsel = qa.ragged ? qa.sel_rows.v[kv & (kMaxKvHeads - 1)] : qa.row_sel;
+            const size_t offs = ((size_t)kv * qa.cap_sel + rsel) * dh + i;
+            store_elem(sel + offs, va);
+            store_elem(sel + offs + half, vb);
+          }
         }
       }
     }
   }
-  if constexpr (RG > 1) {  // row groups 1.. add into group 0, in order
-    __shared__ float grp[kTealWaves * kWave * 8];  // 16 KB
-    static_assert(!DUAL, "row groups are for single-matrix projections");
-    if (rg > 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) grp[((wave - CW) * kWave + lane) * 8 + e] = acc0[e];
-    }
-    __syncthreads();
-    if (rg == 0) {
-#pragma unroll
-      for (int r = 1; r < RG; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc0[e] += grp[(((r - 1) * CW + cw) * kWave + lane) * 8 + e];
-    }
-  }
-  // 3. partial sums of this slice
-  if (rg == 0 && col_ok) {
-    store8(part0 + (size_t)s * d_out + 8 * c8, acc0);
-    if constexpr (DUAL) store8(part1 + (size_t)s * d_out + 8 * c8, acc1);
-  }
 }
 
-// Sum of the P partials of column c: slice sl of the column sums partitions
-// [sl per, sl per + per) in order, then the slices are added in order.
-template <int COLS>
-__device__ __forceinline__ float column_sum(const float* __restrict__ part, int P, int d_out,
-                                            int c, int sl, int cl, float (*red)[COLS]) {
-  const int per = (P + kRSlices - 1) / kRSlices;
-  const int w0 = sl * per;
-  float v[kRPer];
-#pragma unroll
-  for (int i = 0; i < kRPer; ++i)
-    v[i] = (c < d_out && i < per && w0 + i < P) ? part[(size_t)(w0 + i) * d_out + c] : 0.f;
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRPer; ++i)
-    if (i < per && w0 + i < P) sum += v[i];
-  red[sl][cl] = sum;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int k = 0; k < kRSlices; ++k) tot += red[k][cl];
-  return tot;
+__global__ void teal_zero_kernel(unsigned* __restrict__ t, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) t[i] = 0u;
 }
 
-// y[c] (+)= sum of partials (EPI 0), or y[c] = SiLU(sum part0) * (sum part1) (EPI 1).
-// keep (optional): keep[c] = |y[c]| > t (t < 0: 1), decided on the float32
-// value stored, the rule the next projection applies to its input.
-template <int EPI>
-__global__ __launch_bounds__(kRCols2 * kRSlices) void teal_reduce_kernel(
-    const float* __restrict__ part0, const float* __restrict__ part1, int P, int d_out,
-    float* __restrict__ y, int accumulate, float t, uint8_t* __restrict__ keep) {
-  __shared__ float red0[kRSlices][kRCols2], red1[kRSlices][kRCols2];
-  const int cl = threadIdx.x % kRCols2, sl = threadIdx.x / kRCols2;
-  const int c = blockIdx.x * kRCols2 + cl;
-  const float a = column_sum<kRCols2>(part0, P, d_out, c, sl, cl, red0);
-  float b = 0.f;
-  if (EPI == 1) b = column_sum<kRCols2>(part1, P, d_out, c, sl, cl, red1);
-  if (sl == 0 && c < d_out) {
-    const float v = EPI == 1 ? silu(a) * b : accumulate ? y[c] + a : a;
-    y[c] = v;
-    if (keep) keep[c] = t < 0.f || fabsf(v) > t;
-  }
+// Slices per projection: about two workgroups per compute unit over all
+// blocks, at most kTealMaxRange input channels per slice, at most
+// kTealMaxSlices slices.
+int teal_slices(int d_in, int d_out) {
+  const int nblk = (d_out + kTealBlock - 1) / kTealBlock;
+  int s = (2 * cu_count_dev() + nblk - 1) / nblk;
+  const int need = (d_in + kTealMaxRange - 1) / kTealMaxRange;
+  if (s < need) s = need;
+  if (s > kTealMaxSlices) s = kTealMaxSlices;
+  const int most = (d_in + 7) / 8;  // at least 8 channels per slice
+  if (s > most) s = most;
+  return s < 1 ? 1 : s;
 }
 
-// QKV epilogue: a workgroup owns 8 rotation pairs (i, i + d_h/2) of one head:
-// columns head d_h + i0 .. +8 and head d_h + d_h/2 + i0 .. +8 (d_h/2 % 8 == 0).
-template <typename KT>
-__global__ __launch_bounds__(kRCols * kRSlices) void teal_qkv_reduce_kernel(
-    const float* __restrict__ part, int P, int d_out, int h_q, int h_kv, int dh,
-    RopeTable rope, float* __restrict__ q_out, KT* __restrict__ k_full, KT* __restrict__ v_full,
-    int cap_full, int row_full, KT* __restrict__ k_sel, KT* __restrict__ v_sel, int cap_sel,
-    int row_sel, int ragged, HeadInts sel_rows) {
-  __shared__ float red[kRSlices][kRCols];
-  __shared__ float tot[kRCols];
-  const int half = dh >> 1;
-  const int per_head = half / 8;  // workgroups per head
-  const int head = blockIdx.x / per_head, i0 = (blockIdx.x % per_head) * 8;
-  const int cl = threadIdx.x % kRCols, sl = threadIdx.x / kRCols;
-  const int c = head * dh + (cl < 8 ? i0 + cl : half + i0 + cl - 8);
-  const float v = column_sum<kRCols>(part, P, d_out, c, sl, cl, red);
-  if (sl == 0) tot[cl] = v;
-  __syncthreads();
-  if (threadIdx.x >= 8) return;
-  const int i = i0 + threadIdx.x;
-  float a = tot[threadIdx.x], b = tot[threadIdx.x + 8];
-  if (head < h_q + h_kv) {  // rotate q and k, not v
-    const float cs = rope.c[i], sn = rope.s[i];
-    const float ra = a * cs - b * sn, rb = b * cs + a * sn;
-    a = ra;
-    b = rb;
-  }
-  if (head < h_q) {
-    q_out[head * dh + i] = a;
-    q_out[head * dh + i + half] = b;
-  } else {
-    const bool is_k = head < h_q + h_kv;
-    const int kv = is_k ? head - h_q : head - h_q - h_kv;
-    KT* full = is_k ? k_full : v_full;
-    const size_t off = ((size_t)kv * cap_full + row_full) * dh + i;
-    store_elem(full + off, a);
-    store_elem(full + off + half, b);
-    if (k_sel) {
-      KT* sel = is_k ? k_sel : v_sel;
-      // ragged budgets: each KV head appends at its own row
-      const int rsel = ragged ? sel_rows.v[kv & (kMaxKvHeads - 1)] : row_sel;
-      const size_t offs = ((size_t)kv * cap_sel + rsel) * dh + i;
-      store_elem(sel + offs, a);
-      store_elem(sel + offs + half, b);
-    }
-  }
-}
-
-TealGrid teal_grid(int d_in, int d_out) {
-  TealGrid g;
-  g.tiles = (d_out + kTealTile - 1) / kTealTile;
-  int p = kTealMinBlocks / g.tiles;
-  const int need = (d_in + kTealList - 1) / kTealList;
-  if (p < need) p = need;
-  if (p < 1) p = 1;
-  g.parts = p;
-  return g;
-}
-
-// Row groups for a projection: four for a single matrix of at most 8192
-// outputs whose slices and tiles fill at most half the compute units (O and
-// QKV of the 8B-class layer: 256 and 384 workgroups at 64 slices instead of
-// 64 and 128), one otherwise.  Measured on MI355X: the down projection (224
-// slices of a 14336-wide input) went from 20.6 to 25.7 us per launch with
-// four groups, its rows read in 2 KB pieces with no idle units to gain.
-template <bool DUAL>
-static int teal_row_groups(const TealGrid& g, int d_out) {
-  return !DUAL && d_out <= 8192 && 2 * g.parts * g.tiles <= cu_count_dev() ? 4 : 1;
-}
-
-template <typename WT, bool DUAL>
+template <typename WT, bool DUAL, typename KT>
 static void teal_typed(const TealArgs& a, hipStream_t s) {
-  const TealGrid g = teal_grid(a.d_in, a.d_out);  // slices as the workspace is sized
-  const int rgs = teal_row_groups<DUAL>(g, a.d_out);
-  const int tiles = (a.d_out + kTealTile / rgs - 1) / (kTealTile / rgs);
-  const int nq4 = (a.d_in + 4 * kTealThreads - 1) / (4 * kTealThreads);  // float4 per thread
-#define SD_TEAL(NQ, RGV)                                                                    \
-  launch_kernel(a.kind, teal_kernel<WT, NQ, DUAL, RGV>, dim3(g.parts, tiles),                \
-                dim3(kTealThreads), 0, s, a.x, a.d_in, a.norm, a.eps, a.t, (const WT*)a.w0,   \
-                (const WT*)a.w1, a.d_out, a.part0, a.part1, a.idx_out, a.n_kept_out,          \
-                a.keep_out)
-#define SD_TEAL_RG(NQ)           \
-  do {                           \
-    if constexpr (!DUAL) {       \
-      if (rgs == 4) {            \
-        SD_TEAL(NQ, 4);          \
-        break;                   \
-      }                          \
-    }                            \
-    SD_TEAL(NQ, 1);              \
-  } while (0)
-  if (nq4 <= 2) SD_TEAL_RG(2);
-  else if (nq4 <= 4) SD_TEAL_RG(4);
-  else if (nq4 <= 8) SD_TEAL_RG(8);
-  else SD_TEAL_RG(16);
-#undef SD_TEAL_RG
-#undef SD_TEAL
-}
-
-void launch_teal(const TealArgs& a, int w_dtype, hipStream_t s) {
-  const bool dual = a.w1 != nullptr;
-  if (w_dtype == 1) {
-    if (dual) teal_typed<bf16_t, true>(a, s);
-    else teal_typed<bf16_t, false>(a, s);
-  } else {
-    if (dual) teal_typed<float, true>(a, s);
-    else teal_typed<float, false>(a, s);
+  const dim3 grid(teal_slices(a.d_in, a.d_out), (a.d_out + kTealBlock - 1) / kTealBlock);
+  switch (a.epi) {
+    case TEAL_STORE:
+      launch_kernel(a.kind, teal_kernel<WT, DUAL, TEAL_STORE, KT>, grid, dim3(kTbThreads), 0, s, a);
+      break;
+    case TEAL_ACC:
+      launch_kernel(a.kind, teal_kernel<WT, DUAL, TEAL_ACC, KT>, grid, dim3(kTbThreads), 0, s, a);
+      break;
+    case TEAL_SWIGLU:
+      if constexpr (DUAL)
+        launch_kernel(a.kind, teal_kernel<WT, true, TEAL_SWIGLU, KT>, grid, dim3(kTbThreads), 0,
+                      s, a);
+      break;
+    default:
+      if constexpr (!DUAL)
+        launch_kernel(a.kind, teal_kernel<WT, false, TEAL_QKV, KT>, grid, dim3(kTbThreads), 0, s,
+                      a);
+      break;
   }
 }
 
-void launch_teal_reduce(const float* part0, const float* part1, int parts, int d_out, float* y,
-                        int accumulate, int swiglu, int kind, hipStream_t s, float t,
-                        uint8_t* keep) {
-  const dim3 grid((d_out + kRCols2 - 1) / kRCols2), block(kRCols2 * kRSlices);
-  if (swiglu)
-    launch_kernel(kind, teal_reduce_kernel<1>, grid, block, 0, s, part0, part1, parts, d_out, y,
-                  accumulate, t, keep);
-  else
-    launch_kernel(kind, teal_reduce_kernel<0>, grid, block, 0, s, part0, part1, parts, d_out, y,
-                  accumulate, t, keep);
+void launch_teal(const TealArgs& a, int w_dtype, int kv_dtype, hipStream_t s) {
+  const bool dual = a.w1 != nullptr;
+  if (a.epi == TEAL_QKV) {  // single matrix; the cache type matters
+    if (w_dtype == 1) {
+      if (kv_dtype == 1) teal_typed<bf16_t, false, bf16_t>(a, s);
+      else teal_typed<bf16_t, false, float>(a, s);
+    } else {
+      if (kv_dtype == 1) teal_typed<float, false, bf16_t>(a, s);
+      else teal_typed<float, false, float>(a, s);
+    }
+    return;
+  }
+  if (w_dtype == 1) {
+    if (dual) teal_typed<bf16_t, true, float>(a, s);
+    else teal_typed<bf16_t, false, float>(a, s);
+  } else {
+    if (dual) teal_typed<float, true, float>(a, s);
+    else teal_typed<float, false, float>(a, s);
+  }
 }
 
-void launch_teal_qkv_reduce(const float* part, int parts, const QkvArgs& a, int kv_dtype,
-                            hipStream_t s) {
-  const int d_out = (a.h_q + 2 * a.h_kv) * a.dh;
-  const dim3 grid((a.h_q + 2 * a.h_kv) * (a.dh / 2 / 8)), block(kRCols * kRSlices);
-#define SD_QKV_R(KT)                                                                          \
-  launch_kernel(K_TEAL_QKV_REDUCE, teal_qkv_reduce_kernel<KT>, grid, block, 0, s, part, parts, \
-                d_out, a.h_q, a.h_kv, a.dh, a.rope, a.q_out, (KT*)a.k_full, (KT*)a.v_full,     \
-                a.cap_full, a.row_full, (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel,       \
-                a.ragged, a.sel_rows)
-  if (kv_dtype == 1) SD_QKV_R(bf16_t);
-  else SD_QKV_R(float);
-#undef SD_QKV_R
+void launch_teal_zero(unsigned* tickets, int n, hipStream_t s) {
+  launch_kernel(K_TEAL_ZERO, teal_zero_kernel, dim3(1), dim3(256), 0, s, tickets, n);
 }
 
 }  // namespace sd

@@ -85,3 +85,14 @@ def plant_keys(wl: Workload, layer: int, k, n: int, q_win, n_planted: int):
     key = (4.0 * wl.head_dim ** 0.5) * s / s.norm(dim=1, keepdim=True)
     k[:, pos.to(k.device)] = key.to(k.dtype)[:, None, :]
     return pos
+
+
+def teal_blocked(w, block: int = 128):
+    """W [d_out, d_in] (nn.Linear order) in the column-block layout of the
+    TEAL projections: [ceil(d_out / block)][d_in][block], columns past d_out
+    zero.  A relayout only."""
+    d_out, d_in = w.shape
+    nblk = (d_out + block - 1) // block
+    wt = torch.zeros(nblk * block, d_in, dtype=w.dtype, device=w.device)
+    wt[:d_out] = w
+    return wt.view(nblk, block, d_in).transpose(1, 2).contiguous()

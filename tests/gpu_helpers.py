@@ -35,6 +35,13 @@ def to_dev(a: np.ndarray, dtype: str = "f32") -> torch.Tensor:
     return t.to(DEV)
 
 
+def teal_dev(w_out_in: np.ndarray, dtype: str = "f32") -> torch.Tensor:
+    """A projection W [d_out, d_in] on the device in the column-block layout
+    the TEAL projections read ([ceil(d_out / 128)][d_in][128])."""
+    from synth import device as sdev
+    return sdev.teal_blocked(to_dev(np.ascontiguousarray(w_out_in), dtype))
+
+
 def to_host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 

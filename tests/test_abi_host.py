@@ -232,7 +232,7 @@ def test_window_and_baseline_reject_before_launch():
     (dict(t=float("nan")), sd.SD_EINVAL),
     (dict(flags=1), sd.SD_EINVAL),
     (dict(w2=FAKE, y2=None), sd.SD_EINVAL),
-    (dict(d_in=14336, d_out=14336, w2=FAKE, y2=FAKE), sd.SD_ENOSPC),
+    (dict(d_in=32768, d_out=32768, w2=FAKE, y2=FAKE), sd.SD_ENOSPC),
     (dict(ws_bytes=64), sd.SD_ENOSPC),
 ])
 def test_teal_gemv_rejects_before_launch(case, status):
@@ -244,16 +244,16 @@ def test_teal_gemv_rejects_before_launch(case, status):
     assert e.value.status == status
 
 
-def test_decode_step_teal_needs_transposed_weights_and_no_cats():
+def test_decode_step_teal_needs_block_weights_and_no_cats():
     L = (sd.sd_layer * 1)()
     l = L[0]
     for f in ("attn_norm", "mlp_norm", "w_down_t", "k_full", "v_full"):
         setattr(l, f, FAKE)
     l.cap_full, l.n_full = 100, 10
     ws = _FakeWs(1 << 30)
-    with pytest.raises(sd.SdError) as e:  # no transposed weights
+    with pytest.raises(sd.SdError) as e:  # no column-block weights
         sd.sd_decode_step(_dims(), L, 10, FAKE, sd.SD_PROJ_TEAL, ws, 0)
-    assert e.value.status == sd.SD_EINVAL and "transposed" in sd.sd_last_error()
+    assert e.value.status == sd.SD_EINVAL and "column-block" in sd.sd_last_error()
     for f in ("w_qkv_t", "w_o_t", "w_gate_t", "w_up_t"):
         setattr(l, f, FAKE)
     with pytest.raises(sd.SdError) as e:  # excludes CATS

@@ -15,8 +15,8 @@ from oracle import teal as oteal, step as ostep
 pytestmark = pytest.mark.gpu
 
 sd = pytest.importorskip("kv_cache_activation_amd")
-from gpu_helpers import (DEV, TOL, dims_for, midpoint_threshold, rel_l2, to_dev, to_host,  # noqa
-                         workspace)
+from gpu_helpers import (DEV, TOL, dims_for, midpoint_threshold, rel_l2, teal_dev, to_dev,  # noqa
+                         to_host, workspace)
 from test_gpu_step import Stack  # noqa: E402
 
 
@@ -33,8 +33,9 @@ class Gemv:
         self.wt = _weight_t(r, d_in, d_out, wl.dtype)
         self.wt2 = _weight_t(r, d_in, d_out, wl.dtype) if dual else None
         self.norm = (1.0 + 0.1 * r.standard_normal(d_in)).astype(np.float32)
-        self.dw = to_dev(self.wt, wl.dtype)
-        self.dw2 = to_dev(self.wt2, wl.dtype) if dual else None
+        # the device copies in the column-block layout of W = wt^T
+        self.dw = teal_dev(self.wt.T, wl.dtype)
+        self.dw2 = teal_dev(self.wt2.T, wl.dtype) if dual else None
         self.y = torch.empty(d_out, device=DEV)
         self.y2 = torch.empty(d_out, device=DEV) if dual else None
         self.idx = torch.empty(d_in, dtype=torch.int32, device=DEV)
@@ -127,7 +128,7 @@ def test_teal_gemv_is_deterministic():
 # ------------------------------------------------------------------ the step
 
 class TealStack(Stack):
-    """Stack plus the transposed weights and the mask buffers of SD_PROJ_TEAL."""
+    """Stack plus the column-block weights and the mask buffers of SD_PROJ_TEAL."""
 
     def __init__(self, wl, n_layers, n, k_keep, **kw):
         super().__init__(wl, n_layers, n, k_keep, **kw)
@@ -139,8 +140,7 @@ class TealStack(Stack):
         self.mask_sizes = (d, qd, d, ff)
         for li in range(n_layers):
             W = synth.layer_weights(wl, li)
-            dt = {k: to_dev(np.ascontiguousarray(W[k].T), wl.dtype)
-                  for k in ("w_qkv", "w_o", "w_gate", "w_up")}
+            dt = {k: teal_dev(W[k], wl.dtype) for k in ("w_qkv", "w_o", "w_gate", "w_up")}
             masks = torch.zeros(sum(self.mask_sizes), dtype=torch.uint8, device=DEV)
             self.teal_keep.append((dt, masks))
             L = self.layers[li]
@@ -239,7 +239,7 @@ def test_8b_teal_layer_matches_oracle_with_its_masks(kv_sparse):
 
 @pytest.mark.parametrize("t_down", [1e30, -1.0])
 def test_tiny_fp32_teal_step_down_input_all_dropped_or_all_kept(t_down):
-    # the step decides the down projection's mask in the SwiGLU reduce and
+    # the step decides the down projection's mask in the SwiGLU epilogue and
     # streams the kept rows with the kept-row kernel: with every down input
     # dropped the MLP adds nothing, with t < 0 it reads every row
     wl = synth.TINY
@@ -267,10 +267,9 @@ def test_tiny_fp32_teal_step_down_input_all_dropped_or_all_kept(t_down):
 @pytest.mark.parametrize("d_in,d_out", [(32768, 4096), (32768, 8192), (4096, 8192), (4096, 8000),
                                         (6144, 1000)])
 @pytest.mark.parametrize("norm", [False, True])
-def test_teal_gemv_widest_inputs_and_row_group_tails(d_in, d_out, norm):
-    # the widest input the library accepts (64 channels x 512 slices), and
-    # single-matrix outputs on the four-row-group form (1024-column tiles)
-    # with a ragged last tile
+def test_teal_gemv_widest_inputs_and_ragged_last_block(d_in, d_out, norm):
+    # the widest input the library accepts (32768 channels over 16 slices of
+    # 2048), and outputs whose last 128-column block is partly padding
     # dims whose widths cover these sizes (the workspace is sized from them)
     wl = dataclasses.replace(synth.L8B_DENSE_8K, name="teal-widest", wid=7, d_model=8192,
                              n_q_heads=64, d_ff=32768)
