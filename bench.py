@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--catekv-contexts", type=str, default="32768,131072")
     ap.add_argument("--batches", type=str, default="4,8")
     ap.add_argument("--batch-contexts", type=str, default="8192,32768")
+    ap.add_argument("--batch-paths", type=str, default="vector,matrix_cores",
+                    help="batched projections on the vector ALUs and/or the matrix cores")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--out", type=str, default="")
     ap.add_argument("--pmc-copy-bytes", type=int, default=0,
@@ -224,6 +226,27 @@ class Stack:
             L.teal_masks_out = None
         del self.WT, self.TMASK
         self.teal = False
+        self.torch.cuda.empty_cache()
+
+    def enable_tiles(self):
+        """The batched matrix-core path reads the five projections in 16-row x
+        32-channel tiles, packed on the device by the library."""
+        torch, sd = self.torch, self.sd
+        self.TILES = []
+        for li in range(self.L):
+            W, L, t = self.W[li], self.layers[li], {}
+            for f, w in (("w_qkv_m", W["w_qkv"]), ("w_o_m", W["w_o"]), ("w_gate_m", W["w_gate"]),
+                         ("w_up_m", W["w_up"]), ("w_down_m", W["w_down_t"].t().contiguous())):
+                t[f] = torch.empty(sd.sd_tile_bytes(*w.shape), dtype=torch.uint8, device=self.dev)
+                sd.sd_pack_tiles(w, w.shape[0], w.shape[1], t[f])
+                setattr(L, f, t[f].data_ptr())
+            self.TILES.append(t)
+        torch.cuda.synchronize()
+
+    def disable_tiles(self):
+        for L in self.layers:
+            L.w_qkv_m = L.w_o_m = L.w_gate_m = L.w_up_m = L.w_down_m = None
+        del self.TILES
         self.torch.cuda.empty_cache()
 
     # -------------------------------------------------------------- stepping
@@ -731,15 +754,17 @@ def attention_baselines(stack, n, window_ratio=0.3, steps=4, warmup=1):
                 window_speedup=speedup, window_byte_bound=rec.bound_kv)
 
 
-def batch_cells(stack, n, B, modes):
+def batch_cells(stack, n, B, modes, matrix_cores=False):
     """Batched decode ([Cross] §3.3 "Dispatch and batching", §4.4
     "Batching"): B sequences of context n, each with its own synthetic
     caches, selection and hidden state, stepped together so that every
     weight row is read once per step.  Per mode: µs per step (median block
     of a shorter protocol: blocks of a fifth of the sweep's length),
     tokens/s, algorithmic GB/s (weights once, the union's up and down rows
-    under CATS, every sequence's cache rows), and the measured union
-    fraction u_B of the CATS masks."""
+    under CATS, every sequence's cache rows), the measured union fraction
+    u_B of the CATS masks, and per-kernel times of one more block (library
+    profiler).  matrix_cores: the projections on the matrix cores (tile
+    weights), which read up and down whole."""
     torch, sd, wl, args = stack.torch, stack.sd, stack.wl, stack.args
     from synth import device as sdev
     bs = max(1, args.block_steps // 5)
@@ -773,7 +798,7 @@ def batch_cells(stack, n, B, modes):
     row = 2 * wl.n_kv_heads * dh * 2
     out = []
     for mode in modes:
-        flags = stack.mode_flags(mode)
+        flags = stack.mode_flags(mode) | (sd.SD_MATRIX_CORES if matrix_cores else 0)
         for c in kv:
             c.n_full, c.n_sel = n, k_keep
         hid.copy_(h0)
@@ -793,10 +818,29 @@ def batch_cells(stack, n, B, modes):
         base = k_keep if flags & sd.SD_KV_SPARSE else n
         n_read = base + bs + (args.blocks * bs - 1) / 2.0 + 1
         b_step = stack.L * (w_attn + 2 * d * wl.d_ff * (1 + 2 * u) + B * row * n_read)
-        out.append(dict(context=n, batch=B, mode=mode, us=us, us_min=blk[0], us_max=blk[-1],
-                        tokens_per_s=B / (us * 1e-6), bytes=b_step, gbs=b_step / us / 1e3,
-                        frac=b_step / us / 1e3 / HBM_PEAK_GBS,
-                        union_fraction=u if flags & sd.SD_MLP_SPARSE else None))
+        # per-kernel times of one more block; bytes as the account assigns them
+        torch.cuda.synchronize()
+        sd.sd_profile_start()
+        run(0, bs)
+        stats = sd.sd_profile_stop()
+        qd = wl.n_q_heads * dh
+        alg = {"batch_qkv": 2 * d * wl.qkv_out, "batch_o": 2 * qd * d,
+               "batch_gate_up": 2 * d * wl.d_ff * (1 + u), "batch_down": 2 * d * wl.d_ff * u,
+               "cats_down": 2 * d * wl.d_ff * u,
+               "attn_partial": B * row * (n_read + bs)}
+        kern = {}
+        for name, (launches, tot) in stats.items():
+            avg = tot / launches * 1e3
+            e = dict(launches=launches, avg_us=avg)
+            if name in alg:
+                e["gbs"] = alg[name] / (avg * 1e-6) / 1e9
+                e["frac"] = e["gbs"] / HBM_PEAK_GBS
+            kern[name] = e
+        out.append(dict(context=n, batch=B, mode=mode,
+                        path="matrix_cores" if matrix_cores else "vector", us=us, us_min=blk[0],
+                        us_max=blk[-1], tokens_per_s=B / (us * 1e-6), bytes=b_step,
+                        gbs=b_step / us / 1e3, frac=b_step / us / 1e3 / HBM_PEAK_GBS,
+                        union_fraction=u if flags & sd.SD_MLP_SPARSE else None, kernels=kern))
     del keep, kv, ws, scores, idx, sws
     torch.cuda.empty_cache()
     return out
@@ -1093,11 +1137,18 @@ def main():
             attn_frac={k: v["attn_frac_of_peak"] for k, v in base["paths"].items()}), 3))
     if "batch" in legs and args.batches:
         cells = []
+        paths = [p for p in args.batch_paths.split(",") if p]
+        if "matrix_cores" in paths:
+            stack.enable_tiles()
         for n in [int(c) for c in args.batch_contexts.split(",") if c]:
             for B in [int(b) for b in args.batches.split(",") if b]:
-                for c in batch_cells(stack, n, B, HEAD_MODES):
-                    cells.append(c)
-                    note("batch", rnd(c, 3))
+                for path in paths:
+                    for c in batch_cells(stack, n, B, HEAD_MODES, path == "matrix_cores"):
+                        cells.append(c)
+                        note("batch", rnd({k: v for k, v in c.items() if k != "kernels"}, 3))
+                        note("batch_kernels", rnd(c["kernels"], 3))
+        if "matrix_cores" in paths:
+            stack.disable_tiles()
         union = {}
         for B in sorted({c["batch"] for c in cells}):
             us = [c["union_fraction"] for c in cells if c["batch"] == B and c["union_fraction"]]

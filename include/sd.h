@@ -85,7 +85,8 @@ enum {
   SD_ATTN_MASKED = 32u, /* sd_decode_step: dense attention by the masked comparison path */
   SD_ATTN_FUSED = 64u,  /* sd_decode_step: dense attention by the fused (no split-K) path */
   SD_PROJ_TEAL = 128u,  /* sd_decode_step: TEAL-threshold the inputs of all seven projections */
-  SD_ACCUMULATE = 256u  /* sd_teal_gemv: y += result instead of y = result */
+  SD_ACCUMULATE = 256u, /* sd_teal_gemv: y += result instead of y = result */
+  SD_MATRIX_CORES = 512u /* sd_decode_step_batch: projections on the matrix cores (tile weights) */
 };
 
 /* output columns per block of the TEAL weight layout (sd_teal_gemv) */
@@ -321,6 +322,13 @@ typedef struct {
   int32_t* n_sel_heads;    /* optional [h_kv] [host]: per-KV-head valid gathered rows (ragged
                               budgets of sd_select_kv_ragged); replaces n_sel when not NULL,
                               each entry advanced by one; excludes SD_KV_WINDOW */
+  /* sd_decode_step_batch with SD_MATRIX_CORES: bf16 weights in the tile layout
+   * of sd_pack_tiles (the other modes and entry points do not read them) */
+  const void* w_qkv_m;     /* W_qkv [(h_q + 2 h_kv) d_h, d] */
+  const void* w_o_m;       /* W_o [d, h_q d_h] */
+  const void* w_gate_m;    /* W_gate [d_ff, d] */
+  const void* w_up_m;      /* W_up [d_ff, d] */
+  const void* w_down_m;    /* W_down [d, d_ff] (the down projection itself, not w_down_t) */
 } sd_layer;
 
 /*
@@ -401,21 +409,45 @@ size_t sd_batch_workspace_bytes(const sd_dims* dims, int32_t batch);
  * the up rows and down columns read are those of the union of the batch's
  * masks (a channel kept by at least one sequence); a sequence that dropped a
  * channel gets no contribution from it.
+ * SD_MATRIX_CORES runs the five projections as matrix products on the
+ * matrix cores instead (bf16 weights in the tile layout, w_*_m of sd_layer;
+ * float32 inputs split exactly into three bf16 parts, float32 sums): same
+ * results to float32 rounding, same masks and union.  That path reads up and
+ * down whole rather than the union's rows: at the batch sizes it is for, the
+ * union keeps nearly every channel.
  * layers  [host] [n_layers]: weights, norms and cats_threshold as in
  *         sd_decode_step (its cache fields are not used); mask_out, when not
  *         NULL, receives the union mask [d_ff] (1 kept by some sequence).
  * kv      [host] [batch * n_layers], sequence-major (kv[b * n_layers + l]):
  *         each sequence's caches; n_full and n_sel advanced on success.
  * pos     [host] [batch] positions; hidden [batch, d] float32, in place.
- * mode    0, SD_KV_SPARSE, SD_MLP_SPARSE or both.
+ * mode    0, SD_KV_SPARSE, SD_MLP_SPARSE or both, optionally | SD_MATRIX_CORES.
  * Sizes:  d_model and n_q_heads * d_h at most 4096.
  * Errors: EINVAL for batch outside 2..8, other mode bits, bad pointers or a
- *         missing gathered buffer under SD_KV_SPARSE; ENOSPC for a full cache or
- *         a short workspace (sd_batch_workspace_bytes); EUNSUPPORTED for widths.
+ *         missing gathered buffer under SD_KV_SPARSE, or SD_MATRIX_CORES
+ *         without all five tile weights; ENOSPC for a full cache or a short
+ *         workspace (sd_batch_workspace_bytes); EUNSUPPORTED for widths, or
+ *         SD_MATRIX_CORES with float32 weights.
  */
 sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_layer* layers,
                                int32_t batch, sd_seq_kv* kv, const int32_t* pos, float* hidden,
                                uint32_t mode, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sd_pack_tiles -- a bf16 weight W [rows, d_in] (row-major, d_in a multiple of
+ * 8, 16-byte aligned) rewritten into the tile layout that SD_MATRIX_CORES
+ * reads: tiles of 16 rows by steps of 32 input channels, each (tile, step)
+ * 1 KB in the A-operand order of the gfx950 matrix core, element (r, c) at
+ * index ((r / 16) S + c / 32) 512 + ((r % 16) + 16 ((c % 32) / 8)) 8 + c % 8,
+ * S = ceil(d_in / 32), padding rows and channels zero ([Cross] §3.3
+ * "Dispatch and batching": a batch shares one read of every weight).
+ * out     device, SD_TILE_BYTES(rows, d_in) bytes, 16-byte aligned, not
+ *         overlapping w; enqueued on `stream`.
+ * Errors: EINVAL for bad pointers or sizes.
+ */
+#define SD_TILE_BYTES(rows, d_in) \
+  ((((size_t)(rows) + 15) / 16) * (((size_t)(d_in) + 31) / 32) * (size_t)1024)
+sd_status sd_pack_tiles(const void* w, int32_t rows, int32_t d_in, void* out, void* stream);
 
 /* Byte account record ([Cross] §3). Bytes as doubles (exact below 2^53). */
 typedef struct {

@@ -27,14 +27,14 @@ SD_OK, SD_EINVAL, SD_ENOSPC, SD_EUNSUPPORTED, SD_EHIP = range(5)
 SD_F32, SD_BF16 = 0, 1
 SD_SCORES_IN, SD_GATE_IN, SD_KV_SPARSE, SD_MLP_SPARSE = 1, 2, 4, 8
 SD_KV_WINDOW, SD_ATTN_MASKED, SD_ATTN_FUSED = 16, 32, 64
-SD_PROJ_TEAL, SD_ACCUMULATE = 128, 256
+SD_PROJ_TEAL, SD_ACCUMULATE, SD_MATRIX_CORES = 128, 256, 512
 SD_PROJ_ALL7, SD_PROJ_FFN, SD_PROJ_CATS = 0, 1, 2
 
 EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_decode_attn",
            "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
            "sd_decode_step", "sd_decode_step_noalloc", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account",
-           "sd_byte_crossover_batch", "sd_latency_fit", "sd_latency_crossing", "sd_latency_gate",
+           "sd_pack_tiles", "sd_byte_crossover_batch", "sd_latency_fit", "sd_latency_crossing", "sd_latency_gate",
            "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
@@ -63,7 +63,10 @@ class sd_layer(ctypes.Structure):
                 ("w_qkv_t", ctypes.c_void_p), ("w_o_t", ctypes.c_void_p),
                 ("w_gate_t", ctypes.c_void_p), ("w_up_t", ctypes.c_void_p),
                 ("teal_t", ctypes.c_float * 4), ("teal_masks_out", ctypes.c_void_p),
-                ("n_sel_heads", ctypes.POINTER(ctypes.c_int32))]
+                ("n_sel_heads", ctypes.POINTER(ctypes.c_int32)),
+                ("w_qkv_m", ctypes.c_void_p), ("w_o_m", ctypes.c_void_p),
+                ("w_gate_m", ctypes.c_void_p), ("w_up_m", ctypes.c_void_p),
+                ("w_down_m", ctypes.c_void_p)]
 
 
 class sd_seq_kv(ctypes.Structure):
@@ -112,6 +115,8 @@ _lib.sd_decode_step_batch.restype = _I
 _lib.sd_decode_step_batch.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_layer), _I,
                                       ctypes.POINTER(sd_seq_kv), ctypes.POINTER(_I), _P, _U, _P,
                                       _S, _P]
+_lib.sd_pack_tiles.restype = _I
+_lib.sd_pack_tiles.argtypes = [_P, _I, _I, _P, _P]
 _lib.sd_decode_attn.restype = _I
 _lib.sd_decode_attn.argtypes = [ctypes.POINTER(sd_dims), _P, _P, _P, _I, _I, _F, _I, _P, _P,
                                 _P, _S, _P]
@@ -286,6 +291,15 @@ def sd_decode_step_batch(dims, layers, kv, pos, hidden, mode, ws, stream=None) -
     _check(_lib.sd_decode_step_batch(ctypes.byref(dims), n_layers, layers, batch, kv,
                                      _host_ints(pos), _ptr(hidden), mode, p, nb,
                                      _stream(stream)))
+
+
+def sd_tile_bytes(rows: int, d_in: int) -> int:
+    """Bytes of a [rows, d_in] weight in the tile layout (SD_TILE_BYTES)."""
+    return ((rows + 15) // 16) * ((d_in + 31) // 32) * 1024
+
+
+def sd_pack_tiles(w, rows, d_in, out, stream=None) -> None:
+    _check(_lib.sd_pack_tiles(_ptr(w), rows, d_in, _ptr(out), _stream(stream)))
 
 
 def sd_decode_step(dims, layers, pos, hidden, mode, ws, stream=None) -> None:

@@ -557,6 +557,17 @@ sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const 
   return check_launch("sd_teal_gemv");
 }
 
+sd_status sd_pack_tiles(const void* w, int32_t rows, int32_t d_in, void* out, void* stream) {
+  if (!aligned(w) || !aligned(out)) return fail(SD_EINVAL, "null or misaligned pointer");
+  if (rows < 1 || d_in < 8 || d_in % 8)
+    return fail(SD_EINVAL, "rows must be positive and d_in a positive multiple of 8");
+  const size_t in_bytes = (size_t)rows * d_in * 2, out_bytes = SD_TILE_BYTES(rows, d_in);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(out);
+  if (a < b + out_bytes && b < a + in_bytes) return fail(SD_EINVAL, "out overlaps w");
+  sd::launch_pack_tiles(w, rows, d_in, out, static_cast<hipStream_t>(stream));
+  return check_launch("sd_pack_tiles");
+}
+
 sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers, int32_t pos,
                          float* hidden, uint32_t mode, void* ws, size_t ws_bytes, void* stream) {
   sd_status st = check_dims(dims);
@@ -762,7 +773,9 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
 // every sequence in stream order) plus the batch's own buffers.
 struct BatchLayout {
   Layout base;
-  size_t qkv, q, attn, pm, pl, pacc, act, hmid, keep, uni, part, total;
+  size_t qkv, q, attn, pm, pl, pacc, act, hmid, keep, uni, part, mm_part, mm_ssq, mm_tickets,
+      total;
+  int mm_groups;
 };
 
 BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
@@ -787,6 +800,21 @@ BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
   B.keep = take(n * ff);
   B.uni = take(ff);
   B.part = take((size_t)sd::down_parts((int)ff) * n * d * 4);
+  {  // matrix-core path: the largest of the layer's four launches
+    const int qo = (int)((hq + 2 * hkv) * dh), od = (int)(hq * dh);
+    const size_t pf = std::max(std::max(sd::bmma_part_floats(qo, (int)d, false),
+                                        sd::bmma_part_floats((int)d, od, false)),
+                               std::max(sd::bmma_part_floats((int)ff, (int)d, true),
+                                        sd::bmma_part_floats((int)d, (int)ff, false)));
+    const size_t sf = std::max(sd::bmma_ssq_floats(qo, (int)d, false),
+                               sd::bmma_ssq_floats((int)ff, (int)d, true));
+    const int groups = std::max(std::max(sd::bmma_groups(qo), sd::bmma_groups((int)d)),
+                                sd::bmma_groups((int)ff));
+    B.mm_part = take(pf * 4);
+    B.mm_ssq = take(sf * 4);
+    B.mm_tickets = take((size_t)groups * 4);
+    B.mm_groups = groups;
+  }
   B.total = off;
   return B;
 }
@@ -851,16 +879,27 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
   if (st) return st;
   if (n_layers < 1 || !layers || !kv || !pos || !aligned(hidden) || !aligned(ws))
     return fail(SD_EINVAL, "null or misaligned argument");
-  if (mode & ~(uint32_t)(SD_KV_SPARSE | SD_MLP_SPARSE))
-    return fail(SD_EINVAL, "batched step modes: SD_KV_SPARSE and/or SD_MLP_SPARSE");
+  if (mode & ~(uint32_t)(SD_KV_SPARSE | SD_MLP_SPARSE | SD_MATRIX_CORES))
+    return fail(SD_EINVAL,
+                "batched step modes: SD_KV_SPARSE and/or SD_MLP_SPARSE, optionally SD_MATRIX_CORES");
   const bool kv_sparse = mode & SD_KV_SPARSE, mlp_sparse = mode & SD_MLP_SPARSE;
+  const bool mc = mode & SD_MATRIX_CORES;
+  if (mc && dims->w_dtype != SD_BF16)
+    return fail(SD_EUNSUPPORTED, "SD_MATRIX_CORES needs bf16 weights");
   const BatchLayout B = make_batch_layout(*dims, batch);
   if (ws_bytes < B.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, B.total);
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
-    if (!aligned(l.attn_norm) || !aligned(l.mlp_norm) || !aligned(l.w_qkv) || !aligned(l.w_o) ||
-        !aligned(l.w_gate) || !aligned(l.w_up) || !aligned(l.w_down_t))
+    if (!aligned(l.attn_norm) || !aligned(l.mlp_norm))
+      return fail(SD_EINVAL, "layer %d: null or misaligned norm weights", i);
+    if (mc) {
+      if (!aligned(l.w_qkv_m) || !aligned(l.w_o_m) || !aligned(l.w_gate_m) ||
+          !aligned(l.w_up_m) || !aligned(l.w_down_m))
+        return fail(SD_EINVAL, "layer %d: SD_MATRIX_CORES needs the five tile weights", i);
+    } else if (!aligned(l.w_qkv) || !aligned(l.w_o) || !aligned(l.w_gate) || !aligned(l.w_up) ||
+               !aligned(l.w_down_t)) {
       return fail(SD_EINVAL, "layer %d: null or misaligned weight", i);
+    }
     if (std::isnan(l.cats_threshold)) return fail(SD_EINVAL, "layer %d: threshold is NaN", i);
     if (l.mask_out && !aligned(l.mask_out))
       return fail(SD_EINVAL, "layer %d: misaligned mask_out", i);
@@ -889,21 +928,49 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
   float* qkv = reinterpret_cast<float*>(wsb + B.qkv);
   float* q = reinterpret_cast<float*>(wsb + B.q);
   float* attn = reinterpret_cast<float*>(wsb + B.attn);
+  unsigned* mm_tickets = reinterpret_cast<unsigned*>(wsb + B.mm_tickets);
+  // one matrix-core projection of the batch (tile weights w0, and w1 for up)
+  auto mm = [&](int kind, const float* x, int d_in, const float* norm, const void* w0,
+                const void* w1, int rows, int epi, float* out) {
+    sd::BmmaArgs m{};
+    m.kind = kind;
+    m.x = x;
+    m.nb = batch;
+    m.d_in = d_in;
+    m.norm = norm;
+    m.eps = dims->rms_eps;
+    m.w0 = w0;
+    m.w1 = w1;
+    m.rows = rows;
+    m.epi = epi;
+    m.out = out;
+    m.part = reinterpret_cast<float*>(wsb + B.mm_part);
+    m.ssq = reinterpret_cast<float*>(wsb + B.mm_ssq);
+    m.tickets = mm_tickets;
+    return m;
+  };
+  if (mc) sd::launch_teal_zero(mm_tickets, B.mm_groups, s);  // every launch leaves them zero
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
     // QKV for every sequence from one read of W_qkv, then RoPE and the appends
     sd::BgemvArgs g{};
-    g.kind = sd::K_BATCH_QKV;
-    g.x = hidden;
-    g.nb = batch;
-    g.d_in = d;
-    g.norm = l.attn_norm;
-    g.eps = dims->rms_eps;
-    g.w = l.w_qkv;
-    g.rows = qkv_out;
-    g.mode = 0;
-    g.out = qkv;
-    sd::launch_bgemv(g, dims->w_dtype, s);
+    if (mc) {
+      sd::launch_bmma(mm(sd::K_BATCH_QKV, hidden, d, l.attn_norm, l.w_qkv_m, nullptr, qkv_out,
+                         sd::MM_STORE, qkv),
+                      s);
+    } else {
+      g.kind = sd::K_BATCH_QKV;
+      g.x = hidden;
+      g.nb = batch;
+      g.d_in = d;
+      g.norm = l.attn_norm;
+      g.eps = dims->rms_eps;
+      g.w = l.w_qkv;
+      g.rows = qkv_out;
+      g.mode = 0;
+      g.out = qkv;
+      sd::launch_bgemv(g, dims->w_dtype, s);
+    }
     sd::BatchKv kvs{};
     for (int b = 0; b < batch; ++b) {
       const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
@@ -955,6 +1022,28 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
       a.sink = a.n_ctx;
       sd::launch_attn(a, dims->kv_dtype, s);
     }
+    uint8_t* uni = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + B.uni);
+    float* hmid = reinterpret_cast<float*>(wsb + B.hmid);
+    if (mc) {
+      // O with the residual; gate and up with the CATS gate, the union and
+      // hmid; down with the residual (hmid is zero where a sequence dropped
+      // the channel)
+      sd::launch_bmma(mm(sd::K_BATCH_O, attn, hq * dh, nullptr, l.w_o_m, nullptr, d,
+                         sd::MM_RESID, hidden),
+                      s);
+      sd::BmmaArgs m = mm(sd::K_BATCH_GATE_UP, hidden, d, l.mlp_norm, l.w_gate_m, l.w_up_m, ff,
+                          sd::MM_SWIGLU, nullptr);
+      m.t = mlp_sparse ? l.cats_threshold : -1.0f;
+      m.act = reinterpret_cast<float*>(wsb + B.act);
+      m.keep = reinterpret_cast<uint8_t*>(wsb + B.keep);
+      m.hmid = hmid;
+      m.uni = uni;
+      sd::launch_bmma(m, s);
+      sd::launch_bmma(mm(sd::K_BATCH_DOWN, hmid, ff, nullptr, l.w_down_m, nullptr, d,
+                         sd::MM_RESID, hidden),
+                      s);
+      continue;
+    }
     // O with the residual, for every sequence from one read of W_o
     g = sd::BgemvArgs{};
     g.kind = sd::K_BATCH_O;
@@ -967,8 +1056,6 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
     g.out = hidden;
     sd::launch_bgemv(g, dims->w_dtype, s);
     // CATS gate per sequence, the union, the union's up rows
-    uint8_t* uni = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + B.uni);
-    float* hmid = reinterpret_cast<float*>(wsb + B.hmid);
     g = sd::BgemvArgs{};
     g.kind = sd::K_BATCH_GATE_UP;
     g.x = hidden;

@@ -28,6 +28,56 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// ---------------------------------------------------------------- cross-workgroup
+// Agent-scope (device-coherent) stores and loads of float32 partial sums that
+// one workgroup writes and another, possibly on another XCD, reads after a
+// ticket: the stores are written through to memory, the loads bypass the
+// XCD-local caches.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// ---------------------------------------------------------------- matrix cores
+// Operand type of v_mfma_f32_16x16x32_bf16 (eight bf16 values per lane).
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight float32 values as three bf16 parts, hi + mid + lo == x: hi carries
+// the top 8 significand bits, mid the next 8 (x - hi is exact in float32),
+// lo the rest.  Products of a part with a bf16 value are exact in float32, so
+// a matrix-core sum over the three parts keeps float32 accuracy.
+__device__ __forceinline__ void split3_bf16(const float (&x)[8], u32x4& hi, u32x4& mid,
+                                            u32x4& lo) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t hh[2], mm[2], ll[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float v = x[2 * p + e];
+      const bf16_t bh = f32_to_bf16(v);
+      const float r1 = v - bf16_lo((uint32_t)bh);
+      const bf16_t bm = f32_to_bf16(r1);
+      hh[e] = bh;
+      mm[e] = bm;
+      ll[e] = f32_to_bf16(r1 - bf16_lo((uint32_t)bm));
+    }
+    h[p] = hh[0] | (hh[1] << 16);
+    m[p] = mm[0] | (mm[1] << 16);
+    l[p] = ll[0] | (ll[1] << 16);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  mid = u32x4{m[0], m[1], m[2], m[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Eight consecutive elements of a row as float32, from one 16-byte load
 // (bf16) or two (float32).  p must be 16-byte aligned.
 template <typename T> struct Vec8;

@@ -17,7 +17,8 @@ enum KernelKind {
   K_QKV, K_ATTN_PARTIAL, K_ATTN_COMBINE, K_O, K_GATE_UP, K_DOWN, K_MLP_REDUCE, K_SEL_LSE,
   K_SEL_LSE_FINAL, K_SEL_SCORE, K_SEL_TOPK, K_SEL_GATHER, K_KTH, K_MASKED_SCORES,
   K_MASKED_SOFTMAX, K_MASKED_PV, K_TEAL_QKV, K_TEAL_ZERO, K_TEAL_O, K_TEAL_GATE_UP,
-  K_TEAL_DOWN, K_BATCH_QKV, K_BATCH_ROPE, K_BATCH_O, K_BATCH_GATE_UP, K_COUNT
+  K_TEAL_DOWN, K_BATCH_QKV, K_BATCH_ROPE, K_BATCH_O, K_BATCH_GATE_UP, K_BATCH_DOWN,
+  K_PACK_TILES, K_COUNT
 };
 
 // Start/stop events of one launch of kind `kind` while profiling is on (both
@@ -230,6 +231,38 @@ void launch_bgemv(const BgemvArgs& a, int w_dtype, hipStream_t s);
 void launch_brope_append(const float* qkv, int nb, int qkv_out, int h_q, int h_kv, int dh,
                          float theta, const BatchKv& kvs, float* q, int kv_dtype, hipStream_t s);
 int cu_count_dev();
+
+// Batched projections on the matrix cores, weights in 16-row x 32-channel
+// tiles (A-operand order of v_mfma_f32_16x16x32_bf16, bf16 only).  Grid
+// (input slices, bmma_groups row groups of 128 rows); the last
+// slice of a row group to finish sums the slices' partials and applies the
+// epilogue.
+enum { MM_STORE = 0, MM_RESID = 1, MM_SWIGLU = 2 };
+struct BmmaArgs {
+  int kind;
+  const float* x;      // [nb, d_in] float32 (d_in % 8 == 0)
+  int nb, d_in;
+  const float* norm;   // RMSNorm weights [d_in], or nullptr
+  float eps;
+  const void* w0;      // tiles of W [rows, d_in]
+  const void* w1;      // MM_SWIGLU: tiles of W_up (same shape); nullptr otherwise
+  int rows, epi;
+  float* out;          // MM_STORE: out = y; MM_RESID: out += y ([nb, rows])
+  float t;             // MM_SWIGLU: CATS threshold (t < 0 keeps every channel)
+  float* act;          // MM_SWIGLU outputs [nb, rows]: SiLU(gate), keep bytes, hmid,
+  uint8_t* keep;       //   and the union uni [rows]
+  float* hmid;
+  uint8_t* uni;
+  float* part;         // bmma_part_floats(rows, d_in, w1 != nullptr)
+  float* ssq;          // bmma_ssq_floats(...) (with a norm)
+  unsigned* tickets;   // [bmma_groups(rows)]: zero before the launch, zero after it
+};
+int bmma_groups(int rows);
+size_t bmma_part_floats(int rows, int d_in, bool dual);
+size_t bmma_ssq_floats(int rows, int d_in, bool dual);
+void launch_bmma(const BmmaArgs& a, hipStream_t s);
+// W [rows, d_in] bf16 row-major (d_in % 8 == 0) -> the tile layout
+void launch_pack_tiles(const void* w, int rows, int d_in, void* out, hipStream_t s);
 
 void launch_qkv(const QkvArgs& a, int w_dtype, int kv_dtype, hipStream_t s);
 void launch_o(const float* attn, const void* w, int din, int dout, float* h, int w_dtype,

@@ -41,7 +41,8 @@ const char* kKindNames[K_COUNT] = {
     "cats_down",       "cats_reduce", "sel_lse_partial", "sel_lse_final", "sel_score",
     "sel_topk",        "sel_gather",    "kth_select",      "masked_scores", "masked_softmax",
     "masked_pv",       "teal_qkv",      "teal_zero",       "teal_o",        "teal_gate_up",
-    "teal_down",       "batch_qkv",     "batch_rope",      "batch_o",       "batch_gate_up"};
+    "teal_down",       "batch_qkv",     "batch_rope",      "batch_o",       "batch_gate_up",
+    "batch_down",      "pack_tiles"};
 
 }  // namespace
 

@@ -231,40 +231,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_score_kernel(
 //   LDS -> the chunk partial, as the vector-ALU kernel writes it.  score pass:
 //   each key's sum over the queries of 2^(z - lse), lanes of one column added
 //   with lane swaps, accumulated over the query tiles in a fixed order.
-typedef __attribute__((ext_vector_type(8))) __bf16 sel_bf16x8;
 constexpr int kSelQB = 64;  // queries staged per batch (four 16-row tiles)
 constexpr int kSelSub = 1;  // key chunks per workgroup (measured: staging once for 2 or 4
                             // chunks, or batches of 128 queries, were no faster)
-
-__device__ __forceinline__ sel_bf16x8 sel_as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(sel_bf16x8, v);
-}
-
-// Eight float32 values as three bf16 parts (hi + mid + lo == x to 24 bits).
-__device__ __forceinline__ void sel_split3(const float (&x)[8], u32x4& hi, u32x4& mid,
-                                           u32x4& lo) {
-  uint32_t h[4], m[4], l[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t hh[2], mm[2], ll[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float v = x[2 * p + e];
-      const bf16_t bh = f32_to_bf16(v);
-      const float r1 = v - bf16_lo((uint32_t)bh);
-      const bf16_t bm = f32_to_bf16(r1);
-      hh[e] = bh;
-      mm[e] = bm;
-      ll[e] = f32_to_bf16(r1 - bf16_lo((uint32_t)bm));
-    }
-    h[p] = hh[0] | (hh[1] << 16);
-    m[p] = mm[0] | (mm[1] << 16);
-    l[p] = ll[0] | (ll[1] << 16);
-  }
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  mid = u32x4{m[0], m[1], m[2], m[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
-}
 
 // Staged queries on the matrix-core path: the three bf16 parts (hi, mid, lo)
 // of kSelQB query rows, part p of row r at qp[(p kSelQB + r) QS + dim], rows
@@ -291,11 +260,11 @@ __device__ __forceinline__ void sel_tile_logits(const bf16_t* qp, int qrow,
     const u32x4 al = *reinterpret_cast<const u32x4*>(base + 2 * kSelQB * QS);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(ah), sel_as_bf16x8(kf[c][st]),
+      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(kf[c][st]),
                                                      z[c], 0, 0, 0);
-      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(am), sel_as_bf16x8(kf[c][st]),
+      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(am), as_bf16x8(kf[c][st]),
                                                      z[c], 0, 0, 0);
-      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel_as_bf16x8(al), sel_as_bf16x8(kf[c][st]),
+      z[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(kf[c][st]),
                                                      z[c], 0, 0, 0);
     }
   }
@@ -327,7 +296,7 @@ __device__ void sel_stage_q(const float* __restrict__ q_win, int kv, int Q, int 
     float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (qb + qq < Q) load8f(src + (size_t)(qb + qq) * DH + 8 * c8, xv);
     u32x4 hi, mid, lo;
-    sel_split3(xv, hi, mid, lo);
+    split3_bf16(xv, hi, mid, lo);
     bf16_t* dst = qp + qq * QS + 8 * c8;
     *reinterpret_cast<u32x4*>(dst) = hi;
     *reinterpret_cast<u32x4*>(dst + kSelQB * QS) = mid;

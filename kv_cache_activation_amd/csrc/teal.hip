@@ -49,16 +49,6 @@ constexpr int kTbGroups = kTbWaves * kTbSub;   // row groups of a workgroup (16)
 constexpr int kTbCh = kTealMaxRange / kTbThreads;  // slice channels per thread, at most (8)
 static_assert(kTealBlock == 16 * 8, "a block row is 16 lanes x 8 columns");
 
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
 template <typename WT, bool DUAL, int EPI, typename KT>
 __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
   // rows per wave instruction group in flight: 8 instructions (32 rows) per

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
-    assert ctypes.sizeof(sd.sd_layer) == 192
+    assert ctypes.sizeof(sd.sd_layer) == 232
     assert ctypes.sizeof(sd.sd_byte_record) == 104
     assert ctypes.sizeof(sd.sd_latency_model) == 24
     assert ctypes.sizeof(sd.sd_seq_kv) == 48
@@ -347,6 +347,9 @@ def test_decode_step_ragged_checks_every_head_and_advances_each():
     (dict(full=True), sd.SD_ENOSPC),
     (dict(no_sel=True, mode=sd.SD_KV_SPARSE), sd.SD_EINVAL),
     (dict(dims=dict(d_model=8192)), sd.SD_EUNSUPPORTED),
+    (dict(mode=sd.SD_MATRIX_CORES), sd.SD_EINVAL),           # no tile weights
+    (dict(mode=sd.SD_MATRIX_CORES, dims=dict(w_dtype=sd.SD_F32)), sd.SD_EUNSUPPORTED),
+    (dict(mode=1024), sd.SD_EINVAL),
 ])
 def test_decode_step_batch_rejects_before_launch(case, status):
     batch = case.get("batch", 4)
@@ -381,3 +384,36 @@ def test_noalloc_step_rejects_beyond_its_buffer_before_launch():
     assert e.value.status == sd.SD_ENOSPC
     assert sd.SD_NOALLOC_SCRATCH_BYTES == 64 << 20
     assert sd.sd_workspace_bytes(_dims(), 0, 0) <= sd.SD_NOALLOC_SCRATCH_BYTES
+
+
+def test_batch_matrix_cores_accepts_tile_weights_alone():
+    # with SD_MATRIX_CORES the row-major weights are not needed; a full cache
+    # still stops the step on the host
+    L = sd.sd_layer(attn_norm=FAKE, mlp_norm=FAKE, w_qkv_m=FAKE, w_o_m=FAKE, w_gate_m=FAKE,
+                    w_up_m=FAKE, w_down_m=FAKE, cats_threshold=0.1)
+    layers = (sd.sd_layer * 1)(L)
+    kv = (sd.sd_seq_kv * 2)(sd.sd_seq_kv(FAKE, FAKE, 64, 10, None, None, 0, 0),
+                            sd.sd_seq_kv(FAKE, FAKE, 64, 64, None, None, 0, 0))
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_decode_step_batch(_dims(), layers, kv, [10, 64], FAKE, sd.SD_MATRIX_CORES,
+                                _FakeWs(1 << 32), 0)
+    assert e.value.status == sd.SD_ENOSPC and "sequence 1" in sd.sd_last_error()
+
+
+@pytest.mark.parametrize("case", [
+    dict(w=None), dict(out=None), dict(w=FAKE + 8), dict(rows=0), dict(d_in=12), dict(d_in=0),
+    dict(out=FAKE + 4096),   # overlaps w
+])
+def test_pack_tiles_rejects_before_launch(case):
+    args = dict(w=FAKE, rows=64, d_in=256, out=FAKE + (1 << 24))
+    args.update(case)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_pack_tiles(args["w"], args["rows"], args["d_in"], args["out"], 0)
+    assert e.value.status == sd.SD_EINVAL
+
+
+def test_tile_bytes_pads_rows_and_channels():
+    assert sd.sd_tile_bytes(16, 32) == 1024
+    assert sd.sd_tile_bytes(17, 32) == 2048
+    assert sd.sd_tile_bytes(16, 40) == 2048
+    assert sd.sd_tile_bytes(6144, 4096) == 6144 * 4096 * 2

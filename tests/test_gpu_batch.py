@@ -5,6 +5,7 @@ float64 batch oracle: every sequence's new hidden state, the union mask bit
 for bit, and the appended cache rows."""
 
 import copy
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -28,8 +29,9 @@ class BatchStack:
     (its own context length) and its own gathered buffer from the oracle's
     selection."""
 
-    def __init__(self, wl, n_layers, batch, n, keep_ratio, extra=8):
+    def __init__(self, wl, n_layers, batch, n, keep_ratio, extra=8, matrix_cores=False):
         self.wl, self.B, self.L = wl, batch, n_layers
+        self.mc = matrix_cores
         self.dims = dims_for(wl)
         self.odims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
                           head_dim=wl.head_dim, kv_dtype=wl.dtype, eps=1e-5, theta=500000.0)
@@ -45,6 +47,14 @@ class BatchStack:
                                       dW["w_gate"].data_ptr(), dW["w_up"].data_ptr(),
                                       dW["w_down_t"].data_ptr(), -1.0, 0, None, None, 0, 0,
                                       None, None, 0, 0, mask.data_ptr()))
+            if matrix_cores:   # the tile weights, packed by the library
+                for f, w in (("w_qkv_m", dW["w_qkv"]), ("w_o_m", dW["w_o"]),
+                             ("w_gate_m", dW["w_gate"]), ("w_up_m", dW["w_up"]),
+                             ("w_down_m", dW["w_down_t"].t().contiguous())):
+                    t = torch.empty(sd.sd_tile_bytes(*w.shape), dtype=torch.uint8, device=DEV)
+                    sd.sd_pack_tiles(w, w.shape[0], w.shape[1], t)
+                    self.keep_alive.append(t)
+                    setattr(layers[-1], f, t.data_ptr())
         self.layers = (sd.sd_layer * n_layers)(*layers)
         self.n = [n - 3 * b for b in range(batch)]       # a different length per sequence
         self.seq, kvs, self.dev_kv = [], [], []
@@ -110,9 +120,11 @@ class BatchStack:
         want, unions = obatch.decode_step_batch(self.seq, hs, pos, kv_sparse=kv_sparse,
                                                 mlp_sparse=mlp_sparse, trace=tr, **self.odims)
         hd = to_dev(np.stack(hs))
-        sd.sd_decode_step_batch(self.dims, self.layers, self.kv, pos, hd, MODES[mode], self.ws)
+        flags = MODES[mode] | (sd.SD_MATRIX_CORES if self.mc else 0)
+        sd.sd_decode_step_batch(self.dims, self.layers, self.kv, pos, hd, flags, self.ws)
         torch.cuda.synchronize()
-        got_unions = [m.cpu().numpy().astype(bool) for _, m in self.keep_alive]
+        got_unions = [e[1].cpu().numpy().astype(bool) for e in self.keep_alive
+                      if isinstance(e, tuple)]
         return to_host(hd), want, unions, got_unions
 
 
@@ -224,3 +236,83 @@ def test_more_sequence_heads_than_split_workgroups():
         hs = [w for w in want]
         pos = [p + 1 for p in pos]
     _check_appends(st, TOL["f32"])
+
+
+# ---------------------------------------------------------------- matrix cores
+# Widths that are not multiples of the 16-row tiles or the 32-channel steps:
+# O and down have 264 output rows (16.5 tiles), QKV and gate/up read 264
+# input channels (8.25 steps), down reads 680 (21.25 steps), gate/up have
+# 680 rows.
+RAGGED_BF16 = replace(synth.TINY, name="ragged-bf16-2layer", wid=9, d_model=264, d_ff=680,
+                      dtype="bf16")
+
+
+def test_pack_tiles_is_the_documented_relayout():
+    from synth import device as sdev
+    g = torch.Generator().manual_seed(5)
+    for rows, d_in in ((40, 200), (16, 32), (6144 // 8, 4096 // 8)):
+        w = torch.randn(rows, d_in, generator=g).to(torch.bfloat16).to(DEV)
+        out = torch.full((sd.sd_tile_bytes(rows, d_in),), 0xAB, dtype=torch.uint8, device=DEV)
+        sd.sd_pack_tiles(w, rows, d_in, out)
+        torch.cuda.synchronize()
+        want = sdev.mma_tiles(w).view(torch.uint8).flatten()
+        assert torch.equal(out, want), (rows, d_in)
+    # element (r, c) sits where the header says
+    rows, d_in = 40, 200
+    w = torch.arange(rows * d_in, dtype=torch.float32).remainder(251).to(torch.bfloat16)
+    w = w.view(rows, d_in).to(DEV)
+    out = torch.empty(sd.sd_tile_bytes(rows, d_in), dtype=torch.uint8, device=DEV)
+    sd.sd_pack_tiles(w, rows, d_in, out)
+    flat = out.view(torch.bfloat16).cpu()
+    S = (d_in + 31) // 32
+    for r, c in ((0, 0), (17, 33), (39, 199), (5, 100), (31, 64)):
+        i = ((r // 16) * S + c // 32) * 512 + ((r % 16) + 16 * ((c % 32) // 8)) * 8 + c % 8
+        assert flat[i] == w[r, c].cpu(), (r, c)
+
+
+@pytest.mark.parametrize("batch", [2, 3, 5, 8])
+def test_matrix_cores_ragged_widths_modes_over_steps(batch):
+    wl = RAGGED_BF16
+    st = BatchStack(wl, 2, batch, 600, 0.25, extra=8, matrix_cores=True)
+    hs = [synth.hidden(wl, 10 + b).astype(np.float64) for b in range(batch)]
+    pos = list(st.n)
+    for mode in ("dense", "both", "kv", "cats"):
+        got, want, unions, gu = st.step(hs, pos, mode)
+        for b in range(batch):
+            assert rel_l2(got[b], want[b]) <= TOL["bf16"], (mode, b)
+        if MODES[mode] & sd.SD_MLP_SPARSE:
+            for li in range(st.L):
+                assert np.array_equal(gu[li], unions[li]), (mode, li)
+        else:
+            assert all(u.all() for u in gu)
+        hs = [w for w in want]
+        pos = [p + 1 for p in pos]
+    _check_appends(st, TOL["bf16"])
+
+
+@pytest.mark.parametrize("batch", [2, 4, 8])
+def test_matrix_cores_8b_bf16_batch_both(batch):
+    wl = synth.L8B_DENSE_8K
+    st = BatchStack(wl, 1, batch, 2048, 0.16, matrix_cores=True)
+    hs = [synth.hidden(wl, 20 + b) for b in range(batch)]
+    got, want, unions, gu = st.step(hs, list(st.n), "both")
+    for b in range(batch):
+        assert rel_l2(got[b], want[b]) <= TOL["bf16"], b
+    assert np.array_equal(gu[0], unions[0])
+    _check_appends(st, TOL["bf16"])
+
+
+def test_matrix_cores_8b_two_layers_dense_then_cats():
+    wl = synth.L8B_DENSE_8K
+    st = BatchStack(wl, 2, 8, 1024, 0.2, matrix_cores=True)
+    hs = [synth.hidden(wl, 60 + b) for b in range(8)]
+    pos = list(st.n)
+    for mode in ("dense", "cats"):
+        got, want, unions, gu = st.step(hs, pos, mode)
+        for b in range(8):
+            assert rel_l2(got[b], want[b]) <= TOL["bf16"], (mode, b)
+        if mode == "cats":
+            for li in range(2):
+                assert np.array_equal(gu[li], unions[li]), li
+        hs = [w for w in want]
+        pos = [p + 1 for p in pos]
