@@ -258,13 +258,11 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   __syncthreads();
   if (tk_s != (unsigned)(KS - 1)) return;  // workgroup-uniform: not the group's last slice
 
-  // 5. the group's sums over the slices, in slice order (eight loads in flight)
+  // 5. the group's sums over the slices, in slice order
   if (threadIdx.x < NB) {
     float r = 1.f;
     if (a.norm) {
-      float tot = 0.f;
-      for (int k = 0; k < KS; ++k)
-        tot += load_agent(a.ssq + ((size_t)g * KS + k) * kMmNB + threadIdx.x);
+      const float tot = sum_agent(a.ssq + (size_t)g * KS * kMmNB + threadIdx.x, kMmNB, KS);
       r = 1.0f / sqrtf(tot / (float)d_in + a.eps);
     }
     rs_s[threadIdx.x] = r;
@@ -273,17 +271,9 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
     const int r = u % kMmGroupRows, b = (u / kMmGroupRows) % NB, mat = u / (kMmGroupRows * NB);
     const int row = g * kMmGroupRows + r;
     float v = 0.f;
-    if (b < nb && row < rows_pad) {
-      const float* p = a.part + mat * mat_stride + (size_t)b * rows_pad + row;
-      for (int k0 = 0; k0 < KS; k0 += 8) {
-        float t[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          t[k] = k0 + k < KS ? load_agent(p + (size_t)(k0 + k) * kMmNB * rows_pad) : 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v += t[k];
-      }
-    }
+    if (b < nb && row < rows_pad)
+      v = sum_agent(a.part + mat * mat_stride + (size_t)b * rows_pad + row,
+                    (size_t)kMmNB * rows_pad, KS);
     ys[mat][b][r] = v;
   }
   if (threadIdx.x == 0)

@@ -43,6 +43,22 @@ __device__ __forceinline__ float load_agent(const float* p) {
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
+// p[0] + p[stride] + ... + p[(n - 1) stride], added in index order, loaded at
+// agent scope sixteen at a time: the compiler keeps atomic loads in program
+// order and waits for each before its add, so a plain loop would pay one
+// memory round trip per term.
+__device__ __forceinline__ float sum_agent(const float* p, size_t stride, int n) {
+  float v = 0.f;
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    float t[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t[k] = k0 + k < n ? load_agent(p + (size_t)(k0 + k) * stride) : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v += t[k];  // terms past n add +0
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------- matrix cores
 // Operand type of v_mfma_f32_16x16x32_bf16 (eight bf16 values per lane).
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;

@@ -221,9 +221,7 @@ __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
   if (threadIdx.x < NCOL) {
     const int mat = threadIdx.x / kTealBlock, cc = threadIdx.x % kTealBlock;
     const float* p = a.part + (size_t)mat * S * bw + b * kTealBlock + cc;
-    float v = 0.f;
-    for (int k = 0; k < S; ++k) v += load_agent(p + (size_t)k * bw);
-    col[threadIdx.x] = v;
+    col[threadIdx.x] = sum_agent(p, bw, S);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
