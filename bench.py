@@ -54,7 +54,7 @@ HEAD_MODES = ("dense", "kv", "cats", "both")
 CATEKV_RATIO, CATEKV_ETA, CATEKV_BUDGET = 0.4, 1.0, 2048
 # decode lengths over which the latency gate charges one-time selection
 GATE_HORIZONS = (256, 1024, 4096, 16384)
-LEGS = ("sweep", "cells", "teal", "catekv", "batch", "baselines", "cpu")
+LEGS = ("head", "sweep", "cells", "teal", "catekv", "batch", "baselines", "cpu")
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -72,9 +72,11 @@ def parse():
     ap.add_argument("--modes", type=str, default=",".join(HEAD_MODES),
                     help="modes of the sweep (the crossing needs all four)")
     ap.add_argument("--teal-contexts", type=str, default="32768,131072")
+    ap.add_argument("--teal-modes", type=str, default="teal,teal+kv")
     ap.add_argument("--catekv-contexts", type=str, default="32768,131072")
     ap.add_argument("--batches", type=str, default="4,8")
     ap.add_argument("--batch-contexts", type=str, default="8192,32768")
+    ap.add_argument("--batch-modes", type=str, default=",".join(HEAD_MODES))
     ap.add_argument("--batch-paths", type=str, default="vector,matrix_cores",
                     help="batched projections on the vector ALUs and/or the matrix cores")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -86,6 +88,13 @@ def parse():
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs of this script into "
                          "per-kernel HBM bytes (needs --pmc-copy-bytes of those runs)")
     ap.add_argument("--pmc-out", type=str, default=TRAFFIC_JSON)
+    ap.add_argument("--trace-summary", type=str, metavar="KERNEL_TRACE_CSV",
+                    help="no GPU: per-kernel durations from a rocprofv3 --kernel-trace CSV of "
+                         "this script, as a markdown summary (--trace-out, --trace-title, "
+                         "--trace-cmd)")
+    ap.add_argument("--trace-out", type=str, default="")
+    ap.add_argument("--trace-title", type=str, default="")
+    ap.add_argument("--trace-cmd", type=str, default="")
     return ap.parse_args()
 
 
@@ -846,15 +855,30 @@ def batch_cells(stack, n, B, modes, matrix_cores=False):
     return out
 
 
-# library profiler kind -> (rocprofv3 kernel name, source file)
+# library profiler kind -> rocprofv3 kernel name, source file, and a pattern on
+# rocprofv3's full (templated) kernel name where one kernel serves several kinds
 KERNEL_SOURCES = {
-    "qkv_rope_append": ("qkv_rope_append_kernel", "gemv.hip"),
-    "attn_partial": ("attn_kernel", "attn.hip"),
-    "attn_combine": ("attn_merge_kernel", "attn.hip"),
-    "o_residual": ("o_residual_kernel", "gemv.hip"),
-    "cats_gate_up": ("gate_kernel", "gemv.hip"),
-    "cats_down": ("down_kernel", "down.hip"),
-    "cats_reduce": ("mlp_reduce_kernel", "down.hip"),
+    "qkv_rope_append": dict(rocprof="qkv_rope_append_kernel", src="gemv.hip"),
+    "attn_partial": dict(rocprof="attn_kernel", src="attn.hip"),
+    "attn_combine": dict(rocprof="attn_merge_kernel", src="attn.hip"),
+    "o_residual": dict(rocprof="o_residual_kernel", src="gemv.hip"),
+    "cats_gate_up": dict(rocprof="gate_kernel", src="gemv.hip",
+                         match=r"gate_kernel<[^<>]*false, \d+>"),  # not the calibration gate
+    "cats_down": dict(rocprof="down_kernel", src="down.hip", match=r"down_kernel<[^,]+, 1>"),
+    "cats_reduce": dict(rocprof="mlp_reduce_kernel", src="down.hip"),
+    "teal_qkv": dict(rocprof="teal_kernel", src="teal.hip",
+                     match=r"teal_kernel<unsigned short, false, 3,"),
+    "teal_o": dict(rocprof="teal_kernel", src="teal.hip",
+                   match=r"teal_kernel<unsigned short, false, 1,"),
+    "teal_gate_up": dict(rocprof="teal_kernel", src="teal.hip",
+                         match=r"teal_kernel<unsigned short, true, 2,"),
+    "batch_qkv": dict(rocprof="bmma_kernel", src="batch_mma.hip", match=r"bmma_kernel<8, false, 0,"),
+    "batch_o": dict(rocprof="bmma_kernel", src="batch_mma.hip",
+                    match=r"bmma_kernel<8, false, 1, 16>"),
+    "batch_gate_up": dict(rocprof="bmma_kernel", src="batch_mma.hip",
+                          match=r"bmma_kernel<8, true, 2,"),
+    "batch_down": dict(rocprof="bmma_kernel", src="batch_mma.hip",
+                       match=r"bmma_kernel<8, false, 1, 32>"),
 }
 
 
@@ -873,7 +897,7 @@ def traffic_for(kernel: str):
         return None
     try:
         rec = json.load(open(TRAFFIC_JSON))["kernels"][kernel]
-        if source_digest(KERNEL_SOURCES[kernel][1]) != rec["sha256"]:
+        if source_digest(KERNEL_SOURCES[kernel]["src"]) != rec["sha256"]:
             return None
         return rec["bytes_per_launch"]
     except Exception:
@@ -885,7 +909,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out: str) -> No
     script (FETCH_SIZE, then WRITE_SIZE, in KiB), each scaled by what the same
     counter reads for the plain device copy of `copy_bytes` bytes that the runs
     start with (--pmc-copy-bytes).  The decode-step launches of a kernel are
-    its most frequent grid size (calibration launches differ)."""
+    its most frequent grid size (calibration launches differ) among the
+    dispatches whose full kernel name matches the kind's pattern."""
     import collections
     import csv
     import re
@@ -893,16 +918,21 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out: str) -> No
     def load(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Correlation_Id"]))
+        # the calibration: the first three large copies of the run (later ones,
+        # such as the copy-ceiling measurement, move other sizes)
         copies = [float(r["Counter_Value"]) for r in rows
                   if "copy" in r["Kernel_Name"] and float(r["Counter_Value"]) * 1024 > copy_bytes / 4]
+        copies = copies[:3]
         if not copies:
             raise SystemExit(f"{path}: no copy-kernel dispatch of about {copy_bytes} bytes found")
         scale = copy_bytes / (sorted(copies)[len(copies) // 2] * 1024)
         per = collections.defaultdict(lambda: collections.defaultdict(list))
-        for r in rows:
-            m = re.search(r"sd::(\w+)", r["Kernel_Name"])
-            if m:
-                per[m.group(1)][r["Grid_Size"]].append(float(r["Counter_Value"]) * 1024 * scale)
+        for kind, e in KERNEL_SOURCES.items():
+            pat = e.get("match", r"sd::%s\b" % e["rocprof"])
+            for r in rows:
+                if re.search(r"sd::%s\b" % e["rocprof"], r["Kernel_Name"]) and \
+                        re.search(pat, r["Kernel_Name"]):
+                    per[kind][r["Grid_Size"]].append(float(r["Counter_Value"]) * 1024 * scale)
         return scale, per
 
     fs, fetch = load(fetch_csv, "FETCH_SIZE")
@@ -911,20 +941,68 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out: str) -> No
                       "FETCH_SIZE and WRITE_SIZE, each scaled by the counter's reading for a "
                       f"plain {copy_bytes}-byte device copy"),
                fetch_scale=fs, write_scale=ws, kernels={})
-    for kind, (rname, src) in KERNEL_SOURCES.items():
-        if rname not in fetch or rname not in write:
+    for kind, e in KERNEL_SOURCES.items():
+        if kind not in fetch or kind not in write:
             continue
-        grid = max(fetch[rname], key=lambda g: len(fetch[rname][g]))
-        f = fetch[rname][grid]
-        w = write[rname].get(grid, [0.0])
+        grid = max(fetch[kind], key=lambda g: len(fetch[kind][g]))
+        f = fetch[kind][grid]
+        w = write[kind].get(grid, [0.0])
         fb, wb = sum(f) / len(f), sum(w) / len(w)
-        res["kernels"][kind] = dict(rocprof_name=rname, grid_size=int(grid), dispatches=len(f),
-                                    fetch_bytes=round(fb), write_bytes=round(wb),
-                                    bytes_per_launch=round(fb + wb), source=src,
-                                    sha256=source_digest(src))
+        res["kernels"][kind] = dict(rocprof_name=e["rocprof"], grid_size=int(grid),
+                                    dispatches=len(f), fetch_bytes=round(fb),
+                                    write_bytes=round(wb), bytes_per_launch=round(fb + wb),
+                                    source=e["src"], sha256=source_digest(e["src"]))
     with open(out, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res, indent=1))
+
+
+def trace_summary(csv_path: str, out: str, title: str, cmd: str) -> None:
+    """Markdown summary of a rocprofv3 --kernel-trace CSV of this script: per
+    library kind (KERNEL_SOURCES), the decode-step launches (the kind's most
+    frequent grid size) with their mean, min and max duration, and every
+    library kernel's launch count and mean duration."""
+    import collections
+    import csv
+    import re
+
+    rows = [r for r in csv.DictReader(open(csv_path)) if "sd::" in r["Kernel_Name"]]
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    lines = [f"# rocprofv3 kernel summary: {title}", "",
+             "Command (from the repository root, on one MI355X), then this summary:", "", "```",
+             cmd, f"python3 bench.py --trace-summary {csv_path} --trace-out {out} "
+             f"--trace-title \"{title}\" --trace-cmd \"<the command above>\"", "```", "",
+             "## Decode-step launches per kernel kind", "",
+             "Launches of the kind's most frequent grid size (one per layer and step; the "
+             "one-time selection and calibration launches have other grids).", "",
+             "| kind | kernel | grid (threads) | launches | mean µs | min µs | max µs |",
+             "|---|---|---|---|---|---|---|"]
+    for kind, e in KERNEL_SOURCES.items():
+        pat = e.get("match", r"sd::%s\b" % e["rocprof"])
+        sel = [r for r in rows if re.search(r"sd::%s\b" % e["rocprof"], r["Kernel_Name"])
+               and re.search(pat, r["Kernel_Name"])]
+        if not sel:
+            continue
+        by = collections.Counter(int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) *
+                                 int(r["Grid_Size_Z"]) for r in sel)
+        grid = by.most_common(1)[0][0]
+        ds = [dur(r) for r in sel
+              if int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) == grid]
+        lines.append(f"| {kind} | `{e['rocprof']}` | {grid} | {len(ds)} | "
+                     f"{sum(ds) / len(ds):.2f} | {min(ds):.2f} | {max(ds):.2f} |")
+    lines += ["", "## Every library kernel", "", "| kernel | launches | mean µs | total ms |",
+              "|---|---|---|---|"]
+    agg = collections.defaultdict(list)
+    for r in rows:
+        m = re.search(r"sd::(\w+(<[^()]*>)?)", r["Kernel_Name"])
+        agg[m.group(1) if m else r["Kernel_Name"]].append(dur(r))
+    for name, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {len(ds)} | {sum(ds) / len(ds):.2f} | {sum(ds) / 1e3:.2f} |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def cpu_baseline(stack, n, seconds):
@@ -1032,6 +1110,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_copy_bytes, args.pmc_out)
         return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.trace_out, args.trace_title, args.trace_cmd)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
               "(the sharded multi-GPU path is a design note only)", file=sys.stderr)
@@ -1050,6 +1131,8 @@ def main():
         del src, dst
     t_start = time.perf_counter()
     stack = Stack(args)
+    note("setup", dict(layers=stack.L, contexts=stack.contexts,
+                       s=round(time.perf_counter() - t_start, 1)))
     full = dict(protocol=dict(blocks=args.blocks, block_steps=args.block_steps,
                               warmup_block_steps=args.block_steps,
                               headline_warmup=args.warmup, headline_steps=args.steps))
@@ -1058,7 +1141,7 @@ def main():
     n_head = max(stack.contexts)
     k_head = int(math.floor(stack.wl.keep_ratio * n_head))
     for n in stack.contexts:
-        if "sweep" not in legs and n != n_head:
+        if "sweep" not in legs and (n != n_head or "head" not in legs):
             continue
         secs, k_keep = stack.select(n)
         sel_ms[n] = secs * 1e3
@@ -1070,20 +1153,22 @@ def main():
             print(f"# n={n:6d} {mode:5s} {c['us']:9.1f} us/step (blocks {c['us_min']:.1f}.."
                   f"{c['us_max']:.1f}) {c['gbs']:7.1f} GB/s ({100 * c['frac']:.1f}% of peak)",
                   flush=True)
-    # the headline cell: the contract's W + K steps (the selection of n_head in place)
-    head = stack.headline(n_head, k_head, "both")
-    print(f"# headline n={n_head} both: {head['ms'] * 1e3:.1f} us/step over {args.steps} steps, "
-          f"{head['gbs']:.1f} GB/s ({100 * head['frac']:.1f}% of peak)", flush=True)
-    kern = stack.profile_cell(n_head, k_head, "both")
-    dom = max((k for k in kern if "alg_bytes" in kern[k]), key=lambda k: kern[k]["total_ms"])
-    dk = kern[dom]
-    roof = dict(bound="hbm", achieved=round(dk["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(dk["frac"], 4), traffic=traffic_for(dom),
-                kernel=KERNEL_SOURCES[dom][0], avg_us=round(dk["avg_us"], 2),
-                alg_bytes_per_launch=dk["alg_bytes"])
-    full["kernels"] = rnd(kern)
-    note("kernels", {k: rnd({kk: e[kk] for kk in ("launches", "avg_us", "gbs", "frac") if kk in e},
-                            3) for k, e in kern.items()})
+    head = roof = None
+    if "head" in legs:
+        # the headline cell: the contract's W + K steps (the selection of n_head in place)
+        head = stack.headline(n_head, k_head, "both")
+        print(f"# headline n={n_head} both: {head['ms'] * 1e3:.1f} us/step over {args.steps} "
+              f"steps, {head['gbs']:.1f} GB/s ({100 * head['frac']:.1f}% of peak)", flush=True)
+        kern = stack.profile_cell(n_head, k_head, "both")
+        dom = max((k for k in kern if "alg_bytes" in kern[k]), key=lambda k: kern[k]["total_ms"])
+        dk = kern[dom]
+        roof = dict(bound="hbm", achieved=round(dk["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dk["frac"], 4), traffic=traffic_for(dom),
+                    kernel=KERNEL_SOURCES[dom]["rocprof"], avg_us=round(dk["avg_us"], 2),
+                    alg_bytes_per_launch=dk["alg_bytes"])
+        full["kernels"] = rnd(kern)
+        note("kernels", {k: rnd({kk: e[kk] for kk in ("launches", "avg_us", "gbs", "frac")
+                                 if kk in e}, 3) for k, e in kern.items()})
     cross = crossing(stack, sweep) if "sweep" in legs else None
     if cross:
         full["crossing"] = rnd(cross)
@@ -1107,7 +1192,7 @@ def main():
         stack.enable_teal()
         for n in sorted(int(c) for c in args.teal_contexts.split(",") if c):
             _, k_keep = stack.select(n)
-            for mode in ("teal", "teal+kv"):
+            for mode in [m for m in args.teal_modes.split(",") if m]:
                 c = stack.cell(n, k_keep, mode)
                 extra.append(c)
                 note("teal", rnd(c))
@@ -1143,7 +1228,8 @@ def main():
         for n in [int(c) for c in args.batch_contexts.split(",") if c]:
             for B in [int(b) for b in args.batches.split(",") if b]:
                 for path in paths:
-                    for c in batch_cells(stack, n, B, HEAD_MODES, path == "matrix_cores"):
+                    bmodes = [m for m in args.batch_modes.split(",") if m]
+                    for c in batch_cells(stack, n, B, bmodes, path == "matrix_cores"):
                         cells.append(c)
                         note("batch", rnd({k: v for k, v in c.items() if k != "kernels"}, 3))
                         note("batch_kernels", rnd(c["kernels"], 3))
@@ -1167,12 +1253,17 @@ def main():
     full["copy_ceiling_gbs"] = round(stack.copy_ceiling(), 1)
     full["sweep"] = rnd(sweep)
     full["wall_s"] = round(time.perf_counter() - t_start, 1)
-    line = headline_line(args, stack, head, roof, cpu, sweep, cross, full["wall_s"])
-    if args.out:
+    line = None
+    if head is not None:
+        line = headline_line(args, stack, head, roof, cpu, sweep, cross, full["wall_s"])
         full["headline"] = line
+    if args.out:
         with open(args.out, "w") as f:
             json.dump(full, f, indent=1)
-    print(json.dumps(line, separators=(",", ":")), flush=True)
+    if line is not None:
+        print(json.dumps(line, separators=(",", ":")), flush=True)
+    else:  # a run without the head leg (profiling runs): no contract line
+        note("done", dict(legs=sorted(legs), wall_s=full["wall_s"]))
 
 
 if __name__ == "__main__":

@@ -96,3 +96,53 @@ def test_headline_line_is_compact_json():
     assert back["roofline"]["frac"] == 0.7338 and back["cpu_baseline"]["kind"] == "oracle"
     assert back["sweep"]["ctx"] == CTX and len(back["sweep"]["us"]["both"]) == len(CTX)
     assert not math.isnan(back["crossing"]["n_lat_k"])
+
+
+def test_pmc_summary_maps_templated_kernels_and_scales(tmp_path):
+    # two fake rocprofv3 counter CSVs: a 1 MiB copy kernel read as half its
+    # bytes (FETCH) and as all of them (WRITE), then kernels whose full names
+    # carry template arguments; each kind takes its own instances
+    import csv
+    import json
+
+    import bench
+
+    copy = 1 << 20
+    rows = [("void at::copy_kernel(...)", 8192, copy / 2 / 1024, copy / 1024)]
+    names = {
+        "void sd::teal_kernel<unsigned short, false, 3, unsigned short>(sd::TealArgs)": 135168,
+        "void sd::teal_kernel<unsigned short, false, 1, float>(sd::TealArgs)": 131072,
+        "void sd::teal_kernel<unsigned short, true, 2, float>(sd::TealArgs)": 143360,
+        "void sd::bmma_kernel<8, false, 1, 16>(sd::BmmaArgs)": 131072,
+        "void sd::bmma_kernel<8, false, 1, 32>(sd::BmmaArgs)": 229376,
+        "void sd::down_kernel<unsigned short, 1>(sd::DownArgs)": 131072,
+        "void sd::down_kernel<unsigned short, 8>(sd::DownArgs)": 131072,
+    }
+    for i, (n, g) in enumerate(names.items()):
+        for _ in range(3):
+            rows.append((n, g, 100.0 * (i + 1), 10.0 * (i + 1)))
+
+    def write(path, counter, col):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, ["Correlation_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                   "Counter_Value"])
+            w.writeheader()
+            for cid, r in enumerate(rows):
+                w.writerow(dict(Correlation_Id=cid, Kernel_Name=r[0], Grid_Size=r[1],
+                                Counter_Name=counter, Counter_Value=r[col]))
+
+    fc, wc, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
+    write(fc, "FETCH_SIZE", 2)
+    write(wc, "WRITE_SIZE", 3)
+    bench.pmc_summary(str(fc), str(wc), copy, str(out))
+    res = json.load(open(out))
+    assert abs(res["fetch_scale"] - 2.0) < 1e-9 and abs(res["write_scale"] - 1.0) < 1e-9
+    k = res["kernels"]
+    # index of each kind's row in `names` (+1) sets its counter values
+    want = {"teal_qkv": 1, "teal_o": 2, "teal_gate_up": 3, "batch_o": 4, "batch_down": 5,
+            "cats_down": 6}
+    for kind, i in want.items():
+        assert k[kind]["fetch_bytes"] == round(100.0 * i * 1024 * 2.0), kind
+        assert k[kind]["write_bytes"] == round(10.0 * i * 1024), kind
+        assert k[kind]["dispatches"] == 3
+    assert "batch_qkv" not in k and "qkv_rope_append" not in k
