@@ -235,19 +235,29 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
       mm_load_chunk<DUAL>(W0, W1, j0, c + kMmDepth, nsteps, A[c % kMmDepth]);
   }
 
-  // 4. the parts added; this slice's partials: part[mat][s][b][row]
+  // 4. the parts added, staged in LDS per row group, then this slice's
+  //    partials part[mat][s][b][row] stored with consecutive threads on
+  //    consecutive rows (whole lines per store instruction: every agent-scope
+  //    store is written through on its own)
   float y0[4], y1[4];
   mm_parts<NB, NM>(c0, y0);
   if constexpr (DUAL) mm_parts<NB, NM>(c1, y1);
   const int n = lane & 15, q = lane >> 4;
-  const size_t mat_stride = (size_t)KS * kMmNB * rows_pad;
-  if (t_raw < ntiles && n < nb) {
-    float* p = a.part + ((size_t)s * kMmNB + n) * rows_pad + tile * kMmRows + 4 * q;
+  if (n < NB) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      store_agent(p + i, y0[i]);
-      if constexpr (DUAL) store_agent(p + mat_stride + i, y1[i]);
+      ys[0][n][wave * kMmRows + 4 * q + i] = y0[i];
+      if constexpr (DUAL) ys[1][n][wave * kMmRows + 4 * q + i] = y1[i];
     }
+  }
+  __syncthreads();
+  const size_t mat_stride = (size_t)KS * kMmNB * rows_pad;
+  for (int u = threadIdx.x; u < NMAT * NB * kMmGroupRows; u += kMmThreads) {
+    const int r = u % kMmGroupRows, b = (u / kMmGroupRows) % NB, mat = u / (kMmGroupRows * NB);
+    const int row = g * kMmGroupRows + r;  // rows of clamped tiles lie past rows_pad
+    if (b < nb && row < rows_pad)
+      store_agent(a.part + mat * mat_stride + ((size_t)s * kMmNB + b) * rows_pad + row,
+                  ys[mat][b][r]);
   }
   if (a.norm && wave < NB && lane == 0)
     store_agent(a.ssq + ((size_t)g * KS + s) * kMmNB + wave, ss);
