@@ -51,9 +51,11 @@
  *   sd_last_error() gives a message for the calling thread's last failure.
  *   No exception crosses the ABI and the library never aborts.
  * Threads.  Every compute entry point is reentrant and keeps no state between
- *   calls.  The opt-in kernel profiler (sd_profile_start / sd_profile_stop)
- *   is the exception: it keeps one process-wide recording that is not safe to
- *   drive from several threads at once.
+ *   calls (beyond per-device launch-shape caches, filled once under a lock),
+ *   with two exceptions: the opt-in kernel profiler (sd_profile_start /
+ *   sd_profile_stop) keeps one process-wide recording that is not safe to
+ *   drive from several threads at once, and sd_decode_step_noalloc runs on
+ *   one scratch buffer per GPU, so its calls on one GPU must not overlap.
  */
 #ifndef SD_H
 #define SD_H
