@@ -439,9 +439,9 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
  * sd_pack_tiles -- a bf16 weight W [rows, d_in] (row-major, d_in a multiple of
  * 8, 16-byte aligned) rewritten into the tile layout that SD_MATRIX_CORES
  * reads: tiles of 16 rows by steps of 32 input channels, each (tile, step)
- * 1 KB in the A-operand order of the gfx950 matrix core, element (r, c) at
- * index ((r / 16) S + c / 32) 512 + ((r % 16) + 16 ((c % 32) / 8)) 8 + c % 8,
- * S = ceil(d_in / 32), padding rows and channels zero ([Cross] §3.3
+ * 1 KB in the A-operand order of the gfx950 matrix core, step-major: element
+ * (r, c) at index ((c / 32) T + r / 16) 512 + ((r % 16) + 16 ((c % 32) / 8)) 8
+ * + c % 8, T = ceil(rows / 16), padding rows and channels zero ([Cross] §3.3
  * "Dispatch and batching": a batch shares one read of every weight).
  * out     device, SD_TILE_BYTES(rows, d_in) bytes, 16-byte aligned, not
  *         overlapping w; enqueued on `stream`.

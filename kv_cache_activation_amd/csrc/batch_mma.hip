@@ -11,11 +11,15 @@
 // Weight layout ("tiles").  W is cut into tiles of 16 rows and steps of 32
 // input channels.  The 1 KB of one (tile, step) is stored in the A-operand
 // order of the matrix core (lane l: row l % 16, channels 8 (l / 16) .. + 7 of
-// the step), element (r, c) at
-//   ((r / 16) S + c / 32) 512 + ((r % 16) + 16 ((c % 32) / 8)) 8 + c % 8
-// with S = ceil(d_in / 32) and padding rows and channels zero.  One wave load
+// the step), step-major: element (r, c) at
+//   ((c / 32) T + r / 16) 512 + ((r % 16) + 16 ((c % 32) / 8)) 8 + c % 8
+// with T = ceil(rows / 16) and padding rows and channels zero.  One wave load
 // instruction reads 1 KB of contiguous memory straight into operand
-// registers, and a tile's steps follow each other in memory.
+// registers, and at each step a workgroup's eight waves read eight adjacent
+// KB.  (Tile-major order, each tile's steps contiguous, put the eight streams
+// of a workgroup 128 KB apart; measured with no other work, 8-wave
+// workgroups then streamed at 4.8-5.1 TB/s against 6.8-6.9 TB/s step-major,
+// at every grid size.)
 //
 // Inputs.  A float32 input x_b (times the RMSNorm weights) is split into three
 // bf16 parts, hi + mid + lo == x_b exactly.  Column p NB + b of the B operand
@@ -27,8 +31,9 @@
 // bmma_kernel: grid (KS input slices, row groups of 8 tiles), eight waves;
 // wave w owns tile 8 g + w of row group g.
 //   1. the wave streams its tile's fragments of the slice (8, 16 or 32
-//      steps) in chunks of four 1 KB loads, four chunks in flight: chunk c + 4
-//      is issued as soon as chunk c has gone into the products;
+//      steps, T KB apart) in chunks of four 1 KB loads, four chunks in
+//      flight: chunk c + 4 is issued as soon as chunk c has gone into the
+//      products;
 //   2. before the products, wave b stages sequence b's inputs of the slice as
 //      B fragments in LDS (load, norm weights, split; the input loads are
 //      issued right after the first chunk) and adds up its x^2 for the
@@ -116,12 +121,12 @@ __device__ __forceinline__ void mm_parts(const f32x4 (&c)[NM], float (&y)[4]) {
 // (their inputs are zero).
 template <bool DUAL>
 __device__ __forceinline__ void mm_load_chunk(const u32x4* W0, const u32x4* W1, int j0, int c,
-                                              int nsteps, u32x4 (&A)[kMmChunk]) {
+                                              int nsteps, int ntiles, u32x4 (&A)[kMmChunk]) {
   constexpr int SC = DUAL ? kMmChunk / 2 : kMmChunk;  // steps per chunk
 #pragma unroll
   for (int f = 0; f < kMmChunk; ++f) {
     const int step = c * SC + (DUAL ? f / 2 : f);
-    const size_t off = (size_t)min(j0 + step, nsteps - 1) * kWave;
+    const size_t off = (size_t)min(j0 + step, nsteps - 1) * ntiles * kWave;
     A[f] = __builtin_nontemporal_load(((DUAL && (f & 1)) ? W1 : W0) + off);
   }
 }
@@ -145,14 +150,13 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   const int t_raw = g * kMmWaves + wave;
   const int tile = min(t_raw, ntiles - 1);
   const int j0 = s * CH;
-  const u32x4* W0 = static_cast<const u32x4*>(a.w0) + (size_t)tile * nsteps * kWave + lane;
-  const u32x4* W1 =
-      DUAL ? static_cast<const u32x4*>(a.w1) + (size_t)tile * nsteps * kWave + lane : W0;
+  const u32x4* W0 = static_cast<const u32x4*>(a.w0) + (size_t)tile * kWave + lane;
+  const u32x4* W1 = DUAL ? static_cast<const u32x4*>(a.w1) + (size_t)tile * kWave + lane : W0;
 
   // 1. the first chunk of weights, then the inputs, then the next chunks: the
   //    staging below waits for the first chunk and the inputs only
   u32x4 A[kMmDepth][kMmChunk];
-  mm_load_chunk<DUAL>(W0, W1, j0, 0, nsteps, A[0]);
+  mm_load_chunk<DUAL>(W0, W1, j0, 0, nsteps, ntiles, A[0]);
 
   // 2. B fragments: wave b stages sequence b, lane l the slice's 8-channel
   //    groups l, l + 64, ...; column p NB + b holds part p
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   }
 #pragma unroll
   for (int c = 1; c < kMmDepth; ++c)
-    if (c < NCH) mm_load_chunk<DUAL>(W0, W1, j0, c, nsteps, A[c]);
+    if (c < NCH) mm_load_chunk<DUAL>(W0, W1, j0, c, nsteps, ntiles, A[c]);
   float ss = 0.f;
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
       }
     }
     if (c + kMmDepth < NCH)
-      mm_load_chunk<DUAL>(W0, W1, j0, c + kMmDepth, nsteps, A[c % kMmDepth]);
+      mm_load_chunk<DUAL>(W0, W1, j0, c + kMmDepth, nsteps, ntiles, A[c % kMmDepth]);
   }
 
   // 4. the parts added, staged in LDS per row group, then this slice's
@@ -317,15 +321,16 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   }
 }
 
-// W [rows, d_in] bf16 row-major -> tiles; one thread per 16-byte fragment.
+// W [rows, d_in] bf16 row-major -> tiles (step-major); one thread per 16-byte
+// fragment.
 __global__ void pack_tiles_kernel(const bf16_t* __restrict__ w, int rows, int d_in,
                                   u32x4* __restrict__ out, size_t n_frag) {
-  const int nsteps = (d_in + kMmK - 1) / kMmK;
+  const int ntiles = (rows + kMmRows - 1) / kMmRows;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_frag;
        i += (size_t)gridDim.x * blockDim.x) {
     const int lane = (int)(i % kWave);
     const size_t ts = i / kWave;
-    const int step = (int)(ts % nsteps), tile = (int)(ts / nsteps);
+    const int tile = (int)(ts % ntiles), step = (int)(ts / ntiles);
     const int r = tile * kMmRows + lane % 16, c = step * kMmK + 8 * (lane / 16);
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
     if (r < rows && c < d_in) v = *reinterpret_cast<const u32x4*>(w + (size_t)r * d_in + c);

@@ -101,12 +101,12 @@ def teal_blocked(w, block: int = 128):
 def mma_tiles(w):
     """W [rows, d_in] (nn.Linear order) in the tile layout of the batched
     matrix-core projections: tiles of 16 rows by steps of 32 input channels,
-    each (tile, step) in the A-operand lane order of the matrix core (lane l:
-    row l % 16, channels 8 (l // 16) .. + 7 of the step), padding zero.  A
-    relayout only."""
+    step-major, each (tile, step) in the A-operand lane order of the matrix
+    core (lane l: row l % 16, channels 8 (l // 16) .. + 7 of the step),
+    padding zero.  A relayout only."""
     rows, d_in = w.shape
     rp, kp = (rows + 15) // 16 * 16, (d_in + 31) // 32 * 32
     wp = torch.zeros(rp, kp, dtype=w.dtype, device=w.device)
     wp[:rows, :d_in] = w
-    # [tile, r, step, q, e] -> [tile, step, q, r, e]: lane = r + 16 q
-    return wp.view(rp // 16, 16, kp // 32, 4, 8).permute(0, 2, 3, 1, 4).contiguous()
+    # [tile, r, step, q, e] -> [step, tile, q, r, e]: lane = r + 16 q
+    return wp.view(rp // 16, 16, kp // 32, 4, 8).permute(2, 0, 3, 1, 4).contiguous()

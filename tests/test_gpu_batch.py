@@ -264,9 +264,9 @@ def test_pack_tiles_is_the_documented_relayout():
     out = torch.empty(sd.sd_tile_bytes(rows, d_in), dtype=torch.uint8, device=DEV)
     sd.sd_pack_tiles(w, rows, d_in, out)
     flat = out.view(torch.bfloat16).cpu()
-    S = (d_in + 31) // 32
+    T = (rows + 15) // 16
     for r, c in ((0, 0), (17, 33), (39, 199), (5, 100), (31, 64)):
-        i = ((r // 16) * S + c // 32) * 512 + ((r % 16) + 16 * ((c % 32) // 8)) * 8 + c % 8
+        i = ((c // 32) * T + r // 16) * 512 + ((r % 16) + 16 * ((c % 32) // 8)) * 8 + c % 8
         assert flat[i] == w[r, c].cpu(), (r, c)
 
 
