@@ -763,21 +763,14 @@ def attention_baselines(stack, n, window_ratio=0.3, steps=4, warmup=1):
                 window_speedup=speedup, window_byte_bound=rec.bound_kv)
 
 
-def batch_cells(stack, n, B, modes, matrix_cores=False):
-    """Batched decode ([Cross] §3.3 "Dispatch and batching", §4.4
-    "Batching"): B sequences of context n, each with its own synthetic
-    caches, selection and hidden state, stepped together so that every
-    weight row is read once per step.  Per mode: µs per step (median block
-    of a shorter protocol: blocks of a fifth of the sweep's length),
-    tokens/s, algorithmic GB/s (weights once, the union's up and down rows
-    under CATS, every sequence's cache rows), the measured union fraction
-    u_B of the CATS masks, and per-kernel times of one more block (library
-    profiler).  matrix_cores: the projections on the matrix cores (tile
-    weights), which read up and down whole."""
-    torch, sd, wl, args = stack.torch, stack.sd, stack.wl, stack.args
+def batch_caches(stack, n, B, grow):
+    """B sequences of context n for the batched step: each sequence's own
+    synthetic caches per layer (room for `grow` more rows), its own one-time
+    selection at keep ratio wl.keep_ratio into gathered buffers, and its own
+    hidden state.  Returns (tensors to keep alive, sd_seq_kv array [B * L],
+    sequence-major, k_keep, hidden states [B, d])."""
+    torch, sd, wl = stack.torch, stack.sd, stack.wl
     from synth import device as sdev
-    bs = max(1, args.block_steps // 5)
-    grow = (1 + args.blocks) * bs + 8
     cap, k_keep = n + grow + 64, int(math.floor(wl.keep_ratio * n))
     cap_sel = k_keep + grow + 64
     keep, kvs = [], []
@@ -799,6 +792,25 @@ def batch_cells(stack, n, B, modes, matrix_cores=False):
                                     vs.data_ptr(), cap_sel, k_keep))
     kv = (sd.sd_seq_kv * (B * stack.L))(*kvs)
     h0 = torch.stack([sdev.hidden(wl, b, stack.dev) for b in range(B)])
+    torch.cuda.synchronize()
+    return keep, kv, k_keep, h0
+
+
+def batch_cells(stack, n, B, modes, matrix_cores=False):
+    """Batched decode ([Cross] §3.3 "Dispatch and batching", §4.4
+    "Batching"): B sequences of context n, each with its own synthetic
+    caches, selection and hidden state, stepped together so that every
+    weight row is read once per step.  Per mode: µs per step (median block
+    of a shorter protocol: blocks of a fifth of the sweep's length),
+    tokens/s, algorithmic GB/s (weights once, the union's up and down rows
+    under CATS, every sequence's cache rows), the measured union fraction
+    u_B of the CATS masks, and per-kernel times of one more block (library
+    profiler).  matrix_cores: the projections on the matrix cores (tile
+    weights), which read up and down whole."""
+    torch, sd, wl, args = stack.torch, stack.sd, stack.wl, stack.args
+    bs = max(1, args.block_steps // 5)
+    grow = (1 + args.blocks) * bs + 8
+    keep, kv, k_keep, h0 = batch_caches(stack, n, B, grow)
     hid = h0.clone()
     ws = torch.empty(sd.sd_batch_workspace_bytes(stack.dims, B), dtype=torch.uint8,
                      device=stack.dev)
@@ -850,7 +862,7 @@ def batch_cells(stack, n, B, modes, matrix_cores=False):
                         us_max=blk[-1], tokens_per_s=B / (us * 1e-6), bytes=b_step,
                         gbs=b_step / us / 1e3, frac=b_step / us / 1e3 / HBM_PEAK_GBS,
                         union_fraction=u if flags & sd.SD_MLP_SPARSE else None, kernels=kern))
-    del keep, kv, ws, scores, idx, sws
+    del keep, kv, ws
     torch.cuda.empty_cache()
     return out
 

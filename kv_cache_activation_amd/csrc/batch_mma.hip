@@ -116,9 +116,9 @@ __device__ __forceinline__ void mm_parts(const f32x4 (&c)[NM], float (&y)[4]) {
   }
 }
 
-// Fragment loads of chunk c of a wave's slice: eight steps of one matrix, or
-// four steps of each of two (gate and up); steps past the last repeat it
-// (their inputs are zero).
+// Fragment loads of chunk c of a wave's slice: four steps of one matrix, or
+// two steps of each of two (gate and up); steps past the last repeat it
+// (their inputs are zero).  Step j of the wave's tile is T KB after step j - 1.
 template <bool DUAL>
 __device__ __forceinline__ void mm_load_chunk(const u32x4* W0, const u32x4* W1, int j0, int c,
                                               int nsteps, int ntiles, u32x4 (&A)[kMmChunk]) {
