@@ -525,6 +525,26 @@ class Stack:
             out[name] = e
         return out
 
+    def read_ceiling(self, nbytes=4 << 30, reps=10):
+        """GB/s of one plain read of a resident nbytes buffer (sd_stream_read,
+        the library's own read-only kernel)."""
+        torch, sd = self.torch, self.sd
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.dev)
+        out = torch.empty(sd.SD_STREAM_BLOCKS, dtype=torch.int32, device=self.dev)
+        sd.sd_stream_read(buf, nbytes, out)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            sd.sd_stream_read(buf, nbytes, out)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del buf, out
+        torch.cuda.empty_cache()
+        return nbytes / ms / 1e6
+
     def copy_ceiling(self, nbytes=1 << 30, reps=10):
         """GB/s (read + write) of a plain device-to-device copy of nbytes."""
         torch = self.torch
@@ -1263,11 +1283,14 @@ def main():
         full["cpu_baseline"] = rnd(cpu)
         note("cpu_baseline", rnd({k: v for k, v in cpu.items() if k != "sample"}, 3))
     full["copy_ceiling_gbs"] = round(stack.copy_ceiling(), 1)
+    full["read_ceiling_gbs"] = round(stack.read_ceiling(), 1)
+    note("ceilings", dict(read_gbs=full["read_ceiling_gbs"], copy_gbs=full["copy_ceiling_gbs"]))
     full["sweep"] = rnd(sweep)
     full["wall_s"] = round(time.perf_counter() - t_start, 1)
     line = None
     if head is not None:
         line = headline_line(args, stack, head, roof, cpu, sweep, cross, full["wall_s"])
+        line["read_ceiling_gbs"] = full["read_ceiling_gbs"]
         full["headline"] = line
     if args.out:
         with open(args.out, "w") as f:

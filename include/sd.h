@@ -451,6 +451,20 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
   ((((size_t)(rows) + 15) / 16) * (((size_t)(d_in) + 31) / 32) * (size_t)1024)
 sd_status sd_pack_tiles(const void* w, int32_t rows, int32_t d_in, void* out, void* stream);
 
+/*
+ * sd_stream_read -- one plain read of a device buffer with the access pattern
+ * of the library's weight streams (16-byte non-temporal loads, eight per wave
+ * in flight, the waves in flight reading one contiguous window), for the
+ * read-bandwidth ceiling that the decode kernels are measured against
+ * ([Cross] §4.1 "Timing and quality": achieved bandwidth is the measure).
+ * buf    device, bytes a positive multiple of 8192, 16-byte aligned.
+ * out    [SD_STREAM_BLOCKS] uint32 device out: the XOR of every 32-bit word
+ *        each workgroup read; the XOR of all entries is the XOR of the buffer.
+ * Errors: EINVAL for bad pointers or sizes.
+ */
+#define SD_STREAM_BLOCKS 2048
+sd_status sd_stream_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 /* Byte account record ([Cross] §3). Bytes as doubles (exact below 2^53). */
 typedef struct {
   double b_attn;        /* bytes of W_q, W_k, W_v, W_o per layer */

@@ -34,7 +34,7 @@ EXPORTS = ("sd_workspace_bytes", "sd_select_kv", "sd_select_kv_ragged", "sd_deco
            "sd_decode_attn_ragged", "sd_decode_attn_window",
            "sd_decode_attn_baseline", "sd_sparse_mlp", "sd_teal_gemv",
            "sd_decode_step", "sd_decode_step_noalloc", "sd_batch_workspace_bytes", "sd_decode_step_batch", "sd_byte_account",
-           "sd_pack_tiles", "sd_byte_crossover_batch", "sd_latency_fit", "sd_latency_crossing", "sd_latency_gate",
+           "sd_pack_tiles", "sd_stream_read", "sd_byte_crossover_batch", "sd_latency_fit", "sd_latency_crossing", "sd_latency_gate",
            "sd_calibrate_workspace_bytes",
            "sd_cats_calibrate", "sd_profile_start", "sd_profile_stop", "sd_status_string",
            "sd_last_error")
@@ -115,6 +115,9 @@ _lib.sd_decode_step_batch.restype = _I
 _lib.sd_decode_step_batch.argtypes = [ctypes.POINTER(sd_dims), _I, ctypes.POINTER(sd_layer), _I,
                                       ctypes.POINTER(sd_seq_kv), ctypes.POINTER(_I), _P, _U, _P,
                                       _S, _P]
+_lib.sd_stream_read.restype = _I
+_lib.sd_stream_read.argtypes = [_P, _S, _P, _P]
+SD_STREAM_BLOCKS = 2048
 _lib.sd_pack_tiles.restype = _I
 _lib.sd_pack_tiles.argtypes = [_P, _I, _I, _P, _P]
 _lib.sd_decode_attn.restype = _I
@@ -296,6 +299,11 @@ def sd_decode_step_batch(dims, layers, kv, pos, hidden, mode, ws, stream=None) -
 def sd_tile_bytes(rows: int, d_in: int) -> int:
     """Bytes of a [rows, d_in] weight in the tile layout (SD_TILE_BYTES)."""
     return ((rows + 15) // 16) * ((d_in + 31) // 32) * 1024
+
+
+def sd_stream_read(buf, nbytes, out, stream=None) -> None:
+    """One plain read of nbytes of buf; out [SD_STREAM_BLOCKS] uint32/int32 checksums."""
+    _check(_lib.sd_stream_read(_ptr(buf), nbytes, _ptr(out), _stream(stream)))
 
 
 def sd_pack_tiles(w, rows, d_in, out, stream=None) -> None:

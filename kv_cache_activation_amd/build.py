@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "byte_account.cpp", "profile.cpp", "gemv.hip", "down.hip", "attn.hip",
            "attn_naive.hip", "select.hip", "teal.hip", "batch.hip", "batch_mma.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

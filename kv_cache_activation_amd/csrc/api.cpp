@@ -557,6 +557,14 @@ sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const 
   return check_launch("sd_teal_gemv");
 }
 
+sd_status sd_stream_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!aligned(buf) || !aligned(out)) return fail(SD_EINVAL, "null or misaligned pointer");
+  if (bytes == 0 || bytes % 8192)
+    return fail(SD_EINVAL, "bytes must be a positive multiple of 8192 (got %zu)", bytes);
+  sd::launch_stream_read(buf, bytes, out, static_cast<hipStream_t>(stream));
+  return check_launch("sd_stream_read");
+}
+
 sd_status sd_pack_tiles(const void* w, int32_t rows, int32_t d_in, void* out, void* stream) {
   if (!aligned(w) || !aligned(out)) return fail(SD_EINVAL, "null or misaligned pointer");
   if (rows < 1 || d_in < 8 || d_in % 8)

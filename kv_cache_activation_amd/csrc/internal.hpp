@@ -283,6 +283,9 @@ void launch_select(const SelectArgs& a, int kv_dtype, hipStream_t s);
 void launch_kth_smallest(const float* vals, size_t n, size_t k, unsigned* hist, unsigned* state,
                          float* out, hipStream_t s);
 
+// One read of bytes (a multiple of 8192) of buf; out[SD_STREAM_BLOCKS] XOR checksums.
+void launch_stream_read(const void* buf, size_t bytes, unsigned* out, hipStream_t s);
+
 // Records a message for sd_last_error() on the calling thread; returns st.
 sd_status set_error(sd_status st, const char* msg);
 

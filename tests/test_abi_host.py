@@ -417,3 +417,13 @@ def test_tile_bytes_pads_rows_and_channels():
     assert sd.sd_tile_bytes(17, 32) == 2048
     assert sd.sd_tile_bytes(16, 40) == 2048
     assert sd.sd_tile_bytes(6144, 4096) == 6144 * 4096 * 2
+
+
+@pytest.mark.parametrize("case", [dict(buf=None), dict(buf=FAKE + 8), dict(nbytes=0),
+                                  dict(nbytes=8192 + 16), dict(out=None)])
+def test_stream_read_rejects_before_launch(case):
+    args = dict(buf=FAKE, nbytes=1 << 20, out=FAKE + (1 << 24))
+    args.update(case)
+    with pytest.raises(sd.SdError) as e:
+        sd.sd_stream_read(args["buf"], args["nbytes"], args["out"], 0)
+    assert e.value.status == sd.SD_EINVAL
