@@ -153,10 +153,11 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   const u32x4* W0 = static_cast<const u32x4*>(a.w0) + (size_t)tile * kWave + lane;
   const u32x4* W1 = DUAL ? static_cast<const u32x4*>(a.w1) + (size_t)tile * kWave + lane : W0;
 
-  // 1. the first chunk of weights, then the inputs, then the next chunks: the
-  //    staging below waits for the first chunk and the inputs only
+  // 1. the inputs first, then the first chunks of weights: a wave's loads
+  //    return in issue order, so the staging below waits for the inputs only
+  //    (behind a weight chunk it waited, at launch, for the whole chip's
+  //    first burst of weight loads)
   u32x4 A[kMmDepth][kMmChunk];
-  mm_load_chunk<DUAL>(W0, W1, j0, 0, nsteps, ntiles, A[0]);
 
   // 2. B fragments: wave b stages sequence b, lane l the slice's 8-channel
   //    groups l, l + 64, ...; column p NB + b holds part p
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
     }
   }
 #pragma unroll
-  for (int c = 1; c < kMmDepth; ++c)
+  for (int c = 0; c < kMmDepth; ++c)
     if (c < NCH) mm_load_chunk<DUAL>(W0, W1, j0, c, nsteps, ntiles, A[c]);
   float ss = 0.f;
 #pragma unroll
@@ -272,34 +273,72 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   __syncthreads();
   if (tk_s != (unsigned)(KS - 1)) return;  // workgroup-uniform: not the group's last slice
 
-  // 5. the group's sums over the slices, in slice order
-  if (threadIdx.x < NB) {
-    float r = 1.f;
-    if (a.norm) {
-      const float tot = sum_agent(a.ssq + (size_t)g * KS * kMmNB + threadIdx.x, kMmNB, KS);
-      r = 1.0f / sqrtf(tot / (float)d_in + a.eps);
-    }
-    rs_s[threadIdx.x] = r;
+  // 5. the group's sums over the slices, in slice order.  The compiler keeps
+  //    agent-scope loads in order and waits for each before its first use, so
+  //    every load of a batch (the thread's sums over up to 16 slices, and
+  //    the x^2 sums) is issued before the first add: one round trip per batch
+  //    instead of one per sum
+  constexpr int NU = NMAT * NB * kMmGroupRows;            // sums of the group
+  constexpr int IPT = (NU + kMmThreads - 1) / kMmThreads;  // sums per thread
+  constexpr int KB = 32 / IPT < 16 ? 32 / IPT : 16;        // slices per batch
+  const size_t sl_stride = (size_t)kMmNB * rows_pad;
+  const bool has_ss = a.norm && threadIdx.x < NB;
+  float acc[IPT], old[IPT], tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    acc[i] = 0.f;
+    // the residual the sums are added to, loaded with the first batch (a
+    // single matrix: the thread's sums are the outputs it writes)
+    const int u = threadIdx.x + i * kMmThreads, b = u / kMmGroupRows;
+    const int row = g * kMmGroupRows + u % kMmGroupRows;
+    old[i] = EPI == MM_RESID && u < NU && b < nb && row < rows ? a.out[(size_t)b * rows + row]
+                                                                 : 0.f;
   }
-  for (int u = threadIdx.x; u < NMAT * NB * kMmGroupRows; u += kMmThreads) {
-    const int r = u % kMmGroupRows, b = (u / kMmGroupRows) % NB, mat = u / (kMmGroupRows * NB);
-    const int row = g * kMmGroupRows + r;
-    float v = 0.f;
-    if (b < nb && row < rows_pad)
-      v = sum_agent(a.part + mat * mat_stride + (size_t)b * rows_pad + row,
-                    (size_t)kMmNB * rows_pad, KS);
-    ys[mat][b][r] = v;
+  for (int k0 = 0; k0 < KS; k0 += KB) {
+    float t[IPT][KB], q[KB];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int k = k0 + kk;
+      q[kk] = has_ss && k < KS ? load_agent(a.ssq + ((size_t)g * KS + k) * kMmNB + threadIdx.x)
+                               : 0.f;
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const int u = threadIdx.x + i * kMmThreads;
+        const int r = u % kMmGroupRows, b = (u / kMmGroupRows) % NB, mat = u / (kMmGroupRows * NB);
+        const int row = g * kMmGroupRows + r;
+        t[i][kk] = u < NU && b < nb && row < rows_pad && k < KS
+                       ? load_agent(a.part + mat * mat_stride + (size_t)k * sl_stride +
+                                    (size_t)b * rows_pad + row)
+                       : 0.f;  // terms past KS add +0
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) tot += q[kk];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i)
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) acc[i] += t[i][kk];
+  }
+  if (threadIdx.x < NB) rs_s[threadIdx.x] = a.norm ? 1.0f / sqrtf(tot / (float)d_in + a.eps) : 1.f;
+  if constexpr (EPI == MM_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int u = threadIdx.x + i * kMmThreads;
+      if (u < NU)
+        ys[u / (kMmGroupRows * NB)][(u / kMmGroupRows) % NB][u % kMmGroupRows] = acc[i];
+    }
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(a.tickets + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if constexpr (EPI == MM_STORE || EPI == MM_RESID) {
-    for (int u = threadIdx.x; u < NB * kMmGroupRows; u += kMmThreads) {
-      const int r = u % kMmGroupRows, b = u / kMmGroupRows, row = g * kMmGroupRows + r;
-      if (b < nb && row < rows) {
-        float* o = a.out + (size_t)b * rows + row;
-        const float v = rs_s[b] * ys[0][b][r];
-        *o = EPI == MM_RESID ? *o + v : v;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int u = threadIdx.x + i * kMmThreads, b = u / kMmGroupRows;
+      const int row = g * kMmGroupRows + u % kMmGroupRows;
+      if (u < NU && b < nb && row < rows) {
+        const float v = rs_s[b] * acc[i];
+        a.out[(size_t)b * rows + row] = EPI == MM_RESID ? old[i] + v : v;
       }
     }
   } else {  // MM_SWIGLU: the CATS gate per sequence, the union per row
