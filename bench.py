@@ -545,6 +545,40 @@ class Stack:
         torch.cuda.empty_cache()
         return nbytes / ms / 1e6
 
+    def launch_ceiling(self, read_gbs, layers=8, passes=5):
+        """Cost of a kernel boundary between streaming launches: sd_stream_read
+        over the four weight streams of a composed layer (QKV, O, gate + up at
+        50% kept, down at 50% kept), `layers` sets of distinct buffers launched
+        back to back on one stream; the time beyond the bytes at the read
+        ceiling, per launch."""
+        torch, sd, wl = self.torch, self.sd, self.wl
+        d, ff = wl.d_model, wl.d_ff
+        sizes = [(wl.n_q_heads + 2 * wl.n_kv_heads) * wl.head_dim * d * 2, d * d * 2,
+                 int(1.5 * ff * d * 2), int(0.5 * ff * d * 2)]
+        sizes = [s // 8192 * 8192 for s in sizes]
+        bufs = [torch.zeros(s, dtype=torch.uint8, device=self.dev) for _ in range(layers)
+                for s in sizes]
+        out = torch.empty(sd.SD_STREAM_BLOCKS, dtype=torch.int32, device=self.dev)
+        total = sum(b.numel() for b in bufs)
+        times = []
+        for it in range(passes + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for b in bufs:
+                sd.sd_stream_read(b, b.numel(), out)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            if it:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        del bufs, out
+        torch.cuda.empty_cache()
+        us = sorted(times)[len(times) // 2]
+        n = layers * len(sizes)
+        return dict(launches=n, mb=round(total / 1e6, 1), us=round(us, 1),
+                    gbs=round(total / us / 1e3, 1),
+                    per_launch_us=round((us - total / read_gbs / 1e3) / n, 2))
+
     def copy_ceiling(self, nbytes=1 << 30, reps=10):
         """GB/s (read + write) of a plain device-to-device copy of nbytes."""
         torch = self.torch
@@ -1284,13 +1318,16 @@ def main():
         note("cpu_baseline", rnd({k: v for k, v in cpu.items() if k != "sample"}, 3))
     full["copy_ceiling_gbs"] = round(stack.copy_ceiling(), 1)
     full["read_ceiling_gbs"] = round(stack.read_ceiling(), 1)
-    note("ceilings", dict(read_gbs=full["read_ceiling_gbs"], copy_gbs=full["copy_ceiling_gbs"]))
+    full["launch_ceiling"] = stack.launch_ceiling(full["read_ceiling_gbs"])
+    note("ceilings", dict(read_gbs=full["read_ceiling_gbs"], copy_gbs=full["copy_ceiling_gbs"],
+                          launch=full["launch_ceiling"]))
     full["sweep"] = rnd(sweep)
     full["wall_s"] = round(time.perf_counter() - t_start, 1)
     line = None
     if head is not None:
         line = headline_line(args, stack, head, roof, cpu, sweep, cross, full["wall_s"])
         line["read_ceiling_gbs"] = full["read_ceiling_gbs"]
+        line["launch_overhead_us"] = full["launch_ceiling"]["per_launch_us"]
         full["headline"] = line
     if args.out:
         with open(args.out, "w") as f:
