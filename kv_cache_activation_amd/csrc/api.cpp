@@ -540,7 +540,9 @@ sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const 
   const Layout L = make_layout(*dims, 0, 0);
   if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
   const int nblk = (d_out + sd::kTealBlock - 1) / sd::kTealBlock;
-  const size_t need = (size_t)sd::teal_slices(d_in, d_out) * nblk * sd::kTealBlock * (w2_t ? 2 : 1);
+  const int mats = w2_t ? 2 : 1;
+  const size_t need = (size_t)sd::teal_slices(d_in, d_out, mats, dims->w_dtype == SD_BF16 ? 2 : 4) *
+                      nblk * sd::kTealBlock * mats;
   if (need > L.teal_part_floats || nblk > sd::kTealMaxBlocks)
     return fail(SD_ENOSPC, "d_in %d x d_out %d needs %zu partial floats, the workspace holds %zu",
                 d_in, d_out, need, L.teal_part_floats);

@@ -116,7 +116,7 @@ constexpr int kTealMaxRange = 2048;  // input channels per slice, at most
 constexpr int kTealMaxSlices = 32;
 constexpr int kTealMaxBlocks = 1024; // blocks' tickets in the workspace
 enum TealEpi { TEAL_STORE = 0, TEAL_ACC = 1, TEAL_SWIGLU = 2, TEAL_QKV = 3 };
-int teal_slices(int d_in, int d_out);
+int teal_slices(int d_in, int d_out, int mats, int wbytes);
 
 struct TealArgs {
   int kind;            // profiler kind of this projection
