@@ -36,7 +36,7 @@
 //      products;
 //   2. before the products, wave b stages sequence b's inputs of the slice as
 //      B fragments in LDS (load, norm weights, split; the input loads are
-//      issued right after the first chunk) and adds up its x^2 for the
+//      issued before the first weight chunk) and adds up its x^2 for the
 //      RMSNorm;
 //   3. per step, NM = ceil(3 NB / 16) products per matrix;
 //   4. the three parts of each sum are added; the slice's partial sums (and
