@@ -784,7 +784,7 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
 struct BatchLayout {
   Layout base;
   size_t qkv, q, attn, pm, pl, pacc, act, hmid, keep, uni, part, mm_part, mm_ssq, mm_tickets,
-      total;
+      rope, total;
   int mm_groups;
 };
 
@@ -810,6 +810,7 @@ BatchLayout make_batch_layout(const sd_dims& dm, int nb) {
   B.keep = take(n * ff);
   B.uni = take(ff);
   B.part = take((size_t)sd::down_parts((int)ff) * n * d * 4);
+  B.rope = take(n * (dh / 2) * 2 * 4);
   {  // matrix-core path: the largest of the layer's four launches
     const int qo = (int)((hq + 2 * hkv) * dh), od = (int)(hq * dh);
     const size_t pf = std::max(std::max(sd::bmma_part_floats(qo, (int)d, false),
@@ -960,27 +961,18 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
     return m;
   };
   if (mc) sd::launch_teal_zero(mm_tickets, B.mm_groups, s);  // every launch leaves them zero
+  // 128-dim heads make each 128-row group of W_qkv one head, so the matrix-core
+  // QKV applies RoPE and appends to bf16 caches itself
+  const bool fused_rope = mc && dh == 128 && dims->kv_dtype == SD_BF16;
+  float2* rope_cs = reinterpret_cast<float2*>(wsb + B.rope);
+  if (fused_rope && dims->rope_theta > 0.f) {  // the positions are the same in every layer
+    sd::BatchKv at{};
+    for (int b = 0; b < batch; ++b) at.pos[b] = pos[b];
+    sd::launch_brope_table(at, batch, dh, dims->rope_theta, rope_cs, s);
+  }
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
     // QKV for every sequence from one read of W_qkv, then RoPE and the appends
-    sd::BgemvArgs g{};
-    if (mc) {
-      sd::launch_bmma(mm(sd::K_BATCH_QKV, hidden, d, l.attn_norm, l.w_qkv_m, nullptr, qkv_out,
-                         sd::MM_STORE, qkv),
-                      s);
-    } else {
-      g.kind = sd::K_BATCH_QKV;
-      g.x = hidden;
-      g.nb = batch;
-      g.d_in = d;
-      g.norm = l.attn_norm;
-      g.eps = dims->rms_eps;
-      g.w = l.w_qkv;
-      g.rows = qkv_out;
-      g.mode = 0;
-      g.out = qkv;
-      sd::launch_bgemv(g, dims->w_dtype, s);
-    }
     sd::BatchKv kvs{};
     for (int b = 0; b < batch; ++b) {
       const sd_seq_kv& c = kv[(size_t)b * n_layers + i];
@@ -994,8 +986,38 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
       kvs.cap_sel[b] = c.cap_sel;
       kvs.row_sel[b] = c.n_sel;
     }
-    sd::launch_brope_append(qkv, batch, qkv_out, hq, hkv, dh, dims->rope_theta, kvs, q,
-                            dims->kv_dtype, s);
+    sd::BgemvArgs g{};
+    if (mc && fused_rope) {  // RoPE and the appends in the last slice's epilogue
+      sd::BmmaArgs m = mm(sd::K_BATCH_QKV, hidden, d, l.attn_norm, l.w_qkv_m, nullptr, qkv_out,
+                          sd::MM_QKV, qkv);
+      m.kvs = kvs;
+      m.rope_cs = rope_cs;
+      m.q_out = q;
+      m.h_q = hq;
+      m.h_kv = hkv;
+      m.theta = dims->rope_theta;
+      sd::launch_bmma(m, s);
+    } else {
+      if (mc) {
+        sd::launch_bmma(mm(sd::K_BATCH_QKV, hidden, d, l.attn_norm, l.w_qkv_m, nullptr, qkv_out,
+                           sd::MM_STORE, qkv),
+                        s);
+      } else {
+        g.kind = sd::K_BATCH_QKV;
+        g.x = hidden;
+        g.nb = batch;
+        g.d_in = d;
+        g.norm = l.attn_norm;
+        g.eps = dims->rms_eps;
+        g.w = l.w_qkv;
+        g.rows = qkv_out;
+        g.mode = 0;
+        g.out = qkv;
+        sd::launch_bgemv(g, dims->w_dtype, s);
+      }
+      sd::launch_brope_append(qkv, batch, qkv_out, hq, hkv, dh, dims->rope_theta, kvs, q,
+                              dims->kv_dtype, s);
+    }
     // attention: one launch over every sequence's own cache (full or
     // gathered), chunks planned over all sequences' rows, then one merge
     {

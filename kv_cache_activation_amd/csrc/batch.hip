@@ -214,9 +214,8 @@ __global__ void brope_append_kernel(const float* __restrict__ qkv, int qkv_out, 
   const float* src = qkv + (size_t)b * qkv_out + (size_t)head * dh;
   float lo = src[i], hi = src[i + half];
   if (head < h_q + h_kv && theta > 0.f) {  // rotate-half pair (i, i + d_h / 2)
-    const double inv = pow((double)theta, -2.0 * (double)i / (double)dh);
-    const double ang = (double)kvs.pos[b] * inv;
-    const float c = (float)cos(ang), s = (float)sin(ang);
+    float c, s;
+    rope_cs(kvs.pos[b], i, dh, theta, c, s);
     const float l2 = lo * c - hi * s, h2 = hi * c + lo * s;
     lo = l2;
     hi = h2;
@@ -239,6 +238,15 @@ __global__ void brope_append_kernel(const float* __restrict__ qkv, int qkv_out, 
     store_elem(srow + i, lo);
     store_elem(srow + i + half, hi);
   }
+}
+
+// The rotations of every pair at each sequence's position, once per step.
+__global__ void brope_table_kernel(BatchKv kvs, int dh, float theta, float2* __restrict__ cs) {
+  const int b = blockIdx.x, i = threadIdx.x, half = dh / 2;
+  if (i >= half) return;
+  float c, s;
+  rope_cs(kvs.pos[b], i, dh, theta, c, s);
+  cs[b * half + i] = make_float2(c, s);
 }
 
 template <typename WT, int NB, int NCH, bool GATE>
@@ -304,6 +312,11 @@ int cu_count_dev() {
 void launch_bgemv(const BgemvArgs& a, int w_dtype, hipStream_t s) {
   if (w_dtype == 1) bgemv_typed<bf16_t>(a, s);
   else bgemv_typed<float>(a, s);
+}
+
+void launch_brope_table(const BatchKv& kvs, int nb, int dh, float theta, float2* cs,
+                        hipStream_t s) {
+  launch_kernel(K_BATCH_ROPE, brope_table_kernel, dim3(nb), dim3(dh / 2), 0, s, kvs, dh, theta, cs);
 }
 
 void launch_brope_append(const float* qkv, int nb, int qkv_out, int h_q, int h_kv, int dh,

@@ -43,9 +43,11 @@
 //      x^2 sums) are stored at agent scope, then the workgroup takes its row
 //      group's ticket;
 //   5. the slice that draws the group's last ticket adds the KS partials in
-//      slice order and applies the epilogue: y = (QKV), y += (O and down, the
-//      residual), or the CATS gate: a = SiLU(gate), keep_b = |a_b| > t,
-//      hmid_b = keep_b ? a_b up_b : 0, and the union of the keeps.
+//      slice order and applies the epilogue: y = (QKV), or for QKV with
+//      128-dim heads (a row group is one head) RoPE at each sequence's
+//      position with q written out and k, v appended to its caches; y += (O
+//      and down, the residual); or the CATS gate: a = SiLU(gate), keep_b =
+//      |a_b| > t, hmid_b = keep_b ? a_b up_b : 0, and the union of the keeps.
 // The slice length (8, 16 or 32 steps) is chosen per launch so that the grid
 // covers every compute unit and the chip holds it at once: every workgroup
 // streams from the start and none waits for a second round.  No workgroup waits for another, and the summation
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
       for (int kk = 0; kk < KB; ++kk) acc[i] += t[i][kk];
   }
   if (threadIdx.x < NB) rs_s[threadIdx.x] = a.norm ? 1.0f / sqrtf(tot / (float)d_in + a.eps) : 1.f;
-  if constexpr (EPI == MM_SWIGLU) {
+  if constexpr (EPI == MM_SWIGLU || EPI == MM_QKV) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int u = threadIdx.x + i * kMmThreads;
@@ -339,6 +341,39 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
       if (u < NU && b < nb && row < rows) {
         const float v = rs_s[b] * acc[i];
         a.out[(size_t)b * rows + row] = EPI == MM_RESID ? old[i] + v : v;
+      }
+    }
+  } else if constexpr (EPI == MM_QKV) {
+    // row group g is head g: thread (b, i) rotates pair (i, i + 64) of
+    // sequence b, then writes q or appends k, v (bf16) to b's caches
+    constexpr int DH = kMmGroupRows, HALF = DH / 2;
+    const int b = threadIdx.x / HALF, i = threadIdx.x % HALF, head = g;
+    if (b < nb) {
+      float lo = rs_s[b] * ys[0][b][i], hi = rs_s[b] * ys[0][b][i + HALF];
+      if (head < a.h_q + a.h_kv && a.theta > 0.f) {
+        const float2 r = a.rope_cs[b * HALF + i];
+        const float c = r.x, sn = r.y;
+        const float l2 = lo * c - hi * sn, h2 = hi * c + lo * sn;
+        lo = l2;
+        hi = h2;
+      }
+      if (head < a.h_q) {
+        float* dst = a.q_out + ((size_t)b * a.h_q + head) * DH;
+        dst[i] = lo;
+        dst[i + HALF] = hi;
+      } else {
+        const bool is_k = head < a.h_q + a.h_kv;
+        const int kv = is_k ? head - a.h_q : head - a.h_q - a.h_kv;
+        bf16_t* full = static_cast<bf16_t*>(is_k ? a.kvs.k_full[b] : a.kvs.v_full[b]);
+        bf16_t* row = full + ((size_t)kv * a.kvs.cap_full[b] + a.kvs.row_full[b]) * DH;
+        store_elem(row + i, lo);
+        store_elem(row + i + HALF, hi);
+        bf16_t* sel = static_cast<bf16_t*>(is_k ? a.kvs.k_sel[b] : a.kvs.v_sel[b]);
+        if (sel) {
+          bf16_t* srow = sel + ((size_t)kv * a.kvs.cap_sel[b] + a.kvs.row_sel[b]) * DH;
+          store_elem(srow + i, lo);
+          store_elem(srow + i + HALF, hi);
+        }
       }
     }
   } else {  // MM_SWIGLU: the CATS gate per sequence, the union per row
@@ -424,6 +459,7 @@ template <int NB>
 static void bmma_nb(const BmmaArgs& a, hipStream_t s) {
   if (a.w1) mm_launch<NB, true, MM_SWIGLU>(a, s);
   else if (a.epi == MM_RESID) mm_launch<NB, false, MM_RESID>(a, s);
+  else if (a.epi == MM_QKV) mm_launch<NB, false, MM_QKV>(a, s);
   else mm_launch<NB, false, MM_STORE>(a, s);
 }
 

@@ -59,6 +59,16 @@ __device__ __forceinline__ float sum_agent(const float* p, size_t stride, int n)
   return v;
 }
 
+// ---------------------------------------------------------------- RoPE
+// cos and sin of the rotation of pair (i, i + d_h / 2) at position pos:
+// angle pos * theta^(-2 i / d_h), formed in double precision.
+__device__ __forceinline__ void rope_cs(int pos, int i, int dh, float theta, float& c, float& s) {
+  const double inv = pow((double)theta, -2.0 * (double)i / (double)dh);
+  const double ang = (double)pos * inv;
+  c = (float)cos(ang);
+  s = (float)sin(ang);
+}
+
 // ---------------------------------------------------------------- matrix cores
 // Operand type of v_mfma_f32_16x16x32_bf16 (eight bf16 values per lane).
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;

@@ -228,6 +228,10 @@ struct BgemvArgs {
   float* hmid;
 };
 void launch_bgemv(const BgemvArgs& a, int w_dtype, hipStream_t s);
+// cs[b][i] = (cos, sin) of rotation pair i at sequence b's position (the
+// rotation of launch_brope_append), for b < nb and i < dh / 2.
+void launch_brope_table(const BatchKv& kvs, int nb, int dh, float theta, float2* cs,
+                        hipStream_t s);
 void launch_brope_append(const float* qkv, int nb, int qkv_out, int h_q, int h_kv, int dh,
                          float theta, const BatchKv& kvs, float* q, int kv_dtype, hipStream_t s);
 int cu_count_dev();
@@ -237,7 +241,7 @@ int cu_count_dev();
 // (input slices, bmma_groups row groups of 128 rows); the last
 // slice of a row group to finish sums the slices' partials and applies the
 // epilogue.
-enum { MM_STORE = 0, MM_RESID = 1, MM_SWIGLU = 2 };
+enum { MM_STORE = 0, MM_RESID = 1, MM_SWIGLU = 2, MM_QKV = 3 };
 struct BmmaArgs {
   int kind;
   const float* x;      // [nb, d_in] float32 (d_in % 8 == 0)
@@ -256,6 +260,15 @@ struct BmmaArgs {
   float* part;         // bmma_part_floats(rows, d_in, w1 != nullptr)
   float* ssq;          // bmma_ssq_floats(...) (with a norm)
   unsigned* tickets;   // [bmma_groups(rows)]: zero before the launch, zero after it
+  // MM_QKV (head_dim 128, bf16 caches: row group g is head g): RoPE at each
+  // sequence's position on q and k (rope_cs from launch_brope_table; theta
+  // <= 0: none), q written to q_out [nb, h_q, 128], k and v appended to each
+  // sequence's caches (as launch_brope_append)
+  BatchKv kvs;
+  const float2* rope_cs;
+  float* q_out;
+  int h_q, h_kv;
+  float theta;
 };
 int bmma_groups(int rows);
 size_t bmma_part_floats(int rows, int d_in, bool dual);
