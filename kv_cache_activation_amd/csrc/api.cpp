@@ -964,6 +964,7 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
   // 128-dim heads make each 128-row group of W_qkv one head, so the matrix-core
   // QKV applies RoPE and appends to bf16 caches itself
   const bool fused_rope = mc && dh == 128 && dims->kv_dtype == SD_BF16;
+  const bool fused_merge = mc && dh == 128;  // O merges the attention's split partials
   float2* rope_cs = reinterpret_cast<float2*>(wsb + B.rope);
   if (fused_rope && dims->rope_theta > 0.f) {  // the positions are the same in every layer
     sd::BatchKv at{};
@@ -1019,7 +1020,10 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
                               dims->kv_dtype, s);
     }
     // attention: one launch over every sequence's own cache (full or
-    // gathered), chunks planned over all sequences' rows, then one merge
+    // gathered), chunks planned over all sequences' rows, then one merge (on
+    // the matrix-core path with 128-dim heads the O projection merges the
+    // split partials itself)
+    int m_stride = 0, m_splits[sd::kMaxBatch] = {};
     {
       sd::AttnArgs a{};
       a.q = q;
@@ -1052,7 +1056,10 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
       a.k = a.bt.k[0];
       a.v = a.bt.v[0];
       a.sink = a.n_ctx;
+      a.no_merge = fused_merge;
       sd::launch_attn(a, dims->kv_dtype, s);
+      m_stride = a.n_splits;
+      for (int b = 0; b < batch; ++b) m_splits[b] = a.bt.splits[b];
     }
     uint8_t* uni = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + B.uni);
     float* hmid = reinterpret_cast<float*>(wsb + B.hmid);
@@ -1060,9 +1067,21 @@ sd_status sd_decode_step_batch(const sd_dims* dims, int32_t n_layers, const sd_l
       // O with the residual; gate and up with the CATS gate, the union and
       // hmid; down with the residual (hmid is zero where a sequence dropped
       // the channel)
-      sd::launch_bmma(mm(sd::K_BATCH_O, attn, hq * dh, nullptr, l.w_o_m, nullptr, d,
-                         sd::MM_RESID, hidden),
-                      s);
+      if (fused_merge) {
+        sd::BmmaArgs m = mm(sd::K_BATCH_O, attn, hq * dh, nullptr, l.w_o_m, nullptr, d,
+                            sd::MM_OMERGE, hidden);
+        m.h_q = hq;
+        m.pm = reinterpret_cast<float*>(wsb + B.pm);
+        m.pl = reinterpret_cast<float*>(wsb + B.pl);
+        m.pacc = reinterpret_cast<float*>(wsb + B.pacc);
+        m.m_stride = m_stride;
+        for (int b = 0; b < batch; ++b) m.m_splits[b] = m_splits[b];
+        sd::launch_bmma(m, s);
+      } else {
+        sd::launch_bmma(mm(sd::K_BATCH_O, attn, hq * dh, nullptr, l.w_o_m, nullptr, d,
+                           sd::MM_RESID, hidden),
+                        s);
+      }
       sd::BmmaArgs m = mm(sd::K_BATCH_GATE_UP, hidden, d, l.mlp_norm, l.w_gate_m, l.w_up_m, ff,
                           sd::MM_SWIGLU, nullptr);
       m.t = mlp_sparse ? l.cats_threshold : -1.0f;

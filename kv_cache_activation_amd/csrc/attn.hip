@@ -463,6 +463,7 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   }
 #undef SD_ATTN_G
 #undef SD_ATTN_M
+  if (a.no_merge) return;  // the consumer merges the partials itself
   const dim3 mgrid(nq, DH / kMergeCols);
   const int G_all = a.h_q / a.h_kv;
 #define SD_MERGE_M(CAPV, MM)                                                                   \

@@ -172,7 +172,41 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
     ok[gi] = wave < nb && e8 < CH * 4 && k < d_in;  // d_in % 8 == 0: the group is whole
 #pragma unroll
     for (int e = 0; e < 8; ++e) xv[gi][e] = nv[gi][e] = 0.f;
-    if (ok[gi]) {
+    if constexpr (EPI == MM_OMERGE) {
+      // the merged attention output of head k / 128, columns k % 128 .. + 7:
+      // the sequence's split partials combined with the weights
+      // 2^(m_sp - max m) as the split-K combine does, online over the splits
+      if (ok[gi]) {
+        const int col = k % kMmGroupRows;
+        const size_t hb = ((size_t)wave * a.h_q + k / kMmGroupRows) * a.m_stride;
+        const int ns = a.m_splits[wave];
+        float M = -INFINITY, L = 0.f, acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int sp0 = 0; sp0 < ns; sp0 += 4) {
+          float mv[4], lv[4], vv[4][8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {  // the loads of four splits first
+            const size_t sp = hb + min(sp0 + u, ns - 1);
+            mv[u] = a.pm[sp];
+            lv[u] = a.pl[sp];
+            load8f(a.pacc + sp * kMmGroupRows + col, vv[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (sp0 + u >= ns || mv[u] == -INFINITY) continue;  // past the end, or empty
+            const float mn = fmaxf(M, mv[u]);
+            const float so = M == -INFINITY ? 0.f : exp2f(M - mn), w = exp2f(mv[u] - mn);
+            L = fmaf(L, so, w * lv[u]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(acc[e], so, w * vv[u][e]);
+            M = mn;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[gi][e] = acc[e] / L;
+      }
+    } else if (ok[gi]) {
       load8f(a.x + (size_t)wave * d_in + k, xv[gi]);
       if (a.norm) load8f(a.norm + k, nv[gi]);
     }
@@ -293,8 +327,9 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
     // single matrix: the thread's sums are the outputs it writes)
     const int u = threadIdx.x + i * kMmThreads, b = u / kMmGroupRows;
     const int row = g * kMmGroupRows + u % kMmGroupRows;
-    old[i] = EPI == MM_RESID && u < NU && b < nb && row < rows ? a.out[(size_t)b * rows + row]
-                                                                 : 0.f;
+    old[i] = (EPI == MM_RESID || EPI == MM_OMERGE) && u < NU && b < nb && row < rows
+                 ? a.out[(size_t)b * rows + row]
+                 : 0.f;
   }
   for (int k0 = 0; k0 < KS; k0 += KB) {
     float t[IPT][KB], q[KB];
@@ -333,14 +368,14 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   if (threadIdx.x == 0)
     __hip_atomic_store(a.tickets + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if constexpr (EPI == MM_STORE || EPI == MM_RESID) {
+  if constexpr (EPI == MM_STORE || EPI == MM_RESID || EPI == MM_OMERGE) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int u = threadIdx.x + i * kMmThreads, b = u / kMmGroupRows;
       const int row = g * kMmGroupRows + u % kMmGroupRows;
       if (u < NU && b < nb && row < rows) {
         const float v = rs_s[b] * acc[i];
-        a.out[(size_t)b * rows + row] = EPI == MM_RESID ? old[i] + v : v;
+        a.out[(size_t)b * rows + row] = EPI == MM_STORE ? v : old[i] + v;
       }
     }
   } else if constexpr (EPI == MM_QKV) {
@@ -460,6 +495,7 @@ static void bmma_nb(const BmmaArgs& a, hipStream_t s) {
   if (a.w1) mm_launch<NB, true, MM_SWIGLU>(a, s);
   else if (a.epi == MM_RESID) mm_launch<NB, false, MM_RESID>(a, s);
   else if (a.epi == MM_QKV) mm_launch<NB, false, MM_QKV>(a, s);
+  else if (a.epi == MM_OMERGE) mm_launch<NB, false, MM_OMERGE>(a, s);
   else mm_launch<NB, false, MM_STORE>(a, s);
 }
 

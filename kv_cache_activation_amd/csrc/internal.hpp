@@ -168,6 +168,7 @@ struct AttnArgs {
   float* pacc;
   float* out;
   float* lse;
+  int no_merge;         // leave the split partials for the consumer (no merge launch)
 };
 
 struct SelectArgs {
@@ -241,7 +242,7 @@ int cu_count_dev();
 // (input slices, bmma_groups row groups of 128 rows); the last
 // slice of a row group to finish sums the slices' partials and applies the
 // epilogue.
-enum { MM_STORE = 0, MM_RESID = 1, MM_SWIGLU = 2, MM_QKV = 3 };
+enum { MM_STORE = 0, MM_RESID = 1, MM_SWIGLU = 2, MM_QKV = 3, MM_OMERGE = 4 };
 struct BmmaArgs {
   int kind;
   const float* x;      // [nb, d_in] float32 (d_in % 8 == 0)
@@ -269,6 +270,14 @@ struct BmmaArgs {
   float* q_out;
   int h_q, h_kv;
   float theta;
+  // MM_OMERGE (O with the residual, head_dim 128): x is not read; sequence b's
+  // input is merged from the batched attention's split partials of its h_q
+  // heads (pm, pl, pacc with stride m_stride splits, m_splits[b] of them)
+  const float* pm;
+  const float* pl;
+  const float* pacc;
+  int m_stride;
+  int m_splits[kMaxBatch];
 };
 int bmma_groups(int rows);
 size_t bmma_part_floats(int rows, int d_in, bool dual);
