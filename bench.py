@@ -938,9 +938,13 @@ KERNEL_SOURCES = {
                    match=r"teal_kernel<unsigned short, false, 1,"),
     "teal_gate_up": dict(rocprof="teal_kernel", src="teal.hip",
                          match=r"teal_kernel<unsigned short, true, 2,"),
-    "batch_qkv": dict(rocprof="bmma_kernel", src="batch_mma.hip", match=r"bmma_kernel<8, false, 0,"),
+    # QKV: the RoPE epilogue (3) with 128-dim heads, else the plain store (0);
+    # O: the attention merge in its staging (4) with 128-dim heads, else the
+    # residual (1) at 16-step slices
+    "batch_qkv": dict(rocprof="bmma_kernel", src="batch_mma.hip",
+                      match=r"bmma_kernel<8, false, [03],"),
     "batch_o": dict(rocprof="bmma_kernel", src="batch_mma.hip",
-                    match=r"bmma_kernel<8, false, 1, 16>"),
+                    match=r"bmma_kernel<8, false, (4, \d+|1, 16)>"),
     "batch_gate_up": dict(rocprof="bmma_kernel", src="batch_mma.hip",
                           match=r"bmma_kernel<8, true, 2,"),
     "batch_down": dict(rocprof="bmma_kernel", src="batch_mma.hip",
