@@ -29,12 +29,15 @@ class BatchStack:
     (its own context length) and its own gathered buffer from the oracle's
     selection."""
 
-    def __init__(self, wl, n_layers, batch, n, keep_ratio, extra=8, matrix_cores=False):
+    def __init__(self, wl, n_layers, batch, n, keep_ratio, extra=8, matrix_cores=False,
+                 kv_dtype=None):
         self.wl, self.B, self.L = wl, batch, n_layers
         self.mc = matrix_cores
+        kvt = kv_dtype or wl.dtype   # the caches' type (the weights' by default)
         self.dims = dims_for(wl)
+        self.dims.kv_dtype = sd.SD_BF16 if kvt == "bf16" else sd.SD_F32
         self.odims = dict(n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
-                          head_dim=wl.head_dim, kv_dtype=wl.dtype, eps=1e-5, theta=500000.0)
+                          head_dim=wl.head_dim, kv_dtype=kvt, eps=1e-5, theta=500000.0)
         self.keep_alive = []
         W = [synth.layer_weights(wl, li) for li in range(n_layers)]
         layers = []
@@ -78,7 +81,7 @@ class BatchStack:
                 seq.append(ostep.Layer(w["attn_norm"], w["w_qkv"], w["w_o"], w["mlp_norm"],
                                        w["w_gate"], w["w_up"], w["w_down_t"], -1.0, k, v, nb,
                                        ks, vs, ke))
-                dk, dv, dks, dvs = (to_dev(a, wl.dtype) for a in (k, v, ks, vs))
+                dk, dv, dks, dvs = (to_dev(a, kvt) for a in (k, v, ks, vs))
                 self.dev_kv.append((dk, dv, dks, dvs))
                 kvs.append(sd.sd_seq_kv(dk.data_ptr(), dv.data_ptr(), cap, nb, dks.data_ptr(),
                                         dvs.data_ptr(), ke + extra, ke))
@@ -316,3 +319,30 @@ def test_matrix_cores_8b_two_layers_dense_then_cats():
                 assert np.array_equal(gu[li], unions[li]), li
         hs = [w for w in want]
         pos = [p + 1 for p in pos]
+
+
+# 128-dim heads: each 128-row group of W_qkv is one head, so the matrix-core
+# QKV applies RoPE and the appends in its epilogue (bf16 caches; float32
+# caches keep the separate RoPE launch), and O merges the attention's split
+# partials while staging its input.
+HEAD128_BF16 = replace(synth.TINY, name="head128-bf16-2layer", wid=10, d_model=512, n_q_heads=4,
+                       n_kv_heads=2, head_dim=128, d_ff=1024, dtype="bf16")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("batch", [2, 8])
+def test_matrix_cores_head128_fused_epilogues_modes_over_steps(batch, kv_dtype):
+    wl = HEAD128_BF16
+    st = BatchStack(wl, 2, batch, 600, 0.25, extra=8, matrix_cores=True, kv_dtype=kv_dtype)
+    hs = [synth.hidden(wl, 30 + b).astype(np.float64) for b in range(batch)]
+    pos = list(st.n)
+    for mode in ("both", "dense", "kv", "cats"):
+        got, want, unions, gu = st.step(hs, pos, mode)
+        for b in range(batch):
+            assert rel_l2(got[b], want[b]) <= TOL["bf16"], (mode, b)
+        if MODES[mode] & sd.SD_MLP_SPARSE:
+            for li in range(st.L):
+                assert np.array_equal(gu[li], unions[li]), (mode, li)
+        hs = [w for w in want]
+        pos = [p + 1 for p in pos]
+    _check_appends(st, TOL["bf16"])
