@@ -71,6 +71,7 @@ constexpr int kMmK = 32;                           // input channels per step
 constexpr int kMmWaves = 8;                        // tiles per row group
 constexpr int kMmThreads = kMmWaves * kWave;       // 512
 constexpr int kMmGroupRows = kMmWaves * kMmRows;   // 128
+constexpr int kMmHeadDim = kMmGroupRows;           // the fused QKV and O paths' head size
 constexpr int kMmNB = 8;                           // partial-sum stride in sequences
 constexpr int kMmChunk = 4;                        // fragment loads per wave and chunk (4 KB)
 constexpr int kMmDepth = 4;                        // chunks in flight per wave
@@ -177,8 +178,8 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
       // the sequence's split partials combined with the weights
       // 2^(m_sp - max m) as the split-K combine does, online over the splits
       if (ok[gi]) {
-        const int col = k % kMmGroupRows;
-        const size_t hb = ((size_t)wave * a.h_q + k / kMmGroupRows) * a.m_stride;
+        const int col = k % kMmHeadDim;
+        const size_t hb = ((size_t)wave * a.h_q + k / kMmHeadDim) * a.m_stride;
         const int ns = a.m_splits[wave];
         float M = -INFINITY, L = 0.f, acc[8];
 #pragma unroll
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
             const size_t sp = hb + min(sp0 + u, ns - 1);
             mv[u] = a.pm[sp];
             lv[u] = a.pl[sp];
-            load8f(a.pacc + sp * kMmGroupRows + col, vv[u]);
+            load8f(a.pacc + sp * kMmHeadDim + col, vv[u]);
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kMmThreads) void bmma_kernel(BmmaArgs a) {
   } else if constexpr (EPI == MM_QKV) {
     // row group g is head g: thread (b, i) rotates pair (i, i + 64) of
     // sequence b, then writes q or appends k, v (bf16) to b's caches
-    constexpr int DH = kMmGroupRows, HALF = DH / 2;
+    constexpr int DH = kMmHeadDim, HALF = DH / 2;
     const int b = threadIdx.x / HALF, i = threadIdx.x % HALF, head = g;
     if (b < nb) {
       float lo = rs_s[b] * ys[0][b][i], hi = rs_s[b] * ys[0][b][i + HALF];
