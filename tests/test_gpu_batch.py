@@ -330,7 +330,7 @@ HEAD128_BF16 = replace(synth.TINY, name="head128-bf16-2layer", wid=10, d_model=5
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("batch", [2, 8])
+@pytest.mark.parametrize("batch", [2, 3, 5, 8])
 def test_matrix_cores_head128_fused_epilogues_modes_over_steps(batch, kv_dtype):
     wl = HEAD128_BF16
     st = BatchStack(wl, 2, batch, 600, 0.25, extra=8, matrix_cores=True, kv_dtype=kv_dtype)
