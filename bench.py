@@ -166,6 +166,9 @@ class Stack:
                 W["w_down_t"].data_ptr(), self.thresholds[li], 0, self.K[li].data_ptr(),
                 self.V[li].data_ptr(), self.cap_full, 0, self.KS[li].data_ptr(),
                 self.VS[li].data_ptr(), self.cap_sel, 0, self.MASK[li].data_ptr()))
+            # the down projection in column blocks of 128 outputs as well
+            W["w_down_b"] = sdev.teal_blocked(W["w_down_t"].t())
+            layers[-1].w_down_b = W["w_down_b"].data_ptr()
         self.layers = (sd.sd_layer * self.L)(*layers)
         self.ragged = False
         self.teal = False
@@ -513,7 +516,7 @@ class Stack:
             f = [sum(x[k] for x in fr) / len(fr) for k in range(4)]
             qd = wl.n_q_heads * dh
             alg.update(teal_qkv=2 * d * wl.qkv_out * f[0], teal_o=2 * qd * d * f[1],
-                       teal_gate_up=4 * d * wl.d_ff * f[2], cats_down=2 * wl.d_ff * d * f[3])
+                       teal_gate_up=4 * d * wl.d_ff * f[2], teal_down=2 * wl.d_ff * d * f[3])
         out = {}
         for name, (launches, tot) in stats.items():
             avg_us = tot / launches * 1e3
@@ -682,6 +685,7 @@ def single_layer_cells(stack, copies=4):
                 W["w_down_t"].data_ptr(), thr[i], 0, K[i].data_ptr(), V[i].data_ptr(), cap, n,
                 None if KS is None else KS[i].data_ptr(),
                 None if VS is None else VS[i].data_ptr(), cap_sel, 0, stack.MASK[i].data_ptr())))
+            ls[-1][0].w_down_b = W["w_down_b"].data_ptr()
         return ls
 
     def run_cell(ls, n, k_keep, flags):
@@ -930,8 +934,12 @@ KERNEL_SOURCES = {
     "o_residual": dict(rocprof="o_residual_kernel", src="gemv.hip"),
     "cats_gate_up": dict(rocprof="gate_kernel", src="gemv.hip",
                          match=r"gate_kernel<[^<>]*false, \d+>"),  # not the calibration gate
-    "cats_down": dict(rocprof="down_kernel", src="down.hip", match=r"down_kernel<[^,]+, 1>"),
-    "cats_reduce": dict(rocprof="mlp_reduce_kernel", src="down.hip"),
+    # the step's down projection over column blocks (after the CATS gate or a
+    # dense one; after TEAL's gate and up), partial sums added in the launch
+    "cats_down": dict(rocprof="teal_kernel", src="teal.hip",
+                      match=r"teal_kernel<unsigned short, false, 5,"),
+    "teal_down": dict(rocprof="teal_kernel", src="teal.hip",
+                      match=r"teal_kernel<unsigned short, false, 4,"),
     "teal_qkv": dict(rocprof="teal_kernel", src="teal.hip",
                      match=r"teal_kernel<unsigned short, false, 3,"),
     "teal_o": dict(rocprof="teal_kernel", src="teal.hip",
@@ -1085,7 +1093,7 @@ def cpu_baseline(stack, n, seconds):
     from oracle import cats as ocats, step as ostep
 
     wl = stack.wl
-    W = {k: v.float().cpu().numpy() for k, v in stack.W[0].items()}
+    W = {k: v.float().cpu().numpy() for k, v in stack.W[0].items() if k != "w_down_b"}
     reps_cap = 512
     shape = (wl.n_kv_heads, n + reps_cap, wl.head_dim)
     k = np.zeros(shape, np.float32)

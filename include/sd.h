@@ -331,6 +331,12 @@ typedef struct {
   const void* w_gate_m;    /* W_gate [d_ff, d] */
   const void* w_up_m;      /* W_up [d_ff, d] */
   const void* w_down_m;    /* W_down [d, d_ff] (the down projection itself, not w_down_t) */
+  /* optional, sd_decode_step: W_down [d, d_ff] in the column-block layout of
+   * sd_teal_gemv (w_t with d_out = d, d_in = d_ff).  When set, the down
+   * projection reads only the kept channels' pieces of it, with the partial
+   * sums added inside the launch, instead of w_down_t's rows and a separate
+   * reduce; NULL: w_down_t */
+  const void* w_down_b;
 } sd_layer;
 
 /*

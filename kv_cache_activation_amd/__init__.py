@@ -66,7 +66,7 @@ class sd_layer(ctypes.Structure):
                 ("n_sel_heads", ctypes.POINTER(ctypes.c_int32)),
                 ("w_qkv_m", ctypes.c_void_p), ("w_o_m", ctypes.c_void_p),
                 ("w_gate_m", ctypes.c_void_p), ("w_up_m", ctypes.c_void_p),
-                ("w_down_m", ctypes.c_void_p)]
+                ("w_down_m", ctypes.c_void_p), ("w_down_b", ctypes.c_void_p)]
 
 
 class sd_seq_kv(ctypes.Structure):

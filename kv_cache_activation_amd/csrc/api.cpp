@@ -209,6 +209,29 @@ void enqueue_attn(const sd_dims& dm, const Layout& L, char* ws, const float* q, 
   sd::launch_attn(a, dm.kv_dtype, s);
 }
 
+// The CATS gate with the up rows of the kept channels: act, keep bytes, and
+// hmid in the workspace (zero where dropped).
+float* enqueue_gate(const sd_dims& dm, const Layout& L, char* ws, const float* x,
+                    const float* norm, const void* wg, const void* wu, float t, int gate_in,
+                    float* act, uint8_t* keep, hipStream_t s) {
+  sd::GateArgs g{};
+  g.x = x;
+  g.norm = norm;
+  g.eps = dm.rms_eps;
+  g.w_gate = wg;
+  g.w_up = wu;
+  g.d = dm.d_model;
+  g.dff = dm.d_ff;
+  g.t = t;
+  g.gate_in = gate_in;
+  g.act = act;
+  g.keep = keep;
+  g.hmid = reinterpret_cast<float*>(ws + L.hmid);
+  g.n_states = 1;
+  sd::launch_gate(g, dm.w_dtype, s);
+  return g.hmid;
+}
+
 void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, const float* norm,
                  const void* wg, const void* wu, const void* wd, float t, int gate_in, float* act,
                  uint8_t* keep, float* y, int accumulate, int32_t* idx, int32_t* n_kept,
@@ -241,6 +264,20 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   dn.idx_out = idx;
   dn.n_kept_out = n_kept;
   sd::launch_down(dn, dm.w_dtype, s);
+}
+
+// Input slices of the column-block down projection: the fewest (at most 2048
+// channels each) that give every compute unit two workgroups, so that a unit
+// streams with eight waves (measured at 8B-class widths, isolated launches,
+// 50% kept: 16 slices 15.4 us, 12 15.6 us, 8 16.2 us, 24 17.8 us).
+int down_block_slices(int d_ff, int d) {
+  const int nblk = (d + sd::kTealBlock - 1) / sd::kTealBlock;
+  int s = (2 * sd::cu_count_dev() + nblk - 1) / nblk;
+  const int need = (d_ff + sd::kTealMaxRange - 1) / sd::kTealMaxRange;
+  if (s < need) s = need;
+  if (s > sd::kTealMaxSlices) s = sd::kTealMaxSlices;
+  if (s > d_ff / 8) s = d_ff / 8;
+  return s < 1 ? 1 : s;
 }
 
 // One TEAL projection over column blocks, epilogue included (the layout's
@@ -600,6 +637,10 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     if (layers[i].cap_full > max_cap) max_cap = layers[i].cap_full;
   const Layout L = make_layout(*dims, masked ? max_cap : 0, 0);
   if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  bool blk_down = false;  // some layer's down projection reads column blocks
+  for (int i = 0; i < n_layers; ++i) blk_down = blk_down || layers[i].w_down_b != nullptr;
+  if (blk_down && (dims->d_model + sd::kTealBlock - 1) / sd::kTealBlock > sd::kTealMaxBlocks)
+    return fail(SD_EUNSUPPORTED, "w_down_b: d_model above %d", sd::kTealMaxBlocks * sd::kTealBlock);
   for (int i = 0; i < n_layers; ++i) {
     const sd_layer& l = layers[i];
     if (!aligned(l.attn_norm) || !aligned(l.mlp_norm) || !aligned(l.w_down_t) ||
@@ -638,6 +679,8 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     if (std::isnan(l.cats_threshold)) return fail(SD_EINVAL, "layer %d: threshold is NaN", i);
     if (l.mask_out && !aligned(l.mask_out))
       return fail(SD_EINVAL, "layer %d: misaligned mask_out", i);
+    if (l.w_down_b && !aligned(l.w_down_b))
+      return fail(SD_EINVAL, "layer %d: misaligned w_down_b", i);
     if (kv_window && (l.window_keep < 1 || l.window_sink < 0 || l.window_sink > l.window_keep))
       return fail(SD_EINVAL, "layer %d: need 0 <= window_sink <= window_keep, window_keep >= 1", i);
   }
@@ -692,10 +735,10 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     }
     const int qkv_out = (hq + 2 * hkv) * dh;
     uint8_t* tm = teal ? l.teal_masks_out : nullptr;  // [d | h_q d_h | d | d_ff]
+    if (i == 0 && (teal || blk_down))  // every column-block launch leaves its tickets zero
+      sd::launch_teal_zero(reinterpret_cast<unsigned*>(wsb + L.teal_tickets), sd::kTealMaxBlocks,
+                           s);
     if (teal) {
-      if (i == 0)  // every TEAL launch leaves its tickets zero for the next
-        sd::launch_teal_zero(reinterpret_cast<unsigned*>(wsb + L.teal_tickets), sd::kTealMaxBlocks,
-                             s);
       sd::TealArgs a = teal_args(sd::K_TEAL_QKV, *dims, L, wsb, hidden, d, l.attn_norm,
                                  l.teal_t[0], l.w_qkv_t, nullptr, qkv_out, sd::TEAL_QKV);
       a.qkv = qa;
@@ -744,6 +787,14 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
       ag.keep_next = dkeep;
       ag.keep_out = tm ? tm + d + hq * dh : nullptr;
       sd::launch_teal(ag, dims->w_dtype, dims->kv_dtype, s);
+      if (l.w_down_b) {  // down over column blocks: |hmid| > t tested per slice again
+        sd::TealArgs db = teal_args(sd::K_TEAL_DOWN, *dims, L, wsb, hmid, ff, nullptr, l.teal_t[3],
+                                    l.w_down_b, nullptr, d, sd::TEAL_DOWN);
+        db.y = hidden;
+        db.slices = down_block_slices(ff, d);
+        sd::launch_teal(db, dims->w_dtype, dims->kv_dtype, s);
+        continue;
+      }
       // down: h += W_down (mask * hmid)
       sd::DownArgs dn{};
       dn.w_down_t = l.w_down_t;
@@ -760,9 +811,23 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
     sd::launch_o(attn, l.w_o, hq * dh, d, hidden, dims->w_dtype, s);
 
     uint8_t* keep = l.mask_out ? l.mask_out : reinterpret_cast<uint8_t*>(wsb + L.keep);
-    enqueue_mlp(*dims, L, wsb, hidden, l.mlp_norm, l.w_gate, l.w_up, l.w_down_t,
-                mlp_sparse ? l.cats_threshold : -1.0f, 0, reinterpret_cast<float*>(wsb + L.act),
-                keep, hidden, 1, nullptr, nullptr, s);
+    const float t_mlp = mlp_sparse ? l.cats_threshold : -1.0f;
+    if (l.w_down_b) {
+      // the gate writes hmid, zero where a channel is dropped; the down
+      // projection over column blocks then reads the pieces of the channels
+      // with hmid != 0 (dense: every channel), partial sums inside the launch
+      float* hm = enqueue_gate(*dims, L, wsb, hidden, l.mlp_norm, l.w_gate, l.w_up, t_mlp, 0,
+                               reinterpret_cast<float*>(wsb + L.act), keep, s);
+      sd::TealArgs db = teal_args(sd::K_DOWN, *dims, L, wsb, hm, dims->d_ff, nullptr,
+                                  mlp_sparse ? 0.0f : -1.0f, l.w_down_b, nullptr, d,
+                                  sd::TEAL_CATS_DOWN);
+      db.y = hidden;
+      db.slices = down_block_slices(dims->d_ff, d);
+      sd::launch_teal(db, dims->w_dtype, dims->kv_dtype, s);
+      continue;
+    }
+    enqueue_mlp(*dims, L, wsb, hidden, l.mlp_norm, l.w_gate, l.w_up, l.w_down_t, t_mlp, 0,
+                reinterpret_cast<float*>(wsb + L.act), keep, hidden, 1, nullptr, nullptr, s);
   }
   st = check_launch("sd_decode_step");
   if (st) return st;

@@ -228,8 +228,8 @@ __global__ __launch_bounds__(T) void o_residual_kernel(const float* __restrict__
 // dense in CATS: every row is read, so the first phase is a plain
 // row-streaming GEMV over the wave's rows.  With W_up given, each wave then
 // reads the up rows of its kept channels only, two at a time with both
-// loads issued together, and writes hmid_i = a_i (W_up[i] . x) (hmid of a
-// dropped channel is left as it was and never read).  blockIdx.y selects one
+// loads issued together, and writes hmid_i = a_i (W_up[i] . x), zero for a
+// dropped channel.  blockIdx.y selects one
 // of several input states (calibration); the calibration instance (CALIB)
 // only has a kernel name of its own.
 template <typename WT, int NCH, bool FULL, bool NORM, bool CALIB, int T>
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(T) void gate_kernel(
   if (lane < n) {
     if (!gate_in) act[r] = store_abs ? fabsf(a) : a;
     if (!CALIB && keep) keep[r] = kept;
-    if (!CALIB && Wu && kept) hmid[r] = hm;
+    if (!CALIB && Wu) hmid[r] = hm;  // zero for a dropped channel
   }
 }
 

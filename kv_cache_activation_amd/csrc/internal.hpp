@@ -115,7 +115,17 @@ constexpr int kTealBlock = 128;
 constexpr int kTealMaxRange = 2048;  // input channels per slice, at most
 constexpr int kTealMaxSlices = 32;
 constexpr int kTealMaxBlocks = 1024; // blocks' tickets in the workspace
-enum TealEpi { TEAL_STORE = 0, TEAL_ACC = 1, TEAL_SWIGLU = 2, TEAL_QKV = 3 };
+// TEAL_DOWN and TEAL_CATS_DOWN are TEAL_ACC under kernel names of their own:
+// the down projection after TEAL's gate and up, and after the CATS gate (or a
+// dense one), so that traces and counters tell them from the O projection.
+enum TealEpi {
+  TEAL_STORE = 0,
+  TEAL_ACC = 1,
+  TEAL_SWIGLU = 2,
+  TEAL_QKV = 3,
+  TEAL_DOWN = 4,
+  TEAL_CATS_DOWN = 5
+};
 int teal_slices(int d_in, int d_out, int mats, int wbytes);
 
 struct TealArgs {
@@ -138,6 +148,7 @@ struct TealArgs {
   int32_t* idx_out;    // optional ascending kept list
   int32_t* n_kept_out; // optional
   uint8_t* keep_out;   // optional keep bytes [d_in]
+  int slices;          // input slices; 0: teal_slices
 };
 
 // Batched attention: sequence s has its own cache (k[s], v[s], cap[s]) of

@@ -227,11 +227,12 @@ __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
     __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int cb = b * kTealBlock;
-  if constexpr (EPI == TEAL_STORE || EPI == TEAL_ACC) {
+  constexpr bool ACC = EPI == TEAL_ACC || EPI == TEAL_DOWN || EPI == TEAL_CATS_DOWN;
+  if constexpr (EPI == TEAL_STORE || ACC) {
     if (threadIdx.x < NCOL) {
       const int mat = threadIdx.x / kTealBlock, c = cb + threadIdx.x % kTealBlock;
       float* y = mat ? a.y2 : a.y;
-      if (c < d_out) y[c] = (EPI == TEAL_ACC ? y[c] : 0.f) + col[threadIdx.x];
+      if (c < d_out) y[c] = (ACC ? y[c] : 0.f) + col[threadIdx.x];
     }
   } else if constexpr (EPI == TEAL_SWIGLU) {
     if (threadIdx.x < kTealBlock) {
@@ -322,7 +323,7 @@ int teal_slices(int d_in, int d_out, int mats, int wbytes) {
 
 template <typename WT, bool DUAL, typename KT>
 static void teal_typed(const TealArgs& a, hipStream_t s) {
-  const dim3 grid(teal_slices(a.d_in, a.d_out, DUAL ? 2 : 1, (int)sizeof(WT)),
+  const dim3 grid(a.slices > 0 ? a.slices : teal_slices(a.d_in, a.d_out, DUAL ? 2 : 1, (int)sizeof(WT)),
                   (a.d_out + kTealBlock - 1) / kTealBlock);
   switch (a.epi) {
     case TEAL_STORE:
@@ -330,6 +331,16 @@ static void teal_typed(const TealArgs& a, hipStream_t s) {
       break;
     case TEAL_ACC:
       launch_kernel(a.kind, teal_kernel<WT, DUAL, TEAL_ACC, KT>, grid, dim3(kTbThreads), 0, s, a);
+      break;
+    case TEAL_DOWN:
+      if constexpr (!DUAL)
+        launch_kernel(a.kind, teal_kernel<WT, false, TEAL_DOWN, KT>, grid, dim3(kTbThreads), 0, s,
+                      a);
+      break;
+    case TEAL_CATS_DOWN:
+      if constexpr (!DUAL)
+        launch_kernel(a.kind, teal_kernel<WT, false, TEAL_CATS_DOWN, KT>, grid, dim3(kTbThreads),
+                      0, s, a);
       break;
     case TEAL_SWIGLU:
       if constexpr (DUAL)

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(sd.sd_dims) == 36
-    assert ctypes.sizeof(sd.sd_layer) == 232
+    assert ctypes.sizeof(sd.sd_layer) == 240
     assert ctypes.sizeof(sd.sd_byte_record) == 104
     assert ctypes.sizeof(sd.sd_latency_model) == 24
     assert ctypes.sizeof(sd.sd_seq_kv) == 48

@@ -115,8 +115,9 @@ def test_pmc_summary_maps_templated_kernels_and_scales(tmp_path):
         "void sd::teal_kernel<unsigned short, true, 2, float>(sd::TealArgs)": 143360,
         "void sd::bmma_kernel<8, false, 1, 16>(sd::BmmaArgs)": 131072,
         "void sd::bmma_kernel<8, false, 1, 32>(sd::BmmaArgs)": 229376,
+        "void sd::teal_kernel<unsigned short, false, 5, float>(sd::TealArgs)": 131072,
+        "void sd::teal_kernel<unsigned short, false, 4, float>(sd::TealArgs)": 131072,
         "void sd::down_kernel<unsigned short, 1>(sd::DownArgs)": 131072,
-        "void sd::down_kernel<unsigned short, 8>(sd::DownArgs)": 131072,
     }
     for i, (n, g) in enumerate(names.items()):
         for _ in range(3):
@@ -140,7 +141,7 @@ def test_pmc_summary_maps_templated_kernels_and_scales(tmp_path):
     k = res["kernels"]
     # index of each kind's row in `names` (+1) sets its counter values
     want = {"teal_qkv": 1, "teal_o": 2, "teal_gate_up": 3, "batch_o": 4, "batch_down": 5,
-            "cats_down": 6}
+            "cats_down": 6, "teal_down": 7}
     for kind, i in want.items():
         assert k[kind]["fetch_bytes"] == round(100.0 * i * 1024 * 2.0), kind
         assert k[kind]["write_bytes"] == round(10.0 * i * 1024), kind

@@ -52,7 +52,7 @@ def _one_layer(b, li):
 
 def _oracle_layer(b, caches, li, bb):
     keep, kv, k_keep, _ = caches
-    W = {k: to_host(v) for k, v in b.W[li].items()}
+    W = {k: to_host(v) for k, v in b.W[li].items() if k != "w_down_b"}
     k, v, ks, vs = keep[bb * b.L + li]
     return ostep.Layer(W["attn_norm"], W["w_qkv"], W["w_o"], W["mlp_norm"], W["w_gate"],
                        W["w_up"], W["w_down_t"], b.layers[li].cats_threshold,

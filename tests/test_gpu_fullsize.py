@@ -49,7 +49,7 @@ def _one_layer(b, li):
 
 
 def _oracle_layer(b, li, k_keep):
-    W = {k: to_host(v) for k, v in b.W[li].items()}
+    W = {k: to_host(v) for k, v in b.W[li].items() if k != "w_down_b"}
     L = b.layers[li]
     n, ns = L.n_full, L.n_sel
     k = to_host(b.K[li][:, :n + 1])

@@ -43,7 +43,7 @@ def _one_layer(b, li):
 
 
 def _oracle_layer(b, li):
-    W = {k: to_host(v) for k, v in b.W[li].items()}
+    W = {k: to_host(v) for k, v in b.W[li].items() if k != "w_down_b"}
     L = b.layers[li]
     n, ns = L.n_full, L.n_sel
     return ostep.Layer(W["attn_norm"], W["w_qkv"], W["w_o"], W["mlp_norm"], W["w_gate"],

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import synth
+from synth import device as sdev
 from oracle import selection as osel, step as ostep
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +30,7 @@ class Stack:
     """Host (oracle) and device copies of a small layer stack with caches,
     gathered buffers built from the oracle's own selection."""
 
-    def __init__(self, wl, n_layers, n, k_keep, extra=8, theta=500000.0):
+    def __init__(self, wl, n_layers, n, k_keep, extra=8, theta=500000.0, blocked_down=False):
         self.wl, self.n, self.k_keep, self.theta = wl, n, k_keep, theta
         self.window_keep = k_keep  # the window reads as many entries as the selection keeps
         self.dims = dims_for(wl, theta)
@@ -55,6 +56,8 @@ class Stack:
             dW = {kk: to_dev(vv, "f32" if "norm" in kk else wl.dtype) for kk, vv in W.items()}
             dk, dv, dks, dvs = (to_dev(a, wl.dtype) for a in (k, v, ks, vs))
             mask = torch.zeros(wl.d_ff, dtype=torch.uint8, device=DEV)
+            if blocked_down:  # W_down [d, d_ff] in column blocks of 128 outputs
+                dW["w_down_b"] = sdev.teal_blocked(dW["w_down_t"].t())
             self.keep_alive.append((dW, dk, dv, dks, dvs, mask))
             layers.append(sd.sd_layer(dW["attn_norm"].data_ptr(), dW["w_qkv"].data_ptr(),
                                       dW["w_o"].data_ptr(), dW["mlp_norm"].data_ptr(),
@@ -62,6 +65,8 @@ class Stack:
                                       dW["w_down_t"].data_ptr(), -1.0, 0, dk.data_ptr(),
                                       dv.data_ptr(), cap, n, dks.data_ptr(), dvs.data_ptr(),
                                       ke + extra, ke, mask.data_ptr(), self.window_keep, 4))
+            if blocked_down:
+                layers[-1].w_down_b = dW["w_down_b"].data_ptr()
         self.layers = (sd.sd_layer * n_layers)(*layers)
         self.ws = workspace(self.dims, cap)
 
@@ -146,10 +151,46 @@ def test_8b_two_layers_each_mode(stack8b, mode):
     _check_caches(st, TOL["bf16"])
 
 
-def _identity_props(wl, n, n_layers=1):
+@pytest.fixture(scope="module")
+def stack8b_blocked():
+    wl = synth.L8B_DENSE_8K
+    n = wl.n_ctx
+    return Stack(wl, 2, n, int(0.16 * n), blocked_down=True)
+
+
+@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both", "window+cats"])
+def test_8b_two_layers_down_column_blocks(stack8b_blocked, mode):
+    """The down projection over column blocks (w_down_b): the kept channels'
+    pieces of W_down with the partial sums added inside the launch."""
+    st = stack8b_blocked
+    h = synth.hidden(st.wl, 8)
+    pos = st.olayers[0].n
+    got, want, tr = st.step(h, pos, mode)
+    assert rel_l2(got, want) <= TOL["bf16"], mode
+    if MODES[mode] & sd.SD_MLP_SPARSE:
+        for li in range(2):
+            gmask = st.keep_alive[li][5].cpu().numpy().astype(bool)
+            assert np.array_equal(gmask, tr[li]["mask"])
+    _check_caches(st, TOL["bf16"])
+
+
+def test_tiny_fp32_down_column_blocks_mode_switching():
+    wl = synth.TINY
+    st = Stack(wl, 2, wl.n_ctx, wl.k_keep, extra=16, blocked_down=True)
+    h = synth.hidden(wl, 3).astype(np.float64)
+    pos = wl.n_ctx
+    for mode in ("cats", "dense", "both", "kv", "cats"):
+        got, want, tr = st.step(h, pos, mode)
+        assert rel_l2(got, want) <= TOL["f32"], mode
+        h = want
+        pos += 1
+    _check_caches(st, TOL["f32"])
+
+
+def _identity_props(wl, n, n_layers=1, blocked_down=False):
     """Dense vs KV with an identity gathered buffer, and CATS at t < 0 vs dense:
     the same kernels on the same rows, so the results are bitwise equal."""
-    st = Stack(wl, n_layers, n, n)  # keep ratio 1: gathered buffer == full cache
+    st = Stack(wl, n_layers, n, n, blocked_down=blocked_down)  # gathered buffer == full cache
     h = synth.hidden(wl, 9)
     outs = {}
     for mode in ("dense", "kv", "cats"):
@@ -167,6 +208,10 @@ def _identity_props(wl, n, n_layers=1):
 
 def test_identity_branches_equal_dense_tiny():
     _identity_props(synth.TINY, 1500, 2)
+
+
+def test_identity_branches_equal_dense_tiny_down_column_blocks():
+    _identity_props(synth.TINY, 1500, 2, blocked_down=True)
 
 
 def test_errors_leave_state_untouched(stack8b):

@@ -188,9 +188,11 @@ class TealStack(Stack):
         return to_host(hd), want, tr, gmasks
 
 
-def test_tiny_fp32_teal_step_with_mode_switching():
+@pytest.mark.parametrize("blocked_down", [False, True])
+def test_tiny_fp32_teal_step_with_mode_switching(blocked_down):
+    # blocked_down: the down projection over column blocks (w_down_b)
     wl = synth.TINY
-    st = TealStack(wl, 1, wl.n_ctx, wl.k_keep, extra=16)
+    st = TealStack(wl, 1, wl.n_ctx, wl.k_keep, extra=16, blocked_down=blocked_down)
     h = synth.hidden(wl, 0).astype(np.float64)
     pos = wl.n_ctx
     from test_gpu_step import MODES
@@ -226,10 +228,11 @@ def test_tiny_fp32_teal_two_layers_dense_limit_matches_dense():
         assert st.teal_keep[li][1].cpu().numpy().all()
 
 
+@pytest.mark.parametrize("blocked_down", [False, True])
 @pytest.mark.parametrize("kv_sparse", [False, True])
-def test_8b_teal_layer_matches_oracle_with_its_masks(kv_sparse):
+def test_8b_teal_layer_matches_oracle_with_its_masks(kv_sparse, blocked_down):
     wl = synth.L8B_DENSE_8K
-    st = TealStack(wl, 1, 4096, 655)
+    st = TealStack(wl, 1, 4096, 655, blocked_down=blocked_down)
     h = synth.hidden(wl, 11)
     got, want, tr, gm = st.teal_step(h, 4096, kv_sparse, inject=True)
     assert rel_l2(got, want) <= TOL["bf16"]
@@ -237,13 +240,15 @@ def test_8b_teal_layer_matches_oracle_with_its_masks(kv_sparse):
         assert abs(gm[0][k].mean() - 0.5) < 0.01, k
 
 
+@pytest.mark.parametrize("blocked_down", [False, True])
 @pytest.mark.parametrize("t_down", [1e30, -1.0])
-def test_tiny_fp32_teal_step_down_input_all_dropped_or_all_kept(t_down):
+def test_tiny_fp32_teal_step_down_input_all_dropped_or_all_kept(t_down, blocked_down):
     # the step decides the down projection's mask in the SwiGLU epilogue and
-    # streams the kept rows with the kept-row kernel: with every down input
-    # dropped the MLP adds nothing, with t < 0 it reads every row
+    # streams the kept rows (of w_down_t, or of the column blocks w_down_b):
+    # with every down input dropped the MLP adds nothing, with t < 0 it reads
+    # every row
     wl = synth.TINY
-    st = TealStack(wl, 1, 1000, 300)
+    st = TealStack(wl, 1, 1000, 300, blocked_down=blocked_down)
     h = synth.hidden(wl, 7).astype(np.float64)
     ts = st.thresholds(h, 1000, False, 0.5)
     ts = [(t[0], t[1], t[2], t_down) for t in ts]
