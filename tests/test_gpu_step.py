@@ -225,6 +225,23 @@ def test_errors_leave_state_untouched(stack8b):
     assert [(L.n_full, L.n_sel) for L in st.layers] == saved
 
 
+@pytest.mark.parametrize("n_q,n_kv,n", [(4, 4, 700), (4, 1, 16383), (8, 1, 2400), (4, 2, 2400)])
+def test_head_groups_and_split_counts(n_q, n_kv, n):
+    """The step with one, two, four and eight query heads per KV head, from 10
+    to 256 attention splits with a ragged last chunk, over consecutive steps."""
+    wl = dataclasses.replace(synth.TINY, name=f"tiny-f32-h{n_q}x{n_kv}", n_q_heads=n_q,
+                             n_kv_heads=n_kv, n_ctx=n)
+    st = Stack(wl, 2, n, n // 4, extra=8)
+    h = synth.hidden(wl, 4).astype(np.float64)
+    pos = n
+    for mode in ("dense", "kv", "dense", "both"):
+        got, want, _ = st.step(h, pos, mode)
+        assert rel_l2(got, want) <= TOL["f32"], mode
+        h = want
+        pos += 1
+    _check_caches(st, TOL["f32"])
+
+
 @pytest.fixture(scope="module")
 def stack_wide():
     # a wide layer (d_model 8192, 64 query heads over 8 KV heads, FFN 28672,
