@@ -53,6 +53,7 @@ template <typename WT, bool DUAL, int EPI, typename KT>
 __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
   // rows per wave instruction group in flight: 8 instructions (32 rows) per
   // matrix and wave for bf16, half for float32
+  constexpr bool ACC = EPI == TEAL_ACC || EPI == TEAL_DOWN || EPI == TEAL_CATS_DOWN;
   constexpr int U = (DUAL ? 8 : 16) * 2 / (int)sizeof(WT);
   __shared__ int list[kTealMaxRange];
   __shared__ float xl[kTealMaxRange];
@@ -67,6 +68,14 @@ __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
   const int nblk = gridDim.y;
   const float* __restrict__ x = a.x;
   const float* __restrict__ nw = a.norm;
+  constexpr int NCOL = (DUAL ? 2 : 1) * kTealBlock;  // <= kTbThreads
+  // y += : the block's current outputs, loaded with the inputs (only the
+  // block's last slice writes them, at the end)
+  float y_old = 0.f;
+  if constexpr (ACC) {
+    const int c = b * kTealBlock + threadIdx.x % kTealBlock;
+    if (threadIdx.x < NCOL && c < d_out) y_old = (threadIdx.x >= kTealBlock ? a.y2 : a.y)[c];
+  }
 
   // 1. this slice's inputs (and norm weights) are loaded with the pass that
   //    adds up x^2 for the RMSNorm scale, so both take one memory round trip
@@ -200,7 +209,6 @@ __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
     if constexpr (DUAL) red[g][kTealBlock + 8 * q + e] = acc1[e];
   }
   __syncthreads();
-  constexpr int NCOL = (DUAL ? 2 : 1) * kTealBlock;  // <= kTbThreads
   const int bw = nblk * kTealBlock;                  // a slice's partial width per matrix
   float* part = a.part + (size_t)s * bw;
   if (threadIdx.x < NCOL) {
@@ -227,12 +235,11 @@ __global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
     __hip_atomic_store(a.tickets + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int cb = b * kTealBlock;
-  constexpr bool ACC = EPI == TEAL_ACC || EPI == TEAL_DOWN || EPI == TEAL_CATS_DOWN;
   if constexpr (EPI == TEAL_STORE || ACC) {
     if (threadIdx.x < NCOL) {
       const int mat = threadIdx.x / kTealBlock, c = cb + threadIdx.x % kTealBlock;
       float* y = mat ? a.y2 : a.y;
-      if (c < d_out) y[c] = (ACC ? y[c] : 0.f) + col[threadIdx.x];
+      if (c < d_out) y[c] = y_old + col[threadIdx.x];
     }
   } else if constexpr (EPI == TEAL_SWIGLU) {
     if (threadIdx.x < kTealBlock) {
