@@ -313,7 +313,8 @@ typedef struct {
   int32_t window_sink;     /* SD_KV_WINDOW: sink entries among them */
   /* SD_PROJ_TEAL: the projections in the column-block layout of sd_teal_gemv
    * ([ceil(d_out / 128)][d_in][128]) and the four input thresholds, attention
-   * input, O input, MLP input, down input (w_down_t above serves both modes) */
+   * input, O input, MLP input, down input (w_down_t above, or w_down_b below,
+   * serves every mode) */
   const void* w_qkv_t;     /* W_qkv in column blocks: d_in = d, d_out = (h_q + 2 h_kv) d_h */
   const void* w_o_t;       /* W_o: d_in = h_q d_h, d_out = d */
   const void* w_gate_t;    /* W_gate: d_in = d, d_out = d_ff */
@@ -331,11 +332,13 @@ typedef struct {
   const void* w_gate_m;    /* W_gate [d_ff, d] */
   const void* w_up_m;      /* W_up [d_ff, d] */
   const void* w_down_m;    /* W_down [d, d_ff] (the down projection itself, not w_down_t) */
-  /* optional, sd_decode_step: W_down [d, d_ff] in the column-block layout of
-   * sd_teal_gemv (w_t with d_out = d, d_in = d_ff).  When set, the down
-   * projection reads only the kept channels' pieces of it, with the partial
+  /* optional, sd_decode_step, any mode: W_down [d, d_ff] in the column-block
+   * layout of sd_teal_gemv (w_t with d_out = d, d_in = d_ff), 16-byte
+   * aligned, d at most 131072.  When set, the down projection reads only the
+   * kept channels' pieces of it (every channel when dense), with the partial
    * sums added inside the launch, instead of w_down_t's rows and a separate
-   * reduce; NULL: w_down_t */
+   * reduce launch; same results up to float32 summation order.  NULL:
+   * w_down_t.  The caller owns it; the library only reads it. */
   const void* w_down_b;
 } sd_layer;
 

@@ -271,6 +271,10 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
 // streams with eight waves (measured at 8B-class widths, isolated launches,
 // 50% kept: 16 slices 15.4 us, 12 15.6 us, 8 16.2 us, 24 17.8 us).
 int down_block_slices(int d_ff, int d) {
+  // d_ff <= kDownList * kDownMaxParts (checked with the dims) keeps every
+  // slice within kTealMaxRange channels at kTealMaxSlices slices
+  static_assert(sd::kDownList * sd::kDownMaxParts <= sd::kTealMaxSlices * sd::kTealMaxRange,
+                "the largest accepted d_ff fits the column-block slices");
   const int nblk = (d + sd::kTealBlock - 1) / sd::kTealBlock;
   int s = (2 * sd::cu_count_dev() + nblk - 1) / nblk;
   const int need = (d_ff + sd::kTealMaxRange - 1) / sd::kTealMaxRange;
