@@ -13,17 +13,17 @@
 // owns one block reads, for each kept channel, exactly that channel's piece:
 // two whole 128-byte lines, with no other workgroup sharing them.
 //
-// Grid (S slices, nblk blocks), 256 threads.  Workgroup (s, b):
+// Grid (S slices, nblk blocks), 512 threads.  Workgroup (s, b):
 //   1. with an RMSNorm, adds up x^2 over the whole input (every workgroup
 //      needs the scale); then decides keep_j = |x_j * rs * norm_j| > t (t < 0:
 //      all) in float32 for the channels of its slice [s R, (s + 1) R) and
 //      ranks the kept ones in channel order (block scan of per-thread counts);
 //   2. streams the kept channels' pieces of block b: lane l loads 16 bytes of
 //      row (l / 16) of a group of four, so a wave instruction brings four
-//      rows and the four waves sixteen; U instructions per wave are issued
+//      rows and the eight waves thirty-two; U instructions per wave are issued
 //      before any arithmetic, entries past the list's end repeat its last
 //      row with weight 0;
-//   3. adds its sixteen row groups in LDS in a fixed order and stores the
+//   3. adds its thirty-two row groups in LDS in a fixed order and stores the
 //      slice's partial sums of the block with agent-scope stores (written
 //      through to memory, where every XCD's loads see them), then takes a
 //      ticket for the block;
@@ -42,30 +42,28 @@
 
 namespace sd {
 
-constexpr int kTbThreads = 256;
-constexpr int kTbWaves = kTbThreads / kWave;   // 4
+// 512 threads: a compute unit holding two workgroups streams with sixteen
+// waves (against 256 threads, measured at 8B-class widths with 50% kept:
+// down 15.6 -> 15.2 us, O 9.5 -> 8.8-9.2, gate + up 25.9 -> 25.2-25.7, QKV
+// unchanged)
+constexpr int kTbThreads = 512;
+constexpr int kTbWaves = kTbThreads / kWave;   // 8
 constexpr int kTbSub = kWave / 16;             // rows per wave load instruction (4)
-constexpr int kTbGroups = kTbWaves * kTbSub;   // row groups of a workgroup (16)
-// threads of a workgroup: the down projections, whose slices run two
-// workgroups per compute unit, take twice as many, so that a unit streams
-// with sixteen waves
-constexpr int teal_threads(int epi) {
-  return epi == TEAL_DOWN || epi == TEAL_CATS_DOWN ? 2 * kTbThreads : kTbThreads;
-}
+constexpr int kTbGroups = kTbWaves * kTbSub;   // row groups of a workgroup (32)
+constexpr int kTbCh = kTealMaxRange / kTbThreads;  // slice channels per thread, at most (4)
 static_assert(kTealBlock == 16 * 8, "a block row is 16 lanes x 8 columns");
 
 template <typename WT, bool DUAL, int EPI, typename KT>
-__global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
-  constexpr int TB = teal_threads(EPI), TW = TB / kWave, TG = TW * kTbSub, TCH = kTealMaxRange / TB;
+__global__ __launch_bounds__(kTbThreads) void teal_kernel(TealArgs a) {
   // rows per wave instruction group in flight: 8 instructions (32 rows) per
   // matrix and wave for bf16, half for float32
   constexpr bool ACC = EPI == TEAL_ACC || EPI == TEAL_DOWN || EPI == TEAL_CATS_DOWN;
   constexpr int U = (DUAL ? 8 : 16) * 2 / (int)sizeof(WT);
   __shared__ int list[kTealMaxRange];
   __shared__ float xl[kTealMaxRange];
-  __shared__ int wave_tot[TW];
-  __shared__ float wred[TW];
-  __shared__ float red[TG][(DUAL ? 2 : 1) * kTealBlock];
+  __shared__ int wave_tot[kTbWaves];
+  __shared__ float wred[kTbWaves];
+  __shared__ float red[kTbGroups][(DUAL ? 2 : 1) * kTealBlock];
   __shared__ float col[(DUAL ? 2 : 1) * kTealBlock];
   __shared__ unsigned tk_s;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -74,7 +72,7 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   const int nblk = gridDim.y;
   const float* __restrict__ x = a.x;
   const float* __restrict__ nw = a.norm;
-  constexpr int NCOL = (DUAL ? 2 : 1) * kTealBlock;  // <= TB
+  constexpr int NCOL = (DUAL ? 2 : 1) * kTealBlock;  // <= kTbThreads
   // y += : the block's current outputs, loaded with the inputs (only the
   // block's last slice writes them, at the end)
   float y_old = 0.f;
@@ -87,11 +85,11 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   //    adds up x^2 for the RMSNorm scale, so both take one memory round trip
   const int R = (d_in + S - 1) / S;
   const int r0 = s * R, r1 = min(d_in, r0 + R);
-  const int ch = (R + TB - 1) / TB;  // <= TCH
+  const int ch = (R + kTbThreads - 1) / kTbThreads;  // <= kTbCh
   const int c0 = r0 + threadIdx.x * ch;              // this thread's channels [c0, c0 + ch)
-  float xv[TCH], wv[TCH];
+  float xv[kTbCh], wv[kTbCh];
 #pragma unroll
-  for (int k = 0; k < TCH; ++k) {
+  for (int k = 0; k < kTbCh; ++k) {
     const int c = min(c0 + k, d_in - 1);  // unconditional loads, discarded past the slice
     xv[k] = k < ch ? x[c] : 0.f;
     wv[k] = nw && k < ch ? nw[c] : 1.f;
@@ -99,7 +97,7 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   float rs = 1.f;
   if (nw) {
     float ss = 0.f;
-    for (int i = 4 * threadIdx.x; i < d_in; i += 4 * TB) {
+    for (int i = 4 * threadIdx.x; i < d_in; i += 4 * kTbThreads) {
       const float4 v = *reinterpret_cast<const float4*>(x + i);
       ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
     }
@@ -108,12 +106,12 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int v = 0; v < TW; ++v) tot += wred[v];
+    for (int v = 0; v < kTbWaves; ++v) tot += wred[v];
     rs = 1.0f / sqrtf(tot / (float)d_in + a.eps);
   }
   uint32_t mask = 0;
 #pragma unroll
-  for (int k = 0; k < TCH; ++k) {
+  for (int k = 0; k < kTbCh; ++k) {
     float v = 0.f;
     if (k < ch && c0 + k < r1) {
       v = xv[k];
@@ -124,7 +122,7 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   }
   if (a.keep_out && b == 0) {
 #pragma unroll
-    for (int k = 0; k < TCH; ++k)
+    for (int k = 0; k < kTbCh; ++k)
       if (k < ch && c0 + k < r1) a.keep_out[c0 + k] = (uint8_t)((mask >> k) & 1u);
   }
   const int cnt = __popc(mask);
@@ -133,14 +131,14 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   __syncthreads();
   int before = incl - cnt, m = 0;
 #pragma unroll
-  for (int v = 0; v < TW; ++v) {
+  for (int v = 0; v < kTbWaves; ++v) {
     before += v < wave ? wave_tot[v] : 0;
     m += wave_tot[v];
   }
   {
     int r = before;
 #pragma unroll
-    for (int k = 0; k < TCH; ++k)
+    for (int k = 0; k < kTbCh; ++k)
       if ((mask >> k) & 1u) {
         list[r] = c0 + k;
         xl[r] = xv[k];
@@ -150,7 +148,7 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   if ((a.idx_out || a.n_kept_out) && b == 0) {
     // ranks before this slice: the kept channels of [0, r0), same rule
     int prior = 0;
-    for (int c = threadIdx.x; c < r0; c += TB) {
+    for (int c = threadIdx.x; c < r0; c += kTbThreads) {
       float v = x[c];
       if (nw) v = v * rs * nw[c];
       prior += (a.t < 0.f || fabsf(v) > a.t) ? 1 : 0;
@@ -161,11 +159,11 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
     __syncthreads();
     int off = 0;
 #pragma unroll
-    for (int v = 0; v < TW; ++v) off += wave_tot[v];
+    for (int v = 0; v < kTbWaves; ++v) off += wave_tot[v];
     if (a.idx_out) {
       int r = before;
 #pragma unroll
-      for (int k = 0; k < TCH; ++k)
+      for (int k = 0; k < kTbCh; ++k)
         if ((mask >> k) & 1u) a.idx_out[off + r++] = c0 + k;
     }
     if (a.n_kept_out && s == S - 1 && threadIdx.x == 0) *a.n_kept_out = off + m;
@@ -183,18 +181,18 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   for (int e = 0; e < 8; ++e) acc0[e] = acc1[e] = 0.f;
   const int g = wave * kTbSub + sub;  // this lane's row group
 #pragma unroll 1
-  for (int j0 = 0; j0 < m; j0 += U * TG) {
+  for (int j0 = 0; j0 < m; j0 += U * kTbGroups) {
     Vec8<WT> w0[U], w1[DUAL ? U : 1];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = min(j0 + u * TG + g, m - 1);
+      const int j = min(j0 + u * kTbGroups + g, m - 1);
       const uint32_t off = (uint32_t)list[j] * kTealBlock;  // d_in * 128 < 2^32
       w0[u].load(W0 + off);
       if constexpr (DUAL) w1[u].load(W1 + off);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * TG + g;
+      const int j = j0 + u * kTbGroups + g;
       const float h = j < m ? xl[min(j, m - 1)] : 0.f;
       float f[8];
       w0[u].to_float(f);
@@ -220,7 +218,7 @@ __global__ __launch_bounds__(teal_threads(EPI)) void teal_kernel(TealArgs a) {
   if (threadIdx.x < NCOL) {
     float v = 0.f;
 #pragma unroll
-    for (int k = 0; k < TG; ++k) v += red[k][threadIdx.x];
+    for (int k = 0; k < kTbGroups; ++k) v += red[k][threadIdx.x];
     const int mat = threadIdx.x / kTealBlock, cc = threadIdx.x % kTealBlock;
     store_agent(part + (size_t)mat * S * bw + b * kTealBlock + cc, v);
     __builtin_amdgcn_s_waitcnt(0);  // stored before the ticket
@@ -348,12 +346,12 @@ static void teal_typed(const TealArgs& a, hipStream_t s) {
     case TEAL_DOWN:
       if constexpr (!DUAL)
         launch_kernel(a.kind, teal_kernel<WT, false, TEAL_DOWN, KT>, grid,
-                      dim3(teal_threads(TEAL_DOWN)), 0, s, a);
+                      dim3(kTbThreads), 0, s, a);
       break;
     case TEAL_CATS_DOWN:
       if constexpr (!DUAL)
         launch_kernel(a.kind, teal_kernel<WT, false, TEAL_CATS_DOWN, KT>, grid,
-                      dim3(teal_threads(TEAL_CATS_DOWN)), 0, s, a);
+                      dim3(kTbThreads), 0, s, a);
       break;
     case TEAL_SWIGLU:
       if constexpr (DUAL)
