@@ -266,24 +266,6 @@ void enqueue_mlp(const sd_dims& dm, const Layout& L, char* ws, const float* x, c
   sd::launch_down(dn, dm.w_dtype, s);
 }
 
-// Input slices of the column-block down projection: the fewest (at most 2048
-// channels each) that give every compute unit two workgroups, so that a unit
-// streams with eight waves (measured at 8B-class widths, isolated launches,
-// 50% kept: 16 slices 15.4 us, 12 15.6 us, 8 16.2 us, 24 17.8 us).
-int down_block_slices(int d_ff, int d) {
-  // d_ff <= kDownList * kDownMaxParts (checked with the dims) keeps every
-  // slice within kTealMaxRange channels at kTealMaxSlices slices
-  static_assert(sd::kDownList * sd::kDownMaxParts <= sd::kTealMaxSlices * sd::kTealMaxRange,
-                "the largest accepted d_ff fits the column-block slices");
-  const int nblk = (d + sd::kTealBlock - 1) / sd::kTealBlock;
-  int s = (2 * sd::cu_count_dev() + nblk - 1) / nblk;
-  const int need = (d_ff + sd::kTealMaxRange - 1) / sd::kTealMaxRange;
-  if (s < need) s = need;
-  if (s > sd::kTealMaxSlices) s = sd::kTealMaxSlices;
-  if (s > d_ff / 8) s = d_ff / 8;
-  return s < 1 ? 1 : s;
-}
-
 // One TEAL projection over column blocks, epilogue included (the layout's
 // partials and tickets; the tickets must be zero, and the launch leaves them
 // zero).
@@ -582,8 +564,7 @@ sd_status sd_teal_gemv(const sd_dims* dims, const float* x, int32_t d_in, const 
   if (ws_bytes < L.total) return fail(SD_ENOSPC, "workspace %zu < %zu bytes", ws_bytes, L.total);
   const int nblk = (d_out + sd::kTealBlock - 1) / sd::kTealBlock;
   const int mats = w2_t ? 2 : 1;
-  const size_t need = (size_t)sd::teal_slices(d_in, d_out, mats, dims->w_dtype == SD_BF16 ? 2 : 4) *
-                      nblk * sd::kTealBlock * mats;
+  const size_t need = (size_t)sd::teal_slices(d_in, d_out) * nblk * sd::kTealBlock * mats;
   if (need > L.teal_part_floats || nblk > sd::kTealMaxBlocks)
     return fail(SD_ENOSPC, "d_in %d x d_out %d needs %zu partial floats, the workspace holds %zu",
                 d_in, d_out, need, L.teal_part_floats);
@@ -795,7 +776,6 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
         sd::TealArgs db = teal_args(sd::K_TEAL_DOWN, *dims, L, wsb, hmid, ff, nullptr, l.teal_t[3],
                                     l.w_down_b, nullptr, d, sd::TEAL_DOWN);
         db.y = hidden;
-        db.slices = down_block_slices(ff, d);
         sd::launch_teal(db, dims->w_dtype, dims->kv_dtype, s);
         continue;
       }
@@ -826,7 +806,6 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
                                   mlp_sparse ? 0.0f : -1.0f, l.w_down_b, nullptr, d,
                                   sd::TEAL_CATS_DOWN);
       db.y = hidden;
-      db.slices = down_block_slices(dims->d_ff, d);
       sd::launch_teal(db, dims->w_dtype, dims->kv_dtype, s);
       continue;
     }

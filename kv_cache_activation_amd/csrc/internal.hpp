@@ -126,7 +126,7 @@ enum TealEpi {
   TEAL_DOWN = 4,
   TEAL_CATS_DOWN = 5
 };
-int teal_slices(int d_in, int d_out, int mats, int wbytes);
+int teal_slices(int d_in, int d_out);
 
 struct TealArgs {
   int kind;            // profiler kind of this projection
@@ -148,7 +148,6 @@ struct TealArgs {
   int32_t* idx_out;    // optional ascending kept list
   int32_t* n_kept_out; // optional
   uint8_t* keep_out;   // optional keep bytes [d_in]
-  int slices;          // input slices; 0: teal_slices
 };
 
 // Batched attention: sequence s has its own cache (k[s], v[s], cap[s]) of

@@ -298,44 +298,32 @@ __global__ void teal_zero_kernel(unsigned* __restrict__ t, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) t[i] = 0u;
 }
 
-// Slices per projection.  Workgroup (s, b) reads the kept pieces of d_in / S
-// channels of block b, and the chip holds every workgroup at once, so a
-// launch lasts about as long as its busiest compute unit: the number of
-// workgroups it holds times (one workgroup's weight bytes plus a fixed cost
-// worth about 64 KB of them: the x^2 pass, the staging, the partial sums and
-// the ticket).  S minimises that, over the counts whose grid gives every
-// compute unit a workgroup when there are such counts, with at most
-// kTealMaxRange and at least 8 channels per slice and at most kTealMaxSlices
-// slices.  (Measured at 8B-class widths, 50% kept: gate + up 4 slices,
-// 25.1 us, against 28.1 us for 5; QKV 10, 11.5 against 13.2 us for 11; O 8,
-// 9.4 against 11.6 us for 16.)
-int teal_slices(int d_in, int d_out, int mats, int wbytes) {
-  const int nblk = (d_out + kTealBlock - 1) / kTealBlock, cus = cu_count_dev();
+// Slices per projection: the most that keep every compute unit at one
+// workgroup at most (S * nblk <= CUs), within kTealMaxRange and at least 8
+// channels per slice and kTealMaxSlices slices.  A 512-thread workgroup
+// streams with eight waves; a second workgroup on a unit adds its own
+// partial sums, ticket and staging more than it adds bandwidth.  Measured
+// at 8B-class widths, 50% kept, in the step at 131072 context: QKV 5
+// slices 10.4-10.6 us, against 11.5 for 4, 11.3-11.9 for 8, 11.6 for 10;
+// O 8 slices 8.5-9.5 us against 10.1 for 12 and 11.7 for 16; gate + up 2
+// slices 24.6 us against 27.3 for 3 and 25.6-25.9 for 4; the down
+// projection 8 slices (composed step 2507-2522 us) against 7 (2542-2544),
+// 10 (2569) and 16 (2541-2548).
+int teal_slices(int d_in, int d_out) {
+  const int nblk = (d_out + kTealBlock - 1) / kTealBlock;
   const int lo = (d_in + kTealMaxRange - 1) / kTealMaxRange;
   int hi = d_in / 8;
   if (hi > kTealMaxSlices) hi = kTealMaxSlices;
   if (hi < lo) hi = lo;
-  int best = lo;
-  bool best_full = false;
-  double best_cost = 0.0;
-  for (int S = lo; S <= hi; ++S) {
-    const long long wgs = (long long)S * nblk;
-    const bool full = wgs >= cus;
-    const double per = (double)d_in * kTealBlock * wbytes * mats / S + 65536.0;
-    const double cost = (double)((wgs + cus - 1) / cus) * per;
-    if (S == lo || (full && !best_full) || (full == best_full && cost < best_cost)) {
-      best = S;
-      best_full = full;
-      best_cost = cost;
-    }
-  }
-  return best < 1 ? 1 : best;
+  int s = cu_count_dev() / nblk;
+  if (s < lo) s = lo;
+  if (s > hi) s = hi;
+  return s < 1 ? 1 : s;
 }
 
 template <typename WT, bool DUAL, typename KT>
 static void teal_typed(const TealArgs& a, hipStream_t s) {
-  const dim3 grid(a.slices > 0 ? a.slices : teal_slices(a.d_in, a.d_out, DUAL ? 2 : 1, (int)sizeof(WT)),
-                  (a.d_out + kTealBlock - 1) / kTealBlock);
+  const dim3 grid(teal_slices(a.d_in, a.d_out), (a.d_out + kTealBlock - 1) / kTealBlock);
   switch (a.epi) {
     case TEAL_STORE:
       launch_kernel(a.kind, teal_kernel<WT, DUAL, TEAL_STORE, KT>, grid, dim3(kTbThreads), 0, s, a);
