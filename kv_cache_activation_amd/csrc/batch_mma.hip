@@ -50,8 +50,9 @@
 //      |a_b| > t, hmid_b = keep_b ? a_b up_b : 0, and the union of the keeps.
 // The slice length (8, 16 or 32 steps) is chosen per launch so that the grid
 // covers every compute unit and the chip holds it at once: every workgroup
-// streams from the start and none waits for a second round.  No workgroup waits for another, and the summation
-// order is fixed.
+// streams from the start and none waits for a second round.  Gate + up takes
+// 64-step slices instead when that grid keeps every unit at one workgroup.
+// No workgroup waits for another, and the summation order is fixed.
 // Gate, up and down are read whole: at the batch sizes that need this path
 // the union of the masks keeps nearly every channel, and the channels it
 // drops are too few and too scattered to skip 16 rows or 32 channels at a
@@ -482,6 +483,15 @@ static bool mm_try(const BmmaArgs& a, hipStream_t s, int mode) {
 
 template <int NB, bool DUAL, int EPI>
 static void mm_launch(const BmmaArgs& a, hipStream_t s) {
+  // gate + up: 64-step slices when that keeps every compute unit at one
+  // workgroup at most, each unit then streaming both matrices' rows with one
+  // set of partial sums (measured at B = 8, 8B-class widths: 42.1-43.4 us
+  // against 45.7-46.4 for 32-step slices, two workgroups on most units; the
+  // same rule for down, 25.1-25.8 against 25.0, and QKV, 14.9 against 15.0,
+  // gained nothing)
+  if (DUAL && (long long)bmma_groups(a.rows) * mm_slices(a.d_in, 64) <= cu_count_dev() &&
+      mm_try<NB, DUAL, EPI, 64>(a, s, 1))
+    return;
   if (mm_try<NB, DUAL, EPI, 32>(a, s, 0)) return;
   if (mm_try<NB, DUAL, EPI, 16>(a, s, 0)) return;
   if (mm_try<NB, DUAL, EPI, 8>(a, s, 0)) return;
