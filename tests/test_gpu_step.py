@@ -158,7 +158,7 @@ def stack8b_blocked():
     return Stack(wl, 2, n, int(0.16 * n), blocked_down=True)
 
 
-@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both", "window+cats"])
+@pytest.mark.parametrize("mode", ["dense", "kv", "cats", "both", "window+cats", "masked", "fused"])
 def test_8b_two_layers_down_column_blocks(stack8b_blocked, mode):
     """The down projection over column blocks (w_down_b): the kept channels'
     pieces of W_down with the partial sums added inside the launch."""
