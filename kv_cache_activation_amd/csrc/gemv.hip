@@ -32,6 +32,13 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // row per wave, stage its 16 KB input once per 16 rows instead of per 4
 // (7.0 vs 8.2 us per launch); QKV and gate + up were no faster that way.
 constexpr int kQkvWide = kThreads, kOWide = 1024, kGateWide = kThreads;
+// QKV workgroups per compute unit, at most: with one, each unit stages the
+// input once and its four waves take more rows each.  Measured in the
+// composed step at 131072 context: 2483-2484 us per step against 2494-2496
+// with the three the occupancy allows (2486-2489 with two, 2505 with 384
+// workgroups); gate + up was slower with fewer workgroups (2511 with 768,
+// 2541 with 512, against 2506 with 1024).
+constexpr int kQkvPerCu = 1;
 
 // float4 chunks per thread when T threads stage a row of 512 NCH elements
 // (EXACT: no bounds tests)
@@ -294,10 +301,11 @@ __global__ __launch_bounds__(T) void gate_kernel(
 // ------------------------------------------------------------------ launchers
 // Grid of a row-streaming kernel: as many workgroups as the chip holds at
 // once (compute units x resident workgroups per unit, which the kernel's
-// register use decides), no more waves than work items, and at most
-// per_wave items per wave (a wave keeps one result per lane).
+// register use decides, at most cap_per_cu when that is positive), no more
+// waves than work items, and at most per_wave items per wave (a wave keeps
+// one result per lane).
 template <int T, typename K>
-static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
+static int gemv_grid(K kernel, int rows, int per_wave, size_t lds, int cap_per_cu) {
   constexpr int kWavesPerBlock = T / kWave;
   // resident workgroups per compute unit, per kernel and LDS size (queried once)
   static std::mutex mu;
@@ -316,6 +324,7 @@ static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
     }
     per_cu = it->second;
   }
+  if (cap_per_cu > 0 && per_cu > cap_per_cu) per_cu = cap_per_cu;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -339,8 +348,8 @@ static int gemv_grid(K kernel, int rows, int per_wave, size_t lds) {
 
 template <int T, typename K, typename... Args>
 static void launch_rows(int kind, K kernel, int items, int per_wave, int grid_y, size_t lds,
-                        hipStream_t s, Args... args) {
-  const int grid = gemv_grid<T>(kernel, items, per_wave, lds);
+                        int cap_per_cu, hipStream_t s, Args... args) {
+  const int grid = gemv_grid<T>(kernel, items, per_wave, lds, cap_per_cu);
   launch_kernel(kind, kernel, dim3(grid, grid_y), dim3(T), (uint32_t)lds, s, args...);
 }
 
@@ -350,7 +359,7 @@ static void qkv_typed(const QkvArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.d * sizeof(float);
   SD_ROW_DISPATCH(a.d, constexpr int TH = (NCH == 8 && FULL && sizeof(WT) == 2) ? kQkvWide : kThreads;
                   launch_rows<TH>(K_QKV, qkv_rope_append_kernel<WT, KT, NCH, FULL, TH>, pairs, kWave / 2,
-                                   1, lds, s, a.h, a.norm, a.eps,
+                                   1, lds, kQkvPerCu, s, a.h, a.norm, a.eps,
                                       (const WT*)a.w, a.d, a.h_q, a.h_kv, a.dh, a.rope, a.q_out,
                                       (KT*)a.k_full, (KT*)a.v_full, a.cap_full, a.row_full,
                                       (KT*)a.k_sel, (KT*)a.v_sel, a.cap_sel, a.row_sel, a.ragged,
@@ -372,7 +381,7 @@ void launch_o(const float* attn, const void* w, int din, int dout, float* h, int
 #define SD_O(T, ONE_)                                                                          \
   SD_ROW_DISPATCH(din, constexpr int TH = (NCH == 8 && FULL && sizeof(T) == 2) ? kOWide : kThreads; \
                   launch_rows<TH>(K_O, o_residual_kernel<T, NCH, FULL, ONE_, TH>, dout,       \
-                                   ONE_ ? 1 : kWave, 1, lds, s, attn, (const T*)w, din, dout, h))
+                                   ONE_ ? 1 : kWave, 1, lds, 0, s, attn, (const T*)w, din, dout, h))
   if (w_dtype == 1) {
     if (one) {
       SD_O(bf16_t, true);
@@ -395,7 +404,7 @@ void launch_gate(const GateArgs& a, int w_dtype, hipStream_t s) {
 #define SD_GATE_N(T, NRM, CAL)                                                               \
   SD_ROW_DISPATCH(a.d, constexpr int TH = (NCH == 8 && FULL && sizeof(T) == 2) ? kGateWide : kThreads; \
                   launch_rows<TH>(K_GATE_UP, gate_kernel<T, NCH, FULL, NRM, CAL, TH>, a.dff, kWave, \
-                                   a.n_states, lds, s, a.x, a.norm, a.eps,                    \
+                                   a.n_states, lds, 0, s, a.x, a.norm, a.eps,                 \
                                    (const T*)a.w_gate, (const T*)a.w_up, a.d, a.dff, a.t,     \
                                    a.gate_in, a.store_abs, a.act, a.keep, a.hmid))
 #define SD_GATE(T, CAL)          \
