@@ -228,6 +228,24 @@ def test_tiny_fp32_teal_two_layers_dense_limit_matches_dense():
         assert st.teal_keep[li][1].cpu().numpy().all()
 
 
+@pytest.mark.parametrize("n_q,n_kv,n", [(4, 1, 2400), (8, 2, 5000), (4, 1, 16383)])
+def test_tiny_fp32_teal_step_head_groups_and_split_counts(n_q, n_kv, n):
+    """The TEAL step with four query heads per KV head and dense steps of 38,
+    79 and 256 attention splits, KV steps of 10, 20 and 64."""
+    wl = dataclasses.replace(synth.TINY, name=f"tiny-f32-h{n_q}x{n_kv}", n_q_heads=n_q,
+                             n_kv_heads=n_kv, n_ctx=n)
+    st = TealStack(wl, 1, n, n // 4, extra=8, blocked_down=True)
+    h = synth.hidden(wl, 6).astype(np.float64)
+    pos = n
+    for kv_sparse in (False, True):
+        got, want, tr, gm = st.teal_step(h, pos, kv_sparse)
+        assert rel_l2(got, want) <= TOL["f32"], kv_sparse
+        for k in range(4):
+            assert np.array_equal(gm[0][k], tr[0]["masks"][k]), (kv_sparse, k)
+        h = want
+        pos += 1
+
+
 @pytest.mark.parametrize("blocked_down", [False, True])
 @pytest.mark.parametrize("kv_sparse", [False, True])
 def test_8b_teal_layer_matches_oracle_with_its_masks(kv_sparse, blocked_down):
