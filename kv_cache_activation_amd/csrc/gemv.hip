@@ -28,10 +28,12 @@ namespace sd {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 // Workgroup size of the d = 4096 instances with bf16 weights.  Measured on
-// MI355X (32-layer composed step at 131072 context): 1024 threads for O, one
-// row per wave, stage its 16 KB input once per 16 rows instead of per 4
-// (7.0 vs 8.2 us per launch); QKV and gate + up were no faster that way.
-constexpr int kQkvWide = kThreads, kOWide = 1024, kGateWide = kThreads;
+// MI355X (32-layer composed step at 131072 context): 512 threads for O, one
+// row per wave, two workgroups per unit, each staging its 16 KB input once
+// per 8 rows (1024 threads: 7.0 against 8.2 us per launch for 256; 512: the
+// step 2485-2487 against 2495-2499 us for 1024); QKV and gate + up were no
+// faster with wider workgroups.
+constexpr int kQkvWide = kThreads, kOWide = 512, kGateWide = kThreads;
 // QKV workgroups per compute unit, at most: with one, each unit stages the
 // input once and its four waves take more rows each.  Measured in the
 // composed step at 131072 context: 2483-2484 us per step against 2494-2496
