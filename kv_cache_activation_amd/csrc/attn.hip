@@ -54,8 +54,13 @@ constexpr float kLazyMax = 8.f;
 // Maximum of a lane group that has seen no row yet: finite, so 2^(z - m) of a
 // masked logit (z = -inf) is 0 and never NaN.
 constexpr float kNoRow = -1e30f;
-// Register buffers of rows in rotation (NBUF - 1 in flight during a compute).
+// Register buffers of rows in rotation (NBUF - 1 in flight during a compute):
+// three for chunks of at least kAttnLongChunk rows (one cache and one length;
+// measured at 131072 rows per head, 4096-row chunks: dense decoding 5178-5180
+// -> 5148-5161 us per step), two otherwise (three slowed the 410-row chunks of
+// the KV branch at 131072 and the batched chunks).
 constexpr int kAttnBufs = 2;
+constexpr int kAttnLongChunk = 2048;
 
 // Max and sum over aligned groups of N lanes (16, 32 or 64), VALU exchanges.
 template <int N>
@@ -441,16 +446,17 @@ static void attn_dh(const AttnArgs& a, hipStream_t s) {
   }
   const KT* k = (const KT*)a.k;
   const KT* v = (const KT*)a.v;
-#define SD_ATTN_M(GG, UU, EE, MM)                                                           \
-  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU, EE, MM, kAttnBufs>, grid,            \
+#define SD_ATTN_M(GG, UU, EE, MM, NB)                                                       \
+  launch_kernel(K_ATTN_PARTIAL, attn_kernel<KT, DH, GG, UU, EE, MM, NB>, grid,                   \
                 dim3(kAttnThreads), 0,                                                        \
                 s, a.q, k, v, a.cap, a.n_ctx, a.sink, a.shift, kv_div, a.ragged, a.lens, starts,   \
                 a.batched, a.bt, a.h_q, scale_log2, a.chunk, a.n_splits, a.pm, a.pl, a.pacc)
-#define SD_ATTN_G(GG, UU, EE)                  \
-  do {                                         \
-    if (a.batched) SD_ATTN_M(GG, UU, EE, 2);   \
-    else if (a.ragged) SD_ATTN_M(GG, UU, EE, 1); \
-    else SD_ATTN_M(GG, UU, EE, 0);             \
+#define SD_ATTN_G(GG, UU, EE)                                       \
+  do {                                                              \
+    if (a.batched) SD_ATTN_M(GG, UU, EE, 2, kAttnBufs);             \
+    else if (a.ragged) SD_ATTN_M(GG, UU, EE, 1, kAttnBufs);         \
+    else if (a.chunk >= kAttnLongChunk) SD_ATTN_M(GG, UU, EE, 0, 3); \
+    else SD_ATTN_M(GG, UU, EE, 0, kAttnBufs);                       \
   } while (0)
   switch (G) {
     // rows per slot and buffer: one for four query heads per KV head (measured

@@ -181,10 +181,11 @@ def test_baselines_8b_bf16_match_oracle(path):
 
 @pytest.mark.parametrize("h_q,h_kv", [(8, 8), (64, 8)])
 @pytest.mark.parametrize("dtype,dh", [("f32", 64), ("bf16", 128)])
-@pytest.mark.parametrize("n_ctx,splits", [(4099, 0), (20001, 256), (20001, 129)])
+@pytest.mark.parametrize("n_ctx,splits", [(4099, 0), (20001, 256), (20001, 129), (20001, 8)])
 def test_query_group_sizes_match_oracle(h_q, h_kv, dtype, dh, n_ctx, splits):
     # one and eight query heads per KV head (the kernel's other group
-    # instances), up to the largest split count and the widest merge
+    # instances), up to the largest split count and the widest merge, and
+    # 2501-row chunks (the three-buffer instances)
     wl = dataclasses.replace(synth.L8B_DENSE_8K, name=f"attn-g{h_q // h_kv}-{dtype}", wid=6,
                              n_q_heads=h_q, n_kv_heads=h_kv, head_dim=dh, dtype=dtype)
     k, v = synth.kv_cache(wl, 0, n_ctx, n_ctx + 3)
