@@ -760,10 +760,10 @@ sd_status sd_decode_step(const sd_dims* dims, int32_t n_layers, sd_layer* layers
       ao.keep_out = tm ? tm + d : nullptr;
       sd::launch_teal(ao, dims->w_dtype, dims->kv_dtype, s);
       // gate and up share the MLP input; hmid = SiLU(gate) * up.  The epilogue
-      // also decides the down projection's input mask, so the down projection
-      // is the kept-row kernel of the CATS branch (w_down_t is the same
-      // [d_ff, d] layout): it ranks keep bytes instead of re-reading and
-      // re-testing the float input in every workgroup
+      // also decides the down projection's input mask: without w_down_b the
+      // down projection is the kept-row kernel of the CATS branch (w_down_t is
+      // the same [d_ff, d] layout), which ranks those keep bytes instead of
+      // re-reading and re-testing the float input in every workgroup
       uint8_t* dkeep = tm ? tm + 2 * d + hq * dh : reinterpret_cast<uint8_t*>(wsb + L.keep);
       sd::TealArgs ag = teal_args(sd::K_TEAL_GATE_UP, *dims, L, wsb, hidden, d, l.mlp_norm,
                                   l.teal_t[2], l.w_gate_t, l.w_up_t, ff, sd::TEAL_SWIGLU);
